@@ -1,0 +1,168 @@
+"""Pins for the oracle's balancing and row rounding (SJ-KVaRN section 2.2
+"Balancing" and "Rounding"; section 2.3 "Scalar body").
+
+The closed form: for X_ij = a_i b_j (-1)^(i+j) with b_(2k) = b_(2k+1) > 0, every
+row and column of X has mean zero, the first row pass leaves
+y_ij = b_j (-1)^(i+j) / rms(b), the first column pass makes every entry +-1,
+and every later pass changes nothing; centring gives
+C_j = fp16(b_j / geomean(b)) and the codes are 2^b - 1 where X > 0 and 0 where X < 0."""
+import numpy as np
+import pytest
+
+from oracle import record, rounding, sinkhorn
+from quantized_kv_cache_seal_amd import inputs
+
+
+def _checker(a, b):
+    i = np.arange(len(a))[:, None]
+    j = np.arange(len(b))[None, :]
+    return np.outer(a, b) * np.where((i + j) % 2 == 0, 1.0, -1.0)
+
+
+def _pairs(seed, cols):
+    half = np.exp(inputs.normal_np(seed, 2, 0, cols // 2) * 0.7)
+    return np.repeat(half, 2)
+
+
+@pytest.mark.parametrize("passes", [2, 3, 8, 16])
+@pytest.mark.parametrize("cols", [128, 256])
+def test_checkerboard_closed_form(passes, cols):
+    a = np.exp(inputs.normal_np(1, 1, 0, 128))
+    b = _pairs(2, cols)
+    x = _checker(a, b)
+    bal = sinkhorn.balance(x, passes)
+    gm = np.exp(np.mean(np.log(b)))
+    assert np.array_equal(bal["C"], (b / gm).astype(np.float16))
+    for bits in (4, 8):
+        codes, S, Z = rounding.round_rows(x.astype(np.float32), bal["C"], bits)
+        assert np.array_equal(codes, np.where(x > 0, 2 ** bits - 1, 0).astype(np.uint8))
+
+
+def test_single_row_pass_leaves_unit_columns():
+    x = _checker(np.exp(inputs.normal_np(1, 1, 0, 128)), _pairs(2, 256))
+    assert np.all(sinkhorn.balance(x, 1)["C"] == np.float16(1.0))
+    assert np.all(sinkhorn.balance(x, 0)["C"] == np.float16(1.0))
+
+
+def _tile(seed, cols=256):
+    x = inputs.normal_np(seed, 3, 0, 128 * cols).reshape(128, cols)
+    x *= np.exp(inputs.normal_np(seed, 4, 0, cols))[None, :]      # uneven columns
+    x *= np.exp(0.5 * inputs.normal_np(seed, 5, 0, 128))[:, None]  # uneven rows
+    return x.astype(np.float16).astype(np.float32)
+
+
+def test_final_column_pass_gives_unit_column_spread():
+    x = _tile(9).astype(np.float64)
+    for passes in (2, 8, 16):
+        bal = sinkhorn.balance(x, passes)
+        y = x * np.exp(-bal["lr"][:, None] - bal["lc_raw"][None, :])
+        assert np.max(np.abs(y.std(axis=0) - 1.0)) < 1e-12
+        assert abs(np.mean(bal["lc"])) < 1e-12
+    # more passes make the row spreads more even
+    y2 = x * np.exp(-sinkhorn.balance(x, 2)["lr"][:, None] - sinkhorn.balance(x, 2)["lc_raw"][None, :])
+    b16 = sinkhorn.balance(x, 16)
+    y16 = x * np.exp(-b16["lr"][:, None] - b16["lc_raw"][None, :])
+    assert np.std(y16.std(axis=1)) < np.std(y2.std(axis=1))
+
+
+def test_power_of_two_row_scaling_invariance():
+    x = _tile(10)
+    k = (inputs.uniform_np(10, 6, 0, 128) * 8).astype(int) - 4
+    xs = (x * np.exp2(k)[:, None].astype(np.float32)).astype(np.float32)
+    c1 = sinkhorn.balance(x.astype(np.float64), 16)["C"]
+    c2 = sinkhorn.balance(xs.astype(np.float64), 16)["C"]
+    ulps = np.abs(c1.view(np.int16).astype(int) - c2.view(np.int16).astype(int))
+    assert ulps.max() <= 1
+    # codes are unchanged where the column scales are identical
+    if np.array_equal(c1, c2):
+        a, _, _ = rounding.round_rows(x, c1, 4)
+        b, _, _ = rounding.round_rows(xs, c2, 4)
+        assert np.array_equal(a, b)
+
+
+def test_column_scaling_equivariance():
+    x = _tile(11).astype(np.float64)
+    c = np.exp(inputs.normal_np(11, 7, 0, 256))
+    b1 = sinkhorn.balance(x, 16)
+    b2 = sinkhorn.balance(x * c[None, :], 16)
+    gm = np.exp(np.mean(np.log(c)))
+    assert np.allclose(b2["lc"], b1["lc"] + np.log(c / gm), atol=1e-9)
+
+
+def test_round_rows_brute_force_nearest_level():
+    x = _tile(12)
+    C = sinkhorn.balance(x.astype(np.float64), 16)["C"]
+    for bits in (4, 8):
+        codes, S, Z = rounding.round_rows(x, C, bits)
+        t = rounding.pre_round_values(x, C, S, Z).astype(np.float64)
+        lv = np.arange(2 ** bits)
+        best = np.argmin(np.abs(t[..., None] - lv), axis=-1)
+        tie = np.abs(np.abs(t - np.floor(t)) - 0.5) < 1e-12
+        assert np.array_equal(codes[~tie], best[~tie])
+        # bound on the dequantised error: C_j (S_i / 2 + |Z_i - mn_i|), plus fp32 slack
+        y = x.astype(np.float64) / C.astype(np.float64)[None, :]
+        mn = y.min(axis=1)
+        deq = rounding.dequant(codes, C, S, Z)
+        bound = C.astype(np.float64)[None, :] * (S.astype(np.float64)[:, None] / 2 * (1 + 1e-5)
+                                                 + np.abs(Z.astype(np.float64) - mn)[:, None]
+                                                 + 1e-6 * np.abs(y).max(axis=1)[:, None])
+        assert np.all(np.abs(deq - x) <= bound)
+
+
+def test_round_rows_exact_grid():
+    # a row already on its grid (values Z + k S, C = 1) comes back with codes k
+    S = np.float16(0.25)
+    Z = np.float16(-1.5)
+    k = (inputs.uniform_np(13, 1, 0, 256) * 16).astype(np.int64)
+    k[0], k[1] = 0, 15
+    row = (np.float32(Z) + k.astype(np.float32) * np.float32(S)).astype(np.float32)
+    codes, S2, Z2 = rounding.round_rows(row[None, :], np.ones(256, np.float16), 4)
+    assert S2[0] == S and Z2[0] == Z and np.array_equal(codes[0], k)
+
+
+def test_constant_row_scale_one():
+    x = np.full((128, 256), 3.0, np.float32)
+    codes, S, Z = rounding.round_rows(x, np.ones(256, np.float16), 4)
+    assert np.all(S == np.float16(1.0)) and np.all(Z == np.float16(3.0)) and np.all(codes == 0)
+
+
+def test_nibble_order_every_position_and_value():
+    rng = np.random.default_rng(1)
+    for bits, rows, cols in ((4, 128, 256), (4, 256, 128), (8, 128, 128)):
+        for pos in range(cols):
+            for val in range(0, 2 ** bits, 1 if bits == 4 else 17):
+                c = rng.integers(0, 2 ** bits, (rows, cols)).astype(np.uint8)
+                c[pos % rows, pos] = val
+                buf = record.pack_rows(c, bits)
+                assert len(buf) == rows * cols * bits // 8
+                raw = np.frombuffer(buf, np.uint8).reshape(rows, -1)
+                if bits == 4:
+                    byte = raw[pos % rows, pos // 2]
+                    assert ((byte >> (4 * (pos % 2))) & 15) == val
+                else:
+                    assert raw[pos % rows, pos] == val
+                assert np.array_equal(record.unpack_rows(buf, rows, cols, bits), c)
+
+
+def test_record_sizes_and_round_trip():
+    assert record.record_bytes(256, 4, 4) == 34816
+    assert record.record_bytes(512, 4, 4) == 2 * 34816
+    assert record.record_bytes(128, 8, 4) == 128 * 128 + 128 * 64 + 2 * 2 * (128 + 256)
+    x = _tile(14)
+    rng = np.random.default_rng(2)
+    sides = []
+    for bits in (4, 4):
+        C = sinkhorn.balance(x.astype(np.float64), 8)["C"]
+        codes, S, Z = rounding.round_rows(x, C, bits)
+        sides.append({"codes": codes, "C": C, "S": S, "Z": Z})
+    buf = record.build_sub(sides[0], sides[1], 4, 4)
+    assert len(buf) == 34816
+    k, v = record.parse_sub(buf, 256, 4, 4)
+    for a, b in ((k, sides[0]), (v, sides[1])):
+        for n in ("codes", "C", "S", "Z"):
+            assert np.array_equal(a[n], b[n])
+    # V codes are stored channel-major: byte b of channel row j holds tokens 2b, 2b+1
+    raw = np.frombuffer(buf, np.uint8)
+    j, t = 37, 91
+    byte = raw[16384 + j * 64 + t // 2]
+    assert ((byte >> (4 * (t % 2))) & 15) == sides[1]["codes"][t, j]

@@ -1,0 +1,198 @@
+/*
+ * kvq.h -- C ABI of an MI355X (gfx950) quantized KV cache: a 128-token fp16
+ * sink, a rotated 6-bit staging ring holding the exact tail, and sealed 4-bit
+ * (or 8-bit key) body records, read by one split-K decode-attention pass.
+ *
+ * The method is SJ-KVaRN (page "SJ-KVaRN", sections 2-4) built on KVarN:
+ *   - section 2.1 "The life of a token": sink, staging, exact tail, seal;
+ *   - section 2.2: Hadamard rotation, Sinkhorn-style balancing, per-row
+ *     rounding with fp16 scale and zero point;
+ *   - section 4.3 "Adaptive tail": the tail grows from tail_min to tail_max,
+ *     then every full 128-token group older than the newest tail_min tokens
+ *     is sealed in one batch; an idle server seals back to tail_min;
+ *   - section 10: sealed records cannot be partly rewritten.
+ * Page "KV cache math": the randomized Walsh-Hadamard transform on 128
+ * values (sign flip, transform, sign flip) and the fused rotated-domain
+ * attention (rotate the query once, read raw blocks, rotate the output back).
+ *
+ * Conventions for every call:
+ *   - Every function returns a kvq_status; no C++ exception crosses the ABI.
+ *   - Argument, capacity and state errors are detected on the host before
+ *     anything is enqueued, and then leave the cache unchanged.
+ *   - "device" pointers are HIP device memory owned by the caller; they must
+ *     stay valid until the work enqueued on `stream` has finished.  "host"
+ *     pointers are read or written before the call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously on it; the hot path (append, seal,
+ *     decode) never waits for the device.
+ *   - A cache handle is not thread-safe: use one handle per host thread.
+ *   - kvq_last_error() returns a thread-local message for the last failure.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID = -1,     /* bad argument, shape or configuration            */
+  KVQ_ERR_CAPACITY = -2,    /* context beyond max_ctx, or arena too small      */
+  KVQ_ERR_RING_FULL = -3,   /* staging ring cannot take the tokens: seal first */
+  KVQ_ERR_SEALED = -4,      /* would rewrite part of a sealed record           */
+  KVQ_ERR_DEVICE = -5,      /* a HIP call failed (detail in kvq_last_error)    */
+  KVQ_ERR_UNSUPPORTED = -6  /* valid but not supported by this build / mode    */
+} kvq_status;
+
+enum { KVQ_SEAL_IF_FULL = 0, KVQ_SEAL_TO_MIN = 1 };
+enum { KVQ_REGION_SINK = 0, KVQ_REGION_RING = 1, KVQ_REGION_BODY = 2 };
+enum { KVQ_OUT_F32 = 0, KVQ_OUT_F16 = 1 };
+enum { KVQ_PATH_AUTO = 0, KVQ_PATH_VALU = 1, KVQ_PATH_MFMA = 2 };
+enum { KVQ_FLAG_PLAN_ONLY = 1 };   /* metadata only: no arena, no kernels */
+
+/* Sizes are in tokens unless noted.  Constraints checked by every call:
+ *   head_dim in {128, 256, 512}; n_q_heads a multiple of n_kv_heads with
+ *   n_q_heads / n_kv_heads <= 16; k_bits in {4, 8}, v_bits == 4;
+ *   tail_min a multiple of 128, 128 <= tail_min <= tail_max;
+ *   margin >= 0; max_ctx >= 1; 0 <= sinkhorn_passes <= 64.
+ * Ring capacity = round_up(tail_max + margin, 128) token slots, allocated up
+ * front (SJ-KVaRN section 3).  Body capacity = (max_ctx - 128) / 128 records
+ * per (sequence, layer, KV head). */
+typedef struct {
+  int32_t n_layers;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t n_q_heads;
+  int32_t max_seqs;
+  int32_t tail_min;
+  int32_t tail_max;
+  int32_t margin;
+  int64_t max_ctx;          /* tokens per sequence */
+  int32_t k_bits;
+  int32_t v_bits;
+  int32_t sinkhorn_passes;  /* alternating row/column sweeps, rows first */
+  int32_t flags;            /* KVQ_FLAG_* */
+  /* Sign flips of the 128-point randomized Walsh-Hadamard transform used for
+   * 128-wide heads: entries 0..127 are applied before the transform, 128..255
+   * after; bit b of word w set means entry 64*w+b is -1.  Ignored otherwise. */
+  uint64_t rot_signs[4];
+} kvq_config;
+
+typedef struct kvq_cache kvq_cache;
+
+/* Device bytes the arena of a cache with this configuration needs.
+ * device_bytes: host out.  Errors: KVQ_ERR_INVALID. */
+kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* device_bytes);
+
+/* Create a cache over a caller-owned device arena of at least
+ * kvq_cache_bytes() bytes (256-byte aligned).  The arena is not cleared:
+ * only regions written by kvq_append / kvq_seal / kvq_import are ever read.
+ * With KVQ_FLAG_PLAN_ONLY, arena may be NULL and the cache keeps only the
+ * host metadata (appends and seals update counts; no kernel runs, decode and
+ * export return KVQ_ERR_UNSUPPORTED).  out: host out, owned by the caller
+ * until kvq_cache_destroy.  Errors: KVQ_ERR_INVALID, KVQ_ERR_CAPACITY. */
+kvq_status kvq_cache_create(const kvq_config* cfg, void* device_arena, size_t arena_bytes, kvq_cache** out);
+
+/* Free the host metadata.  Does not free the arena or wait for the device. */
+kvq_status kvq_cache_destroy(kvq_cache* cache);
+
+/* Append n_tok tokens to each listed sequence of one layer (SJ-KVaRN 2.1,
+ * items 1-2).  Position p < 128 is copied to the fp16 sink unchanged; every
+ * later position is rotated (section 2.2; 128-wide heads: KV cache math) and
+ * written to the ring slot (p - 128) mod capacity as tq6_0 blocks (98 bytes
+ * per 128 values: an fp16 scale d = fp16(amax/31) and 128 six-bit codes
+ * q + 32, q = clamp(rne(x / d), -31, 31)).
+ * seq_ids: host [n_seqs], distinct, in [0, max_seqs).
+ * k, v: device fp16 [n_seqs][n_tok][n_kv_heads][head_dim], contiguous.
+ * Never seals: if the ring cannot take the tokens it returns
+ * KVQ_ERR_RING_FULL (call kvq_seal first).  Errors: KVQ_ERR_INVALID,
+ * KVQ_ERR_CAPACITY (beyond max_ctx), KVQ_ERR_RING_FULL, KVQ_ERR_DEVICE. */
+kvq_status kvq_append(kvq_cache* cache, int32_t layer, const int32_t* seq_ids, int32_t n_seqs,
+                      const void* k, const void* v, int32_t n_tok, void* stream);
+
+/* Seal eligible groups (SJ-KVaRN 2.1 item 4 and 4.3) of one layer, or of
+ * every layer when layer == -1, for every sequence.  For each sequence and
+ * layer with ring length n: with KVQ_SEAL_IF_FULL nothing happens unless
+ * n >= tail_max; then (both modes) the oldest floor((n - tail_min)/128)
+ * groups are sealed: each 128-token x 256-channel tile (128-channel for
+ * 128-wide heads) of K and of V is read back from the ring, balanced by
+ * sinkhorn_passes alternating row/column log-domain passes (section 2.2),
+ * divided by its fp16 column scales C, and each row rounded to k_bits / v_bits
+ * with its own fp16 scale S and zero point Z.
+ * groups_sealed: host out (may be NULL), number of 128-token groups sealed
+ * summed over sequences and layers.  Errors: KVQ_ERR_INVALID, KVQ_ERR_DEVICE. */
+kvq_status kvq_seal(kvq_cache* cache, int32_t layer, int32_t mode, void* stream, int32_t* groups_sealed);
+
+/* Device workspace kvq_attn_decode needs for a call on n_seqs sequences
+ * whose contexts are at most max_ctx.  bytes: host out. */
+kvq_status kvq_workspace_bytes(const kvq_cache* cache, int32_t n_seqs, size_t* bytes);
+
+/* Decode attention of one query per sequence over every cached token of one
+ * layer: the sink, the ring (exact tail) and the sealed body, merged under one
+ * softmax (SJ-KVaRN 2.1; KV Cache Precision Tail, section 2).  The query is
+ * rotated once and the ring and body are read in the rotated domain; the
+ * output is rotated back once (KV cache math, fused rotated-domain kernel).
+ * Query head h uses KV head h / (n_q_heads / n_kv_heads).
+ * q: device fp16 [n_seqs][n_q_heads][head_dim].  out: device
+ * [n_seqs][n_q_heads][head_dim], fp32 or fp16 per out_dtype.  scale
+ * multiplies q.k.  workspace: device, ws_bytes >= kvq_workspace_bytes(n_seqs).
+ * Every listed sequence must hold at least one token.  Errors:
+ * KVQ_ERR_INVALID, KVQ_ERR_CAPACITY (workspace too small), KVQ_ERR_DEVICE. */
+kvq_status kvq_attn_decode(kvq_cache* cache, int32_t layer, const int32_t* seq_ids, int32_t n_seqs,
+                           const void* q, void* out, int32_t out_dtype, float scale,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/* Select the kernel that scans sealed records: KVQ_PATH_MFMA (matrix cores,
+ * the default) or KVQ_PATH_VALU (vector ALU reference, kept for A/B checks).
+ * Errors: KVQ_ERR_INVALID. */
+kvq_status kvq_set_decode_path(kvq_cache* cache, int32_t path);
+
+/* Host-side counts of one (sequence, layer): tokens cached, sealed records,
+ * ring length.  Any out pointer may be NULL. */
+kvq_status kvq_seq_info(const kvq_cache* cache, int32_t seq, int32_t layer, int64_t* n_tok,
+                        int64_t* n_records, int32_t* ring_len);
+
+/* Drop every token of one sequence (all layers); its slots are reused. */
+kvq_status kvq_seq_reset(kvq_cache* cache, int32_t seq);
+
+/* Roll one sequence back to n_tok tokens on one layer (or all when layer ==
+ * -1).  Only unsealed tokens can be removed: a target below the sealed
+ * boundary 128 + 128 * n_records (when n_records > 0) returns KVQ_ERR_SEALED
+ * (SJ-KVaRN section 10: removing tokens older than the seal boundary requires
+ * reprocessing).  Growing is not allowed (KVQ_ERR_INVALID). */
+kvq_status kvq_seq_truncate(kvq_cache* cache, int32_t seq, int32_t layer, int64_t n_tok);
+
+/* Copy canonical bytes of one cache unit to the host, synchronising `stream`:
+ *   KVQ_REGION_SINK, index = token (< 128): [K fp16 x head_dim][V fp16 x head_dim];
+ *   KVQ_REGION_RING, index = ring slot: for K then V, head_dim/128 tq6_0
+ *     blocks of 98 bytes, each [fp16 d][96-byte LSB-first 6-bit stream];
+ *   KVQ_REGION_BODY, index = record: the record bytes, per 256-channel
+ *     sub-tile (128 for 128-wide heads) [K codes 128 tokens x sub, row-major,
+ *     two 4-bit codes per byte with the even channel low, or one 8-bit code]
+ *     [V codes sub channels x 128 tokens, channel-major, even token low]
+ *     [K: C[sub] S[128] Z[128] fp16][V: the same].
+ * bytes must equal the unit's size (kvq_unit_bytes).  Errors:
+ * KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED (plan-only cache), KVQ_ERR_DEVICE. */
+kvq_status kvq_export(const kvq_cache* cache, int32_t seq, int32_t layer, int32_t kv_head, int32_t region,
+                      int64_t index, void* host_dst, size_t bytes, void* stream);
+
+/* The inverse of kvq_export: write canonical bytes into one unit (a hook for
+ * tests that place reference-built records; counts are not changed). */
+kvq_status kvq_import(kvq_cache* cache, int32_t seq, int32_t layer, int32_t kv_head, int32_t region,
+                      int64_t index, const void* host_src, size_t bytes, void* stream);
+
+/* Size in bytes of one exported unit of a region.  bytes: host out. */
+kvq_status kvq_unit_bytes(const kvq_cache* cache, int32_t region, size_t* bytes);
+
+const char* kvq_status_string(kvq_status status);
+const char* kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

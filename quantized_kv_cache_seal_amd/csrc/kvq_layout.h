@@ -1,0 +1,106 @@
+// Device-memory layout of one cache arena and the by-value kernel arguments.
+//
+// Arena (every region 256-byte aligned), S = max_seqs, L = layers, H = KV heads,
+// D = head_dim, NB = D / 128 tq6_0 blocks per vector, CAP = ring slots:
+//   sink        fp16  [S][L][H][2 (K,V)][128][D]            original domain
+//   ring codes  u8    [S][L][H][2][CAP][NB][96]             6-bit LSB-first codes
+//   ring scales fp16  [S][L][H][2][CAP][NB]                 d of each block
+//   body        u8    [S][L][H][MAX_REC][REC_BYTES]         sealed records
+// A record is NSUB sub-records of SUB channels (SUB = 256, or 128 for 128-wide
+// heads), each [K codes 128 x SUB row-major][V codes SUB x 128 channel-major]
+// [K: C[SUB] S[128] Z[128] fp16][V: C S Z], codes packed two per byte (even
+// element in the low nibble) at 4 bits or one per byte at 8 bits.
+#pragma once
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kSink = 128;        // sink tokens (SJ-KVaRN 2.1, item 1)
+constexpr int kGroup = 128;       // tokens per sealed record (SJ-KVaRN 2)
+constexpr int kQBlock = 128;      // values per tq6_0 block
+constexpr int kQBytes = 96;       // code bytes per tq6_0 block (128 x 6 bits)
+constexpr int kMaxLaunchSeqs = 32;
+constexpr int kMaxSealTasks = 64;
+constexpr int kMaxGroup = 16;     // query heads per KV head
+constexpr int kMaxChunks = 4096;  // split-K partials per (sequence, query head)
+
+struct Layout {
+  int32_t S, L, H, D, NB, cap, nsub, sub, kbits, vbits, max_rec, pad0;
+  int64_t sub_bytes, rec_bytes, kcode_bytes, vcode_bytes;
+  int64_t off_sink, off_rcode, off_rscale, off_body, total;
+};
+
+// (seq, layer, head) flattened
+__host__ __device__ inline int64_t slh(const Layout& y, int s, int l, int h) {
+  return ((int64_t)s * y.L + l) * y.H + h;
+}
+// fp16 element index of sink[s][l][h][kv][t][0]
+__host__ __device__ inline int64_t sink_elem(const Layout& y, int s, int l, int h, int kv, int t) {
+  return ((slh(y, s, l, h) * 2 + kv) * kSink + t) * (int64_t)y.D;
+}
+// byte offset (from arena) of ring codes[s][l][h][kv][slot][0]
+__host__ __device__ inline int64_t rcode_off(const Layout& y, int s, int l, int h, int kv, int slot) {
+  return y.off_rcode + ((slh(y, s, l, h) * 2 + kv) * y.cap + slot) * (int64_t)(y.NB * kQBytes);
+}
+// byte offset of ring scales[s][l][h][kv][slot][0]
+__host__ __device__ inline int64_t rscale_off(const Layout& y, int s, int l, int h, int kv, int slot) {
+  return y.off_rscale + ((slh(y, s, l, h) * 2 + kv) * y.cap + slot) * (int64_t)(y.NB * 2);
+}
+// byte offset of body record r of (s, l, h)
+__host__ __device__ inline int64_t rec_off(const Layout& y, int s, int l, int h, int64_t r) {
+  return y.off_body + (slh(y, s, l, h) * y.max_rec + r) * y.rec_bytes;
+}
+
+struct AppendArgs {
+  const uint16_t* k;  // fp16 [n_seqs][n_tok][H][D]
+  const uint16_t* v;
+  uint8_t* arena;
+  Layout y;
+  int32_t layer, n_tok, n_seqs, pad;
+  uint32_t signs[8];  // bit i set: entry i of [s1 (128); s2 (128)] is -1
+  int32_t slot[kMaxLaunchSeqs];
+  int64_t pos0[kMaxLaunchSeqs];
+};
+
+struct SealTask {
+  int32_t slot, layer, rec0, n_groups, first;  // first = index of its first group in the grid
+};
+
+struct SealArgs {
+  uint8_t* arena;
+  Layout y;
+  int32_t passes, n_tasks, total_groups, pad;
+  SealTask task[kMaxSealTasks];
+};
+
+struct DecodeSeq {
+  int32_t slot;      // sequence index in the arena
+  int32_t n_sink;    // tokens in the sink (1..128)
+  int32_t ring_len;  // tokens in the ring
+  int32_t ring0;     // ring slot of the oldest unsealed token
+  int32_t n_rec;     // sealed records
+  int32_t n_ring_chunks, n_body_chunks, n_chunks;
+};
+
+struct DecodeArgs {
+  const uint8_t* arena;
+  Layout y;
+  const uint16_t* q;  // fp16 [n_seqs][Hq][D]
+  float* part;        // [n_seqs][Hq][max_chunks][D + 2]: m, l, acc[D]
+  float scale;
+  int32_t layer, Hq, g, n_seqs, max_chunks, ring_chunk, rec_per_chunk;
+  int32_t chunk_base;  // first chunk index this launch covers (0 for sink/ring launch)
+  int32_t pad;
+  uint32_t signs[8];
+  DecodeSeq seq[kMaxLaunchSeqs];
+};
+
+struct MergeArgs {
+  const float* part;
+  void* out;          // [n_seqs][Hq][D] fp32 or fp16
+  int32_t D, Hq, n_seqs, max_chunks, out_f16, pad;
+  uint32_t signs[8];
+  int32_t n_chunks[kMaxLaunchSeqs];
+};
+
+}  // namespace kvq

@@ -1,0 +1,494 @@
+// Host runtime behind include/kvq.h: configuration checks, arena carving, the
+// per-(sequence, layer) counts, the journaled adaptive seal rule, the split-K
+// work plan, and kernel launches on the caller's stream.  All state needed to
+// size a launch lives on the host, so no call waits for the device except
+// kvq_export / kvq_import.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/kvq.h"
+#include "kvq_layout.h"
+
+namespace kvq {
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_seal(const SealArgs& a, hipStream_t stream);
+hipError_t launch_decode_valu(const DecodeArgs& a, int grid_x, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int grid_x, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+}  // namespace kvq
+
+using namespace kvq;
+
+struct kvq_cache {
+  kvq_config cfg;
+  Layout y;
+  uint8_t* arena;
+  bool plan_only;
+  int32_t path;
+  uint32_t signs[8];
+  std::vector<int64_t> n_tok;  // [S * L]
+  std::vector<int64_t> n_rec;  // [S * L]
+  int64_t& tok(int s, int l) { return n_tok[(size_t)s * y.L + l]; }
+  int64_t& rec(int s, int l) { return n_rec[(size_t)s * y.L + l]; }
+  int64_t tok(int s, int l) const { return n_tok[(size_t)s * y.L + l]; }
+  int64_t rec(int s, int l) const { return n_rec[(size_t)s * y.L + l]; }
+  int64_t ring_len(int s, int l) const { return std::max<int64_t>(0, tok(s, l) - kSink - kGroup * rec(s, l)); }
+};
+
+static thread_local std::string g_err;
+
+static kvq_status fail(kvq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+static kvq_status hip_fail(hipError_t e, const char* what) {
+  return fail(KVQ_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+static kvq_status check_config(const kvq_config* c) {
+  if (!c) return fail(KVQ_ERR_INVALID, "config is NULL");
+  if (c->n_layers < 1 || c->n_kv_heads < 1 || c->max_seqs < 1)
+    return fail(KVQ_ERR_INVALID, "n_layers, n_kv_heads and max_seqs must be >= 1");
+  if (c->head_dim != 128 && c->head_dim != 256 && c->head_dim != 512)
+    return fail(KVQ_ERR_INVALID, "head_dim must be 128, 256 or 512 (got %d)", c->head_dim);
+  if (c->n_q_heads < c->n_kv_heads || c->n_q_heads % c->n_kv_heads != 0 ||
+      c->n_q_heads / c->n_kv_heads > kMaxGroup)
+    return fail(KVQ_ERR_INVALID, "n_q_heads must be a multiple of n_kv_heads, at most %d per KV head", kMaxGroup);
+  if (c->tail_min < kGroup || c->tail_min % kGroup != 0 || c->tail_max < c->tail_min)
+    return fail(KVQ_ERR_INVALID, "need tail_min a positive multiple of 128 and tail_min <= tail_max");
+  if (c->margin < 0) return fail(KVQ_ERR_INVALID, "margin must be >= 0");
+  if (c->max_ctx < 1 || c->max_ctx > ((int64_t)1 << 31) - kGroup)
+    return fail(KVQ_ERR_INVALID, "max_ctx out of range");
+  if ((c->k_bits != 4 && c->k_bits != 8) || c->v_bits != 4)
+    return fail(KVQ_ERR_INVALID, "supported bodies: k_bits 4 or 8, v_bits 4");
+  if (c->sinkhorn_passes < 0 || c->sinkhorn_passes > 64)
+    return fail(KVQ_ERR_INVALID, "sinkhorn_passes must be in [0, 64]");
+  if ((int64_t)c->tail_max + c->margin > (1 << 28)) return fail(KVQ_ERR_INVALID, "ring too large");
+  if (c->flags & ~KVQ_FLAG_PLAN_ONLY) return fail(KVQ_ERR_INVALID, "unknown flags");
+  return KVQ_OK;
+}
+
+static Layout make_layout(const kvq_config& c) {
+  Layout y{};
+  y.S = c.max_seqs;
+  y.L = c.n_layers;
+  y.H = c.n_kv_heads;
+  y.D = c.head_dim;
+  y.NB = c.head_dim / kQBlock;
+  y.cap = (int32_t)round_up((int64_t)c.tail_max + c.margin, kGroup);
+  y.sub = c.head_dim == 128 ? 128 : 256;
+  y.nsub = c.head_dim / y.sub;
+  y.kbits = c.k_bits;
+  y.vbits = c.v_bits;
+  y.max_rec = (int32_t)std::max<int64_t>(0, (c.max_ctx - kSink) / kGroup);
+  y.kcode_bytes = (int64_t)kGroup * y.sub * y.kbits / 8;
+  y.vcode_bytes = (int64_t)y.sub * kGroup * y.vbits / 8;
+  y.sub_bytes = y.kcode_bytes + y.vcode_bytes + 4 * (y.sub + 2 * kGroup);
+  y.rec_bytes = y.nsub * y.sub_bytes;
+  const int64_t slh = (int64_t)y.S * y.L * y.H;
+  int64_t off = 0;
+  y.off_sink = off;
+  off = round_up(off + slh * 2 * kSink * y.D * 2, 256);
+  y.off_rcode = off;
+  off = round_up(off + slh * 2 * y.cap * (int64_t)y.NB * kQBytes, 256);
+  y.off_rscale = off;
+  off = round_up(off + slh * 2 * y.cap * (int64_t)y.NB * 2, 256);
+  y.off_body = off;
+  off = round_up(off + slh * y.max_rec * y.rec_bytes, 256);
+  y.total = off;
+  return y;
+}
+
+// Split-K plan: tokens per ring chunk and records per body chunk, sized so a
+// sequence never has more than kMaxChunks partials.
+static int ring_chunk_tokens(const Layout& y) {
+  return kGroup * (int)std::max<int64_t>(1, (y.cap / kGroup + 1023) / 1024);
+}
+static int valu_rec_per_chunk(const Layout& y) { return std::max(1, (y.max_rec + 2999) / 3000); }
+
+static DecodeSeq plan_seq(const kvq_cache* c, int s, int layer, int rc, int rpc) {
+  DecodeSeq d{};
+  d.slot = s;
+  const int64_t nt = c->tok(s, layer);
+  d.n_sink = (int32_t)std::min<int64_t>(nt, kSink);
+  d.n_rec = (int32_t)c->rec(s, layer);
+  d.ring_len = (int32_t)c->ring_len(s, layer);
+  d.ring0 = (int32_t)(((int64_t)kGroup * d.n_rec) % c->y.cap);
+  d.n_ring_chunks = (d.ring_len + rc - 1) / rc;
+  d.n_body_chunks = (d.n_rec + rpc - 1) / rpc;
+  d.n_chunks = 1 + d.n_ring_chunks + d.n_body_chunks;
+  return d;
+}
+
+static void fill_signs(const kvq_config& c, uint32_t* out) {
+  for (int w = 0; w < 4; ++w) {
+    out[2 * w] = (uint32_t)(c.rot_signs[w] & 0xFFFFFFFFu);
+    out[2 * w + 1] = (uint32_t)(c.rot_signs[w] >> 32);
+  }
+}
+
+extern "C" {
+
+const char* kvq_status_string(kvq_status st) {
+  switch (st) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID: return "invalid argument";
+    case KVQ_ERR_CAPACITY: return "capacity exceeded";
+    case KVQ_ERR_RING_FULL: return "staging ring full";
+    case KVQ_ERR_SEALED: return "sealed records cannot be rewritten";
+    case KVQ_ERR_DEVICE: return "device error";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported";
+  }
+  return "unknown status";
+}
+
+const char* kvq_last_error(void) { return g_err.c_str(); }
+
+kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* device_bytes) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!device_bytes) return fail(KVQ_ERR_INVALID, "device_bytes is NULL");
+  *device_bytes = (cfg->flags & KVQ_FLAG_PLAN_ONLY) ? 0 : (size_t)make_layout(*cfg).total;
+  return KVQ_OK;
+}
+
+kvq_status kvq_cache_create(const kvq_config* cfg, void* device_arena, size_t arena_bytes, kvq_cache** out) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!out) return fail(KVQ_ERR_INVALID, "out is NULL");
+  const bool plan_only = (cfg->flags & KVQ_FLAG_PLAN_ONLY) != 0;
+  Layout y = make_layout(*cfg);
+  if (!plan_only) {
+    if (!device_arena) return fail(KVQ_ERR_INVALID, "device_arena is NULL");
+    if ((uintptr_t)device_arena % 256 != 0) return fail(KVQ_ERR_INVALID, "device_arena must be 256-byte aligned");
+    if (arena_bytes < (size_t)y.total)
+      return fail(KVQ_ERR_CAPACITY, "arena has %zu bytes, needs %lld", arena_bytes, (long long)y.total);
+  }
+  kvq_cache* c = new (std::nothrow) kvq_cache();
+  if (!c) return fail(KVQ_ERR_CAPACITY, "out of host memory");
+  c->cfg = *cfg;
+  c->y = y;
+  c->arena = plan_only ? nullptr : (uint8_t*)device_arena;
+  c->plan_only = plan_only;
+  c->path = KVQ_PATH_AUTO;
+  fill_signs(*cfg, c->signs);
+  c->n_tok.assign((size_t)y.S * y.L, 0);
+  c->n_rec.assign((size_t)y.S * y.L, 0);
+  *out = c;
+  return KVQ_OK;
+}
+
+kvq_status kvq_cache_destroy(kvq_cache* c) {
+  delete c;
+  return KVQ_OK;
+}
+
+static kvq_status check_seqs(const kvq_cache* c, const int32_t* ids, int32_t n) {
+  if (n < 0) return fail(KVQ_ERR_INVALID, "n_seqs < 0");
+  if (n > 0 && !ids) return fail(KVQ_ERR_INVALID, "seq_ids is NULL");
+  std::vector<char> seen((size_t)c->y.S, 0);
+  for (int i = 0; i < n; ++i) {
+    if (ids[i] < 0 || ids[i] >= c->y.S) return fail(KVQ_ERR_INVALID, "seq id %d out of range", ids[i]);
+    if (seen[ids[i]]) return fail(KVQ_ERR_INVALID, "seq id %d listed twice", ids[i]);
+    seen[ids[i]] = 1;
+  }
+  return KVQ_OK;
+}
+
+kvq_status kvq_append(kvq_cache* c, int32_t layer, const int32_t* seq_ids, int32_t n_seqs, const void* k,
+                      const void* v, int32_t n_tok, void* stream) {
+  if (!c) return fail(KVQ_ERR_INVALID, "cache is NULL");
+  if (layer < 0 || layer >= c->y.L) return fail(KVQ_ERR_INVALID, "layer %d out of range", layer);
+  if (n_tok < 0) return fail(KVQ_ERR_INVALID, "n_tok < 0");
+  kvq_status st = check_seqs(c, seq_ids, n_seqs);
+  if (st != KVQ_OK) return st;
+  if (n_seqs == 0 || n_tok == 0) return KVQ_OK;
+  if (!c->plan_only && (!k || !v)) return fail(KVQ_ERR_INVALID, "k or v is NULL");
+  for (int i = 0; i < n_seqs; ++i) {
+    const int s = seq_ids[i];
+    if (c->tok(s, layer) + n_tok > c->cfg.max_ctx)
+      return fail(KVQ_ERR_CAPACITY, "sequence %d would exceed max_ctx %lld", s, (long long)c->cfg.max_ctx);
+    const int64_t ring_after = std::max<int64_t>(0, c->tok(s, layer) + n_tok - kSink - kGroup * c->rec(s, layer));
+    if (ring_after > c->y.cap)
+      return fail(KVQ_ERR_RING_FULL, "sequence %d: ring would hold %lld of %d slots; seal first", s,
+                  (long long)ring_after, c->y.cap);
+  }
+  if (!c->plan_only) {
+    const int64_t per_seq = (int64_t)n_tok * c->y.H * c->y.D;
+    for (int b0 = 0; b0 < n_seqs; b0 += kMaxLaunchSeqs) {
+      AppendArgs a{};
+      a.k = (const uint16_t*)k + b0 * per_seq;
+      a.v = (const uint16_t*)v + b0 * per_seq;
+      a.arena = c->arena;
+      a.y = c->y;
+      a.layer = layer;
+      a.n_tok = n_tok;
+      a.n_seqs = std::min(kMaxLaunchSeqs, n_seqs - b0);
+      std::memcpy(a.signs, c->signs, sizeof a.signs);
+      for (int b = 0; b < a.n_seqs; ++b) {
+        a.slot[b] = seq_ids[b0 + b];
+        a.pos0[b] = c->tok(seq_ids[b0 + b], layer);
+      }
+      hipError_t e = launch_append(a, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e, "append launch");
+    }
+  }
+  for (int i = 0; i < n_seqs; ++i) c->tok(seq_ids[i], layer) += n_tok;
+  return KVQ_OK;
+}
+
+static int64_t groups_to_seal(int64_t ring_len, const kvq_config& cfg, int mode) {
+  if (mode == KVQ_SEAL_IF_FULL && ring_len < cfg.tail_max) return 0;
+  return std::max<int64_t>(0, (ring_len - cfg.tail_min) / kGroup);
+}
+
+kvq_status kvq_seal(kvq_cache* c, int32_t layer, int32_t mode, void* stream, int32_t* groups_sealed) {
+  if (!c) return fail(KVQ_ERR_INVALID, "cache is NULL");
+  if (layer < -1 || layer >= c->y.L) return fail(KVQ_ERR_INVALID, "layer %d out of range", layer);
+  if (mode != KVQ_SEAL_IF_FULL && mode != KVQ_SEAL_TO_MIN) return fail(KVQ_ERR_INVALID, "bad seal mode %d", mode);
+  int64_t total = 0;
+  const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c->y.L : layer + 1;
+  for (int l = l0; l < l1; ++l) {
+    std::vector<SealTask> tasks;
+    for (int s = 0; s < c->y.S; ++s) {
+      const int64_t g = groups_to_seal(c->ring_len(s, l), c->cfg, mode);
+      if (g <= 0) continue;
+      SealTask t{};
+      t.slot = s;
+      t.layer = l;
+      t.rec0 = (int32_t)c->rec(s, l);
+      t.n_groups = (int32_t)g;
+      tasks.push_back(t);
+    }
+    for (size_t t0 = 0; t0 < tasks.size(); t0 += kMaxSealTasks) {
+      SealArgs a{};
+      a.arena = c->arena;
+      a.y = c->y;
+      a.passes = c->cfg.sinkhorn_passes;
+      a.n_tasks = (int32_t)std::min<size_t>(kMaxSealTasks, tasks.size() - t0);
+      int32_t first = 0;
+      for (int i = 0; i < a.n_tasks; ++i) {
+        a.task[i] = tasks[t0 + i];
+        a.task[i].first = first;
+        first += a.task[i].n_groups;
+      }
+      a.total_groups = first;
+      if (!c->plan_only) {
+        hipError_t e = launch_seal(a, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "seal launch");
+      }
+      for (int i = 0; i < a.n_tasks; ++i) {
+        c->rec(a.task[i].slot, l) += a.task[i].n_groups;
+        total += a.task[i].n_groups;
+      }
+    }
+  }
+  if (groups_sealed) *groups_sealed = (int32_t)total;
+  return KVQ_OK;
+}
+
+static int max_chunks_bound(const kvq_cache* c) {
+  const int rc = ring_chunk_tokens(c->y);
+  const int rpc = valu_rec_per_chunk(c->y);
+  return 1 + (c->y.cap + rc - 1) / rc + (c->y.max_rec + rpc - 1) / rpc;
+}
+
+kvq_status kvq_workspace_bytes(const kvq_cache* c, int32_t n_seqs, size_t* bytes) {
+  if (!c || !bytes || n_seqs < 0) return fail(KVQ_ERR_INVALID, "bad arguments");
+  *bytes = (size_t)n_seqs * c->cfg.n_q_heads * max_chunks_bound(c) * (c->y.D + 2) * sizeof(float);
+  return KVQ_OK;
+}
+
+kvq_status kvq_set_decode_path(kvq_cache* c, int32_t path) {
+  if (!c || path < KVQ_PATH_AUTO || path > KVQ_PATH_MFMA) return fail(KVQ_ERR_INVALID, "bad decode path");
+  c->path = path;
+  return KVQ_OK;
+}
+
+kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, int32_t n_seqs, const void* q,
+                           void* out, int32_t out_dtype, float scale, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  if (!c) return fail(KVQ_ERR_INVALID, "cache is NULL");
+  if (c->plan_only) return fail(KVQ_ERR_UNSUPPORTED, "decode on a plan-only cache");
+  if (layer < 0 || layer >= c->y.L) return fail(KVQ_ERR_INVALID, "layer %d out of range", layer);
+  if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_F16) return fail(KVQ_ERR_INVALID, "bad out_dtype");
+  kvq_status st = check_seqs(c, seq_ids, n_seqs);
+  if (st != KVQ_OK) return st;
+  if (n_seqs == 0) return KVQ_OK;
+  if (!q || !out || !workspace) return fail(KVQ_ERR_INVALID, "q, out and workspace must be non-NULL");
+  const int rc = ring_chunk_tokens(c->y);
+  const int rpc = valu_rec_per_chunk(c->y);
+  std::vector<DecodeSeq> plan(n_seqs);
+  int max_chunks = 1;
+  for (int i = 0; i < n_seqs; ++i) {
+    if (c->tok(seq_ids[i], layer) < 1) return fail(KVQ_ERR_INVALID, "sequence %d holds no tokens", seq_ids[i]);
+    plan[i] = plan_seq(c, seq_ids[i], layer, rc, rpc);
+    max_chunks = std::max(max_chunks, plan[i].n_chunks);
+  }
+  if (max_chunks > kMaxChunks) return fail(KVQ_ERR_CAPACITY, "too many split-K chunks");
+  const int Hq = c->cfg.n_q_heads, D = c->y.D;
+  const size_t need = (size_t)n_seqs * Hq * max_chunks * (D + 2) * sizeof(float);
+  if (ws_bytes < need) return fail(KVQ_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  const size_t out_elem = out_dtype == KVQ_OUT_F16 ? 2 : 4;
+  for (int b0 = 0; b0 < n_seqs; b0 += kMaxLaunchSeqs) {
+    DecodeArgs a{};
+    a.arena = c->arena;
+    a.y = c->y;
+    a.n_seqs = std::min(kMaxLaunchSeqs, n_seqs - b0);
+    a.q = (const uint16_t*)q + (int64_t)b0 * Hq * D;
+    a.part = (float*)workspace + (int64_t)b0 * Hq * max_chunks * (D + 2);
+    a.scale = scale;
+    a.layer = layer;
+    a.Hq = Hq;
+    a.g = Hq / c->y.H;
+    a.max_chunks = max_chunks;
+    a.ring_chunk = rc;
+    a.rec_per_chunk = rpc;
+    a.chunk_base = 0;
+    std::memcpy(a.signs, c->signs, sizeof a.signs);
+    int grid_x = 1;
+    for (int b = 0; b < a.n_seqs; ++b) {
+      a.seq[b] = plan[b0 + b];
+      grid_x = std::max(grid_x, a.seq[b].n_chunks);
+    }
+    hipError_t e = launch_decode_valu(a, grid_x, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    MergeArgs m{};
+    m.part = a.part;
+    m.out = (uint8_t*)out + (size_t)b0 * Hq * D * out_elem;
+    m.D = D;
+    m.Hq = Hq;
+    m.n_seqs = a.n_seqs;
+    m.max_chunks = max_chunks;
+    m.out_f16 = out_dtype == KVQ_OUT_F16;
+    std::memcpy(m.signs, c->signs, sizeof m.signs);
+    for (int b = 0; b < a.n_seqs; ++b) m.n_chunks[b] = a.seq[b].n_chunks;
+    e = launch_merge(m, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  return KVQ_OK;
+}
+
+kvq_status kvq_seq_info(const kvq_cache* c, int32_t seq, int32_t layer, int64_t* n_tok, int64_t* n_records,
+                        int32_t* ring_len) {
+  if (!c) return fail(KVQ_ERR_INVALID, "cache is NULL");
+  if (seq < 0 || seq >= c->y.S || layer < 0 || layer >= c->y.L) return fail(KVQ_ERR_INVALID, "seq/layer out of range");
+  if (n_tok) *n_tok = c->tok(seq, layer);
+  if (n_records) *n_records = c->rec(seq, layer);
+  if (ring_len) *ring_len = (int32_t)c->ring_len(seq, layer);
+  return KVQ_OK;
+}
+
+kvq_status kvq_seq_reset(kvq_cache* c, int32_t seq) {
+  if (!c) return fail(KVQ_ERR_INVALID, "cache is NULL");
+  if (seq < 0 || seq >= c->y.S) return fail(KVQ_ERR_INVALID, "seq out of range");
+  for (int l = 0; l < c->y.L; ++l) {
+    c->tok(seq, l) = 0;
+    c->rec(seq, l) = 0;
+  }
+  return KVQ_OK;
+}
+
+kvq_status kvq_seq_truncate(kvq_cache* c, int32_t seq, int32_t layer, int64_t n_tok) {
+  if (!c) return fail(KVQ_ERR_INVALID, "cache is NULL");
+  if (seq < 0 || seq >= c->y.S || layer < -1 || layer >= c->y.L) return fail(KVQ_ERR_INVALID, "seq/layer out of range");
+  if (n_tok < 0) return fail(KVQ_ERR_INVALID, "n_tok < 0");
+  const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c->y.L : layer + 1;
+  for (int l = l0; l < l1; ++l) {
+    if (n_tok > c->tok(seq, l)) return fail(KVQ_ERR_INVALID, "truncate cannot grow a sequence");
+    if (c->rec(seq, l) > 0 && n_tok < kSink + kGroup * c->rec(seq, l))
+      return fail(KVQ_ERR_SEALED, "target %lld is below the sealed boundary %lld", (long long)n_tok,
+                  (long long)(kSink + kGroup * c->rec(seq, l)));
+  }
+  for (int l = l0; l < l1; ++l) c->tok(seq, l) = n_tok;
+  return KVQ_OK;
+}
+
+kvq_status kvq_unit_bytes(const kvq_cache* c, int32_t region, size_t* bytes) {
+  if (!c || !bytes) return fail(KVQ_ERR_INVALID, "bad arguments");
+  switch (region) {
+    case KVQ_REGION_SINK: *bytes = (size_t)2 * c->y.D * 2; return KVQ_OK;
+    case KVQ_REGION_RING: *bytes = (size_t)2 * c->y.NB * (2 + kQBytes); return KVQ_OK;
+    case KVQ_REGION_BODY: *bytes = (size_t)c->y.rec_bytes; return KVQ_OK;
+  }
+  return fail(KVQ_ERR_INVALID, "bad region %d", region);
+}
+
+static kvq_status check_unit(const kvq_cache* c, int32_t seq, int32_t layer, int32_t h, int32_t region, int64_t index,
+                             const void* host, size_t bytes) {
+  if (!c) return fail(KVQ_ERR_INVALID, "cache is NULL");
+  if (c->plan_only) return fail(KVQ_ERR_UNSUPPORTED, "no device arena");
+  if (seq < 0 || seq >= c->y.S || layer < 0 || layer >= c->y.L || h < 0 || h >= c->y.H)
+    return fail(KVQ_ERR_INVALID, "seq/layer/head out of range");
+  if (!host) return fail(KVQ_ERR_INVALID, "host buffer is NULL");
+  size_t need = 0;
+  kvq_status st = kvq_unit_bytes(c, region, &need);
+  if (st != KVQ_OK) return st;
+  if (bytes != need) return fail(KVQ_ERR_INVALID, "unit has %zu bytes, got %zu", need, bytes);
+  const int64_t lim = region == KVQ_REGION_SINK ? kSink : region == KVQ_REGION_RING ? c->y.cap : c->y.max_rec;
+  if (index < 0 || index >= lim) return fail(KVQ_ERR_INVALID, "index %lld out of range", (long long)index);
+  return KVQ_OK;
+}
+
+static kvq_status copy_unit(const kvq_cache* c, int32_t seq, int32_t layer, int32_t h, int32_t region, int64_t index,
+                            uint8_t* host, bool to_host, hipStream_t stream) {
+  const Layout& y = c->y;
+  struct Piece {
+    int64_t dev_off;
+    size_t host_off, n;
+  };
+  std::vector<Piece> pieces;
+  if (region == KVQ_REGION_SINK) {
+    for (int kv = 0; kv < 2; ++kv)
+      pieces.push_back({y.off_sink + sink_elem(y, seq, layer, h, kv, (int)index) * 2, (size_t)kv * y.D * 2,
+                        (size_t)y.D * 2});
+  } else if (region == KVQ_REGION_RING) {
+    size_t ho = 0;
+    for (int kv = 0; kv < 2; ++kv)
+      for (int bl = 0; bl < y.NB; ++bl) {
+        pieces.push_back({rscale_off(y, seq, layer, h, kv, (int)index) + 2 * bl, ho, 2});
+        pieces.push_back({rcode_off(y, seq, layer, h, kv, (int)index) + (int64_t)kQBytes * bl, ho + 2, kQBytes});
+        ho += 2 + kQBytes;
+      }
+  } else {
+    pieces.push_back({rec_off(y, seq, layer, h, index), 0, (size_t)y.rec_bytes});
+  }
+  for (const Piece& p : pieces) {
+    hipError_t e = to_host ? hipMemcpyAsync(host + p.host_off, c->arena + p.dev_off, p.n, hipMemcpyDeviceToHost, stream)
+                           : hipMemcpyAsync(c->arena + p.dev_off, host + p.host_off, p.n, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "copy");
+  }
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  return KVQ_OK;
+}
+
+kvq_status kvq_export(const kvq_cache* c, int32_t seq, int32_t layer, int32_t h, int32_t region, int64_t index,
+                      void* host_dst, size_t bytes, void* stream) {
+  kvq_status st = check_unit(c, seq, layer, h, region, index, host_dst, bytes);
+  if (st != KVQ_OK) return st;
+  return copy_unit(c, seq, layer, h, region, index, (uint8_t*)host_dst, true, (hipStream_t)stream);
+}
+
+kvq_status kvq_import(kvq_cache* c, int32_t seq, int32_t layer, int32_t h, int32_t region, int64_t index,
+                      const void* host_src, size_t bytes, void* stream) {
+  kvq_status st = check_unit(c, seq, layer, h, region, index, host_src, bytes);
+  if (st != KVQ_OK) return st;
+  return copy_unit(c, seq, layer, h, region, index, (uint8_t*)host_src, false, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+"""The C ABI without a GPU: the library loads, exports every function the header
+declares, validates configurations, and its host bookkeeping (plan-only mode,
+no kernels) follows the oracle's four-region cache schedule exactly."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import cache as ocache
+from oracle import record
+from quantized_kv_cache_seal_amd import configs, inputs, kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kvq.LIB_PATH), reason="libkvq.so not built")
+
+
+def test_every_declared_symbol_is_exported():
+    decl = set(re.findall(r"\b(kvq_\w+)\s*\(", open(HEADER).read()))
+    assert decl == set(kvq.EXPORTS)
+    L = kvq.lib()
+    for name in decl:
+        assert getattr(L, name) is not None
+
+
+def _plan(cfg):
+    return kvq.Cache(cfg, plan_only=True)
+
+
+def test_config_validation():
+    good = kvq.make_config(2, 4, 256, 24, 1, 4096, 256, 512)
+    n = ctypes.c_size_t()
+    assert kvq.lib().kvq_cache_bytes(ctypes.byref(good), ctypes.byref(n)) == kvq.OK
+    for field, val in (("head_dim", 192), ("n_q_heads", 25), ("tail_min", 100), ("tail_max", 128),
+                       ("k_bits", 3), ("v_bits", 8), ("sinkhorn_passes", 65), ("max_ctx", 0), ("n_layers", 0)):
+        bad = kvq.make_config(2, 4, 256, 24, 1, 4096, 256, 512)
+        setattr(bad, field, val)
+        assert kvq.lib().kvq_cache_bytes(ctypes.byref(bad), ctypes.byref(n)) == kvq.ERR_INVALID, field
+    g17 = kvq.make_config(1, 1, 256, 17, 1, 4096, 256, 512)
+    assert kvq.lib().kvq_cache_bytes(ctypes.byref(g17), ctypes.byref(n)) == kvq.ERR_INVALID
+
+
+def test_arena_size_matches_layout():
+    for w in configs.ALL:
+        cfg = kvq.config_for(w)
+        n = ctypes.c_size_t()
+        kvq.check(kvq.lib().kvq_cache_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+        S, L, H, D = w.n_seqs, w.n_layers, w.n_kv_heads, w.head_dim
+        cap = ocache.ring_capacity(w.tail_max, w.margin)
+        rup = lambda x: -(-x // 256) * 256
+        expect = rup(S * L * H * 2 * 128 * D * 2)
+        expect += rup(S * L * H * 2 * cap * (D // 128) * 96)
+        expect += rup(S * L * H * 2 * cap * (D // 128) * 2)
+        expect += rup(S * L * H * ocache.max_records(w.ctx) * record.record_bytes(D, w.k_bits, w.v_bits))
+        assert n.value == expect, w.name
+    # the 110,592-token shape: 831 records in use, 863 allocated, 34,816 B each
+    assert record.record_bytes(256, 4, 4) == 34816
+
+
+def test_unit_bytes():
+    c = _plan(kvq.make_config(1, 2, 512, 4, 1, 4096, 256, 512))
+    assert c.unit_bytes(kvq.REGION_SINK) == 2 * 512 * 2
+    assert c.unit_bytes(kvq.REGION_RING) == 2 * 4 * 98
+    assert c.unit_bytes(kvq.REGION_BODY) == record.record_bytes(512, 4, 4)
+
+
+def test_plan_only_schedule_matches_oracle():
+    rng = np.random.default_rng(3)
+    w = configs.BATCHED.scaled(n_layers=2, ctx=30_000, n_seqs=3, tail_min=1024, tail_max=2048, margin=512)
+    c = _plan(kvq.config_for(w))
+    sim = {(s, l): [0, 0] for s in range(3) for l in range(2)}
+    for step in range(300):
+        seqs = sorted(rng.choice(3, size=rng.integers(1, 4), replace=False).tolist())
+        n_tok = int(rng.choice([1, 1, 1, 7, 128, 300, 512]))
+        layer = int(rng.integers(0, 2))
+        # oracle-side expectation
+        expect = ocache.OK
+        for s in seqs:
+            nt, nr = sim[(s, layer)]
+            ring_after = max(0, nt + n_tok - 128 - 128 * nr)
+            if nt + n_tok > w.ctx:
+                expect = ocache.ERR_CAPACITY
+                break
+            if ring_after > ocache.ring_capacity(w.tail_max, w.margin):
+                expect = ocache.ERR_RING_FULL
+                break
+        st = kvq.lib().kvq_append(c.h, layer, *kvq._ids(seqs), None, None, n_tok, None)
+        assert st == expect
+        if st == kvq.OK:
+            for s in seqs:
+                sim[(s, layer)][0] += n_tok
+        mode = kvq.SEAL_TO_MIN if step % 37 == 0 else kvq.SEAL_IF_FULL
+        sealed = c.seal(-1, mode)
+        tot = 0
+        for key, (nt, nr) in sim.items():
+            ring = max(0, nt - 128 - 128 * nr)
+            g = ocache.groups_to_seal(ring, w.tail_min, w.tail_max, mode)
+            sim[key][1] += g
+            tot += g
+        assert sealed == tot
+        for (s, l), (nt, nr) in sim.items():
+            assert c.info(s, l) == (nt, nr, max(0, nt - 128 - 128 * nr))
+
+
+def test_errors_and_truncate():
+    c = _plan(kvq.make_config(2, 1, 256, 4, 2, 2000, 256, 512, margin=0))
+    assert kvq.lib().kvq_append(c.h, 2, *kvq._ids([0]), None, None, 10, None) == kvq.ERR_INVALID
+    assert kvq.lib().kvq_append(c.h, 0, *kvq._ids([0, 0]), None, None, 10, None) == kvq.ERR_INVALID
+    assert kvq.lib().kvq_append(c.h, 0, *kvq._ids([2]), None, None, 10, None) == kvq.ERR_INVALID
+    assert kvq.lib().kvq_append(c.h, 0, *kvq._ids([0]), None, None, 641, None) == kvq.ERR_RING_FULL
+    assert c.info(0, 0) == (0, 0, 0)
+    kvq.check(kvq.lib().kvq_append(c.h, 0, *kvq._ids([0]), None, None, 640, None))
+    assert c.info(0, 0) == (640, 0, 512)
+    assert c.seal(0) == 2
+    assert c.info(0, 0) == (640, 2, 256)
+    assert c.truncate(0, 0, 383) == kvq.ERR_SEALED
+    assert c.truncate(0, 0, 700) == kvq.ERR_INVALID
+    assert c.truncate(0, 0, 384) == kvq.OK
+    assert c.info(0, 0) == (384, 2, 0)
+    c.reset(0)
+    assert c.info(0, 0) == (0, 0, 0)
+    kvq.check(kvq.lib().kvq_append(c.h, 1, *kvq._ids([1]), None, None, 100, None))
+    assert c.truncate(1, 1, 5) == kvq.OK          # inside the sink, nothing sealed
+    assert c.info(1, 1) == (5, 0, 0)
+    while c.info(1, 1)[0] + 128 <= 2000:
+        kvq.check(kvq.lib().kvq_append(c.h, 1, *kvq._ids([1]), None, None, 128, None))
+        c.seal(1, kvq.SEAL_TO_MIN)
+        assert c.info(1, 1)[2] < 384
+    assert kvq.lib().kvq_append(c.h, 1, *kvq._ids([1]), None, None, 200, None) == kvq.ERR_CAPACITY
+    # decode and export need a device arena
+    assert kvq.lib().kvq_attn_decode(c.h, 0, *kvq._ids([0]), None, None, 0, 1.0, None, 0, None) == kvq.ERR_UNSUPPORTED
+    buf = ctypes.create_string_buffer(1024)
+    assert kvq.lib().kvq_export(c.h, 0, 0, 0, kvq.REGION_SINK, 0, buf, 1024, None) == kvq.ERR_UNSUPPORTED
+    assert b"max_ctx" in kvq.lib().kvq_last_error() or kvq.lib().kvq_last_error()

@@ -1,0 +1,115 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, element by
+element, on seeded inputs shaped like the five workloads at sizes the oracle
+finishes in seconds (several tiles, ragged tails, ring wrap-around)."""
+import sys
+
+import numpy as np
+import pytest
+
+from quantized_kv_cache_seal_amd import configs, inputs, kvq
+
+from harness import ATTN_TOL, Pair
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    # config 1 as specified (1 layer, 1 KV head, 256, GQA 4, 2,048 tokens, 8 passes, tail 256/512)
+    "tiny": (configs.TINY, [2048], 512, None),
+    # config 2 shape, two layers, ragged chunking
+    "qwen27b": (configs.QWEN27B.scaled(n_layers=2, tail_min=256, tail_max=512, ctx=2600), [2600], 300, None),
+    # config 3 shape: 512-wide heads as two 256-point halves, Student-t keys
+    "gemma": (configs.GEMMA31B.scaled(n_layers=1, tail_min=256, tail_max=512, ctx=1500), [1500], 256, None),
+    # config 4 shape: 128-wide heads, randomized WHT, 8-bit keys
+    "qwen14b": (configs.QWEN14B1M.scaled(n_layers=1, n_kv_heads=2, n_q_heads=10, tail_min=256, tail_max=512,
+                                         ctx=1900), [1900], 500, "signs"),
+    # config 5 shape: a ragged batch (sink-only, exact boundaries, ring-only, wrap-around)
+    "batched": (configs.BATCHED.scaled(n_layers=1, tail_min=256, tail_max=512, ctx=3000),
+                [1, 127, 128, 129, 700, 3000], 128, None),
+}
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", params=list(SMALL))
+def pair(request):
+    w, lens, chunk, signs = SMALL[request.param]
+    _say(f"[case {request.param}] build lens={lens} chunk={chunk}")
+    sg = inputs.rotation_signs(w.seed) if signs else None
+    p = Pair(w, lens, sg).build(chunk)
+    p.name = request.param
+    return p
+
+
+def test_counts(pair):
+    pair.check_info()
+
+
+def test_sink_and_ring_bytes_exact(pair):
+    n = pair.check_sink_ring()
+    _say(f"[{pair.name}] sink+ring units bit-exact: {n}")
+    assert n > 0
+
+
+def test_records_conditional_parity(pair):
+    st = pair.check_records()
+    _say(f"[{pair.name}] records: {st}")
+    if pair.name != "batched" or any(pair.ora.info(s, 0)[1] for s in range(pair.n)):
+        assert st["scales"] > 0
+    assert st["boundary"] <= max(1, st["codes"] // 10 ** 5)
+    assert st["uncond_mismatch"] <= 0.01 * max(1, st["codes"])
+
+
+def test_decode_gpu_built_cache(pair):
+    """GPU decode over the GPU-built cache against float64 attention over the
+    oracle-built cache: the two caches differ only where an fp16 column scale
+    rounded the other way, so the bound is looser than on identical records."""
+    for layer in range(pair.w.n_layers):
+        errs, _ = pair.decode_errors(layer, pair.queries(0, layer))
+        _say(f"[{pair.name}] layer={layer} decode (GPU-built cache) err={max(errs):.2e}")
+        assert max(errs) <= 2e-2
+
+
+@pytest.mark.parametrize("path", [kvq.PATH_VALU, kvq.PATH_AUTO])
+def test_decode_on_oracle_records(pair, path):
+    pair.import_oracle_records()
+    for layer in range(pair.w.n_layers):
+        q = pair.queries(0, layer)
+        errs, _ = pair.decode_errors(layer, q, path=path)
+        _say(f"[{pair.name}] path={path} layer={layer} decode err={max(errs):.2e}")
+        assert max(errs) <= ATTN_TOL
+
+
+def test_decode_f16_output_and_scale(pair):
+    pair.import_oracle_records()
+    q = pair.queries(1, 0)
+    errs, out = pair.decode_errors(0, q, scale=0.7, out_f16=True)
+    _say(f"[{pair.name}] f16 out, scale 0.7: err={max(errs):.2e}")
+    assert max(errs) <= ATTN_TOL + 1e-3    # plus fp16 output rounding
+
+
+def test_streaming_one_token_per_step():
+    """Decode-style appends (one token per call) with the seal rule checked after
+    every step, through several ring wrap-arounds."""
+    w = configs.QWEN27B.scaled(n_layers=1, n_kv_heads=1, n_q_heads=6, tail_min=256, tail_max=384, margin=128,
+                               ctx=1200)
+    _say("[streaming] build")
+    p = Pair(w, [1200]).build(1)
+    p.check_info()
+    assert p.check_sink_ring() > 0
+    st = p.check_records()
+    assert st["scales"] == 2 * 7
+    p.import_oracle_records()
+    errs, _ = p.decode_errors(0, p.queries(0, 0))
+    assert max(errs) <= ATTN_TOL
+
+
+def test_decode_deterministic():
+    w = configs.TINY
+    p = Pair(w, [1000]).build(256)
+    q = p.torch.from_numpy(p.queries(0, 0)).cuda()
+    a = p.gpu.attn_decode(0, [0], q).cpu().numpy()
+    b = p.gpu.attn_decode(0, [0], q).cpu().numpy()
+    assert np.array_equal(a, b)

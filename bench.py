@@ -1,0 +1,278 @@
+#!/usr/bin/env python
+"""Decode-step benchmark of the quantized KV-cache hot path on one MI355X.
+
+Workload: the Qwen 27B-class full-attention shape (16 layers, 4 KV heads x 256,
+24 query heads) at a 110,592-token context in the just-sealed state (sink 128,
+831 sealed records per head, 4,096 ring tokens), keys and values drawn by the
+seeded generator.  One step = for every layer: append one token (rotation +
+tq6_0 staging), the seal-if-full check, and decode attention of one query over
+all four regions.  Inputs for every step are resident in HBM before timing.
+
+value = decode-attention effective KV GB/s: the compressed bytes the step must
+read (sink fp16 + ring tq6_0 + sealed records, all layers and heads) divided by
+the measured time per step.  The seal is measured separately as sealed
+tokens/s on a full 4,096-token seal batch (32 groups per layer, 16 layers, 4 KV
+heads, K and V).  The oracle (CPU) is timed on a bounded sample for the
+cpu_baseline entry.  Progress goes to stderr; stdout carries one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn effective KV GB/s (% HBM peak) at 110,592 ctx; seal tokens/s"
+HBM_PEAK_GBS = 8000.0
+FP32_VALU_PEAK_TFLOPS = 157.3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(cache, w, layer, seq=0):
+    """Algorithmic compressed bytes one decode call on `layer` reads: the fp16
+    sink, the tq6_0 ring (98 B per 128 values) and the sealed records."""
+    n_tok, n_rec, ring = cache.info(seq, layer)
+    sink = min(n_tok, 128)
+    per_head = sink * 2 * w.head_dim * 2 + ring * 2 * (w.head_dim // 128) * 98 + n_rec * cache.unit_bytes(2)
+    return per_head * w.n_kv_heads
+
+
+def seal_flops_per_tile(passes, rows=128, cols=256):
+    # per pass: scale, add, square-accumulate over the tile (3 ops, 4 flops with the fma)
+    # plus the final rounding (scale, min/max, subtract, multiply, round: ~6 ops per element)
+    return passes * 4 * rows * cols + 6 * rows * cols
+
+
+def run_decode(args, w, torch, kvq, synthetic, inputs):
+    L, H, D, Hq = w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads
+    W, K = args.warmup, args.steps
+    t0 = time.time()
+    cache = synthetic.build(w, ctx=w.ctx, max_ctx=w.ctx + W + K + 1)
+    log(f"[bench] built {w.name} in {time.time() - t0:.1f}s: layer0 info {cache.info(0, 0)}")
+    path = {"auto": kvq.PATH_AUTO, "valu": kvq.PATH_VALU, "mfma": kvq.PATH_MFMA}[args.path]
+    cache.set_decode_path(path)
+    dev = "cuda"
+    spec = synthetic.spec_for(w)
+    nk = [[spec.tokens(l, "k", w.ctx + s, 1, backend="torch", device=dev)[None].contiguous() for l in range(L)]
+          for s in range(W + K)]
+    nv = [[spec.tokens(l, "v", w.ctx + s, 1, backend="torch", device=dev)[None].contiguous() for l in range(L)]
+          for s in range(W + K)]
+    qs = [[inputs.queries(w.seed, s, l, 1, Hq, D, backend="torch", device=dev).contiguous() for l in range(L)]
+          for s in range(W + K)]
+    out = torch.empty((L, 1, Hq, D), dtype=torch.float32, device=dev)
+    ws = cache.workspace(1)
+    stream = torch.cuda.current_stream()
+
+    def one_step(s, evs=None):
+        nbytes = 0
+        for l in range(L):
+            cache.append(l, [0], nk[s][l], nv[s][l], stream=stream)
+            cache.seal(l, kvq.SEAL_IF_FULL, stream=stream)
+            nbytes += decode_bytes(cache, w, l)
+            if evs is not None:
+                evs[l][0].record(stream)
+            cache.attn_decode(l, [0], qs[s][l], out=out[l], workspace=ws, stream=stream)
+            if evs is not None:
+                evs[l][1].record(stream)
+        return nbytes
+
+    for s in range(W):
+        one_step(s)
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(L)]
+           for _ in range(K)]
+    tot_bytes = 0
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for s in range(K):
+        tot_bytes += one_step(W + s, evs[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(end) / K
+    call_ms = [evs[s][l][0].elapsed_time(evs[s][l][1]) for s in range(K) for l in range(L)]
+    avg_call_ms = sum(call_ms) / len(call_ms)
+    bytes_step = tot_bytes / K
+    gbs = bytes_step / (ms_step * 1e-3) / 1e9
+    per_call_bytes = bytes_step / L
+    achieved = per_call_bytes / (avg_call_ms * 1e-3) / 1e9
+    log(f"[bench] decode: {ms_step * 1e3:.1f} us/step (wall {wall / K * 1e3:.1f} ms), {bytes_step / 1e9:.4f} GB/step, "
+        f"{gbs:.1f} GB/s; decode call avg {avg_call_ms * 1e3:.1f} us -> {achieved:.1f} GB/s")
+    info = cache.info(0, 0)
+    del cache
+    torch.cuda.empty_cache()
+    return {
+        "ms_per_step": ms_step, "gbs": gbs, "bytes_step": bytes_step, "avg_call_ms": avg_call_ms,
+        "achieved": achieved, "per_call_bytes": per_call_bytes, "info_after": info,
+    }
+
+
+def run_seal(args, w, torch, kvq, synthetic):
+    """Seal batch: ring filled to tail_max (8,192) in every layer, then one
+    seal-if-full seals the 32 oldest groups of every layer and head."""
+    L = w.n_layers
+    ctx = 128 + w.tail_max
+    cache = synthetic.build(w, ctx=ctx, max_ctx=ctx, seal_to_min=False, seal_if_full=False, chunk=512)
+    ring = cache.info(0, 0)[2]
+    assert ring == w.tail_max, ring
+    spec = synthetic.spec_for(w)
+    dev = "cuda"
+    # the same tokens again after each timed seal (untimed): reset and refill
+    ks = [[spec.tokens(l, "k", t0, min(512, ctx - t0), backend="torch", device=dev)[None].contiguous()
+           for t0 in range(0, ctx, 512)] for l in range(L)]
+    vs = [[spec.tokens(l, "v", t0, min(512, ctx - t0), backend="torch", device=dev)[None].contiguous()
+           for t0 in range(0, ctx, 512)] for l in range(L)]
+    stream = torch.cuda.current_stream()
+    times, groups = [], 0
+    for rep in range(args.seal_reps + 1):
+        if rep > 0:
+            cache.reset(0)
+            for l in range(L):
+                for k, v in zip(ks[l], vs[l]):
+                    cache.append(l, [0], k, v, stream=stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g = cache.seal(-1, kvq.SEAL_IF_FULL, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if rep > 0:            # the first seal is a warm-up
+            times.append(a.elapsed_time(b))
+            groups = g
+    ms = sorted(times)[len(times) // 2]
+    tokens = groups * 128 // L          # groups summed over layers; every layer seals the same tokens
+    tiles = groups * w.n_kv_heads * 2 * (w.head_dim // 256 if w.head_dim >= 256 else 1)
+    flops = tiles * seal_flops_per_tile(w.passes, 128, min(w.head_dim, 256))
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] seal: {groups} groups ({tokens} tokens x {L} layers), {ms * 1e3:.1f} us -> "
+        f"{tokens / (ms * 1e-3) / 1e6:.2f} M tokens/s, {tflops:.2f} TFLOP/s (VALU)")
+    del cache
+    torch.cuda.empty_cache()
+    return {"ms": ms, "tokens": tokens, "tokens_per_s": tokens / (ms * 1e-3), "tiles": tiles, "tflops": tflops}
+
+
+def run_cpu_baseline(w, budget_s):
+    """The oracle as it stands, single thread, on a bounded sample: one layer and
+    one KV head of the same shape at a shorter context (decode), and a few
+    sealed groups (seal)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import cache as ocache
+    from quantized_kv_cache_seal_amd import inputs, synthetic
+
+    ctx = 16_384
+    with threadpool_limits(limits=1):
+        oc = ocache.OracleCache(1, 1, w.head_dim, w.group, 1, ctx, w.tail_min, w.tail_max, w.margin,
+                                w.k_bits, w.v_bits, w.passes, synthetic.signs(w))
+        spec = inputs.KVSpec(1, 1, w.head_dim, w.seed, w.k_dist, w.outliers, w.outlier_scale)
+        t_seal, groups = 0.0, 0
+        for t0 in range(0, ctx, 512):
+            k = spec.tokens(0, "k", t0, 512)[None]
+            v = spec.tokens(0, "v", t0, 512)[None]
+            oc.append(0, [0], k, v)
+            a = time.perf_counter()
+            groups += oc.seal(0, ocache.SEAL_IF_FULL)
+            t_seal += time.perf_counter() - a
+        a = time.perf_counter()
+        groups += oc.seal(0, ocache.SEAL_TO_MIN)
+        t_seal += time.perf_counter() - a
+        n_tok, n_rec, ring = oc.info(0, 0)
+        q = inputs.queries(w.seed, 0, 0, 1, w.group, w.head_dim)[0]
+        reps, t_dec = 0, 0.0
+        while t_dec < budget_s or reps == 0:
+            a = time.perf_counter()
+            oc.attention(0, 0, q, 1.0)
+            t_dec += time.perf_counter() - a
+            reps += 1
+    nbytes = 128 * 2 * w.head_dim * 2 + ring * 2 * (w.head_dim // 128) * 98 + n_rec * 34816
+    gbs = nbytes * reps / t_dec / 1e9
+    # a sealed token of the full shape is one group-row in every layer and KV head
+    seal_tok_s = groups * 128 / t_seal / (w.n_layers * w.n_kv_heads)
+    log(f"[bench] cpu oracle: decode {gbs:.4f} GB/s over {n_tok} tokens x 1 head ({reps} reps, {t_dec:.1f}s); "
+        f"seal {seal_tok_s:.1f} tokens/s ({groups} groups in {t_seal:.1f}s)")
+    return {
+        "value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"float64 decode attention of one layer, one KV head ({w.group} query heads) at "
+                  f"{n_tok} tokens ({n_rec} records, ring {ring}), {reps} calls; seal: {groups} groups of one "
+                  f"head, scaled to {w.n_layers} layers x {w.n_kv_heads} heads",
+        "seal_tokens_per_s": seal_tok_s,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--seal-reps", type=int, default=5)
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle decode timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-seal", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the cache shards by sequence or KV head without communication).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from quantized_kv_cache_seal_amd import configs, inputs, kvq, synthetic
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    kvq.lib()
+    w = configs.QWEN27B
+    dec = run_decode(args, w, torch, kvq, synthetic, inputs)
+    seal = None if args.no_seal else run_seal(args, w, torch, kvq, synthetic)
+    cpu = None if args.no_cpu_baseline else run_cpu_baseline(w, args.cpu_budget)
+    res = {
+        "metric": METRIC,
+        "value": round(dec["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if args.path != "valu" else "f32",
+        "data": "synthetic",
+        "pct_hbm_peak": round(100 * dec["gbs"] / HBM_PEAK_GBS, 2),
+        "config": {
+            "workload": w.name, "layers": w.n_layers, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+            "q_heads": w.n_q_heads, "ctx": w.ctx, "batch": 1, "body_bits": f"{w.k_bits}/{w.v_bits}",
+            "sinkhorn_passes": w.passes, "tail": [w.tail_min, w.tail_max], "decode_path": args.path,
+            "bytes_per_step": int(dec["bytes_step"]),
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(dec["achieved"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "kvq_attn_decode (split-K decode + merge), one layer",
+            "bytes_per_launch": int(dec["per_call_bytes"]), "avg_launch_us": round(dec["avg_call_ms"] * 1e3, 2),
+        },
+        "cpu_baseline": cpu,
+    }
+    if seal:
+        res["seal"] = {
+            "tokens_per_s": round(seal["tokens_per_s"], 1), "batch_tokens": seal["tokens"],
+            "us_per_batch": round(seal["ms"] * 1e3, 2),
+            "roofline": {"bound": "alu", "achieved": round(seal["tflops"], 3), "peak": FP32_VALU_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(seal["tflops"] / FP32_VALU_PEAK_TFLOPS, 4)},
+        }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

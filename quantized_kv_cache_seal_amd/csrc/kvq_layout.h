@@ -90,7 +90,7 @@ struct DecodeArgs {
   float scale;
   int32_t layer, Hq, g, n_seqs, max_chunks, ring_chunk, rec_per_chunk;
   int32_t chunk_base;  // first chunk index this launch covers (0 for sink/ring launch)
-  int32_t pad;
+  int32_t valu_body;   // 1: the vector-ALU kernel also scans body chunks
   uint32_t signs[8];
   DecodeSeq seq[kMaxLaunchSeqs];
 };

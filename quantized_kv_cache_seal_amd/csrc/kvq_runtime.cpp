@@ -119,6 +119,13 @@ static int ring_chunk_tokens(const Layout& y) {
   return kGroup * (int)std::max<int64_t>(1, (y.cap / kGroup + 1023) / 1024);
 }
 static int valu_rec_per_chunk(const Layout& y) { return std::max(1, (y.max_rec + 2999) / 3000); }
+// Matrix-core path: a multiple of 4 records per workgroup (one per wave), about
+// two workgroups per compute unit over the whole call.
+static int mfma_rec_per_chunk(int64_t total_records) {
+  const int64_t slots = 4 * 512;
+  return 4 * (int)std::max<int64_t>(1, (total_records + slots - 1) / slots);
+}
+static bool mfma_supported(const Layout& y) { return y.D == 256 && y.kbits == 4 && y.vbits == 4; }
 
 static DecodeSeq plan_seq(const kvq_cache* c, int s, int layer, int rc, int rpc) {
   DecodeSeq d{};
@@ -331,11 +338,18 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
   if (n_seqs == 0) return KVQ_OK;
   if (!q || !out || !workspace) return fail(KVQ_ERR_INVALID, "q, out and workspace must be non-NULL");
   const int rc = ring_chunk_tokens(c->y);
-  const int rpc = valu_rec_per_chunk(c->y);
+  const bool use_mfma = c->path != KVQ_PATH_VALU && mfma_supported(c->y);
+  if (c->path == KVQ_PATH_MFMA && !use_mfma)
+    return fail(KVQ_ERR_UNSUPPORTED, "matrix-core body scan needs head_dim 256 with 4-bit K and V");
+  int64_t total_rec = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    if (c->tok(seq_ids[i], layer) < 1) return fail(KVQ_ERR_INVALID, "sequence %d holds no tokens", seq_ids[i]);
+    total_rec += c->rec(seq_ids[i], layer) * c->y.H;
+  }
+  const int rpc = use_mfma ? mfma_rec_per_chunk(total_rec) : valu_rec_per_chunk(c->y);
   std::vector<DecodeSeq> plan(n_seqs);
   int max_chunks = 1;
   for (int i = 0; i < n_seqs; ++i) {
-    if (c->tok(seq_ids[i], layer) < 1) return fail(KVQ_ERR_INVALID, "sequence %d holds no tokens", seq_ids[i]);
     plan[i] = plan_seq(c, seq_ids[i], layer, rc, rpc);
     max_chunks = std::max(max_chunks, plan[i].n_chunks);
   }
@@ -360,13 +374,19 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
     a.rec_per_chunk = rpc;
     a.chunk_base = 0;
     std::memcpy(a.signs, c->signs, sizeof a.signs);
-    int grid_x = 1;
+    a.valu_body = use_mfma ? 0 : 1;
+    int grid_valu = 1, grid_body = 0;
     for (int b = 0; b < a.n_seqs; ++b) {
       a.seq[b] = plan[b0 + b];
-      grid_x = std::max(grid_x, a.seq[b].n_chunks);
+      grid_valu = std::max(grid_valu, use_mfma ? 1 + a.seq[b].n_ring_chunks : a.seq[b].n_chunks);
+      grid_body = std::max(grid_body, a.seq[b].n_body_chunks);
     }
-    hipError_t e = launch_decode_valu(a, grid_x, (hipStream_t)stream);
+    hipError_t e = launch_decode_valu(a, grid_valu, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
+    if (use_mfma && grid_body > 0) {
+      e = launch_decode_mfma(a, grid_body, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e, "body decode launch");
+    }
     MergeArgs m{};
     m.part = a.part;
     m.out = (uint8_t*)out + (size_t)b0 * Hq * D * out_elem;

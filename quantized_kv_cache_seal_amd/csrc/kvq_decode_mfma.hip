@@ -40,14 +40,24 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// (a & m) | b in one v_and_or_b32.  The masks and the exponent pattern are
+// passed in registers: a VOP3 instruction on this target cannot carry two
+// literal constants, and the compiler otherwise splits it into an AND and an OR.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t b) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(m), "v"(b));
+  return d;
+}
+
 __device__ __forceinline__ half8 nib8(uint32_t w) {
   // halves: [n0, n4, 16 n1, 16 n5, n2, n6, 16 n3, 16 n7] + 1024
   const uint32_t w8 = w >> 8;
+  const uint32_t lo_m = 0x000F000Fu, hi_m = 0x00F000F0u, e = 0x64006400u;
   uint4 u;
-  u.x = (w & 0x000F000Fu) | 0x64006400u;
-  u.y = (w & 0x00F000F0u) | 0x64006400u;
-  u.z = (w8 & 0x000F000Fu) | 0x64006400u;
-  u.w = (w8 & 0x00F000F0u) | 0x64006400u;
+  u.x = and_or(w, lo_m, e);
+  u.y = and_or(w, hi_m, e);
+  u.z = and_or(w8, lo_m, e);
+  u.w = and_or(w8, hi_m, e);
   half8 h;
   __builtin_memcpy(&h, &u, 16);
   return h;
@@ -106,37 +116,75 @@ __device__ __forceinline__ void qtilde_pair(uint32_t qh2, uint32_t ql2, uint32_t
   lo2 = pack_h2(r0, r1);
 }
 
-// One wave, one record.  State: m (log2 units), l (partial over this lane's
-// tokens), acc[cb][i] = channel 16 cb + 4 g + i for query column q.
-__device__ __forceinline__ void body_record(const uint8_t* __restrict__ rec, const uint4* qph, const uint4* qpl,
-                                            int lane, float scale_log2, float& m_run, float& l_run, float4v* acc) {
-  const int q16 = lane & 15, g = lane >> 4;
-  const uint8_t* km = rec + 16384 + 16384;   // K meta: C[256] S[128] Z[128]
-  const uint8_t* vm = km + 1024;             // V meta
-  // ---- loads: key codes (16 x 16 B), value codes (16 x 16 B)
-  uint4 kd[8][2];
-#pragma unroll
-  for (int bb = 0; bb < 8; ++bb) {
-    const int t = bb >> 1, hh = bb & 1;
-    const int tok = 32 * (q16 >> 2) + 8 * t + 4 * hh + (q16 & 3);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) kd[bb][s] = *(const uint4*)(rec + tok * 128 + 64 * s + 16 * g);
-  }
-  uint4 vd[16];
-#pragma unroll
-  for (int cb = 0; cb < 16; ++cb) vd[cb] = *(const uint4*)(rec + 16384 + (16 * cb + q16) * 64 + 16 * g);
+// ---------------------------------------------------------------------------
+// Streaming kernel.  Each wave scans whole records with its own online-softmax
+// state and a private LDS staging area: 32 KB for one record's codes (stored
+// in the order the matrix-core operands are read back, so each 16-byte read
+// of a 1 KB slice is contiguous and free of bank conflicts) and two 2 KB areas
+// for scales.  Per record the wave copies the codes into registers, starts the
+// direct global->LDS loads of its next record into the same area, and computes
+// the current one from registers and the scale area while those loads land:
+// the next record's HBM latency hides behind this record's arithmetic, with
+// no workgroup barrier in the loop.  The four waves' states are combined in
+// LDS at the end into one partial per query head.
 
-  // ---- S^T = K . Q~^T over 8 blocks of 16 tokens; q~ built per k-step
+constexpr int kCodeBytes = 32768;     // K and V codes of one 256-channel 4/4 record
+constexpr int kMetaBytes = 2048;      // C S Z of K and V
+constexpr int kWaveLds = kCodeBytes + 2 * kMetaBytes;
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u8*)p);
+}
+
+// one 16-byte direct global->LDS load per lane: LDS[m0 + 16 lane] <- *src.
+// Issued as inline assembly so that the compiler does not add a wait for it in
+// front of every later LDS read; completion is awaited explicitly (wait_vm0).
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+// stage record `rec` into this wave's area: 16 key slices (block bb, half s),
+// 16 value slices (channel block cb), then the 2 KB of scales.
+__device__ __forceinline__ void stage(const uint8_t* __restrict__ rec, uint32_t codes, uint32_t meta, int lane) {
+  const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int sl = 0; sl < 16; ++sl) {
+    const int bb = sl >> 1, s = sl & 1, t = bb >> 1, hh = bb & 1;
+    const int tok = 32 * (m >> 2) + 8 * t + 4 * hh + (m & 3);
+    dma16(rec + tok * 128 + 64 * s + 16 * g, codes + sl * 1024);
+  }
+#pragma unroll
+  for (int cb = 0; cb < 16; ++cb) dma16(rec + 16384 + (16 * cb + m) * 64 + 16 * g, codes + (16 + cb) * 1024);
+  dma16(rec + 32768 + 16 * lane, meta);
+  dma16(rec + 33792 + 16 * lane, meta + 1024);
+}
+
+__device__ __forceinline__ uint32_t pick(const uint4& v, int e) {
+  return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+}
+
+// One record from registers (codes) and LDS (scales).  acc[cb][i] holds
+// channel 16 cb + 4 g + i for query column q = lane & 15; m_run in log2 units;
+// l_part sums this lane's tokens.
+__device__ __forceinline__ void record_step(const uint4 (&kd)[8][2], const uint4 (&vd)[16], const uint8_t* km,
+                                            const uint4* qph, const uint4* qpl, int lane, float scale_log2,
+                                            float& m_run, float& l_part, float4v* acc) {
+  const int g = lane >> 4;
+  const uint8_t* vm = km + 1024;
+  const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
+  // ---- S^T = K . Q~^T, q~ built per k-step as exact hi + lo
   float4v sc[8];
 #pragma unroll
   for (int bb = 0; bb < 8; ++bb) sc[bb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
   float a1 = 0.0f, a16 = 0.0f;
-  const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     const int s = kk >> 2, e = kk & 3;
-    const int base = 128 * s + 32 * g + 8 * e;
-    const uint4 c = *(const uint4*)(km + 2 * base);   // C[base .. base+8)
+    const uint4 c = *(const uint4*)(km + 2 * (128 * s + 32 * g + 8 * e));
     const uint32_t c04 = __builtin_amdgcn_perm(c.z, c.x, 0x05040100u);
     const uint32_t c15 = __builtin_amdgcn_perm(c.z, c.x, 0x07060302u);
     const uint32_t c26 = __builtin_amdgcn_perm(c.w, c.y, 0x05040100u);
@@ -157,37 +205,29 @@ __device__ __forceinline__ void body_record(const uint8_t* __restrict__ rec, con
     half8 bh, bl;
     __builtin_memcpy(&bh, &hi, 16);
     __builtin_memcpy(&bl, &lo, 16);
+    half8 av[8];
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb) {
-      const uint32_t w = e == 0 ? kd[bb][s].x : e == 1 ? kd[bb][s].y : e == 2 ? kd[bb][s].z : kd[bb][s].w;
-      const half8 av = nib8_centred(w);
-      sc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bh, sc[bb], 0, 0, 0);
-      sc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bl, sc[bb], 0, 0, 0);
-    }
+    for (int bb = 0; bb < 8; ++bb) av[bb] = nib8_centred(pick(kd[bb][s], e));
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) sc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[bb], bh, sc[bb], 0, 0, 0);
+#pragma unroll
+    for (int bb = 0; bb < 8; ++bb) sc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[bb], bl, sc[bb], 0, 0, 0);
   }
   a1 = xsum4(a1);
   a16 = xsum4(a16);
-  const float sig_q = a1 + 16.0f * a16;    // sum of q~
+  const float sig_q = a1 + 16.0f * a16;
 
-  // ---- scores (log2 units): s = scale (S_i M + (Z_i + 8 S_i) sig_q)
-  const uint8_t* skz = km + 512;  // S^K[128] then Z^K[128]
-  uint4 sk[4], zk[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    sk[t] = *(const uint4*)(skz + 2 * (32 * g + 8 * t));
-    zk[t] = *(const uint4*)(skz + 256 + 2 * (32 * g + 8 * t));
-  }
+  // ---- scores in log2 units: scale (S_i M + (Z_i + 8 S_i) sig_q)
   float mx = -INFINITY;
 #pragma unroll
-  for (int bb = 0; bb < 8; ++bb) {
-    const int t = bb >> 1, hh = bb & 1;
+  for (int t = 0; t < 4; ++t) {
+    const uint4 skv = *(const uint4*)(km + 512 + 2 * (32 * g + 8 * t));
+    const uint4 zkv = *(const uint4*)(km + 768 + 2 * (32 * g + 8 * t));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k8 = 4 * hh + i;  // token 32 g + 8 t + k8
-      const uint32_t sw = (k8 >> 1) == 0 ? sk[t].x : (k8 >> 1) == 1 ? sk[t].y : (k8 >> 1) == 2 ? sk[t].z : sk[t].w;
-      const uint32_t zw = (k8 >> 1) == 0 ? zk[t].x : (k8 >> 1) == 1 ? zk[t].y : (k8 >> 1) == 2 ? zk[t].z : zk[t].w;
-      const float S = h2f((uint16_t)(sw >> (16 * (k8 & 1))));
-      const float Z = h2f((uint16_t)(zw >> (16 * (k8 & 1))));
+    for (int k8 = 0; k8 < 8; ++k8) {
+      const float S = h2f((uint16_t)(pick(skv, k8 >> 1) >> (16 * (k8 & 1))));
+      const float Z = h2f((uint16_t)(pick(zkv, k8 >> 1) >> (16 * (k8 & 1))));
+      const int bb = 2 * t + (k8 >> 2), i = k8 & 3;
       const float v = (S * sc[bb][i] + fmaf(8.0f, S, Z) * sig_q) * scale_log2;
       sc[bb][i] = v;
       mx = fmaxf(mx, v);
@@ -195,85 +235,91 @@ __device__ __forceinline__ void body_record(const uint8_t* __restrict__ rec, con
   }
   mx = xmax4(mx);
   const float m_new = fmaxf(m_run, mx);
-  const float alpha = exp2f(m_run - m_new);
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
   m_run = m_new;
   if (alpha != 1.0f) {
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb) acc[cb] *= alpha;
   }
-  l_run *= alpha;
+  l_part *= alpha;
 
-  // ---- P' = p S^V (operand order) and the zero-point term
-  const uint8_t* svz = vm + 512;
-  uint4 pb[4];
+  // ---- P' = p S^V in operand order, zero-point term with the centred codes
+  half8 pb[4];
   float zt = 0.0f;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const uint4 sv = *(const uint4*)(svz + 2 * (32 * g + 8 * t));
-    const uint4 zv = *(const uint4*)(svz + 256 + 2 * (32 * g + 8 * t));
-    float p[8], S[8], Z[8];
-    const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
-    const uint32_t zw[4] = {zv.x, zv.y, zv.z, zv.w};
+    const uint4 sv = *(const uint4*)(vm + 512 + 2 * (32 * g + 8 * t));
+    const uint4 zv = *(const uint4*)(vm + 768 + 2 * (32 * g + 8 * t));
+    float p[8], S[8];
 #pragma unroll
     for (int k8 = 0; k8 < 8; ++k8) {
-      S[k8] = h2f((uint16_t)(sw[k8 >> 1] >> (16 * (k8 & 1))));
-      Z[k8] = h2f((uint16_t)(zw[k8 >> 1] >> (16 * (k8 & 1))));
-      p[k8] = exp2f(sc[2 * t + (k8 >> 2)][k8 & 3] - m_new);
-      l_run += p[k8];
-      zt = fmaf(p[k8], fmaf(8.0f, S[k8], Z[k8]), zt);
+      S[k8] = h2f((uint16_t)(pick(sv, k8 >> 1) >> (16 * (k8 & 1))));
+      const float Z = h2f((uint16_t)(pick(zv, k8 >> 1) >> (16 * (k8 & 1))));
+      p[k8] = __builtin_amdgcn_exp2f(sc[2 * t + (k8 >> 2)][k8 & 3] - m_new);  // argument <= 0
+      l_part += p[k8];
+      zt = fmaf(p[k8], fmaf(8.0f, S[k8], Z), zt);
     }
-    // operand order: tokens 0,4,1,5,2,6,3,7 with x1, x1, /16, /16, ...
     uint4 r;
     r.x = pack_h2(p[0] * S[0], p[4] * S[4]);
     r.y = pack_h2(p[1] * S[1] * 0.0625f, p[5] * S[5] * 0.0625f);
     r.z = pack_h2(p[2] * S[2], p[6] * S[6]);
     r.w = pack_h2(p[3] * S[3] * 0.0625f, p[7] * S[7] * 0.0625f);
-    pb[t] = r;
+    __builtin_memcpy(&pb[t], &r, 16);
   }
-  const float corr = -xsum4(zt);
+  // value codes enter centred like key codes: keeping the 1024 offset in the
+  // accumulator and removing it afterwards measurably loses precision in the
+  // matrix cores' accumulation
+  const float corr = xsum4(zt);
 
-  // ---- O^T = V^T . P'^T per block of 16 channels, folded into acc with C^V
+  // ---- O^T = V^T . P'^T, four channel blocks at a time, folded into acc with C^V
 #pragma unroll
-  for (int cb = 0; cb < 16; ++cb) {
-    float4v o = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c4 = 0; c4 < 4; ++c4) {
+    float4v o[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint32_t w = t == 0 ? vd[cb].x : t == 1 ? vd[cb].y : t == 2 ? vd[cb].z : vd[cb].w;
-      half8 bop;
-      __builtin_memcpy(&bop, &pb[t], 16);
-      o = __builtin_amdgcn_mfma_f32_16x16x32_f16(nib8_centred(w), bop, o, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) o[j] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(nib8_centred(pick(vd[4 * c4 + j], t)), pb[t], o[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cb = 4 * c4 + j;
+      const uint2 cv = *(const uint2*)(vm + 2 * (16 * cb + 4 * g));
+      acc[cb][0] = fmaf(h2f((uint16_t)cv.x), o[j][0] + corr, acc[cb][0]);
+      acc[cb][1] = fmaf(h2f((uint16_t)(cv.x >> 16)), o[j][1] + corr, acc[cb][1]);
+      acc[cb][2] = fmaf(h2f((uint16_t)cv.y), o[j][2] + corr, acc[cb][2]);
+      acc[cb][3] = fmaf(h2f((uint16_t)(cv.y >> 16)), o[j][3] + corr, acc[cb][3]);
     }
-    const uint2 cv = *(const uint2*)(vm + 2 * (16 * cb + 4 * g));
-    const float c0 = h2f((uint16_t)cv.x), c1 = h2f((uint16_t)(cv.x >> 16));
-    const float c2 = h2f((uint16_t)cv.y), c3 = h2f((uint16_t)(cv.y >> 16));
-    acc[cb][0] = fmaf(c0, o[0] - corr, acc[cb][0]);
-    acc[cb][1] = fmaf(c1, o[1] - corr, acc[cb][1]);
-    acc[cb][2] = fmaf(c2, o[2] - corr, acc[cb][2]);
-    acc[cb][3] = fmaf(c3, o[3] - corr, acc[cb][3]);
   }
 }
 
-__global__ __launch_bounds__(256) void decode_body_mfma_kernel(DecodeArgs a) {
+// Query operands of the G query heads of one KV head, written once per decode
+// call, each as hi + lo fp16 in the operand order of the score products:
+//   set 0: q' = H q / 16 in the body's nibble order [0,4,1,5,2,6,3,7] with the
+//          high-nibble slots divided by 16;
+//   set 1: q' in natural channel order (staging ring, 6-bit codes);
+//   set 2: the unrotated q in natural order (fp16 sink).
+// Grid (H, n_seqs), 256 threads.
+constexpr int kQopsSet = 2 * 8 * 64;   // uint4 per set: (hi, lo) x 8 k-steps x 64 lanes
+
+__device__ __forceinline__ void split_h2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = pack_h2(x0, x1);
+  lo = pack_h2(x0 - h2f((uint16_t)hi), x1 - h2f((uint16_t)(hi >> 16)));
+}
+
+__global__ __launch_bounds__(256) void decode_qprep_kernel(DecodeArgs a) {
+  __shared__ float qraw[kMaxGroup][256];
   __shared__ float qrot[kMaxGroup][256];
-  __shared__ float wm[4][16], wl[4][16];
-  __shared__ float4v wacc[4][16][64];   // [wave][cb][lane]: 64 KB
-
-  const Layout& y = a.y;
-  const DecodeSeq sq = a.seq[blockIdx.z];
-  const int cbk = blockIdx.x;
-  if (cbk >= sq.n_body_chunks) return;
-  const int h = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int q16 = lane & 15, g = lane >> 4;
-  const int G = a.g;
-
-  // rotated query (fp32, LDS), rows >= G are zero
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int q16 = lane & 15, g = lane >> 4, G = a.g;
   for (int idx = tid; idx < kMaxGroup * 256; idx += 256) {
     const int i = idx >> 8, j = idx & 255;
-    qrot[i][j] = i < G ? h2f(a.q[((int64_t)blockIdx.z * a.Hq + h * G + i) * 256 + j]) : 0.0f;
+    const float v = i < G ? h2f(a.q[((int64_t)b * a.Hq + h * G + i) * 256 + j]) : 0.0f;
+    qraw[i][j] = v;
+    qrot[i][j] = v;
   }
   __syncthreads();
-  // 256-point Hadamard per row, /16
   for (int st = 1; st < 256; st <<= 1) {
     for (int p = tid; p < kMaxGroup * 128; p += 256) {
       const int i = p >> 7, pp = p & 127;
@@ -284,72 +330,108 @@ __global__ __launch_bounds__(256) void decode_body_mfma_kernel(DecodeArgs a) {
     }
     __syncthreads();
   }
-  // this lane's rotated query values in operand order, as hi + lo fp16: the
-  // butterflies above leave H q, so x1/16 gives q'; the high-nibble slots take
-  // a further /16
-  uint4 qph[8], qpl[8];
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
+  uint4* out = a.qops + ((int64_t)b * a.y.H + h) * (3 * kQopsSet);
+  for (int kk = 2 * wave; kk < 2 * wave + 2; ++kk) {
     const int s = kk >> 2, e = kk & 3;
     const int base = 128 * s + 32 * g + 8 * e;
     const float* qr = qrot[q16];
+    const float* qw = qraw[q16];
     const int ord[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-    uint32_t h[4], l[4];
-#pragma unroll
+    uint32_t hb[4], lb[4], hr[4], lr[4], hs[4], ls[4];
     for (int pr = 0; pr < 4; ++pr) {
       const float f = (pr & 1) ? 0.0625f * 0.0625f : 0.0625f;
-      const float x0 = qr[base + ord[2 * pr]] * f, x1 = qr[base + ord[2 * pr + 1]] * f;
-      h[pr] = pack_h2(x0, x1);
-      const float h0 = h2f((uint16_t)h[pr]), h1 = h2f((uint16_t)(h[pr] >> 16));
-      l[pr] = pack_h2(x0 - h0, x1 - h1);
+      split_h2(qr[base + ord[2 * pr]] * f, qr[base + ord[2 * pr + 1]] * f, hb[pr], lb[pr]);
+      split_h2(qr[base + 2 * pr] * 0.0625f, qr[base + 2 * pr + 1] * 0.0625f, hr[pr], lr[pr]);
+      split_h2(qw[base + 2 * pr], qw[base + 2 * pr + 1], hs[pr], ls[pr]);
     }
-    qph[kk] = make_uint4(h[0], h[1], h[2], h[3]);
-    qpl[kk] = make_uint4(l[0], l[1], l[2], l[3]);
+    out[kk * 64 + lane] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
+    out[(8 + kk) * 64 + lane] = make_uint4(lb[0], lb[1], lb[2], lb[3]);
+    out[kQopsSet + kk * 64 + lane] = make_uint4(hr[0], hr[1], hr[2], hr[3]);
+    out[kQopsSet + (8 + kk) * 64 + lane] = make_uint4(lr[0], lr[1], lr[2], lr[3]);
+    out[2 * kQopsSet + kk * 64 + lane] = make_uint4(hs[0], hs[1], hs[2], hs[3]);
+    out[2 * kQopsSet + (8 + kk) * 64 + lane] = make_uint4(ls[0], ls[1], ls[2], ls[3]);
+  }
+}
+
+__global__ __launch_bounds__(256) void decode_body_stream_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * kWaveLds];
+  __shared__ float xm[4][16], xl[4][16];
+
+  const Layout& y = a.y;
+  const DecodeSeq sq = a.seq[blockIdx.z];
+  const int cbk = blockIdx.x;
+  if (cbk >= sq.n_body_chunks) return;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int q16 = lane & 15, g = lane >> 4;
+  const int G = a.g;
+
+  // ---- rotated query operands (hi, lo), prepared once per call
+  uint4 qph[8], qpl[8];
+  const uint4* qo = a.qops + ((int64_t)blockIdx.z * y.H + h) * (3 * kQopsSet);
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    qph[kk] = qo[kk * 64 + lane];
+    qpl[kk] = qo[(8 + kk) * 64 + lane];
   }
 
+  // ---- this wave's records: r0 + wave, r0 + wave + 4, ...
+  uint8_t* mine = lds + wave * kWaveLds;
+  const uint32_t codes_lds = lds_addr(mine);
+  const uint32_t meta_lds[2] = {lds_addr(mine + kCodeBytes), lds_addr(mine + kCodeBytes + kMetaBytes)};
+  const int r0 = cbk * a.rec_per_chunk;
+  const int r1 = min(sq.n_rec, r0 + a.rec_per_chunk);
   const float scale_log2 = a.scale * kLog2e;
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY, l_part = 0.0f;
   float4v acc[16];
 #pragma unroll
   for (int cb = 0; cb < 16; ++cb) acc[cb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int r0 = cbk * a.rec_per_chunk;
-  const int r1 = min(sq.n_rec, r0 + a.rec_per_chunk);
-  for (int r = r0 + wave; r < r1; r += 4) {
-    const uint8_t* rec = a.arena + rec_off(y, sq.slot, a.layer, h, r);
-    body_record(rec, qph, qpl, lane, scale_log2, m_run, l_run, acc);
+  int r = r0 + wave;
+  if (r < r1) stage(a.arena + rec_off(y, sq.slot, a.layer, h, r), codes_lds, meta_lds[0], lane);
+  for (int it = 0; r < r1; ++it, r += 4) {
+    wait_vm0();
+    uint4 kd[8][2], vd[16];
+#pragma unroll
+    for (int sl = 0; sl < 16; ++sl) kd[sl >> 1][sl & 1] = *(const uint4*)(mine + sl * 1024 + 16 * lane);
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb) vd[cb] = *(const uint4*)(mine + (16 + cb) * 1024 + 16 * lane);
+    wait_lgkm0();
+    if (r + 4 < r1) stage(a.arena + rec_off(y, sq.slot, a.layer, h, r + 4), codes_lds, meta_lds[(it + 1) & 1], lane);
+    record_step(kd, vd, mine + kCodeBytes + (it & 1) * kMetaBytes, qph, qpl, lane, scale_log2, m_run, l_part, acc);
   }
 
-  // ---- combine the four waves
-  l_run = xsum4(l_run);
+  // ---- combine the four waves (codes areas reused as scratch)
+  const float lsum = xsum4(l_part);
   if (g == 0) {
-    wm[wave][q16] = m_run;
-    wl[wave][q16] = l_run;
+    xm[wave][q16] = m_run;
+    xl[wave][q16] = lsum;
   }
   __syncthreads();
-  const float M = fmaxf(fmaxf(wm[0][q16], wm[1][q16]), fmaxf(wm[2][q16], wm[3][q16]));
+  const float M = fmaxf(fmaxf(xm[0][q16], xm[1][q16]), fmaxf(xm[2][q16], xm[3][q16]));
   const float f = m_run == -INFINITY ? 0.0f : exp2f(m_run - M);
+  float4v* wacc = (float4v*)lds;   // [wave][cb][lane]
 #pragma unroll
-  for (int cb = 0; cb < 16; ++cb) wacc[wave][cb][lane] = acc[cb] * f;
+  for (int cb = 0; cb < 16; ++cb) wacc[(wave * 16 + cb) * 64 + lane] = acc[cb] * f;
   __syncthreads();
-  // thread (wave w', lane) sums channel blocks cb = 4 w' .. 4 w' + 3 for its lane
-  const int c = 1 + sq.n_ring_chunks + cbk;
   if (q16 < G) {
+    const int c = 1 + sq.n_ring_chunks + cbk;
     float* P = a.part + (((int64_t)blockIdx.z * a.Hq + h * G + q16) * a.max_chunks + c) * (256 + 2);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int cb = 4 * wave + k;
-      const float4v s = wacc[0][cb][lane] + wacc[1][cb][lane] + wacc[2][cb][lane] + wacc[3][cb][lane];
+      const float4v s4 = wacc[(0 * 16 + cb) * 64 + lane] + wacc[(1 * 16 + cb) * 64 + lane] +
+                         wacc[(2 * 16 + cb) * 64 + lane] + wacc[(3 * 16 + cb) * 64 + lane];
       const int ch = 16 * cb + 4 * g;
-      P[2 + ch + 0] = s[0];
-      P[2 + ch + 1] = s[1];
-      P[2 + ch + 2] = s[2];
-      P[2 + ch + 3] = s[3];
+      P[2 + ch + 0] = s4[0];
+      P[2 + ch + 1] = s4[1];
+      P[2 + ch + 2] = s4[2];
+      P[2 + ch + 3] = s4[3];
     }
     if (wave == 0 && g == 0) {
       float L = 0.0f;
       for (int w = 0; w < 4; ++w)
-        if (wm[w][q16] != -INFINITY) L += wl[w][q16] * exp2f(wm[w][q16] - M);
+        if (xm[w][q16] != -INFINITY) L += xl[w][q16] * exp2f(xm[w][q16] - M);
       P[0] = M * kLn2;
       P[1] = L;
     }
@@ -358,8 +440,9 @@ __global__ __launch_bounds__(256) void decode_body_mfma_kernel(DecodeArgs a) {
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int grid_x, hipStream_t stream) {
   if (a.y.D != 256 || a.y.kbits != 4 || a.y.vbits != 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(decode_qprep_kernel, dim3(a.y.H, a.n_seqs), dim3(256), 0, stream, a);
   dim3 grid(grid_x, a.y.H, a.n_seqs);
-  hipLaunchKernelGGL(decode_body_mfma_kernel, grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(decode_body_stream_kernel, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

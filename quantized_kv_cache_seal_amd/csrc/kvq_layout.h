@@ -87,6 +87,7 @@ struct DecodeArgs {
   Layout y;
   const uint16_t* q;  // fp16 [n_seqs][Hq][D]
   float* part;        // [n_seqs][Hq][max_chunks][D + 2]: m, l, acc[D]
+  uint4* qops;        // [n_seqs][H][2 (hi, lo)][8][64]: rotated query in matrix-core operand order
   float scale;
   int32_t layer, Hq, g, n_seqs, max_chunks, ring_chunk, rec_per_chunk;
   int32_t chunk_base;  // first chunk index this launch covers (0 for sink/ring launch)

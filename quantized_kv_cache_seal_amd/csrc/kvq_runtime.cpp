@@ -31,6 +31,7 @@ struct kvq_cache {
   uint8_t* arena;
   bool plan_only;
   int32_t path;
+  int32_t n_cu;
   uint32_t signs[8];
   std::vector<int64_t> n_tok;  // [S * L]
   std::vector<int64_t> n_rec;  // [S * L]
@@ -119,12 +120,20 @@ static int ring_chunk_tokens(const Layout& y) {
   return kGroup * (int)std::max<int64_t>(1, (y.cap / kGroup + 1023) / 1024);
 }
 static int valu_rec_per_chunk(const Layout& y) { return std::max(1, (y.max_rec + 2999) / 3000); }
-// Matrix-core path: a multiple of 4 records per workgroup (one per wave), about
-// two workgroups per compute unit over the whole call.
-static int mfma_rec_per_chunk(int64_t total_records) {
-  const int64_t slots = 4 * 512;
-  return 4 * (int)std::max<int64_t>(1, (total_records + slots - 1) / slots);
+// Matrix-core path: one workgroup per compute unit (the kernel's LDS staging
+// takes most of a CU), each streaming about total / n_cu records, at least one
+// per wave.
+static int mfma_rec_per_chunk(int64_t total_records, int n_cu) {
+  return (int)std::max<int64_t>(4, (total_records + n_cu - 1) / n_cu);
 }
+static int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+// bytes of rotated-query operands per (sequence, KV head) in the workspace
+static constexpr size_t kQopsBytes = 3 * 2 * 8 * 64 * 16;
 static bool mfma_supported(const Layout& y) { return y.D == 256 && y.kbits == 4 && y.vbits == 4; }
 
 static DecodeSeq plan_seq(const kvq_cache* c, int s, int layer, int rc, int rpc) {
@@ -192,6 +201,7 @@ kvq_status kvq_cache_create(const kvq_config* cfg, void* device_arena, size_t ar
   c->arena = plan_only ? nullptr : (uint8_t*)device_arena;
   c->plan_only = plan_only;
   c->path = KVQ_PATH_AUTO;
+  c->n_cu = 0;
   fill_signs(*cfg, c->signs);
   c->n_tok.assign((size_t)y.S * y.L, 0);
   c->n_rec.assign((size_t)y.S * y.L, 0);
@@ -316,7 +326,8 @@ static int max_chunks_bound(const kvq_cache* c) {
 
 kvq_status kvq_workspace_bytes(const kvq_cache* c, int32_t n_seqs, size_t* bytes) {
   if (!c || !bytes || n_seqs < 0) return fail(KVQ_ERR_INVALID, "bad arguments");
-  *bytes = (size_t)n_seqs * c->cfg.n_q_heads * max_chunks_bound(c) * (c->y.D + 2) * sizeof(float);
+  *bytes = (size_t)n_seqs * c->cfg.n_q_heads * max_chunks_bound(c) * (c->y.D + 2) * sizeof(float) + 256 +
+           (size_t)n_seqs * c->y.H * kQopsBytes;
   return KVQ_OK;
 }
 
@@ -346,7 +357,8 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
     if (c->tok(seq_ids[i], layer) < 1) return fail(KVQ_ERR_INVALID, "sequence %d holds no tokens", seq_ids[i]);
     total_rec += c->rec(seq_ids[i], layer) * c->y.H;
   }
-  const int rpc = use_mfma ? mfma_rec_per_chunk(total_rec) : valu_rec_per_chunk(c->y);
+  if (use_mfma && c->n_cu == 0) c->n_cu = device_cu_count();
+  const int rpc = use_mfma ? mfma_rec_per_chunk(total_rec, c->n_cu) : valu_rec_per_chunk(c->y);
   std::vector<DecodeSeq> plan(n_seqs);
   int max_chunks = 1;
   for (int i = 0; i < n_seqs; ++i) {
@@ -355,7 +367,9 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
   }
   if (max_chunks > kMaxChunks) return fail(KVQ_ERR_CAPACITY, "too many split-K chunks");
   const int Hq = c->cfg.n_q_heads, D = c->y.D;
-  const size_t need = (size_t)n_seqs * Hq * max_chunks * (D + 2) * sizeof(float);
+  const size_t part_bytes = (size_t)n_seqs * Hq * max_chunks * (D + 2) * sizeof(float);
+  const size_t qops_off = (part_bytes + 255) / 256 * 256;
+  const size_t need = qops_off + (size_t)n_seqs * c->y.H * kQopsBytes;
   if (ws_bytes < need) return fail(KVQ_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   const size_t out_elem = out_dtype == KVQ_OUT_F16 ? 2 : 4;
   for (int b0 = 0; b0 < n_seqs; b0 += kMaxLaunchSeqs) {
@@ -365,6 +379,7 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
     a.n_seqs = std::min(kMaxLaunchSeqs, n_seqs - b0);
     a.q = (const uint16_t*)q + (int64_t)b0 * Hq * D;
     a.part = (float*)workspace + (int64_t)b0 * Hq * max_chunks * (D + 2);
+    a.qops = (uint4*)((uint8_t*)workspace + qops_off) + (int64_t)b0 * c->y.H * (kQopsBytes / 16);
     a.scale = scale;
     a.layer = layer;
     a.Hq = Hq;

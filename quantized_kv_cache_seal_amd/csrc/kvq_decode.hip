@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   const int g = a.g;
   const int s = sq.slot, layer = a.layer;
   const int region = c == 0 ? 0 : (c < 1 + sq.n_ring_chunks ? 1 : 2);
-  if (region == 2 && !a.valu_body) return;  // body chunks belong to the matrix-core kernel
+  if (!((a.valu_regions >> region) & 1)) return;  // region handled by a matrix-core kernel
 
   for (int idx = tid; idx < g * D; idx += 256) {
     const int i = idx / D, j = idx % D;

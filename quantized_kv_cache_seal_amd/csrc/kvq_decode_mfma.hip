@@ -29,16 +29,9 @@
 // each wave takes every fourth record with its own online-softmax state; the
 // four states are combined in LDS and written as one fp32 partial
 // (m, l, acc[D]) in natural-log units, for the merge kernel.
-#include "kvq_device.h"
+#include "kvq_mfma.h"
 
 namespace kvq {
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float float4v __attribute__((ext_vector_type(4)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 
 // (a & m) | b in one v_and_or_b32.  The masks and the exponent pattern are
 // passed in registers: a VOP3 instruction on this target cannot carry two
@@ -74,32 +67,6 @@ __device__ __forceinline__ half8 nib8_centred(uint32_t w) {
   const half8 off = {(_Float16)1032.0f, (_Float16)1032.0f, (_Float16)1152.0f, (_Float16)1152.0f,
                      (_Float16)1032.0f, (_Float16)1032.0f, (_Float16)1152.0f, (_Float16)1152.0f};
   return h - off;
-}
-
-__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
-  return (uint32_t)f2h_bits(lo) | ((uint32_t)f2h_bits(hi) << 16);
-}
-
-__device__ __forceinline__ half2v as_h2(uint32_t u) {
-  half2v h;
-  __builtin_memcpy(&h, &u, 4);
-  return h;
-}
-__device__ __forceinline__ uint32_t as_u32(half2v h) {
-  uint32_t u;
-  __builtin_memcpy(&u, &h, 4);
-  return u;
-}
-
-__device__ __forceinline__ float xsum4(float x) {  // sum over the four lane groups
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
-}
-__device__ __forceinline__ float xmax4(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  x = fmaxf(x, __shfl_xor(x, 32, 64));
-  return x;
 }
 
 // q~ = q' * C for one operand slot pair, split into hi + lo fp16 so that the
@@ -294,65 +261,6 @@ __device__ __forceinline__ void record_step(const uint4 (&kd)[8][2], const uint4
   }
 }
 
-// Query operands of the G query heads of one KV head, written once per decode
-// call, each as hi + lo fp16 in the operand order of the score products:
-//   set 0: q' = H q / 16 in the body's nibble order [0,4,1,5,2,6,3,7] with the
-//          high-nibble slots divided by 16;
-//   set 1: q' in natural channel order (staging ring, 6-bit codes);
-//   set 2: the unrotated q in natural order (fp16 sink).
-// Grid (H, n_seqs), 256 threads.
-constexpr int kQopsSet = 2 * 8 * 64;   // uint4 per set: (hi, lo) x 8 k-steps x 64 lanes
-
-__device__ __forceinline__ void split_h2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  hi = pack_h2(x0, x1);
-  lo = pack_h2(x0 - h2f((uint16_t)hi), x1 - h2f((uint16_t)(hi >> 16)));
-}
-
-__global__ __launch_bounds__(256) void decode_qprep_kernel(DecodeArgs a) {
-  __shared__ float qraw[kMaxGroup][256];
-  __shared__ float qrot[kMaxGroup][256];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int q16 = lane & 15, g = lane >> 4, G = a.g;
-  for (int idx = tid; idx < kMaxGroup * 256; idx += 256) {
-    const int i = idx >> 8, j = idx & 255;
-    const float v = i < G ? h2f(a.q[((int64_t)b * a.Hq + h * G + i) * 256 + j]) : 0.0f;
-    qraw[i][j] = v;
-    qrot[i][j] = v;
-  }
-  __syncthreads();
-  for (int st = 1; st < 256; st <<= 1) {
-    for (int p = tid; p < kMaxGroup * 128; p += 256) {
-      const int i = p >> 7, pp = p & 127;
-      const int j = (pp / st) * 2 * st + (pp % st);
-      const float u = qrot[i][j], v = qrot[i][j + st];
-      qrot[i][j] = u + v;
-      qrot[i][j + st] = u - v;
-    }
-    __syncthreads();
-  }
-  uint4* out = a.qops + ((int64_t)b * a.y.H + h) * (3 * kQopsSet);
-  for (int kk = 2 * wave; kk < 2 * wave + 2; ++kk) {
-    const int s = kk >> 2, e = kk & 3;
-    const int base = 128 * s + 32 * g + 8 * e;
-    const float* qr = qrot[q16];
-    const float* qw = qraw[q16];
-    const int ord[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-    uint32_t hb[4], lb[4], hr[4], lr[4], hs[4], ls[4];
-    for (int pr = 0; pr < 4; ++pr) {
-      const float f = (pr & 1) ? 0.0625f * 0.0625f : 0.0625f;
-      split_h2(qr[base + ord[2 * pr]] * f, qr[base + ord[2 * pr + 1]] * f, hb[pr], lb[pr]);
-      split_h2(qr[base + 2 * pr] * 0.0625f, qr[base + 2 * pr + 1] * 0.0625f, hr[pr], lr[pr]);
-      split_h2(qw[base + 2 * pr], qw[base + 2 * pr + 1], hs[pr], ls[pr]);
-    }
-    out[kk * 64 + lane] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
-    out[(8 + kk) * 64 + lane] = make_uint4(lb[0], lb[1], lb[2], lb[3]);
-    out[kQopsSet + kk * 64 + lane] = make_uint4(hr[0], hr[1], hr[2], hr[3]);
-    out[kQopsSet + (8 + kk) * 64 + lane] = make_uint4(lr[0], lr[1], lr[2], lr[3]);
-    out[2 * kQopsSet + kk * 64 + lane] = make_uint4(hs[0], hs[1], hs[2], hs[3]);
-    out[2 * kQopsSet + (8 + kk) * 64 + lane] = make_uint4(ls[0], ls[1], ls[2], ls[3]);
-  }
-}
-
 __global__ __launch_bounds__(256) void decode_body_stream_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * kWaveLds];
   __shared__ float xm[4][16], xl[4][16];
@@ -368,7 +276,7 @@ __global__ __launch_bounds__(256) void decode_body_stream_kernel(DecodeArgs a) {
 
   // ---- rotated query operands (hi, lo), prepared once per call
   uint4 qph[8], qpl[8];
-  const uint4* qo = a.qops + ((int64_t)blockIdx.z * y.H + h) * (3 * kQopsSet);
+  const uint4* qo = a.qops + ((int64_t)blockIdx.z * y.H + h) * kQopsPerHead;
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     qph[kk] = qo[kk * 64 + lane];
@@ -440,7 +348,6 @@ __global__ __launch_bounds__(256) void decode_body_stream_kernel(DecodeArgs a) {
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int grid_x, hipStream_t stream) {
   if (a.y.D != 256 || a.y.kbits != 4 || a.y.vbits != 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(decode_qprep_kernel, dim3(a.y.H, a.n_seqs), dim3(256), 0, stream, a);
   dim3 grid(grid_x, a.y.H, a.n_seqs);
   hipLaunchKernelGGL(decode_body_stream_kernel, grid, dim3(256), 0, stream, a);
   return hipGetLastError();

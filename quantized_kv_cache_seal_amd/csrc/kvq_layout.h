@@ -87,11 +87,11 @@ struct DecodeArgs {
   Layout y;
   const uint16_t* q;  // fp16 [n_seqs][Hq][D]
   float* part;        // [n_seqs][Hq][max_chunks][D + 2]: m, l, acc[D]
-  uint4* qops;        // [n_seqs][H][2 (hi, lo)][8][64]: rotated query in matrix-core operand order
+  uint4* qops;        // [n_seqs][H][3 sets][2 (hi, lo)][8][64]: query in matrix-core operand order
   float scale;
   int32_t layer, Hq, g, n_seqs, max_chunks, ring_chunk, rec_per_chunk;
   int32_t chunk_base;  // first chunk index this launch covers (0 for sink/ring launch)
-  int32_t valu_body;   // 1: the vector-ALU kernel also scans body chunks
+  int32_t valu_regions;  // bit r set: the vector-ALU kernel scans region r (0 sink, 1 ring, 2 body)
   uint32_t signs[8];
   DecodeSeq seq[kMaxLaunchSeqs];
 };

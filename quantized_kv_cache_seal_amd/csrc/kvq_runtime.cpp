@@ -20,6 +20,8 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_seal(const SealArgs& a, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs& a, int grid_x, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int grid_x, hipStream_t stream);
+hipError_t launch_decode_qprep(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_staged(const DecodeArgs& a, int grid_x, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 }  // namespace kvq
 
@@ -133,8 +135,11 @@ static int device_cu_count() {
   return n;
 }
 // bytes of rotated-query operands per (sequence, KV head) in the workspace
-static constexpr size_t kQopsBytes = 3 * 2 * 8 * 64 * 16;
+static constexpr size_t kQopsBytes = 3 * 2 * 8 * 64 * 16;  // query operand sets per (sequence, KV head)
 static bool mfma_supported(const Layout& y) { return y.D == 256 && y.kbits == 4 && y.vbits == 4; }
+// matrix-core sink and ring scan: head_dim 128 or 256, 128-token ring chunks
+static bool staged_supported(const Layout& y) { return y.D == 128 || y.D == 256; }
+static constexpr int kStagedRingChunk = 128;
 
 static DecodeSeq plan_seq(const kvq_cache* c, int s, int layer, int rc, int rpc) {
   DecodeSeq d{};
@@ -319,8 +324,10 @@ kvq_status kvq_seal(kvq_cache* c, int32_t layer, int32_t mode, void* stream, int
 }
 
 static int max_chunks_bound(const kvq_cache* c) {
-  const int rc = ring_chunk_tokens(c->y);
-  const int rpc = valu_rec_per_chunk(c->y);
+  // the smallest chunks any path uses: 128-token ring chunks, and at most 4
+  // records per body chunk
+  const int rc = std::min(ring_chunk_tokens(c->y), kStagedRingChunk);
+  const int rpc = std::min(valu_rec_per_chunk(c->y), 4);
   return 1 + (c->y.cap + rc - 1) / rc + (c->y.max_rec + rpc - 1) / rpc;
 }
 
@@ -348,8 +355,9 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
   if (st != KVQ_OK) return st;
   if (n_seqs == 0) return KVQ_OK;
   if (!q || !out || !workspace) return fail(KVQ_ERR_INVALID, "q, out and workspace must be non-NULL");
-  const int rc = ring_chunk_tokens(c->y);
   const bool use_mfma = c->path != KVQ_PATH_VALU && mfma_supported(c->y);
+  const bool staged = c->path != KVQ_PATH_VALU && staged_supported(c->y);
+  const int rc = staged ? kStagedRingChunk : ring_chunk_tokens(c->y);
   if (c->path == KVQ_PATH_MFMA && !use_mfma)
     return fail(KVQ_ERR_UNSUPPORTED, "matrix-core body scan needs head_dim 256 with 4-bit K and V");
   int64_t total_rec = 0;
@@ -389,15 +397,28 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
     a.rec_per_chunk = rpc;
     a.chunk_base = 0;
     std::memcpy(a.signs, c->signs, sizeof a.signs);
-    a.valu_body = use_mfma ? 0 : 1;
-    int grid_valu = 1, grid_body = 0;
+    // regions left to the vector-ALU kernel: bit 0 sink, 1 ring, 2 body
+    a.valu_regions = (staged ? 0 : 3) | (use_mfma ? 0 : 4);
+    int grid_valu = 0, grid_ring = 1, grid_body = 0;
     for (int b = 0; b < a.n_seqs; ++b) {
       a.seq[b] = plan[b0 + b];
-      grid_valu = std::max(grid_valu, use_mfma ? 1 + a.seq[b].n_ring_chunks : a.seq[b].n_chunks);
+      grid_ring = std::max(grid_ring, 1 + a.seq[b].n_ring_chunks);
       grid_body = std::max(grid_body, a.seq[b].n_body_chunks);
+      grid_valu = std::max(grid_valu, (a.valu_regions & 4) ? a.seq[b].n_chunks : 1 + a.seq[b].n_ring_chunks);
     }
-    hipError_t e = launch_decode_valu(a, grid_valu, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    hipError_t e = hipSuccess;
+    if (staged || use_mfma) {
+      e = launch_decode_qprep(a, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e, "query preparation launch");
+    }
+    if (staged) {
+      e = launch_decode_staged(a, grid_ring, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e, "sink/ring decode launch");
+    }
+    if (a.valu_regions != 0) {
+      e = launch_decode_valu(a, grid_valu, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e, "decode launch");
+    }
     if (use_mfma && grid_body > 0) {
       e = launch_decode_mfma(a, grid_body, (hipStream_t)stream);
       if (e != hipSuccess) return hip_fail(e, "body decode launch");

@@ -10,6 +10,8 @@
 //     sum_i p_i v_ij = C_j ( sum_i (p_i S_i) code_ij + sum_i p_i Z_i ).
 // Both inner products are dense (16 query rows, the group padded to 16) x
 // (32 codes) x (16 tokens or channels) and run on v_mfma_f32_16x16x32_f16.
+// The non-code operand of each (q~, and the weights p S) is split into
+// hi + lo fp16 halves, two products each, which keeps fp32-level precision.
 //
 // Codes reach the matrix cores without a conversion loop: one AND-OR per pair
 // turns a nibble n into the fp16 1024 + n (low nibble) or 1024 + 16 n (high
@@ -42,8 +44,18 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t b) {
   return d;
 }
 
-__device__ __forceinline__ half8 nib8(uint32_t w) {
-  // halves: [n0, n4, 16 n1, 16 n5, n2, n6, 16 n3, 16 n7] + 1024
+// Eight 4-bit codes of one dword as exact, centred fp16 values.
+// One AND-OR per pair puts a nibble n into the mantissa of 1024 (the high
+// nibble of a byte stays in place, i.e. 1024 + 16 n; its 1/16 is folded into
+// the query operand) and one packed subtract leaves n - 8 (or 16 (n - 8)).
+// Slots: [n0, n4, 16 n1, 16 n5, n2, n6, 16 n3, 16 n7] - centre.
+// Centring keeps the fp32 accumulators free of a large common term: with
+// codes in [0, 15] the score product carries 7.5 sum(q~), and q~ = q' C
+// reaches thousands in outlier channels; the value product carries
+// 7.5 sum(p S), hundreds of times the weighted average when attention is
+// diffuse.  fp32 rounding of such a term swamps the result.  The centre moves
+// into the zero point instead: x = C (S (n - 8) + (Z + 8 S)).
+__device__ __forceinline__ half8 nib8_centred(uint32_t w) {
   const uint32_t w8 = w >> 8;
   const uint32_t lo_m = 0x000F000Fu, hi_m = 0x00F000F0u, e = 0x64006400u;
   uint4 u;
@@ -51,22 +63,9 @@ __device__ __forceinline__ half8 nib8(uint32_t w) {
   u.y = and_or(w, hi_m, e);
   u.z = and_or(w8, lo_m, e);
   u.w = and_or(w8, hi_m, e);
-  half8 h;
-  __builtin_memcpy(&h, &u, 16);
-  return h;
-}
-
-// Recentred code values n - 8 (slots of the high nibble: 16 (n - 8)), exact in
-// fp16: one packed subtract removes the 1024 exponent offset and the centre.
-// Centring matters for precision: with codes in [0, 15] the products carry a
-// large common component S * 7.5 that the zero point later cancels, so fp16
-// rounding of the weights would be amplified; the centre moves into the zero
-// point instead (v = S (n - 8) + (Z + 8 S)).
-__device__ __forceinline__ half8 nib8_centred(uint32_t w) {
-  half8 h = nib8(w);
   const half8 off = {(_Float16)1032.0f, (_Float16)1032.0f, (_Float16)1152.0f, (_Float16)1152.0f,
                      (_Float16)1032.0f, (_Float16)1032.0f, (_Float16)1152.0f, (_Float16)1152.0f};
-  return h - off;
+  return mfma_a(u) - off;
 }
 
 // q~ = q' * C for one operand slot pair, split into hi + lo fp16 so that the
@@ -135,10 +134,11 @@ __device__ __forceinline__ uint32_t pick(const uint4& v, int e) {
 }
 
 // One record from registers (codes) and LDS (scales).  acc[cb][i] holds
-// channel 16 cb + 4 g + i for query column q = lane & 15; m_run in log2 units;
-// l_part sums this lane's tokens.
+// channel 16 cb + 4 g + i for query column q = lane & 15.  The query operands
+// already carry the softmax scale and log2(e): scores come out in log2 units.
+// m_run is the running maximum, l_part sums this lane's tokens.
 __device__ __forceinline__ void record_step(const uint4 (&kd)[8][2], const uint4 (&vd)[16], const uint8_t* km,
-                                            const uint4* qph, const uint4* qpl, int lane, float scale_log2,
+                                            const uint4* qph, const uint4* qpl, int lane,
                                             float& m_run, float& l_part, float4v* acc) {
   const int g = lane >> 4;
   const uint8_t* vm = km + 1024;
@@ -169,22 +169,20 @@ __device__ __forceinline__ void record_step(const uint4 (&kd)[8][2], const uint4
     a1 = __builtin_amdgcn_fdot2(as_h2(lo.z), ones, a1, false);
     a16 = __builtin_amdgcn_fdot2(as_h2(hi.w), ones, a16, false);
     a16 = __builtin_amdgcn_fdot2(as_h2(lo.w), ones, a16, false);
-    half8 bh, bl;
-    __builtin_memcpy(&bh, &hi, 16);
-    __builtin_memcpy(&bl, &lo, 16);
+    const half8 bh = mfma_a(hi), bl = mfma_a(lo);
     half8 av[8];
 #pragma unroll
     for (int bb = 0; bb < 8; ++bb) av[bb] = nib8_centred(pick(kd[bb][s], e));
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb) sc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[bb], bh, sc[bb], 0, 0, 0);
+    for (int bb = 0; bb < 8; ++bb) sc[bb] = mfma16(av[bb], bh, sc[bb]);
 #pragma unroll
-    for (int bb = 0; bb < 8; ++bb) sc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[bb], bl, sc[bb], 0, 0, 0);
+    for (int bb = 0; bb < 8; ++bb) sc[bb] = mfma16(av[bb], bl, sc[bb]);
   }
   a1 = xsum4(a1);
   a16 = xsum4(a16);
-  const float sig_q = a1 + 16.0f * a16;
+  const float sig = a1 + 16.0f * a16;  // sum of q~ over the channels
 
-  // ---- scores in log2 units: scale (S_i M + (Z_i + 8 S_i) sig_q)
+  // ---- scores S_i M_i + (Z_i + 8 S_i) sigma
   float mx = -INFINITY;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -192,10 +190,10 @@ __device__ __forceinline__ void record_step(const uint4 (&kd)[8][2], const uint4
     const uint4 zkv = *(const uint4*)(km + 768 + 2 * (32 * g + 8 * t));
 #pragma unroll
     for (int k8 = 0; k8 < 8; ++k8) {
-      const float S = h2f((uint16_t)(pick(skv, k8 >> 1) >> (16 * (k8 & 1))));
-      const float Z = h2f((uint16_t)(pick(zkv, k8 >> 1) >> (16 * (k8 & 1))));
+      const float S = (float)as_h2(pick(skv, k8 >> 1))[k8 & 1];
+      const float Z = (float)as_h2(pick(zkv, k8 >> 1))[k8 & 1];
       const int bb = 2 * t + (k8 >> 2), i = k8 & 3;
-      const float v = (S * sc[bb][i] + fmaf(8.0f, S, Z) * sig_q) * scale_log2;
+      const float v = fmaf(S, sc[bb][i], fmaf(8.0f, S, Z) * sig);
       sc[bb][i] = v;
       mx = fmaxf(mx, v);
     }
@@ -210,32 +208,32 @@ __device__ __forceinline__ void record_step(const uint4 (&kd)[8][2], const uint4
   }
   l_part *= alpha;
 
-  // ---- P' = p S^V in operand order, zero-point term with the centred codes
-  half8 pb[4];
+  // ---- P' = p S^V in operand order, as hi + lo; zero-point term sum p (Z^V + 8 S^V)
+  half8 pbh[4], pbl[4];
   float zt = 0.0f;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const uint4 sv = *(const uint4*)(vm + 512 + 2 * (32 * g + 8 * t));
     const uint4 zv = *(const uint4*)(vm + 768 + 2 * (32 * g + 8 * t));
-    float p[8], S[8];
+    float x[8];
 #pragma unroll
     for (int k8 = 0; k8 < 8; ++k8) {
-      S[k8] = h2f((uint16_t)(pick(sv, k8 >> 1) >> (16 * (k8 & 1))));
-      const float Z = h2f((uint16_t)(pick(zv, k8 >> 1) >> (16 * (k8 & 1))));
-      p[k8] = __builtin_amdgcn_exp2f(sc[2 * t + (k8 >> 2)][k8 & 3] - m_new);  // argument <= 0
-      l_part += p[k8];
-      zt = fmaf(p[k8], fmaf(8.0f, S[k8], Z), zt);
+      const _Float16 S = as_h2(pick(sv, k8 >> 1))[k8 & 1];
+      const _Float16 Z = as_h2(pick(zv, k8 >> 1))[k8 & 1];
+      const float p = __builtin_amdgcn_exp2f(sc[2 * t + (k8 >> 2)][k8 & 3] - m_new);  // argument <= 0
+      l_part += p;
+      zt = fmaf(p, fmaf(8.0f, (float)S, (float)Z), zt);
+      x[k8] = p * (float)S;
     }
-    uint4 r;
-    r.x = pack_h2(p[0] * S[0], p[4] * S[4]);
-    r.y = pack_h2(p[1] * S[1] * 0.0625f, p[5] * S[5] * 0.0625f);
-    r.z = pack_h2(p[2] * S[2], p[6] * S[6]);
-    r.w = pack_h2(p[3] * S[3] * 0.0625f, p[7] * S[7] * 0.0625f);
-    __builtin_memcpy(&pb[t], &r, 16);
+    // slot order [0, 4, 1/16 x 1, 1/16 x 5, 2, 6, 1/16 x 3, 1/16 x 7]
+    uint4 h, l;
+    split_h2(x[0], x[4], h.x, l.x);
+    split_h2(x[1] * 0.0625f, x[5] * 0.0625f, h.y, l.y);
+    split_h2(x[2], x[6], h.z, l.z);
+    split_h2(x[3] * 0.0625f, x[7] * 0.0625f, h.w, l.w);
+    pbh[t] = mfma_a(h);
+    pbl[t] = mfma_a(l);
   }
-  // value codes enter centred like key codes: keeping the 1024 offset in the
-  // accumulator and removing it afterwards measurably loses precision in the
-  // matrix cores' accumulation
   const float corr = xsum4(zt);
 
   // ---- O^T = V^T . P'^T, four channel blocks at a time, folded into acc with C^V
@@ -247,16 +245,20 @@ __device__ __forceinline__ void record_step(const uint4 (&kd)[8][2], const uint4
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        o[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(nib8_centred(pick(vd[4 * c4 + j], t)), pb[t], o[j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        const half8 av = nib8_centred(pick(vd[4 * c4 + j], t));
+        o[j] = mfma16(av, pbh[t], o[j]);
+        o[j] = mfma16(av, pbl[t], o[j]);
+      }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int cb = 4 * c4 + j;
       const uint2 cv = *(const uint2*)(vm + 2 * (16 * cb + 4 * g));
-      acc[cb][0] = fmaf(h2f((uint16_t)cv.x), o[j][0] + corr, acc[cb][0]);
-      acc[cb][1] = fmaf(h2f((uint16_t)(cv.x >> 16)), o[j][1] + corr, acc[cb][1]);
-      acc[cb][2] = fmaf(h2f((uint16_t)cv.y), o[j][2] + corr, acc[cb][2]);
-      acc[cb][3] = fmaf(h2f((uint16_t)(cv.y >> 16)), o[j][3] + corr, acc[cb][3]);
+      const half2v c01 = as_h2(cv.x), c23 = as_h2(cv.y);
+      acc[cb][0] = fmaf((float)c01[0], o[j][0] + corr, acc[cb][0]);
+      acc[cb][1] = fmaf((float)c01[1], o[j][1] + corr, acc[cb][1]);
+      acc[cb][2] = fmaf((float)c23[0], o[j][2] + corr, acc[cb][2]);
+      acc[cb][3] = fmaf((float)c23[1], o[j][3] + corr, acc[cb][3]);
     }
   }
 }
@@ -289,7 +291,6 @@ __global__ __launch_bounds__(256) void decode_body_stream_kernel(DecodeArgs a) {
   const uint32_t meta_lds[2] = {lds_addr(mine + kCodeBytes), lds_addr(mine + kCodeBytes + kMetaBytes)};
   const int r0 = cbk * a.rec_per_chunk;
   const int r1 = min(sq.n_rec, r0 + a.rec_per_chunk);
-  const float scale_log2 = a.scale * kLog2e;
   float m_run = -INFINITY, l_part = 0.0f;
   float4v acc[16];
 #pragma unroll
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(256) void decode_body_stream_kernel(DecodeArgs a) {
     for (int cb = 0; cb < 16; ++cb) vd[cb] = *(const uint4*)(mine + (16 + cb) * 1024 + 16 * lane);
     wait_lgkm0();
     if (r + 4 < r1) stage(a.arena + rec_off(y, sq.slot, a.layer, h, r + 4), codes_lds, meta_lds[(it + 1) & 1], lane);
-    record_step(kd, vd, mine + kCodeBytes + (it & 1) * kMetaBytes, qph, qpl, lane, scale_log2, m_run, l_part, acc);
+    record_step(kd, vd, mine + kCodeBytes + (it & 1) * kMetaBytes, qph, qpl, lane, m_run, l_part, acc);
   }
 
   // ---- combine the four waves (codes areas reused as scratch)

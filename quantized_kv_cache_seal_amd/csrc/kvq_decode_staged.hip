@@ -33,8 +33,9 @@ constexpr int kStagedTokens = 128;
 
 // ---------------------------------------------------------------------------
 // Query preparation: grid (H, n_seqs), 256 threads.  Rotates the G query heads
-// of one KV head (R = H/16 for head_dim 256, s2 . H . s1 / sqrt(128) for 128)
-// and writes the operand sets described in kvq_mfma.h.
+// of one KV head (R = H/16 for head_dim 256, s2 . H . s1 / sqrt(128) for 128),
+// multiplies them by scale * log2(e) so that every product below yields scores
+// in log2 units, and writes the operand sets described in kvq_mfma.h.
 template <int D>
 __global__ __launch_bounds__(256) void decode_qprep_kernel(DecodeArgs a) {
   constexpr int KK = D / 32;
@@ -42,9 +43,10 @@ __global__ __launch_bounds__(256) void decode_qprep_kernel(DecodeArgs a) {
   __shared__ float qrot[kMaxGroup][D];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int q16 = lane & 15, g = lane >> 4, G = a.g;
+  const float sl = a.scale * kLog2e;  // scores come out in log2 units
   for (int idx = tid; idx < kMaxGroup * D; idx += 256) {
     const int i = idx / D, j = idx % D;
-    const float v = i < G ? h2f(a.q[((int64_t)b * a.Hq + h * G + i) * D + j]) : 0.0f;
+    const float v = i < G ? h2f(a.q[((int64_t)b * a.Hq + h * G + i) * D + j]) * sl : 0.0f;
     qraw[i][j] = v;
     qrot[i][j] = (D == 128 && sign_neg(a.signs, j)) ? -v : v;
   }
@@ -224,7 +226,6 @@ __global__ __launch_bounds__(256) void decode_staged_kernel(DecodeArgs a) {
       ql[kk] = qo[(8 + kk) * 64 + lane];
     }
   }
-  const float scale_log2 = a.scale * kLog2e;
   float sc[2][4];
   float mx = -INFINITY;
 #pragma unroll
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(256) void decode_staged_kernel(DecodeArgs a) {
       float v = 0.0f;
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) v = sink ? v + acc[blk][r] : fmaf(dks[t][blk], acc[blk][r], v);
-      v = t < n ? v * scale_log2 : -INFINITY;
+      v = t < n ? v : -INFINITY;
       sc[i][r] = v;
       mx = fmaxf(mx, v);
     }

@@ -20,17 +20,15 @@
 // values, so the fp32 accumulators never carry a large offset term.
 //
 // Orientation: S^T = K . Q~^T (A = key codes, rows = tokens) and
-// O^T = V^T . P'^T (A = value codes, rows = channels), so the score layout that
-// comes out of the first product is the operand layout the second needs, with
-// no lane exchange.  Token rows are assigned so that lane group g (lanes
-// 16g..16g+15) holds the 32 tokens 32g..32g+31 of a record; step t of the
-// value product uses tokens 32g + 8t + 0..7, exactly one dword of the
-// channel-major value row.
+// O^T = V^T . P'^T (A = value codes, rows = channels): both A operands are
+// 16-byte pieces of the record as stored (key rows, channel-major value rows).
+// The weights P' pass through LDS between the two products, stored in the
+// slot order of the value codes' nibbles.
 //
-// Work split: one workgroup (4 waves) per chunk of records of one KV head;
-// each wave takes every fourth record with its own online-softmax state; the
-// four states are combined in LDS and written as one fp32 partial
-// (m, l, acc[D]) in natural-log units, for the merge kernel.
+// Work split: one workgroup (4 waves) per chunk of consecutive records of one
+// KV head, the four waves sharing each record (see the kernel); one fp32
+// partial (m, l, acc[D]) per chunk and query head, m in natural-log units, for
+// the merge kernel.
 #include "kvq_mfma.h"
 
 namespace kvq {
@@ -83,21 +81,7 @@ __device__ __forceinline__ void qtilde_pair(uint32_t qh2, uint32_t ql2, uint32_t
 }
 
 // ---------------------------------------------------------------------------
-// Streaming kernel.  Each wave scans whole records with its own online-softmax
-// state and a private LDS staging area: 32 KB for one record's codes (stored
-// in the order the matrix-core operands are read back, so each 16-byte read
-// of a 1 KB slice is contiguous and free of bank conflicts) and two 2 KB areas
-// for scales.  Per record the wave copies the codes into registers, starts the
-// direct global->LDS loads of its next record into the same area, and computes
-// the current one from registers and the scale area while those loads land:
-// the next record's HBM latency hides behind this record's arithmetic, with
-// no workgroup barrier in the loop.  The four waves' states are combined in
-// LDS at the end into one partial per query head.
-
-constexpr int kCodeBytes = 32768;     // K and V codes of one 256-channel 4/4 record
-constexpr int kMetaBytes = 2048;      // C S Z of K and V
-constexpr int kWaveLds = kCodeBytes + 2 * kMetaBytes;
-
+// Direct global->LDS loads.
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -111,56 +95,74 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
 }
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
-
-// stage record `rec` into this wave's area: 16 key slices (block bb, half s),
-// 16 value slices (channel block cb), then the 2 KB of scales.
-__device__ __forceinline__ void stage(const uint8_t* __restrict__ rec, uint32_t codes, uint32_t meta, int lane) {
-  const int m = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int sl = 0; sl < 16; ++sl) {
-    const int bb = sl >> 1, s = sl & 1, t = bb >> 1, hh = bb & 1;
-    const int tok = 32 * (m >> 2) + 8 * t + 4 * hh + (m & 3);
-    dma16(rec + tok * 128 + 64 * s + 16 * g, codes + sl * 1024);
-  }
-#pragma unroll
-  for (int cb = 0; cb < 16; ++cb) dma16(rec + 16384 + (16 * cb + m) * 64 + 16 * g, codes + (16 + cb) * 1024);
-  dma16(rec + 32768 + 16 * lane, meta);
-  dma16(rec + 33792 + 16 * lane, meta + 1024);
-}
 
 __device__ __forceinline__ uint32_t pick(const uint4& v, int e) {
   return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
 }
 
-// One record from registers (codes) and LDS (scales).  acc[cb][i] holds
-// channel 16 cb + 4 g + i for query column q = lane & 15.  The query operands
-// already carry the softmax scale and log2(e): scores come out in log2 units.
-// m_run is the running maximum, l_part sums this lane's tokens.
-__device__ __forceinline__ void record_step(const uint4 (&kd)[8][2], const uint4 (&vd)[16], const uint8_t* km,
-                                            const uint4* qph, const uint4* qpl, int lane,
-                                            float& m_run, float& l_part, float4v* acc) {
-  const int g = lane >> 4;
-  const uint8_t* vm = km + 1024;
-  const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
-  // ---- S^T = K . Q~^T, q~ built per k-step as exact hi + lo
-  float4v sc[8];
+// ---------------------------------------------------------------------------
+// Cooperative kernel: the four waves of a workgroup share each record.
+//   q~:      wave w forms the q~ operands of k-steps 2w, 2w+1 and shares them;
+//   scores:  wave w takes token tiles 2w, 2w+1 (32 tokens) over all channels;
+//   values:  wave w takes channel tiles 4w..4w+3 (64 channels) over all tokens.
+// Records are staged in LDS by direct global->LDS loads into three areas, each
+// refilled as soon as its last reader is done, so that every load has about
+// half a record of work to land in:
+//   key codes    after the scores of record r      -> record r + 1
+//   value codes  after the value product of r       -> record r + 1
+//   scales (x2)  after the value product of r       -> record r + 2
+// Three barriers per record; per-wave state is small (16 accumulators), so
+// two workgroups share a compute unit and cover each other's waits.
+constexpr int kPPitch = 128 + 8;  // halves per weight row (padding spreads LDS banks)
+
+__device__ __forceinline__ void stage_keys(const uint8_t* __restrict__ rec, uint32_t buf, int wave, int lane) {
+  const int m = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int bb = 0; bb < 8; ++bb) sc[bb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < 4; ++j) {
+    const int sl = wave + 4 * j, bb = sl >> 1, s = sl & 1;  // slice 2 bb + s: tile bb, half s
+    dma16(rec + (16 * bb + m) * 128 + 64 * s + 16 * g, __builtin_amdgcn_readfirstlane(buf + sl * 1024));
+  }
+}
+__device__ __forceinline__ void stage_values(const uint8_t* __restrict__ rec, uint32_t buf, int wave, int lane) {
+  const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int cb = wave + 4 * j;
+    dma16(rec + 16384 + (16 * cb + m) * 64 + 16 * g, __builtin_amdgcn_readfirstlane(buf + cb * 1024));
+  }
+}
+__device__ __forceinline__ void stage_scales(const uint8_t* __restrict__ rec, uint32_t buf, int wave, int lane) {
+  if (wave < 2) dma16(rec + 32768 + wave * 1024 + 16 * lane, __builtin_amdgcn_readfirstlane(buf + wave * 1024));
+}
+__device__ __forceinline__ void wait_vm4() { __builtin_amdgcn_s_waitcnt(4 | (7 << 4) | (15 << 8)); }
+
+// position of token T in a weight row: the value product's k-step t of lane
+// group g takes tokens 32 g + 8 t + [0, 4, 1, 5, 2, 6, 3, 7] in its 8 slots
+__device__ __forceinline__ int wpos(int T) {
+  const int i = T & 7;
+  return (T & ~7) + (i < 4 ? 2 * i : 2 * (i - 4) + 1);
+}
+
+// q~ operands (hi, lo) of k-steps 2 wave, 2 wave + 1 from the key scales C,
+// and this wave's part of sigma = sum q~
+__device__ __forceinline__ void make_qtilde(const uint8_t* km, const uint4 (&qph)[2], const uint4 (&qpl)[2],
+                                            uint4 (*qt)[2][64], float (*xs)[16], int wave, int lane) {
+  const int g = lane >> 4;
+  const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
   float a1 = 0.0f, a16 = 0.0f;
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    const int s = kk >> 2, e = kk & 3;
+  for (int i = 0; i < 2; ++i) {
+    const int kk = 2 * wave + i, s = kk >> 2, e = kk & 3;
     const uint4 c = *(const uint4*)(km + 2 * (128 * s + 32 * g + 8 * e));
     const uint32_t c04 = __builtin_amdgcn_perm(c.z, c.x, 0x05040100u);
     const uint32_t c15 = __builtin_amdgcn_perm(c.z, c.x, 0x07060302u);
     const uint32_t c26 = __builtin_amdgcn_perm(c.w, c.y, 0x05040100u);
     const uint32_t c37 = __builtin_amdgcn_perm(c.w, c.y, 0x07060302u);
     uint4 hi, lo;
-    qtilde_pair(qph[kk].x, qpl[kk].x, c04, hi.x, lo.x);
-    qtilde_pair(qph[kk].y, qpl[kk].y, c15, hi.y, lo.y);
-    qtilde_pair(qph[kk].z, qpl[kk].z, c26, hi.z, lo.z);
-    qtilde_pair(qph[kk].w, qpl[kk].w, c37, hi.w, lo.w);
+    qtilde_pair(qph[i].x, qpl[i].x, c04, hi.x, lo.x);
+    qtilde_pair(qph[i].y, qpl[i].y, c15, hi.y, lo.y);
+    qtilde_pair(qph[i].z, qpl[i].z, c26, hi.z, lo.z);
+    qtilde_pair(qph[i].w, qpl[i].w, c37, hi.w, lo.w);
     a1 = __builtin_amdgcn_fdot2(as_h2(hi.x), ones, a1, false);
     a1 = __builtin_amdgcn_fdot2(as_h2(lo.x), ones, a1, false);
     a16 = __builtin_amdgcn_fdot2(as_h2(hi.y), ones, a16, false);
@@ -169,103 +171,21 @@ __device__ __forceinline__ void record_step(const uint4 (&kd)[8][2], const uint4
     a1 = __builtin_amdgcn_fdot2(as_h2(lo.z), ones, a1, false);
     a16 = __builtin_amdgcn_fdot2(as_h2(hi.w), ones, a16, false);
     a16 = __builtin_amdgcn_fdot2(as_h2(lo.w), ones, a16, false);
-    const half8 bh = mfma_a(hi), bl = mfma_a(lo);
-    half8 av[8];
-#pragma unroll
-    for (int bb = 0; bb < 8; ++bb) av[bb] = nib8_centred(pick(kd[bb][s], e));
-#pragma unroll
-    for (int bb = 0; bb < 8; ++bb) sc[bb] = mfma16(av[bb], bh, sc[bb]);
-#pragma unroll
-    for (int bb = 0; bb < 8; ++bb) sc[bb] = mfma16(av[bb], bl, sc[bb]);
+    qt[kk][0][lane] = hi;
+    qt[kk][1][lane] = lo;
   }
-  a1 = xsum4(a1);
-  a16 = xsum4(a16);
-  const float sig = a1 + 16.0f * a16;  // sum of q~ over the channels
-
-  // ---- scores S_i M_i + (Z_i + 8 S_i) sigma
-  float mx = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint4 skv = *(const uint4*)(km + 512 + 2 * (32 * g + 8 * t));
-    const uint4 zkv = *(const uint4*)(km + 768 + 2 * (32 * g + 8 * t));
-#pragma unroll
-    for (int k8 = 0; k8 < 8; ++k8) {
-      const float S = (float)as_h2(pick(skv, k8 >> 1))[k8 & 1];
-      const float Z = (float)as_h2(pick(zkv, k8 >> 1))[k8 & 1];
-      const int bb = 2 * t + (k8 >> 2), i = k8 & 3;
-      const float v = fmaf(S, sc[bb][i], fmaf(8.0f, S, Z) * sig);
-      sc[bb][i] = v;
-      mx = fmaxf(mx, v);
-    }
-  }
-  mx = xmax4(mx);
-  const float m_new = fmaxf(m_run, mx);
-  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-  m_run = m_new;
-  if (alpha != 1.0f) {
-#pragma unroll
-    for (int cb = 0; cb < 16; ++cb) acc[cb] *= alpha;
-  }
-  l_part *= alpha;
-
-  // ---- P' = p S^V in operand order, as hi + lo; zero-point term sum p (Z^V + 8 S^V)
-  half8 pbh[4], pbl[4];
-  float zt = 0.0f;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint4 sv = *(const uint4*)(vm + 512 + 2 * (32 * g + 8 * t));
-    const uint4 zv = *(const uint4*)(vm + 768 + 2 * (32 * g + 8 * t));
-    float x[8];
-#pragma unroll
-    for (int k8 = 0; k8 < 8; ++k8) {
-      const _Float16 S = as_h2(pick(sv, k8 >> 1))[k8 & 1];
-      const _Float16 Z = as_h2(pick(zv, k8 >> 1))[k8 & 1];
-      const float p = __builtin_amdgcn_exp2f(sc[2 * t + (k8 >> 2)][k8 & 3] - m_new);  // argument <= 0
-      l_part += p;
-      zt = fmaf(p, fmaf(8.0f, (float)S, (float)Z), zt);
-      x[k8] = p * (float)S;
-    }
-    // slot order [0, 4, 1/16 x 1, 1/16 x 5, 2, 6, 1/16 x 3, 1/16 x 7]
-    uint4 h, l;
-    split_h2(x[0], x[4], h.x, l.x);
-    split_h2(x[1] * 0.0625f, x[5] * 0.0625f, h.y, l.y);
-    split_h2(x[2], x[6], h.z, l.z);
-    split_h2(x[3] * 0.0625f, x[7] * 0.0625f, h.w, l.w);
-    pbh[t] = mfma_a(h);
-    pbl[t] = mfma_a(l);
-  }
-  const float corr = xsum4(zt);
-
-  // ---- O^T = V^T . P'^T, four channel blocks at a time, folded into acc with C^V
-#pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4) {
-    float4v o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const half8 av = nib8_centred(pick(vd[4 * c4 + j], t));
-        o[j] = mfma16(av, pbh[t], o[j]);
-        o[j] = mfma16(av, pbl[t], o[j]);
-      }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int cb = 4 * c4 + j;
-      const uint2 cv = *(const uint2*)(vm + 2 * (16 * cb + 4 * g));
-      const half2v c01 = as_h2(cv.x), c23 = as_h2(cv.y);
-      acc[cb][0] = fmaf((float)c01[0], o[j][0] + corr, acc[cb][0]);
-      acc[cb][1] = fmaf((float)c01[1], o[j][1] + corr, acc[cb][1]);
-      acc[cb][2] = fmaf((float)c23[0], o[j][2] + corr, acc[cb][2]);
-      acc[cb][3] = fmaf((float)c23[1], o[j][3] + corr, acc[cb][3]);
-    }
-  }
+  const float part = xsum4(a1) + 16.0f * xsum4(a16);
+  if (g == 0) xs[wave][lane & 15] = part;
 }
 
-__global__ __launch_bounds__(256) void decode_body_stream_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * kWaveLds];
-  __shared__ float xm[4][16], xl[4][16];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_body_coop_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[16 * 1024];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[16 * 1024];
+  __shared__ __attribute__((aligned(1024))) uint8_t mbuf[2][2048];
+  __shared__ uint4 qt[8][2][64];
+  __shared__ __attribute__((aligned(16))) uint16_t pw[2][16][kPPitch];  // P' hi, lo [query][token slot]
+  __shared__ float xm[4][16], xz[4][16], xs[4][16];
 
   const Layout& y = a.y;
   const DecodeSeq sq = a.seq[blockIdx.z];
@@ -276,73 +196,169 @@ __global__ __launch_bounds__(256) void decode_body_stream_kernel(DecodeArgs a) {
   const int q16 = lane & 15, g = lane >> 4;
   const int G = a.g;
 
-  // ---- rotated query operands (hi, lo), prepared once per call
-  uint4 qph[8], qpl[8];
-  const uint4* qo = a.qops + ((int64_t)blockIdx.z * y.H + h) * kQopsPerHead;
+  uint4 qph[2], qpl[2];  // this wave's k-steps of the prepared query
+  {
+    const uint4* qo = a.qops + ((int64_t)blockIdx.z * y.H + h) * kQopsPerHead;
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    qph[kk] = qo[kk * 64 + lane];
-    qpl[kk] = qo[(8 + kk) * 64 + lane];
+    for (int i = 0; i < 2; ++i) {
+      qph[i] = qo[(2 * wave + i) * 64 + lane];
+      qpl[i] = qo[(8 + 2 * wave + i) * 64 + lane];
+    }
   }
-
-  // ---- this wave's records: r0 + wave, r0 + wave + 4, ...
-  uint8_t* mine = lds + wave * kWaveLds;
-  const uint32_t codes_lds = lds_addr(mine);
-  const uint32_t meta_lds[2] = {lds_addr(mine + kCodeBytes), lds_addr(mine + kCodeBytes + kMetaBytes)};
   const int r0 = cbk * a.rec_per_chunk;
   const int r1 = min(sq.n_rec, r0 + a.rec_per_chunk);
+  const uint8_t* rec0 = a.arena + rec_off(y, sq.slot, a.layer, h, 0);
+  const uint32_t kb_lds = lds_addr(kbuf), vb_lds = lds_addr(vbuf);
+  const uint32_t mb_lds[2] = {lds_addr(mbuf[0]), lds_addr(mbuf[1])};
   float m_run = -INFINITY, l_part = 0.0f;
-  float4v acc[16];
+  float4v acc[4];
 #pragma unroll
-  for (int cb = 0; cb < 16; ++cb) acc[cb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+  for (int i = 0; i < 4; ++i) acc[i] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 
-  int r = r0 + wave;
-  if (r < r1) stage(a.arena + rec_off(y, sq.slot, a.layer, h, r), codes_lds, meta_lds[0], lane);
-  for (int it = 0; r < r1; ++it, r += 4) {
-    wait_vm0();
-    uint4 kd[8][2], vd[16];
-#pragma unroll
-    for (int sl = 0; sl < 16; ++sl) kd[sl >> 1][sl & 1] = *(const uint4*)(mine + sl * 1024 + 16 * lane);
-#pragma unroll
-    for (int cb = 0; cb < 16; ++cb) vd[cb] = *(const uint4*)(mine + (16 + cb) * 1024 + 16 * lane);
-    wait_lgkm0();
-    if (r + 4 < r1) stage(a.arena + rec_off(y, sq.slot, a.layer, h, r + 4), codes_lds, meta_lds[(it + 1) & 1], lane);
-    record_step(kd, vd, mine + kCodeBytes + (it & 1) * kMetaBytes, qph, qpl, lane, m_run, l_part, acc);
-  }
-
-  // ---- combine the four waves (codes areas reused as scratch)
-  const float lsum = xsum4(l_part);
-  if (g == 0) {
-    xm[wave][q16] = m_run;
-    xl[wave][q16] = lsum;
-  }
+  // ---- prologue: record r0 whole, q~ of r0, scales of r0 + 1
+  stage_scales(rec0 + (int64_t)r0 * y.rec_bytes, mb_lds[0], wave, lane);
+  stage_keys(rec0 + (int64_t)r0 * y.rec_bytes, kb_lds, wave, lane);
+  stage_values(rec0 + (int64_t)r0 * y.rec_bytes, vb_lds, wave, lane);
+  wait_vm0();
   __syncthreads();
-  const float M = fmaxf(fmaxf(xm[0][q16], xm[1][q16]), fmaxf(xm[2][q16], xm[3][q16]));
-  const float f = m_run == -INFINITY ? 0.0f : exp2f(m_run - M);
-  float4v* wacc = (float4v*)lds;   // [wave][cb][lane]
+  make_qtilde(mbuf[0], qph, qpl, qt, xs, wave, lane);
+  __syncthreads();
+  if (r0 + 1 < r1) stage_scales(rec0 + (int64_t)(r0 + 1) * y.rec_bytes, mb_lds[1], wave, lane);
+
+  for (int r = r0, it = 0; r < r1; ++r, ++it) {
+    const uint8_t* km = mbuf[it & 1];
+    const uint8_t* vm = km + 1024;
+    const bool more = r + 1 < r1;
+
+    // ---- scores of tiles 2 wave, 2 wave + 1
+    uint4 kd[2][2];
 #pragma unroll
-  for (int cb = 0; cb < 16; ++cb) wacc[(wave * 16 + cb) * 64 + lane] = acc[cb] * f;
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) kd[i][s] = *(const uint4*)(kbuf + (2 * (2 * wave + i) + s) * 1024 + 16 * lane);
+    float4v sc[2] = {(float4v){0.0f, 0.0f, 0.0f, 0.0f}, (float4v){0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int s = kk >> 2, e = kk & 3;
+      const half8 bh = mfma_a(qt[kk][0][lane]), bl = mfma_a(qt[kk][1][lane]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const half8 av = nib8_centred(pick(kd[i][s], e));
+        sc[i] = mfma16(av, bh, sc[i]);
+        sc[i] = mfma16(av, bl, sc[i]);
+      }
+    }
+    const float sig = xs[0][q16] + xs[1][q16] + xs[2][q16] + xs[3][q16];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int T = 16 * (2 * wave + i) + 4 * g;  // tokens T .. T + 3 of this lane
+      const uint2 sk = *(const uint2*)(km + 512 + 2 * T);
+      const uint2 zk = *(const uint2*)(km + 768 + 2 * T);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float S = (float)as_h2(j < 2 ? sk.x : sk.y)[j & 1];
+        const float Z = (float)as_h2(j < 2 ? zk.x : zk.y)[j & 1];
+        const float v = fmaf(S, sc[i][j], fmaf(8.0f, S, Z) * sig);
+        sc[i][j] = v;
+        mx = fmaxf(mx, v);
+      }
+    }
+    mx = xmax4(mx);
+    if (g == 0) xm[wave][q16] = mx;
+    __syncthreads();  // (B2) record maxima; key codes and q~ are free
+    if (more) stage_keys(rec0 + (int64_t)(r + 1) * y.rec_bytes, kb_lds, wave, lane);
+
+    const float mrec = fmaxf(fmaxf(xm[0][q16], xm[1][q16]), fmaxf(xm[2][q16], xm[3][q16]));
+    const float m_new = fmaxf(m_run, mrec);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first record
+    m_run = m_new;
+    if (alpha != 1.0f) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= alpha;
+    }
+    l_part *= alpha;
+    float zt = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int T = 16 * (2 * wave + i) + 4 * g;
+      const uint2 sv = *(const uint2*)(vm + 512 + 2 * T);
+      const uint2 zv = *(const uint2*)(vm + 768 + 2 * T);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float S = (float)as_h2(j < 2 ? sv.x : sv.y)[j & 1];
+        const float Z = (float)as_h2(j < 2 ? zv.x : zv.y)[j & 1];
+        const float p = __builtin_amdgcn_exp2f(sc[i][j] - m_new);  // argument <= 0
+        l_part += p;
+        zt = fmaf(p, fmaf(8.0f, S, Z), zt);
+        const int Tj = T + j;
+        float x = p * S;
+        if (Tj & 1) x *= 0.0625f;  // slots of high nibbles carry 1/16
+        const uint16_t xh = f2h_bits(x);
+        const uint16_t xl = f2h_bits(x - h2f(xh));
+        const int pos = wpos(Tj);
+        pw[0][q16][pos] = xh;
+        pw[1][q16][pos] = xl;
+      }
+    }
+    zt = xsum4(zt);
+    if (g == 0) xz[wave][q16] = zt;
+    if (more)
+      wait_vm4();  // value codes of r and scales of r + 1 in; the 4 key loads of r + 1 may fly
+    else
+      wait_vm0();
+    __syncthreads();  // (B3) weights, zero-point sums, value codes of r, scales of r + 1
+    if (more) make_qtilde(mbuf[(it + 1) & 1], qph, qpl, qt, xs, wave, lane);
+
+    const float corr = xz[0][q16] + xz[1][q16] + xz[2][q16] + xz[3][q16];
+    half8 pbh[4], pbl[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      pbh[t] = mfma_a(*(const uint4*)&pw[0][q16][32 * g + 8 * t]);
+      pbl[t] = mfma_a(*(const uint4*)&pw[1][q16][32 * g + 8 * t]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cb = 4 * wave + j;
+      const uint4 vd = *(const uint4*)(vbuf + cb * 1024 + 16 * lane);
+      float4v o = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const half8 av = nib8_centred(pick(vd, t));
+        o = mfma16(av, pbh[t], o);
+        o = mfma16(av, pbl[t], o);
+      }
+      const uint2 cv = *(const uint2*)(vm + 2 * (16 * cb + 4 * g));
+      const half2v c01 = as_h2(cv.x), c23 = as_h2(cv.y);
+      acc[j][0] = fmaf((float)c01[0], o[0] + corr, acc[j][0]);
+      acc[j][1] = fmaf((float)c01[1], o[1] + corr, acc[j][1]);
+      acc[j][2] = fmaf((float)c23[0], o[2] + corr, acc[j][2]);
+      acc[j][3] = fmaf((float)c23[1], o[3] + corr, acc[j][3]);
+    }
+    wait_vm0();       // key codes of r + 1
+    __syncthreads();  // (B1) record r done everywhere; key codes and q~ of r + 1 in
+    if (more) stage_values(rec0 + (int64_t)(r + 1) * y.rec_bytes, vb_lds, wave, lane);
+    if (r + 2 < r1) stage_scales(rec0 + (int64_t)(r + 2) * y.rec_bytes, mb_lds[it & 1], wave, lane);
+  }
+
+  // ---- partial of this chunk: every wave holds the same m; l sums over waves
+  const float lsum = xsum4(l_part);
+  if (g == 0) xm[wave][q16] = lsum;
   __syncthreads();
   if (q16 < G) {
     const int c = 1 + sq.n_ring_chunks + cbk;
     float* P = a.part + (((int64_t)blockIdx.z * a.Hq + h * G + q16) * a.max_chunks + c) * (256 + 2);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int cb = 4 * wave + k;
-      const float4v s4 = wacc[(0 * 16 + cb) * 64 + lane] + wacc[(1 * 16 + cb) * 64 + lane] +
-                         wacc[(2 * 16 + cb) * 64 + lane] + wacc[(3 * 16 + cb) * 64 + lane];
-      const int ch = 16 * cb + 4 * g;
-      P[2 + ch + 0] = s4[0];
-      P[2 + ch + 1] = s4[1];
-      P[2 + ch + 2] = s4[2];
-      P[2 + ch + 3] = s4[3];
+    for (int j = 0; j < 4; ++j) {
+      const int ch = 16 * (4 * wave + j) + 4 * g;
+      P[2 + ch + 0] = acc[j][0];
+      P[2 + ch + 1] = acc[j][1];
+      P[2 + ch + 2] = acc[j][2];
+      P[2 + ch + 3] = acc[j][3];
     }
     if (wave == 0 && g == 0) {
-      float L = 0.0f;
-      for (int w = 0; w < 4; ++w)
-        if (xm[w][q16] != -INFINITY) L += xl[w][q16] * exp2f(xm[w][q16] - M);
-      P[0] = M * kLn2;
-      P[1] = L;
+      P[0] = m_run * kLn2;
+      P[1] = xm[0][q16] + xm[1][q16] + xm[2][q16] + xm[3][q16];
     }
   }
 }
@@ -350,7 +366,7 @@ __global__ __launch_bounds__(256) void decode_body_stream_kernel(DecodeArgs a) {
 hipError_t launch_decode_mfma(const DecodeArgs& a, int grid_x, hipStream_t stream) {
   if (a.y.D != 256 || a.y.kbits != 4 || a.y.vbits != 4) return hipErrorInvalidValue;
   dim3 grid(grid_x, a.y.H, a.n_seqs);
-  hipLaunchKernelGGL(decode_body_stream_kernel, grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(decode_body_coop_kernel, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -122,11 +122,12 @@ static int ring_chunk_tokens(const Layout& y) {
   return kGroup * (int)std::max<int64_t>(1, (y.cap / kGroup + 1023) / 1024);
 }
 static int valu_rec_per_chunk(const Layout& y) { return std::max(1, (y.max_rec + 2999) / 3000); }
-// Matrix-core path: one workgroup per compute unit (the kernel's LDS staging
-// takes most of a CU), each streaming about total / n_cu records, at least one
-// per wave.
+// Matrix-core body path: two workgroups per compute unit, each streaming
+// about total / (2 n_cu) records.
+static constexpr int kBodyWgPerCu = 2;
 static int mfma_rec_per_chunk(int64_t total_records, int n_cu) {
-  return (int)std::max<int64_t>(4, (total_records + n_cu - 1) / n_cu);
+  const int64_t wgs = (int64_t)kBodyWgPerCu * n_cu;
+  return (int)std::max<int64_t>(1, (total_records + wgs - 1) / wgs);
 }
 static int device_cu_count() {
   int dev = 0, n = 0;
@@ -206,7 +207,7 @@ kvq_status kvq_cache_create(const kvq_config* cfg, void* device_arena, size_t ar
   c->arena = plan_only ? nullptr : (uint8_t*)device_arena;
   c->plan_only = plan_only;
   c->path = KVQ_PATH_AUTO;
-  c->n_cu = 0;
+  c->n_cu = plan_only ? 0 : device_cu_count();  // sizes the matrix-core body chunks
   fill_signs(*cfg, c->signs);
   c->n_tok.assign((size_t)y.S * y.L, 0);
   c->n_rec.assign((size_t)y.S * y.L, 0);
@@ -324,11 +325,17 @@ kvq_status kvq_seal(kvq_cache* c, int32_t layer, int32_t mode, void* stream, int
 }
 
 static int max_chunks_bound(const kvq_cache* c) {
-  // the smallest chunks any path uses: 128-token ring chunks, and at most 4
-  // records per body chunk
+  // the most chunks any path makes: 128-token ring chunks; body chunks of the
+  // vector-ALU path, or of the matrix-core path, whose chunk size grows with
+  // the record total so that a sequence gets at most 2 n_cu / H + 1 of them
   const int rc = std::min(ring_chunk_tokens(c->y), kStagedRingChunk);
-  const int rpc = std::min(valu_rec_per_chunk(c->y), 4);
-  return 1 + (c->y.cap + rc - 1) / rc + (c->y.max_rec + rpc - 1) / rpc;
+  const int rpc = valu_rec_per_chunk(c->y);
+  int body = (c->y.max_rec + rpc - 1) / rpc;
+  if (mfma_supported(c->y)) {
+    const int n_cu = c->n_cu ? c->n_cu : 256;
+    body = std::max(body, std::min(c->y.max_rec, (kBodyWgPerCu * n_cu + c->y.H - 1) / c->y.H + 1));
+  }
+  return 1 + (c->y.cap + rc - 1) / rc + body;
 }
 
 kvq_status kvq_workspace_bytes(const kvq_cache* c, int32_t n_seqs, size_t* bytes) {
@@ -365,7 +372,6 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
     if (c->tok(seq_ids[i], layer) < 1) return fail(KVQ_ERR_INVALID, "sequence %d holds no tokens", seq_ids[i]);
     total_rec += c->rec(seq_ids[i], layer) * c->y.H;
   }
-  if (use_mfma && c->n_cu == 0) c->n_cu = device_cu_count();
   const int rpc = use_mfma ? mfma_rec_per_chunk(total_rec, c->n_cu) : valu_rec_per_chunk(c->y);
   std::vector<DecodeSeq> plan(n_seqs);
   int max_chunks = 1;

@@ -9,7 +9,7 @@
 // with the unrotated query.
 //
 // Work split: chunk 0 of a sequence is its sink; then ring chunks of
-// ring_chunk tokens; then body chunks of rec_per_chunk records.  Each
+// ring_chunk tokens; then body chunks (the records split evenly).  Each
 // workgroup handles one chunk of one KV head for its g query heads and writes
 // an fp32 partial (m, l, acc[D]): m the largest score, l = sum exp(s - m),
 // acc = sum exp(s - m) v (in the rotated domain, except for chunk 0).
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   __shared__ float ms[kMaxGroup], lsum[kMaxGroup], al[kMaxGroup];
 
   const Layout& y = a.y;
-  const int c = a.chunk_base + blockIdx.x;
+  const int c = blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   const DecodeSeq sq = a.seq[b];
   if (c >= sq.n_chunks) return;
@@ -97,9 +97,9 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     t_begin = (c - 1) * a.ring_chunk;
     t_end = min(sq.ring_len, t_begin + a.ring_chunk);
   } else {
-    const int cb = c - 1 - sq.n_ring_chunks;
-    t_begin = cb * a.rec_per_chunk * kGroup;
-    t_end = min(sq.n_rec, (cb + 1) * a.rec_per_chunk) * kGroup;
+    const int cb = c - 1 - sq.n_ring_chunks;  // records split evenly over the body chunks
+    t_begin = (int)((int64_t)cb * sq.n_rec / sq.n_body_chunks) * kGroup;
+    t_end = (int)((int64_t)(cb + 1) * sq.n_rec / sq.n_body_chunks) * kGroup;
   }
 
   float acc[kMaxGroup][CPT];
@@ -213,64 +213,90 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   }
 }
 
+// Merge of the split-K partials of one query head (grid Hq x n_seqs): one
+// softmax over all chunks, R^T applied to the rotated part (chunks 1..), the
+// sink part (chunk 0) added as is, divided by the total weight.  The four
+// waves split the chunks; each lane owns D / 64 channels.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  constexpr int VPL = D / 64;
   __shared__ float wts[kMaxChunks];
-  __shared__ float red[256];
-  __shared__ float rot[D];
-  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  __shared__ float red[4][D];
+  __shared__ float rm[8];
+  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = a.n_chunks[b];
   const float* P = a.part + ((int64_t)b * a.Hq + hq) * a.max_chunks * (D + 2);
 
   float mx = -INFINITY;
   for (int c = tid; c < n; c += 256) mx = fmaxf(mx, P[(int64_t)c * (D + 2)]);
-  red[tid] = mx;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  if (lane == 0) rm[wave] = mx;
   __syncthreads();
-  for (int st = 128; st > 0; st >>= 1) {
-    if (tid < st) red[tid] = fmaxf(red[tid], red[tid + st]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
+  const float M = fmaxf(fmaxf(rm[0], rm[1]), fmaxf(rm[2], rm[3]));
   float ls = 0.0f;
   for (int c = tid; c < n; c += 256) {
     const float w = expf(P[(int64_t)c * (D + 2)] - M);
     wts[c] = w;
     ls += w * P[(int64_t)c * (D + 2) + 1];
   }
-  red[tid] = ls;
-  __syncthreads();
-  for (int st = 128; st > 0; st >>= 1) {
-    if (tid < st) red[tid] += red[tid + st];
-    __syncthreads();
-  }
-  const float L = red[0];
-  constexpr int CPT = (D + 255) / 256;
-  float sinkp[CPT];
 #pragma unroll
-  for (int q = 0; q < CPT; ++q) {
-    const int j = tid + 256 * q;
-    sinkp[q] = 0.0f;
-    if (j < D) {
-      float ar = 0.0f;
-      for (int c = 1; c < n; ++c) ar = fmaf(wts[c], P[(int64_t)c * (D + 2) + 2 + j], ar);
-      rot[j] = ar;
-      sinkp[q] = wts[0] * P[2 + j];
+  for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o, 64);
+  if (lane == 0) rm[4 + wave] = ls;
+  __syncthreads();
+  const float L = rm[4] + rm[5] + rm[6] + rm[7];
+
+  // weighted sum of the rotated partials (chunks 1..n-1)
+  float v[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) v[i] = 0.0f;
+#pragma unroll 4
+  for (int c = 1 + wave; c < n; c += 4) {
+    const float w = wts[c];
+    const float2* row = (const float2*)(P + (int64_t)c * (D + 2) + 2 + VPL * lane);  // 8-byte aligned
+#pragma unroll
+    for (int i = 0; i < VPL / 2; ++i) {
+      const float2 x = row[i];
+      v[2 * i] = fmaf(w, x.x, v[2 * i]);
+      v[2 * i + 1] = fmaf(w, x.y, v[2 * i + 1]);
     }
   }
-  __syncthreads();
-  lds_rotate<D>(rot, a.signs, true);
 #pragma unroll
-  for (int q = 0; q < CPT; ++q) {
-    const int j = tid + 256 * q;
-    if (j < D) {
-      const float o = (rot[j] + sinkp[q]) / L;
-      const int64_t oi = ((int64_t)b * a.Hq + hq) * D + j;
-      if (a.out_f16)
-        ((uint16_t*)a.out)[oi] = f2h_bits(o);
-      else
-        ((float*)a.out)[oi] = o;
+  for (int i = 0; i < VPL; ++i) red[wave][VPL * lane + i] = v[i];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int j = VPL * lane + i;
+    v[i] = red[0][j] + red[1][j] + red[2][j] + red[3][j];
+  }
+  // R^T: head_dim 128: s1 . H . s2 / sqrt(128); 256 and 512: H_256 / 16 per 256-block
+  if (D == 128) {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (sign_neg(a.signs, 128 + VPL * lane + i)) v[i] = -v[i];
+    wave_fwht<VPL, 128>(v, lane);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      v[i] *= (float)kInvSqrt128;
+      if (sign_neg(a.signs, VPL * lane + i)) v[i] = -v[i];
     }
+  } else {
+    wave_fwht<VPL, 256>(v, lane);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) v[i] *= 0.0625f;
+  }
+  const float w0 = wts[0];
+  const float inv_l = 1.0f / L;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int j = VPL * lane + i;
+    const float o = fmaf(w0, P[2 + j], v[i]) * inv_l;
+    const int64_t oi = ((int64_t)b * a.Hq + hq) * D + j;
+    if (a.out_f16)
+      ((uint16_t*)a.out)[oi] = f2h_bits(o);
+    else
+      ((float*)a.out)[oi] = o;
   }
 }
 

@@ -38,4 +38,31 @@ __device__ __forceinline__ bool sign_neg(const uint32_t* signs, int i) {
   return (signs[i >> 5] >> (i & 31)) & 1u;
 }
 
+// In-register Walsh-Hadamard transform of size N over one wave: lane l holds
+// the VPL consecutive elements VPL l .. VPL l + VPL - 1 (N / VPL lanes per
+// transform, so a wave holds 64 VPL / N independent transforms).  Butterflies
+// of stride < VPL stay in the lane; larger strides pair lane l with l ^ (st / VPL).
+template <int VPL, int N>
+__device__ __forceinline__ void wave_fwht(float (&v)[VPL], int lane) {
+#pragma unroll
+  for (int st = 1; st < N; st <<= 1) {
+    if (st < VPL) {
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (!(i & st)) {
+          const float x = v[i], y = v[i + st];
+          v[i] = x + y;
+          v[i + st] = x - y;
+        }
+    } else {
+      const bool upper = (lane & (st / VPL)) != 0;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const float o = __shfl_xor(v[i], st / VPL, 64);
+        v[i] = upper ? o - v[i] : v[i] + o;
+      }
+    }
+  }
+}
+
 }  // namespace kvq

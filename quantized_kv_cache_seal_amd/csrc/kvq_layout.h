@@ -79,7 +79,7 @@ struct DecodeSeq {
   int32_t ring_len;  // tokens in the ring
   int32_t ring0;     // ring slot of the oldest unsealed token
   int32_t n_rec;     // sealed records
-  int32_t n_ring_chunks, n_body_chunks, n_chunks;
+  int32_t n_ring_chunks, n_body_chunks, n_chunks;  // body chunks split the records evenly
 };
 
 struct DecodeArgs {
@@ -87,10 +87,10 @@ struct DecodeArgs {
   Layout y;
   const uint16_t* q;  // fp16 [n_seqs][Hq][D]
   float* part;        // [n_seqs][Hq][max_chunks][D + 2]: m, l, acc[D]
-  uint4* qops;        // [n_seqs][H][3 sets][2 (hi, lo)][8][64]: query in matrix-core operand order
   float scale;
-  int32_t layer, Hq, g, n_seqs, max_chunks, ring_chunk, rec_per_chunk;
-  int32_t chunk_base;  // first chunk index this launch covers (0 for sink/ring launch)
+  int32_t layer, Hq, g, n_seqs, max_chunks;
+  int32_t ring_chunk;    // ring tokens per chunk
+  int32_t n_body_items;  // matrix-core launch: work items before the sink/ring items
   int32_t valu_regions;  // bit r set: the vector-ALU kernel scans region r (0 sink, 1 ring, 2 body)
   uint32_t signs[8];
   DecodeSeq seq[kMaxLaunchSeqs];

@@ -16,15 +16,6 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Query operands prepared once per decode call for each (sequence, KV head):
-// three sets of (hi, lo) fp16 halves x up to 8 k-steps x 64 lanes (uint4 each),
-// all multiplied by the softmax scale and log2(e).
-//   set 0: rotated query in the 4-bit body's nibble order (head_dim 256 only)
-//   set 1: rotated query, natural channel order (staging ring)
-//   set 2: unrotated query, natural channel order (fp16 sink)
-constexpr int kQopsSet = 2 * 8 * 64;
-constexpr int kQopsPerHead = 3 * kQopsSet;
-
 __device__ __forceinline__ half8 mfma_a(const uint4& u) {
   half8 h;
   __builtin_memcpy(&h, &u, 16);

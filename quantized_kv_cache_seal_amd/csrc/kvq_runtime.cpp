@@ -6,6 +6,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -19,9 +20,8 @@ namespace kvq {
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_seal(const SealArgs& a, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs& a, int grid_x, hipStream_t stream);
-hipError_t launch_decode_mfma(const DecodeArgs& a, int grid_x, hipStream_t stream);
-hipError_t launch_decode_qprep(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_decode_staged(const DecodeArgs& a, int grid_x, hipStream_t stream);
+hipError_t launch_decode_main(const DecodeArgs& a, int n_items, hipStream_t stream);
+hipError_t launch_decode_ring(const DecodeArgs& a, int n_items, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 }  // namespace kvq
 
@@ -116,33 +116,52 @@ static Layout make_layout(const kvq_config& c) {
   return y;
 }
 
-// Split-K plan: tokens per ring chunk and records per body chunk, sized so a
-// sequence never has more than kMaxChunks partials.
+// Split-K plan.  Vector-ALU path: ring chunks of a multiple of 128 tokens and
+// body chunks of a fixed number of records, sized so that a sequence never has
+// more than kMaxChunks partials.
 static int ring_chunk_tokens(const Layout& y) {
   return kGroup * (int)std::max<int64_t>(1, (y.cap / kGroup + 1023) / 1024);
 }
 static int valu_rec_per_chunk(const Layout& y) { return std::max(1, (y.max_rec + 2999) / 3000); }
-// Matrix-core body path: two workgroups per compute unit, each streaming
-// about total / (2 n_cu) records.
-static constexpr int kBodyWgPerCu = 2;
-static int mfma_rec_per_chunk(int64_t total_records, int n_cu) {
-  const int64_t wgs = (int64_t)kBodyWgPerCu * n_cu;
-  return (int)std::max<int64_t>(1, (total_records + wgs - 1) / wgs);
-}
 static int device_cu_count() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     return 256;
   return n;
 }
-// bytes of rotated-query operands per (sequence, KV head) in the workspace
-static constexpr size_t kQopsBytes = 3 * 2 * 8 * 64 * 16;  // query operand sets per (sequence, KV head)
+// matrix-core body scan (fused with the sink and ring): head_dim 256, 4-bit K and V
 static bool mfma_supported(const Layout& y) { return y.D == 256 && y.kbits == 4 && y.vbits == 4; }
-// matrix-core sink and ring scan: head_dim 128 or 256, 128-token ring chunks
+// matrix-core sink and ring scan on its own: head_dim 128 or 256
 static bool staged_supported(const Layout& y) { return y.D == 128 || y.D == 256; }
-static constexpr int kStagedRingChunk = 128;
+static constexpr int kRingStep = 64;         // tokens per step of the matrix-core sink/ring scan
+static constexpr int kStagedRingChunk = 256; // ring tokens per chunk next to a vector-ALU body scan
+static constexpr int kBodyWgPerCu = 2;       // resident workgroups per CU of the fused kernel
 
-static DecodeSeq plan_seq(const kvq_cache* c, int s, int layer, int rc, int rpc) {
+// Matrix-core plan.  Work in units of one record (about one 64-token ring step
+// or half a sink).  Body chunks are sized to the average work per resident
+// workgroup and issued first; ring chunks are half that size and fill the
+// remaining slots in two rounds.
+struct MfmaPlan {
+  int ring_chunk;
+  double body_target;  // records per body chunk
+};
+static MfmaPlan mfma_plan(const kvq_cache* c, const std::vector<int64_t>& n_rec, const std::vector<int64_t>& ring) {
+  const int H = c->y.H;
+  double body = 0, other = 0;
+  for (size_t i = 0; i < n_rec.size(); ++i) {
+    body += (double)H * n_rec[i];
+    other += (double)H * ((ring[i] + kRingStep - 1) / kRingStep + 2);
+  }
+  const double slots = (double)kBodyWgPerCu * (c->n_cu ? c->n_cu : 256);
+  const double per = std::max(1.0, (body + other) / slots);
+  MfmaPlan p;
+  p.ring_chunk = kRingStep * std::max(1, (int)(per / 2));
+  const double body_slots = std::max(1.0, slots - std::ceil(other / per));
+  p.body_target = std::max(1.0, body / body_slots);
+  return p;
+}
+
+static DecodeSeq plan_seq(const kvq_cache* c, int s, int layer, int rc, int n_body_chunks) {
   DecodeSeq d{};
   d.slot = s;
   const int64_t nt = c->tok(s, layer);
@@ -151,7 +170,7 @@ static DecodeSeq plan_seq(const kvq_cache* c, int s, int layer, int rc, int rpc)
   d.ring_len = (int32_t)c->ring_len(s, layer);
   d.ring0 = (int32_t)(((int64_t)kGroup * d.n_rec) % c->y.cap);
   d.n_ring_chunks = (d.ring_len + rc - 1) / rc;
-  d.n_body_chunks = (d.n_rec + rpc - 1) / rpc;
+  d.n_body_chunks = n_body_chunks;
   d.n_chunks = 1 + d.n_ring_chunks + d.n_body_chunks;
   return d;
 }
@@ -325,10 +344,11 @@ kvq_status kvq_seal(kvq_cache* c, int32_t layer, int32_t mode, void* stream, int
 }
 
 static int max_chunks_bound(const kvq_cache* c) {
-  // the most chunks any path makes: 128-token ring chunks; body chunks of the
-  // vector-ALU path, or of the matrix-core path, whose chunk size grows with
-  // the record total so that a sequence gets at most 2 n_cu / H + 1 of them
-  const int rc = std::min(ring_chunk_tokens(c->y), kStagedRingChunk);
+  // the most chunks any path makes: ring chunks of at least 64 tokens; body
+  // chunks of the vector-ALU path, or of the matrix-core path, whose records
+  // per chunk grow with the record total so that a sequence gets at most
+  // 2 n_cu / H + 1 of them
+  const int rc = std::min(ring_chunk_tokens(c->y), kRingStep);
   const int rpc = valu_rec_per_chunk(c->y);
   int body = (c->y.max_rec + rpc - 1) / rpc;
   if (mfma_supported(c->y)) {
@@ -340,8 +360,7 @@ static int max_chunks_bound(const kvq_cache* c) {
 
 kvq_status kvq_workspace_bytes(const kvq_cache* c, int32_t n_seqs, size_t* bytes) {
   if (!c || !bytes || n_seqs < 0) return fail(KVQ_ERR_INVALID, "bad arguments");
-  *bytes = (size_t)n_seqs * c->cfg.n_q_heads * max_chunks_bound(c) * (c->y.D + 2) * sizeof(float) + 256 +
-           (size_t)n_seqs * c->y.H * kQopsBytes;
+  *bytes = (size_t)n_seqs * c->cfg.n_q_heads * max_chunks_bound(c) * (c->y.D + 2) * sizeof(float);
   return KVQ_OK;
 }
 
@@ -364,26 +383,37 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
   if (!q || !out || !workspace) return fail(KVQ_ERR_INVALID, "q, out and workspace must be non-NULL");
   const bool use_mfma = c->path != KVQ_PATH_VALU && mfma_supported(c->y);
   const bool staged = c->path != KVQ_PATH_VALU && staged_supported(c->y);
-  const int rc = staged ? kStagedRingChunk : ring_chunk_tokens(c->y);
   if (c->path == KVQ_PATH_MFMA && !use_mfma)
     return fail(KVQ_ERR_UNSUPPORTED, "matrix-core body scan needs head_dim 256 with 4-bit K and V");
-  int64_t total_rec = 0;
+  std::vector<int64_t> n_rec(n_seqs), ring(n_seqs);
   for (int i = 0; i < n_seqs; ++i) {
     if (c->tok(seq_ids[i], layer) < 1) return fail(KVQ_ERR_INVALID, "sequence %d holds no tokens", seq_ids[i]);
-    total_rec += c->rec(seq_ids[i], layer) * c->y.H;
+    n_rec[i] = c->rec(seq_ids[i], layer);
+    ring[i] = c->ring_len(seq_ids[i], layer);
   }
-  const int rpc = use_mfma ? mfma_rec_per_chunk(total_rec, c->n_cu) : valu_rec_per_chunk(c->y);
+  int rc;
+  MfmaPlan mp{};
+  if (use_mfma) {
+    mp = mfma_plan(c, n_rec, ring);
+    rc = mp.ring_chunk;
+  } else {
+    rc = staged ? kStagedRingChunk : ring_chunk_tokens(c->y);
+  }
+  const int valu_rpc = valu_rec_per_chunk(c->y);
   std::vector<DecodeSeq> plan(n_seqs);
   int max_chunks = 1;
   for (int i = 0; i < n_seqs; ++i) {
-    plan[i] = plan_seq(c, seq_ids[i], layer, rc, rpc);
+    int nb;
+    if (use_mfma)
+      nb = n_rec[i] == 0 ? 0 : (int)std::min<int64_t>(n_rec[i], std::max<int64_t>(1, std::llround(n_rec[i] / mp.body_target)));
+    else
+      nb = (int)((n_rec[i] + valu_rpc - 1) / valu_rpc);
+    plan[i] = plan_seq(c, seq_ids[i], layer, rc, nb);
     max_chunks = std::max(max_chunks, plan[i].n_chunks);
   }
   if (max_chunks > kMaxChunks) return fail(KVQ_ERR_CAPACITY, "too many split-K chunks");
   const int Hq = c->cfg.n_q_heads, D = c->y.D;
-  const size_t part_bytes = (size_t)n_seqs * Hq * max_chunks * (D + 2) * sizeof(float);
-  const size_t qops_off = (part_bytes + 255) / 256 * 256;
-  const size_t need = qops_off + (size_t)n_seqs * c->y.H * kQopsBytes;
+  const size_t need = (size_t)n_seqs * Hq * max_chunks * (D + 2) * sizeof(float);
   if (ws_bytes < need) return fail(KVQ_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   const size_t out_elem = out_dtype == KVQ_OUT_F16 ? 2 : 4;
   for (int b0 = 0; b0 < n_seqs; b0 += kMaxLaunchSeqs) {
@@ -393,41 +423,34 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
     a.n_seqs = std::min(kMaxLaunchSeqs, n_seqs - b0);
     a.q = (const uint16_t*)q + (int64_t)b0 * Hq * D;
     a.part = (float*)workspace + (int64_t)b0 * Hq * max_chunks * (D + 2);
-    a.qops = (uint4*)((uint8_t*)workspace + qops_off) + (int64_t)b0 * c->y.H * (kQopsBytes / 16);
     a.scale = scale;
     a.layer = layer;
     a.Hq = Hq;
     a.g = Hq / c->y.H;
     a.max_chunks = max_chunks;
     a.ring_chunk = rc;
-    a.rec_per_chunk = rpc;
-    a.chunk_base = 0;
     std::memcpy(a.signs, c->signs, sizeof a.signs);
     // regions left to the vector-ALU kernel: bit 0 sink, 1 ring, 2 body
     a.valu_regions = (staged ? 0 : 3) | (use_mfma ? 0 : 4);
-    int grid_valu = 0, grid_ring = 1, grid_body = 0;
+    int grid_valu = 0, n_body_items = 0, n_ring_items = 0;
     for (int b = 0; b < a.n_seqs; ++b) {
       a.seq[b] = plan[b0 + b];
-      grid_ring = std::max(grid_ring, 1 + a.seq[b].n_ring_chunks);
-      grid_body = std::max(grid_body, a.seq[b].n_body_chunks);
+      n_body_items += c->y.H * a.seq[b].n_body_chunks;
+      n_ring_items += c->y.H * (1 + a.seq[b].n_ring_chunks);
       grid_valu = std::max(grid_valu, (a.valu_regions & 4) ? a.seq[b].n_chunks : 1 + a.seq[b].n_ring_chunks);
     }
     hipError_t e = hipSuccess;
-    if (staged || use_mfma) {
-      e = launch_decode_qprep(a, (hipStream_t)stream);
-      if (e != hipSuccess) return hip_fail(e, "query preparation launch");
-    }
-    if (staged) {
-      e = launch_decode_staged(a, grid_ring, (hipStream_t)stream);
-      if (e != hipSuccess) return hip_fail(e, "sink/ring decode launch");
-    }
-    if (a.valu_regions != 0) {
+    if (use_mfma) {
+      a.n_body_items = n_body_items;
+      e = launch_decode_main(a, n_body_items + n_ring_items, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e, "decode launch");
+    } else {
+      if (staged) {
+        e = launch_decode_ring(a, n_ring_items, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "sink/ring decode launch");
+      }
       e = launch_decode_valu(a, grid_valu, (hipStream_t)stream);
       if (e != hipSuccess) return hip_fail(e, "decode launch");
-    }
-    if (use_mfma && grid_body > 0) {
-      e = launch_decode_mfma(a, grid_body, (hipStream_t)stream);
-      if (e != hipSuccess) return hip_fail(e, "body decode launch");
     }
     MergeArgs m{};
     m.part = a.part;

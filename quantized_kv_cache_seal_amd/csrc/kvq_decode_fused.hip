@@ -103,25 +103,6 @@ __device__ __forceinline__ void qtilde_pair(uint32_t qh2, uint32_t ql2, uint32_t
 }
 
 // ---------------------------------------------------------------------------
-// Direct global->LDS loads
-
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u8*)p);
-}
-
-// one 16-byte direct global->LDS load per lane: LDS[m0 + 16 lane] <- *src.
-// Issued as inline assembly so that the compiler does not add a wait for it in
-// front of every later LDS read; completion is awaited explicitly.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
-}
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); }
-__device__ __forceinline__ void wait_vm4() { __builtin_amdgcn_s_waitcnt(4 | (7 << 4) | (15 << 8)); }
-__device__ __forceinline__ void wait_vm5() { __builtin_amdgcn_s_waitcnt(5 | (7 << 4) | (15 << 8)); }
-
-// ---------------------------------------------------------------------------
 // Query rows: the G query heads of KV head h, times scale * log2(e), rotated
 // (R = H/16 for head_dim 256, s2 . H . s1 / sqrt(128) for 128) or not, into
 // rows[16][D] of LDS (rows G..15 zero).  Wave w transforms rows w, w + 4, ...
@@ -164,44 +145,25 @@ __device__ __forceinline__ void query_rows(const DecodeArgs& a, int b, int h, bo
 //   q~:      wave w forms the q~ operands of k-steps 2w, 2w+1 and shares them;
 //   scores:  wave w takes token tiles 2w, 2w+1 (32 tokens) over all channels;
 //   values:  wave w takes channel tiles 4w..4w+3 (64 channels) over all tokens.
-// Records are staged by direct global->LDS loads into three areas, each
-// refilled as soon as its last reader is done, so that every load has about
-// half a record of work to land in:
-//   key codes    after the scores of record r      -> record r + 1
-//   value codes  after the value product of r       -> record r + 1
-//   scales (x2)  after the value product of r       -> record r + 2
-// Three barriers per record.  Key slices hold 16 token rows x 64 bytes in
-// lane order (tile bb, half s of the row), value slices 16 channel rows x 64
-// bytes; each lane then reads its 16-byte operand piece without bank conflicts.
+// Key and value codes go from memory straight into the registers of the lane
+// that feeds them to the matrix cores (16 bytes per lane and operand), each
+// set reloaded as soon as its product is done, so that it has the other half
+// of a record's work to land in.  The 2 KB of scales pass through a ring of
+// three LDS areas, loaded two records ahead.  Two barriers per record:
+//   (B2) after the scores: record maxima exchanged;
+//   (B3) after the weights: P', the zero-point sums, q~ and scales of the next
+//        record exchanged.
+// Token rows are assigned so that the four score rows of a lane are four
+// consecutive slots of the value product's operand order (one 8-byte store of
+// the weights per tile): position P of a tile holds token
+// (P & ~7) + [0, 4, 1, 5, 2, 6, 3, 7][P & 7].
 constexpr int kPPitch = 128 + 8;  // halves per weight row (padding spreads LDS banks)
-constexpr int kBodyK = 0, kBodyV = 16384, kBodyM = 32768, kBodyQt = 36864, kBodyPw = 53248, kBodyX = 61952;
+constexpr int kBodyQt = 0, kBodyPw = 16384, kBodyM = kBodyPw + 2 * 16 * kPPitch * 2, kBodyX = kBodyM + 3 * 2048;
 constexpr int kBodyLds = kBodyX + 3 * 256;
+static_assert(16 * 256 * 4 == 8 * 2 * 64 * 16, "query rows must fit the q~ area");
 
-__device__ __forceinline__ void stage_keys(const uint8_t* __restrict__ rec, uint32_t buf, int wave, int lane) {
-  const int m = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int sl = wave + 4 * j, bb = sl >> 1, s = sl & 1;
-    dma16(rec + (16 * bb + m) * 128 + 64 * s + 16 * g, __builtin_amdgcn_readfirstlane(buf + sl * 1024));
-  }
-}
-__device__ __forceinline__ void stage_values(const uint8_t* __restrict__ rec, uint32_t buf, int wave, int lane) {
-  const int m = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int cb = wave + 4 * j;
-    dma16(rec + 16384 + (16 * cb + m) * 64 + 16 * g, __builtin_amdgcn_readfirstlane(buf + cb * 1024));
-  }
-}
-__device__ __forceinline__ void stage_scales(const uint8_t* __restrict__ rec, uint32_t buf, int wave, int lane) {
-  if (wave < 2) dma16(rec + 32768 + wave * 1024 + 16 * lane, __builtin_amdgcn_readfirstlane(buf + wave * 1024));
-}
-
-// position of token T in a weight row: the value product's k-step t of lane
-// group g takes tokens 32 g + 8 t + [0, 4, 1, 5, 2, 6, 3, 7] in its 8 slots
-__device__ __forceinline__ int wpos(int T) {
-  const int i = T & 7;
-  return (T & ~7) + (i < 4 ? 2 * i : 2 * (i - 4) + 1);
+__device__ __forceinline__ int slot_token(int p) {  // token at position p (0..7) of an 8-token group
+  return (p >> 1) + 4 * (p & 1);
 }
 
 // q~ operands (hi, lo) of k-steps 2 wave, 2 wave + 1 from the key scales C,
@@ -239,17 +201,29 @@ __device__ __forceinline__ void make_qtilde(const uint8_t* km, const uint4 (&qph
   if (g == 0) xs[wave][lane & 15] = part;
 }
 
+__device__ __forceinline__ void load_keys(const uint8_t* __restrict__ rec, uint4 (&kd)[2][2], int wave, int lane) {
+  const int m = lane & 15, g = lane >> 4;
+  const int row = (m & 8) + slot_token(m & 7);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) kd[i][s] = *(const uint4*)(rec + (16 * (2 * wave + i) + row) * 128 + 64 * s + 16 * g);
+}
+__device__ __forceinline__ void load_values(const uint8_t* __restrict__ rec, uint4 (&vd)[4], int wave, int lane) {
+  const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) vd[j] = *(const uint4*)(rec + 16384 + (16 * (4 * wave + j) + m) * 64 + 16 * g);
+}
+
 __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int cbk, uint8_t* smem) {
   const Layout& y = a.y;
   const DecodeSeq& sq = a.seq[b];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int q16 = lane & 15, g = lane >> 4;
   const int G = a.g;
-  uint8_t* kbuf = smem + kBodyK;
-  uint8_t* vbuf = smem + kBodyV;
-  uint8_t* mbuf[2] = {smem + kBodyM, smem + kBodyM + 2048};
   uint4(*qt)[2][64] = (uint4(*)[2][64])(smem + kBodyQt);
   uint16_t(*pw)[16][kPPitch] = (uint16_t(*)[16][kPPitch])(smem + kBodyPw);
+  uint8_t* mbuf = smem + kBodyM;  // [3][2048] scales of records r, r + 1, r + 2 (mod 3)
   float(*xm)[16] = (float(*)[16])(smem + kBodyX);
   float(*xz)[16] = (float(*)[16])(smem + kBodyX + 256);
   float(*xs)[16] = (float(*)[16])(smem + kBodyX + 512);
@@ -258,13 +232,17 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
   const int r0 = (int)((int64_t)cbk * sq.n_rec / sq.n_body_chunks);
   const int r1 = (int)((int64_t)(cbk + 1) * sq.n_rec / sq.n_body_chunks);
   const uint8_t* rec0 = a.arena + rec_off(y, sq.slot, a.layer, h, 0);
-  const uint32_t kb_lds = lds_addr(kbuf), vb_lds = lds_addr(vbuf);
-  const uint32_t mb_lds[2] = {lds_addr(mbuf[0]), lds_addr(mbuf[1])};
+  auto rec = [&](int r) { return rec0 + (int64_t)r * y.rec_bytes; };
+  auto mslot = [&](int r) { return mbuf + ((r - r0) % 3) * 2048; };
 
-  // ---- prologue: keys and scales of r0 in flight while the query is rotated
-  stage_scales(rec0 + (int64_t)r0 * y.rec_bytes, mb_lds[0], wave, lane);
-  stage_keys(rec0 + (int64_t)r0 * y.rec_bytes, kb_lds, wave, lane);
-  float* rows = (float*)vbuf;  // 16 x 256 floats, before the value codes arrive
+  // ---- prologue: scales of r0, r0 + 1 and the key codes of r0 in flight while
+  // the query is rotated (its rows borrow the q~ area, 16 x 256 floats)
+  uint2 m0 = *(const uint2*)(rec(r0) + 32768 + 8 * tid);
+  uint2 m1 = make_uint2(0, 0);
+  if (r0 + 1 < r1) m1 = *(const uint2*)(rec(r0 + 1) + 32768 + 8 * tid);
+  uint4 kd[2][2], vd[4];
+  load_keys(rec(r0), kd, wave, lane);
+  float* rows = (float*)qt;
   query_rows<256>(a, b, h, true, rows, wave, lane);
   __syncthreads();
   uint4 qph[2], qpl[2];  // this wave's k-steps of q' in the nibble slot order
@@ -281,16 +259,13 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
     qph[i] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
     qpl[i] = make_uint4(lb[0], lb[1], lb[2], lb[3]);
   }
+  *(uint2*)(mslot(r0) + 8 * tid) = m0;
+  if (r0 + 1 < r1) *(uint2*)(mslot(r0 + 1) + 8 * tid) = m1;
   __syncthreads();
-  const bool more0 = r0 + 1 < r1;
-  stage_values(rec0 + (int64_t)r0 * y.rec_bytes, vb_lds, wave, lane);
-  if (more0) stage_scales(rec0 + (int64_t)(r0 + 1) * y.rec_bytes, mb_lds[1], wave, lane);
-  if (wave < 2 && more0)
-    wait_vm5();  // scales and keys of r0 in; values of r0 and scales of r0 + 1 may fly
-  else
-    wait_vm4();
-  __syncthreads();
-  make_qtilde(mbuf[0], qph, qpl, qt, xs, wave, lane);
+  make_qtilde(mslot(r0), qph, qpl, qt, xs, wave, lane);
+  uint2 mnext = make_uint2(0, 0);  // scales two records ahead
+  if (r0 + 2 < r1) mnext = *(const uint2*)(rec(r0 + 2) + 32768 + 8 * tid);
+  load_values(rec(r0), vd, wave, lane);
   __syncthreads();
 
   float m_run = -INFINITY, l_part = 0.0f;
@@ -298,49 +273,53 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int r = r0, it = 0; r < r1; ++r, ++it) {
-    const uint8_t* km = mbuf[it & 1];
+  for (int r = r0; r < r1; ++r) {
+    const uint8_t* km = mslot(r);
     const uint8_t* vm = km + 1024;
     const bool more = r + 1 < r1;
 
-    // ---- scores of tiles 2 wave, 2 wave + 1
-    uint4 kd[2][2];
+    // ---- scores of tiles 2 wave, 2 wave + 1: four independent accumulation
+    // chains (tile x hi/lo) keep the matrix core busy between dependent products
+    float4v sh[2], sl[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) kd[i][s] = *(const uint4*)(kbuf + (2 * (2 * wave + i) + s) * 1024 + 16 * lane);
-    float4v sc[2] = {(float4v){0.0f, 0.0f, 0.0f, 0.0f}, (float4v){0.0f, 0.0f, 0.0f, 0.0f}};
+    for (int i = 0; i < 2; ++i) sh[i] = sl[i] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const int s = kk >> 2, e = kk & 3;
       const half8 bh = mfma_a(qt[kk][0][lane]), bl = mfma_a(qt[kk][1][lane]);
+      half8 av[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const half8 av = nib8_centred(pick(kd[i][s], e));
-        sc[i] = mfma16(av, bh, sc[i]);
-        sc[i] = mfma16(av, bl, sc[i]);
-      }
+      for (int i = 0; i < 2; ++i) av[i] = nib8_centred(pick(kd[i][s], e));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) sh[i] = mfma16(av[i], bh, sh[i]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) sl[i] = mfma16(av[i], bl, sl[i]);
     }
+    float4v sc[2] = {sh[0] + sl[0], sh[1] + sl[1]};
     const float sig = xs[0][q16] + xs[1][q16] + xs[2][q16] + xs[3][q16];
+    // this lane's rows are positions 16 bb + 4 g + j: tokens base + {0,4,1,5}
+    // (g even) or base + {2,6,3,7} (g odd), base = 16 bb + 8 (g / 2)
+    const int tb = 8 * (g >> 1) + 2 * (g & 1);
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int T = 16 * (2 * wave + i) + 4 * g;  // tokens T .. T + 3 of this lane
-      const uint2 sk = *(const uint2*)(km + 512 + 2 * T);
-      const uint2 zk = *(const uint2*)(km + 768 + 2 * T);
+      const int T = 16 * (2 * wave + i) + tb;
+      const uint32_t s01 = *(const uint32_t*)(km + 512 + 2 * T), s45 = *(const uint32_t*)(km + 512 + 2 * T + 8);
+      const uint32_t z01 = *(const uint32_t*)(km + 768 + 2 * T), z45 = *(const uint32_t*)(km + 768 + 2 * T + 8);
+      const half2v S0 = as_h2(s01), S1 = as_h2(s45), Z0 = as_h2(z01), Z1 = as_h2(z45);
+      const float Sj[4] = {(float)S0[0], (float)S1[0], (float)S0[1], (float)S1[1]};
+      const float Zj[4] = {(float)Z0[0], (float)Z1[0], (float)Z0[1], (float)Z1[1]};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float S = (float)as_h2(j < 2 ? sk.x : sk.y)[j & 1];
-        const float Z = (float)as_h2(j < 2 ? zk.x : zk.y)[j & 1];
-        const float v = fmaf(S, sc[i][j], fmaf(8.0f, S, Z) * sig);
+        const float v = fmaf(Sj[j], sc[i][j], fmaf(8.0f, Sj[j], Zj[j]) * sig);
         sc[i][j] = v;
         mx = fmaxf(mx, v);
       }
     }
     mx = xmax4(mx);
     if (g == 0) xm[wave][q16] = mx;
-    __syncthreads();  // (B2) record maxima; key codes and q~ are free
-    if (more) stage_keys(rec0 + (int64_t)(r + 1) * y.rec_bytes, kb_lds, wave, lane);
+    __syncthreads();  // (B2) record maxima; q~ of r and the key codes are free
+    if (more) load_keys(rec(r + 1), kd, wave, lane);
 
     const float mrec = fmaxf(fmaxf(xm[0][q16], xm[1][q16]), fmaxf(xm[2][q16], xm[3][q16]));
     const float m_new = fmaxf(m_run, mrec);
@@ -354,34 +333,34 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
     float zt = 0.0f;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int T = 16 * (2 * wave + i) + 4 * g;
-      const uint2 sv = *(const uint2*)(vm + 512 + 2 * T);
-      const uint2 zv = *(const uint2*)(vm + 768 + 2 * T);
+      const int T = 16 * (2 * wave + i) + tb;
+      const uint32_t s01 = *(const uint32_t*)(vm + 512 + 2 * T), s45 = *(const uint32_t*)(vm + 512 + 2 * T + 8);
+      const uint32_t z01 = *(const uint32_t*)(vm + 768 + 2 * T), z45 = *(const uint32_t*)(vm + 768 + 2 * T + 8);
+      const half2v S0 = as_h2(s01), S1 = as_h2(s45), Z0 = as_h2(z01), Z1 = as_h2(z45);
+      const float Sj[4] = {(float)S0[0], (float)S1[0], (float)S0[1], (float)S1[1]};
+      const float Zj[4] = {(float)Z0[0], (float)Z1[0], (float)Z0[1], (float)Z1[1]};
+      float x[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float S = (float)as_h2(j < 2 ? sv.x : sv.y)[j & 1];
-        const float Z = (float)as_h2(j < 2 ? zv.x : zv.y)[j & 1];
         const float p = __builtin_amdgcn_exp2f(sc[i][j] - m_new);  // argument <= 0
         l_part += p;
-        zt = fmaf(p, fmaf(8.0f, S, Z), zt);
-        const int Tj = T + j;
-        float x = p * S;
-        if (Tj & 1) x *= 0.0625f;  // slots of high nibbles carry 1/16
-        const uint16_t xh = f2h_bits(x);
-        const uint16_t xl = f2h_bits(x - h2f(xh));
-        const int pos = wpos(Tj);
-        pw[0][q16][pos] = xh;
-        pw[1][q16][pos] = xl;
+        zt = fmaf(p, fmaf(8.0f, Sj[j], Zj[j]), zt);
+        x[j] = p * Sj[j];
       }
+      x[2] *= 0.0625f;  // odd tokens sit in the high nibbles: their slots carry 1/16
+      x[3] *= 0.0625f;
+      uint2 hi, lo;
+      split_h2(x[0], x[1], hi.x, lo.x);
+      split_h2(x[2], x[3], hi.y, lo.y);
+      *(uint2*)&pw[0][q16][16 * (2 * wave + i) + 4 * g] = hi;
+      *(uint2*)&pw[1][q16][16 * (2 * wave + i) + 4 * g] = lo;
     }
     zt = xsum4(zt);
     if (g == 0) xz[wave][q16] = zt;
-    if (more)
-      wait_vm4();  // value codes of r and scales of r + 1 in; the 4 key loads of r + 1 may fly
-    else
-      wait_vm0();
-    __syncthreads();  // (B3) weights, zero-point sums, value codes of r, scales of r + 1
-    if (more) make_qtilde(mbuf[(it + 1) & 1], qph, qpl, qt, xs, wave, lane);
+    if (more) make_qtilde(mslot(r + 1), qph, qpl, qt, xs, wave, lane);
+    if (r + 2 < r1) *(uint2*)(mslot(r + 2) + 8 * tid) = mnext;
+    if (r + 3 < r1) mnext = *(const uint2*)(rec(r + 3) + 32768 + 8 * tid);
+    __syncthreads();  // (B3) weights, zero-point sums; q~ and scales of r + 1, r + 2
 
     const float corr = xz[0][q16] + xz[1][q16] + xz[2][q16] + xz[3][q16];
     half8 pbh[4], pbl[4];
@@ -390,28 +369,30 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
       pbh[t] = mfma_a(*(const uint4*)&pw[0][q16][32 * g + 8 * t]);
       pbl[t] = mfma_a(*(const uint4*)&pw[1][q16][32 * g + 8 * t]);
     }
+    float4v o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {  // four channel tiles as independent chains
+      half8 av[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) av[j] = nib8_centred(pick(vd[j], t));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = mfma16(av[j], pbh[t], o[j]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = mfma16(av[j], pbl[t], o[j]);
+    }
+    if (more) load_values(rec(r + 1), vd, wave, lane);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int cb = 4 * wave + j;
-      const uint4 vd = *(const uint4*)(vbuf + cb * 1024 + 16 * lane);
-      float4v o = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const half8 av = nib8_centred(pick(vd, t));
-        o = mfma16(av, pbh[t], o);
-        o = mfma16(av, pbl[t], o);
-      }
       const uint2 cv = *(const uint2*)(vm + 2 * (16 * cb + 4 * g));
       const half2v c01 = as_h2(cv.x), c23 = as_h2(cv.y);
-      acc[j][0] = fmaf((float)c01[0], o[0] + corr, acc[j][0]);
-      acc[j][1] = fmaf((float)c01[1], o[1] + corr, acc[j][1]);
-      acc[j][2] = fmaf((float)c23[0], o[2] + corr, acc[j][2]);
-      acc[j][3] = fmaf((float)c23[1], o[3] + corr, acc[j][3]);
+      acc[j][0] = fmaf((float)c01[0], o[j][0] + corr, acc[j][0]);
+      acc[j][1] = fmaf((float)c01[1], o[j][1] + corr, acc[j][1]);
+      acc[j][2] = fmaf((float)c23[0], o[j][2] + corr, acc[j][2]);
+      acc[j][3] = fmaf((float)c23[1], o[j][3] + corr, acc[j][3]);
     }
-    wait_vm0();       // key codes of r + 1
-    __syncthreads();  // (B1) record r done everywhere; key codes and q~ of r + 1 in
-    if (more) stage_values(rec0 + (int64_t)(r + 1) * y.rec_bytes, vb_lds, wave, lane);
-    if (r + 2 < r1) stage_scales(rec0 + (int64_t)(r + 2) * y.rec_bytes, mb_lds[it & 1], wave, lane);
   }
 
   // ---- partial of this chunk: every wave holds the same m; l sums over waves
@@ -556,8 +537,8 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
   const int t_begin = sink ? 0 : (c - 1) * a.ring_chunk;
   const int t_end = sink ? sq.n_sink : min(sq.ring_len, c * a.ring_chunk);
 
-  RingRegs<D> cur;
-  if (!sink) ring_load<D>(a, sq, h, t_begin, t_end - t_begin, cur);
+  RingRegs<D> ra, rb;
+  if (!sink) ring_load<D>(a, sq, h, t_begin, t_end - t_begin, ra);
 
   // ---- query operands in natural channel order, rotated (ring) or not (sink),
   // kept in LDS: wave w forms k-steps w, w + 4, ...
@@ -583,9 +564,11 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
 #pragma unroll
   for (int i = 0; i < CPW; ++i) acc[i] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int t0 = t_begin; t0 < t_end; t0 += kStep) {
+  // one step over tokens t0 .. t0 + 63 from `cur`, loading the next step into
+  // `nxt`; called with the two register sets alternating, so no copy (and no
+  // early wait for the loads in flight) is needed
+  auto step = [&](int t0, const RingRegs<D>& cur, RingRegs<D>& nxt) {
     const int n = min(kStep, t_end - t0);
-    RingRegs<D> nxt;
     if (!sink && t0 + kStep < t_end) ring_load<D>(a, sq, h, t0 + kStep, t_end - t0 - kStep, nxt);
 
     // ---- (1) V^T
@@ -692,7 +675,10 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
       }
     }
     __syncthreads();  // V^T and the weights are free
-    cur = nxt;
+  };
+  for (int t0 = t_begin; t0 < t_end; t0 += 2 * kStep) {
+    step(t0, ra, rb);
+    if (t0 + kStep < t_end) step(t0 + kStep, rb, ra);
   }
 
   const float lsum = xsum4(l_part);

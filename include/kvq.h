@@ -188,6 +188,22 @@ kvq_status kvq_import(kvq_cache* cache, int32_t seq, int32_t layer, int32_t kv_h
 /* Size in bytes of one exported unit of a region.  bytes: host out. */
 kvq_status kvq_unit_bytes(const kvq_cache* cache, int32_t region, size_t* bytes);
 
+/* Profiling hook.  kvq_profile_start(cache, max_calls) allocates a small
+ * device buffer (2 timestamps per call) on the current device; each of the
+ * following kvq_attn_decode calls (up to max_calls of them) stamps, with the
+ * device wall clock, the start of the first workgroup and the end of the last
+ * workgroup of its main decode kernel: the fused sink/ring/body scan on the
+ * matrix-core path, the vector-ALU scan otherwise (the merge is not
+ * included).  The stamps cost two atomics per workgroup and add no launch or
+ * synchronisation to the stream.  kvq_profile_stop waits for the device,
+ * writes the kernel durations in microseconds to us[0 .. *n_calls - 1] (us
+ * may be NULL; otherwise it must hold max_calls floats), and frees the
+ * buffer.  Starting again discards an unfinished profile.  Not for use under
+ * graph capture.  Errors: KVQ_ERR_INVALID (bad arguments, stop without
+ * start), KVQ_ERR_UNSUPPORTED (plan-only cache), KVQ_ERR_DEVICE. */
+kvq_status kvq_profile_start(kvq_cache* cache, int32_t max_calls);
+kvq_status kvq_profile_stop(kvq_cache* cache, float* us, int32_t* n_calls);
+
 const char* kvq_status_string(kvq_status status);
 const char* kvq_last_error(void);
 

@@ -70,6 +70,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   const int c = blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   const DecodeSeq sq = a.seq[b];
+  prof_start(a.prof_ts);
   if (c >= sq.n_chunks) return;
   const int tid = threadIdx.x;
   const int g = a.g;
@@ -211,6 +212,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
       P[1] = lsum[i];
     }
   }
+  prof_end(a.prof_ts);
 }
 
 // Merge of the split-K partials of one query head (grid Hq x n_seqs): one

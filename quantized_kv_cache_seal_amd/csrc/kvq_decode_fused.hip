@@ -726,11 +726,13 @@ void decode_main_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kMainLds];
   int b, h, c;
   const int item = blockIdx.x;
+  prof_start(a.prof_ts);
   if (item < a.n_body_items) {
     if (find_item(a, item, true, b, h, c)) body_role(a, b, h, c, smem);
   } else {
     if (find_item(a, item - a.n_body_items, false, b, h, c)) ring_role<256>(a, b, h, c, smem);
   }
+  prof_end(a.prof_ts);
 }
 
 template <int D>

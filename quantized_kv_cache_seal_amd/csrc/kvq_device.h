@@ -34,6 +34,21 @@ __device__ __forceinline__ double shfl_xor_d(double x, int m) {
 __device__ __forceinline__ float shfl_xor_f(float x, int m) {
   return __shfl_xor(x, m, 64);
 }
+// Profiling stamps of a kernel by the device wall clock: the start of
+// workgroup 0, which the dispatcher launches first (one plain store: an atomic
+// from every workgroup at launch would contend on one address and hold up each
+// workgroup's first wait for memory), and the latest workgroup end (atomic
+// max from one lane, after the workgroup's work).
+__device__ __forceinline__ void prof_start(unsigned long long* ts) {
+  if (ts && threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    ts[0] = (unsigned long long)wall_clock64();
+}
+__device__ __forceinline__ void prof_end(unsigned long long* ts) {
+  if (ts) {
+    __syncthreads();
+    if (threadIdx.x == 0) atomicMax(&ts[1], (unsigned long long)wall_clock64());
+  }
+}
 __device__ __forceinline__ bool sign_neg(const uint32_t* signs, int i) {
   return (signs[i >> 5] >> (i & 31)) & 1u;
 }

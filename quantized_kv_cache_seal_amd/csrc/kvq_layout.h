@@ -93,6 +93,7 @@ struct DecodeArgs {
   int32_t n_body_items;  // matrix-core launch: work items before the sink/ring items
   int32_t valu_regions;  // bit r set: the vector-ALU kernel scans region r (0 sink, 1 ring, 2 body)
   uint32_t signs[8];
+  unsigned long long* prof_ts;  // profiling: {first start, last end} wall-clock stamps, or null
   DecodeSeq seq[kMaxLaunchSeqs];
 };
 

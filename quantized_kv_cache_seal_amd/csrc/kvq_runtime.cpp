@@ -35,6 +35,8 @@ struct kvq_cache {
   int32_t path;
   int32_t n_cu;
   uint32_t signs[8];
+  unsigned long long* prof_ts = nullptr;  // profiling: {start, end} wall-clock stamps per decode call
+  int32_t prof_n = 0, prof_used = 0;
   std::vector<int64_t> n_tok;  // [S * L]
   std::vector<int64_t> n_rec;  // [S * L]
   int64_t& tok(int s, int l) { return n_tok[(size_t)s * y.L + l]; }
@@ -234,7 +236,10 @@ kvq_status kvq_cache_create(const kvq_config* cfg, void* device_arena, size_t ar
   return KVQ_OK;
 }
 
+static void profile_clear(kvq_cache* c);
+
 kvq_status kvq_cache_destroy(kvq_cache* c) {
+  if (c) profile_clear(c);
   delete c;
   return KVQ_OK;
 }
@@ -440,13 +445,16 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
       grid_valu = std::max(grid_valu, (a.valu_regions & 4) ? a.seq[b].n_chunks : 1 + a.seq[b].n_ring_chunks);
     }
     hipError_t e = hipSuccess;
+    if (b0 == 0 && c->prof_used < c->prof_n) a.prof_ts = c->prof_ts + 2 * c->prof_used++;
     if (use_mfma) {
       a.n_body_items = n_body_items;
       e = launch_decode_main(a, n_body_items + n_ring_items, (hipStream_t)stream);
       if (e != hipSuccess) return hip_fail(e, "decode launch");
     } else {
       if (staged) {
-        e = launch_decode_ring(a, n_ring_items, (hipStream_t)stream);
+        DecodeArgs r = a;
+        r.prof_ts = nullptr;  // stamps belong to the main scan
+        e = launch_decode_ring(r, n_ring_items, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(e, "sink/ring decode launch");
       }
       e = launch_decode_valu(a, grid_valu, (hipStream_t)stream);
@@ -465,6 +473,51 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
     e = launch_merge(m, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
+  return KVQ_OK;
+}
+
+static void profile_clear(kvq_cache* c) {
+  if (c->prof_ts) (void)hipFree(c->prof_ts);
+  c->prof_ts = nullptr;
+  c->prof_n = c->prof_used = 0;
+}
+
+kvq_status kvq_profile_start(kvq_cache* c, int32_t max_calls) {
+  if (!c || max_calls < 1) return fail(KVQ_ERR_INVALID, "bad arguments");
+  if (c->plan_only) return fail(KVQ_ERR_UNSUPPORTED, "profiling a plan-only cache");
+  profile_clear(c);
+  std::vector<unsigned long long> init((size_t)2 * max_calls);
+  for (size_t i = 0; i < init.size(); i += 2) {
+    init[i] = 0;      // start of workgroup 0
+    init[i + 1] = 0;  // latest end: atomic max
+  }
+  hipError_t e = hipMalloc((void**)&c->prof_ts, init.size() * sizeof(unsigned long long));
+  if (e == hipSuccess) e = hipMemcpy(c->prof_ts, init.data(), init.size() * sizeof(unsigned long long), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    profile_clear(c);
+    return hip_fail(e, "profile buffer");
+  }
+  c->prof_n = max_calls;
+  return KVQ_OK;
+}
+
+kvq_status kvq_profile_stop(kvq_cache* c, float* us, int32_t* n_calls) {
+  if (!c || !n_calls) return fail(KVQ_ERR_INVALID, "bad arguments");
+  if (!c->prof_ts) return fail(KVQ_ERR_INVALID, "no profile started");
+  const int32_t n = c->prof_used;
+  std::vector<unsigned long long> ts((size_t)2 * std::max(n, 1));
+  int dev = 0, khz = 0;
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess && n > 0)
+    e = hipMemcpy(ts.data(), c->prof_ts, (size_t)2 * n * sizeof(unsigned long long), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+  profile_clear(c);
+  if (e != hipSuccess) return hip_fail(e, "profile read");
+  if (khz <= 0) return fail(KVQ_ERR_DEVICE, "device reports no wall clock rate");
+  for (int32_t i = 0; us && i < n; ++i)
+    us[i] = ts[2 * i + 1] >= ts[2 * i] ? (float)((double)(ts[2 * i + 1] - ts[2 * i]) * 1000.0 / khz) : 0.0f;
+  *n_calls = n;
   return KVQ_OK;
 }
 

@@ -23,7 +23,8 @@ FLAG_PLAN_ONLY = 1
 EXPORTS = [
     "kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_append", "kvq_seal",
     "kvq_workspace_bytes", "kvq_attn_decode", "kvq_set_decode_path", "kvq_seq_info", "kvq_seq_reset",
-    "kvq_seq_truncate", "kvq_export", "kvq_import", "kvq_unit_bytes", "kvq_status_string", "kvq_last_error",
+    "kvq_seq_truncate", "kvq_export", "kvq_import", "kvq_unit_bytes", "kvq_profile_start", "kvq_profile_stop",
+    "kvq_status_string", "kvq_last_error",
 ]
 
 
@@ -70,6 +71,8 @@ def lib():
             "kvq_export": [vp, i32, i32, i32, i32, i64, vp, sz, vp],
             "kvq_import": [vp, i32, i32, i32, i32, i64, vp, sz, vp],
             "kvq_unit_bytes": [vp, i32, P(sz)],
+            "kvq_profile_start": [vp, i32],
+            "kvq_profile_stop": [vp, P(ctypes.c_float), P(i32)],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -187,6 +190,19 @@ class Cache:
                                     ctypes.c_void_p(out.data_ptr()), OUT_F16 if out_f16 else OUT_F32,
                                     float(scale), ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream)))
         return out
+
+    def profile_start(self, max_calls: int):
+        """Record the duration of the main decode kernel of the next max_calls
+        attn_decode calls (HIP events on their stream)."""
+        self._prof_n = int(max_calls)
+        check(lib().kvq_profile_start(self.h, self._prof_n))
+
+    def profile_stop(self):
+        """Kernel durations in microseconds of the profiled calls."""
+        buf = (ctypes.c_float * self._prof_n)()
+        n = ctypes.c_int32()
+        check(lib().kvq_profile_stop(self.h, buf, ctypes.byref(n)))
+        return list(buf[:n.value])
 
     def set_decode_path(self, path: int):
         check(lib().kvq_set_decode_path(self.h, path))

@@ -27,6 +27,8 @@
 // of one KV head) first, then the sink and ring chunks of every KV head.
 // Each item writes one fp32 partial per query head; partial 0 is the sink,
 // 1.. the ring chunks, then the body chunks.
+#include <type_traits>
+
 #include "kvq_mfma.h"
 
 namespace kvq {
@@ -110,33 +112,49 @@ __device__ __forceinline__ void qtilde_pair(uint32_t qh2, uint32_t ql2, uint32_t
 template <int D>
 __device__ __forceinline__ void query_rows(const DecodeArgs& a, int b, int h, bool rotate, float* rows, int wave,
                                            int lane) {
-  constexpr int VPL = D / 64;
+  constexpr int VPL = D / 64, NR = kMaxGroup / 4;  // values per lane, rows per wave
+  static_assert(VPL % 2 == 0, "two fp16 per load");
   const float sl = a.scale * kLog2e;
-  for (int i = wave; i < kMaxGroup; i += 4) {
-    float v[VPL];
-    const bool live = i < a.g;
+  // all rows of this wave loaded at once (VPL fp16 per lane each), then transformed
+  uint32_t raw[NR][VPL / 2];
 #pragma unroll
-    for (int k = 0; k < VPL; ++k)
-      v[k] = live ? h2f(a.q[((int64_t)b * a.Hq + h * a.g + i) * D + VPL * lane + k]) * sl : 0.0f;
+  for (int k = 0; k < NR; ++k) {
+    const int i = wave + 4 * k;
+    const int ii = i < a.g ? i : 0;  // rows past the group read row 0 and are zeroed below
+    const uint32_t* src = (const uint32_t*)(a.q + ((int64_t)b * a.Hq + h * a.g + ii) * D + VPL * lane);
+#pragma unroll
+    for (int w = 0; w < VPL / 2; ++w) raw[k][w] = src[w];
+  }
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    const int i = wave + 4 * k;
+    const bool live = i < a.g;
+    float v[VPL];
+#pragma unroll
+    for (int w = 0; w < VPL / 2; ++w) {
+      const half2v x = as_h2(raw[k][w]);
+      v[2 * w] = live ? (float)x[0] * sl : 0.0f;
+      v[2 * w + 1] = live ? (float)x[1] * sl : 0.0f;
+    }
     if (rotate) {
       if (D == 128) {
 #pragma unroll
-        for (int k = 0; k < VPL; ++k)
-          if (sign_neg(a.signs, VPL * lane + k)) v[k] = -v[k];
+        for (int j = 0; j < VPL; ++j)
+          if (sign_neg(a.signs, VPL * lane + j)) v[j] = -v[j];
       }
       wave_fwht<VPL, D>(v, lane);
 #pragma unroll
-      for (int k = 0; k < VPL; ++k) {
+      for (int j = 0; j < VPL; ++j) {
         if (D == 128) {
-          v[k] *= (float)kInvSqrt128;
-          if (sign_neg(a.signs, 128 + VPL * lane + k)) v[k] = -v[k];
+          v[j] *= (float)kInvSqrt128;
+          if (sign_neg(a.signs, 128 + VPL * lane + j)) v[j] = -v[j];
         } else {
-          v[k] *= 0.0625f;
+          v[j] *= 0.0625f;
         }
       }
     }
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) rows[i * D + VPL * lane + k] = v[k];
+    for (int j = 0; j < VPL; ++j) rows[i * D + VPL * lane + j] = v[j];
   }
 }
 
@@ -201,18 +219,22 @@ __device__ __forceinline__ void make_qtilde(const uint8_t* km, const uint4 (&qph
   if (g == 0) xs[wave][lane & 15] = part;
 }
 
-__device__ __forceinline__ void load_keys(const uint8_t* __restrict__ rec, uint4 (&kd)[2][2], int wave, int lane) {
+// dummy: every lane reads the first 16 bytes of `rec` (one line, result unused)
+__device__ __forceinline__ void load_keys(const uint8_t* __restrict__ rec, uint4 (&kd)[2][2], int wave, int lane,
+                                          bool dummy = false) {
   const int m = lane & 15, g = lane >> 4;
   const int row = (m & 8) + slot_token(m & 7);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int s = 0; s < 2; ++s) kd[i][s] = *(const uint4*)(rec + (16 * (2 * wave + i) + row) * 128 + 64 * s + 16 * g);
+    for (int s = 0; s < 2; ++s)
+      kd[i][s] = *(const uint4*)(rec + (dummy ? 0 : (16 * (2 * wave + i) + row) * 128 + 64 * s + 16 * g));
 }
-__device__ __forceinline__ void load_values(const uint8_t* __restrict__ rec, uint4 (&vd)[4], int wave, int lane) {
+__device__ __forceinline__ void load_values(const uint8_t* __restrict__ rec, uint4 (&vd)[4], int wave, int lane,
+                                            bool dummy = false) {
   const int m = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) vd[j] = *(const uint4*)(rec + 16384 + (16 * (4 * wave + j) + m) * 64 + 16 * g);
+  for (int j = 0; j < 4; ++j) vd[j] = *(const uint4*)(rec + (dummy ? 0 : 16384 + (16 * (4 * wave + j) + m) * 64 + 16 * g));
 }
 
 __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int cbk, uint8_t* smem) {
@@ -238,8 +260,7 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
   // ---- prologue: scales of r0, r0 + 1 and the key codes of r0 in flight while
   // the query is rotated (its rows borrow the q~ area, 16 x 256 floats)
   uint2 m0 = *(const uint2*)(rec(r0) + 32768 + 8 * tid);
-  uint2 m1 = make_uint2(0, 0);
-  if (r0 + 1 < r1) m1 = *(const uint2*)(rec(r0 + 1) + 32768 + 8 * tid);
+  uint2 m1 = *(const uint2*)(r0 + 1 < r1 ? rec(r0 + 1) + 32768 + 8 * tid : rec0);
   uint4 kd[2][2], vd[4];
   load_keys(rec(r0), kd, wave, lane);
   float* rows = (float*)qt;
@@ -263,8 +284,7 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
   if (r0 + 1 < r1) *(uint2*)(mslot(r0 + 1) + 8 * tid) = m1;
   __syncthreads();
   make_qtilde(mslot(r0), qph, qpl, qt, xs, wave, lane);
-  uint2 mnext = make_uint2(0, 0);  // scales two records ahead
-  if (r0 + 2 < r1) mnext = *(const uint2*)(rec(r0 + 2) + 32768 + 8 * tid);
+  uint2 mnext = *(const uint2*)(r0 + 2 < r1 ? rec(r0 + 2) + 32768 + 8 * tid : rec0);
   load_values(rec(r0), vd, wave, lane);
   __syncthreads();
 
@@ -319,7 +339,10 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
     mx = xmax4(mx);
     if (g == 0) xm[wave][q16] = mx;
     __syncthreads();  // (B2) record maxima; q~ of r and the key codes are free
-    if (more) load_keys(rec(r + 1), kd, wave, lane);
+    // loads are unconditional (a branch around them makes the compiler's wait
+    // counting conservative): past the last record they re-read one 16-byte
+    // line of record r0 and are not used
+    load_keys(more ? rec(r + 1) : rec0, kd, wave, lane, !more);
 
     const float mrec = fmaxf(fmaxf(xm[0][q16], xm[1][q16]), fmaxf(xm[2][q16], xm[3][q16]));
     const float m_new = fmaxf(m_run, mrec);
@@ -359,7 +382,7 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
     if (g == 0) xz[wave][q16] = zt;
     if (more) make_qtilde(mslot(r + 1), qph, qpl, qt, xs, wave, lane);
     if (r + 2 < r1) *(uint2*)(mslot(r + 2) + 8 * tid) = mnext;
-    if (r + 3 < r1) mnext = *(const uint2*)(rec(r + 3) + 32768 + 8 * tid);
+    mnext = *(const uint2*)(r + 3 < r1 ? rec(r + 3) + 32768 + 8 * tid : rec0);
     __syncthreads();  // (B3) weights, zero-point sums; q~ and scales of r + 1, r + 2
 
     const float corr = xz[0][q16] + xz[1][q16] + xz[2][q16] + xz[3][q16];
@@ -382,7 +405,7 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[j] = mfma16(av[j], pbl[t], o[j]);
     }
-    if (more) load_values(rec(r + 1), vd, wave, lane);
+    load_values(more ? rec(r + 1) : rec0, vd, wave, lane, !more);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int cb = 4 * wave + j;
@@ -489,33 +512,32 @@ __device__ __forceinline__ void ring_load(const DecodeArgs& a, const DecodeSeq& 
       R.k[kk] = make_uint2(p[0], p[1]);
     }
   }
+  // every load is unconditional (clamped indices, results selected
+  // afterwards): loads under branches make the compiler's wait counting
+  // conservative across the step loop, which would stall on the prefetch
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = 16 * wave + 4 * g + r;
-    uint32_t dk = 0, dv = 0;
-    if (t < n) {
-      const int sl = slot_of(t);
-      if (NB == 2) {
-        dk = *(const uint32_t*)(ks + (int64_t)sl * 4);
-        dv = *(const uint32_t*)(vs + (int64_t)sl * 4);
-      } else {
-        dk = *(const uint16_t*)(ks + (int64_t)sl * 2);
-        dv = *(const uint16_t*)(vs + (int64_t)sl * 2);
-      }
+    const int sl = slot_of(t < n ? t : 0);
+    uint32_t dk, dv;
+    if (NB == 2) {
+      dk = *(const uint32_t*)(ks + (int64_t)sl * 4);
+      dv = *(const uint32_t*)(vs + (int64_t)sl * 4);
+    } else {
+      dk = *(const uint16_t*)(ks + (int64_t)sl * 2);
+      dv = *(const uint16_t*)(vs + (int64_t)sl * 2);
     }
-    R.dk[r] = dk;
+    R.dk[r] = dk;  // a masked token carries the (finite) scales of token 0; its weight is 0
     R.dv[r] = dv;
   }
-  const int tq = tid & 15, c16 = tid >> 4;
-  if (c16 < D / 16) {
+  const int tq = tid & 15, c16 = (tid >> 4) % (D / 16);  // head_dim 128: two threads per item, one used
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int t = 4 * tq + k;
-      const uint32_t* p = (const uint32_t*)(vc + (int64_t)slot_of(t < n ? t : 0) * (NB * kQBytes) + 12 * c16);
-      R.v[k][0] = p[0];
-      R.v[k][1] = p[1];
-      R.v[k][2] = p[2];
-    }
+  for (int k = 0; k < 4; ++k) {
+    const int t = 4 * tq + k;
+    const uint32_t* p = (const uint32_t*)(vc + (int64_t)slot_of(t < n ? t : 0) * (NB * kQBytes) + 12 * c16);
+    R.v[k][0] = p[0];
+    R.v[k][1] = p[1];
+    R.v[k][2] = p[2];
   }
 }
 
@@ -564,24 +586,40 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
 #pragma unroll
   for (int i = 0; i < CPW; ++i) acc[i] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 
-  // one step over tokens t0 .. t0 + 63 from `cur`, loading the next step into
-  // `nxt`; called with the two register sets alternating, so no copy (and no
-  // early wait for the loads in flight) is needed
-  auto step = [&](int t0, const RingRegs<D>& cur, RingRegs<D>& nxt) {
+  // one step over tokens t0 .. t0 + 63; the ring step reads `cur` and loads the
+  // next step into `nxt` (unconditionally: past the end the clamped loads are
+  // harmless), the two register sets alternating so that no copy, and no early
+  // wait for the loads in flight, is needed.  The sink and ring steps are
+  // compiled separately (no branch around the loads inside a step).
+  auto step = [&](auto sink_c, int t0, const RingRegs<D>& cur, RingRegs<D>& nxt) {
+    constexpr bool sink = decltype(sink_c)::value;
     const int n = min(kStep, t_end - t0);
-    if (!sink && t0 + kStep < t_end) ring_load<D>(a, sq, h, t0 + kStep, t_end - t0 - kStep, nxt);
+    if (!sink) ring_load<D>(a, sq, h, t0 + kStep, t_end - t0 - kStep, nxt);
 
-    // ---- (1) V^T
+    // ---- (1) V^T; the sink's key operands are loaded here too, all at once
+    uint4 ks_op[KK];
     if (sink) {
-      for (int it = tid; it < (kStep / 4) * (D / 8); it += 256) {
-        const int tq = it % (kStep / 4), c8 = it / (kStep / 4);
-        uint4 r[4];
+      constexpr int ITEMS = (kStep / 4) * (D / 8) / 256;  // 4-token x 8-channel pieces per thread
+      uint4 r[ITEMS][4];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        ks_op[kk] = *(const uint4*)(ksink + (int64_t)(t0 + 16 * wave + q16) * D + 32 * kk + 8 * g);
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j) {
+        const int it = tid + 256 * j, tq = it % (kStep / 4), c8 = it / (kStep / 4);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int tok = 4 * tq + k;
-          r[k] = tok < n ? *(const uint4*)(vsink + (int64_t)(t0 + tok) * D + 8 * c8) : make_uint4(0, 0, 0, 0);
+          r[j][k] = *(const uint4*)(vsink + (int64_t)(t0 + (tok < n ? tok : 0)) * D + 8 * c8);
         }
-        store_t4x8(vt, kRPitch, 8 * c8, 4 * tq, r);
+      }
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j) {  // zero the rows past the sink only once everything is in flight
+        const int it = tid + 256 * j;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (4 * (it % (kStep / 4)) + k >= n) r[j][k] = make_uint4(0, 0, 0, 0);
+        store_t4x8(vt, kRPitch, 8 * (it / (kStep / 4)), 4 * (it % (kStep / 4)), r[j]);
       }
     } else {
       const int tq = tid & 15, c16 = tid >> 4;
@@ -607,7 +645,7 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
     for (int kk = 0; kk < KK; ++kk) {
       half8 av;
       if (sink) {
-        av = mfma_a(*(const uint4*)(ksink + (int64_t)(t0 + 16 * wave + q16) * D + 32 * kk + 8 * g));
+        av = mfma_a(ks_op[kk]);
       } else {
         const uint32_t sh = (g & 1) ? 16u : 0u;
         av = codes6_reg(__builtin_amdgcn_alignbit(cur.k[kk].y, cur.k[kk].x, sh), cur.k[kk].y >> sh);
@@ -676,9 +714,15 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
     }
     __syncthreads();  // V^T and the weights are free
   };
-  for (int t0 = t_begin; t0 < t_end; t0 += 2 * kStep) {
-    step(t0, ra, rb);
-    if (t0 + kStep < t_end) step(t0 + kStep, rb, ra);
+  if (sink) {
+    for (int t0 = t_begin; t0 < t_end; t0 += kStep) step(std::true_type{}, t0, ra, rb);
+  } else {
+    for (int t0 = t_begin;;) {
+      step(std::false_type{}, t0, ra, rb);
+      if ((t0 += kStep) >= t_end) break;
+      step(std::false_type{}, t0, rb, ra);
+      if ((t0 += kStep) >= t_end) break;
+    }
   }
 
   const float lsum = xsum4(l_part);

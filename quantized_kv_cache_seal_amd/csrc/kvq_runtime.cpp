@@ -139,13 +139,15 @@ static constexpr int kRingStep = 64;         // tokens per step of the matrix-co
 static constexpr int kStagedRingChunk = 256; // ring tokens per chunk next to a vector-ALU body scan
 static constexpr int kBodyWgPerCu = 2;       // resident workgroups per CU of the fused kernel
 
-// Matrix-core plan.  Work in units of one record (about one 64-token ring step
-// or half a sink).  Body chunks are sized to the average work per resident
-// workgroup and issued first; ring chunks are half that size and fill the
-// remaining slots in two rounds.
+// Matrix-core plan.  Work in units of one record (about one 64-token ring
+// step; the sink is two).  Every work item should take about the average work
+// per resident workgroup, so that all of them run in one round: ring chunks
+// of that many steps, and the remaining slots split evenly among the body
+// records (body items are issued first).
 struct MfmaPlan {
   int ring_chunk;
-  double body_target;  // records per body chunk
+  int body_slots;      // workgroups left for body chunks
+  double body_total;   // records of all the launch's (sequence, head) pairs
 };
 static MfmaPlan mfma_plan(const kvq_cache* c, const std::vector<int64_t>& n_rec, const std::vector<int64_t>& ring) {
   const int H = c->y.H;
@@ -154,12 +156,14 @@ static MfmaPlan mfma_plan(const kvq_cache* c, const std::vector<int64_t>& n_rec,
     body += (double)H * n_rec[i];
     other += (double)H * ((ring[i] + kRingStep - 1) / kRingStep + 2);
   }
-  const double slots = (double)kBodyWgPerCu * (c->n_cu ? c->n_cu : 256);
+  const int slots = kBodyWgPerCu * (c->n_cu ? c->n_cu : 256);
   const double per = std::max(1.0, (body + other) / slots);
   MfmaPlan p;
-  p.ring_chunk = kRingStep * std::max(1, (int)(per / 2));
-  const double body_slots = std::max(1.0, slots - std::ceil(other / per));
-  p.body_target = std::max(1.0, body / body_slots);
+  p.ring_chunk = kRingStep * std::max(1, (int)std::lround(per));
+  int64_t ring_items = 0;
+  for (size_t i = 0; i < ring.size(); ++i) ring_items += (int64_t)H * (1 + (ring[i] + p.ring_chunk - 1) / p.ring_chunk);
+  p.body_slots = (int)std::max<int64_t>(H, slots - ring_items);
+  p.body_total = body;
   return p;
 }
 
@@ -409,8 +413,10 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
   int max_chunks = 1;
   for (int i = 0; i < n_seqs; ++i) {
     int nb;
-    if (use_mfma)
-      nb = n_rec[i] == 0 ? 0 : (int)std::min<int64_t>(n_rec[i], std::max<int64_t>(1, std::llround(n_rec[i] / mp.body_target)));
+    if (use_mfma)  // this sequence's share of the body slots, whole per KV head
+      nb = n_rec[i] == 0 ? 0
+                         : (int)std::min<int64_t>(n_rec[i], std::max<int64_t>(1, (int64_t)std::floor(
+                               (double)n_rec[i] * c->y.H * mp.body_slots / std::max(1.0, mp.body_total) / c->y.H)));
     else
       nb = (int)((n_rec[i] + valu_rpc - 1) / valu_rpc);
     plan[i] = plan_seq(c, seq_ids[i], layer, rc, nb);

@@ -36,6 +36,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_main_kernel_qwen27b_ctx110592.md")
+KERNEL_SOURCE = os.path.join(ROOT, "quantized_kv_cache_seal_amd", "csrc", "kvq_decode_fused.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the main decode kernel from the counter runs
+    recorded in the profile summary (FETCH_SIZE and WRITE_SIZE in KiB per
+    dispatch, each times its copy-calibrated scale), or None when the kernel
+    source has changed since the counters were taken."""
+    import hashlib
+    try:
+        line = next(l for l in open(TRAFFIC_PROFILE) if l.startswith("traffic-record:"))
+    except (OSError, StopIteration):
+        return None
+    rec = dict(kv.split("=", 1) for kv in line.split()[1:])
+    src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    if rec.get("kernel_sha256") != src:
+        return None
+    return (float(rec["fetch_kib"]) * float(rec["fetch_scale"]) + float(rec["write_kib"]) * float(rec["write_scale"])) * 1024
+
+
 def region_bytes(w, rec_bytes, n_tok, n_rec, ring):
     """Algorithmic compressed bytes one decode call reads for one layer (all KV
     heads): the fp16 sink, the tq6_0 ring (98 B per 128 values) and the sealed
@@ -227,6 +248,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle decode timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-seal", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-sized device buffer 20 times (calibrates HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -238,11 +261,23 @@ def main():
     from quantized_kv_cache_seal_amd import configs, inputs, kvq, synthetic
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 20 copies of {n} bytes")
+        return
     kvq.lib()
     w = configs.QWEN27B
     dec = run_decode(args, w, torch, kvq, synthetic, inputs)
     seal = None if args.no_seal else run_seal(args, w, torch, kvq, synthetic)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(w, args.cpu_budget)
+    traffic = measured_traffic()
+    if traffic is not None:
+        traffic = int(traffic)
     res = {
         "metric": METRIC,
         "value": round(dec["gbs"], 2),
@@ -265,9 +300,10 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": round(dec["achieved"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": "decode_main_kernel (fused sink, ring and body scan of one layer)",
             "bytes_per_launch": int(dec["per_call_bytes"]), "avg_launch_us": round(dec["avg_kernel_us"], 2),
+            "traffic_over_algorithmic": None if traffic is None else round(traffic / dec["per_call_bytes"], 4),
         },
         "cpu_baseline": cpu,
     }

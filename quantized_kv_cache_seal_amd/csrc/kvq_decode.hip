@@ -215,45 +215,52 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   prof_end(a.prof_ts);
 }
 
-// Merge of the split-K partials of one query head (grid Hq x n_seqs): one
-// softmax over all chunks, R^T applied to the rotated part (chunks 1..), the
-// sink part (chunk 0) added as is, divided by the total weight.  The four
-// waves split the chunks; each lane owns D / 64 channels.
+// Merge of the split-K partials of one query head (grid Hq x n_seqs, 1024
+// threads): one softmax over all chunks, R^T applied to the rotated part
+// (chunks 1..), the sink part (chunk 0) added as is, divided by the total
+// weight.  The 16 waves split the chunks (more loads in flight than a
+// 256-thread block); each lane owns D / 64 channels.
+constexpr int kMergeWaves = 16;
+
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  constexpr int VPL = D / 64;
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
+  constexpr int VPL = D / 64, NW = kMergeWaves;
   __shared__ float wts[kMaxChunks];
-  __shared__ float red[4][D];
-  __shared__ float rm[8];
+  __shared__ float red[NW][D];
+  __shared__ float rm[2 * NW];
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = a.n_chunks[b];
   const float* P = a.part + ((int64_t)b * a.Hq + hq) * a.max_chunks * (D + 2);
 
   float mx = -INFINITY;
-  for (int c = tid; c < n; c += 256) mx = fmaxf(mx, P[(int64_t)c * (D + 2)]);
+  for (int c = tid; c < n; c += 64 * NW) mx = fmaxf(mx, P[(int64_t)c * (D + 2)]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
   if (lane == 0) rm[wave] = mx;
   __syncthreads();
-  const float M = fmaxf(fmaxf(rm[0], rm[1]), fmaxf(rm[2], rm[3]));
+  float M = rm[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, rm[w]);
   float ls = 0.0f;
-  for (int c = tid; c < n; c += 256) {
+  for (int c = tid; c < n; c += 64 * NW) {
     const float w = expf(P[(int64_t)c * (D + 2)] - M);
     wts[c] = w;
     ls += w * P[(int64_t)c * (D + 2) + 1];
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o, 64);
-  if (lane == 0) rm[4 + wave] = ls;
+  if (lane == 0) rm[NW + wave] = ls;
   __syncthreads();
-  const float L = rm[4] + rm[5] + rm[6] + rm[7];
+  float L = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) L += rm[NW + w];
 
   // weighted sum of the rotated partials (chunks 1..n-1)
   float v[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) v[i] = 0.0f;
 #pragma unroll 4
-  for (int c = 1 + wave; c < n; c += 4) {
+  for (int c = 1 + wave; c < n; c += NW) {
     const float w = wts[c];
     const float2* row = (const float2*)(P + (int64_t)c * (D + 2) + 2 + VPL * lane);  // 8-byte aligned
 #pragma unroll
@@ -270,7 +277,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int j = VPL * lane + i;
-    v[i] = red[0][j] + red[1][j] + red[2][j] + red[3][j];
+    float x = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) x += red[w][j];
+    v[i] = x;
   }
   // R^T: head_dim 128: s1 . H . s2 / sqrt(128); 256 and 512: H_256 / 16 per 256-block
   if (D == 128) {
@@ -316,9 +326,9 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int grid_x, hipStream_t strea
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   dim3 grid(a.Hq, a.n_seqs);
   switch (a.D) {
-    case 128: hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(256), 0, stream, a); break;
-    case 256: hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(256), 0, stream, a); break;
-    case 512: hipLaunchKernelGGL(merge_kernel<512>, grid, dim3(256), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(64 * kMergeWaves), 0, stream, a); break;
+    case 256: hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(64 * kMergeWaves), 0, stream, a); break;
+    case 512: hipLaunchKernelGGL(merge_kernel<512>, grid, dim3(64 * kMergeWaves), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -4,9 +4,9 @@
 Workload: the Qwen 27B-class full-attention shape (16 layers, 4 KV heads x 256,
 24 query heads) at a 110,592-token context in the just-sealed state (sink 128,
 831 sealed records per head, 4,096 ring tokens), keys and values drawn by the
-seeded generator.  One step = for every layer: append one token (rotation +
-tq6_0 staging), the seal-if-full check, and decode attention of one query over
-all four regions.  Inputs for every step are resident in HBM before timing.
+seeded generator.  One step = for every layer one kvq_decode_step: append one
+token (rotation + tq6_0 staging), the seal-if-full check, and decode attention
+of one query over all four regions (--calls: the three separate calls).  Inputs for every step are resident in HBM before timing.
 
 value = decode-attention effective KV GB/s: the compressed bytes the step must
 read (sink fp16 + ring tq6_0 + sealed records, all layers and heads) divided by
@@ -101,14 +101,18 @@ def run_decode(args, w, torch, kvq, synthetic, inputs):
     def one_step(s):
         nbytes = 0
         for l in range(L):
-            cache.append(l, [0], nk[s][l], nv[s][l], stream=stream)
-            g = cache.seal(l, kvq.SEAL_IF_FULL, stream=stream)
+            if args.calls:
+                cache.append(l, [0], nk[s][l], nv[s][l], stream=stream)
+                g = cache.seal(l, kvq.SEAL_IF_FULL, stream=stream)
+                cache.attn_decode(l, [0], qs[s][l], out=out[l], workspace=ws, stream=stream)
+            else:
+                _, g = cache.decode_step(l, [0], nk[s][l], nv[s][l], qs[s][l], out=out[l], workspace=ws,
+                                         stream=stream)
             st = state[l]
             st[0] += 1
             st[1] += g
             st[2] += 1 - 128 * g
             nbytes += region_bytes(w, rec_bytes, *st)
-            cache.attn_decode(l, [0], qs[s][l], out=out[l], workspace=ws, stream=stream)
         return nbytes
 
     for s in range(W):
@@ -244,6 +248,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--calls", action="store_true",
+                    help="run each layer's step as kvq_append + kvq_seal + kvq_attn_decode instead of kvq_decode_step")
     ap.add_argument("--seal-reps", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle decode timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -296,6 +302,7 @@ def main():
             "workload": w.name, "layers": w.n_layers, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
             "q_heads": w.n_q_heads, "ctx": w.ctx, "batch": 1, "body_bits": f"{w.k_bits}/{w.v_bits}",
             "sinkhorn_passes": w.passes, "tail": [w.tail_min, w.tail_max], "decode_path": args.path,
+            "step_call": "append+seal+attn_decode" if args.calls else "decode_step",
             "bytes_per_step": int(dec["bytes_step"]),
         },
         "roofline": {

@@ -127,7 +127,7 @@ kvq_status kvq_append(kvq_cache* cache, int32_t layer, const int32_t* seq_ids, i
  * summed over sequences and layers.  Errors: KVQ_ERR_INVALID, KVQ_ERR_DEVICE. */
 kvq_status kvq_seal(kvq_cache* cache, int32_t layer, int32_t mode, void* stream, int32_t* groups_sealed);
 
-/* Device workspace kvq_attn_decode needs for a call on n_seqs sequences
+/* Device workspace kvq_attn_decode and kvq_decode_step need for a call on n_seqs sequences
  * whose contexts are at most max_ctx.  bytes: host out. */
 kvq_status kvq_workspace_bytes(const kvq_cache* cache, int32_t n_seqs, size_t* bytes);
 
@@ -145,6 +145,25 @@ kvq_status kvq_workspace_bytes(const kvq_cache* cache, int32_t n_seqs, size_t* b
 kvq_status kvq_attn_decode(kvq_cache* cache, int32_t layer, const int32_t* seq_ids, int32_t n_seqs,
                            const void* q, void* out, int32_t out_dtype, float scale,
                            void* workspace, size_t ws_bytes, void* stream);
+
+/* One decode step of one layer: append one token per listed sequence, seal
+ * what a KVQ_SEAL_IF_FULL seal of the layer would seal, then decode
+ * attention of q over every cached token including the new one (SJ-KVaRN
+ * 2.1: a decode pass reads sink, ring and body; the token just written is part
+ * of the tail).  The result is that of kvq_append (n_tok = 1), kvq_seal(layer,
+ * KVQ_SEAL_IF_FULL) and kvq_attn_decode in turn.  When the matrix-core path
+ * runs, every new token lands in the ring and nothing is due for sealing in
+ * the layer, it is one decode launch (plus the merge): the new token is
+ * encoded into its ring slot by the same launch and enters the softmax as
+ * its own split-K partial, with the decoded tq6_0 values the ring holds.
+ * k, v: device fp16 [n_seqs][n_kv_heads][head_dim]; q, out, out_dtype, scale,
+ * workspace, ws_bytes as kvq_attn_decode.  groups_sealed: host out (may be
+ * NULL).  Errors: those of the three calls; on a fused launch, argument and
+ * capacity errors leave the cache unchanged. */
+kvq_status kvq_decode_step(kvq_cache* cache, int32_t layer, const int32_t* seq_ids, int32_t n_seqs,
+                           const void* k, const void* v, const void* q, void* out, int32_t out_dtype,
+                           float scale, void* workspace, size_t ws_bytes, void* stream,
+                           int32_t* groups_sealed);
 
 /* Select the kernel that scans sealed records: KVQ_PATH_MFMA (matrix cores,
  * the default) or KVQ_PATH_VALU (vector ALU reference, kept for A/B checks).

@@ -221,66 +221,96 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 // weight.  The 16 waves split the chunks (more loads in flight than a
 // 256-thread block); each lane owns D / 64 channels.
 constexpr int kMergeWaves = 16;
+constexpr int kMergeUnroll = 8;  // partials per wave and pass, all loaded before any is used
 
+// One workgroup per (sequence, query head).  Wave w takes partials
+// w, w + NW, ... in passes of kMergeUnroll: every load of a pass (the rows and
+// their (m, l), the latter broadcast to all lanes) is issued before the first
+// is used, so a pass costs one memory round trip, and the wave keeps a running
+// (M, L, sum e^(m - M) acc) in registers with no cross-lane step.  The waves'
+// states meet in LDS; wave 0 rotates the rotated-domain sum back and adds the
+// sink's partial (chunk 0, original domain).
 template <int D>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
-  constexpr int VPL = D / 64, NW = kMergeWaves;
-  __shared__ float wts[kMaxChunks];
+  constexpr int VPL = D / 64, NW = kMergeWaves, U = kMergeUnroll;
   __shared__ float red[NW][D];
   __shared__ float rm[2 * NW];
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = a.n_chunks[b];
   const float* P = a.part + ((int64_t)b * a.Hq + hq) * a.max_chunks * (D + 2);
 
-  float mx = -INFINITY;
-  for (int c = tid; c < n; c += 64 * NW) mx = fmaxf(mx, P[(int64_t)c * (D + 2)]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  if (lane == 0) rm[wave] = mx;
-  __syncthreads();
-  float M = rm[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) M = fmaxf(M, rm[w]);
-  float ls = 0.0f;
-  for (int c = tid; c < n; c += 64 * NW) {
-    const float w = expf(P[(int64_t)c * (D + 2)] - M);
-    wts[c] = w;
-    ls += w * P[(int64_t)c * (D + 2) + 1];
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o, 64);
-  if (lane == 0) rm[NW + wave] = ls;
-  __syncthreads();
-  float L = 0.0f;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) L += rm[NW + w];
-
-  // weighted sum of the rotated partials (chunks 1..n-1)
+  float M = -INFINITY, L = 0.0f;
   float v[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) v[i] = 0.0f;
-#pragma unroll 4
-  for (int c = 1 + wave; c < n; c += NW) {
-    const float w = wts[c];
-    const float2* row = (const float2*)(P + (int64_t)c * (D + 2) + 2 + VPL * lane);  // 8-byte aligned
+  float sink[VPL];
+  float m0 = 0.0f;
+  if (wave == 0) {
+    m0 = P[0];
 #pragma unroll
     for (int i = 0; i < VPL / 2; ++i) {
-      const float2 x = row[i];
-      v[2 * i] = fmaf(w, x.x, v[2 * i]);
-      v[2 * i + 1] = fmaf(w, x.y, v[2 * i + 1]);
+      const float2 x = ((const float2*)(P + 2 + VPL * lane))[i];
+      sink[2 * i] = x.x;
+      sink[2 * i + 1] = x.y;
+    }
+  }
+  for (int base = 0; base < n; base += NW * U) {
+    float2 ml[U];
+    float x[U][VPL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = base + wave + NW * u;
+      const float* row = P + (int64_t)(c < n ? c : 0) * (D + 2);
+      ml[u] = *(const float2*)row;
+#pragma unroll
+      for (int i = 0; i < VPL / 2; ++i) {
+        const float2 t = ((const float2*)(row + 2 + VPL * lane))[i];
+        x[u][2 * i] = t.x;
+        x[u][2 * i + 1] = t.y;
+      }
+    }
+    float mp = M;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (base + wave + NW * u < n) mp = fmaxf(mp, ml[u].x);
+    const float alpha = M == -INFINITY ? 0.0f : expf(M - mp);  // nothing to rescale before the first partial
+    L *= alpha;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) v[i] *= alpha;
+    M = mp;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = base + wave + NW * u;
+      if (c < n) {
+        const float w = expf(ml[u].x - M);
+        L = fmaf(w, ml[u].y, L);
+        if (c > 0) {  // chunk 0 (the sink) is in the original domain: added after the rotation
+#pragma unroll
+          for (int i = 0; i < VPL; ++i) v[i] = fmaf(w, x[u][i], v[i]);
+        }
+      }
     }
   }
 #pragma unroll
   for (int i = 0; i < VPL; ++i) red[wave][VPL * lane + i] = v[i];
+  if (lane == 0) {
+    rm[wave] = M;
+    rm[NW + wave] = L;
+  }
   __syncthreads();
   if (wave != 0) return;
+  float Mt = rm[0];
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const int j = VPL * lane + i;
-    float x = 0.0f;
+  for (int w = 1; w < NW; ++w) Mt = fmaxf(Mt, rm[w]);
+  float Lt = 0.0f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) x += red[w][j];
-    v[i] = x;
+  for (int i = 0; i < VPL; ++i) v[i] = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float s = rm[w] == -INFINITY ? 0.0f : expf(rm[w] - Mt);  // a wave with no partial has M = -inf
+    Lt = fmaf(s, rm[NW + w], Lt);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) v[i] = fmaf(s, red[w][VPL * lane + i], v[i]);
   }
   // R^T: head_dim 128: s1 . H . s2 / sqrt(128); 256 and 512: H_256 / 16 per 256-block
   if (D == 128) {
@@ -298,12 +328,12 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
 #pragma unroll
     for (int i = 0; i < VPL; ++i) v[i] *= 0.0625f;
   }
-  const float w0 = wts[0];
-  const float inv_l = 1.0f / L;
+  const float w0 = expf(m0 - Mt);
+  const float inv_l = 1.0f / Lt;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int j = VPL * lane + i;
-    const float o = fmaf(w0, P[2 + j], v[i]) * inv_l;
+    const float o = fmaf(w0, sink[i], v[i]) * inv_l;
     const int64_t oi = ((int64_t)b * a.Hq + hq) * D + j;
     if (a.out_f16)
       ((uint16_t*)a.out)[oi] = f2h_bits(o);

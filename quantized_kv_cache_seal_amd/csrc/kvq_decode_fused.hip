@@ -29,6 +29,7 @@
 // 1.. the ring chunks, then the body chunks.
 #include <type_traits>
 
+#include "kvq_encode.h"
 #include "kvq_mfma.h"
 
 namespace kvq {
@@ -746,6 +747,49 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
 }
 
 // ---------------------------------------------------------------------------
+// Append role (fused decode step): the token appended in the same call, for
+// one (sequence, KV head).  Waves 0 and 1 rotate and encode its key and value
+// into the staging ring slot (the same encoder and bytes as the append
+// kernel; the ring items of this launch stop short of that slot), keeping the
+// decoded rotated-domain values d (u - 32).  The token's split-K partial is
+// then exact and needs no scan: for each query head of the group the score
+// s = q' . k (scale and log2 e folded into q'), m = s, l = 1, acc = v.
+__device__ __forceinline__ void append_role(const DecodeArgs& a, int b, int h, uint8_t* smem) {
+  const Layout& y = a.y;
+  const DecodeSeq& sq = a.seq[b];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int G = a.g;
+  float* rows = (float*)smem;     // [16][256] query rows
+  float* kv = rows + 16 * 256;    // [2][256] decoded key and value
+  uint8_t* arena = const_cast<uint8_t*>(a.arena);  // the one region this launch writes
+  if (wave < 2) {
+    const uint16_t* src = (wave ? a.v_new : a.k_new) + ((int64_t)b * y.H + h) * 256;
+    uint8_t* codes = arena + rcode_off(y, sq.slot, a.layer, h, wave, sq.app_slot);
+    uint16_t* scales = (uint16_t*)(arena + rscale_off(y, sq.slot, a.layer, h, wave, sq.app_slot));
+    float deq[4];
+    encode_chunk<4>(src, codes, scales, lane, a.signs, false, deq);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kv[256 * wave + 4 * lane + j] = deq[j];
+  }
+  query_rows<256>(a, b, h, true, rows, wave, lane);
+  __syncthreads();
+  for (int i = wave; i < G; i += 4) {
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s = fmaf(rows[i * 256 + 4 * lane + j], kv[4 * lane + j], s);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    float* P = a.part + (((int64_t)b * a.Hq + h * G + i) * a.max_chunks + sq.app_chunk) * (256 + 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) P[2 + 4 * lane + j] = kv[256 + 4 * lane + j];
+    if (lane == 0) {
+      P[0] = s * kLn2;
+      P[1] = 1.0f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Kernels.  Work item i of a launch: body items first (when the launch has
 // them), sequence by sequence, KV head-major, then sink/ring items likewise.
 
@@ -769,8 +813,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_main_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kMainLds];
   int b, h, c;
-  const int item = blockIdx.x;
+  int item = blockIdx.x;
   prof_start(a.prof_ts);
+  if (item < a.n_app_items) {
+    append_role(a, item / a.y.H, item % a.y.H, smem);
+    prof_end(a.prof_ts);
+    return;
+  }
+  item -= a.n_app_items;
   if (item < a.n_body_items) {
     if (find_item(a, item, true, b, h, c)) body_role(a, b, h, c, smem);
   } else {
@@ -786,7 +836,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (find_item(a, blockIdx.x, false, b, h, c)) ring_role<D>(a, b, h, c, smem);
 }
 
-// Body (head_dim 256, 4-bit K and V) and sink/ring items in one launch.
+// Append (optional), body (head_dim 256, 4-bit K and V) and sink/ring items in
+// one launch.
 hipError_t launch_decode_main(const DecodeArgs& a, int n_items, hipStream_t stream) {
   if (a.y.D != 256 || a.y.kbits != 4 || a.y.vbits != 4 || a.ring_chunk % kStep != 0 || a.g > kMaxGroup)
     return hipErrorInvalidValue;

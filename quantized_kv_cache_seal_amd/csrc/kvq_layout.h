@@ -80,17 +80,22 @@ struct DecodeSeq {
   int32_t ring0;     // ring slot of the oldest unsealed token
   int32_t n_rec;     // sealed records
   int32_t n_ring_chunks, n_body_chunks, n_chunks;  // body chunks split the records evenly
+  int32_t app_slot;   // fused decode step: ring slot the new token is written to
+  int32_t app_chunk;  // fused decode step: partial index of the new token (the last one)
 };
 
 struct DecodeArgs {
   const uint8_t* arena;
   Layout y;
   const uint16_t* q;  // fp16 [n_seqs][Hq][D]
+  const uint16_t* k_new;  // fused decode step: fp16 [n_seqs][H][D] token appended first, or null
+  const uint16_t* v_new;
   float* part;        // [n_seqs][Hq][max_chunks][D + 2]: m, l, acc[D]
   float scale;
   int32_t layer, Hq, g, n_seqs, max_chunks;
   int32_t ring_chunk;    // ring tokens per chunk
-  int32_t n_body_items;  // matrix-core launch: work items before the sink/ring items
+  int32_t n_app_items;   // fused decode step: one append item per (sequence, KV head), first
+  int32_t n_body_items;  // matrix-core launch: body items, after the append items
   int32_t valu_regions;  // bit r set: the vector-ALU kernel scans region r (0 sink, 1 ring, 2 body)
   uint32_t signs[8];
   unsigned long long* prof_ts;  // profiling: {first start, last end} wall-clock stamps, or null

@@ -149,14 +149,17 @@ struct MfmaPlan {
   int body_slots;      // workgroups left for body chunks
   double body_total;   // records of all the launch's (sequence, head) pairs
 };
-static MfmaPlan mfma_plan(const kvq_cache* c, const std::vector<int64_t>& n_rec, const std::vector<int64_t>& ring) {
+static MfmaPlan mfma_plan(const kvq_cache* c, const std::vector<int64_t>& n_rec, const std::vector<int64_t>& ring,
+                          int reserved) {
   const int H = c->y.H;
   double body = 0, other = 0;
   for (size_t i = 0; i < n_rec.size(); ++i) {
     body += (double)H * n_rec[i];
     other += (double)H * ((ring[i] + kRingStep - 1) / kRingStep + 2);
   }
-  const int slots = kBodyWgPerCu * (c->n_cu ? c->n_cu : 256);
+  // `reserved` workgroups (the append items of a fused step) are short and
+  // leave their slots idle once done
+  const int slots = std::max(1, kBodyWgPerCu * (c->n_cu ? c->n_cu : 256) - reserved);
   const double per = std::max(1.0, (body + other) / slots);
   MfmaPlan p;
   p.ring_chunk = kRingStep * std::max(1, (int)std::lround(per));
@@ -364,7 +367,7 @@ static int max_chunks_bound(const kvq_cache* c) {
     const int n_cu = c->n_cu ? c->n_cu : 256;
     body = std::max(body, std::min(c->y.max_rec, (kBodyWgPerCu * n_cu + c->y.H - 1) / c->y.H + 1));
   }
-  return 1 + (c->y.cap + rc - 1) / rc + body;
+  return 1 + (c->y.cap + rc - 1) / rc + body + 1;  // + the new token of a fused decode step
 }
 
 kvq_status kvq_workspace_bytes(const kvq_cache* c, int32_t n_seqs, size_t* bytes) {
@@ -379,17 +382,25 @@ kvq_status kvq_set_decode_path(kvq_cache* c, int32_t path) {
   return KVQ_OK;
 }
 
-kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, int32_t n_seqs, const void* q,
-                           void* out, int32_t out_dtype, float scale, void* workspace, size_t ws_bytes,
-                           void* stream) {
+static kvq_status check_decode_args(const kvq_cache* c, int32_t layer, const int32_t* seq_ids, int32_t n_seqs,
+                                    const void* q, void* out, int32_t out_dtype, void* workspace) {
   if (!c) return fail(KVQ_ERR_INVALID, "cache is NULL");
   if (c->plan_only) return fail(KVQ_ERR_UNSUPPORTED, "decode on a plan-only cache");
   if (layer < 0 || layer >= c->y.L) return fail(KVQ_ERR_INVALID, "layer %d out of range", layer);
   if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_F16) return fail(KVQ_ERR_INVALID, "bad out_dtype");
   kvq_status st = check_seqs(c, seq_ids, n_seqs);
   if (st != KVQ_OK) return st;
-  if (n_seqs == 0) return KVQ_OK;
-  if (!q || !out || !workspace) return fail(KVQ_ERR_INVALID, "q, out and workspace must be non-NULL");
+  if (n_seqs > 0 && (!q || !out || !workspace)) return fail(KVQ_ERR_INVALID, "q, out and workspace must be non-NULL");
+  return KVQ_OK;
+}
+
+// Decode launches.  With k_new/v_new (fused decode step, matrix-core path
+// only) the caller has checked that every sequence's new token goes to the
+// ring and that no seal is due; the token is written and counted here.
+static kvq_status decode_impl(kvq_cache* c, int32_t layer, const int32_t* seq_ids, int32_t n_seqs, const void* q,
+                              void* out, int32_t out_dtype, float scale, void* workspace, size_t ws_bytes,
+                              void* stream, const void* k_new, const void* v_new) {
+  const bool fused = k_new != nullptr;
   const bool use_mfma = c->path != KVQ_PATH_VALU && mfma_supported(c->y);
   const bool staged = c->path != KVQ_PATH_VALU && staged_supported(c->y);
   if (c->path == KVQ_PATH_MFMA && !use_mfma)
@@ -403,7 +414,7 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
   int rc;
   MfmaPlan mp{};
   if (use_mfma) {
-    mp = mfma_plan(c, n_rec, ring);
+    mp = mfma_plan(c, n_rec, ring, fused ? std::min(n_seqs, kMaxLaunchSeqs) * c->y.H : 0);
     rc = mp.ring_chunk;
   } else {
     rc = staged ? kStagedRingChunk : ring_chunk_tokens(c->y);
@@ -420,6 +431,10 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
     else
       nb = (int)((n_rec[i] + valu_rpc - 1) / valu_rpc);
     plan[i] = plan_seq(c, seq_ids[i], layer, rc, nb);
+    if (fused) {
+      plan[i].app_slot = (int32_t)((plan[i].ring0 + plan[i].ring_len) % c->y.cap);
+      plan[i].app_chunk = plan[i].n_chunks++;
+    }
     max_chunks = std::max(max_chunks, plan[i].n_chunks);
   }
   if (max_chunks > kMaxChunks) return fail(KVQ_ERR_CAPACITY, "too many split-K chunks");
@@ -433,6 +448,10 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
     a.y = c->y;
     a.n_seqs = std::min(kMaxLaunchSeqs, n_seqs - b0);
     a.q = (const uint16_t*)q + (int64_t)b0 * Hq * D;
+    if (fused) {
+      a.k_new = (const uint16_t*)k_new + (int64_t)b0 * c->y.H * D;
+      a.v_new = (const uint16_t*)v_new + (int64_t)b0 * c->y.H * D;
+    }
     a.part = (float*)workspace + (int64_t)b0 * Hq * max_chunks * (D + 2);
     a.scale = scale;
     a.layer = layer;
@@ -453,8 +472,9 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
     hipError_t e = hipSuccess;
     if (b0 == 0 && c->prof_used < c->prof_n) a.prof_ts = c->prof_ts + 2 * c->prof_used++;
     if (use_mfma) {
+      a.n_app_items = fused ? a.n_seqs * c->y.H : 0;
       a.n_body_items = n_body_items;
-      e = launch_decode_main(a, n_body_items + n_ring_items, (hipStream_t)stream);
+      e = launch_decode_main(a, a.n_app_items + n_body_items + n_ring_items, (hipStream_t)stream);
       if (e != hipSuccess) return hip_fail(e, "decode launch");
     } else {
       if (staged) {
@@ -479,7 +499,50 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
     e = launch_merge(m, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
+  if (fused)
+    for (int i = 0; i < n_seqs; ++i) c->tok(seq_ids[i], layer) += 1;
   return KVQ_OK;
+}
+
+kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, int32_t n_seqs, const void* q,
+                           void* out, int32_t out_dtype, float scale, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  kvq_status st = check_decode_args(c, layer, seq_ids, n_seqs, q, out, out_dtype, workspace);
+  if (st != KVQ_OK || n_seqs == 0) return st;
+  return decode_impl(c, layer, seq_ids, n_seqs, q, out, out_dtype, scale, workspace, ws_bytes, stream, nullptr,
+                     nullptr);
+}
+
+kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, const int32_t* seq_ids, int32_t n_seqs, const void* k,
+                           const void* v, const void* q, void* out, int32_t out_dtype, float scale,
+                           void* workspace, size_t ws_bytes, void* stream, int32_t* groups_sealed) {
+  kvq_status st = check_decode_args(c, layer, seq_ids, n_seqs, q, out, out_dtype, workspace);
+  if (st != KVQ_OK) return st;
+  if (groups_sealed) *groups_sealed = 0;
+  if (n_seqs == 0) return KVQ_OK;
+  if (!k || !v) return fail(KVQ_ERR_INVALID, "k or v is NULL");
+  // one launch when the matrix-core path runs, every new token lands in the
+  // ring and the seal-if-full that follows the append would seal nothing (in
+  // any sequence of the layer); otherwise the three calls in turn
+  bool fused = c->path != KVQ_PATH_VALU && mfma_supported(c->y);
+  std::vector<char> listed((size_t)c->y.S, 0);
+  for (int i = 0; fused && i < n_seqs; ++i) {
+    const int s = seq_ids[i];
+    listed[s] = 1;
+    if (c->tok(s, layer) < kSink || c->tok(s, layer) + 1 > c->cfg.max_ctx ||
+        c->ring_len(s, layer) + 1 > c->y.cap ||
+        groups_to_seal(c->ring_len(s, layer) + 1, c->cfg, KVQ_SEAL_IF_FULL) > 0)
+      fused = false;
+  }
+  for (int s = 0; fused && s < c->y.S; ++s)
+    if (!listed[s] && groups_to_seal(c->ring_len(s, layer), c->cfg, KVQ_SEAL_IF_FULL) > 0) fused = false;
+  if (!fused) {
+    st = kvq_append(c, layer, seq_ids, n_seqs, k, v, 1, stream);
+    if (st == KVQ_OK) st = kvq_seal(c, layer, KVQ_SEAL_IF_FULL, stream, groups_sealed);
+    if (st == KVQ_OK) st = kvq_attn_decode(c, layer, seq_ids, n_seqs, q, out, out_dtype, scale, workspace, ws_bytes, stream);
+    return st;
+  }
+  return decode_impl(c, layer, seq_ids, n_seqs, q, out, out_dtype, scale, workspace, ws_bytes, stream, k, v);
 }
 
 static void profile_clear(kvq_cache* c) {

@@ -22,7 +22,7 @@ FLAG_PLAN_ONLY = 1
 
 EXPORTS = [
     "kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_append", "kvq_seal",
-    "kvq_workspace_bytes", "kvq_attn_decode", "kvq_set_decode_path", "kvq_seq_info", "kvq_seq_reset",
+    "kvq_workspace_bytes", "kvq_attn_decode", "kvq_decode_step", "kvq_set_decode_path", "kvq_seq_info", "kvq_seq_reset",
     "kvq_seq_truncate", "kvq_export", "kvq_import", "kvq_unit_bytes", "kvq_profile_start", "kvq_profile_stop",
     "kvq_status_string", "kvq_last_error",
 ]
@@ -64,6 +64,7 @@ def lib():
             "kvq_seal": [vp, i32, i32, vp, P(i32)],
             "kvq_workspace_bytes": [vp, i32, P(sz)],
             "kvq_attn_decode": [vp, i32, P(i32), i32, vp, vp, i32, ctypes.c_float, vp, sz, vp],
+            "kvq_decode_step": [vp, i32, P(i32), i32, vp, vp, vp, vp, i32, ctypes.c_float, vp, sz, vp, P(i32)],
             "kvq_set_decode_path": [vp, i32],
             "kvq_seq_info": [vp, i32, i32, P(i64), P(i64), P(i32)],
             "kvq_seq_reset": [vp, i32],
@@ -190,6 +191,25 @@ class Cache:
                                     ctypes.c_void_p(out.data_ptr()), OUT_F16 if out_f16 else OUT_F32,
                                     float(scale), ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream)))
         return out
+
+    def decode_step(self, layer, seq_ids, k, v, q, out=None, scale=1.0, out_f16=False, workspace=None,
+                    stream=None) -> tuple:
+        """Append one token per sequence (k, v: fp16 device [n_seqs][H][D]), seal
+        if full, decode q; returns (out, groups sealed)."""
+        import torch
+        ids, n = _ids(seq_ids)
+        for t in (k, v, q):
+            assert t.is_contiguous() and t.dtype == torch.float16
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float16 if out_f16 else torch.float32, device=q.device)
+        ws = workspace if workspace is not None else self.workspace(n)
+        g = ctypes.c_int32()
+        check(lib().kvq_decode_step(self.h, layer, ids, n, ctypes.c_void_p(k.data_ptr()),
+                                    ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(q.data_ptr()),
+                                    ctypes.c_void_p(out.data_ptr()), OUT_F16 if out_f16 else OUT_F32,
+                                    float(scale), ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream),
+                                    ctypes.byref(g)))
+        return out, g.value
 
     def profile_start(self, max_calls: int):
         """Record the duration of the main decode kernel of the next max_calls

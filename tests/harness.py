@@ -31,13 +31,15 @@ def seq_spec(w, s):
 
 
 class Pair:
-    def __init__(self, w, lens, signs=None):
+    def __init__(self, w, lens, signs=None, extra_ctx=0):
+        """extra_ctx: room for that many more tokens per sequence after build()."""
         import torch
         self.w, self.lens, self.signs = w, list(lens), signs
         self.n = len(lens)
         words = inputs.signs_to_words(signs) if signs is not None else [0, 0, 0, 0]
-        self.gpu = kvq.Cache(kvq.config_for(w, max_ctx=max(lens), max_seqs=self.n, sign_words=words))
-        self.ora = ocache.OracleCache(w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads, self.n, max(lens),
+        max_ctx = max(lens) + extra_ctx
+        self.gpu = kvq.Cache(kvq.config_for(w, max_ctx=max_ctx, max_seqs=self.n, sign_words=words))
+        self.ora = ocache.OracleCache(w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads, self.n, max_ctx,
                                       w.tail_min, w.tail_max, w.margin, w.k_bits, w.v_bits, w.passes, signs)
         self.specs = [seq_spec(w, s) for s in range(self.n)]
         self.kv = {}   # (s, layer) -> (k, v) fp16 numpy [len][H][D]
@@ -146,11 +148,12 @@ class Pair:
                                 stats["uncond_mismatch"] += int((g["codes"] != o["codes"]).sum())
         return stats
 
-    def import_oracle_records(self):
+    def import_oracle_records(self, first=0):
+        """Copy the oracle's records (from record index `first` on) into the GPU cache."""
         for s in range(self.n):
             for l in range(self.w.n_layers):
                 for h in range(self.w.n_kv_heads):
-                    for r in range(self.ora.info(s, l)[1]):
+                    for r in range(first, self.ora.info(s, l)[1]):
                         self.gpu.import_(s, l, h, kvq.REGION_BODY, r, self.ora.export(s, l, h, ocache.REGION_BODY, r))
 
     # ------------------------------------------------------------ attention

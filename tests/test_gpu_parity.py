@@ -6,6 +6,7 @@ import sys
 import numpy as np
 import pytest
 
+from oracle import cache as ocache
 from quantized_kv_cache_seal_amd import configs, inputs, kvq
 
 from harness import ATTN_TOL, Pair
@@ -110,6 +111,54 @@ def test_streaming_one_token_per_step():
     p.import_oracle_records()
     errs, _ = p.decode_errors(0, p.queries(0, 0))
     assert max(errs) <= ATTN_TOL
+
+
+@pytest.mark.parametrize("name", ["qwen27b", "batched"])
+def test_decode_step(name):
+    """kvq_decode_step (append one token, seal if full, decode) step after step:
+    one fused launch while every new token lands in the ring and no seal is due,
+    the three calls otherwise (a sequence still in the sink, a seal step).  Ring
+    bytes stay bit-exact with the oracle's appends; the attention of each step
+    is checked against float64 attention over the oracle cache (records
+    imported from the oracle; on a seal step the just-sealed records are the
+    GPU's own, hence the looser bound of a GPU-built cache there)."""
+    steps = 40
+    if name == "qwen27b":  # ring 360 after the build: the seal fires at step 24
+        w = configs.QWEN27B.scaled(n_layers=2, tail_min=256, tail_max=384, ctx=1000)
+        lens = [1000]
+    else:                  # one sequence starts in the sink: unfused until it leaves it
+        w = configs.BATCHED.scaled(n_layers=1, n_kv_heads=2, n_q_heads=12, tail_min=256, tail_max=384, ctx=1000)
+        lens = [1000, 897, 120]
+    _say(f"[step {name}] build lens={lens}")
+    p = Pair(w, lens, extra_ctx=steps).build(128)
+    p.import_oracle_records()
+    t = p.torch
+    seqs = list(range(p.n))
+    n_seal_steps = 0
+    for st in range(steps):
+        for l in range(w.n_layers):
+            pos = [p.ora.info(s, l)[0] for s in seqs]
+            k = np.stack([p.specs[s].tokens(l, "k", pos[s], 1)[0] for s in seqs])
+            v = np.stack([p.specs[s].tokens(l, "v", pos[s], 1)[0] for s in seqs])
+            q = inputs.queries(w.seed, 100 + st, l, p.n, w.n_q_heads, w.head_dim)
+            rec0 = [p.ora.info(s, l)[1] for s in seqs]
+            out, g = p.gpu.decode_step(l, seqs, t.from_numpy(k).cuda(), t.from_numpy(v).cuda(),
+                                       t.from_numpy(q).cuda(), scale=0.9)
+            assert p.ora.append(l, seqs, k[:, None], v[:, None]) == ocache.OK
+            assert g == p.ora.seal(l, ocache.SEAL_IF_FULL)
+            got = out.cpu().numpy().astype(np.float64)
+            tol = 2e-2 if g else ATTN_TOL
+            n_seal_steps += g > 0
+            for s in seqs:
+                ref = p.ora.attention(l, s, q[s], 0.9)
+                err = float(np.max(np.abs(got[s] - ref)) / np.sqrt(np.mean(ref ** 2)))
+                assert err <= tol, (st, l, s, err, g)
+            if g:
+                p.import_oracle_records(first=min(rec0))
+    _say(f"[step {name}] {steps} steps, {n_seal_steps} seal steps")
+    assert n_seal_steps > 0
+    p.check_info()
+    assert p.check_sink_ring() > 0
 
 
 def test_decode_deterministic():

@@ -161,7 +161,7 @@ __device__ __forceinline__ void query_rows(const DecodeArgs& a, int b, int h, bo
 
 // ---------------------------------------------------------------------------
 // Body role: one chunk of records of one KV head.
-//   q~:      wave w forms the q~ operands of k-steps 2w, 2w+1 and shares them;
+//   q~:      wave w forms the q~ operands of k-steps 2w, 2w+1 (live rows) and shares them;
 //   scores:  wave w takes token tiles 2w, 2w+1 (32 tokens) over all channels;
 //   values:  wave w takes channel tiles 4w..4w+3 (64 channels) over all tokens.
 // Key and value codes go from memory straight into the registers of the lane
@@ -186,25 +186,30 @@ __device__ __forceinline__ int slot_token(int p) {  // token at position p (0..7
 }
 
 // q~ operands (hi, lo) of k-steps 2 wave, 2 wave + 1 from the key scales C,
-// and this wave's part of sigma = sum q~
+// for the live query rows only: lane (i, g, kk) = (lane & 7, (lane >> 3) & 3,
+// 2 wave + (lane >> 5)) forms the 8 slots of row i (and i + 8 when the group has
+// more than 8 heads) that lane group g of k-step kk feeds to the matrix core;
+// rows past 8 (or 16) are never written and stay zero.  Also this wave's part
+// of sigma = sum q~ per row.
 __device__ __forceinline__ void make_qtilde(const uint8_t* km, const uint4 (&qph)[2], const uint4 (&qpl)[2],
-                                            uint4 (*qt)[2][64], float (*xs)[16], int wave, int lane) {
-  const int g = lane >> 4;
+                                            uint4 (*qt)[2][64], float (*xs)[16], int G, int wave, int lane) {
+  const int i = lane & 7, g = (lane >> 3) & 3, kk = 2 * wave + (lane >> 5);
   const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
-  float a1 = 0.0f, a16 = 0.0f;
+  const uint4 c = *(const uint4*)(km + 2 * (128 * (kk >> 2) + 32 * g + 8 * (kk & 3)));
+  const uint32_t c04 = __builtin_amdgcn_perm(c.z, c.x, 0x05040100u);
+  const uint32_t c15 = __builtin_amdgcn_perm(c.z, c.x, 0x07060302u);
+  const uint32_t c26 = __builtin_amdgcn_perm(c.w, c.y, 0x05040100u);
+  const uint32_t c37 = __builtin_amdgcn_perm(c.w, c.y, 0x07060302u);
+  const int np = G > 8 ? 2 : 1;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int kk = 2 * wave + i, s = kk >> 2, e = kk & 3;
-    const uint4 c = *(const uint4*)(km + 2 * (128 * s + 32 * g + 8 * e));
-    const uint32_t c04 = __builtin_amdgcn_perm(c.z, c.x, 0x05040100u);
-    const uint32_t c15 = __builtin_amdgcn_perm(c.z, c.x, 0x07060302u);
-    const uint32_t c26 = __builtin_amdgcn_perm(c.w, c.y, 0x05040100u);
-    const uint32_t c37 = __builtin_amdgcn_perm(c.w, c.y, 0x07060302u);
+  for (int p = 0; p < 2; ++p) {
+    if (p >= np) break;
     uint4 hi, lo;
-    qtilde_pair(qph[i].x, qpl[i].x, c04, hi.x, lo.x);
-    qtilde_pair(qph[i].y, qpl[i].y, c15, hi.y, lo.y);
-    qtilde_pair(qph[i].z, qpl[i].z, c26, hi.z, lo.z);
-    qtilde_pair(qph[i].w, qpl[i].w, c37, hi.w, lo.w);
+    qtilde_pair(qph[p].x, qpl[p].x, c04, hi.x, lo.x);
+    qtilde_pair(qph[p].y, qpl[p].y, c15, hi.y, lo.y);
+    qtilde_pair(qph[p].z, qpl[p].z, c26, hi.z, lo.z);
+    qtilde_pair(qph[p].w, qpl[p].w, c37, hi.w, lo.w);
+    float a1 = 0.0f, a16 = 0.0f;
     a1 = __builtin_amdgcn_fdot2(as_h2(hi.x), ones, a1, false);
     a1 = __builtin_amdgcn_fdot2(as_h2(lo.x), ones, a1, false);
     a16 = __builtin_amdgcn_fdot2(as_h2(hi.y), ones, a16, false);
@@ -213,11 +218,14 @@ __device__ __forceinline__ void make_qtilde(const uint8_t* km, const uint4 (&qph
     a1 = __builtin_amdgcn_fdot2(as_h2(lo.z), ones, a1, false);
     a16 = __builtin_amdgcn_fdot2(as_h2(hi.w), ones, a16, false);
     a16 = __builtin_amdgcn_fdot2(as_h2(lo.w), ones, a16, false);
-    qt[kk][0][lane] = hi;
-    qt[kk][1][lane] = lo;
+    qt[kk][0][16 * g + i + 8 * p] = hi;
+    qt[kk][1][16 * g + i + 8 * p] = lo;
+    float part = fmaf(16.0f, a16, a1);
+    part += __shfl_xor(part, 8, 64);
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    if ((lane >> 3) == 0) xs[wave][i + 8 * p] = part;
   }
-  const float part = xsum4(a1) + 16.0f * xsum4(a16);
-  if (g == 0) xs[wave][lane & 15] = part;
 }
 
 // dummy: every lane reads the first 16 bytes of `rec` (one line, result unused)
@@ -267,24 +275,31 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
   float* rows = (float*)qt;
   query_rows<256>(a, b, h, true, rows, wave, lane);
   __syncthreads();
-  uint4 qph[2], qpl[2];  // this wave's k-steps of q' in the nibble slot order
+  uint4 qph[2], qpl[2];  // q' of this lane's q~ slots (make_qtilde), rows i and i + 8
+  {
+    const int ui = lane & 7, ug = (lane >> 3) & 3, ukk = 2 * wave + (lane >> 5);
+    const int base = 128 * (ukk >> 2) + 32 * ug + 8 * (ukk & 3);  // channels of the key dword of lane group ug
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int kk = 2 * wave + i;
-    const int base = 128 * (kk >> 2) + 32 * g + 8 * (kk & 3);  // channels of the key dword of lane group g
-    uint32_t hb[4], lb[4];
+    for (int p = 0; p < 2; ++p) {
+      const float* row = rows + (ui + 8 * p) * 256 + base;  // rows past the group are zero
+      uint32_t hb[4], lb[4];
 #pragma unroll
-    for (int pr = 0; pr < 4; ++pr) {
-      const float f = (pr & 1) ? 0.0625f : 1.0f;  // pairs read from high nibbles carry 1/16
-      split_h2(rows[q16 * 256 + base + pr] * f, rows[q16 * 256 + base + pr + 4] * f, hb[pr], lb[pr]);
+      for (int pr = 0; pr < 4; ++pr) {
+        const float f = (pr & 1) ? 0.0625f : 1.0f;  // pairs read from high nibbles carry 1/16
+        split_h2(row[pr] * f, row[pr + 4] * f, hb[pr], lb[pr]);
+      }
+      qph[p] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
+      qpl[p] = make_uint4(lb[0], lb[1], lb[2], lb[3]);
     }
-    qph[i] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
-    qpl[i] = make_uint4(lb[0], lb[1], lb[2], lb[3]);
   }
+  __syncthreads();  // the query rows are read: the q~ area is cleared (rows make_qtilde skips stay zero)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ((uint4*)qt)[tid + 256 * j] = make_uint4(0, 0, 0, 0);
+  if (tid < 64) (&xs[0][0])[tid] = 0.0f;
   *(uint2*)(mslot(r0) + 8 * tid) = m0;
   if (r0 + 1 < r1) *(uint2*)(mslot(r0 + 1) + 8 * tid) = m1;
   __syncthreads();
-  make_qtilde(mslot(r0), qph, qpl, qt, xs, wave, lane);
+  make_qtilde(mslot(r0), qph, qpl, qt, xs, G, wave, lane);
   uint2 mnext = *(const uint2*)(r0 + 2 < r1 ? rec(r0 + 2) + 32768 + 8 * tid : rec0);
   load_values(rec(r0), vd, wave, lane);
   __syncthreads();
@@ -304,10 +319,21 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
     float4v sh[2], sl[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) sh[i] = sl[i] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+    // q~ operands read from LDS two k-steps ahead of their products
+    half8 qb[8][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      qb[kk][0] = mfma_a(qt[kk][0][lane]);
+      qb[kk][1] = mfma_a(qt[kk][1][lane]);
+    }
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const int s = kk >> 2, e = kk & 3;
-      const half8 bh = mfma_a(qt[kk][0][lane]), bl = mfma_a(qt[kk][1][lane]);
+      if (kk + 2 < 8) {
+        qb[kk + 2][0] = mfma_a(qt[kk + 2][0][lane]);
+        qb[kk + 2][1] = mfma_a(qt[kk + 2][1][lane]);
+      }
+      const half8 bh = qb[kk][0], bl = qb[kk][1];
       half8 av[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) av[i] = nib8_centred(pick(kd[i][s], e));
@@ -381,7 +407,7 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
     }
     zt = xsum4(zt);
     if (g == 0) xz[wave][q16] = zt;
-    if (more) make_qtilde(mslot(r + 1), qph, qpl, qt, xs, wave, lane);
+    if (more) make_qtilde(mslot(r + 1), qph, qpl, qt, xs, G, wave, lane);
     if (r + 2 < r1) *(uint2*)(mslot(r + 2) + 8 * tid) = mnext;
     mnext = *(const uint2*)(r + 3 < r1 ? rec(r + 3) + 32768 + 8 * tid : rec0);
     __syncthreads();  // (B3) weights, zero-point sums; q~ and scales of r + 1, r + 2

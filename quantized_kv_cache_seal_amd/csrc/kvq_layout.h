@@ -96,6 +96,8 @@ struct DecodeArgs {
   int32_t ring_chunk;    // ring tokens per chunk
   int32_t n_app_items;   // fused decode step: one append item per (sequence, KV head), first
   int32_t n_body_items;  // matrix-core launch: body items, after the append items
+  int32_t n_old;         // matrix-core launch: workgroups 0 .. n_old - 1 are the first resident on
+                         // their compute unit (issue priority): they take more records
   int32_t valu_regions;  // bit r set: the vector-ALU kernel scans region r (0 sink, 1 ring, 2 body)
   uint32_t signs[8];
   unsigned long long* prof_ts;  // profiling: {first start, last end} wall-clock stamps, or null

@@ -140,10 +140,13 @@ static constexpr int kStagedRingChunk = 256; // ring tokens per chunk next to a 
 static constexpr int kBodyWgPerCu = 2;       // resident workgroups per CU of the fused kernel
 
 // Matrix-core plan.  Work in units of one record (about one 64-token ring
-// step; the sink is two).  Every work item should take about the average work
-// per resident workgroup, so that all of them run in one round: ring chunks
-// of that many steps, and the remaining slots split evenly among the body
-// records (body items are issued first).
+// step; the sink is two).  All work items run in one round, two workgroups per
+// compute unit; the first workgroup on a unit (grid index below the unit
+// count) scans 1.3 times as fast as the second (the kernel gives it that much
+// more of the records).  T = work / capacity is the time of the round in
+// second-workgroup records; ring chunks take floor(T) steps (ring items come
+// last in the grid, second on their unit), the remaining slots split the
+// body records (body items are issued first).
 struct MfmaPlan {
   int ring_chunk;
   int body_slots;      // workgroups left for body chunks
@@ -159,10 +162,12 @@ static MfmaPlan mfma_plan(const kvq_cache* c, const std::vector<int64_t>& n_rec,
   }
   // `reserved` workgroups (the append items of a fused step) are short and
   // leave their slots idle once done
-  const int slots = std::max(1, kBodyWgPerCu * (c->n_cu ? c->n_cu : 256) - reserved);
-  const double per = std::max(1.0, (body + other) / slots);
+  const int n_cu = c->n_cu ? c->n_cu : 256;
+  const int slots = std::max(1, kBodyWgPerCu * n_cu - reserved);
+  const double capacity = std::max(1.0, slots + 0.3 * std::min(n_cu, slots));
+  const double per = std::max(1.0, (body + other) / capacity);
   MfmaPlan p;
-  p.ring_chunk = kRingStep * std::max(1, (int)std::lround(per));
+  p.ring_chunk = kRingStep * std::max(1, (int)std::floor(per));
   int64_t ring_items = 0;
   for (size_t i = 0; i < ring.size(); ++i) ring_items += (int64_t)H * (1 + (ring[i] + p.ring_chunk - 1) / p.ring_chunk);
   p.body_slots = (int)std::max<int64_t>(H, slots - ring_items);
@@ -474,6 +479,7 @@ static kvq_status decode_impl(kvq_cache* c, int32_t layer, const int32_t* seq_id
     if (use_mfma) {
       a.n_app_items = fused ? a.n_seqs * c->y.H : 0;
       a.n_body_items = n_body_items;
+      a.n_old = c->n_cu ? c->n_cu : 256;
       e = launch_decode_main(a, a.n_app_items + n_body_items + n_ring_items, (hipStream_t)stream);
       if (e != hipSuccess) return hip_fail(e, "decode launch");
     } else {

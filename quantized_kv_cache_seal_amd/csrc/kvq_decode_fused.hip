@@ -192,7 +192,7 @@ constexpr int kBodyQt = 0, kBodyPw = 16384, kBodyM = kBodyPw + 2 * 16 * kPPitch 
 constexpr int kBodyLds = kBodyX + 3 * 256;
 static_assert(16 * 256 * 4 == 8 * 2 * 64 * 16, "query rows must fit the q~ area");
 
-constexpr int kWOld = 13, kWYoung = 10;  // record shares of the first and second workgroup of a compute unit
+constexpr int kWOld = 14, kWYoung = 10;  // record shares of the first and second workgroup of a compute unit
 
 __device__ __forceinline__ int slot_token(int p) {  // token at position p (0..7) of an 8-token group
   return (p >> 1) + 4 * (p & 1);
@@ -274,7 +274,7 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
 
   // Partition of the sequence's records over its chunks.  The first workgroup
   // to land on a compute unit (grid index below n_old) wins the issue
-  // arbitration against the second and scans a record ~1.3 times as fast
+  // arbitration against the second and scans a record ~1.4 times as fast
   // (measured), so it takes kWOld records for every kWYoung of the second,
   // and both end together; with few records per chunk the split is even.
   const int nb = sq.n_body_chunks;
@@ -864,6 +864,14 @@ constexpr int kMainLds = kBodyLds > RingLds<256>::total ? kBodyLds : RingLds<256
 // chunk i / H), so that every head gets its share of first and second
 // workgroups of the compute units; sink/ring items are head-major.
 __device__ __forceinline__ bool find_item(const DecodeArgs& a, int item, bool body, int& b, int& h, int& c) {
+  if (a.n_seqs == 1) {  // no loop: sequence 0's fields are already in registers
+    b = 0;
+    const int per = body ? a.seq[0].n_body_chunks : 1 + a.seq[0].n_ring_chunks;
+    if (item >= a.y.H * per) return false;
+    h = body ? item % a.y.H : item / per;
+    c = body ? item / a.y.H : item % per;
+    return true;
+  }
   for (b = 0; b < a.n_seqs; ++b) {
     const int per = body ? a.seq[b].n_body_chunks : 1 + a.seq[b].n_ring_chunks;
     const int n = a.y.H * per;
@@ -887,6 +895,19 @@ void decode_main_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kMainLds];
   int b, h, c;
   int item = blockIdx.x;
+  // Each dependent round of kernel-argument loads costs a trip to memory at
+  // the start of every workgroup; the fields the work items start from are
+  // read in one round (empty asm statements consuming them keep the compiler
+  // from spreading the loads over the branches that use them).
+  {
+    const DecodeSeq& s0 = a.seq[0];
+    asm volatile("" ::"s"(a.n_app_items), "s"(a.n_body_items), "s"(a.n_seqs), "s"(a.y.H), "s"(a.y.cap),
+                 "s"(s0.slot), "s"(s0.n_sink), "s"(s0.ring_len), "s"(s0.ring0), "s"(s0.n_rec), "s"(s0.n_ring_chunks),
+                 "s"(s0.n_body_chunks), "s"(s0.app_slot), "s"(s0.app_chunk));
+    asm volatile("" ::"s"(a.arena), "s"(a.q), "s"(a.part), "s"(a.prof_ts), "s"(a.y.off_body), "s"(a.y.rec_bytes),
+                 "s"(a.y.max_rec), "s"(a.y.L), "s"(a.layer), "s"(a.Hq), "s"(a.g), "s"(a.scale), "s"(a.max_chunks),
+                 "s"(a.n_old), "s"(a.ring_chunk));
+  }
   prof_start(a.prof_ts);
   if (item < a.n_app_items) {
     append_role(a, item / a.y.H, item % a.y.H, smem);

@@ -142,7 +142,7 @@ static constexpr int kBodyWgPerCu = 2;       // resident workgroups per CU of th
 // Matrix-core plan.  Work in units of one record (about one 64-token ring
 // step; the sink is two).  All work items run in one round, two workgroups per
 // compute unit; the first workgroup on a unit (grid index below the unit
-// count) scans 1.3 times as fast as the second (the kernel gives it that much
+// count) scans 1.4 times as fast as the second (the kernel gives it that much
 // more of the records).  T = work / capacity is the time of the round in
 // second-workgroup records; ring chunks take floor(T) steps (ring items come
 // last in the grid, second on their unit), the remaining slots split the
@@ -164,7 +164,7 @@ static MfmaPlan mfma_plan(const kvq_cache* c, const std::vector<int64_t>& n_rec,
   // leave their slots idle once done
   const int n_cu = c->n_cu ? c->n_cu : 256;
   const int slots = std::max(1, kBodyWgPerCu * n_cu - reserved);
-  const double capacity = std::max(1.0, slots + 0.3 * std::min(n_cu, slots));
+  const double capacity = std::max(1.0, slots + 0.4 * std::min(n_cu, slots));
   const double per = std::max(1.0, (body + other) / capacity);
   MfmaPlan p;
   p.ring_chunk = kRingStep * std::max(1, (int)std::floor(per));

@@ -321,8 +321,10 @@ kvq_status kvq_seal(kvq_cache* c, int32_t layer, int32_t mode, void* stream, int
   if (mode != KVQ_SEAL_IF_FULL && mode != KVQ_SEAL_TO_MIN) return fail(KVQ_ERR_INVALID, "bad seal mode %d", mode);
   int64_t total = 0;
   const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c->y.L : layer + 1;
+  // every (sequence, layer) with groups due, all layers in the same launches:
+  // the tiles are independent, and one wide launch keeps the whole GPU busy
+  std::vector<SealTask> tasks;
   for (int l = l0; l < l1; ++l) {
-    std::vector<SealTask> tasks;
     for (int s = 0; s < c->y.S; ++s) {
       const int64_t g = groups_to_seal(c->ring_len(s, l), c->cfg, mode);
       if (g <= 0) continue;
@@ -333,27 +335,27 @@ kvq_status kvq_seal(kvq_cache* c, int32_t layer, int32_t mode, void* stream, int
       t.n_groups = (int32_t)g;
       tasks.push_back(t);
     }
-    for (size_t t0 = 0; t0 < tasks.size(); t0 += kMaxSealTasks) {
-      SealArgs a{};
-      a.arena = c->arena;
-      a.y = c->y;
-      a.passes = c->cfg.sinkhorn_passes;
-      a.n_tasks = (int32_t)std::min<size_t>(kMaxSealTasks, tasks.size() - t0);
-      int32_t first = 0;
-      for (int i = 0; i < a.n_tasks; ++i) {
-        a.task[i] = tasks[t0 + i];
-        a.task[i].first = first;
-        first += a.task[i].n_groups;
-      }
-      a.total_groups = first;
-      if (!c->plan_only) {
-        hipError_t e = launch_seal(a, (hipStream_t)stream);
-        if (e != hipSuccess) return hip_fail(e, "seal launch");
-      }
-      for (int i = 0; i < a.n_tasks; ++i) {
-        c->rec(a.task[i].slot, l) += a.task[i].n_groups;
-        total += a.task[i].n_groups;
-      }
+  }
+  for (size_t t0 = 0; t0 < tasks.size(); t0 += kMaxSealTasks) {
+    SealArgs a{};
+    a.arena = c->arena;
+    a.y = c->y;
+    a.passes = c->cfg.sinkhorn_passes;
+    a.n_tasks = (int32_t)std::min<size_t>(kMaxSealTasks, tasks.size() - t0);
+    int32_t first = 0;
+    for (int i = 0; i < a.n_tasks; ++i) {
+      a.task[i] = tasks[t0 + i];
+      a.task[i].first = first;
+      first += a.task[i].n_groups;
+    }
+    a.total_groups = first;
+    if (!c->plan_only) {
+      hipError_t e = launch_seal(a, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e, "seal launch");
+    }
+    for (int i = 0; i < a.n_tasks; ++i) {
+      c->rec(a.task[i].slot, a.task[i].layer) += a.task[i].n_groups;
+      total += a.task[i].n_groups;
     }
   }
   if (groups_sealed) *groups_sealed = (int32_t)total;

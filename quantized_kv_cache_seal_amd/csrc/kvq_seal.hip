@@ -16,8 +16,10 @@
 // current factors; the updated side's factor becomes 1/spread (equal to
 // exp(-l) of the log-domain update l += ln spread).
 //
-// Rounding is IEEE fp32 with no fused multiply-add (built with
-// -ffp-contract=off): y = x * fp32(1/C), S = fp16((max - min) / (2^b - 1))
+// The balancing factors (1/spread, ln spread) use the hardware square root,
+// reciprocal and log2 (about 1 ulp): only the column scales C leave the
+// balancing, and they are rounded to fp16.  Rounding is IEEE fp32 with no
+// fused multiply-add (built with -ffp-contract=off): y = x * fp32(1/C), S = fp16((max - min) / (2^b - 1))
 // (1.0 if zero), Z = fp16(min), code = clamp(rne((y - Z) * fp32(1/S)), 0, 2^b - 1).
 #include "kvq_device.h"
 
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(256) void seal_kernel(SealArgs a) {
         }
         const float mean = sm / (float)COLS;
         const float var = fmaxf(sq / (float)COLS - mean * mean, 0.0f);
-        rf[i] = 1.0f / fmaxf(sqrtf(var), 1e-30f);
+        rf[i] = __builtin_amdgcn_rcpf(fmaxf(__builtin_amdgcn_sqrtf(var), 1e-30f));
       }
     } else {
       float sm[CPT], sq[CPT];
@@ -138,9 +140,9 @@ __global__ __launch_bounds__(256) void seal_kernel(SealArgs a) {
         const float tq = red[0][col0 + j][1] + red[1][col0 + j][1] + red[2][col0 + j][1] + red[3][col0 + j][1];
         const float mean = ts / (float)kGroup;
         const float var = fmaxf(tq / (float)kGroup - mean * mean, 0.0f);
-        const float sig = fmaxf(sqrtf(var), 1e-30f);
-        cf[j] = 1.0f / sig;
-        lc[j] = logf(sig);
+        const float sig = fmaxf(__builtin_amdgcn_sqrtf(var), 1e-30f);
+        cf[j] = __builtin_amdgcn_rcpf(sig);
+        lc[j] = __builtin_amdgcn_logf(sig) * 0.6931471805599453f;  // log2 -> ln
       }
       __syncthreads();
     }

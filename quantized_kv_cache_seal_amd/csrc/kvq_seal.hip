@@ -10,9 +10,9 @@
 //
 // Tile mapping: thread (wave w, lane l = 16 r4 + c16) holds rows 32w + 8r4 + i
 // (i < 8) and columns CPT*c16 + j (j < CPT), CPT = SUB/16, in registers for the
-// whole seal.  A row reduction is in-thread plus a 16-lane xor exchange; a
-// column reduction is in-thread, an xor exchange across r4, then LDS across the
-// four waves.  Each pass computes the spread of x scaled by the other side's
+// whole seal.  A row reduction is in-thread plus a 16-lane DPP exchange; a
+// column reduction is in-thread, a swap exchange across r4, then LDS across
+// the four waves.  Each pass computes the spread of x scaled by the other side's
 // current factors; the updated side's factor becomes 1/spread (equal to
 // exp(-l) of the log-domain update l += ln spread).
 //
@@ -24,6 +24,40 @@
 #include "kvq_device.h"
 
 namespace kvq {
+
+// Reductions over the 16 lanes of a row (DPP: quad swaps, then the half-row
+// and row mirrors; every lane ends with the result) and over the four rows of
+// a wave for the same lane (the 32- and 16-lane swaps of this target: each
+// returns the lane's own value and its partner's, in some order).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum16(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  x += dpp<0x140>(x);  // row_mirror
+  return x;
+}
+__device__ __forceinline__ float min16(float x) {
+  x = fminf(x, dpp<0xB1>(x));
+  x = fminf(x, dpp<0x4E>(x));
+  x = fminf(x, dpp<0x141>(x));
+  return fminf(x, dpp<0x140>(x));
+}
+__device__ __forceinline__ float max16(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  return fmaxf(x, dpp<0x140>(x));
+}
+__device__ __forceinline__ float sum_rows4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = __int_as_float(a[0]) + __int_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(b[0]) + __int_as_float(b[1]);
+}
 
 __device__ __forceinline__ uint32_t bits6(const uint32_t* wd, int j) {
   const int p = 6 * j;
@@ -100,11 +134,8 @@ __global__ __launch_bounds__(256) void seal_kernel(SealArgs a) {
           sm += t;
           sq = fmaf(t, t, sq);
         }
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) {
-          sm += shfl_xor_f(sm, m);
-          sq += shfl_xor_f(sq, m);
-        }
+        sm = sum16(sm);
+        sq = sum16(sq);
         const float mean = sm / (float)COLS;
         const float var = fmaxf(sq / (float)COLS - mean * mean, 0.0f);
         rf[i] = __builtin_amdgcn_rcpf(fmaxf(__builtin_amdgcn_sqrtf(var), 1e-30f));
@@ -121,10 +152,8 @@ __global__ __launch_bounds__(256) void seal_kernel(SealArgs a) {
           sm[j] += t;
           sq[j] = fmaf(t, t, sq[j]);
         }
-        sm[j] += shfl_xor_f(sm[j], 16);
-        sq[j] += shfl_xor_f(sq[j], 16);
-        sm[j] += shfl_xor_f(sm[j], 32);
-        sq[j] += shfl_xor_f(sq[j], 32);
+        sm[j] = sum_rows4(sm[j]);
+        sq[j] = sum_rows4(sq[j]);
       }
       if (r4 == 0) {
 #pragma unroll
@@ -152,8 +181,7 @@ __global__ __launch_bounds__(256) void seal_kernel(SealArgs a) {
   float ls = 0.0f;
 #pragma unroll
   for (int j = 0; j < CPT; ++j) ls += lc[j];
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) ls += shfl_xor_f(ls, m);
+  ls = sum16(ls);
   const float lmean = ls / (float)COLS;
   uint16_t Cb[CPT];
   float invC[CPT];
@@ -182,11 +210,8 @@ __global__ __launch_bounds__(256) void seal_kernel(SealArgs a) {
       mn = fminf(mn, yv[j]);
       mx = fmaxf(mx, yv[j]);
     }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-      mn = fminf(mn, shfl_xor_f(mn, m));
-      mx = fmaxf(mx, shfl_xor_f(mx, m));
-    }
+    mn = min16(mn);
+    mx = max16(mx);
     uint16_t Sb = f2h_sat_bits((mx - mn) / levels);
     if (h2f(Sb) == 0.0f) Sb = 0x3C00;  // 1.0
     const uint16_t Zb = f2h_sat_bits(mn);

@@ -73,7 +73,7 @@ def seal_flops_per_tile(passes, rows=128, cols=256):
 
 
 def run_decode(args, w, torch, kvq, synthetic, inputs):
-    L, H, D, Hq = w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads
+    L, H, D, Hq, N = w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads, w.n_seqs
     W, K = args.warmup, args.steps
     t0 = time.time()
     cache = synthetic.build(w, ctx=w.ctx, max_ctx=w.ctx + W + K + 1)
@@ -81,38 +81,43 @@ def run_decode(args, w, torch, kvq, synthetic, inputs):
     path = {"auto": kvq.PATH_AUTO, "valu": kvq.PATH_VALU, "mfma": kvq.PATH_MFMA}[args.path]
     cache.set_decode_path(path)
     dev = "cuda"
-    spec = synthetic.spec_for(w)
-    nk = [[spec.tokens(l, "k", w.ctx + s, 1, backend="torch", device=dev)[None].contiguous() for l in range(L)]
+    seqs = list(range(N))
+    specs = [synthetic.spec_for(w, s) for s in seqs]
+    # per layer: the new tokens of every step, [step][sequence][H][D], contiguous per step
+    nk, nv = [], []
+    for l in range(L):
+        for kind, dst in (("k", nk), ("v", nv)):
+            t = torch.stack([sp.tokens(l, kind, w.ctx, W + K, backend="torch", device=dev) for sp in specs], dim=1)
+            dst.append(t.contiguous())
+    qs = [[inputs.queries(w.seed, s, l, N, Hq, D, backend="torch", device=dev).contiguous() for l in range(L)]
           for s in range(W + K)]
-    nv = [[spec.tokens(l, "v", w.ctx + s, 1, backend="torch", device=dev)[None].contiguous() for l in range(L)]
-          for s in range(W + K)]
-    qs = [[inputs.queries(w.seed, s, l, 1, Hq, D, backend="torch", device=dev).contiguous() for l in range(L)]
-          for s in range(W + K)]
-    out = torch.empty((L, 1, Hq, D), dtype=torch.float32, device=dev)
-    ws = cache.workspace(1)
+    out = torch.empty((L, N, Hq, D), dtype=torch.float32, device=dev)
+    ws = cache.workspace(N)
     stream = torch.cuda.current_stream()
 
-    # host-side counts of every layer, advanced by the step itself (one token
-    # appended, minus 128 per group the seal check seals), so that the timed
-    # loop makes no extra calls
-    state = [list(cache.info(0, l)) for l in range(L)]   # [n_tok, n_rec, ring]
+    # host-side counts of every (sequence, layer), advanced by the step itself
+    # (one token appended; a seal, which is rare, re-reads the counts), so
+    # that the timed loop makes no extra calls
+    state = [[list(cache.info(s, l)) for s in seqs] for l in range(L)]   # [n_tok, n_rec, ring]
     rec_bytes = cache.unit_bytes(kvq.REGION_BODY)
 
     def one_step(s):
         nbytes = 0
         for l in range(L):
             if args.calls:
-                cache.append(l, [0], nk[s][l], nv[s][l], stream=stream)
+                cache.append(l, seqs, nk[l][s], nv[l][s], stream=stream)
                 g = cache.seal(l, kvq.SEAL_IF_FULL, stream=stream)
-                cache.attn_decode(l, [0], qs[s][l], out=out[l], workspace=ws, stream=stream)
+                cache.attn_decode(l, seqs, qs[s][l], out=out[l], workspace=ws, stream=stream)
             else:
-                _, g = cache.decode_step(l, [0], nk[s][l], nv[s][l], qs[s][l], out=out[l], workspace=ws,
+                _, g = cache.decode_step(l, seqs, nk[l][s], nv[l][s], qs[s][l], out=out[l], workspace=ws,
                                          stream=stream)
-            st = state[l]
-            st[0] += 1
-            st[1] += g
-            st[2] += 1 - 128 * g
-            nbytes += region_bytes(w, rec_bytes, *st)
+            if g:
+                state[l] = [list(cache.info(q, l)) for q in seqs]
+            else:
+                for st in state[l]:
+                    st[0] += 1
+                    st[2] += 1
+            nbytes += sum(region_bytes(w, rec_bytes, *st) for st in state[l])
         return nbytes
 
     for s in range(W):
@@ -136,7 +141,8 @@ def run_decode(args, w, torch, kvq, synthetic, inputs):
     per_call_bytes = bytes_step / L
     avg_kernel_us = sum(kernel_us) / len(kernel_us)
     achieved = per_call_bytes / (avg_kernel_us * 1e-6) / 1e9
-    assert state[0][:2] == list(cache.info(0, 0))[:2] and state[0][2] == cache.info(0, 0)[2]
+    for l in (0, L - 1):
+        assert [list(cache.info(q, l)) for q in seqs] == state[l]
     log(f"[bench] decode: {ms_step * 1e3:.1f} us/step (wall {wall / K * 1e3:.1f} ms), {bytes_step / 1e9:.4f} GB/step, "
         f"{gbs:.1f} GB/s; main decode kernel avg {avg_kernel_us:.1f} us over {len(kernel_us)} calls -> "
         f"{achieved:.1f} GB/s")
@@ -150,28 +156,34 @@ def run_decode(args, w, torch, kvq, synthetic, inputs):
 
 
 def run_seal(args, w, torch, kvq, synthetic):
-    """Seal batch: ring filled to tail_max (8,192) in every layer, then one
-    seal-if-full seals the 32 oldest groups of every layer and head."""
-    L = w.n_layers
+    """Seal batch: the ring of every sequence filled to tail_max in every
+    layer, then one seal-if-full seals the oldest (tail_max - tail_min) / 128
+    groups of every sequence, layer and head: 32 groups per layer in the
+    one-sequence workload (ring 8,192 -> 4,096), 16 x 2 in the batched one
+    (4,352 -> 4,096: the batch its decode steps meet every 256 steps)."""
+    L, N = w.n_layers, w.n_seqs
     ctx = 128 + w.tail_max
     cache = synthetic.build(w, ctx=ctx, max_ctx=ctx, seal_to_min=False, seal_if_full=False, chunk=512)
     ring = cache.info(0, 0)[2]
     assert ring == w.tail_max, ring
-    spec = synthetic.spec_for(w)
+    specs = [synthetic.spec_for(w, s) for s in range(N)]
+    seqs = list(range(N))
     dev = "cuda"
     # the same tokens again after each timed seal (untimed): reset and refill
-    ks = [[spec.tokens(l, "k", t0, min(512, ctx - t0), backend="torch", device=dev)[None].contiguous()
-           for t0 in range(0, ctx, 512)] for l in range(L)]
-    vs = [[spec.tokens(l, "v", t0, min(512, ctx - t0), backend="torch", device=dev)[None].contiguous()
-           for t0 in range(0, ctx, 512)] for l in range(L)]
+    def chunk(l, kind, t0):
+        n = min(512, ctx - t0)
+        return torch.stack([sp.tokens(l, kind, t0, n, backend="torch", device=dev) for sp in specs]).contiguous()
+    ks = [[chunk(l, "k", t0) for t0 in range(0, ctx, 512)] for l in range(L)]
+    vs = [[chunk(l, "v", t0) for t0 in range(0, ctx, 512)] for l in range(L)]
     stream = torch.cuda.current_stream()
     times, groups = [], 0
     for rep in range(args.seal_reps + 1):
         if rep > 0:
-            cache.reset(0)
+            for q in seqs:
+                cache.reset(q)
             for l in range(L):
                 for k, v in zip(ks[l], vs[l]):
-                    cache.append(l, [0], k, v, stream=stream)
+                    cache.append(l, seqs, k, v, stream=stream)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
@@ -183,7 +195,7 @@ def run_seal(args, w, torch, kvq, synthetic):
             groups = g
     ms = sorted(times)[len(times) // 2]
     tokens = groups * 128 // L          # groups summed over layers; every layer seals the same tokens
-    tiles = groups * w.n_kv_heads * 2 * (w.head_dim // 256 if w.head_dim >= 256 else 1)
+    tiles = groups * w.n_kv_heads * 2 * max(1, w.head_dim // 256)
     flops = tiles * seal_flops_per_tile(w.passes, 128, min(w.head_dim, 256))
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"[bench] seal: {groups} groups ({tokens} tokens x {L} layers), {ms * 1e3:.1f} us -> "
@@ -227,7 +239,9 @@ def run_cpu_baseline(w, budget_s):
             oc.attention(0, 0, q, 1.0)
             t_dec += time.perf_counter() - a
             reps += 1
-    nbytes = 128 * 2 * w.head_dim * 2 + ring * 2 * (w.head_dim // 128) * 98 + n_rec * 34816
+    from oracle import record as orecord
+    nbytes = (128 * 2 * w.head_dim * 2 + ring * 2 * (w.head_dim // 128) * 98
+              + n_rec * orecord.record_bytes(w.head_dim, w.k_bits, w.v_bits))
     gbs = nbytes * reps / t_dec / 1e9
     # a sealed token of the full shape is one group-row in every layer and KV head
     seal_tok_s = groups * 128 / t_seal / (w.n_layers * w.n_kv_heads)
@@ -248,6 +262,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--workload", default="qwen27b", choices=["qwen27b", "gemma31b", "qwen14b1m", "batched"],
+                    help="qwen27b (the default, the headline line) or another of the measured shapes")
     ap.add_argument("--calls", action="store_true",
                     help="run each layer's step as kvq_append + kvq_seal + kvq_attn_decode instead of kvq_decode_step")
     ap.add_argument("--seal-reps", type=int, default=5)
@@ -277,11 +293,13 @@ def main():
         log(f"[bench] copy probe: 20 copies of {n} bytes")
         return
     kvq.lib()
-    w = configs.QWEN27B
+    w = {"qwen27b": configs.QWEN27B, "gemma31b": configs.GEMMA31B, "qwen14b1m": configs.QWEN14B1M,
+         "batched": configs.BATCHED}[args.workload]
     dec = run_decode(args, w, torch, kvq, synthetic, inputs)
     seal = None if args.no_seal else run_seal(args, w, torch, kvq, synthetic)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(w, args.cpu_budget)
-    traffic = measured_traffic()
+    mfma_body = w.head_dim == 256 and w.k_bits == 4 and w.v_bits == 4 and args.path != "valu"
+    traffic = measured_traffic() if (args.workload == "qwen27b" and mfma_body) else None
     if traffic is not None:
         traffic = int(traffic)
     res = {
@@ -300,7 +318,7 @@ def main():
         "pct_hbm_peak": round(100 * dec["gbs"] / HBM_PEAK_GBS, 2),
         "config": {
             "workload": w.name, "layers": w.n_layers, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
-            "q_heads": w.n_q_heads, "ctx": w.ctx, "batch": 1, "body_bits": f"{w.k_bits}/{w.v_bits}",
+            "q_heads": w.n_q_heads, "ctx": w.ctx, "batch": w.n_seqs, "body_bits": f"{w.k_bits}/{w.v_bits}",
             "sinkhorn_passes": w.passes, "tail": [w.tail_min, w.tail_max], "decode_path": args.path,
             "step_call": "append+seal+attn_decode" if args.calls else "decode_step",
             "bytes_per_step": int(dec["bytes_step"]),
@@ -308,12 +326,15 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(dec["achieved"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(dec["achieved"] / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "decode_main_kernel (fused sink, ring and body scan of one layer)",
+            "kernel": ("decode_main_kernel (fused sink, ring and body scan of one layer)" if mfma_body else
+                       "decode_valu_kernel (body scan of one layer; sink and ring in decode_ring_kernel)"),
             "bytes_per_launch": int(dec["per_call_bytes"]), "avg_launch_us": round(dec["avg_kernel_us"], 2),
             "traffic_over_algorithmic": None if traffic is None else round(traffic / dec["per_call_bytes"], 4),
         },
         "cpu_baseline": cpu,
     }
+    if seal and w.n_seqs > 1:   # the batched workload meets one seal batch every 256 steps
+        res["amortized_ms_per_step"] = round(dec["ms_per_step"] + seal["ms"] / 256, 4)
     if seal:
         res["seal"] = {
             "tokens_per_s": round(seal["tokens_per_s"], 1), "batch_tokens": seal["tokens"],

@@ -108,7 +108,8 @@ __device__ __forceinline__ void qtilde_pair(uint32_t qh2, uint32_t ql2, uint32_t
 // ---------------------------------------------------------------------------
 // Query rows: the G query heads of KV head h, times scale * log2(e), rotated
 // (R = H/16 for head_dim 256, s2 . H . s1 / sqrt(128) for 128) or not, into
-// rows[16][D] of LDS (rows G..15 zero).  Wave w transforms rows w, w + 4, ...
+// rows[16][D] of LDS (rows G..15 zero; 512-wide heads rotate each 256-point
+// half on its own).  Wave w transforms rows w, w + 4, ...
 // in registers.  query_load issues the loads (first, ahead of the bulk loads
 // of an item, so that waiting for the query does not wait for them);
 // query_rows transforms and stores.  The caller synchronises before reading.
@@ -154,7 +155,7 @@ __device__ __forceinline__ void query_rows(const DecodeArgs& a, const QueryRaw<D
         for (int j = 0; j < VPL; ++j)
           if (sign_neg(a.signs, VPL * lane + j)) v[j] = -v[j];
       }
-      wave_fwht<VPL, D>(v, lane);
+      wave_fwht<VPL, D == 128 ? 128 : 256>(v, lane);  // 512: two 256-point halves
 #pragma unroll
       for (int j = 0; j < VPL; ++j) {
         if (D == 128) {
@@ -172,14 +173,22 @@ __device__ __forceinline__ void query_rows(const DecodeArgs& a, const QueryRaw<D
 
 // ---------------------------------------------------------------------------
 // Body role: one chunk of records of one KV head.
-//   q~:      wave w forms the q~ operands of k-steps 2w, 2w+1 (live rows) and shares them;
+//
+// Record shapes (compile time, BodyShape): a record is NSUB sub-records of
+// SUBW channels, each with its own C, S, Z: 256 channels at 4/4 bits; 128
+// channels with 8-bit keys and 4-bit values; a 512-wide head is two 256 x 4/4
+// sub-records, one per rotation half (SJ-KVaRN section 9).  A key row is 128
+// bytes in every shape (256 nibbles or 128 bytes).  A token's score sums the
+// sub-records' terms; each sub-record's values take their own weights p S^V.
+//   q~:      wave w forms the q~ operands of its k-steps (2 of 8 per 256-channel
+//            sub-record, 1 of 4 at 128 channels) for the live rows and shares them;
 //   scores:  wave w takes token tiles 2w, 2w+1 (32 tokens) over all channels;
-//   values:  wave w takes channel tiles 4w..4w+3 (64 channels) over all tokens.
+//   values:  wave w takes SUBW / 64 channel tiles of every sub-record over all tokens.
 // Key and value codes go from memory straight into the registers of the lane
 // that feeds them to the matrix cores (16 bytes per lane and operand), each
 // set reloaded as soon as its product is done, so that it has the other half
-// of a record's work to land in.  The 2 KB of scales pass through a ring of
-// three LDS areas, loaded two records ahead.  Two barriers per record:
+// of a record's work to land in.  The scales pass through a ring of three LDS
+// areas, loaded two records ahead.  Two barriers per record:
 //   (B2) after the scores: record maxima exchanged;
 //   (B3) after the weights: P', the zero-point sums, q~ and scales of the next
 //        record exchanged.
@@ -188,41 +197,95 @@ __device__ __forceinline__ void query_rows(const DecodeArgs& a, const QueryRaw<D
 // the weights per tile): position P of a tile holds token
 // (P & ~7) + [0, 4, 1, 5, 2, 6, 3, 7][P & 7].
 constexpr int kPPitch = 128 + 8;  // halves per weight row (padding spreads LDS banks)
-constexpr int kBodyQt = 0, kBodyPw = 16384, kBodyM = kBodyPw + 2 * 16 * kPPitch * 2, kBodyX = kBodyM + 3 * 2048;
-constexpr int kBodyLds = kBodyX + 3 * 256;
-static_assert(16 * 256 * 4 == 8 * 2 * 64 * 16, "query rows must fit the q~ area");
-
 constexpr int kWOld = 14, kWYoung = 10;  // record shares of the first and second workgroup of a compute unit
+
+template <int D_, int KB_>
+struct BodyShape {
+  static constexpr int D = D_, KB = KB_;
+  static constexpr int SUBW = D == 128 ? 128 : 256;
+  static constexpr int NSUB = D / SUBW;
+  static constexpr int KK = SUBW / 32;         // k-steps of 32 channels per sub-record
+  static constexpr int KPW = KK / 4;           // k-steps whose q~ one wave forms
+  static constexpr int NP = KPW == 2 ? 2 : 1;  // q~ rows per lane (i and i + 8, or one)
+  static constexpr int VT = SUBW / 64;         // value channel tiles per wave and sub-record
+  static constexpr int KCODE = 128 * SUBW * KB / 8, VCODE = SUBW * 64;
+  static constexpr int META = 4 * (SUBW + 256);  // K and V: C[SUBW], S[128], Z[128] fp16
+  static constexpr int SUB_BYTES = KCODE + VCODE + META;
+  static constexpr int KS = 2 * SUBW, KZ = KS + 256, VM = KZ + 256;  // offsets in the scales: K S, K Z, V C
+  static constexpr float KCENTRE = KB == 8 ? 128.0f : 8.0f;
+  static constexpr int WG_PER_CU = NSUB == 2 ? 1 : 2;  // resident workgroups per compute unit
+  static constexpr int MSTRIDE = 2048;                 // LDS bytes per sub-record's scales
+  // LDS: q~ operands [NSUB][KK][hi, lo][64 lanes]; weights [NSUB][hi, lo][16][kPPitch];
+  // scales [3][NSUB][MSTRIDE]; exchange xm[4][16], xz[NSUB][4][16], xs[NSUB][4][16]
+  static constexpr int QT = 0, PW = QT + NSUB * KK * 2 * 64 * 16, MB = PW + NSUB * 2 * 16 * kPPitch * 2;
+  static constexpr int X = MB + 3 * NSUB * MSTRIDE;
+  static constexpr int total = X + (1 + 2 * NSUB) * 256;
+  static_assert(SUBW * KB / 8 == 128 && KCODE == 16384, "key rows of 128 bytes");
+  static_assert(16 * D * 4 <= PW - QT, "query rows must fit the q~ area");
+  static_assert(META <= MSTRIDE, "scales of a sub-record fit one LDS area");
+  // first channel of the 8 that lane group g feeds to the score product at k-step kk
+  static __device__ __forceinline__ int kbase(int kk, int g) {
+    return KB == 4 ? 128 * (kk >> 2) + 32 * g + 8 * (kk & 3) : 64 * (kk >> 1) + 16 * g + 8 * (kk & 1);
+  }
+};
 
 __device__ __forceinline__ int slot_token(int p) {  // token at position p (0..7) of an 8-token group
   return (p >> 1) + 4 * (p & 1);
 }
 
-// q~ operands (hi, lo) of k-steps 2 wave, 2 wave + 1 from the key scales C,
-// for the live query rows only: lane (i, g, kk) = (lane & 7, (lane >> 3) & 3,
-// 2 wave + (lane >> 5)) forms the 8 slots of row i (and i + 8 when the group has
-// more than 8 heads) that lane group g of k-step kk feeds to the matrix core;
-// rows past 8 (or 16) are never written and stay zero.  Also this wave's part
-// of sigma = sum q~ per row.
-__device__ __forceinline__ void make_qtilde(const uint8_t* km, const uint4 (&qph)[2], const uint4 (&qpl)[2],
+// Eight 8-bit codes of two dwords as exact, centred fp16 values n - 128 in
+// channel order: one byte permute per pair places each byte under the
+// exponent pattern of 1024 (giving 1024 + n exactly), one packed subtract
+// removes 1152.
+__device__ __forceinline__ half8 byte8_centred(uint32_t w0, uint32_t w1) {
+  const uint32_t e = 0x64646464u;
+  uint4 u;
+  u.x = __builtin_amdgcn_perm(e, w0, 0x04010400u);
+  u.y = __builtin_amdgcn_perm(e, w0, 0x04030402u);
+  u.z = __builtin_amdgcn_perm(e, w1, 0x04010400u);
+  u.w = __builtin_amdgcn_perm(e, w1, 0x04030402u);
+  const half8 off = {(_Float16)1152.0f, (_Float16)1152.0f, (_Float16)1152.0f, (_Float16)1152.0f,
+                     (_Float16)1152.0f, (_Float16)1152.0f, (_Float16)1152.0f, (_Float16)1152.0f};
+  return mfma_a(u) - off;
+}
+
+// q~ operands (hi, lo) of this wave's k-steps of one sub-record from its key
+// scales C, for the live query rows only.  Lane (i, g) = (lane & 7,
+// (lane >> 3) & 3) forms the 8 slots of row i (and i + 8 when the group has
+// more than 8 heads) that lane group g of k-step 2 wave + (lane >> 5) feeds to
+// the matrix core; at 128 channels (one k-step per wave) the lane's row is
+// i + 8 (lane >> 5).  Rows never written stay zero.  Also this wave's part of
+// sigma = sum q~ per row.
+template <class Sh>
+__device__ __forceinline__ void make_qtilde(const uint8_t* km, const uint4 (&qph)[Sh::NP], const uint4 (&qpl)[Sh::NP],
                                             uint4 (*qt)[2][64], float (*xs)[16], int G, int wave, int lane) {
-  const int i = lane & 7, g = (lane >> 3) & 3, kk = 2 * wave + (lane >> 5);
+  const int i = lane & 7, g = (lane >> 3) & 3, h5 = lane >> 5;
+  const int kk = Sh::KPW == 2 ? 2 * wave + h5 : wave;
   const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
-  const uint4 c = *(const uint4*)(km + 2 * (128 * (kk >> 2) + 32 * g + 8 * (kk & 3)));
-  const uint32_t c04 = __builtin_amdgcn_perm(c.z, c.x, 0x05040100u);
-  const uint32_t c15 = __builtin_amdgcn_perm(c.z, c.x, 0x07060302u);
-  const uint32_t c26 = __builtin_amdgcn_perm(c.w, c.y, 0x05040100u);
-  const uint32_t c37 = __builtin_amdgcn_perm(c.w, c.y, 0x07060302u);
-  const int np = G > 8 ? 2 : 1;
+  const uint4 c = *(const uint4*)(km + 2 * Sh::kbase(kk, g));
+  uint32_t cp[4];
+  if constexpr (Sh::KB == 4) {  // slot pairs (n0, n4), (n1, n5), (n2, n6), (n3, n7)
+    cp[0] = __builtin_amdgcn_perm(c.z, c.x, 0x05040100u);
+    cp[1] = __builtin_amdgcn_perm(c.z, c.x, 0x07060302u);
+    cp[2] = __builtin_amdgcn_perm(c.w, c.y, 0x05040100u);
+    cp[3] = __builtin_amdgcn_perm(c.w, c.y, 0x07060302u);
+  } else {  // channel order
+    cp[0] = c.x;
+    cp[1] = c.y;
+    cp[2] = c.z;
+    cp[3] = c.w;
+  }
+  const int np = Sh::NP == 2 && G > 8 ? 2 : 1;
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
+  for (int p = 0; p < Sh::NP; ++p) {
     if (p >= np) break;
+    const int row = Sh::KPW == 2 ? i + 8 * p : i + 8 * h5;
     uint4 hi, lo;
-    qtilde_pair(qph[p].x, qpl[p].x, c04, hi.x, lo.x);
-    qtilde_pair(qph[p].y, qpl[p].y, c15, hi.y, lo.y);
-    qtilde_pair(qph[p].z, qpl[p].z, c26, hi.z, lo.z);
-    qtilde_pair(qph[p].w, qpl[p].w, c37, hi.w, lo.w);
-    float a1 = 0.0f, a16 = 0.0f;
+    qtilde_pair(qph[p].x, qpl[p].x, cp[0], hi.x, lo.x);
+    qtilde_pair(qph[p].y, qpl[p].y, cp[1], hi.y, lo.y);
+    qtilde_pair(qph[p].z, qpl[p].z, cp[2], hi.z, lo.z);
+    qtilde_pair(qph[p].w, qpl[p].w, cp[3], hi.w, lo.w);
+    float a1 = 0.0f, a16 = 0.0f;  // 4-bit keys: slots y and w carry 1/16
     a1 = __builtin_amdgcn_fdot2(as_h2(hi.x), ones, a1, false);
     a1 = __builtin_amdgcn_fdot2(as_h2(lo.x), ones, a1, false);
     a16 = __builtin_amdgcn_fdot2(as_h2(hi.y), ones, a16, false);
@@ -231,18 +294,18 @@ __device__ __forceinline__ void make_qtilde(const uint8_t* km, const uint4 (&qph
     a1 = __builtin_amdgcn_fdot2(as_h2(lo.z), ones, a1, false);
     a16 = __builtin_amdgcn_fdot2(as_h2(hi.w), ones, a16, false);
     a16 = __builtin_amdgcn_fdot2(as_h2(lo.w), ones, a16, false);
-    qt[kk][0][16 * g + i + 8 * p] = hi;
-    qt[kk][1][16 * g + i + 8 * p] = lo;
-    float part = fmaf(16.0f, a16, a1);
+    qt[kk][0][16 * g + row] = hi;
+    qt[kk][1][16 * g + row] = lo;
+    float part = Sh::KB == 4 ? fmaf(16.0f, a16, a1) : a1 + a16;
     part += __shfl_xor(part, 8, 64);
     part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
-    if ((lane >> 3) == 0) xs[wave][i + 8 * p] = part;
+    if (Sh::KPW == 2) part += __shfl_xor(part, 32, 64);
+    if (Sh::KPW == 2 ? (lane >> 3) == 0 : ((lane >> 3) & 3) == 0) xs[wave][row] = part;
   }
 }
 
-// dummy: every lane reads the first 16 bytes of `rec` (one line, result unused)
-__device__ __forceinline__ void load_keys(const uint8_t* __restrict__ rec, uint4 (&kd)[2][2], int wave, int lane,
+// dummy: every lane reads the first 16 bytes of `sub` (one line, result unused)
+__device__ __forceinline__ void load_keys(const uint8_t* __restrict__ sub, uint4 (&kd)[2][2], int wave, int lane,
                                           bool dummy = false) {
   const int m = lane & 15, g = lane >> 4;
   const int row = (m & 8) + slot_token(m & 7);
@@ -250,36 +313,42 @@ __device__ __forceinline__ void load_keys(const uint8_t* __restrict__ rec, uint4
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-      kd[i][s] = *(const uint4*)(rec + (dummy ? 0 : (16 * (2 * wave + i) + row) * 128 + 64 * s + 16 * g));
+      kd[i][s] = *(const uint4*)(sub + (dummy ? 0 : (16 * (2 * wave + i) + row) * 128 + 64 * s + 16 * g));
 }
-__device__ __forceinline__ void load_values(const uint8_t* __restrict__ rec, uint4 (&vd)[4], int wave, int lane,
+template <class Sh>
+__device__ __forceinline__ void load_values(const uint8_t* __restrict__ sub, uint4 (&vd)[Sh::VT], int wave, int lane,
                                             bool dummy = false) {
   const int m = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) vd[j] = *(const uint4*)(rec + (dummy ? 0 : 16384 + (16 * (4 * wave + j) + m) * 64 + 16 * g));
+  for (int j = 0; j < Sh::VT; ++j)
+    vd[j] = *(const uint4*)(sub + (dummy ? 0 : Sh::KCODE + (16 * (Sh::VT * wave + j) + m) * 64 + 16 * g));
 }
 
+template <class Sh>
 __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int cbk, uint8_t* smem) {
+  constexpr int D = Sh::D, SUBW = Sh::SUBW, NSUB = Sh::NSUB, KK = Sh::KK, VT = Sh::VT, NP = Sh::NP;
+  constexpr int SB = Sh::SUB_BYTES, MS = Sh::MSTRIDE;
   const Layout& y = a.y;
   const DecodeSeq& sq = a.seq[b];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int q16 = lane & 15, g = lane >> 4;
   const int G = a.g;
-  uint4(*qt)[2][64] = (uint4(*)[2][64])(smem + kBodyQt);
-  uint16_t(*pw)[16][kPPitch] = (uint16_t(*)[16][kPPitch])(smem + kBodyPw);
-  uint8_t* mbuf = smem + kBodyM;  // [3][2048] scales of records r, r + 1, r + 2 (mod 3)
-  float(*xm)[16] = (float(*)[16])(smem + kBodyX);
-  float(*xz)[16] = (float(*)[16])(smem + kBodyX + 256);
-  float(*xs)[16] = (float(*)[16])(smem + kBodyX + 512);
+  uint4(*qt)[KK][2][64] = (uint4(*)[KK][2][64])(smem + Sh::QT);
+  uint16_t(*pw)[2][16][kPPitch] = (uint16_t(*)[2][16][kPPitch])(smem + Sh::PW);
+  uint8_t* mbuf = smem + Sh::MB;  // scales of records r, r + 1, r + 2 (mod 3)
+  float(*xm)[16] = (float(*)[16])(smem + Sh::X);
+  float(*xz)[4][16] = (float(*)[4][16])(smem + Sh::X + 256);
+  float(*xs)[4][16] = (float(*)[4][16])(smem + Sh::X + 256 + NSUB * 256);
 
-  // Partition of the sequence's records over its chunks.  The first workgroup
-  // to land on a compute unit (grid index below n_old) wins the issue
-  // arbitration against the second and scans a record ~1.4 times as fast
-  // (measured), so it takes kWOld records for every kWYoung of the second,
-  // and both end together; with few records per chunk the split is even.
+  // Partition of the sequence's records over its chunks.  With two
+  // workgroups per compute unit, the first to land on a unit (grid index below
+  // n_old) wins the issue arbitration against the second and scans a record
+  // ~1.4 times as fast (measured), so it takes kWOld records for every kWYoung
+  // of the second, and both end together; with few records per chunk, or one
+  // workgroup per unit, the split is even.
   const int nb = sq.n_body_chunks;
   int r0, r1;
-  if (sq.n_rec >= 4 * nb) {
+  if (Sh::WG_PER_CU == 2 && sq.n_rec >= 4 * nb) {
     // chunk c of this pair sits at grid index g_base + c H + h (heads interleaved)
     const int g_base = (int)blockIdx.x - cbk * y.H - h;
     const int n_first = max(0, (a.n_old - g_base - h + y.H - 1) / y.H);  // chunks with g < n_old
@@ -295,115 +364,155 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
   }
   const uint8_t* rec0 = a.arena + rec_off(y, sq.slot, a.layer, h, 0);
   auto rec = [&](int r) { return rec0 + (int64_t)r * y.rec_bytes; };
-  auto mslot = [&](int r) { return mbuf + ((r - r0) % 3) * 2048; };
+  auto mslot = [&](int r) { return mbuf + ((r - r0) % 3) * (NSUB * MS); };
+  // this thread's 8 bytes of a sub-record's scales (clamped: threads past the
+  // end re-read the last 8 bytes and store them where nothing reads)
+  const int mo = Sh::KCODE + Sh::VCODE + (Sh::META == 8 * 256 ? 8 * tid : min(8 * tid, Sh::META - 8));
 
   // ---- prologue: the query first, then the scales of r0, r0 + 1 and the key
   // and value codes of r0 in flight while the query is rotated (its rows
-  // borrow the q~ area, 16 x 256 floats)
-  QueryRaw<256> qraw;
-  query_load<256>(a, b, h, wave, lane, qraw);
-  uint2 m0 = *(const uint2*)(rec(r0) + 32768 + 8 * tid);
-  uint2 m1 = *(const uint2*)(r0 + 1 < r1 ? rec(r0 + 1) + 32768 + 8 * tid : rec0);
-  uint4 kd[2][2], vd[4];
-  load_keys(rec(r0), kd, wave, lane);
-  load_values(rec(r0), vd, wave, lane);
+  // borrow the q~ area)
+  QueryRaw<D> qraw;
+  query_load<D>(a, b, h, wave, lane, qraw);
+  uint2 m0[NSUB], m1[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    m0[s] = *(const uint2*)(rec(r0) + s * SB + mo);
+    m1[s] = *(const uint2*)(r0 + 1 < r1 ? rec(r0 + 1) + s * SB + mo : rec0);
+  }
+  uint4 kd[NSUB][2][2], vd[NSUB][VT];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) load_keys(rec(r0) + s * SB, kd[s], wave, lane);
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) load_values<Sh>(rec(r0) + s * SB, vd[s], wave, lane);
   float* rows = (float*)qt;
-  query_rows<256>(a, qraw, true, rows, wave, lane);
+  query_rows<D>(a, qraw, true, rows, wave, lane);
   __syncthreads();
-  uint4 qph[2], qpl[2];  // q' of this lane's q~ slots (make_qtilde), rows i and i + 8
+  uint4 qph[NSUB][NP], qpl[NSUB][NP];  // q' of this lane's q~ slots (make_qtilde)
   {
-    const int ui = lane & 7, ug = (lane >> 3) & 3, ukk = 2 * wave + (lane >> 5);
-    const int base = 128 * (ukk >> 2) + 32 * ug + 8 * (ukk & 3);  // channels of the key dword of lane group ug
+    const int ui = lane & 7, ug = (lane >> 3) & 3, h5 = lane >> 5;
+    const int base = Sh::kbase(Sh::KPW == 2 ? 2 * wave + h5 : wave, ug);  // channels of lane group ug's slots
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const float* row = rows + (ui + 8 * p) * 256 + base;  // rows past the group are zero
-      uint32_t hb[4], lb[4];
+    for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-      for (int pr = 0; pr < 4; ++pr) {
-        const float f = (pr & 1) ? 0.0625f : 1.0f;  // pairs read from high nibbles carry 1/16
-        split_h2(row[pr] * f, row[pr + 4] * f, hb[pr], lb[pr]);
+      for (int p = 0; p < NP; ++p) {
+        const int row_i = Sh::KPW == 2 ? ui + 8 * p : ui + 8 * h5;
+        const float* row = rows + row_i * D + SUBW * s + base;  // rows past the group are zero
+        uint32_t hb[4], lb[4];
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) {
+          if (Sh::KB == 4) {
+            const float f = (pr & 1) ? 0.0625f : 1.0f;  // pairs read from high nibbles carry 1/16
+            split_h2(row[pr] * f, row[pr + 4] * f, hb[pr], lb[pr]);
+          } else {
+            split_h2(row[2 * pr], row[2 * pr + 1], hb[pr], lb[pr]);
+          }
+        }
+        qph[s][p] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
+        qpl[s][p] = make_uint4(lb[0], lb[1], lb[2], lb[3]);
       }
-      qph[p] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
-      qpl[p] = make_uint4(lb[0], lb[1], lb[2], lb[3]);
-    }
   }
   __syncthreads();  // the query rows are read: the q~ area is cleared (rows make_qtilde skips stay zero)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) ((uint4*)qt)[tid + 256 * j] = make_uint4(0, 0, 0, 0);
-  if (tid < 64) (&xs[0][0])[tid] = 0.0f;
-  *(uint2*)(mslot(r0) + 8 * tid) = m0;
-  if (r0 + 1 < r1) *(uint2*)(mslot(r0 + 1) + 8 * tid) = m1;
+  for (int j = 0; j < NSUB * KK / 2; ++j) ((uint4*)qt)[tid + 256 * j] = make_uint4(0, 0, 0, 0);
+  if (tid < 64 * NSUB) (&xs[0][0][0])[tid] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    *(uint2*)(mslot(r0) + s * MS + 8 * tid) = m0[s];
+    if (r0 + 1 < r1) *(uint2*)(mslot(r0 + 1) + s * MS + 8 * tid) = m1[s];
+  }
   __syncthreads();
-  make_qtilde(mslot(r0), qph, qpl, qt, xs, G, wave, lane);
-  uint2 mnext = *(const uint2*)(r0 + 2 < r1 ? rec(r0 + 2) + 32768 + 8 * tid : rec0);
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) make_qtilde<Sh>(mslot(r0) + s * MS, qph[s], qpl[s], qt[s], xs[s], G, wave, lane);
+  uint2 mnext[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) mnext[s] = *(const uint2*)(r0 + 2 < r1 ? rec(r0 + 2) + s * SB + mo : rec0);
   __syncthreads();
 
   float m_run = -INFINITY, l_part = 0.0f;
-  float4v acc[4];
+  float4v acc[NSUB][VT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+    for (int i = 0; i < VT; ++i) acc[s][i] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int r = r0; r < r1; ++r) {
-    const uint8_t* km = mslot(r);
-    const uint8_t* vm = km + 1024;
+    const uint8_t* mr = mslot(r);
     const bool more = r + 1 < r1;
 
-    // ---- scores of tiles 2 wave, 2 wave + 1: four independent accumulation
-    // chains (tile x hi/lo) keep the matrix core busy between dependent products
-    float4v sh[2], sl[2];
+    // ---- scores of tiles 2 wave, 2 wave + 1: independent accumulation chains
+    // (sub-record x tile x hi/lo) keep the matrix core busy between dependent products
+    constexpr int NK = NSUB * KK;
+    float4v sh[NSUB][2], sl[NSUB][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) sh[i] = sl[i] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) sh[s][i] = sl[s][i] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
     // q~ operands read from LDS two k-steps ahead of their products
-    half8 qb[8][2];
+    half8 qb[NK][2];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      qb[kk][0] = mfma_a(qt[kk][0][lane]);
-      qb[kk][1] = mfma_a(qt[kk][1][lane]);
+    for (int k = 0; k < 2; ++k) {
+      qb[k][0] = mfma_a(qt[k / KK][k % KK][0][lane]);
+      qb[k][1] = mfma_a(qt[k / KK][k % KK][1][lane]);
     }
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int s = kk >> 2, e = kk & 3;
-      if (kk + 2 < 8) {
-        qb[kk + 2][0] = mfma_a(qt[kk + 2][0][lane]);
-        qb[kk + 2][1] = mfma_a(qt[kk + 2][1][lane]);
+    for (int k = 0; k < NK; ++k) {
+      const int s = k / KK, kk = k % KK;
+      if (k + 2 < NK) {
+        qb[k + 2][0] = mfma_a(qt[(k + 2) / KK][(k + 2) % KK][0][lane]);
+        qb[k + 2][1] = mfma_a(qt[(k + 2) / KK][(k + 2) % KK][1][lane]);
       }
-      const half8 bh = qb[kk][0], bl = qb[kk][1];
+      const half8 bh = qb[k][0], bl = qb[k][1];
       half8 av[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) av[i] = nib8_centred(pick(kd[i][s], e));
+      for (int i = 0; i < 2; ++i) {
+        if (Sh::KB == 4)
+          av[i] = nib8_centred(pick(kd[s][i][kk >> 2], kk & 3));
+        else
+          av[i] = byte8_centred(pick(kd[s][i][kk >> 1], 2 * (kk & 1)), pick(kd[s][i][kk >> 1], 2 * (kk & 1) + 1));
+      }
 #pragma unroll
-      for (int i = 0; i < 2; ++i) sh[i] = mfma16(av[i], bh, sh[i]);
+      for (int i = 0; i < 2; ++i) sh[s][i] = mfma16(av[i], bh, sh[s][i]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) sl[i] = mfma16(av[i], bl, sl[i]);
+      for (int i = 0; i < 2; ++i) sl[s][i] = mfma16(av[i], bl, sl[s][i]);
     }
-    float4v sc[2] = {sh[0] + sl[0], sh[1] + sl[1]};
-    const float sig = xs[0][q16] + xs[1][q16] + xs[2][q16] + xs[3][q16];
     // this lane's rows are positions 16 bb + 4 g + j: tokens base + {0,4,1,5}
     // (g even) or base + {2,6,3,7} (g odd), base = 16 bb + 8 (g / 2)
     const int tb = 8 * (g >> 1) + 2 * (g & 1);
-    float mx = -INFINITY;
+    float sc[2][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int T = 16 * (2 * wave + i) + tb;
-      const uint32_t s01 = *(const uint32_t*)(km + 512 + 2 * T), s45 = *(const uint32_t*)(km + 512 + 2 * T + 8);
-      const uint32_t z01 = *(const uint32_t*)(km + 768 + 2 * T), z45 = *(const uint32_t*)(km + 768 + 2 * T + 8);
-      const half2v S0 = as_h2(s01), S1 = as_h2(s45), Z0 = as_h2(z01), Z1 = as_h2(z45);
-      const float Sj[4] = {(float)S0[0], (float)S1[0], (float)S0[1], (float)S1[1]};
-      const float Zj[4] = {(float)Z0[0], (float)Z1[0], (float)Z0[1], (float)Z1[1]};
+    for (int s = 0; s < NSUB; ++s) {
+      const uint8_t* km = mr + s * MS;
+      const float sig = xs[s][0][q16] + xs[s][1][q16] + xs[s][2][q16] + xs[s][3][q16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float v = fmaf(Sj[j], sc[i][j], fmaf(8.0f, Sj[j], Zj[j]) * sig);
-        sc[i][j] = v;
-        mx = fmaxf(mx, v);
+      for (int i = 0; i < 2; ++i) {
+        const int T = 16 * (2 * wave + i) + tb;
+        const uint32_t s01 = *(const uint32_t*)(km + Sh::KS + 2 * T), s45 = *(const uint32_t*)(km + Sh::KS + 2 * T + 8);
+        const uint32_t z01 = *(const uint32_t*)(km + Sh::KZ + 2 * T), z45 = *(const uint32_t*)(km + Sh::KZ + 2 * T + 8);
+        const half2v S0 = as_h2(s01), S1 = as_h2(s45), Z0 = as_h2(z01), Z1 = as_h2(z45);
+        const float Sj[4] = {(float)S0[0], (float)S1[0], (float)S0[1], (float)S1[1]};
+        const float Zj[4] = {(float)Z0[0], (float)Z1[0], (float)Z0[1], (float)Z1[1]};
+        const float4v dot = sh[s][i] + sl[s][i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float v = fmaf(Sj[j], dot[j], fmaf(Sh::KCENTRE, Sj[j], Zj[j]) * sig);
+          sc[i][j] = s == 0 ? v : sc[i][j] + v;
+        }
       }
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sc[i][j]);
     mx = xmax4(mx);
     if (g == 0) xm[wave][q16] = mx;
     __syncthreads();  // (B2) record maxima; q~ of r and the key codes are free
     // loads are unconditional (a branch around them makes the compiler's wait
     // counting conservative): past the last record they re-read one 16-byte
     // line of record r0 and are not used
-    load_keys(more ? rec(r + 1) : rec0, kd, wave, lane, !more);
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) load_keys(more ? rec(r + 1) + s * SB : rec0, kd[s], wave, lane, !more);
 
     const float mrec = fmaxf(fmaxf(xm[0][q16], xm[1][q16]), fmaxf(xm[2][q16], xm[3][q16]));
     const float m_new = fmaxf(m_run, mrec);
@@ -411,71 +520,95 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
     m_run = m_new;
     if (alpha != 1.0f) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] *= alpha;
+      for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+        for (int i = 0; i < VT; ++i) acc[s][i] *= alpha;
     }
     l_part *= alpha;
-    float zt = 0.0f;
+    float p[2][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int T = 16 * (2 * wave + i) + tb;
-      const uint32_t s01 = *(const uint32_t*)(vm + 512 + 2 * T), s45 = *(const uint32_t*)(vm + 512 + 2 * T + 8);
-      const uint32_t z01 = *(const uint32_t*)(vm + 768 + 2 * T), z45 = *(const uint32_t*)(vm + 768 + 2 * T + 8);
-      const half2v S0 = as_h2(s01), S1 = as_h2(s45), Z0 = as_h2(z01), Z1 = as_h2(z45);
-      const float Sj[4] = {(float)S0[0], (float)S1[0], (float)S0[1], (float)S1[1]};
-      const float Zj[4] = {(float)Z0[0], (float)Z1[0], (float)Z0[1], (float)Z1[1]};
-      float x[4];
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float p = __builtin_amdgcn_exp2f(sc[i][j] - m_new);  // argument <= 0
-        l_part += p;
-        zt = fmaf(p, fmaf(8.0f, Sj[j], Zj[j]), zt);
-        x[j] = p * Sj[j];
+        p[i][j] = __builtin_amdgcn_exp2f(sc[i][j] - m_new);  // argument <= 0
+        l_part += p[i][j];
       }
-      x[2] *= 0.0625f;  // odd tokens sit in the high nibbles: their slots carry 1/16
-      x[3] *= 0.0625f;
-      uint2 hi, lo;
-      split_h2(x[0], x[1], hi.x, lo.x);
-      split_h2(x[2], x[3], hi.y, lo.y);
-      *(uint2*)&pw[0][q16][16 * (2 * wave + i) + 4 * g] = hi;
-      *(uint2*)&pw[1][q16][16 * (2 * wave + i) + 4 * g] = lo;
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      const uint8_t* vm = mr + s * MS + Sh::VM;
+      float zt = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int T = 16 * (2 * wave + i) + tb;
+        const uint32_t s01 = *(const uint32_t*)(vm + 2 * SUBW + 2 * T), s45 = *(const uint32_t*)(vm + 2 * SUBW + 2 * T + 8);
+        const uint32_t z01 = *(const uint32_t*)(vm + 2 * SUBW + 256 + 2 * T),
+                       z45 = *(const uint32_t*)(vm + 2 * SUBW + 256 + 2 * T + 8);
+        const half2v S0 = as_h2(s01), S1 = as_h2(s45), Z0 = as_h2(z01), Z1 = as_h2(z45);
+        const float Sj[4] = {(float)S0[0], (float)S1[0], (float)S0[1], (float)S1[1]};
+        const float Zj[4] = {(float)Z0[0], (float)Z1[0], (float)Z0[1], (float)Z1[1]};
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          zt = fmaf(p[i][j], fmaf(8.0f, Sj[j], Zj[j]), zt);
+          x[j] = p[i][j] * Sj[j];
+        }
+        x[2] *= 0.0625f;  // odd tokens sit in the high nibbles: their slots carry 1/16
+        x[3] *= 0.0625f;
+        uint2 hi, lo;
+        split_h2(x[0], x[1], hi.x, lo.x);
+        split_h2(x[2], x[3], hi.y, lo.y);
+        *(uint2*)&pw[s][0][q16][16 * (2 * wave + i) + 4 * g] = hi;
+        *(uint2*)&pw[s][1][q16][16 * (2 * wave + i) + 4 * g] = lo;
+      }
+      zt = xsum4(zt);
+      if (g == 0) xz[s][wave][q16] = zt;
     }
-    zt = xsum4(zt);
-    if (g == 0) xz[wave][q16] = zt;
-    if (more) make_qtilde(mslot(r + 1), qph, qpl, qt, xs, G, wave, lane);
-    if (r + 2 < r1) *(uint2*)(mslot(r + 2) + 8 * tid) = mnext;
-    mnext = *(const uint2*)(r + 3 < r1 ? rec(r + 3) + 32768 + 8 * tid : rec0);
+    if (more) {
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s)
+        make_qtilde<Sh>(mslot(r + 1) + s * MS, qph[s], qpl[s], qt[s], xs[s], G, wave, lane);
+    }
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      if (r + 2 < r1) *(uint2*)(mslot(r + 2) + s * MS + 8 * tid) = mnext[s];
+      mnext[s] = *(const uint2*)(r + 3 < r1 ? rec(r + 3) + s * SB + mo : rec0);
+    }
     __syncthreads();  // (B3) weights, zero-point sums; q~ and scales of r + 1, r + 2
 
-    const float corr = xz[0][q16] + xz[1][q16] + xz[2][q16] + xz[3][q16];
-    half8 pbh[4], pbl[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      pbh[t] = mfma_a(*(const uint4*)&pw[0][q16][32 * g + 8 * t]);
-      pbl[t] = mfma_a(*(const uint4*)&pw[1][q16][32 * g + 8 * t]);
-    }
-    float4v o[4];
+    for (int s = 0; s < NSUB; ++s) {
+      const float corr = xz[s][0][q16] + xz[s][1][q16] + xz[s][2][q16] + xz[s][3][q16];
+      half8 pbh[4], pbl[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+      for (int t = 0; t < 4; ++t) {
+        pbh[t] = mfma_a(*(const uint4*)&pw[s][0][q16][32 * g + 8 * t]);
+        pbl[t] = mfma_a(*(const uint4*)&pw[s][1][q16][32 * g + 8 * t]);
+      }
+      float4v o[VT];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {  // four channel tiles as independent chains
-      half8 av[4];
+      for (int j = 0; j < VT; ++j) o[j] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) av[j] = nib8_centred(pick(vd[j], t));
+      for (int t = 0; t < 4; ++t) {  // channel tiles as independent chains
+        half8 av[VT];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = mfma16(av[j], pbh[t], o[j]);
+        for (int j = 0; j < VT; ++j) av[j] = nib8_centred(pick(vd[s][j], t));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = mfma16(av[j], pbl[t], o[j]);
-    }
-    load_values(more ? rec(r + 1) : rec0, vd, wave, lane, !more);
+        for (int j = 0; j < VT; ++j) o[j] = mfma16(av[j], pbh[t], o[j]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int cb = 4 * wave + j;
-      const uint2 cv = *(const uint2*)(vm + 2 * (16 * cb + 4 * g));
-      const half2v c01 = as_h2(cv.x), c23 = as_h2(cv.y);
-      acc[j][0] = fmaf((float)c01[0], o[j][0] + corr, acc[j][0]);
-      acc[j][1] = fmaf((float)c01[1], o[j][1] + corr, acc[j][1]);
-      acc[j][2] = fmaf((float)c23[0], o[j][2] + corr, acc[j][2]);
-      acc[j][3] = fmaf((float)c23[1], o[j][3] + corr, acc[j][3]);
+        for (int j = 0; j < VT; ++j) o[j] = mfma16(av[j], pbl[t], o[j]);
+      }
+      load_values<Sh>(more ? rec(r + 1) + s * SB : rec0, vd[s], wave, lane, !more);
+      const uint8_t* vm = mr + s * MS + Sh::VM;
+#pragma unroll
+      for (int j = 0; j < VT; ++j) {
+        const int cb = VT * wave + j;
+        const uint2 cv = *(const uint2*)(vm + 2 * (16 * cb + 4 * g));
+        const half2v c01 = as_h2(cv.x), c23 = as_h2(cv.y);
+        acc[s][j][0] = fmaf((float)c01[0], o[j][0] + corr, acc[s][j][0]);
+        acc[s][j][1] = fmaf((float)c01[1], o[j][1] + corr, acc[s][j][1]);
+        acc[s][j][2] = fmaf((float)c23[0], o[j][2] + corr, acc[s][j][2]);
+        acc[s][j][3] = fmaf((float)c23[1], o[j][3] + corr, acc[s][j][3]);
+      }
     }
   }
 
@@ -485,15 +618,17 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
   __syncthreads();
   if (q16 < G) {
     const int c = 1 + sq.n_ring_chunks + cbk;
-    float* P = a.part + (((int64_t)b * a.Hq + h * G + q16) * a.max_chunks + c) * (256 + 2);
+    float* P = a.part + (((int64_t)b * a.Hq + h * G + q16) * a.max_chunks + c) * (D + 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ch = 16 * (4 * wave + j) + 4 * g;
-      P[2 + ch + 0] = acc[j][0];
-      P[2 + ch + 1] = acc[j][1];
-      P[2 + ch + 2] = acc[j][2];
-      P[2 + ch + 3] = acc[j][3];
-    }
+    for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+      for (int j = 0; j < VT; ++j) {
+        const int ch = SUBW * s + 16 * (VT * wave + j) + 4 * g;
+        P[2 + ch + 0] = acc[s][j][0];
+        P[2 + ch + 1] = acc[s][j][1];
+        P[2 + ch + 2] = acc[s][j][2];
+        P[2 + ch + 3] = acc[s][j][3];
+      }
     if (wave == 0 && g == 0) {
       P[0] = m_run * kLn2;
       P[1] = xm[0][q16] + xm[1][q16] + xm[2][q16] + xm[3][q16];
@@ -542,14 +677,18 @@ __device__ __forceinline__ half8 codes6_reg(uint32_t lo, uint32_t hi) {
 //          (token 16 wave + (lane & 15), channels 32 kk + 8 g ..);
 //   dk/dv  the block scales of its 4 output tokens 16 wave + 4 g + r;
 //   v      value codes of tokens 4 tq .. 4 tq + 3, channels 16 c16 .. + 15
-//          (12 bytes each), tq = tid & 15, c16 = tid >> 4.
+//          (12 bytes each), tq = tid & 15, c16 = (tid >> 4) + 16 u (u < NV).
 template <int D>
 struct RingRegs {
-  static constexpr int NB = D / kQBlock, KK = D / 32;
+  static constexpr int NB = D / kQBlock, KK = D / 32, NV = D >= 256 ? D / 256 : 1, NS = (NB + 1) / 2;
   uint2 k[KK];
-  uint32_t dk[4], dv[4];
-  uint32_t v[4][3];
+  uint32_t dk[4][NS], dv[4][NS];
+  uint32_t v[NV][4][3];
 };
+template <int D>
+__device__ __forceinline__ float block_scale(const uint32_t (&d)[RingRegs<D>::NS], int blk) {
+  return (float)as_h2(d[blk >> 1])[blk & 1];
+}
 
 template <int D>
 __device__ __forceinline__ void ring_load(const DecodeArgs& a, const DecodeSeq& sq, int h, int t0, int n,
@@ -580,25 +719,31 @@ __device__ __forceinline__ void ring_load(const DecodeArgs& a, const DecodeSeq& 
   for (int r = 0; r < 4; ++r) {
     const int t = 16 * wave + 4 * g + r;
     const int sl = slot_of(t < n ? t : 0);
-    uint32_t dk, dv;
-    if (NB == 2) {
-      dk = *(const uint32_t*)(ks + (int64_t)sl * 4);
-      dv = *(const uint32_t*)(vs + (int64_t)sl * 4);
+    // a masked token carries the (finite) scales of token 0; its weight is 0
+    if (NB == 1) {
+      R.dk[r][0] = *(const uint16_t*)(ks + (int64_t)sl * 2);
+      R.dv[r][0] = *(const uint16_t*)(vs + (int64_t)sl * 2);
     } else {
-      dk = *(const uint16_t*)(ks + (int64_t)sl * 2);
-      dv = *(const uint16_t*)(vs + (int64_t)sl * 2);
-    }
-    R.dk[r] = dk;  // a masked token carries the (finite) scales of token 0; its weight is 0
-    R.dv[r] = dv;
-  }
-  const int tq = tid & 15, c16 = (tid >> 4) % (D / 16);  // head_dim 128: two threads per item, one used
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int t = 4 * tq + k;
-    const uint32_t* p = (const uint32_t*)(vc + (int64_t)slot_of(t < n ? t : 0) * (NB * kQBytes) + 12 * c16);
-    R.v[k][0] = p[0];
-    R.v[k][1] = p[1];
-    R.v[k][2] = p[2];
+      for (int e = 0; e < NB / 2; ++e) {
+        R.dk[r][e] = *(const uint32_t*)(ks + (int64_t)sl * 2 * NB + 4 * e);
+        R.dv[r][e] = *(const uint32_t*)(vs + (int64_t)sl * 2 * NB + 4 * e);
+      }
+    }
+  }
+  constexpr int NV = RingRegs<D>::NV;
+  const int tq = tid & 15;
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int c16 = ((tid >> 4) + 16 * u) % (D / 16);  // head_dim 128: two threads per item, one used
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int t = 4 * tq + k;
+      const uint32_t* p = (const uint32_t*)(vc + (int64_t)slot_of(t < n ? t : 0) * (NB * kQBytes) + 12 * c16);
+      R.v[u][k][0] = p[0];
+      R.v[u][k][1] = p[1];
+      R.v[u][k][2] = p[2];
+    }
   }
 }
 
@@ -685,18 +830,23 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
         store_t4x8(vt, kRPitch, 8 * (it / (kStep / 4)), 4 * (it % (kStep / 4)), r[j]);
       }
     } else {
-      const int tq = tid & 15, c16 = tid >> 4;
-      if (c16 < D / 16) {
-        uint4 lo8[4], hi8[4];  // channels 16 c16 + 0..7 and + 8..15 of tokens 4 tq + k
+      const int tq = tid & 15;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const half8 x0 = codes6_reg(cur.v[k][0], cur.v[k][1]);
-          const half8 x1 = codes6_reg(__builtin_amdgcn_alignbit(cur.v[k][2], cur.v[k][1], 16), cur.v[k][2] >> 16);
-          __builtin_memcpy(&lo8[k], &x0, 16);
-          __builtin_memcpy(&hi8[k], &x1, 16);
+      for (int u = 0; u < RingRegs<D>::NV; ++u) {
+        const int c16 = (tid >> 4) + 16 * u;
+        if (c16 < D / 16) {
+          uint4 lo8[4], hi8[4];  // channels 16 c16 + 0..7 and + 8..15 of tokens 4 tq + k
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const half8 x0 = codes6_reg(cur.v[u][k][0], cur.v[u][k][1]);
+            const half8 x1 =
+                codes6_reg(__builtin_amdgcn_alignbit(cur.v[u][k][2], cur.v[u][k][1], 16), cur.v[u][k][2] >> 16);
+            __builtin_memcpy(&lo8[k], &x0, 16);
+            __builtin_memcpy(&hi8[k], &x1, 16);
+          }
+          store_t4x8(vt, kRPitch, 16 * c16, 4 * tq, lo8);
+          store_t4x8(vt, kRPitch, 16 * c16 + 8, 4 * tq, hi8);
         }
-        store_t4x8(vt, kRPitch, 16 * c16, 4 * tq, lo8);
-        store_t4x8(vt, kRPitch, 16 * c16 + 8, 4 * tq, hi8);
       }
     }
 
@@ -725,7 +875,7 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
       float v = 0.0f;
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk)
-        v = sink ? v + sacc[blk][r] : fmaf((float)as_h2(cur.dk[r])[blk], sacc[blk][r], v);
+        v = sink ? v + sacc[blk][r] : fmaf(block_scale<D>(cur.dk[r], blk), sacc[blk][r], v);
       v = t < n ? v : -INFINITY;
       sc[r] = v;
       mx = fmaxf(mx, v);
@@ -752,7 +902,7 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
     for (int blk = 0; blk < (sink ? 1 : NB); ++blk) {
       float x[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = sink ? p[r] : p[r] * (float)as_h2(cur.dv[r])[blk];
+      for (int r = 0; r < 4; ++r) x[r] = sink ? p[r] : p[r] * block_scale<D>(cur.dv[r], blk);
       uint2 hi, lo;
       split_h2(x[0], x[1], hi.x, lo.x);
       split_h2(x[2], x[3], hi.y, lo.y);
@@ -816,36 +966,48 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
 // decoded rotated-domain values d (u - 32).  The token's split-K partial is
 // then exact and needs no scan: for each query head of the group the score
 // s = q' . k (scale and log2 e folded into q'), m = s, l = 1, acc = v.
+template <int D>
 __device__ __forceinline__ void append_role(const DecodeArgs& a, int b, int h, uint8_t* smem) {
+  constexpr int VPL = D / 64;  // elements of the dot product per lane
   const Layout& y = a.y;
   const DecodeSeq& sq = a.seq[b];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int G = a.g;
-  float* rows = (float*)smem;     // [16][256] query rows
-  float* kv = rows + 16 * 256;    // [2][256] decoded key and value
+  float* rows = (float*)smem;  // [16][D] query rows
+  float* kv = rows + 16 * D;   // [2][D] decoded key and value
   uint8_t* arena = const_cast<uint8_t*>(a.arena);  // the one region this launch writes
   if (wave < 2) {
-    const uint16_t* src = (wave ? a.v_new : a.k_new) + ((int64_t)b * y.H + h) * 256;
+    const uint16_t* src = (wave ? a.v_new : a.k_new) + ((int64_t)b * y.H + h) * D;
     uint8_t* codes = arena + rcode_off(y, sq.slot, a.layer, h, wave, sq.app_slot);
     uint16_t* scales = (uint16_t*)(arena + rscale_off(y, sq.slot, a.layer, h, wave, sq.app_slot));
-    float deq[4];
-    encode_chunk<4>(src, codes, scales, lane, a.signs, false, deq);
+    if (D == 128) {
+      float deq[2];
+      encode_chunk<2>(src, codes, scales, lane, a.signs, true, deq);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kv[256 * wave + 4 * lane + j] = deq[j];
+      for (int j = 0; j < 2; ++j) kv[D * wave + 2 * lane + j] = deq[j];
+    } else {
+#pragma unroll
+      for (int c = 0; c < D / 256; ++c) {
+        float deq[4];
+        encode_chunk<4>(src + 256 * c, codes + 2 * kQBytes * c, scales + 2 * c, lane, a.signs, false, deq);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kv[D * wave + 256 * c + 4 * lane + j] = deq[j];
+      }
+    }
   }
-  QueryRaw<256> qraw;
-  query_load<256>(a, b, h, wave, lane, qraw);
-  query_rows<256>(a, qraw, true, rows, wave, lane);
+  QueryRaw<D> qraw;
+  query_load<D>(a, b, h, wave, lane, qraw);
+  query_rows<D>(a, qraw, true, rows, wave, lane);
   __syncthreads();
   for (int i = wave; i < G; i += 4) {
     float s = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s = fmaf(rows[i * 256 + 4 * lane + j], kv[4 * lane + j], s);
+    for (int j = 0; j < VPL; ++j) s = fmaf(rows[i * D + VPL * lane + j], kv[VPL * lane + j], s);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-    float* P = a.part + (((int64_t)b * a.Hq + h * G + i) * a.max_chunks + sq.app_chunk) * (256 + 2);
+    float* P = a.part + (((int64_t)b * a.Hq + h * G + i) * a.max_chunks + sq.app_chunk) * (D + 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) P[2 + 4 * lane + j] = kv[256 + 4 * lane + j];
+    for (int j = 0; j < VPL; ++j) P[2 + VPL * lane + j] = kv[D + VPL * lane + j];
     if (lane == 0) {
       P[0] = s * kLn2;
       P[1] = 1.0f;
@@ -858,7 +1020,12 @@ __device__ __forceinline__ void append_role(const DecodeArgs& a, int b, int h, u
 // then body items (when the launch has them), then sink/ring items, each
 // sequence by sequence.
 
-constexpr int kMainLds = kBodyLds > RingLds<256>::total ? kBodyLds : RingLds<256>::total;
+template <int D, int KB>
+struct MainLds {
+  static constexpr int body = BodyShape<D, KB>::total, ring = RingLds<D>::total, append = (16 + 2) * D * 4;
+  static constexpr int m0 = body > ring ? body : ring;
+  static constexpr int value = m0 > append ? m0 : append;
+};
 
 // Within a sequence, body items interleave the KV heads (item i: head i mod H,
 // chunk i / H), so that every head gets its share of first and second
@@ -890,9 +1057,8 @@ __device__ __forceinline__ bool find_item(const DecodeArgs& a, int item, bool bo
   return false;
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void decode_main_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kMainLds];
+template <int D, int KB>
+__device__ __forceinline__ void decode_main(const DecodeArgs& a, uint8_t* smem) {
   int b, h, c;
   int item = blockIdx.x;
   // Each dependent round of kernel-argument loads costs a trip to memory at
@@ -910,18 +1076,32 @@ void decode_main_kernel(DecodeArgs a) {
   }
   prof_start(a.prof_ts);
   if (item < a.n_app_items) {
-    append_role(a, item / a.y.H, item % a.y.H, smem);
+    append_role<D>(a, item / a.y.H, item % a.y.H, smem);
     prof_end(a.prof_ts);
     return;
   }
   item -= a.n_app_items;
   if (item < a.n_body_items) {
-    if (find_item(a, item, true, b, h, c)) body_role(a, b, h, c, smem);
+    if (find_item(a, item, true, b, h, c)) body_role<BodyShape<D, KB>>(a, b, h, c, smem);
   } else {
-    if (find_item(a, item - a.n_body_items, false, b, h, c)) ring_role<256>(a, b, h, c, smem);
+    if (find_item(a, item - a.n_body_items, false, b, h, c)) ring_role<D>(a, b, h, c, smem);
   }
   prof_end(a.prof_ts);
 }
+
+// Two resident workgroups per compute unit (256 registers per lane each),
+// or one for 512-wide heads (whose sink/ring scan needs 125 KB of LDS).
+#define KVQ_MAIN_KERNEL(NAME, D, KB, W)                                                      \
+  __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(W, W))) void NAME(DecodeArgs a) { \
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[MainLds<D, KB>::value];           \
+    decode_main<D, KB>(a, smem);                                                             \
+  }
+KVQ_MAIN_KERNEL(decode_main_kernel, 256, 4, 2)
+KVQ_MAIN_KERNEL(decode_main_kernel_d128k8, 128, 8, 2)
+KVQ_MAIN_KERNEL(decode_main_kernel_d512, 512, 4, 1)
+#undef KVQ_MAIN_KERNEL
+static_assert(BodyShape<512, 4>::WG_PER_CU == 1 && BodyShape<256, 4>::WG_PER_CU == 2 &&
+                  BodyShape<128, 8>::WG_PER_CU == 2, "launch bounds match the body shapes");
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_ring_kernel(DecodeArgs a) {
@@ -930,12 +1110,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (find_item(a, blockIdx.x, false, b, h, c)) ring_role<D>(a, b, h, c, smem);
 }
 
-// Append (optional), body (head_dim 256, 4-bit K and V) and sink/ring items in
-// one launch.
+// Append (optional), body and sink/ring items in one launch: head_dim 256
+// with 4-bit keys and values, 512 (two 256-channel sub-records) with 4/4,
+// 128 with 8-bit keys and 4-bit values.
 hipError_t launch_decode_main(const DecodeArgs& a, int n_items, hipStream_t stream) {
-  if (a.y.D != 256 || a.y.kbits != 4 || a.y.vbits != 4 || a.ring_chunk % kStep != 0 || a.g > kMaxGroup)
+  if (a.y.vbits != 4 || a.ring_chunk % kStep != 0 || a.g > kMaxGroup) return hipErrorInvalidValue;
+  if (a.y.D == 256 && a.y.kbits == 4)
+    hipLaunchKernelGGL(decode_main_kernel, dim3(n_items), dim3(256), 0, stream, a);
+  else if (a.y.D == 512 && a.y.kbits == 4)
+    hipLaunchKernelGGL(decode_main_kernel_d512, dim3(n_items), dim3(256), 0, stream, a);
+  else if (a.y.D == 128 && a.y.kbits == 8)
+    hipLaunchKernelGGL(decode_main_kernel_d128k8, dim3(n_items), dim3(256), 0, stream, a);
+  else
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(decode_main_kernel, dim3(n_items), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -131,19 +131,23 @@ static int device_cu_count() {
     return 256;
   return n;
 }
-// matrix-core body scan (fused with the sink and ring): head_dim 256, 4-bit K and V
-static bool mfma_supported(const Layout& y) { return y.D == 256 && y.kbits == 4 && y.vbits == 4; }
+// matrix-core body scan (fused with the sink and ring): head_dim 256 or 512
+// with 4-bit K and V, head_dim 128 with 8-bit K and 4-bit V
+static bool mfma_supported(const Layout& y) {
+  return y.vbits == 4 && (((y.D == 256 || y.D == 512) && y.kbits == 4) || (y.D == 128 && y.kbits == 8));
+}
 // matrix-core sink and ring scan on its own: head_dim 128 or 256
 static bool staged_supported(const Layout& y) { return y.D == 128 || y.D == 256; }
 static constexpr int kRingStep = 64;         // tokens per step of the matrix-core sink/ring scan
 static constexpr int kStagedRingChunk = 256; // ring tokens per chunk next to a vector-ALU body scan
-static constexpr int kBodyWgPerCu = 2;       // resident workgroups per CU of the fused kernel
+// resident workgroups per CU of the fused kernel (512-wide heads: one, for the LDS of their sink/ring scan)
+static int body_wg_per_cu(const Layout& y) { return y.D == 512 ? 1 : 2; }
 
 // Matrix-core plan.  Work in units of one record (about one 64-token ring
 // step; the sink is two).  All work items run in one round, two workgroups per
-// compute unit; the first workgroup on a unit (grid index below the unit
-// count) scans 1.4 times as fast as the second (the kernel gives it that much
-// more of the records).  T = work / capacity is the time of the round in
+// compute unit (one for 512-wide heads); the first workgroup on a unit (grid
+// index below the unit count) scans 1.4 times as fast as the second (the
+// kernel gives it that much more of the records).  T = work / capacity is the time of the round in
 // second-workgroup records; ring chunks take floor(T) steps (ring items come
 // last in the grid, second on their unit), the remaining slots split the
 // body records (body items are issued first).
@@ -163,7 +167,7 @@ static MfmaPlan mfma_plan(const kvq_cache* c, const std::vector<int64_t>& n_rec,
   // `reserved` workgroups (the append items of a fused step) are short and
   // leave their slots idle once done
   const int n_cu = c->n_cu ? c->n_cu : 256;
-  const int slots = std::max(1, kBodyWgPerCu * n_cu - reserved);
+  const int slots = std::max(1, body_wg_per_cu(c->y) * n_cu - reserved);
   const double capacity = std::max(1.0, slots + 0.4 * std::min(n_cu, slots));
   const double per = std::max(1.0, (body + other) / capacity);
   MfmaPlan p;
@@ -372,7 +376,7 @@ static int max_chunks_bound(const kvq_cache* c) {
   int body = (c->y.max_rec + rpc - 1) / rpc;
   if (mfma_supported(c->y)) {
     const int n_cu = c->n_cu ? c->n_cu : 256;
-    body = std::max(body, std::min(c->y.max_rec, (kBodyWgPerCu * n_cu + c->y.H - 1) / c->y.H + 1));
+    body = std::max(body, std::min(c->y.max_rec, (body_wg_per_cu(c->y) * n_cu + c->y.H - 1) / c->y.H + 1));
   }
   return 1 + (c->y.cap + rc - 1) / rc + body + 1;  // + the new token of a fused decode step
 }
@@ -411,7 +415,8 @@ static kvq_status decode_impl(kvq_cache* c, int32_t layer, const int32_t* seq_id
   const bool use_mfma = c->path != KVQ_PATH_VALU && mfma_supported(c->y);
   const bool staged = c->path != KVQ_PATH_VALU && staged_supported(c->y);
   if (c->path == KVQ_PATH_MFMA && !use_mfma)
-    return fail(KVQ_ERR_UNSUPPORTED, "matrix-core body scan needs head_dim 256 with 4-bit K and V");
+    return fail(KVQ_ERR_UNSUPPORTED, "matrix-core body scan needs 4-bit V with 4-bit K at head_dim 256 or 512, "
+                                     "or 8-bit K at head_dim 128");
   std::vector<int64_t> n_rec(n_seqs), ring(n_seqs);
   for (int i = 0; i < n_seqs; ++i) {
     if (c->tok(seq_ids[i], layer) < 1) return fail(KVQ_ERR_INVALID, "sequence %d holds no tokens", seq_ids[i]);

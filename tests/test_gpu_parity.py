@@ -73,8 +73,10 @@ def test_decode_gpu_built_cache(pair):
         assert max(errs) <= 2e-2
 
 
-@pytest.mark.parametrize("path", [kvq.PATH_VALU, kvq.PATH_AUTO])
+@pytest.mark.parametrize("path", [kvq.PATH_VALU, kvq.PATH_MFMA])
 def test_decode_on_oracle_records(pair, path):
+    """Every small shape has a matrix-core body scan (256 and 512 wide at 4/4
+    bits, 128 wide with 8-bit keys) and the vector-ALU reference."""
     pair.import_oracle_records()
     for layer in range(pair.w.n_layers):
         q = pair.queries(0, layer)
@@ -113,7 +115,23 @@ def test_streaming_one_token_per_step():
     assert max(errs) <= ATTN_TOL
 
 
-@pytest.mark.parametrize("name", ["qwen27b", "batched"])
+def test_decode_auto_falls_back_on_shapes_without_matrix_cores():
+    """128-wide heads with 4-bit keys have no matrix-core body scan: AUTO takes
+    the vector-ALU scan (parity as usual), MFMA is refused before any launch."""
+    w = configs.QWEN14B1M.scaled(n_layers=1, n_kv_heads=2, n_q_heads=10, tail_min=256, tail_max=512, ctx=900,
+                                 k_bits=4)
+    p = Pair(w, [900], inputs.rotation_signs(w.seed)).build(300)
+    p.import_oracle_records()
+    q = p.queries(0, 0)
+    errs, _ = p.decode_errors(0, q, path=kvq.PATH_AUTO)
+    _say(f"[d128k4] AUTO decode err={max(errs):.2e}")
+    assert max(errs) <= ATTN_TOL
+    with pytest.raises(kvq.KVQError) as e:
+        p.decode_errors(0, q, path=kvq.PATH_MFMA)
+    assert e.value.status == kvq.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["qwen27b", "batched", "gemma", "qwen14b"])
 def test_decode_step(name):
     """kvq_decode_step (append one token, seal if full, decode) step after step:
     one fused launch while every new token lands in the ring and no seal is due,
@@ -123,14 +141,22 @@ def test_decode_step(name):
     imported from the oracle; on a seal step the just-sealed records are the
     GPU's own, hence the looser bound of a GPU-built cache there)."""
     steps = 40
+    signs = None
     if name == "qwen27b":  # ring 360 after the build: the seal fires at step 24
         w = configs.QWEN27B.scaled(n_layers=2, tail_min=256, tail_max=384, ctx=1000)
         lens = [1000]
-    else:                  # one sequence starts in the sink: unfused until it leaves it
+    elif name == "batched":  # one sequence starts in the sink: unfused until it leaves it
         w = configs.BATCHED.scaled(n_layers=1, n_kv_heads=2, n_q_heads=12, tail_min=256, tail_max=384, ctx=1000)
         lens = [1000, 897, 120]
+    elif name == "gemma":  # 512-wide heads, two sequences
+        w = configs.GEMMA31B.scaled(n_layers=1, tail_min=256, tail_max=384, ctx=1000)
+        lens = [1000, 700]
+    else:                    # 128-wide heads, randomized WHT, 8-bit keys
+        w = configs.QWEN14B1M.scaled(n_layers=1, n_kv_heads=2, n_q_heads=10, tail_min=256, tail_max=384, ctx=1000)
+        lens = [1000]
+        signs = inputs.rotation_signs(w.seed)
     _say(f"[step {name}] build lens={lens}")
-    p = Pair(w, lens, extra_ctx=steps).build(128)
+    p = Pair(w, lens, signs, extra_ctx=steps).build(128)
     p.import_oracle_records()
     t = p.torch
     seqs = list(range(p.n))

@@ -11,10 +11,10 @@
 // Work split: chunk 0 of a sequence is its sink; then ring chunks of
 // ring_chunk tokens; then body chunks (the records split evenly).  Each
 // workgroup handles one chunk of one KV head for its g query heads and writes
-// an fp32 partial (m, l, acc[D]): m the largest score, l = sum exp(s - m),
-// acc = sum exp(s - m) v (in the rotated domain, except for chunk 0).
-// The merge kernel combines the partials of one query head, applies R^T to the
-// rotated part, adds the sink part and divides by the total weight.
+// an fp32 partial row (m, l, acc[D]): m the largest score, l = sum exp(s - m),
+// acc = sum exp(s - m) v, rotated back to the original domain by the
+// workgroup (R^T is linear).  The merge kernel combines the partials of one
+// query head under one softmax and divides by the total weight.
 //
 // This path dequantises each tile into LDS as fp32 and uses plain fp32 dot
 // products: it is the reference the matrix-core body path is checked against.
@@ -198,15 +198,22 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     __syncthreads();
   }
 
+  // rotated-domain sums back to the original domain (the sink's already are)
 #pragma unroll
   for (int i = 0; i < kMaxGroup; ++i) {
     if (i >= g) break;
-    float* P = a.part + (((int64_t)b * a.Hq + h * g + i) * a.max_chunks + c) * (D + 2);
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int j = tid + 256 * q;
-      if (j < D) P[2 + j] = acc[i][q];
+      if (j < D) qs[i][j] = acc[i][q];
     }
+  }
+  __syncthreads();
+  if (region != 0)
+    for (int i = 0; i < g; ++i) lds_rotate<D>(qs[i], a.signs, true);
+  for (int i = 0; i < g; ++i) {
+    float* P = a.part + (((int64_t)b * a.Hq + h * g + i) * a.max_chunks + c) * part_stride(D);
+    for (int j = tid; j < D; j += 256) P[kPartHead + j] = qs[i][j];
     if (tid == 0) {
       P[0] = ms[i];
       P[1] = lsum[i];
@@ -215,130 +222,92 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   prof_end(a.prof_ts);
 }
 
-// Merge of the split-K partials of one query head (grid Hq x n_seqs, 1024
-// threads): one softmax over all chunks, R^T applied to the rotated part
-// (chunks 1..), the sink part (chunk 0) added as is, divided by the total
-// weight.  The 16 waves split the chunks (more loads in flight than a
-// 256-thread block); each lane owns D / 64 channels.
-constexpr int kMergeWaves = 16;
-constexpr int kMergeUnroll = 8;  // partials per wave and pass, all loaded before any is used
+// Merge of the split-K partials (all in the original domain): one softmax
+// over the chunks of a query head, divided by the total weight.  One
+// workgroup per (sequence, query head, 64-channel slice): thread t takes
+// channels 4 (t & 15) .. + 3 of the slice and chunks t >> 4, + 16, ...; every
+// load of a pass (the rows' float4 and their (m, l)) is issued before any is
+// used, so a pass costs one memory round trip, and each thread keeps a
+// running (M, L, sum e^(m - M) acc).  The 16 row groups meet in LDS.
+constexpr int kMergeUnroll = 8;  // partials per thread and pass
 
-// One workgroup per (sequence, query head).  Wave w takes partials
-// w, w + NW, ... in passes of kMergeUnroll: every load of a pass (the rows and
-// their (m, l), the latter broadcast to all lanes) is issued before the first
-// is used, so a pass costs one memory round trip, and the wave keeps a running
-// (M, L, sum e^(m - M) acc) in registers with no cross-lane step.  The waves'
-// states meet in LDS; wave 0 rotates the rotated-domain sum back and adds the
-// sink's partial (chunk 0, original domain).
 template <int D>
-__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(MergeArgs a) {
-  constexpr int VPL = D / 64, NW = kMergeWaves, U = kMergeUnroll;
-  __shared__ float red[NW][D];
-  __shared__ float rm[2 * NW];
-  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  constexpr int NSL = D / 64, U = kMergeUnroll;
+  __shared__ float4 red[16][16];
+  __shared__ float rm[2][16];
+  const int hq = blockIdx.x / NSL, sl = blockIdx.x % NSL, b = blockIdx.y;
+  const int tid = threadIdx.x, rg = tid >> 4, cq = tid & 15;
   const int n = a.n_chunks[b];
-  const float* P = a.part + ((int64_t)b * a.Hq + hq) * a.max_chunks * (D + 2);
+  const int ch = 64 * sl + 4 * cq;
+  const float* P = a.part + ((int64_t)b * a.Hq + hq) * a.max_chunks * part_stride(D);
 
   float M = -INFINITY, L = 0.0f;
-  float v[VPL];
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) v[i] = 0.0f;
-  float sink[VPL];
-  float m0 = 0.0f;
-  if (wave == 0) {
-    m0 = P[0];
-#pragma unroll
-    for (int i = 0; i < VPL / 2; ++i) {
-      const float2 x = ((const float2*)(P + 2 + VPL * lane))[i];
-      sink[2 * i] = x.x;
-      sink[2 * i + 1] = x.y;
-    }
-  }
-  for (int base = 0; base < n; base += NW * U) {
+  float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int base = 0; base < n; base += 16 * U) {
     float2 ml[U];
-    float x[U][VPL];
+    float4 x[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int c = base + wave + NW * u;
-      const float* row = P + (int64_t)(c < n ? c : 0) * (D + 2);
+      const int c = base + rg + 16 * u;
+      const float* row = P + (int64_t)(c < n ? c : 0) * part_stride(D);
       ml[u] = *(const float2*)row;
-#pragma unroll
-      for (int i = 0; i < VPL / 2; ++i) {
-        const float2 t = ((const float2*)(row + 2 + VPL * lane))[i];
-        x[u][2 * i] = t.x;
-        x[u][2 * i + 1] = t.y;
-      }
+      x[u] = *(const float4*)(row + kPartHead + ch);
     }
     float mp = M;
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (base + wave + NW * u < n) mp = fmaxf(mp, ml[u].x);
+      if (base + rg + 16 * u < n) mp = fmaxf(mp, ml[u].x);
     const float alpha = M == -INFINITY ? 0.0f : expf(M - mp);  // nothing to rescale before the first partial
     L *= alpha;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) v[i] *= alpha;
+    v.x *= alpha;
+    v.y *= alpha;
+    v.z *= alpha;
+    v.w *= alpha;
     M = mp;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int c = base + wave + NW * u;
-      if (c < n) {
+      if (base + rg + 16 * u < n) {
         const float w = expf(ml[u].x - M);
         L = fmaf(w, ml[u].y, L);
-        if (c > 0) {  // chunk 0 (the sink) is in the original domain: added after the rotation
-#pragma unroll
-          for (int i = 0; i < VPL; ++i) v[i] = fmaf(w, x[u][i], v[i]);
-        }
+        v.x = fmaf(w, x[u].x, v.x);
+        v.y = fmaf(w, x[u].y, v.y);
+        v.z = fmaf(w, x[u].z, v.z);
+        v.w = fmaf(w, x[u].w, v.w);
       }
     }
   }
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) red[wave][VPL * lane + i] = v[i];
-  if (lane == 0) {
-    rm[wave] = M;
-    rm[NW + wave] = L;
+  red[rg][cq] = v;
+  if (cq == 0) {
+    rm[0][rg] = M;
+    rm[1][rg] = L;
   }
   __syncthreads();
-  if (wave != 0) return;
-  float Mt = rm[0];
+  if (tid >= 16) return;
+  float Mt = rm[0][0];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) Mt = fmaxf(Mt, rm[w]);
+  for (int r = 1; r < 16; ++r) Mt = fmaxf(Mt, rm[0][r]);
   float Lt = 0.0f;
+  float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) v[i] = 0.0f;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const float s = rm[w] == -INFINITY ? 0.0f : expf(rm[w] - Mt);  // a wave with no partial has M = -inf
-    Lt = fmaf(s, rm[NW + w], Lt);
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) v[i] = fmaf(s, red[w][VPL * lane + i], v[i]);
+  for (int r = 0; r < 16; ++r) {
+    const float s = rm[0][r] == -INFINITY ? 0.0f : expf(rm[0][r] - Mt);  // a row group with no partial
+    Lt = fmaf(s, rm[1][r], Lt);
+    const float4 t = red[r][cq];
+    o.x = fmaf(s, t.x, o.x);
+    o.y = fmaf(s, t.y, o.y);
+    o.z = fmaf(s, t.z, o.z);
+    o.w = fmaf(s, t.w, o.w);
   }
-  // R^T: head_dim 128: s1 . H . s2 / sqrt(128); 256 and 512: H_256 / 16 per 256-block
-  if (D == 128) {
-#pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (sign_neg(a.signs, 128 + VPL * lane + i)) v[i] = -v[i];
-    wave_fwht<VPL, 128>(v, lane);
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      v[i] *= (float)kInvSqrt128;
-      if (sign_neg(a.signs, VPL * lane + i)) v[i] = -v[i];
-    }
-  } else {
-    wave_fwht<VPL, 256>(v, lane);
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) v[i] *= 0.0625f;
-  }
-  const float w0 = expf(m0 - Mt);
   const float inv_l = 1.0f / Lt;
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const int j = VPL * lane + i;
-    const float o = fmaf(w0, sink[i], v[i]) * inv_l;
-    const int64_t oi = ((int64_t)b * a.Hq + hq) * D + j;
-    if (a.out_f16)
-      ((uint16_t*)a.out)[oi] = f2h_bits(o);
-    else
-      ((float*)a.out)[oi] = o;
+  const int64_t oi = ((int64_t)b * a.Hq + hq) * D + ch;
+  if (a.out_f16) {
+    uint2 h;
+    h.x = (uint32_t)f2h_bits(o.x * inv_l) | ((uint32_t)f2h_bits(o.y * inv_l) << 16);
+    h.y = (uint32_t)f2h_bits(o.z * inv_l) | ((uint32_t)f2h_bits(o.w * inv_l) << 16);
+    *(uint2*)((uint16_t*)a.out + oi) = h;
+  } else {
+    *(float4*)((float*)a.out + oi) = make_float4(o.x * inv_l, o.y * inv_l, o.z * inv_l, o.w * inv_l);
   }
 }
 
@@ -354,11 +323,11 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int grid_x, hipStream_t strea
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
-  dim3 grid(a.Hq, a.n_seqs);
+  dim3 grid(a.Hq * (a.D / 64), a.n_seqs);
   switch (a.D) {
-    case 128: hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(64 * kMergeWaves), 0, stream, a); break;
-    case 256: hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(64 * kMergeWaves), 0, stream, a); break;
-    case 512: hipLaunchKernelGGL(merge_kernel<512>, grid, dim3(64 * kMergeWaves), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(256), 0, stream, a); break;
+    case 256: hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(256), 0, stream, a); break;
+    case 512: hipLaunchKernelGGL(merge_kernel<512>, grid, dim3(256), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -1,13 +1,16 @@
-// Matrix-core decode attention: the sealed body (256-channel 4-bit records),
-// the fp16 sink and the tq6_0 staging ring in one launch.
+// Matrix-core decode attention: the sealed body, the fp16 sink and the tq6_0
+// staging ring in one launch (body records of 256 channels at 4/4 bits, of
+// 128 channels with 8-bit keys, or two 256-channel halves of a 512-wide head).
 //
 // SJ-KVaRN 2.1: one decode pass reads the sink, the staging ring (the exact
 // tail) and the sealed body; KV Cache Precision Tail section 2: the region
 // results are combined under one softmax (here: split-K partials (m, l, acc)
 // merged by the merge kernel).  KV cache math ("rotate first"): the query is
 // rotated once, ring and body are read in the rotated domain with no
-// dequantise pass, and only the merged output is rotated back; the sink stays
-// in the original domain and is scored with the unrotated query.
+// dequantise pass, and each work item rotates its few accumulated rows back
+// before writing them (R^T is linear, so the merge of rotated-back partials
+// equals the rotated-back merge); the sink stays in the original domain and is
+// scored with the unrotated query.
 //
 // Body record math (SJ-KVaRN 2.2: column balance scales C absorbed, per-row
 // scale S and zero point Z): k_ij = C_j (S_i n_ij + Z_i), so for the rotated
@@ -23,10 +26,11 @@
 // precision.  The softmax scale and log2(e) are folded into the query, so
 // scores come out in log2 units.
 //
-// Work items, one workgroup (4 waves) each: body chunks (consecutive records
-// of one KV head) first, then the sink and ring chunks of every KV head.
-// Each item writes one fp32 partial per query head; partial 0 is the sink,
-// 1.. the ring chunks, then the body chunks.
+// Work items, one workgroup (4 waves) each: the appended token's item (fused
+// decode step), body chunks (consecutive records of one KV head), then the
+// sink and ring chunks of every KV head.  Each item writes one fp32 partial
+// row per query head in the original domain; partial 0 is the sink, 1.. the
+// ring chunks, then the body chunks, then the appended token.
 #include <type_traits>
 
 #include "kvq_encode.h"
@@ -168,6 +172,37 @@ __device__ __forceinline__ void query_rows(const DecodeArgs& a, const QueryRaw<D
     }
 #pragma unroll
     for (int j = 0; j < VPL; ++j) rows[i * D + VPL * lane + j] = v[j];
+  }
+}
+
+// Partial rows of one work item (chunk c of KV head h): rows[i][D] in LDS
+// holds the accumulator of query head i of the group (rotated domain unless
+// `rotate` is false), m the running maximum of this lane's column (log2
+// units, the same in every wave), xl[w][i] wave w's part of l.  Wave w writes
+// rows w, w + 4, ..., rotated back to the original domain when `rotate`.  The
+// caller synchronises after filling rows and xl.
+template <int D>
+__device__ __forceinline__ void write_partial_rows(const DecodeArgs& a, int b, int h, int c, const float* rows,
+                                                   float m, const float (*xl)[16], bool rotate, int wave, int lane) {
+  constexpr int VPL = D / 64;
+  for (int i = wave; i < a.g; i += 4) {
+    float v[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) v[j] = rows[i * D + VPL * lane + j];
+    if (rotate) rotate_back<D>(v, lane, a.signs);
+    float* P = a.part + (((int64_t)b * a.Hq + h * a.g + i) * a.max_chunks + c) * part_stride(D);
+    float* dst = P + kPartHead + VPL * lane;
+    if constexpr (VPL == 2) {
+      *(float2*)dst = make_float2(v[0], v[1]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < VPL; j += 4) *(float4*)(dst + j) = make_float4(v[j], v[j + 1], v[j + 2], v[j + 3]);
+    }
+    const float mi = __shfl(m, i, 64);  // lane i holds column i
+    if (lane == 0) {
+      P[0] = mi * kLn2;
+      P[1] = xl[0][i] + xl[1][i] + xl[2][i] + xl[3][i];
+    }
   }
 }
 
@@ -612,28 +647,20 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
     }
   }
 
-  // ---- partial of this chunk: every wave holds the same m; l sums over waves
+  // ---- partial of this chunk: every wave holds the same m; l sums over
+  // waves.  The accumulators pass through the q~ area (no wave reads q~ after
+  // the last record's scores) to be rotated back row by row.
   const float lsum = xsum4(l_part);
   if (g == 0) xm[wave][q16] = lsum;
-  __syncthreads();
-  if (q16 < G) {
-    const int c = 1 + sq.n_ring_chunks + cbk;
-    float* P = a.part + (((int64_t)b * a.Hq + h * G + q16) * a.max_chunks + c) * (D + 2);
+  if (q16 < G) {  // rows: the q~ area, as in the prologue
 #pragma unroll
     for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-      for (int j = 0; j < VT; ++j) {
-        const int ch = SUBW * s + 16 * (VT * wave + j) + 4 * g;
-        P[2 + ch + 0] = acc[s][j][0];
-        P[2 + ch + 1] = acc[s][j][1];
-        P[2 + ch + 2] = acc[s][j][2];
-        P[2 + ch + 3] = acc[s][j][3];
-      }
-    if (wave == 0 && g == 0) {
-      P[0] = m_run * kLn2;
-      P[1] = xm[0][q16] + xm[1][q16] + xm[2][q16] + xm[3][q16];
-    }
+      for (int j = 0; j < VT; ++j)
+        *(float4v*)(rows + q16 * D + SUBW * s + 16 * (VT * wave + j) + 4 * g) = acc[s][j];
   }
+  __syncthreads();
+  write_partial_rows<D>(a, b, h, 1 + sq.n_ring_chunks + cbk, rows, m_run, xm, true, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -938,24 +965,17 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
     }
   }
 
+  // partial rows through the V^T area (free after the last step); the sink's
+  // sums are in the original domain already
   const float lsum = xsum4(l_part);
   if (g == 0) xl[wave][q16] = lsum;
-  __syncthreads();
+  float* rows = (float*)vt;
   if (q16 < G) {
-    float* P = a.part + (((int64_t)b * a.Hq + h * G + q16) * a.max_chunks + c) * (D + 2);
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int ch = 16 * (CPW * wave + i) + 4 * g;
-      P[2 + ch + 0] = acc[i][0];
-      P[2 + ch + 1] = acc[i][1];
-      P[2 + ch + 2] = acc[i][2];
-      P[2 + ch + 3] = acc[i][3];
-    }
-    if (wave == 0 && g == 0) {
-      P[0] = m_run * kLn2;
-      P[1] = xl[0][q16] + xl[1][q16] + xl[2][q16] + xl[3][q16];
-    }
+    for (int i = 0; i < CPW; ++i) *(float4v*)(rows + q16 * D + 16 * (CPW * wave + i) + 4 * g) = acc[i];
   }
+  __syncthreads();
+  write_partial_rows<D>(a, b, h, c, rows, m_run, xl, !sink, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -999,15 +1019,19 @@ __device__ __forceinline__ void append_role(const DecodeArgs& a, int b, int h, u
   query_load<D>(a, b, h, wave, lane, qraw);
   query_rows<D>(a, qraw, true, rows, wave, lane);
   __syncthreads();
+  float vo[VPL];  // the value, rotated back: the same accumulator for every query head
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) vo[j] = kv[D + VPL * lane + j];
+  rotate_back<D>(vo, lane, a.signs);
   for (int i = wave; i < G; i += 4) {
     float s = 0.0f;
 #pragma unroll
     for (int j = 0; j < VPL; ++j) s = fmaf(rows[i * D + VPL * lane + j], kv[VPL * lane + j], s);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-    float* P = a.part + (((int64_t)b * a.Hq + h * G + i) * a.max_chunks + sq.app_chunk) * (D + 2);
+    float* P = a.part + (((int64_t)b * a.Hq + h * G + i) * a.max_chunks + sq.app_chunk) * part_stride(D);
 #pragma unroll
-    for (int j = 0; j < VPL; ++j) P[2 + VPL * lane + j] = kv[D + VPL * lane + j];
+    for (int j = 0; j < VPL; ++j) P[kPartHead + VPL * lane + j] = vo[j];
     if (lane == 0) {
       P[0] = s * kLn2;
       P[1] = 1.0f;

@@ -80,4 +80,27 @@ __device__ __forceinline__ void wave_fwht(float (&v)[VPL], int lane) {
   }
 }
 
+// R^T of one D-vector held D / 64 values per lane (lane l: elements
+// (D / 64) l ..): head_dim 128: s1 . H . s2 / sqrt(128); 256 and 512: H_256 / 16
+// on each 256-point half.
+template <int D>
+__device__ __forceinline__ void rotate_back(float (&v)[D / 64], int lane, const uint32_t* signs) {
+  constexpr int VPL = D / 64;
+  if (D == 128) {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (sign_neg(signs, 128 + VPL * lane + i)) v[i] = -v[i];
+    wave_fwht<VPL, 128>(v, lane);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      v[i] *= (float)kInvSqrt128;
+      if (sign_neg(signs, VPL * lane + i)) v[i] = -v[i];
+    }
+  } else {
+    wave_fwht<VPL, 256>(v, lane);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) v[i] *= 0.0625f;
+  }
+}
+
 }  // namespace kvq

@@ -23,6 +23,10 @@ constexpr int kMaxLaunchSeqs = 32;
 constexpr int kMaxSealTasks = 64;
 constexpr int kMaxGroup = 16;     // query heads per KV head
 constexpr int kMaxChunks = 4096;  // split-K partials per (sequence, query head)
+// A split-K partial row: [m, l, 0, 0, acc[D]] fp32, acc 16-byte aligned and in
+// the original domain (the producer rotates its rotated-domain sums back).
+constexpr int kPartHead = 4;
+__host__ __device__ inline int part_stride(int D) { return D + kPartHead; }
 
 struct Layout {
   int32_t S, L, H, D, NB, cap, nsub, sub, kbits, vbits, max_rec, pad0;
@@ -90,7 +94,7 @@ struct DecodeArgs {
   const uint16_t* q;  // fp16 [n_seqs][Hq][D]
   const uint16_t* k_new;  // fused decode step: fp16 [n_seqs][H][D] token appended first, or null
   const uint16_t* v_new;
-  float* part;        // [n_seqs][Hq][max_chunks][D + 2]: m, l, acc[D]
+  float* part;        // [n_seqs][Hq][max_chunks][part_stride(D)] split-K partial rows
   float scale;
   int32_t layer, Hq, g, n_seqs, max_chunks;
   int32_t ring_chunk;    // ring tokens per chunk
@@ -108,7 +112,6 @@ struct MergeArgs {
   const float* part;
   void* out;          // [n_seqs][Hq][D] fp32 or fp16
   int32_t D, Hq, n_seqs, max_chunks, out_f16, pad;
-  uint32_t signs[8];
   int32_t n_chunks[kMaxLaunchSeqs];
 };
 

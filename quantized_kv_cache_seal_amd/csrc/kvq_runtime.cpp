@@ -383,7 +383,7 @@ static int max_chunks_bound(const kvq_cache* c) {
 
 kvq_status kvq_workspace_bytes(const kvq_cache* c, int32_t n_seqs, size_t* bytes) {
   if (!c || !bytes || n_seqs < 0) return fail(KVQ_ERR_INVALID, "bad arguments");
-  *bytes = (size_t)n_seqs * c->cfg.n_q_heads * max_chunks_bound(c) * (c->y.D + 2) * sizeof(float);
+  *bytes = (size_t)n_seqs * c->cfg.n_q_heads * max_chunks_bound(c) * part_stride(c->y.D) * sizeof(float);
   return KVQ_OK;
 }
 
@@ -451,7 +451,7 @@ static kvq_status decode_impl(kvq_cache* c, int32_t layer, const int32_t* seq_id
   }
   if (max_chunks > kMaxChunks) return fail(KVQ_ERR_CAPACITY, "too many split-K chunks");
   const int Hq = c->cfg.n_q_heads, D = c->y.D;
-  const size_t need = (size_t)n_seqs * Hq * max_chunks * (D + 2) * sizeof(float);
+  const size_t need = (size_t)n_seqs * Hq * max_chunks * part_stride(D) * sizeof(float);
   if (ws_bytes < need) return fail(KVQ_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   const size_t out_elem = out_dtype == KVQ_OUT_F16 ? 2 : 4;
   for (int b0 = 0; b0 < n_seqs; b0 += kMaxLaunchSeqs) {
@@ -464,7 +464,7 @@ static kvq_status decode_impl(kvq_cache* c, int32_t layer, const int32_t* seq_id
       a.k_new = (const uint16_t*)k_new + (int64_t)b0 * c->y.H * D;
       a.v_new = (const uint16_t*)v_new + (int64_t)b0 * c->y.H * D;
     }
-    a.part = (float*)workspace + (int64_t)b0 * Hq * max_chunks * (D + 2);
+    a.part = (float*)workspace + (int64_t)b0 * Hq * max_chunks * part_stride(D);
     a.scale = scale;
     a.layer = layer;
     a.Hq = Hq;
@@ -507,7 +507,6 @@ static kvq_status decode_impl(kvq_cache* c, int32_t layer, const int32_t* seq_id
     m.n_seqs = a.n_seqs;
     m.max_chunks = max_chunks;
     m.out_f16 = out_dtype == KVQ_OUT_F16;
-    std::memcpy(m.signs, c->signs, sizeof m.signs);
     for (int b = 0; b < a.n_seqs; ++b) m.n_chunks[b] = a.seq[b].n_chunks;
     e = launch_merge(m, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge launch");

@@ -16,12 +16,13 @@
 // scale S and zero point Z): k_ij = C_j (S_i n_ij + Z_i), so for the rotated
 // query q' and q~_j = q'_j C_j, sigma = sum_j q~_j:
 //     q'.k_i = S_i (q~ . n_i) + Z_i sigma
-//     sum_i p_i v_ij = C_j ( sum_i (p_i S_i) n_ij + sum_i p_i Z_i ).
+//     sum_i p_i v_ij = C_j ( sum_i (p_i S_i) (n_ij - 8) + sum_i p_i (Z_i + 8 S_i) ).
 // Ring math (tq6_0: one fp16 scale d per 128-value block, 6-bit codes u):
 //     score_t = sum_blocks d_t,b (q' . u_t,b),   out_j = sum_t (p_t d_t,b(j)) u_t,j.
 // Every inner product is dense (16 query columns, the group padded to 16) x
 // (32 codes) x (16 tokens or channels) on v_mfma_f32_16x16x32_f16, codes
-// entering as exact small integers; the non-code operand (q~, q', the weights)
+// entering exactly (key codes as fp16 subnormals n 2^-24, value and ring codes
+// as centred small integers); the non-code operand (q~, q', the weights)
 // is split into hi + lo fp16 halves, two products each, which keeps fp32-level
 // precision.  The softmax scale and log2(e) are folded into the query, so
 // scores come out in log2 units.
@@ -50,17 +51,17 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t b) {
   return d;
 }
 
-// Eight 4-bit codes of one dword as exact, centred fp16 values.  One AND-OR
-// per pair puts a nibble n into the mantissa of 1024 (the high nibble of a
-// byte stays in place, i.e. 1024 + 16 n; its 1/16 is folded into the other
-// operand) and one packed subtract leaves n - 8 (or 16 (n - 8)).
+// Eight 4-bit value codes of one dword as exact, centred fp16 values.  One
+// AND-OR per pair puts a nibble n into the mantissa of 1024 (the high nibble
+// of a byte stays in place, i.e. 1024 + 16 n; its 1/16 is folded into the
+// other operand) and one packed subtract leaves n - 8 (or 16 (n - 8)).
 // Slots: [n0, n4, 16 n1, 16 n5, n2, n6, 16 n3, 16 n7] - centre.
-// Centring keeps the fp32 accumulators free of a large common term: with
-// codes in [0, 15] the score product carries 7.5 sum(q~), and q~ = q' C
-// reaches thousands in outlier channels; the value product carries
-// 7.5 sum(p S), hundreds of times the weighted average when attention is
-// diffuse.  fp32 rounding of such a term swamps the result.  The centre moves
-// into the zero point instead: x = C (S (n - 8) + (Z + 8 S)).
+// The value product needs the centre: its weights p S enter as fp16 hi + lo,
+// and with codes in [0, 15] their rounding error is summed with one sign
+// against the zero-point sum, which is formed from the exact weights; the
+// product carries 7.5 sum(p S), hundreds of times the weighted average when
+// attention is diffuse, and that error swamps the result (measured).  The
+// centre moves into the zero point instead: x = C (S (n - 8) + (Z + 8 S)).
 __device__ __forceinline__ half8 nib8_centred(uint32_t w) {
   const uint32_t w8 = w >> 8;
   const uint32_t lo_m = 0x000F000Fu, hi_m = 0x00F000F0u, e = 0x64006400u;
@@ -72,6 +73,25 @@ __device__ __forceinline__ half8 nib8_centred(uint32_t w) {
   const half8 off = {(_Float16)1032.0f, (_Float16)1032.0f, (_Float16)1152.0f, (_Float16)1152.0f,
                      (_Float16)1032.0f, (_Float16)1032.0f, (_Float16)1152.0f, (_Float16)1152.0f};
   return mfma_a(u) - off;
+}
+
+// Eight 4-bit key codes of one dword as exact fp16 subnormals n 2^-24 (low
+// nibbles) or 16 n 2^-24 (high nibbles, whose 1/16 is folded into the other
+// operand): one AND per pair, slots as nib8_centred.  The matrix cores
+// multiply fp16 subnormals exactly (checked for subnormal x subnormal too);
+// the 2^24 is restored on the fp32 results.  The score needs no centre: its
+// zero-point term Z sigma is formed from the same rounded q~ operands as the
+// product, so their rounding enters both alike, and the fp32 accumulation of
+// the uncentred product is ~10^-6 relative.
+constexpr float kSub24 = 16777216.0f;  // 2^24
+__device__ __forceinline__ half8 nib8_sub(uint32_t w) {
+  const uint32_t w8 = w >> 8;
+  uint4 u;
+  u.x = w & 0x000F000Fu;
+  u.y = w & 0x00F000F0u;
+  u.z = w8 & 0x000F000Fu;
+  u.w = w8 & 0x00F000F0u;
+  return mfma_a(u);
 }
 
 // Transpose 4 tokens x 8 channels (one half8 per token) into 8 channel rows of
@@ -247,7 +267,6 @@ struct BodyShape {
   static constexpr int META = 4 * (SUBW + 256);  // K and V: C[SUBW], S[128], Z[128] fp16
   static constexpr int SUB_BYTES = KCODE + VCODE + META;
   static constexpr int KS = 2 * SUBW, KZ = KS + 256, VM = KZ + 256;  // offsets in the scales: K S, K Z, V C
-  static constexpr float KCENTRE = KB == 8 ? 128.0f : 8.0f;
   static constexpr int WG_PER_CU = NSUB == 2 ? 1 : 2;  // resident workgroups per compute unit
   static constexpr int MSTRIDE = 2048;                 // LDS bytes per sub-record's scales
   // LDS: q~ operands [NSUB][KK][hi, lo][64 lanes]; weights [NSUB][hi, lo][16][kPPitch];
@@ -268,20 +287,15 @@ __device__ __forceinline__ int slot_token(int p) {  // token at position p (0..7
   return (p >> 1) + 4 * (p & 1);
 }
 
-// Eight 8-bit codes of two dwords as exact, centred fp16 values n - 128 in
-// channel order: one byte permute per pair places each byte under the
-// exponent pattern of 1024 (giving 1024 + n exactly), one packed subtract
-// removes 1152.
-__device__ __forceinline__ half8 byte8_centred(uint32_t w0, uint32_t w1) {
-  const uint32_t e = 0x64646464u;
+// Eight 8-bit codes of two dwords as exact fp16 subnormals n 2^-24 in channel
+// order: one byte permute per pair (selector 12 gives a zero byte).
+__device__ __forceinline__ half8 byte8_sub(uint32_t w0, uint32_t w1) {
   uint4 u;
-  u.x = __builtin_amdgcn_perm(e, w0, 0x04010400u);
-  u.y = __builtin_amdgcn_perm(e, w0, 0x04030402u);
-  u.z = __builtin_amdgcn_perm(e, w1, 0x04010400u);
-  u.w = __builtin_amdgcn_perm(e, w1, 0x04030402u);
-  const half8 off = {(_Float16)1152.0f, (_Float16)1152.0f, (_Float16)1152.0f, (_Float16)1152.0f,
-                     (_Float16)1152.0f, (_Float16)1152.0f, (_Float16)1152.0f, (_Float16)1152.0f};
-  return mfma_a(u) - off;
+  u.x = __builtin_amdgcn_perm(0u, w0, 0x0C010C00u);
+  u.y = __builtin_amdgcn_perm(0u, w0, 0x0C030C02u);
+  u.z = __builtin_amdgcn_perm(0u, w1, 0x0C010C00u);
+  u.w = __builtin_amdgcn_perm(0u, w1, 0x0C030C02u);
+  return mfma_a(u);
 }
 
 // q~ operands (hi, lo) of this wave's k-steps of one sub-record from its key
@@ -502,9 +516,9 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         if (Sh::KB == 4)
-          av[i] = nib8_centred(pick(kd[s][i][kk >> 2], kk & 3));
+          av[i] = nib8_sub(pick(kd[s][i][kk >> 2], kk & 3));
         else
-          av[i] = byte8_centred(pick(kd[s][i][kk >> 1], 2 * (kk & 1)), pick(kd[s][i][kk >> 1], 2 * (kk & 1) + 1));
+          av[i] = byte8_sub(pick(kd[s][i][kk >> 1], 2 * (kk & 1)), pick(kd[s][i][kk >> 1], 2 * (kk & 1) + 1));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) sh[s][i] = mfma16(av[i], bh, sh[s][i]);
@@ -530,7 +544,7 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
         const float4v dot = sh[s][i] + sl[s][i];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float v = fmaf(Sj[j], dot[j], fmaf(Sh::KCENTRE, Sj[j], Zj[j]) * sig);
+          const float v = fmaf(Sj[j] * kSub24, dot[j], Zj[j] * sig);
           sc[i][j] = s == 0 ? v : sc[i][j] + v;
         }
       }

@@ -252,7 +252,7 @@ __device__ __forceinline__ void write_partial_rows(const DecodeArgs& a, int b, i
 // the weights per tile): position P of a tile holds token
 // (P & ~7) + [0, 4, 1, 5, 2, 6, 3, 7][P & 7].
 constexpr int kPPitch = 128 + 8;  // halves per weight row (padding spreads LDS banks)
-constexpr int kWOld = 14, kWYoung = 10;  // record shares of the first and second workgroup of a compute unit
+constexpr int kWOld = 15, kWYoung = 10;  // record shares of the first and second workgroup of a compute unit
 
 template <int D_, int KB_>
 struct BodyShape {
@@ -392,9 +392,10 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
   // Partition of the sequence's records over its chunks.  With two
   // workgroups per compute unit, the first to land on a unit (grid index below
   // n_old) wins the issue arbitration against the second and scans a record
-  // ~1.4 times as fast (measured), so it takes kWOld records for every kWYoung
-  // of the second, and both end together; with few records per chunk, or one
-  // workgroup per unit, the split is even.
+  // ~1.4 times as fast (measured); it takes kWOld records for every kWYoung of
+  // the second (1.5: the second also pays the longer tail, measured best), so
+  // that both end together; with few records per chunk, or one workgroup per
+  // unit, the split is even.
   const int nb = sq.n_body_chunks;
   int r0, r1;
   if (Sh::WG_PER_CU == 2 && sq.n_rec >= 4 * nb) {

@@ -433,8 +433,6 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
   uint4 kd[NSUB][2][2], vd[NSUB][VT];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) load_keys(rec(r0) + s * SB, kd[s], wave, lane);
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) load_values<Sh>(rec(r0) + s * SB, vd[s], wave, lane);
   float* rows = (float*)qt;
   query_rows<D>(a, qraw, true, rows, wave, lane);
   __syncthreads();
@@ -474,6 +472,11 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
   __syncthreads();
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) make_qtilde<Sh>(mslot(r0) + s * MS, qph[s], qpl[s], qt[s], xs[s], G, wave, lane);
+  // the first record's value codes only now: at the start of the launch every
+  // workgroup asks for its first record at once, and keys requested ahead of
+  // values arrive ahead of them, so the first scores start sooner
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) load_values<Sh>(rec(r0) + s * SB, vd[s], wave, lane);
   uint2 mnext[NSUB];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) mnext[s] = *(const uint2*)(r0 + 2 < r1 ? rec(r0 + 2) + s * SB + mo : rec0);

@@ -156,6 +156,31 @@ class Pair:
                     for r in range(first, self.ora.info(s, l)[1]):
                         self.gpu.import_(s, l, h, kvq.REGION_BODY, r, self.ora.export(s, l, h, ocache.REGION_BODY, r))
 
+    def own_record_errors(self, layer, q16, scale=1.0):
+        """The decode criterion on a GPU-built cache (the GPU's exported records
+        dequantised by the oracle): max |o_gpu - o_ref| / rms(o_ref) per sequence
+        against float64 attention over the GPU's own records, and, for the
+        record, the float64 difference the GPU's records make against the
+        oracle's (fp16 flips of C).  The oracle's records are restored."""
+        t = self.torch
+        out = self.gpu.attn_decode(layer, list(range(self.n)), t.from_numpy(q16).cuda(), scale=scale)
+        got = out.float().cpu().numpy().astype(np.float64)
+        errs, cross = [], []
+        for s in range(self.n):
+            ref_o = self.ora.attention(layer, s, q16[s], scale)
+            saved = {}
+            for h in range(self.w.n_kv_heads):
+                for r in range(self.ora.info(s, layer)[1]):
+                    saved[(h, r)] = self.ora.export(s, layer, h, ocache.REGION_BODY, r)
+                    self.ora.import_record(s, layer, h, r, self.gpu.export(s, layer, h, kvq.REGION_BODY, r))
+            ref_g = self.ora.attention(layer, s, q16[s], scale)
+            for (h, r), buf in saved.items():
+                self.ora.import_record(s, layer, h, r, buf)
+            rms = math.sqrt(np.mean(ref_g ** 2))
+            errs.append(float(np.max(np.abs(got[s] - ref_g)) / rms))
+            cross.append(float(np.max(np.abs(ref_g - ref_o)) / rms))
+        return errs, cross
+
     # ------------------------------------------------------------ attention
     def queries(self, step, layer):
         return inputs.queries(self.w.seed, step, layer, self.n, self.w.n_q_heads, self.w.head_dim)

@@ -65,12 +65,16 @@ def test_records_conditional_parity(pair):
 
 def test_decode_gpu_built_cache(pair):
     """GPU decode over the GPU-built cache against float64 attention over the
-    oracle-built cache: the two caches differ only where an fp16 column scale
-    rounded the other way, so the bound is looser than on identical records."""
+    same cache (the GPU's exported records dequantised by the oracle), the
+    decode criterion.  The float64 difference between attention over the GPU's
+    records and over the oracle's (they differ where an fp16 column scale
+    rounded the other way, which the parity rules allow) is reported: one such
+    flip in a key channel moves peaked attention by up to ~2e-2 of its RMS."""
     for layer in range(pair.w.n_layers):
-        errs, _ = pair.decode_errors(layer, pair.queries(0, layer))
-        _say(f"[{pair.name}] layer={layer} decode (GPU-built cache) err={max(errs):.2e}")
-        assert max(errs) <= 2e-2
+        errs, cross = pair.own_record_errors(layer, pair.queries(0, layer))
+        _say(f"[{pair.name}] layer={layer} decode (GPU-built cache) err={max(errs):.2e}, "
+             f"GPU vs oracle records {max(cross):.2e}")
+        assert max(errs) <= ATTN_TOL
 
 
 @pytest.mark.parametrize("path", [kvq.PATH_VALU, kvq.PATH_MFMA])
@@ -139,7 +143,8 @@ def test_decode_step(name):
     bytes stay bit-exact with the oracle's appends; the attention of each step
     is checked against float64 attention over the oracle cache (records
     imported from the oracle; on a seal step the just-sealed records are the
-    GPU's own, hence the looser bound of a GPU-built cache there)."""
+    GPU's own: the oracle takes them too before its reference is computed, the
+    decode criterion on the same cache)."""
     steps = 40
     signs = None
     if name == "qwen27b":  # ring 360 after the build: the seal fires at step 24
@@ -173,14 +178,16 @@ def test_decode_step(name):
             assert p.ora.append(l, seqs, k[:, None], v[:, None]) == ocache.OK
             assert g == p.ora.seal(l, ocache.SEAL_IF_FULL)
             got = out.cpu().numpy().astype(np.float64)
-            tol = 2e-2 if g else ATTN_TOL
             n_seal_steps += g > 0
+            if g:  # both caches hold the GPU's new records from here on
+                for s in seqs:
+                    for h in range(w.n_kv_heads):
+                        for r in range(rec0[s], p.ora.info(s, l)[1]):
+                            p.ora.import_record(s, l, h, r, p.gpu.export(s, l, h, kvq.REGION_BODY, r))
             for s in seqs:
                 ref = p.ora.attention(l, s, q[s], 0.9)
                 err = float(np.max(np.abs(got[s] - ref)) / np.sqrt(np.mean(ref ** 2)))
-                assert err <= tol, (st, l, s, err, g)
-            if g:
-                p.import_oracle_records(first=min(rec0))
+                assert err <= ATTN_TOL, (st, l, s, err, g)
     _say(f"[step {name}] {steps} steps, {n_seal_steps} seal steps")
     assert n_seal_steps > 0
     p.check_info()

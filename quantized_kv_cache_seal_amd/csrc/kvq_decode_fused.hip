@@ -94,23 +94,6 @@ __device__ __forceinline__ half8 nib8_sub(uint32_t w) {
   return mfma_a(u);
 }
 
-// Transpose 4 tokens x 8 channels (one half8 per token) into 8 channel rows of
-// 4 tokens: row e of the destination gets halves e of t0..t3.
-__device__ __forceinline__ void store_t4x8(uint16_t* vt, int pitch, int row0, int col, const uint4 (&t)[4]) {
-  const uint32_t* w0 = (const uint32_t*)&t[0];
-  const uint32_t* w1 = (const uint32_t*)&t[1];
-  const uint32_t* w2 = (const uint32_t*)&t[2];
-  const uint32_t* w3 = (const uint32_t*)&t[3];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-    uint2 r;
-    r.x = __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sel);
-    r.y = __builtin_amdgcn_perm(w3[e >> 1], w2[e >> 1], sel);
-    *(uint2*)(vt + (row0 + e) * pitch + col) = r;
-  }
-}
-
 __device__ __forceinline__ uint32_t pick(const uint4& v, int e) {
   return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
 }
@@ -704,18 +687,6 @@ struct RingLds {
   static constexpr int total = X + 2 * 256;
   static_assert(16 * D * 4 <= D * kRPitch * 2, "query rows must fit the V^T area");
 };
-
-// Eight 6-bit codes held as 48 bits (lo, low 16 bits of hi), as fp16 u - 32.
-__device__ __forceinline__ half8 codes6_reg(uint32_t lo, uint32_t hi) {
-  uint4 u;
-  u.x = (lo & 63u) | ((lo << 10) & 0x3F0000u) | 0x64006400u;
-  u.y = ((lo >> 12) & 63u) | ((lo >> 2) & 0x3F0000u) | 0x64006400u;
-  u.z = ((lo >> 24) & 63u) | ((((lo >> 30) | (hi << 2)) & 63u) << 16) | 0x64006400u;
-  u.w = ((hi >> 4) & 63u) | ((hi << 6) & 0x3F0000u) | 0x64006400u;
-  const half8 off1056 = {(_Float16)1056.0f, (_Float16)1056.0f, (_Float16)1056.0f, (_Float16)1056.0f,
-                         (_Float16)1056.0f, (_Float16)1056.0f, (_Float16)1056.0f, (_Float16)1056.0f};
-  return mfma_a(u) - off1056;
-}
 
 // Registers of one ring step for this thread:
 //   k[kk]  the two aligned dwords holding the 8 key codes of its A operand

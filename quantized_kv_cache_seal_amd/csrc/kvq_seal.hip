@@ -8,269 +8,423 @@
 // zero point), then each row is rounded to the target width with its own fp16
 // scale S and zero point Z.
 //
-// Tile mapping: thread (wave w, lane l = 16 r4 + c16) holds rows 32w + 8r4 + i
-// (i < 8) and columns CPT*c16 + j (j < CPT), CPT = SUB/16, in registers for the
-// whole seal.  A row reduction is in-thread plus a 16-lane DPP exchange; a
-// column reduction is in-thread, a swap exchange across r4, then LDS across
-// the four waves.  Each pass computes the spread of x scaled by the other side's
-// current factors; the updated side's factor becomes 1/spread (equal to
-// exp(-l) of the log-domain update l += ln spread).
+// Balancing on the matrix cores.  The tile is x_ij = d_ib q_ij with q = u - 32
+// an integer in [-31, 31] (exact in fp16) and d_ib the tq6_0 scale of row i's
+// 128-value block b.  A pass needs two sums per row (or column) of the tile
+// scaled by the other side's factors:
+//   rows:    s_i = sum_b d_ib sum_{j in b} q_ij c_j,   s2_i = sum_b d_ib^2 sum_j q_ij^2 c_j^2
+//   columns: t_j = sum_i q_ij (d_ib r_i),              t2_j = sum_i q_ij^2 (d_ib r_i)^2
+// i.e. matrix-vector products, done as v_mfma_f32_16x16x32_f16 with the tile
+// (or its square, exact up to 961) as the A operand and the factor vector as
+// column 0 (fp16 hi) and column 1 (fp16 lo: the remainder) of B, so each factor
+// keeps 22 significant bits and every product is exact; the two columns of the
+// result are added.  Row passes read the tile with 8 consecutive columns of one
+// row per lane, column passes with 8 consecutive rows of one column per lane;
+// both copies stay in registers (the second is built through a transposed tile
+// in LDS).  The updated side's factor is 1/spread (equal to exp(-l) of the
+// log-domain update l += ln spread, spread the population standard deviation);
+// the factors pass between waves through LDS, one barrier per pass.
 //
 // The balancing factors (1/spread, ln spread) use the hardware square root,
 // reciprocal and log2 (about 1 ulp): only the column scales C leave the
 // balancing, and they are rounded to fp16.  Rounding is IEEE fp32 with no
-// fused multiply-add (built with -ffp-contract=off): y = x * fp32(1/C), S = fp16((max - min) / (2^b - 1))
-// (1.0 if zero), Z = fp16(min), code = clamp(rne((y - Z) * fp32(1/S)), 0, 2^b - 1).
-#include "kvq_device.h"
+// fused multiply-add (built with -ffp-contract=off): y = x * fp32(1/C),
+// S = fp16((max - min) / (2^b - 1)) (1.0 if zero), Z = fp16(min),
+// code = clamp(rne((y - Z) * fp32(1/S)), 0, 2^b - 1).
+#include "kvq_mfma.h"
 
 namespace kvq {
 
-// Reductions over the 16 lanes of a row (DPP: quad swaps, then the half-row
-// and row mirrors; every lane ends with the result) and over the four rows of
-// a wave for the same lane (the 32- and 16-lane swaps of this target: each
-// returns the lane's own value and its partner's, in some order).
+template <int SUBW>
+struct SealShape {
+  static constexpr int NB = SUBW / kQBlock;  // tq6_0 blocks per row
+  static constexpr int KR = SUBW / 32;       // row-pass k-steps (32 columns each)
+  static constexpr int CT = SUBW / 64;       // column tiles (16 columns) per wave
+  static constexpr int PITCH = 128 + 8;      // halves per row of the transposed tile (one column)
+  // LDS: the transposed tile, reused once consumed for the factor exchange
+  //   CF  [q, q^2][hi, lo][SUBW] fp16: B operands of the row pass (c, c^2)
+  //   RF  [NB][q, q^2][hi, lo][128] fp16: B operands of the column pass (d r, (d r)^2)
+  static constexpr int QT_BYTES = SUBW * PITCH * 2;
+  static constexpr int CF = 0, RF = CF + 2 * 2 * SUBW * 2, X_BYTES = RF + NB * 2 * 2 * 128 * 2;
+  static constexpr int BYTES = QT_BYTES > X_BYTES ? QT_BYTES : X_BYTES;
+};
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float sum16(float x) {
-  x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
-  x += dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
-  x += dpp<0x141>(x);  // row_half_mirror
-  x += dpp<0x140>(x);  // row_mirror
-  return x;
-}
-__device__ __forceinline__ float min16(float x) {
-  x = fminf(x, dpp<0xB1>(x));
-  x = fminf(x, dpp<0x4E>(x));
-  x = fminf(x, dpp<0x141>(x));
-  return fminf(x, dpp<0x140>(x));
-}
-__device__ __forceinline__ float max16(float x) {
-  x = fmaxf(x, dpp<0xB1>(x));
-  x = fmaxf(x, dpp<0x4E>(x));
-  x = fmaxf(x, dpp<0x141>(x));
-  return fmaxf(x, dpp<0x140>(x));
-}
-__device__ __forceinline__ float sum_rows4(float x) {
+// over lanes l, l ^ 16, l ^ 32, l ^ 48 (the 32- and 16-lane swaps of this
+// target: each returns the lane's own value and its partner's, in some order)
+__device__ __forceinline__ float sum_x16x32(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
   x = __int_as_float(a[0]) + __int_as_float(a[1]);
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
   return __int_as_float(b[0]) + __int_as_float(b[1]);
 }
-
-__device__ __forceinline__ uint32_t bits6(const uint32_t* wd, int j) {
-  const int p = 6 * j;
-  const uint64_t pair = ((uint64_t)wd[(p >> 5) + 1] << 32) | wd[p >> 5];
-  return (uint32_t)(pair >> (p & 31)) & 63u;
+__device__ __forceinline__ float min_x16x32(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = fminf(__int_as_float(a[0]), __int_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fminf(__int_as_float(b[0]), __int_as_float(b[1]));
+}
+__device__ __forceinline__ float max_x16x32(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = fmaxf(__int_as_float(a[0]), __int_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(b[0]), __int_as_float(b[1]));
 }
 
-template <int CPT>
-__global__ __launch_bounds__(256) void seal_kernel(SealArgs a) {
-  constexpr int COLS = 16 * CPT;
-  const Layout& y = a.y;
-  __shared__ float red[4][COLS][2];
+// x as the fp16 pair hi = fp16(x), lo = fp16(x - hi), element i of two arrays
+__device__ __forceinline__ void put_hilo(uint16_t* hi, uint16_t* lo, int i, float x) {
+  const uint16_t hb = f2h_bits(x);
+  hi[i] = hb;
+  lo[i] = f2h_bits(x - h2f(hb));
+}
 
+// q^2 of a packed operand (exact: |q| <= 31), formed in every pass: kept
+// opaque so that the compiler does not hoist the squares of the loop-invariant
+// tile out of the pass loop, which would double the tile's registers.
+__device__ __forceinline__ half8 sq8(half8 v) {
+  uint4 u, o;
+  __builtin_memcpy(&u, &v, 16);
+  asm volatile("v_pk_mul_f16 %0, %1, %1" : "=v"(o.x) : "v"(u.x));
+  asm volatile("v_pk_mul_f16 %0, %1, %1" : "=v"(o.y) : "v"(u.y));
+  asm volatile("v_pk_mul_f16 %0, %1, %1" : "=v"(o.z) : "v"(u.z));
+  asm volatile("v_pk_mul_f16 %0, %1, %1" : "=v"(o.w) : "v"(u.w));
+  return mfma_a(o);
+}
+
+// fp32 of element e of a packed operand, written out so that the second
+// rounding sweep over the tile recomputes y instead of keeping the first
+// sweep's 64 values per row alive
+__device__ __forceinline__ float cvt_e(const half8& v, int e) {
+  uint4 u;
+  __builtin_memcpy(&u, &v, 16);
+  const uint32_t wd = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
+  float d;
+  if (e & 1)
+    asm volatile("v_cvt_f32_f16_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1" : "=v"(d) : "v"(wd));
+  else
+    asm volatile("v_cvt_f32_f16 %0, %1" : "=v"(d) : "v"(wd));
+  return d;
+}
+
+template <int SUBW>
+struct SealLds {
+  uint8_t smem[SealShape<SUBW>::BYTES] __attribute__((aligned(16)));
+  float ds[SealShape<SUBW>::NB][kGroup];     // d_ib
+  float lcs[SUBW] __attribute__((aligned(16)));   // ln spread of each column (last column pass)
+  float invc[SUBW] __attribute__((aligned(16)));  // fp32(1 / C_j)
+  float rinv[kGroup];                       // fp32(1 / S_i)
+  float zrow[kGroup];                       // Z_i
+  float red[4];
+};
+
+// One tile; KV (0 keys, 1 values) is a compile-time choice so that the keys'
+// path holds one copy of the tile once the balancing is done.
+template <int SUBW, int KV>
+__device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, int r, int sub, int h, int s,
+                                          int layer) {
+  using Sh = SealShape<SUBW>;
+  constexpr int NB = Sh::NB, KR = Sh::KR, CT = Sh::CT, PITCH = Sh::PITCH;
+  constexpr int kv = KV;
+  const Layout& y = a.y;
+  uint8_t* smem = L.smem;
+  auto& ds = L.ds;
+  float* lcs = L.lcs;
+  float* invc = L.invc;
+  float* rinv = L.rinv;
+  float* zrow = L.zrow;
+  float* red = L.red;
+  uint16_t* qt = (uint16_t*)smem;
+  uint16_t* cfl = (uint16_t*)(smem + Sh::CF);  // [2][2][SUBW]
+  uint16_t* rfl = (uint16_t*)(smem + Sh::RF);  // [NB][2][2][128]
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
+  const int slot0 = (int)(((int64_t)r * kGroup) % y.cap);
+  auto slot_of = [&](int row) { const int t = slot0 + row; return t >= y.cap ? t - y.cap : t; };
+  // ring rows of this (K|V) head; the sub-tile's channels start at block sub * NB
+  const int64_t row_bytes = (int64_t)y.NB * kQBytes;
+  const uint8_t* codes = a.arena + rcode_off(y, s, layer, h, kv, 0) + (int64_t)sub * NB * kQBytes;
+  const uint8_t* scales = a.arena + rscale_off(y, s, layer, h, kv, 0) + 2 * sub * NB;
+
+  // ---- the tile, row layout: ar[t][kk] = q of row 16 (2w + t) + m, columns
+  // 32 kk + 8 g .. + 7 (the A operand of a row pass)
+  half8 ar[2][KR];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint8_t* row = codes + (int64_t)slot_of(16 * (2 * w + t) + m) * row_bytes + ((6 * g) & ~3);
+    const uint32_t sh = (g & 1) ? 16u : 0u;
+#pragma unroll
+    for (int kk = 0; kk < KR; ++kk) {
+      const uint32_t* p = (const uint32_t*)(row + 24 * kk);
+      const uint32_t lo = p[0], hi = p[1];
+      ar[t][kk] = codes6_reg(__builtin_amdgcn_alignbit(hi, lo, sh), hi >> sh);
+    }
+  }
+  // block scales d of every row
+  for (int i = tid; i < NB * kGroup; i += 256) {
+    const int row = i % kGroup, b = i / kGroup;
+    ds[b][row] = h2f(*(const uint16_t*)(scales + (int64_t)slot_of(row) * (y.NB * 2) + 2 * b));
+  }
+  // transposed tile in LDS: item (tq, c16) = rows 4 tq .. + 3, columns 16 c16 .. + 15
+  for (int it = tid; it < 32 * (SUBW / 16); it += 256) {
+    const int tq = it & 31, c16 = it >> 5;
+    uint4 lo8[4], hi8[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t* p = (const uint32_t*)(codes + (int64_t)slot_of(4 * tq + k) * row_bytes + (c16 / 8) * kQBytes +
+                                            12 * (c16 % 8));
+      const uint32_t v0 = p[0], v1 = p[1], v2 = p[2];
+      const half8 x0 = codes6_reg(v0, v1);
+      const half8 x1 = codes6_reg(__builtin_amdgcn_alignbit(v2, v1, 16), v2 >> 16);
+      __builtin_memcpy(&lo8[k], &x0, 16);
+      __builtin_memcpy(&hi8[k], &x1, 16);
+    }
+    store_t4x8(qt, PITCH, 16 * c16, 4 * tq, lo8);
+    store_t4x8(qt, PITCH, 16 * c16 + 8, 4 * tq, hi8);
+  }
+  __syncthreads();
+  // column layout: ac[ct][kr] = q of column 16 (CT w + ct) + m, rows 32 kr + 8 g .. + 7
+  half8 ac[CT][4];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int kr = 0; kr < 4; ++kr)
+      ac[ct][kr] = mfma_a(*(const uint4*)(qt + (16 * (CT * w + ct) + m) * PITCH + 32 * kr + 8 * g));
+  __syncthreads();  // the transposed tile is consumed: its area holds the factors from here on
+  for (int j = tid; j < SUBW; j += 256) {  // first row pass: c = 1 (exactly: hi 1, lo 0)
+    cfl[0 * SUBW + j] = 0x3C00;
+    cfl[1 * SUBW + j] = 0;
+    cfl[2 * SUBW + j] = 0x3C00;
+    cfl[3 * SUBW + j] = 0;
+    lcs[j] = 0.0f;
+  }
+  __syncthreads();
+
+  const bool bl = m < 2;  // lanes feeding B column 0 (hi) or 1 (lo); the rest feed zeros
+  const half8 zero8 = {};
+  const int wb = SUBW == 256 ? (w >> 1) : 0;  // the block of this wave's columns
+
+  for (int p = 0; p < a.passes; ++p) {
+    if ((p & 1) == 0) {
+      // ---- row pass: rows 16 (2w + t) + 4 g + i end up in lanes m = 0 (hi) and 1 (lo)
+      float4v a1[2][NB], a2[2][NB];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) a1[t][b] = a2[t][b] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < KR; ++kk) {
+        const int b = kk / 4;
+        const half8 v1 = mfma_a(*(const uint4*)(cfl + (0 + (m & 1)) * SUBW + 32 * kk + 8 * g));
+        const half8 v2 = mfma_a(*(const uint4*)(cfl + (2 + (m & 1)) * SUBW + 32 * kk + 8 * g));
+        const half8 b1 = bl ? v1 : zero8, b2 = bl ? v2 : zero8;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          a1[t][b] = mfma16(ar[t][kk], b1, a1[t][b]);
+          a2[t][b] = mfma16(sq8(ar[t][kk]), b2, a2[t][b]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * (2 * w + t) + 4 * g + i;
+          float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const float x1 = a1[t][b][i] + dpp<0xB1>(a1[t][b][i]);  // hi + lo (quad_perm [1, 0, 3, 2])
+            const float x2 = a2[t][b][i] + dpp<0xB1>(a2[t][b][i]);
+            const float d = ds[b][row];
+            s1 = fmaf(d, x1, s1);
+            s2 = fmaf(d * d, x2, s2);
+          }
+          const float mean = s1 / (float)SUBW;
+          const float var = fmaxf(s2 / (float)SUBW - mean * mean, 0.0f);
+          const float rf = __builtin_amdgcn_rcpf(fmaxf(__builtin_amdgcn_sqrtf(var), 1e-30f));
+          if (m == 0) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              const float f = ds[b][row] * rf;
+              uint16_t* base = rfl + b * 4 * kGroup;
+              put_hilo(base + 0 * kGroup, base + 1 * kGroup, row, f);
+              put_hilo(base + 2 * kGroup, base + 3 * kGroup, row, f * f);
+            }
+          }
+        }
+      }
+    } else {
+      // ---- column pass: columns 16 (CT w + ct) + 4 g + i end up in lanes m = 0, 1
+      float4v c1[CT], c2[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) c1[ct] = c2[ct] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+      const uint16_t* base = rfl + wb * 4 * kGroup;
+#pragma unroll
+      for (int kr = 0; kr < 4; ++kr) {
+        const half8 v1 = mfma_a(*(const uint4*)(base + (0 + (m & 1)) * kGroup + 32 * kr + 8 * g));
+        const half8 v2 = mfma_a(*(const uint4*)(base + (2 + (m & 1)) * kGroup + 32 * kr + 8 * g));
+        const half8 b1 = bl ? v1 : zero8, b2 = bl ? v2 : zero8;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          c1[ct] = mfma16(ac[ct][kr], b1, c1[ct]);
+          c2[ct] = mfma16(sq8(ac[ct][kr]), b2, c2[ct]);
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int col = 16 * (CT * w + ct) + 4 * g + i;
+          const float x1 = c1[ct][i] + dpp<0xB1>(c1[ct][i]);
+          const float x2 = c2[ct][i] + dpp<0xB1>(c2[ct][i]);
+          const float mean = x1 / (float)kGroup;
+          const float var = fmaxf(x2 / (float)kGroup - mean * mean, 0.0f);
+          const float sig = fmaxf(__builtin_amdgcn_sqrtf(var), 1e-30f);
+          const float cf = __builtin_amdgcn_rcpf(sig);
+          if (m == 0) {
+            put_hilo(cfl + 0 * SUBW, cfl + 1 * SUBW, col, cf);
+            put_hilo(cfl + 2 * SUBW, cfl + 3 * SUBW, col, cf * cf);
+            lcs[col] = __builtin_amdgcn_logf(sig) * 0.6931471805599453f;  // log2 -> ln
+          }
+        }
+      }
+    }
+    // the other side's factors are written; every wave has read the ones the
+    // pass used (CF in row passes, RF in column passes)
+    __syncthreads();
+  }
+
+  // ---- column scales: centre the log scales, clamp, fp16 (thread j: column j)
+  const int bits = kv ? y.vbits : y.kbits;
+  const float levels = (float)((1 << bits) - 1);
+  uint8_t* rec = a.arena + rec_off(y, s, layer, h, r) + (int64_t)sub * y.sub_bytes;
+  uint8_t* meta = rec + y.kcode_bytes + y.vcode_bytes + kv * 2 * (SUBW + 2 * kGroup);
+  {
+    float v = tid < SUBW ? lcs[tid] : 0.0f;
+    v += dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v += dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v += dpp<0x141>(v);  // row_half_mirror
+    v += dpp<0x140>(v);  // row_mirror
+    v = sum_x16x32(v);
+    if (l == 0) red[w] = v;
+    __syncthreads();
+    const float lmean = (red[0] + red[1] + red[2] + red[3]) / (float)SUBW;
+    if (tid < SUBW) {
+      const float c = fminf(fmaxf(lcs[tid] - lmean, -9.0f), 9.0f);
+      const uint16_t cb = f2h_bits(expf(c));
+      ((uint16_t*)meta)[tid] = cb;
+      invc[tid] = 1.0f / h2f(cb);
+    }
+    __syncthreads();
+  }
+
+  // ---- per-row rounding (row layout): y = x * fp32(1 / C), min and max per row
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int row = 16 * (2 * w + t) + m;
+    float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int kk = 0; kk < KR; ++kk) {
+      const float d = ds[kk / 4][row];
+      const float4 i0 = *(const float4*)(invc + 32 * kk + 8 * g), i1 = *(const float4*)(invc + 32 * kk + 8 * g + 4);
+      const float ic[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float yv = (d * (float)ar[t][kk][e]) * ic[e];
+        mn = fminf(mn, yv);
+        mx = fmaxf(mx, yv);
+      }
+    }
+    mn = min_x16x32(mn);
+    mx = max_x16x32(mx);
+    uint16_t Sb = f2h_sat_bits((mx - mn) / levels);
+    if (h2f(Sb) == 0.0f) Sb = 0x3C00;  // 1.0
+    const uint16_t Zb = f2h_sat_bits(mn);
+    const float Zf = h2f(Zb);
+    const float inv = 1.0f / h2f(Sb);
+    if (g == 0) {
+      ((uint16_t*)(meta + 2 * SUBW))[row] = Sb;
+      ((uint16_t*)(meta + 2 * SUBW + 2 * kGroup))[row] = Zb;
+      rinv[row] = inv;
+      zrow[row] = Zf;
+    }
+    if constexpr (kv == 0) {  // keys: row-major codes, this lane's 8 columns of each k-step
+#pragma unroll
+      for (int kk = 0; kk < KR; ++kk) {
+        const float d = ds[kk / 4][row];
+        const float4 i0 = *(const float4*)(invc + 32 * kk + 8 * g), i1 = *(const float4*)(invc + 32 * kk + 8 * g + 4);
+        const float ic[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+        uint32_t cq[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float yv = (d * cvt_e(ar[t][kk], e)) * ic[e];
+          cq[e] = (uint32_t)fminf(fmaxf(rintf((yv - Zf) * inv), 0.0f), levels);
+        }
+        if (bits == 4) {
+          uint32_t pk = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pk |= cq[e] << (4 * e);
+          *(uint32_t*)(rec + (int64_t)row * (SUBW / 2) + (32 * kk + 8 * g) / 2) = pk;
+        } else {
+          uint2 pk = make_uint2(0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pk.x |= cq[e] << (8 * e);
+            pk.y |= cq[e + 4] << (8 * e);
+          }
+          *(uint2*)(rec + (int64_t)row * SUBW + 32 * kk + 8 * g) = pk;
+        }
+      }
+    }
+  }
+  if constexpr (kv == 1) {  // values: channel-major codes (column layout), 8 tokens of one channel per dword
+    __syncthreads();
+    uint8_t* vbase = rec + y.kcode_bytes;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int col = 16 * (CT * w + ct) + m;
+      const float ic = invc[col];
+#pragma unroll
+      for (int kr = 0; kr < 4; ++kr) {
+        uint32_t pk = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int row = 32 * kr + 8 * g + e;
+          const float yv = (ds[wb][row] * (float)ac[ct][kr][e]) * ic;
+          const uint32_t c = (uint32_t)fminf(fmaxf(rintf((yv - zrow[row]) * rinv[row]), 0.0f), levels);
+          pk |= c << (4 * e);
+        }
+        *(uint32_t*)(vbase + (int64_t)col * (kGroup / 2) + (32 * kr + 8 * g) / 2) = pk;
+      }
+    }
+  }
+}
+
+template <int SUBW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void seal_kernel(SealArgs a) {
+  __shared__ SealLds<SUBW> L;
   const int gx = blockIdx.x;
   int ti = 0;
   while (ti + 1 < a.n_tasks && gx >= a.task[ti + 1].first) ++ti;
   const SealTask tk = a.task[ti];
   const int r = tk.rec0 + (gx - tk.first);
   int by = blockIdx.y;
-  const int sub = by % y.nsub;
-  by /= y.nsub;
+  const int sub = by % a.y.nsub;
+  by /= a.y.nsub;
   const int kv = by & 1, h = by >> 1;
-  const int s = tk.slot, layer = tk.layer;
-
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r4 = l >> 4, c16 = l & 15;
-  const int row0 = 32 * w + 8 * r4, col0 = CPT * c16;
-  const int slot0 = (int)(((int64_t)r * kGroup) % y.cap);
-  const int gch = sub * COLS + col0;
-  const int blk = gch / kQBlock, k0 = gch % kQBlock;
-
-  // ---- load the tile: x = d * (u - 32), exact in fp32
-  float X[8][CPT];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int slot = slot0 + row0 + i;
-    const uint8_t* cp = a.arena + rcode_off(y, s, layer, h, kv, slot) + blk * kQBytes + (k0 * 6) / 8;
-    const float d = h2f(*(const uint16_t*)(a.arena + rscale_off(y, s, layer, h, kv, slot) + 2 * blk));
-    uint32_t wd[4];
-    if constexpr (CPT == 16) {
-      const uint32_t* p32 = (const uint32_t*)cp;
-      wd[0] = p32[0];
-      wd[1] = p32[1];
-      wd[2] = p32[2];
-      wd[3] = 0;
-    } else {
-      const uint16_t* p16 = (const uint16_t*)cp;
-      wd[0] = (uint32_t)p16[0] | ((uint32_t)p16[1] << 16);
-      wd[1] = p16[2];
-      wd[2] = 0;
-      wd[3] = 0;
-    }
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) X[i][j] = d * (float)((int)bits6(wd, j) - 32);
-  }
-
-  // ---- Sinkhorn passes
-  float cf[CPT], rf[8], lc[CPT];
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) {
-    cf[j] = 1.0f;
-    lc[j] = 0.0f;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) rf[i] = 1.0f;
-
-  for (int p = 0; p < a.passes; ++p) {
-    if ((p & 1) == 0) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float sm = 0.0f, sq = 0.0f;
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-          const float t = X[i][j] * cf[j];
-          sm += t;
-          sq = fmaf(t, t, sq);
-        }
-        sm = sum16(sm);
-        sq = sum16(sq);
-        const float mean = sm / (float)COLS;
-        const float var = fmaxf(sq / (float)COLS - mean * mean, 0.0f);
-        rf[i] = __builtin_amdgcn_rcpf(fmaxf(__builtin_amdgcn_sqrtf(var), 1e-30f));
-      }
-    } else {
-      float sm[CPT], sq[CPT];
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        sm[j] = 0.0f;
-        sq[j] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float t = X[i][j] * rf[i];
-          sm[j] += t;
-          sq[j] = fmaf(t, t, sq[j]);
-        }
-        sm[j] = sum_rows4(sm[j]);
-        sq[j] = sum_rows4(sq[j]);
-      }
-      if (r4 == 0) {
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-          red[w][col0 + j][0] = sm[j];
-          red[w][col0 + j][1] = sq[j];
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        const float ts = red[0][col0 + j][0] + red[1][col0 + j][0] + red[2][col0 + j][0] + red[3][col0 + j][0];
-        const float tq = red[0][col0 + j][1] + red[1][col0 + j][1] + red[2][col0 + j][1] + red[3][col0 + j][1];
-        const float mean = ts / (float)kGroup;
-        const float var = fmaxf(tq / (float)kGroup - mean * mean, 0.0f);
-        const float sig = fmaxf(__builtin_amdgcn_sqrtf(var), 1e-30f);
-        cf[j] = __builtin_amdgcn_rcpf(sig);
-        lc[j] = __builtin_amdgcn_logf(sig) * 0.6931471805599453f;  // log2 -> ln
-      }
-      __syncthreads();
-    }
-  }
-
-  // ---- column scales: centre the log scales, clamp, fp16
-  float ls = 0.0f;
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) ls += lc[j];
-  ls = sum16(ls);
-  const float lmean = ls / (float)COLS;
-  uint16_t Cb[CPT];
-  float invC[CPT];
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) {
-    const float v = fminf(fmaxf(lc[j] - lmean, -9.0f), 9.0f);
-    Cb[j] = f2h_bits(expf(v));
-    invC[j] = 1.0f / h2f(Cb[j]);
-  }
-
-  // ---- per-row rounding and packing
-  const int bits = kv ? y.vbits : y.kbits;
-  const float levels = (float)((1 << bits) - 1);
-  uint8_t* rec = a.arena + rec_off(y, s, layer, h, r) + (int64_t)sub * y.sub_bytes;
-  uint8_t* meta = rec + y.kcode_bytes + y.vcode_bytes + kv * 2 * (COLS + 2 * kGroup);
-  uint32_t vw[CPT];
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) vw[j] = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float yv[CPT];
-    float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      yv[j] = X[i][j] * invC[j];
-      mn = fminf(mn, yv[j]);
-      mx = fmaxf(mx, yv[j]);
-    }
-    mn = min16(mn);
-    mx = max16(mx);
-    uint16_t Sb = f2h_sat_bits((mx - mn) / levels);
-    if (h2f(Sb) == 0.0f) Sb = 0x3C00;  // 1.0
-    const uint16_t Zb = f2h_sat_bits(mn);
-    const float Zf = h2f(Zb);
-    const float inv = 1.0f / h2f(Sb);
-    uint32_t cq[CPT];
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) cq[j] = (uint32_t)fminf(fmaxf(rintf((yv[j] - Zf) * inv), 0.0f), levels);
-    const int row = row0 + i;
-    if (kv == 0) {
-      if (bits == 4) {
-        uint32_t pk[CPT / 8];
-#pragma unroll
-        for (int q = 0; q < CPT / 8; ++q) {
-          pk[q] = 0;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pk[q] |= cq[8 * q + e] << (4 * e);
-        }
-        uint32_t* dst = (uint32_t*)(rec + (int64_t)row * (COLS / 2) + col0 / 2);
-#pragma unroll
-        for (int q = 0; q < CPT / 8; ++q) dst[q] = pk[q];
-      } else {
-        uint32_t pk[CPT / 4];
-#pragma unroll
-        for (int q = 0; q < CPT / 4; ++q) {
-          pk[q] = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pk[q] |= cq[4 * q + e] << (8 * e);
-        }
-        uint32_t* dst = (uint32_t*)(rec + (int64_t)row * COLS + col0);
-#pragma unroll
-        for (int q = 0; q < CPT / 4; ++q) dst[q] = pk[q];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) vw[j] |= cq[j] << (4 * i);
-    }
-    if (c16 == 0) {
-      ((uint16_t*)(meta + 2 * COLS))[row] = Sb;
-      ((uint16_t*)(meta + 2 * COLS + 2 * kGroup))[row] = Zb;
-    }
-  }
-  if (kv == 1) {
-    uint8_t* vbase = rec + y.kcode_bytes;
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) *(uint32_t*)(vbase + (int64_t)(col0 + j) * (kGroup / 2) + row0 / 2) = vw[j];
-  }
-  if (w == 0 && r4 == 0) {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) ((uint16_t*)meta)[col0 + j] = Cb[j];
-  }
+  if (kv == 0)
+    seal_tile<SUBW, 0>(a, L, r, sub, h, tk.slot, tk.layer);
+  else
+    seal_tile<SUBW, 1>(a, L, r, sub, h, tk.slot, tk.layer);
 }
 
 hipError_t launch_seal(const SealArgs& a, hipStream_t stream) {
   dim3 grid(a.total_groups, 2 * a.y.H * a.y.nsub);
   if (a.y.sub == 256)
-    hipLaunchKernelGGL(seal_kernel<16>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(seal_kernel<256>, grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(seal_kernel<8>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(seal_kernel<128>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -15,10 +15,10 @@
 //   rows:    s_i = sum_b d_ib sum_{j in b} q_ij c_j,   s2_i = sum_b d_ib^2 sum_j q_ij^2 c_j^2
 //   columns: t_j = sum_i q_ij (d_ib r_i),              t2_j = sum_i q_ij^2 (d_ib r_i)^2
 // i.e. matrix-vector products, done as v_mfma_f32_16x16x32_f16 with the tile
-// (or its square, exact up to 961) as the A operand and the factor vector as
-// column 0 (fp16 hi) and column 1 (fp16 lo: the remainder) of B, so each factor
-// keeps 22 significant bits and every product is exact; the two columns of the
-// result are added.  Row passes read the tile with 8 consecutive columns of one
+// (or its square, exact up to 961) as the A operand and the factor vector in B
+// (fp16 hi in the even columns, fp16 lo, the remainder, in the odd ones), so
+// each factor keeps 22 significant bits and every product is exact; a column
+// pair of the result is added.  Row passes read the tile with 8 consecutive columns of one
 // row per lane, column passes with 8 consecutive rows of one column per lane;
 // both copies stay in registers (the second is built through a transposed tile
 // in LDS).  The updated side's factor is 1/spread (equal to exp(-l) of the
@@ -72,6 +72,11 @@ __device__ __forceinline__ float max_x16x32(float x) {
   x = fmaxf(__int_as_float(a[0]), __int_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
   return fmaxf(__int_as_float(b[0]), __int_as_float(b[1]));
+}
+
+// element i (a per-lane index) of a 4-vector
+__device__ __forceinline__ float pick4(const float4v& v, int i) {
+  return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
 }
 
 // x as the fp16 pair hi = fp16(x), lo = fp16(x - hi), element i of two arrays
@@ -202,13 +207,18 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
   }
   __syncthreads();
 
-  const bool bl = m < 2;  // lanes feeding B column 0 (hi) or 1 (lo); the rest feed zeros
-  const half8 zero8 = {};
+  // B carries the factor's fp16 hi in its even columns and lo in its odd ones
+  // (the same 16 values in every column pair), so every lane ends with sums of
+  // its rows: lane m of lane group g holds rows 4 g .. + 3 (hi part for even m,
+  // lo for odd), and the pair (m, m ^ 1) adds them with one DPP step.  Each
+  // lane pair then takes its own row (or columns) for the statistics.
   const int wb = SUBW == 256 ? (w >> 1) : 0;  // the block of this wave's columns
+  const int pr = m >> 1;                       // lane pair 0..7
+  constexpr int NCL = CT / 2;                  // columns per lane pair in a column pass
 
   for (int p = 0; p < a.passes; ++p) {
     if ((p & 1) == 0) {
-      // ---- row pass: rows 16 (2w + t) + 4 g + i end up in lanes m = 0 (hi) and 1 (lo)
+      // ---- row pass: pair pr takes row 16 (2w + t) + 4 g + i, t = pr / 4, i = pr % 4
       float4v a1[2][NB], a2[2][NB];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -217,54 +227,49 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
 #pragma unroll
       for (int kk = 0; kk < KR; ++kk) {
         const int b = kk / 4;
-        const half8 v1 = mfma_a(*(const uint4*)(cfl + (0 + (m & 1)) * SUBW + 32 * kk + 8 * g));
-        const half8 v2 = mfma_a(*(const uint4*)(cfl + (2 + (m & 1)) * SUBW + 32 * kk + 8 * g));
-        const half8 b1 = bl ? v1 : zero8, b2 = bl ? v2 : zero8;
+        const half8 b1 = mfma_a(*(const uint4*)(cfl + (0 + (m & 1)) * SUBW + 32 * kk + 8 * g));
+        const half8 b2 = mfma_a(*(const uint4*)(cfl + (2 + (m & 1)) * SUBW + 32 * kk + 8 * g));
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           a1[t][b] = mfma16(ar[t][kk], b1, a1[t][b]);
           a2[t][b] = mfma16(sq8(ar[t][kk]), b2, a2[t][b]);
         }
       }
+      const int t = pr >> 2, i = pr & 3;
+      const int row = 16 * (2 * w + t) + 4 * g + i;
+      float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int b = 0; b < NB; ++b) {
+        float x1 = pick4(t ? a1[1][b] : a1[0][b], i), x2 = pick4(t ? a2[1][b] : a2[0][b], i);
+        x1 += dpp<0xB1>(x1);  // hi + lo (quad_perm [1, 0, 3, 2])
+        x2 += dpp<0xB1>(x2);
+        const float d = ds[b][row];
+        s1 = fmaf(d, x1, s1);
+        s2 = fmaf(d * d, x2, s2);
+      }
+      const float mean = s1 / (float)SUBW;
+      const float var = fmaxf(s2 / (float)SUBW - mean * mean, 0.0f);
+      const float rf = __builtin_amdgcn_rcpf(fmaxf(__builtin_amdgcn_sqrtf(var), 1e-30f));
+      if ((m & 1) == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * (2 * w + t) + 4 * g + i;
-          float s1 = 0.0f, s2 = 0.0f;
-#pragma unroll
-          for (int b = 0; b < NB; ++b) {
-            const float x1 = a1[t][b][i] + dpp<0xB1>(a1[t][b][i]);  // hi + lo (quad_perm [1, 0, 3, 2])
-            const float x2 = a2[t][b][i] + dpp<0xB1>(a2[t][b][i]);
-            const float d = ds[b][row];
-            s1 = fmaf(d, x1, s1);
-            s2 = fmaf(d * d, x2, s2);
-          }
-          const float mean = s1 / (float)SUBW;
-          const float var = fmaxf(s2 / (float)SUBW - mean * mean, 0.0f);
-          const float rf = __builtin_amdgcn_rcpf(fmaxf(__builtin_amdgcn_sqrtf(var), 1e-30f));
-          if (m == 0) {
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-              const float f = ds[b][row] * rf;
-              uint16_t* base = rfl + b * 4 * kGroup;
-              put_hilo(base + 0 * kGroup, base + 1 * kGroup, row, f);
-              put_hilo(base + 2 * kGroup, base + 3 * kGroup, row, f * f);
-            }
-          }
+        for (int b = 0; b < NB; ++b) {
+          const float f = ds[b][row] * rf;
+          uint16_t* base = rfl + b * 4 * kGroup;
+          put_hilo(base + 0 * kGroup, base + 1 * kGroup, row, f);
+          put_hilo(base + 2 * kGroup, base + 3 * kGroup, row, f * f);
         }
       }
     } else {
-      // ---- column pass: columns 16 (CT w + ct) + 4 g + i end up in lanes m = 0, 1
+      // ---- column pass: pair pr takes columns 16 (CT w + ct) + 4 g + i of its
+      // NCL slots (ct, i) = (k / 4, k % 4), k = NCL pr + e
       float4v c1[CT], c2[CT];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) c1[ct] = c2[ct] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
       const uint16_t* base = rfl + wb * 4 * kGroup;
 #pragma unroll
       for (int kr = 0; kr < 4; ++kr) {
-        const half8 v1 = mfma_a(*(const uint4*)(base + (0 + (m & 1)) * kGroup + 32 * kr + 8 * g));
-        const half8 v2 = mfma_a(*(const uint4*)(base + (2 + (m & 1)) * kGroup + 32 * kr + 8 * g));
-        const half8 b1 = bl ? v1 : zero8, b2 = bl ? v2 : zero8;
+        const half8 b1 = mfma_a(*(const uint4*)(base + (0 + (m & 1)) * kGroup + 32 * kr + 8 * g));
+        const half8 b2 = mfma_a(*(const uint4*)(base + (2 + (m & 1)) * kGroup + 32 * kr + 8 * g));
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           c1[ct] = mfma16(ac[ct][kr], b1, c1[ct]);
@@ -272,21 +277,27 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
         }
       }
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
+      for (int e = 0; e < NCL; ++e) {
+        const int k = NCL * pr + e, ct = k >> 2, i = k & 3;
+        const int col = 16 * (CT * w + ct) + 4 * g + i;
+        float4v v1 = c1[0], v2 = c2[0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int col = 16 * (CT * w + ct) + 4 * g + i;
-          const float x1 = c1[ct][i] + dpp<0xB1>(c1[ct][i]);
-          const float x2 = c2[ct][i] + dpp<0xB1>(c2[ct][i]);
-          const float mean = x1 / (float)kGroup;
-          const float var = fmaxf(x2 / (float)kGroup - mean * mean, 0.0f);
-          const float sig = fmaxf(__builtin_amdgcn_sqrtf(var), 1e-30f);
-          const float cf = __builtin_amdgcn_rcpf(sig);
-          if (m == 0) {
-            put_hilo(cfl + 0 * SUBW, cfl + 1 * SUBW, col, cf);
-            put_hilo(cfl + 2 * SUBW, cfl + 3 * SUBW, col, cf * cf);
-            lcs[col] = __builtin_amdgcn_logf(sig) * 0.6931471805599453f;  // log2 -> ln
+        for (int c = 1; c < CT; ++c)
+          if (ct == c) {
+            v1 = c1[c];
+            v2 = c2[c];
           }
+        float x1 = pick4(v1, i), x2 = pick4(v2, i);
+        x1 += dpp<0xB1>(x1);
+        x2 += dpp<0xB1>(x2);
+        const float mean = x1 / (float)kGroup;
+        const float var = fmaxf(x2 / (float)kGroup - mean * mean, 0.0f);
+        const float sig = fmaxf(__builtin_amdgcn_sqrtf(var), 1e-30f);
+        const float cf = __builtin_amdgcn_rcpf(sig);
+        if ((m & 1) == 0) {
+          put_hilo(cfl + 0 * SUBW, cfl + 1 * SUBW, col, cf);
+          put_hilo(cfl + 2 * SUBW, cfl + 3 * SUBW, col, cf * cf);
+          lcs[col] = __builtin_amdgcn_logf(sig) * 0.6931471805599453f;  // log2 -> ln
         }
       }
     }

@@ -30,7 +30,8 @@
 // balancing, and they are rounded to fp16.  Rounding is IEEE fp32 with no
 // fused multiply-add (built with -ffp-contract=off): y = x * fp32(1/C),
 // S = fp16((max - min) / (2^b - 1)) (1.0 if zero), Z = fp16(min),
-// code = clamp(rne((y - Z) * fp32(1/S)), 0, 2^b - 1).
+// code = clamp(rne((y - Z) * fp32(1/S)), 0, 2^b - 1) (the clamp as one median
+// of three, the same value for every finite input).
 #include "kvq_mfma.h"
 
 namespace kvq {
@@ -370,7 +371,7 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float yv = (d * cvt_e(ar[t][kk], e)) * ic[e];
-          cq[e] = (uint32_t)fminf(fmaxf(rintf((yv - Zf) * inv), 0.0f), levels);
+          cq[e] = (uint32_t)__builtin_amdgcn_fmed3f(rintf((yv - Zf) * inv), 0.0f, levels);
         }
         if (bits == 4) {
           uint32_t pk = 0;
@@ -403,7 +404,7 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
         for (int e = 0; e < 8; ++e) {
           const int row = 32 * kr + 8 * g + e;
           const float yv = (ds[wb][row] * (float)ac[ct][kr][e]) * ic;
-          const uint32_t c = (uint32_t)fminf(fmaxf(rintf((yv - zrow[row]) * rinv[row]), 0.0f), levels);
+          const uint32_t c = (uint32_t)__builtin_amdgcn_fmed3f(rintf((yv - zrow[row]) * rinv[row]), 0.0f, levels);
           pk |= c << (4 * e);
         }
         *(uint32_t*)(vbase + (int64_t)col * (kGroup / 2) + (32 * kr + 8 * g) / 2) = pk;

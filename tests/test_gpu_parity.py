@@ -119,6 +119,54 @@ def test_streaming_one_token_per_step():
     assert max(errs) <= ATTN_TOL
 
 
+def test_many_sequences_split_launches():
+    """More sequences than one launch carries (32 per decode launch) and more
+    (sequence, layer) seal tasks than one seal launch carries (64): appends,
+    seals and decodes split over several launches, each against the oracle."""
+    w = configs.QWEN27B.scaled(n_layers=2, n_kv_heads=1, n_q_heads=6, tail_min=256, tail_max=384, ctx=1400)
+    lens = [40 + 41 * i for i in range(36)]  # 40 .. 1475: sink-only, ring-only and sealed sequences
+    _say(f"[many] build {len(lens)} sequences")
+    p = Pair(w, lens, extra_ctx=2).build(128)
+    p.check_info()
+    assert p.check_sink_ring() > 0
+    st = p.check_records()
+    _say(f"[many] records: {st}")
+    assert st["scales"] > 0 and st["boundary"] == 0
+    for layer in range(w.n_layers):
+        errs, cross = p.own_record_errors(layer, p.queries(0, layer))
+        _say(f"[many] layer={layer} decode (GPU-built cache) err={max(errs):.2e}, GPU vs oracle records {max(cross):.2e}")
+        assert max(errs) <= ATTN_TOL
+    p.import_oracle_records()
+    for path in (kvq.PATH_VALU, kvq.PATH_MFMA):
+        errs, _ = p.decode_errors(1, p.queries(1, 1), path=path)
+        _say(f"[many] path={path} decode err={max(errs):.2e}")
+        assert max(errs) <= ATTN_TOL
+    # decode steps: all sequences (three calls: some are still in the sink),
+    # then the 33 that have left it (one fused launch per 32 sequences)
+    t = p.torch
+    for step, seqs in ((7, list(range(p.n))), (8, list(range(3, p.n)))):
+        pos = [p.ora.info(s, 0)[0] for s in seqs]
+        k = np.stack([p.specs[s].tokens(0, "k", pos[i], 1)[0] for i, s in enumerate(seqs)])
+        v = np.stack([p.specs[s].tokens(0, "v", pos[i], 1)[0] for i, s in enumerate(seqs)])
+        q = inputs.queries(w.seed, step, 0, len(seqs), w.n_q_heads, w.head_dim)
+        rec0 = [p.ora.info(s, 0)[1] for s in seqs]
+        out, g = p.gpu.decode_step(0, seqs, t.from_numpy(k).cuda(), t.from_numpy(v).cuda(), t.from_numpy(q).cuda())
+        assert p.ora.append(0, seqs, k[:, None], v[:, None]) == ocache.OK
+        assert g == p.ora.seal(0, ocache.SEAL_IF_FULL)
+        for i, s in enumerate(seqs):
+            for r in range(rec0[i], p.ora.info(s, 0)[1]):
+                p.ora.import_record(s, 0, 0, r, p.gpu.export(s, 0, 0, kvq.REGION_BODY, r))
+        got = out.cpu().numpy().astype(np.float64)
+        worst = 0.0
+        for i, s in enumerate(seqs):
+            ref = p.ora.attention(0, s, q[i], 1.0)
+            worst = max(worst, float(np.max(np.abs(got[i] - ref)) / np.sqrt(np.mean(ref ** 2))))
+        _say(f"[many] decode step over {len(seqs)} sequences ({g} groups sealed): err={worst:.2e}")
+        assert worst <= ATTN_TOL
+    p.check_info()
+    assert p.check_sink_ring() > 0
+
+
 def test_decode_auto_falls_back_on_shapes_without_matrix_cores():
     """128-wide heads with 4-bit keys have no matrix-core body scan: AUTO takes
     the vector-ALU scan (parity as usual), MFMA is refused before any launch."""

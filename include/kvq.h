@@ -165,12 +165,10 @@ kvq_status kvq_decode_step(kvq_cache* cache, int32_t layer, const int32_t* seq_i
                            float scale, void* workspace, size_t ws_bytes, void* stream,
                            int32_t* groups_sealed);
 
-/* Select the kernel that scans sealed records: KVQ_PATH_AUTO (the default:
- * matrix cores where the record shape has them, the vector ALU otherwise),
- * KVQ_PATH_MFMA (matrix cores: 4-bit V with 4-bit K at head_dim 256 or 512,
- * or with 8-bit K at head_dim 128; a decode call on another shape fails with
- * KVQ_ERR_UNSUPPORTED) or KVQ_PATH_VALU (vector-ALU reference, kept for A/B
- * checks).  Errors: KVQ_ERR_INVALID. */
+/* Select the kernel that scans sealed records: KVQ_PATH_AUTO (the default)
+ * and KVQ_PATH_MFMA take the matrix cores (every shape the cache accepts:
+ * head_dim 128, 256 or 512, 4- or 8-bit K, 4-bit V), KVQ_PATH_VALU the
+ * vector-ALU reference scan (kept for A/B checks).  Errors: KVQ_ERR_INVALID. */
 kvq_status kvq_set_decode_path(kvq_cache* cache, int32_t path);
 
 /* Host-side counts of one (sequence, layer): tokens cached, sealed records,

@@ -213,11 +213,11 @@ __device__ __forceinline__ void write_partial_rows(const DecodeArgs& a, int b, i
 // Body role: one chunk of records of one KV head.
 //
 // Record shapes (compile time, BodyShape): a record is NSUB sub-records of
-// SUBW channels, each with its own C, S, Z: 256 channels at 4/4 bits; 128
-// channels with 8-bit keys and 4-bit values; a 512-wide head is two 256 x 4/4
-// sub-records, one per rotation half (SJ-KVaRN section 9).  A key row is 128
-// bytes in every shape (256 nibbles or 128 bytes).  A token's score sums the
-// sub-records' terms; each sub-record's values take their own weights p S^V.
+// SUBW channels, each with its own C, S, Z: 128 or 256 channels, or a 512-wide
+// head as two 256-channel sub-records, one per rotation half (SJ-KVaRN section
+// 9); 4- or 8-bit keys, 4-bit values.  A key row is 64, 128 or 256 bytes; each
+// lane loads 16 bytes of it per 64.  A token's score sums the sub-records'
+// terms; each sub-record's values take their own weights p S^V.
 //   q~:      wave w forms the q~ operands of its k-steps (2 of 8 per 256-channel
 //            sub-record, 1 of 4 at 128 channels) for the live rows and shares them;
 //   scores:  wave w takes token tiles 2w, 2w+1 (32 tokens) over all channels;
@@ -246,7 +246,9 @@ struct BodyShape {
   static constexpr int KPW = KK / 4;           // k-steps whose q~ one wave forms
   static constexpr int NP = KPW == 2 ? 2 : 1;  // q~ rows per lane (i and i + 8, or one)
   static constexpr int VT = SUBW / 64;         // value channel tiles per wave and sub-record
-  static constexpr int KCODE = 128 * SUBW * KB / 8, VCODE = SUBW * 64;
+  static constexpr int ROWB = SUBW * KB / 8;   // bytes per key row: 64, 128 or 256
+  static constexpr int NKS = ROWB / 64;        // 16-byte key loads per lane and token tile
+  static constexpr int KCODE = 128 * ROWB, VCODE = SUBW * 64;
   static constexpr int META = 4 * (SUBW + 256);  // K and V: C[SUBW], S[128], Z[128] fp16
   static constexpr int SUB_BYTES = KCODE + VCODE + META;
   static constexpr int KS = 2 * SUBW, KZ = KS + 256, VM = KZ + 256;  // offsets in the scales: K S, K Z, V C
@@ -257,7 +259,7 @@ struct BodyShape {
   static constexpr int QT = 0, PW = QT + NSUB * KK * 2 * 64 * 16, MB = PW + NSUB * 2 * 16 * kPPitch * 2;
   static constexpr int X = MB + 3 * NSUB * MSTRIDE;
   static constexpr int total = X + (1 + 2 * NSUB) * 256;
-  static_assert(SUBW * KB / 8 == 128 && KCODE == 16384, "key rows of 128 bytes");
+  static_assert(NKS * 64 == ROWB && (KB == 4 ? KK == 4 * NKS : KK == 2 * NKS), "a lane's key dwords cover its k-steps");
   static_assert(16 * D * 4 <= PW - QT, "query rows must fit the q~ area");
   static_assert(META <= MSTRIDE, "scales of a sub-record fit one LDS area");
   // first channel of the 8 that lane group g feeds to the score product at k-step kk
@@ -336,16 +338,19 @@ __device__ __forceinline__ void make_qtilde(const uint8_t* km, const uint4 (&qph
   }
 }
 
-// dummy: every lane reads the first 16 bytes of `sub` (one line, result unused)
-__device__ __forceinline__ void load_keys(const uint8_t* __restrict__ sub, uint4 (&kd)[2][2], int wave, int lane,
-                                          bool dummy = false) {
+// Key codes of token tiles 2 wave, 2 wave + 1: lane (m, g) loads 16 bytes at
+// 64 s + 16 g of its token's row, s < NKS.  dummy: every lane reads the first
+// 16 bytes of `sub` (one line, result unused).
+template <class Sh>
+__device__ __forceinline__ void load_keys(const uint8_t* __restrict__ sub, uint4 (&kd)[2][Sh::NKS], int wave,
+                                          int lane, bool dummy = false) {
   const int m = lane & 15, g = lane >> 4;
   const int row = (m & 8) + slot_token(m & 7);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-      kd[i][s] = *(const uint4*)(sub + (dummy ? 0 : (16 * (2 * wave + i) + row) * 128 + 64 * s + 16 * g));
+    for (int s = 0; s < Sh::NKS; ++s)
+      kd[i][s] = *(const uint4*)(sub + (dummy ? 0 : (16 * (2 * wave + i) + row) * Sh::ROWB + 64 * s + 16 * g));
 }
 template <class Sh>
 __device__ __forceinline__ void load_values(const uint8_t* __restrict__ sub, uint4 (&vd)[Sh::VT], int wave, int lane,
@@ -413,9 +418,9 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
     m0[s] = *(const uint2*)(rec(r0) + s * SB + mo);
     m1[s] = *(const uint2*)(r0 + 1 < r1 ? rec(r0 + 1) + s * SB + mo : rec0);
   }
-  uint4 kd[NSUB][2][2], vd[NSUB][VT];
+  uint4 kd[NSUB][2][Sh::NKS], vd[NSUB][VT];
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) load_keys(rec(r0) + s * SB, kd[s], wave, lane);
+  for (int s = 0; s < NSUB; ++s) load_keys<Sh>(rec(r0) + s * SB, kd[s], wave, lane);
   float* rows = (float*)qt;
   query_rows<D>(a, qraw, true, rows, wave, lane);
   __syncthreads();
@@ -548,7 +553,7 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
     // counting conservative): past the last record they re-read one 16-byte
     // line of record r0 and are not used
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) load_keys(more ? rec(r + 1) + s * SB : rec0, kd[s], wave, lane, !more);
+    for (int s = 0; s < NSUB; ++s) load_keys<Sh>(more ? rec(r + 1) + s * SB : rec0, kd[s], wave, lane, !more);
 
     const float mrec = fmaxf(fmaxf(xm[0][q16], xm[1][q16]), fmaxf(xm[2][q16], xm[3][q16]));
     const float m_new = fmaxf(m_run, mrec);
@@ -1112,9 +1117,14 @@ __device__ __forceinline__ void decode_main(const DecodeArgs& a, uint8_t* smem) 
 KVQ_MAIN_KERNEL(decode_main_kernel, 256, 4, 2)
 KVQ_MAIN_KERNEL(decode_main_kernel_d128k8, 128, 8, 2)
 KVQ_MAIN_KERNEL(decode_main_kernel_d512, 512, 4, 1)
+KVQ_MAIN_KERNEL(decode_main_kernel_d128k4, 128, 4, 2)
+KVQ_MAIN_KERNEL(decode_main_kernel_d256k8, 256, 8, 2)
+KVQ_MAIN_KERNEL(decode_main_kernel_d512k8, 512, 8, 1)
 #undef KVQ_MAIN_KERNEL
-static_assert(BodyShape<512, 4>::WG_PER_CU == 1 && BodyShape<256, 4>::WG_PER_CU == 2 &&
-                  BodyShape<128, 8>::WG_PER_CU == 2, "launch bounds match the body shapes");
+static_assert(BodyShape<512, 4>::WG_PER_CU == 1 && BodyShape<512, 8>::WG_PER_CU == 1 &&
+                  BodyShape<256, 4>::WG_PER_CU == 2 && BodyShape<256, 8>::WG_PER_CU == 2 &&
+                  BodyShape<128, 4>::WG_PER_CU == 2 && BodyShape<128, 8>::WG_PER_CU == 2,
+              "launch bounds match the body shapes");
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_ring_kernel(DecodeArgs a) {
@@ -1123,17 +1133,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (find_item(a, blockIdx.x, false, b, h, c)) ring_role<D>(a, b, h, c, smem);
 }
 
-// Append (optional), body and sink/ring items in one launch: head_dim 256
-// with 4-bit keys and values, 512 (two 256-channel sub-records) with 4/4,
-// 128 with 8-bit keys and 4-bit values.
+// Append (optional), body and sink/ring items in one launch: head_dim 128,
+// 256 or 512 (two 256-channel sub-records), 4- or 8-bit keys, 4-bit values.
 hipError_t launch_decode_main(const DecodeArgs& a, int n_items, hipStream_t stream) {
   if (a.y.vbits != 4 || a.ring_chunk % kStep != 0 || a.g > kMaxGroup) return hipErrorInvalidValue;
+  const dim3 grid(n_items), block(256);
   if (a.y.D == 256 && a.y.kbits == 4)
-    hipLaunchKernelGGL(decode_main_kernel, dim3(n_items), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(decode_main_kernel, grid, block, 0, stream, a);
   else if (a.y.D == 512 && a.y.kbits == 4)
-    hipLaunchKernelGGL(decode_main_kernel_d512, dim3(n_items), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(decode_main_kernel_d512, grid, block, 0, stream, a);
   else if (a.y.D == 128 && a.y.kbits == 8)
-    hipLaunchKernelGGL(decode_main_kernel_d128k8, dim3(n_items), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(decode_main_kernel_d128k8, grid, block, 0, stream, a);
+  else if (a.y.D == 128 && a.y.kbits == 4)
+    hipLaunchKernelGGL(decode_main_kernel_d128k4, grid, block, 0, stream, a);
+  else if (a.y.D == 256 && a.y.kbits == 8)
+    hipLaunchKernelGGL(decode_main_kernel_d256k8, grid, block, 0, stream, a);
+  else if (a.y.D == 512 && a.y.kbits == 8)
+    hipLaunchKernelGGL(decode_main_kernel_d512k8, grid, block, 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

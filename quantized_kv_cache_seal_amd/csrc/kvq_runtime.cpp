@@ -131,10 +131,10 @@ static int device_cu_count() {
     return 256;
   return n;
 }
-// matrix-core body scan (fused with the sink and ring): head_dim 256 or 512
-// with 4-bit K and V, head_dim 128 with 8-bit K and 4-bit V
+// matrix-core body scan (fused with the sink and ring): every shape the cache
+// accepts (head_dim 128, 256 or 512; 4- or 8-bit K; 4-bit V)
 static bool mfma_supported(const Layout& y) {
-  return y.vbits == 4 && (((y.D == 256 || y.D == 512) && y.kbits == 4) || (y.D == 128 && y.kbits == 8));
+  return y.vbits == 4 && (y.kbits == 4 || y.kbits == 8) && (y.D == 128 || y.D == 256 || y.D == 512);
 }
 // matrix-core sink and ring scan on its own: head_dim 128 or 256
 static bool staged_supported(const Layout& y) { return y.D == 128 || y.D == 256; }
@@ -415,8 +415,7 @@ static kvq_status decode_impl(kvq_cache* c, int32_t layer, const int32_t* seq_id
   const bool use_mfma = c->path != KVQ_PATH_VALU && mfma_supported(c->y);
   const bool staged = c->path != KVQ_PATH_VALU && staged_supported(c->y);
   if (c->path == KVQ_PATH_MFMA && !use_mfma)
-    return fail(KVQ_ERR_UNSUPPORTED, "matrix-core body scan needs 4-bit V with 4-bit K at head_dim 256 or 512, "
-                                     "or 8-bit K at head_dim 128");
+    return fail(KVQ_ERR_UNSUPPORTED, "matrix-core body scan needs 4-bit V and 4- or 8-bit K");
   std::vector<int64_t> n_rec(n_seqs), ring(n_seqs);
   for (int i = 0; i < n_seqs; ++i) {
     if (c->tok(seq_ids[i], layer) < 1) return fail(KVQ_ERR_INVALID, "sequence %d holds no tokens", seq_ids[i]);

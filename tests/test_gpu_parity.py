@@ -167,20 +167,48 @@ def test_many_sequences_split_launches():
     assert p.check_sink_ring() > 0
 
 
-def test_decode_auto_falls_back_on_shapes_without_matrix_cores():
-    """128-wide heads with 4-bit keys have no matrix-core body scan: AUTO takes
-    the vector-ALU scan (parity as usual), MFMA is refused before any launch."""
-    w = configs.QWEN14B1M.scaled(n_layers=1, n_kv_heads=2, n_q_heads=10, tail_min=256, tail_max=512, ctx=900,
-                                 k_bits=4)
-    p = Pair(w, [900], inputs.rotation_signs(w.seed)).build(300)
-    p.import_oracle_records()
-    q = p.queries(0, 0)
-    errs, _ = p.decode_errors(0, q, path=kvq.PATH_AUTO)
-    _say(f"[d128k4] AUTO decode err={max(errs):.2e}")
+@pytest.mark.parametrize("shape", ["d128k4", "d256k8", "d512k8"])
+def test_other_body_shapes(shape):
+    """The record shapes no configuration uses (128-wide heads with 4-bit keys,
+    8-bit keys at 256 and 512): records against the oracle, the matrix-core and
+    vector-ALU decodes against float64 attention, and fused decode steps."""
+    base = {"d128k4": configs.QWEN14B1M.scaled(n_layers=1, n_kv_heads=2, n_q_heads=10, k_bits=4),
+            "d256k8": configs.QWEN27B.scaled(n_layers=1, n_kv_heads=2, n_q_heads=12, k_bits=8),
+            "d512k8": configs.GEMMA31B.scaled(n_layers=1, k_bits=8)}[shape]
+    w = base.scaled(tail_min=256, tail_max=512, ctx=1300)
+    signs = inputs.rotation_signs(w.seed) if w.head_dim == 128 else None
+    _say(f"[{shape}] build")
+    p = Pair(w, [1300, 700], signs, extra_ctx=3).build(300)
+    p.check_info()
+    assert p.check_sink_ring() > 0
+    st = p.check_records()
+    _say(f"[{shape}] records: {st}")
+    assert st["scales"] > 0 and st["boundary"] <= max(1, st["codes"] // 10 ** 5)
+    errs, cross = p.own_record_errors(0, p.queries(0, 0))
+    _say(f"[{shape}] decode (GPU-built cache) err={max(errs):.2e}, GPU vs oracle records {max(cross):.2e}")
     assert max(errs) <= ATTN_TOL
-    with pytest.raises(kvq.KVQError) as e:
-        p.decode_errors(0, q, path=kvq.PATH_MFMA)
-    assert e.value.status == kvq.ERR_UNSUPPORTED
+    p.import_oracle_records()
+    for path in (kvq.PATH_VALU, kvq.PATH_MFMA):
+        errs, _ = p.decode_errors(0, p.queries(1, 0), path=path)
+        _say(f"[{shape}] path={path} decode err={max(errs):.2e}")
+        assert max(errs) <= ATTN_TOL
+    p.gpu.set_decode_path(kvq.PATH_AUTO)
+    t = p.torch
+    seqs = [0, 1]
+    for step in range(3):
+        pos = [p.ora.info(s, 0)[0] for s in seqs]
+        k = np.stack([p.specs[s].tokens(0, "k", pos[s], 1)[0] for s in seqs])
+        v = np.stack([p.specs[s].tokens(0, "v", pos[s], 1)[0] for s in seqs])
+        q = inputs.queries(w.seed, 50 + step, 0, 2, w.n_q_heads, w.head_dim)
+        out, g = p.gpu.decode_step(0, seqs, t.from_numpy(k).cuda(), t.from_numpy(v).cuda(), t.from_numpy(q).cuda())
+        assert p.ora.append(0, seqs, k[:, None], v[:, None]) == ocache.OK
+        assert g == 0 == p.ora.seal(0, ocache.SEAL_IF_FULL)
+        got = out.cpu().numpy().astype(np.float64)
+        for s in seqs:
+            ref = p.ora.attention(0, s, q[s], 1.0)
+            err = float(np.max(np.abs(got[s] - ref)) / np.sqrt(np.mean(ref ** 2)))
+            assert err <= ATTN_TOL, (shape, step, s, err)
+    assert p.check_sink_ring() > 0
 
 
 @pytest.mark.parametrize("name", ["qwen27b", "batched", "gemma", "qwen14b"])

@@ -331,9 +331,15 @@ __device__ __forceinline__ void make_qtilde(const uint8_t* km, const uint4 (&qph
     qt[kk][0][16 * g + row] = hi;
     qt[kk][1][16 * g + row] = lo;
     float part = Sh::KB == 4 ? fmaf(16.0f, a16, a1) : a1 + a16;
-    part += __shfl_xor(part, 8, 64);
-    part += __shfl_xor(part, 16, 64);
-    if (Sh::KPW == 2) part += __shfl_xor(part, 32, 64);
+    part = add_x8(part);  // over g: lanes l ^ 8, l ^ 16 (and over the two k-steps: l ^ 32)
+    {
+      const auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(part), __float_as_int(part), false, false);
+      part = __int_as_float(b[0]) + __int_as_float(b[1]);
+    }
+    if (Sh::KPW == 2) {
+      const auto c = __builtin_amdgcn_permlane32_swap(__float_as_int(part), __float_as_int(part), false, false);
+      part = __int_as_float(c[0]) + __int_as_float(c[1]);
+    }
     if (Sh::KPW == 2 ? (lane >> 3) == 0 : ((lane >> 3) & 3) == 0) xs[wave][row] = part;
   }
 }

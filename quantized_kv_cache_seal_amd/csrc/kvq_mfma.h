@@ -48,15 +48,24 @@ __device__ __forceinline__ uint32_t as_u32(half2v h) {
   return u;
 }
 
-__device__ __forceinline__ float xsum4(float x) {  // sum over the four lane groups of a wave
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
+// Over the four lane groups of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48), with
+// the 32- and 16-lane swaps of this target (each returns the lane's own value
+// and its partner's, in some order): no trip through LDS.
+__device__ __forceinline__ float xsum4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = __int_as_float(a[0]) + __int_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(b[0]) + __int_as_float(b[1]);
 }
 __device__ __forceinline__ float xmax4(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  x = fmaxf(x, __shfl_xor(x, 32, 64));
-  return x;
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = fmaxf(__int_as_float(a[0]), __int_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(b[0]), __int_as_float(b[1]));
+}
+// x + the value of lane l ^ 8 (within the 16-lane row: DPP row_ror:8)
+__device__ __forceinline__ float add_x8(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
 }
 
 // Eight 6-bit codes held as 48 bits (lo, low 16 bits of hi), as fp16 u - 32.

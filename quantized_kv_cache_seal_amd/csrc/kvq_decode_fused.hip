@@ -290,7 +290,10 @@ __device__ __forceinline__ half8 byte8_sub(uint32_t w0, uint32_t w1) {
 // the matrix core; at 128 channels (one k-step per wave) the lane's row is
 // i + 8 (lane >> 5).  Rows never written stay zero.  Also this wave's part of
 // sigma = sum q~ per row.
-template <class Sh>
+// Packed (PK, at most 8 heads): one operand per k-step, hi in columns 0..7
+// and lo in columns 8..15; at 128 channels lanes 32..63 form the lo halves of
+// the same rows as lanes 0..31.
+template <class Sh, bool PK>
 __device__ __forceinline__ void make_qtilde(const uint8_t* km, const uint4 (&qph)[Sh::NP], const uint4 (&qpl)[Sh::NP],
                                             uint4 (*qt)[2][64], float (*xs)[16], int G, int wave, int lane) {
   const int i = lane & 7, g = (lane >> 3) & 3, h5 = lane >> 5;
@@ -309,11 +312,11 @@ __device__ __forceinline__ void make_qtilde(const uint8_t* km, const uint4 (&qph
     cp[2] = c.z;
     cp[3] = c.w;
   }
-  const int np = Sh::NP == 2 && G > 8 ? 2 : 1;
+  const int np = !PK && Sh::NP == 2 && G > 8 ? 2 : 1;
 #pragma unroll
   for (int p = 0; p < Sh::NP; ++p) {
     if (p >= np) break;
-    const int row = Sh::KPW == 2 ? i + 8 * p : i + 8 * h5;
+    const int row = PK ? i : Sh::KPW == 2 ? i + 8 * p : i + 8 * h5;
     uint4 hi, lo;
     qtilde_pair(qph[p].x, qpl[p].x, cp[0], hi.x, lo.x);
     qtilde_pair(qph[p].y, qpl[p].y, cp[1], hi.y, lo.y);
@@ -328,8 +331,15 @@ __device__ __forceinline__ void make_qtilde(const uint8_t* km, const uint4 (&qph
     a1 = __builtin_amdgcn_fdot2(as_h2(lo.z), ones, a1, false);
     a16 = __builtin_amdgcn_fdot2(as_h2(hi.w), ones, a16, false);
     a16 = __builtin_amdgcn_fdot2(as_h2(lo.w), ones, a16, false);
-    qt[kk][0][16 * g + row] = hi;
-    qt[kk][1][16 * g + row] = lo;
+    if (!PK) {
+      qt[kk][0][16 * g + row] = hi;
+      qt[kk][1][16 * g + row] = lo;
+    } else if (Sh::KPW == 2) {
+      qt[kk][0][16 * g + row] = hi;
+      qt[kk][0][16 * g + 8 + row] = lo;
+    } else {
+      qt[kk][0][16 * g + 8 * h5 + row] = h5 ? lo : hi;
+    }
     float part = Sh::KB == 4 ? fmaf(16.0f, a16, a1) : a1 + a16;
     part = add_x8(part);  // over g: lanes l ^ 8, l ^ 16 (and over the two k-steps: l ^ 32)
     {
@@ -340,7 +350,8 @@ __device__ __forceinline__ void make_qtilde(const uint8_t* km, const uint4 (&qph
       const auto c = __builtin_amdgcn_permlane32_swap(__float_as_int(part), __float_as_int(part), false, false);
       part = __int_as_float(c[0]) + __int_as_float(c[1]);
     }
-    if (Sh::KPW == 2 ? (lane >> 3) == 0 : ((lane >> 3) & 3) == 0) xs[wave][row] = part;
+    // packed at 128 channels: lanes 32..63 repeat the rows of lanes 0..31
+    if (Sh::KPW == 2 || PK ? (lane >> 3) == 0 : ((lane >> 3) & 3) == 0) xs[wave][row] = part;
   }
 }
 
@@ -367,7 +378,7 @@ __device__ __forceinline__ void load_values(const uint8_t* __restrict__ sub, uin
     vd[j] = *(const uint4*)(sub + (dummy ? 0 : Sh::KCODE + (16 * (Sh::VT * wave + j) + m) * 64 + 16 * g));
 }
 
-template <class Sh>
+template <class Sh, bool PK>
 __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int cbk, uint8_t* smem) {
   constexpr int D = Sh::D, SUBW = Sh::SUBW, NSUB = Sh::NSUB, KK = Sh::KK, VT = Sh::VT, NP = Sh::NP;
   constexpr int SB = Sh::SUB_BYTES, MS = Sh::MSTRIDE;
@@ -438,7 +449,7 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
     for (int s = 0; s < NSUB; ++s)
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const int row_i = Sh::KPW == 2 ? ui + 8 * p : ui + 8 * h5;
+        const int row_i = PK ? ui : Sh::KPW == 2 ? ui + 8 * p : ui + 8 * h5;
         const float* row = rows + row_i * D + SUBW * s + base;  // rows past the group are zero
         uint32_t hb[4], lb[4];
 #pragma unroll
@@ -465,7 +476,7 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
   }
   __syncthreads();
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) make_qtilde<Sh>(mslot(r0) + s * MS, qph[s], qpl[s], qt[s], xs[s], G, wave, lane);
+  for (int s = 0; s < NSUB; ++s) make_qtilde<Sh, PK>(mslot(r0) + s * MS, qph[s], qpl[s], qt[s], xs[s], G, wave, lane);
   // the first record's value codes only now: at the start of the launch every
   // workgroup asks for its first record at once, and keys requested ahead of
   // values arrive ahead of them, so the first scores start sooner
@@ -488,7 +499,8 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
     const bool more = r + 1 < r1;
 
     // ---- scores of tiles 2 wave, 2 wave + 1: independent accumulation chains
-    // (sub-record x tile x hi/lo) keep the matrix core busy between dependent products
+    // (sub-record x tile x hi/lo) keep the matrix core busy between dependent
+    // products; packed, one chain per sub-record and tile carries both halves
     constexpr int NK = NSUB * KK;
     float4v sh[NSUB][2], sl[NSUB][2];
 #pragma unroll
@@ -500,16 +512,16 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       qb[k][0] = mfma_a(qt[k / KK][k % KK][0][lane]);
-      qb[k][1] = mfma_a(qt[k / KK][k % KK][1][lane]);
+      if (!PK) qb[k][1] = mfma_a(qt[k / KK][k % KK][1][lane]);
     }
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
       const int s = k / KK, kk = k % KK;
       if (k + 2 < NK) {
         qb[k + 2][0] = mfma_a(qt[(k + 2) / KK][(k + 2) % KK][0][lane]);
-        qb[k + 2][1] = mfma_a(qt[(k + 2) / KK][(k + 2) % KK][1][lane]);
+        if (!PK) qb[k + 2][1] = mfma_a(qt[(k + 2) / KK][(k + 2) % KK][1][lane]);
       }
-      const half8 bh = qb[k][0], bl = qb[k][1];
+      const half8 bh = qb[k][0], bl = PK ? bh : qb[k][1];
       half8 av[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -520,8 +532,20 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) sh[s][i] = mfma16(av[i], bh, sh[s][i]);
+      if (!PK) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) sl[s][i] = mfma16(av[i], bl, sl[s][i]);
+        for (int i = 0; i < 2; ++i) sl[s][i] = mfma16(av[i], bl, sl[s][i]);
+      }
+    }
+    // packed: column c + 8 holds the lo half of column c; lanes l and l ^ 8
+    // (columns c, c + 8 of the same rows) both get the sum, bit for bit
+    if (PK) {
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sh[s][i][j] = add_x8(sh[s][i][j]);
     }
     // this lane's rows are positions 16 bb + 4 g + j: tokens base + {0,4,1,5}
     // (g even) or base + {2,6,3,7} (g odd), base = 16 bb + 8 (g / 2)
@@ -530,7 +554,8 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       const uint8_t* km = mr + s * MS;
-      const float sig = xs[s][0][q16] + xs[s][1][q16] + xs[s][2][q16] + xs[s][3][q16];
+      const int qr = PK ? q16 & 7 : q16;  // packed: columns c and c + 8 score query row c
+      const float sig = xs[s][0][qr] + xs[s][1][qr] + xs[s][2][qr] + xs[s][3][qr];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int T = 16 * (2 * wave + i) + tb;
@@ -539,7 +564,7 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
         const half2v S0 = as_h2(s01), S1 = as_h2(s45), Z0 = as_h2(z01), Z1 = as_h2(z45);
         const float Sj[4] = {(float)S0[0], (float)S1[0], (float)S0[1], (float)S1[1]};
         const float Zj[4] = {(float)Z0[0], (float)Z1[0], (float)Z0[1], (float)Z1[1]};
-        const float4v dot = sh[s][i] + sl[s][i];
+        const float4v dot = PK ? sh[s][i] : sh[s][i] + sl[s][i];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float v = fmaf(Sj[j] * kSub24, dot[j], Zj[j] * sig);
@@ -604,8 +629,12 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
         uint2 hi, lo;
         split_h2(x[0], x[1], hi.x, lo.x);
         split_h2(x[2], x[3], hi.y, lo.y);
-        *(uint2*)&pw[s][0][q16][16 * (2 * wave + i) + 4 * g] = hi;
-        *(uint2*)&pw[s][1][q16][16 * (2 * wave + i) + 4 * g] = lo;
+        if (PK) {  // columns 0..7 take hi, 8..15 lo of the same query rows
+          *(uint2*)&pw[s][0][q16][16 * (2 * wave + i) + 4 * g] = q16 < 8 ? hi : lo;
+        } else {
+          *(uint2*)&pw[s][0][q16][16 * (2 * wave + i) + 4 * g] = hi;
+          *(uint2*)&pw[s][1][q16][16 * (2 * wave + i) + 4 * g] = lo;
+        }
       }
       zt = xsum4(zt);
       if (g == 0) xz[s][wave][q16] = zt;
@@ -613,7 +642,7 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
     if (more) {
 #pragma unroll
       for (int s = 0; s < NSUB; ++s)
-        make_qtilde<Sh>(mslot(r + 1) + s * MS, qph[s], qpl[s], qt[s], xs[s], G, wave, lane);
+        make_qtilde<Sh, PK>(mslot(r + 1) + s * MS, qph[s], qpl[s], qt[s], xs[s], G, wave, lane);
     }
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
@@ -625,11 +654,11 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       const float corr = xz[s][0][q16] + xz[s][1][q16] + xz[s][2][q16] + xz[s][3][q16];
-      half8 pbh[4], pbl[4];
+      half8 pbh[4], pbl[4] = {};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         pbh[t] = mfma_a(*(const uint4*)&pw[s][0][q16][32 * g + 8 * t]);
-        pbl[t] = mfma_a(*(const uint4*)&pw[s][1][q16][32 * g + 8 * t]);
+        if (!PK) pbl[t] = mfma_a(*(const uint4*)&pw[s][1][q16][32 * g + 8 * t]);
       }
       float4v o[VT];
 #pragma unroll
@@ -641,8 +670,16 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
         for (int j = 0; j < VT; ++j) av[j] = nib8_centred(pick(vd[s][j], t));
 #pragma unroll
         for (int j = 0; j < VT; ++j) o[j] = mfma16(av[j], pbh[t], o[j]);
+        if (!PK) {
 #pragma unroll
-        for (int j = 0; j < VT; ++j) o[j] = mfma16(av[j], pbl[t], o[j]);
+          for (int j = 0; j < VT; ++j) o[j] = mfma16(av[j], pbl[t], o[j]);
+        }
+      }
+      if (PK) {
+#pragma unroll
+        for (int j = 0; j < VT; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[j][e] = add_x8(o[j][e]);
       }
       load_values<Sh>(more ? rec(r + 1) + s * SB : rec0, vd[s], wave, lane, !more);
       const uint8_t* vm = mr + s * MS + Sh::VM;
@@ -1106,7 +1143,12 @@ __device__ __forceinline__ void decode_main(const DecodeArgs& a, uint8_t* smem) 
   }
   item -= a.n_app_items;
   if (item < a.n_body_items) {
-    if (find_item(a, item, true, b, h, c)) body_role<BodyShape<D, KB>>(a, b, h, c, smem);
+    if (find_item(a, item, true, b, h, c)) {
+      if (a.g <= 8)
+        body_role<BodyShape<D, KB>, true>(a, b, h, c, smem);
+      else
+        body_role<BodyShape<D, KB>, false>(a, b, h, c, smem);
+    }
   } else {
     if (find_item(a, item - a.n_body_items, false, b, h, c)) ring_role<D>(a, b, h, c, smem);
   }

@@ -211,6 +211,44 @@ def test_other_body_shapes(shape):
     assert p.check_sink_ring() > 0
 
 
+@pytest.mark.parametrize("shape,group", [("d256k4", 16), ("d128k8", 12), ("d512k4", 9)])
+def test_groups_over_eight(shape, group):
+    """Groups of more than 8 query heads per KV head (no configuration has
+    one): the matrix-core body then carries hi and lo in separate products,
+    and q~ rows i + 8.  Both decode paths against float64 attention over the
+    oracle's records, and fused decode steps."""
+    base = {"d256k4": configs.QWEN27B.scaled(n_layers=1, n_kv_heads=1),
+            "d128k8": configs.QWEN14B1M.scaled(n_layers=1, n_kv_heads=2),
+            "d512k4": configs.GEMMA31B.scaled(n_layers=1, n_kv_heads=2)}[shape]
+    w = base.scaled(n_q_heads=group * base.n_kv_heads, tail_min=256, tail_max=512, ctx=1300)
+    signs = inputs.rotation_signs(w.seed) if w.head_dim == 128 else None
+    _say(f"[{shape} g{group}] build")
+    p = Pair(w, [1300, 900], signs, extra_ctx=3).build(300)
+    p.check_info()
+    p.import_oracle_records()
+    for path in (kvq.PATH_VALU, kvq.PATH_MFMA):
+        errs, _ = p.decode_errors(0, p.queries(1, 0), path=path)
+        _say(f"[{shape} g{group}] path={path} decode err={max(errs):.2e}")
+        assert max(errs) <= ATTN_TOL
+    p.gpu.set_decode_path(kvq.PATH_AUTO)
+    t = p.torch
+    seqs = [0, 1]
+    for step in range(2):
+        pos = [p.ora.info(s, 0)[0] for s in seqs]
+        k = np.stack([p.specs[s].tokens(0, "k", pos[s], 1)[0] for s in seqs])
+        v = np.stack([p.specs[s].tokens(0, "v", pos[s], 1)[0] for s in seqs])
+        q = inputs.queries(w.seed, 70 + step, 0, 2, w.n_q_heads, w.head_dim)
+        out, g = p.gpu.decode_step(0, seqs, t.from_numpy(k).cuda(), t.from_numpy(v).cuda(), t.from_numpy(q).cuda())
+        assert p.ora.append(0, seqs, k[:, None], v[:, None]) == ocache.OK
+        assert g == 0 == p.ora.seal(0, ocache.SEAL_IF_FULL)
+        got = out.cpu().numpy().astype(np.float64)
+        for s in seqs:
+            ref = p.ora.attention(0, s, q[s], 1.0)
+            err = float(np.max(np.abs(got[s] - ref)) / np.sqrt(np.mean(ref ** 2)))
+            assert err <= ATTN_TOL, (shape, group, step, s, err)
+    assert p.check_sink_ring() > 0
+
+
 @pytest.mark.parametrize("name", ["qwen27b", "batched", "gemma", "qwen14b"])
 def test_decode_step(name):
     """kvq_decode_step (append one token, seal if full, decode) step after step:

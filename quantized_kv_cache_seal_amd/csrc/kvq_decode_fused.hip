@@ -56,12 +56,13 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t b) {
 // of a byte stays in place, i.e. 1024 + 16 n; its 1/16 is folded into the
 // other operand) and one packed subtract leaves n - 8 (or 16 (n - 8)).
 // Slots: [n0, n4, 16 n1, 16 n5, n2, n6, 16 n3, 16 n7] - centre.
-// The value product needs the centre: its weights p S enter as fp16 hi + lo,
-// and with codes in [0, 15] their rounding error is summed with one sign
-// against the zero-point sum, which is formed from the exact weights; the
-// product carries 7.5 sum(p S), hundreds of times the weighted average when
-// attention is diffuse, and that error swamps the result (measured).  The
-// centre moves into the zero point instead: x = C (S (n - 8) + (Z + 8 S)).
+// The value product needs the centre in the codes.  Uncentred, its sums run
+// with one sign to ~8 sum(p S) per record, and the matrix cores' accumulation
+// loses bits in proportion to them: 1e-3 to 3e-3 of the output at head width
+// 256 and 512 (measured twice: with the centre taken from the exact weights,
+// and from the rounded hi + lo weights by a product with a constant operand),
+// against ~5e-5 centred.  The centre moves into the zero point instead:
+// x = C (S (n - 8) + (Z + 8 S)).
 __device__ __forceinline__ half8 nib8_centred(uint32_t w) {
   const uint32_t w8 = w >> 8;
   const uint32_t lo_m = 0x000F000Fu, hi_m = 0x00F000F0u, e = 0x64006400u;
@@ -81,8 +82,8 @@ __device__ __forceinline__ half8 nib8_centred(uint32_t w) {
 // multiply fp16 subnormals exactly (checked for subnormal x subnormal too);
 // the 2^24 is restored on the fp32 results.  The score needs no centre: its
 // zero-point term Z sigma is formed from the same rounded q~ operands as the
-// product, so their rounding enters both alike, and the fp32 accumulation of
-// the uncentred product is ~10^-6 relative.
+// product, so their rounding enters both alike, and q~ takes both signs, so
+// the uncentred sums do not run away (~1e-6 relative).
 constexpr float kSub24 = 16777216.0f;  // 2^24
 __device__ __forceinline__ half8 nib8_sub(uint32_t w) {
   const uint32_t w8 = w >> 8;
@@ -251,9 +252,13 @@ struct BodyShape {
   static constexpr int KCODE = 128 * ROWB, VCODE = SUBW * 64;
   static constexpr int META = 4 * (SUBW + 256);  // K and V: C[SUBW], S[128], Z[128] fp16
   static constexpr int SUB_BYTES = KCODE + VCODE + META;
-  static constexpr int KS = 2 * SUBW, KZ = KS + 256, VM = KZ + 256;  // offsets in the scales: K S, K Z, V C
   static constexpr int WG_PER_CU = NSUB == 2 ? 1 : 2;  // resident workgroups per compute unit
-  static constexpr int MSTRIDE = 2048;                 // LDS bytes per sub-record's scales
+  // A sub-record's scales in LDS (stage_scales): the key C stays fp16 (the q~
+  // products take it as is); the rest is widened to fp32 once, at staging:
+  // K S times 2^24 [128], K Z [128], V C [SUBW], V S [128], V Z [128].
+  static constexpr int L_KS = 2 * SUBW, L_KZ = L_KS + 512, L_VC = L_KZ + 512, L_VS = L_VC + 4 * SUBW;
+  static constexpr int L_VZ = L_VS + 512;
+  static constexpr int MSTRIDE = 4096;  // LDS bytes per sub-record's scales
   // LDS: q~ operands [NSUB][KK][hi, lo][64 lanes]; weights [NSUB][hi, lo][16][kPPitch];
   // scales [3][NSUB][MSTRIDE]; exchange xm[4][16], xz[NSUB][4][16], xs[NSUB][4][16]
   static constexpr int QT = 0, PW = QT + NSUB * KK * 2 * 64 * 16, MB = PW + NSUB * 2 * 16 * kPPitch * 2;
@@ -261,7 +266,8 @@ struct BodyShape {
   static constexpr int total = X + (1 + 2 * NSUB) * 256;
   static_assert(NKS * 64 == ROWB && (KB == 4 ? KK == 4 * NKS : KK == 2 * NKS), "a lane's key dwords cover its k-steps");
   static_assert(16 * D * 4 <= PW - QT, "query rows must fit the q~ area");
-  static_assert(META <= MSTRIDE, "scales of a sub-record fit one LDS area");
+  static_assert(L_VZ + 512 <= MSTRIDE && 2 * SUBW + 2 * (8 * 256 - 2 * SUBW) <= MSTRIDE,
+                "scales of a sub-record (and the stores of threads past them) fit one LDS area");
   // first channel of the 8 that lane group g feeds to the score product at k-step kk
   static __device__ __forceinline__ int kbase(int kk, int g) {
     return KB == 4 ? 128 * (kk >> 2) + 32 * g + 8 * (kk & 3) : 64 * (kk >> 1) + 16 * g + 8 * (kk & 1);
@@ -281,6 +287,22 @@ __device__ __forceinline__ half8 byte8_sub(uint32_t w0, uint32_t w1) {
   u.z = __builtin_amdgcn_perm(0u, w1, 0x0C010C00u);
   u.w = __builtin_amdgcn_perm(0u, w1, 0x0C030C02u);
   return mfma_a(u);
+}
+
+// Thread tid's 8 bytes of a sub-record's scales (bytes 8 tid.. of the record's
+// scale block) into the LDS layout of BodyShape: key C copied, the rest as
+// fp32 at twice the offset past it (key S times 2^24).
+template <class Sh>
+__device__ __forceinline__ void stage_scales(uint8_t* dst, uint2 m, int tid) {
+  const int o = 8 * tid;
+  if (o < 2 * Sh::SUBW) {
+    *(uint2*)(dst + o) = m;
+    return;
+  }
+  const half2v a = as_h2(m.x), b = as_h2(m.y);
+  const float f = o < 2 * Sh::SUBW + 256 ? kSub24 : 1.0f;
+  *(float4*)(dst + 2 * o - 2 * Sh::SUBW) =
+      make_float4(f * (float)a[0], f * (float)a[1], f * (float)b[0], f * (float)b[1]);
 }
 
 // q~ operands (hi, lo) of this wave's k-steps of one sub-record from its key
@@ -471,8 +493,8 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
   if (tid < 64 * NSUB) (&xs[0][0][0])[tid] = 0.0f;
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
-    *(uint2*)(mslot(r0) + s * MS + 8 * tid) = m0[s];
-    if (r0 + 1 < r1) *(uint2*)(mslot(r0 + 1) + s * MS + 8 * tid) = m1[s];
+    stage_scales<Sh>(mslot(r0) + s * MS, m0[s], tid);
+    if (r0 + 1 < r1) stage_scales<Sh>(mslot(r0 + 1) + s * MS, m1[s], tid);
   }
   __syncthreads();
 #pragma unroll
@@ -559,15 +581,14 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int T = 16 * (2 * wave + i) + tb;
-        const uint32_t s01 = *(const uint32_t*)(km + Sh::KS + 2 * T), s45 = *(const uint32_t*)(km + Sh::KS + 2 * T + 8);
-        const uint32_t z01 = *(const uint32_t*)(km + Sh::KZ + 2 * T), z45 = *(const uint32_t*)(km + Sh::KZ + 2 * T + 8);
-        const half2v S0 = as_h2(s01), S1 = as_h2(s45), Z0 = as_h2(z01), Z1 = as_h2(z45);
-        const float Sj[4] = {(float)S0[0], (float)S1[0], (float)S0[1], (float)S1[1]};
-        const float Zj[4] = {(float)Z0[0], (float)Z1[0], (float)Z0[1], (float)Z1[1]};
+        const float2 s01 = *(const float2*)(km + Sh::L_KS + 4 * T), s45 = *(const float2*)(km + Sh::L_KS + 4 * T + 16);
+        const float2 z01 = *(const float2*)(km + Sh::L_KZ + 4 * T), z45 = *(const float2*)(km + Sh::L_KZ + 4 * T + 16);
+        const float Sj[4] = {s01.x, s45.x, s01.y, s45.y};  // S 2^24
+        const float Zj[4] = {z01.x, z45.x, z01.y, z45.y};
         const float4v dot = PK ? sh[s][i] : sh[s][i] + sl[s][i];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float v = fmaf(Sj[j] * kSub24, dot[j], Zj[j] * sig);
+          const float v = fmaf(Sj[j], dot[j], Zj[j] * sig);
           sc[i][j] = s == 0 ? v : sc[i][j] + v;
         }
       }
@@ -607,17 +628,15 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
       }
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
-      const uint8_t* vm = mr + s * MS + Sh::VM;
+      const uint8_t* vm = mr + s * MS;
       float zt = 0.0f;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int T = 16 * (2 * wave + i) + tb;
-        const uint32_t s01 = *(const uint32_t*)(vm + 2 * SUBW + 2 * T), s45 = *(const uint32_t*)(vm + 2 * SUBW + 2 * T + 8);
-        const uint32_t z01 = *(const uint32_t*)(vm + 2 * SUBW + 256 + 2 * T),
-                       z45 = *(const uint32_t*)(vm + 2 * SUBW + 256 + 2 * T + 8);
-        const half2v S0 = as_h2(s01), S1 = as_h2(s45), Z0 = as_h2(z01), Z1 = as_h2(z45);
-        const float Sj[4] = {(float)S0[0], (float)S1[0], (float)S0[1], (float)S1[1]};
-        const float Zj[4] = {(float)Z0[0], (float)Z1[0], (float)Z0[1], (float)Z1[1]};
+        const float2 s01 = *(const float2*)(vm + Sh::L_VS + 4 * T), s45 = *(const float2*)(vm + Sh::L_VS + 4 * T + 16);
+        const float2 z01 = *(const float2*)(vm + Sh::L_VZ + 4 * T), z45 = *(const float2*)(vm + Sh::L_VZ + 4 * T + 16);
+        const float Sj[4] = {s01.x, s45.x, s01.y, s45.y};
+        const float Zj[4] = {z01.x, z45.x, z01.y, z45.y};
         float x[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -646,14 +665,16 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
     }
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
-      if (r + 2 < r1) *(uint2*)(mslot(r + 2) + s * MS + 8 * tid) = mnext[s];
+      if (r + 2 < r1) stage_scales<Sh>(mslot(r + 2) + s * MS, mnext[s], tid);
       mnext[s] = *(const uint2*)(r + 3 < r1 ? rec(r + 3) + s * SB + mo : rec0);
     }
     __syncthreads();  // (B3) weights, zero-point sums; q~ and scales of r + 1, r + 2
 
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
-      const float corr = xz[s][0][q16] + xz[s][1][q16] + xz[s][2][q16] + xz[s][3][q16];
+      // packed, the lo columns accumulate apart from the hi columns until the
+      // end of the chunk; the zero-point sum goes to the hi columns only
+      const float corr = PK && q16 >= 8 ? 0.0f : xz[s][0][q16] + xz[s][1][q16] + xz[s][2][q16] + xz[s][3][q16];
       half8 pbh[4], pbl[4] = {};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -675,25 +696,26 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
           for (int j = 0; j < VT; ++j) o[j] = mfma16(av[j], pbl[t], o[j]);
         }
       }
-      if (PK) {
-#pragma unroll
-        for (int j = 0; j < VT; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[j][e] = add_x8(o[j][e]);
-      }
       load_values<Sh>(more ? rec(r + 1) + s * SB : rec0, vd[s], wave, lane, !more);
-      const uint8_t* vm = mr + s * MS + Sh::VM;
+      const uint8_t* vm = mr + s * MS;
 #pragma unroll
       for (int j = 0; j < VT; ++j) {
         const int cb = VT * wave + j;
-        const uint2 cv = *(const uint2*)(vm + 2 * (16 * cb + 4 * g));
-        const half2v c01 = as_h2(cv.x), c23 = as_h2(cv.y);
-        acc[s][j][0] = fmaf((float)c01[0], o[j][0] + corr, acc[s][j][0]);
-        acc[s][j][1] = fmaf((float)c01[1], o[j][1] + corr, acc[s][j][1]);
-        acc[s][j][2] = fmaf((float)c23[0], o[j][2] + corr, acc[s][j][2]);
-        acc[s][j][3] = fmaf((float)c23[1], o[j][3] + corr, acc[s][j][3]);
+        const float4 c = *(const float4*)(vm + Sh::L_VC + 4 * (16 * cb + 4 * g));
+        acc[s][j][0] = fmaf(c.x, o[j][0] + corr, acc[s][j][0]);
+        acc[s][j][1] = fmaf(c.y, o[j][1] + corr, acc[s][j][1]);
+        acc[s][j][2] = fmaf(c.z, o[j][2] + corr, acc[s][j][2]);
+        acc[s][j][3] = fmaf(c.w, o[j][3] + corr, acc[s][j][3]);
       }
     }
+  }
+  if (PK) {  // lo columns into the hi columns
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+      for (int j = 0; j < VT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[s][j][e] = add_x8(acc[s][j][e]);
   }
 
   // ---- partial of this chunk: every wave holds the same m; l sums over

@@ -833,7 +833,10 @@ __device__ __forceinline__ void ring_load(const DecodeArgs& a, const DecodeSeq& 
   }
 }
 
-template <int D>
+// PK (at most 8 query heads): the hi and lo halves of the query operands and
+// of the weights share one product, hi in columns 0..7 and lo in 8..15, as in
+// the body; the value sums keep their lo columns apart until the end.
+template <int D, bool PK>
 __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int c, uint8_t* smem) {
   using Ly = RingLds<D>;
   constexpr int NB = Ly::NB, KK = D / 32, CPW = D / 64;
@@ -863,12 +866,17 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
     query_rows<D>(a, qraw, !sink, rows, wave, lane);
     __syncthreads();
     for (int kk = wave; kk < KK; kk += 4) {
-      const float* r = rows + q16 * D + 32 * kk + 8 * g;
+      const float* r = rows + (PK ? q16 & 7 : q16) * D + 32 * kk + 8 * g;
       uint32_t hh[4], ll[4];
 #pragma unroll
       for (int pr = 0; pr < 4; ++pr) split_h2(r[2 * pr], r[2 * pr + 1], hh[pr], ll[pr]);
-      qo[kk][0][lane] = make_uint4(hh[0], hh[1], hh[2], hh[3]);
-      qo[kk][1][lane] = make_uint4(ll[0], ll[1], ll[2], ll[3]);
+      const uint4 hi = make_uint4(hh[0], hh[1], hh[2], hh[3]), lo = make_uint4(ll[0], ll[1], ll[2], ll[3]);
+      if (PK) {
+        qo[kk][0][lane] = q16 < 8 ? hi : lo;
+      } else {
+        qo[kk][0][lane] = hi;
+        qo[kk][1][lane] = lo;
+      }
     }
     __syncthreads();
   }
@@ -951,7 +959,13 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
       }
       const int blk = kk / 4;
       sacc[blk] = mfma16(av, mfma_a(qo[kk][0][lane]), sacc[blk]);
-      sacc[blk] = mfma16(av, mfma_a(qo[kk][1][lane]), sacc[blk]);
+      if (!PK) sacc[blk] = mfma16(av, mfma_a(qo[kk][1][lane]), sacc[blk]);
+    }
+    if (PK) {  // lanes l and l ^ 8 both get the hi + lo sum of their column, bit for bit
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sacc[blk][r] = add_x8(sacc[blk][r]);
     }
     float sc[4];
     float mx = -INFINITY;
@@ -992,8 +1006,12 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
       uint2 hi, lo;
       split_h2(x[0], x[1], hi.x, lo.x);
       split_h2(x[2], x[3], hi.y, lo.y);
-      *(uint2*)(pw + ((blk * 2 + 0) * 16 + q16) * kRPitch + 16 * wave + 4 * g) = hi;
-      *(uint2*)(pw + ((blk * 2 + 1) * 16 + q16) * kRPitch + 16 * wave + 4 * g) = lo;
+      if (PK) {
+        *(uint2*)(pw + ((blk * 2 + 0) * 16 + q16) * kRPitch + 16 * wave + 4 * g) = q16 < 8 ? hi : lo;
+      } else {
+        *(uint2*)(pw + ((blk * 2 + 0) * 16 + q16) * kRPitch + 16 * wave + 4 * g) = hi;
+        *(uint2*)(pw + ((blk * 2 + 1) * 16 + q16) * kRPitch + 16 * wave + 4 * g) = lo;
+      }
     }
     __syncthreads();  // weights
 
@@ -1006,9 +1024,11 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
       for (int j = 0; j < kStep / 32; ++j) {
         const half8 av = mfma_a(*(const uint4*)(vt + (16 * cb + q16) * kRPitch + 32 * j + 8 * g));
         const half8 bh = mfma_a(*(const uint4*)(pw + ((blk * 2 + 0) * 16 + q16) * kRPitch + 32 * j + 8 * g));
-        const half8 bl = mfma_a(*(const uint4*)(pw + ((blk * 2 + 1) * 16 + q16) * kRPitch + 32 * j + 8 * g));
         acc[i] = mfma16(av, bh, acc[i]);
-        acc[i] = mfma16(av, bl, acc[i]);
+        if (!PK) {
+          const half8 bl = mfma_a(*(const uint4*)(pw + ((blk * 2 + 1) * 16 + q16) * kRPitch + 32 * j + 8 * g));
+          acc[i] = mfma16(av, bl, acc[i]);
+        }
       }
     }
     __syncthreads();  // V^T and the weights are free
@@ -1024,6 +1044,12 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
     }
   }
 
+  if (PK) {  // lo columns into the hi columns
+#pragma unroll
+    for (int i = 0; i < CPW; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][e] = add_x8(acc[i][e]);
+  }
   // partial rows through the V^T area (free after the last step); the sink's
   // sums are in the original domain already
   const float lsum = xsum4(l_part);
@@ -1175,7 +1201,12 @@ __device__ __forceinline__ void decode_main(const DecodeArgs& a, uint8_t* smem) 
         body_role<BodyShape<D, KB>, false>(a, b, h, c, smem);
     }
   } else {
-    if (find_item(a, item - a.n_body_items, false, b, h, c)) ring_role<D>(a, b, h, c, smem);
+    if (find_item(a, item - a.n_body_items, false, b, h, c)) {
+      if (D >= 256 && a.g <= 8)
+        ring_role<D, true>(a, b, h, c, smem);
+      else
+        ring_role<D, false>(a, b, h, c, smem);
+    }
   }
   prof_end(a.prof_ts);
 }
@@ -1203,7 +1234,12 @@ template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_ring_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[RingLds<D>::total];
   int b, h, c;
-  if (find_item(a, blockIdx.x, false, b, h, c)) ring_role<D>(a, b, h, c, smem);
+  if (find_item(a, blockIdx.x, false, b, h, c)) {
+    if (D >= 256 && a.g <= 8)
+      ring_role<D, true>(a, b, h, c, smem);
+    else
+      ring_role<D, false>(a, b, h, c, smem);
+  }
 }
 
 // Append (optional), body and sink/ring items in one launch: head_dim 128,

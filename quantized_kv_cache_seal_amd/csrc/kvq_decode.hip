@@ -231,6 +231,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 // running (M, L, sum e^(m - M) acc).  The 16 row groups meet in LDS.
 constexpr int kMergeUnroll = 8;  // partials per thread and pass
 
+// e^x for x <= 0 by the hardware base-2 exponential (the merge weights need
+// fp32 precision, not correct rounding; the partials' m are in natural-log units)
+__device__ __forceinline__ float exp_le0(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int NSL = D / 64, U = kMergeUnroll;
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (base + rg + 16 * u < n) mp = fmaxf(mp, ml[u].x);
-    const float alpha = M == -INFINITY ? 0.0f : expf(M - mp);  // nothing to rescale before the first partial
+    const float alpha = M == -INFINITY ? 0.0f : exp_le0(M - mp);  // nothing to rescale before the first partial
     L *= alpha;
     v.x *= alpha;
     v.y *= alpha;
@@ -268,7 +272,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (base + rg + 16 * u < n) {
-        const float w = expf(ml[u].x - M);
+        const float w = exp_le0(ml[u].x - M);
         L = fmaf(w, ml[u].y, L);
         v.x = fmaf(w, x[u].x, v.x);
         v.y = fmaf(w, x[u].y, v.y);
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float s = rm[0][r] == -INFINITY ? 0.0f : expf(rm[0][r] - Mt);  // a row group with no partial
+    const float s = rm[0][r] == -INFINITY ? 0.0f : exp_le0(rm[0][r] - Mt);  // a row group with no partial
     Lt = fmaf(s, rm[1][r], Lt);
     const float4 t = red[r][cq];
     o.x = fmaf(s, t.x, o.x);

@@ -186,6 +186,27 @@ kvq_status kvq_seq_reset(kvq_cache* cache, int32_t seq);
  * reprocessing).  Growing is not allowed (KVQ_ERR_INVALID). */
 kvq_status kvq_seq_truncate(kvq_cache* cache, int32_t seq, int32_t layer, int64_t n_tok);
 
+/* Whole-sequence save and restore (the pages list save/restore and rollback
+ * among the cache's operations: SJ-KVaRN section 10).  A saved sequence is
+ * one host blob: a header (format version and the cache's layout and encoding
+ * fingerprint: layers, KV heads, head_dim, ring capacity, bit widths,
+ * balancing passes, rotation signs), the per-layer token and record counts,
+ * then the sequence's sink, ring and sealed records as laid out in the arena.
+ * Restoring a snapshot rolls a sequence back past its seal boundary, which
+ * kvq_seq_truncate cannot do.
+ * kvq_seq_save_bytes: host out, the blob size for the sequence as it is now.
+ * kvq_seq_save: host_dst of exactly that many bytes; reads the device in
+ * stream order and synchronises `stream` before returning.
+ * kvq_seq_restore: host_src a blob from kvq_seq_save of a cache with the same
+ * fingerprint (any max_seqs, max_ctx >= the saved counts); replaces slot seq
+ * (any other slot, or the one saved) and synchronises `stream`.
+ * Errors: KVQ_ERR_INVALID (range, size, or a blob that is not a saved
+ * sequence of a matching cache; nothing is changed), KVQ_ERR_UNSUPPORTED
+ * (plan-only cache), KVQ_ERR_DEVICE. */
+kvq_status kvq_seq_save_bytes(const kvq_cache* cache, int32_t seq, size_t* bytes);
+kvq_status kvq_seq_save(const kvq_cache* cache, int32_t seq, void* host_dst, size_t bytes, void* stream);
+kvq_status kvq_seq_restore(kvq_cache* cache, int32_t seq, const void* host_src, size_t bytes, void* stream);
+
 /* Copy canonical bytes of one cache unit to the host, synchronising `stream`:
  *   KVQ_REGION_SINK, index = token (< 128): [K fp16 x head_dim][V fp16 x head_dim];
  *   KVQ_REGION_RING, index = ring slot: for K then V, head_dim/128 tq6_0

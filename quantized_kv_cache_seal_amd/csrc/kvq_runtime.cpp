@@ -636,6 +636,155 @@ kvq_status kvq_seq_truncate(kvq_cache* c, int32_t seq, int32_t layer, int64_t n_
   return KVQ_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Whole-sequence save / restore.  A sequence's state is its per-layer counts
+// and four spans of the arena (the sequence is the outermost index of every
+// region): the sink, the ring codes and the ring scales whole, and the sealed
+// records of each (layer, KV head), which are contiguous from record 0.
+namespace {
+constexpr uint32_t kSaveMagic = 0x5351564Bu;  // "KVQS"
+constexpr uint32_t kSaveVersion = 1;
+struct SaveHeader {
+  uint32_t magic, version;
+  // layout fingerprint: a blob restores only into a cache that lays the same
+  // bytes out the same way and encodes further tokens the same way
+  int32_t L, H, D, NB, cap, kbits, vbits, sinkhorn_passes;
+  int64_t rec_bytes;
+  uint64_t rot_signs[4];
+};
+struct SeqSpans {
+  int64_t sink_off, sink_n, rcode_off, rcode_n, rscale_off, rscale_n;
+};
+SeqSpans seq_spans(const Layout& y, int s) {
+  SeqSpans p;
+  p.sink_n = (int64_t)y.L * y.H * 2 * kSink * y.D * 2;
+  p.sink_off = y.off_sink + (int64_t)s * p.sink_n;
+  p.rcode_n = (int64_t)y.L * y.H * 2 * y.cap * y.NB * kQBytes;
+  p.rcode_off = y.off_rcode + (int64_t)s * p.rcode_n;
+  p.rscale_n = (int64_t)y.L * y.H * 2 * y.cap * y.NB * 2;
+  p.rscale_off = y.off_rscale + (int64_t)s * p.rscale_n;
+  return p;
+}
+SaveHeader save_header(const kvq_cache* c) {
+  SaveHeader hd{};
+  hd.magic = kSaveMagic;
+  hd.version = kSaveVersion;
+  hd.L = c->y.L;
+  hd.H = c->y.H;
+  hd.D = c->y.D;
+  hd.NB = c->y.NB;
+  hd.cap = c->y.cap;
+  hd.kbits = c->y.kbits;
+  hd.vbits = c->y.vbits;
+  hd.sinkhorn_passes = c->cfg.sinkhorn_passes;
+  hd.rec_bytes = c->y.rec_bytes;
+  for (int i = 0; i < 4; ++i) hd.rot_signs[i] = c->cfg.rot_signs[i];
+  return hd;
+}
+size_t save_bytes(const kvq_cache* c, const int64_t* n_rec) {
+  const SeqSpans p = seq_spans(c->y, 0);
+  size_t n = sizeof(SaveHeader) + (size_t)2 * c->y.L * sizeof(int64_t) + p.sink_n + p.rcode_n + p.rscale_n;
+  for (int l = 0; l < c->y.L; ++l) n += (size_t)c->y.H * n_rec[l] * c->y.rec_bytes;
+  return n;
+}
+}  // namespace
+
+kvq_status kvq_seq_save_bytes(const kvq_cache* c, int32_t seq, size_t* bytes) {
+  if (!c || !bytes) return fail(KVQ_ERR_INVALID, "bad arguments");
+  if (seq < 0 || seq >= c->y.S) return fail(KVQ_ERR_INVALID, "seq out of range");
+  std::vector<int64_t> nr(c->y.L);
+  for (int l = 0; l < c->y.L; ++l) nr[l] = c->rec(seq, l);
+  *bytes = save_bytes(c, nr.data());
+  return KVQ_OK;
+}
+
+kvq_status kvq_seq_save(const kvq_cache* c, int32_t seq, void* host_dst, size_t bytes, void* stream) {
+  if (!c || !host_dst) return fail(KVQ_ERR_INVALID, "bad arguments");
+  if (c->plan_only) return fail(KVQ_ERR_UNSUPPORTED, "no device arena");
+  size_t need = 0;
+  kvq_status st = kvq_seq_save_bytes(c, seq, &need);
+  if (st != KVQ_OK) return st;
+  if (bytes != need) return fail(KVQ_ERR_INVALID, "save needs %zu bytes, got %zu", need, bytes);
+  const Layout& y = c->y;
+  uint8_t* out = (uint8_t*)host_dst;
+  const SaveHeader hd = save_header(c);
+  std::memcpy(out, &hd, sizeof hd);
+  size_t o = sizeof hd;
+  for (int l = 0; l < y.L; ++l, o += sizeof(int64_t)) std::memcpy(out + o, &c->n_tok[(size_t)seq * y.L + l], sizeof(int64_t));
+  for (int l = 0; l < y.L; ++l, o += sizeof(int64_t)) std::memcpy(out + o, &c->n_rec[(size_t)seq * y.L + l], sizeof(int64_t));
+  const SeqSpans p = seq_spans(y, seq);
+  hipStream_t sm = (hipStream_t)stream;
+  const int64_t spans[3][2] = {{p.sink_off, p.sink_n}, {p.rcode_off, p.rcode_n}, {p.rscale_off, p.rscale_n}};
+  for (const auto& sp : spans) {
+    hipError_t e = hipMemcpyAsync(out + o, c->arena + sp[0], (size_t)sp[1], hipMemcpyDeviceToHost, sm);
+    if (e != hipSuccess) return hip_fail(e, "save copy");
+    o += (size_t)sp[1];
+  }
+  for (int l = 0; l < y.L; ++l)
+    for (int h = 0; h < y.H; ++h) {
+      const size_t n = (size_t)c->rec(seq, l) * y.rec_bytes;
+      if (n == 0) continue;
+      hipError_t e = hipMemcpyAsync(out + o, c->arena + rec_off(y, seq, l, h, 0), n, hipMemcpyDeviceToHost, sm);
+      if (e != hipSuccess) return hip_fail(e, "save copy");
+      o += n;
+    }
+  hipError_t e = hipStreamSynchronize(sm);
+  if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  return KVQ_OK;
+}
+
+kvq_status kvq_seq_restore(kvq_cache* c, int32_t seq, const void* host_src, size_t bytes, void* stream) {
+  if (!c || !host_src) return fail(KVQ_ERR_INVALID, "bad arguments");
+  if (c->plan_only) return fail(KVQ_ERR_UNSUPPORTED, "no device arena");
+  if (seq < 0 || seq >= c->y.S) return fail(KVQ_ERR_INVALID, "seq out of range");
+  const Layout& y = c->y;
+  const uint8_t* in = (const uint8_t*)host_src;
+  const size_t head = sizeof(SaveHeader) + (size_t)2 * y.L * sizeof(int64_t);
+  if (bytes < head) return fail(KVQ_ERR_INVALID, "blob of %zu bytes is shorter than its header", bytes);
+  SaveHeader hd;
+  std::memcpy(&hd, in, sizeof hd);
+  const SaveHeader want = save_header(c);
+  if (hd.magic != kSaveMagic || hd.version != kSaveVersion)
+    return fail(KVQ_ERR_INVALID, "not a saved sequence (magic or version)");
+  if (std::memcmp(&hd, &want, sizeof hd) != 0)
+    return fail(KVQ_ERR_INVALID, "saved sequence is from a cache with another layout or encoding");
+  std::vector<int64_t> nt(y.L), nr(y.L);
+  std::memcpy(nt.data(), in + sizeof hd, (size_t)y.L * sizeof(int64_t));
+  std::memcpy(nr.data(), in + sizeof hd + (size_t)y.L * sizeof(int64_t), (size_t)y.L * sizeof(int64_t));
+  for (int l = 0; l < y.L; ++l) {
+    if (nt[l] < 0 || nt[l] > c->cfg.max_ctx || nr[l] < 0 || nr[l] > y.max_rec ||
+        (nt[l] > kSink && (nr[l] > (nt[l] - kSink) / kGroup || nt[l] - kSink - kGroup * nr[l] > y.cap)) ||
+        (nt[l] <= kSink && nr[l] != 0))
+      return fail(KVQ_ERR_INVALID, "saved counts of layer %d are inconsistent", l);
+  }
+  if (bytes != save_bytes(c, nr.data())) return fail(KVQ_ERR_INVALID, "blob has %zu bytes, its counts need %zu", bytes,
+                                                     save_bytes(c, nr.data()));
+  size_t o = head;
+  const SeqSpans p = seq_spans(y, seq);
+  hipStream_t sm = (hipStream_t)stream;
+  const int64_t spans[3][2] = {{p.sink_off, p.sink_n}, {p.rcode_off, p.rcode_n}, {p.rscale_off, p.rscale_n}};
+  for (const auto& sp : spans) {
+    hipError_t e = hipMemcpyAsync(c->arena + sp[0], in + o, (size_t)sp[1], hipMemcpyHostToDevice, sm);
+    if (e != hipSuccess) return hip_fail(e, "restore copy");
+    o += (size_t)sp[1];
+  }
+  for (int l = 0; l < y.L; ++l)
+    for (int h = 0; h < y.H; ++h) {
+      const size_t n = (size_t)nr[l] * y.rec_bytes;
+      if (n == 0) continue;
+      hipError_t e = hipMemcpyAsync(c->arena + rec_off(y, seq, l, h, 0), in + o, n, hipMemcpyHostToDevice, sm);
+      if (e != hipSuccess) return hip_fail(e, "restore copy");
+      o += n;
+    }
+  hipError_t e = hipStreamSynchronize(sm);
+  if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  for (int l = 0; l < y.L; ++l) {
+    c->tok(seq, l) = nt[l];
+    c->rec(seq, l) = nr[l];
+  }
+  return KVQ_OK;
+}
+
 kvq_status kvq_unit_bytes(const kvq_cache* c, int32_t region, size_t* bytes) {
   if (!c || !bytes) return fail(KVQ_ERR_INVALID, "bad arguments");
   switch (region) {

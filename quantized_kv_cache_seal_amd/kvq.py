@@ -23,7 +23,8 @@ FLAG_PLAN_ONLY = 1
 EXPORTS = [
     "kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_append", "kvq_seal",
     "kvq_workspace_bytes", "kvq_attn_decode", "kvq_decode_step", "kvq_set_decode_path", "kvq_seq_info", "kvq_seq_reset",
-    "kvq_seq_truncate", "kvq_export", "kvq_import", "kvq_unit_bytes", "kvq_profile_start", "kvq_profile_stop",
+    "kvq_seq_truncate", "kvq_seq_save_bytes", "kvq_seq_save", "kvq_seq_restore", "kvq_export", "kvq_import",
+    "kvq_unit_bytes", "kvq_profile_start", "kvq_profile_stop",
     "kvq_status_string", "kvq_last_error",
 ]
 
@@ -69,6 +70,9 @@ def lib():
             "kvq_seq_info": [vp, i32, i32, P(i64), P(i64), P(i32)],
             "kvq_seq_reset": [vp, i32],
             "kvq_seq_truncate": [vp, i32, i32, i64],
+            "kvq_seq_save_bytes": [vp, i32, P(sz)],
+            "kvq_seq_save": [vp, i32, vp, sz, vp],
+            "kvq_seq_restore": [vp, i32, vp, sz, vp],
             "kvq_export": [vp, i32, i32, i32, i32, i64, vp, sz, vp],
             "kvq_import": [vp, i32, i32, i32, i32, i64, vp, sz, vp],
             "kvq_unit_bytes": [vp, i32, P(sz)],
@@ -238,6 +242,24 @@ class Cache:
 
     def truncate(self, seq, layer, n_tok):
         return lib().kvq_seq_truncate(self.h, seq, layer, n_tok)
+
+    def save_bytes(self, seq) -> int:
+        n = ctypes.c_size_t()
+        check(lib().kvq_seq_save_bytes(self.h, seq, ctypes.byref(n)))
+        return n.value
+
+    def save(self, seq, stream=None):
+        """The sequence's saved state as a numpy uint8 array."""
+        import numpy as np
+        out = np.empty(self.save_bytes(seq), dtype=np.uint8)
+        check(lib().kvq_seq_save(self.h, seq, out.ctypes.data, out.nbytes, _stream(stream)))
+        return out
+
+    def restore(self, seq, blob, stream=None) -> int:
+        """Restore a saved sequence into slot seq; returns the status (not raised)."""
+        import numpy as np
+        b = np.ascontiguousarray(np.frombuffer(blob, dtype=np.uint8) if isinstance(blob, (bytes, bytearray)) else blob)
+        return lib().kvq_seq_restore(self.h, seq, b.ctypes.data, b.nbytes, _stream(stream))
 
     def unit_bytes(self, region) -> int:
         n = ctypes.c_size_t()

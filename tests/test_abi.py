@@ -135,3 +135,21 @@ def test_errors_and_truncate():
     buf = ctypes.create_string_buffer(1024)
     assert kvq.lib().kvq_export(c.h, 0, 0, 0, kvq.REGION_SINK, 0, buf, 1024, None) == kvq.ERR_UNSUPPORTED
     assert b"max_ctx" in kvq.lib().kvq_last_error() or kvq.lib().kvq_last_error()
+
+
+def test_save_bytes_and_plan_only_save():
+    """kvq_seq_save_bytes grows by one record per KV head for each sealed
+    group; save and restore need a device arena."""
+    c = _plan(kvq.make_config(2, 2, 256, 4, 2, 2000, 256, 512, margin=0))
+    rec = c.unit_bytes(kvq.REGION_BODY)
+    b0 = c.save_bytes(0)
+    kvq.check(kvq.lib().kvq_append(c.h, 0, *kvq._ids([0]), None, None, 640, None))
+    assert c.save_bytes(0) == b0                      # the sink and ring are saved whole
+    assert c.seal(0) == 2
+    assert c.save_bytes(0) == b0 + 2 * 2 * rec        # two records in each of 2 KV heads
+    assert c.save_bytes(1) == b0
+    buf = ctypes.create_string_buffer(b0)
+    assert kvq.lib().kvq_seq_save(c.h, 1, buf, b0, None) == kvq.ERR_UNSUPPORTED
+    assert kvq.lib().kvq_seq_restore(c.h, 1, buf, b0, None) == kvq.ERR_UNSUPPORTED
+    n = ctypes.c_size_t()
+    assert kvq.lib().kvq_seq_save_bytes(c.h, 2, ctypes.byref(n)) == kvq.ERR_INVALID

@@ -315,3 +315,63 @@ def test_decode_deterministic():
     a = p.gpu.attn_decode(0, [0], q).cpu().numpy()
     b = p.gpu.attn_decode(0, [0], q).cpu().numpy()
     assert np.array_equal(a, b)
+
+
+def test_save_restore_and_rollback():
+    """kvq_seq_save / kvq_seq_restore: a restored sequence decodes bit for bit
+    as the saved one did, into its own slot or another; restoring a snapshot
+    taken before more tokens were appended and sealed rolls the sequence back
+    past the new seal boundary; blobs that do not match are refused and
+    change nothing."""
+    w = configs.QWEN27B.scaled(n_layers=2, n_kv_heads=2, n_q_heads=12, tail_min=256, tail_max=384, ctx=1300)
+    p = Pair(w, [1300, 700], extra_ctx=600).build(300)
+    p.import_oracle_records()
+    t = p.torch
+    q = p.queries(7, 0)
+    _, out0 = p.decode_errors(0, q)
+    counts0 = [p.gpu.info(0, l) for l in range(w.n_layers)]
+    blob = p.gpu.save(0)
+    assert blob.nbytes == p.gpu.save_bytes(0)
+    _say(f"[save] seq 0 counts {counts0}, {blob.nbytes} bytes")
+
+    # roll forward: 512 more tokens in every layer, sealed as they fill
+    extra = 512
+    for l in range(w.n_layers):
+        n = p.gpu.info(0, l)[0]
+        k = p.specs[0].tokens(l, "k", n, extra)[None]
+        v = p.specs[0].tokens(l, "v", n, extra)[None]
+        for c0 in range(0, extra, 128):
+            p.gpu.append(l, [0], t.from_numpy(k[:, c0:c0 + 128].copy()).cuda(), t.from_numpy(v[:, c0:c0 + 128].copy()).cuda())
+            p.gpu.seal(l, kvq.SEAL_IF_FULL)
+    grown = [p.gpu.info(0, l) for l in range(w.n_layers)]
+    assert all(g[1] > c[1] for g, c in zip(grown, counts0)), (grown, counts0)  # records were sealed
+    assert p.gpu.truncate(0, -1, counts0[0][0]) == kvq.ERR_SEALED           # truncate cannot go back
+
+    # rollback by restore: counts and decode exactly as saved
+    assert p.gpu.restore(0, blob) == kvq.OK
+    assert [p.gpu.info(0, l) for l in range(w.n_layers)] == counts0
+    _, out1 = p.decode_errors(0, q)
+    assert np.array_equal(out1, out0)
+    errs, _ = p.decode_errors(0, q)
+    assert max(errs) <= ATTN_TOL
+
+    # into another slot: seq 1 becomes a copy of seq 0
+    assert p.gpu.restore(1, blob) == kvq.OK
+    q2 = q.copy()
+    q2[1] = q[0]
+    _, out2 = p.decode_errors(0, q2)
+    assert np.array_equal(out2[1], out0[0])
+    for l in range(w.n_layers):
+        for h in range(w.n_kv_heads):
+            for region, idx in ((kvq.REGION_SINK, 5), (kvq.REGION_RING, 3), (kvq.REGION_BODY, counts0[l][1] - 1)):
+                assert p.gpu.export(1, l, h, region, idx) == p.gpu.export(0, l, h, region, idx)
+
+    # refused blobs change nothing
+    bad = blob.copy()
+    bad[0] ^= 0xFF
+    assert p.gpu.restore(1, bad) == kvq.ERR_INVALID
+    assert p.gpu.restore(1, blob[:-1]) == kvq.ERR_INVALID
+    other = kvq.Cache(kvq.config_for(configs.QWEN27B.scaled(n_layers=2, n_kv_heads=2, n_q_heads=12, tail_min=256,
+                                                            tail_max=512, ctx=1300), max_ctx=2000, max_seqs=1))
+    assert other.restore(0, blob) == kvq.ERR_INVALID  # another ring capacity
+    assert [p.gpu.info(1, l) for l in range(w.n_layers)] == counts0

@@ -147,12 +147,39 @@ def run_decode(args, w, torch, kvq, synthetic, inputs):
         f"{gbs:.1f} GB/s; main decode kernel avg {avg_kernel_us:.1f} us over {len(kernel_us)} calls -> "
         f"{achieved:.1f} GB/s")
     info = cache.info(0, 0)
+    sr = run_save_restore(cache, torch, kvq, qs[0][0], ws, stream) if args.save_restore else None
     del cache
     torch.cuda.empty_cache()
     return {
         "ms_per_step": ms_step, "gbs": gbs, "bytes_step": bytes_step, "avg_kernel_us": avg_kernel_us,
-        "achieved": achieved, "per_call_bytes": per_call_bytes, "info_after": info,
+        "achieved": achieved, "per_call_bytes": per_call_bytes, "info_after": info, "save_restore": sr,
     }
+
+
+def run_save_restore(cache, torch, kvq, q, ws, stream):
+    """Save sequence 0 (every layer) to host memory and restore it, timed on
+    the host around each call (each synchronises its stream), into and out of
+    a pinned host buffer allocated beforehand; the decode of layer 0 after the
+    restore must equal the one before bit for bit."""
+    seqs = [0]
+    before = cache.attn_decode(0, seqs, q[:1].contiguous(), workspace=ws, stream=stream).clone()
+    host = torch.empty(cache.save_bytes(0), dtype=torch.uint8, pin_memory=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    blob = cache.save(0, stream=stream, out=host.numpy())
+    t1 = time.perf_counter()
+    assert cache.restore(0, blob, stream=stream) == kvq.OK
+    t2 = time.perf_counter()
+    after = cache.attn_decode(0, seqs, q[:1].contiguous(), workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    assert torch.equal(before, after)
+    gb = blob.nbytes / 1e9
+    del blob, host
+    log(f"[bench] save/restore of sequence 0 (pinned host buffer): {gb:.3f} GB, save {(t1 - t0) * 1e3:.1f} ms "
+        f"({gb / (t1 - t0):.1f} GB/s), restore {(t2 - t1) * 1e3:.1f} ms ({gb / (t2 - t1):.1f} GB/s), "
+        f"decode after restore bit-identical")
+    return {"bytes": int(gb * 1e9), "save_ms": round((t1 - t0) * 1e3, 2), "restore_ms": round((t2 - t1) * 1e3, 2),
+            "save_gbs": round(gb / (t1 - t0), 2), "restore_gbs": round(gb / (t2 - t1), 2)}
 
 
 def run_seal(args, w, torch, kvq, synthetic):
@@ -270,6 +297,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle decode timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-seal", action="store_true")
+    ap.add_argument("--save-restore", action="store_true",
+                    help="also time saving and restoring sequence 0 to and from host memory (kvq_seq_save/_restore)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 20 times (calibrates HBM byte counters) and exit")
     args = ap.parse_args()
@@ -298,7 +327,7 @@ def main():
     dec = run_decode(args, w, torch, kvq, synthetic, inputs)
     seal = None if args.no_seal else run_seal(args, w, torch, kvq, synthetic)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(w, args.cpu_budget)
-    mfma_body = w.head_dim == 256 and w.k_bits == 4 and w.v_bits == 4 and args.path != "valu"
+    mfma_body = args.path != "valu"
     traffic = measured_traffic() if (args.workload == "qwen27b" and mfma_body) else None
     if traffic is not None:
         traffic = int(traffic)
@@ -333,6 +362,8 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if dec["save_restore"]:
+        res["save_restore"] = dec["save_restore"]
     if seal and w.n_seqs > 1:   # the batched workload meets one seal batch every 256 steps
         res["amortized_ms_per_step"] = round(dec["ms_per_step"] + seal["ms"] / 256, 4)
     if seal:

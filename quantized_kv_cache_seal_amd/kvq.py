@@ -248,10 +248,13 @@ class Cache:
         check(lib().kvq_seq_save_bytes(self.h, seq, ctypes.byref(n)))
         return n.value
 
-    def save(self, seq, stream=None):
-        """The sequence's saved state as a numpy uint8 array."""
+    def save(self, seq, stream=None, out=None):
+        """The sequence's saved state as a numpy uint8 array (written into `out`,
+        a contiguous uint8 array of save_bytes(seq) bytes, when given)."""
         import numpy as np
-        out = np.empty(self.save_bytes(seq), dtype=np.uint8)
+        if out is None:
+            out = np.empty(self.save_bytes(seq), dtype=np.uint8)
+        assert out.dtype == np.uint8 and out.flags["C_CONTIGUOUS"] and out.nbytes == self.save_bytes(seq)
         check(lib().kvq_seq_save(self.h, seq, out.ctypes.data, out.nbytes, _stream(stream)))
         return out
 

@@ -15,13 +15,17 @@ Readings:
 * a "pass" is one sweep over all rows or over all columns, rows first (the
   order of the words "row and column"), so 16 passes = 8 row + 8 column sweeps;
 * log-domain state: lr (per row) and lc (per column), with
-  y_ij = x_ij * exp(-lr_i - lc_j); a row pass sets lr_i += ln max(sigma_i, 1e-30)
-  where sigma_i is the spread of row i of y; a column pass does the same for lc;
+  y_ij = x_ij * exp(-lr_i - lc_j); a row pass sets lr_i += ln sigma_i where
+  sigma_i is the spread of row i of y; a column pass does the same for lc;
+* a row or column whose spread is zero (at most 1e-30) cannot be balanced and
+  keeps its scale (its log scale is not updated): an all-zero tile keeps unit
+  scales.  Adding ln of a floor instead would grow the log scales of such a
+  row or column by ~69 per pass until exp overflows;
 * scale absorption: the row factors are not stored (each row gets its own
   rounding scale and zero point afterwards, which absorbs them); the column
   factors are kept as C_j = fp16(exp(lc_j)) after centring lc to mean zero
-  (the gauge) and clamping it to [-9, 9] (the clamp and the 1e-30 floor are
-  this implementation's guards; the pages state neither);
+  (the gauge) and clamping it to [-9, 9] (the clamp and the zero-spread rule
+  are this implementation's guards; the pages state neither);
 * "keep the final scales" (SJ-KVaRN), not "keep the best scales seen".
 Arithmetic is float64 throughout.
 """
@@ -44,10 +48,10 @@ def balance(x, passes: int):
         y = x * np.exp(-lr[:, None] - lc[None, :])
         if p % 2 == 0:
             sigma = y.std(axis=1)
-            lr = lr + np.log(np.maximum(sigma, LOG_FLOOR))
+            lr = lr + np.where(sigma > LOG_FLOOR, np.log(np.maximum(sigma, LOG_FLOOR)), 0.0)
         else:
             sigma = y.std(axis=0)
-            lc = lc + np.log(np.maximum(sigma, LOG_FLOOR))
+            lc = lc + np.where(sigma > LOG_FLOOR, np.log(np.maximum(sigma, LOG_FLOOR)), 0.0)
     lc_c = np.clip(lc - lc.mean(), -LC_CLAMP, LC_CLAMP)
     C = np.exp(lc_c).astype(np.float16)
     return {"lr": lr, "lc_raw": lc, "lc": lc_c, "C": C}

@@ -23,7 +23,9 @@
 // both copies stay in registers (the second is built through a transposed tile
 // in LDS).  The updated side's factor is 1/spread (equal to exp(-l) of the
 // log-domain update l += ln spread, spread the population standard deviation);
-// the factors pass between waves through LDS, one barrier per pass.
+// a row or column whose spread is zero keeps its factor and log scale (it
+// cannot be balanced: an all-zero tile keeps unit scales); the factors pass
+// between waves through LDS, one barrier per pass.
 //
 // The balancing factors (1/spread, ln spread) use the hardware square root,
 // reciprocal and log2 (about 1 ulp): only the column scales C leave the
@@ -35,6 +37,14 @@
 #include "kvq_mfma.h"
 
 namespace kvq {
+
+// Largest balancing factor passed to the matrix cores: the factors and their
+// squares go in as fp16 hi + lo, so f^2 must stay below 65504.  Balanced data
+// has factors near 1 (columns) or 1/|q| (rows); only a column whose spread is
+// nonzero but below 1/255 of the others' (nearly constant over the 128 tokens)
+// reaches the cap, which then keeps its products finite; its log scale still
+// comes from its spread.
+constexpr float kFactorMax = 255.0f;
 
 template <int SUBW>
 struct SealShape {
@@ -216,6 +226,14 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
   const int wb = SUBW == 256 ? (w >> 1) : 0;  // the block of this wave's columns
   const int pr = m >> 1;                       // lane pair 0..7
   constexpr int NCL = CT / 2;                  // columns per lane pair in a column pass
+  // the factors of this lane pair's row and columns from their last update:
+  // a row or column whose spread is zero keeps them (and its log scale)
+  float rf_keep = 1.0f, cf_keep[NCL], lc_keep[NCL];
+#pragma unroll
+  for (int e = 0; e < NCL; ++e) {
+    cf_keep[e] = 1.0f;
+    lc_keep[e] = 0.0f;
+  }
 
   for (int p = 0; p < a.passes; ++p) {
     if ((p & 1) == 0) {
@@ -250,11 +268,13 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
       }
       const float mean = s1 / (float)SUBW;
       const float var = fmaxf(s2 / (float)SUBW - mean * mean, 0.0f);
-      const float rf = __builtin_amdgcn_rcpf(fmaxf(__builtin_amdgcn_sqrtf(var), 1e-30f));
+      const float sd = __builtin_amdgcn_sqrtf(var);
+      const float rf = sd > 1e-30f ? __builtin_amdgcn_rcpf(sd) : rf_keep;
+      rf_keep = rf;
       if ((m & 1) == 0) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          const float f = ds[b][row] * rf;
+          const float f = fminf(ds[b][row] * rf, kFactorMax);
           uint16_t* base = rfl + b * 4 * kGroup;
           put_hilo(base + 0 * kGroup, base + 1 * kGroup, row, f);
           put_hilo(base + 2 * kGroup, base + 3 * kGroup, row, f * f);
@@ -293,12 +313,16 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
         x2 += dpp<0xB1>(x2);
         const float mean = x1 / (float)kGroup;
         const float var = fmaxf(x2 / (float)kGroup - mean * mean, 0.0f);
-        const float sig = fmaxf(__builtin_amdgcn_sqrtf(var), 1e-30f);
-        const float cf = __builtin_amdgcn_rcpf(sig);
+        const float sig = __builtin_amdgcn_sqrtf(var);
+        const bool upd = sig > 1e-30f;
+        const float cf = upd ? fminf(__builtin_amdgcn_rcpf(sig), kFactorMax) : cf_keep[e];
+        const float lc = upd ? __builtin_amdgcn_logf(sig) * 0.6931471805599453f : lc_keep[e];  // log2 -> ln
+        cf_keep[e] = cf;
+        lc_keep[e] = lc;
         if ((m & 1) == 0) {
           put_hilo(cfl + 0 * SUBW, cfl + 1 * SUBW, col, cf);
           put_hilo(cfl + 2 * SUBW, cfl + 3 * SUBW, col, cf * cf);
-          lcs[col] = __builtin_amdgcn_logf(sig) * 0.6931471805599453f;  // log2 -> ln
+          lcs[col] = lc;
         }
       }
     }

@@ -375,3 +375,50 @@ def test_save_restore_and_rollback():
                                                             tail_max=512, ctx=1300), max_ctx=2000, max_seqs=1))
     assert other.restore(0, blob) == kvq.ERR_INVALID  # another ring capacity
     assert [p.gpu.info(1, l) for l in range(w.n_layers)] == counts0
+
+
+def test_degenerate_inputs():
+    """The method's degenerate cases through append, seal and decode, against
+    the oracle: all-zero tokens (tq6_0 scale 0, an all-zero tile through the
+    balancing, row scale 0 read as 1), a one-token sequence (the output is its
+    value), and keys with channels far above the rest (+-2,000, and +-60,000
+    near the fp16 maximum); sink and ring bytes exact, records by the
+    conditional rule, attention within tolerance."""
+    w = configs.QWEN27B.scaled(n_layers=1, n_kv_heads=2, n_q_heads=8, tail_min=256, tail_max=384, ctx=1000)
+    lens = [1000, 1, 1000, 1000]
+    p = Pair(w, lens, extra_ctx=4)
+    H, D = w.n_kv_heads, w.head_dim
+    zeros = np.zeros((lens[0], H, D), dtype=np.float16)
+    p.kv[(0, 0)] = (zeros, zeros.copy())
+    for s, big in ((2, 2000.0), (3, 60000.0)):
+        k, v = (a.copy() for a in p.kv[(s, 0)])
+        k[:, :, 7] = np.where(np.arange(lens[s]) % 2 == 0, big, -big)[:, None].astype(np.float16)
+        k[:, 1, 100] = np.float16(big / 2)
+        p.kv[(s, 0)] = (k, v)
+    p.build(300)
+    p.check_info()
+    assert p.check_sink_ring() > 0
+    st = p.check_records()
+    _say(f"[degenerate] records: {st}")
+    assert st["scales"] > 0 and st["boundary"] <= max(1, st["codes"] // 10 ** 5)
+    p.import_oracle_records()
+    q = p.queries(3, 0)
+    t = p.torch
+    for path in (kvq.PATH_VALU, kvq.PATH_MFMA):
+        p.gpu.set_decode_path(path)
+        got = p.gpu.attn_decode(0, list(range(len(lens))), t.from_numpy(q).cuda()).float().cpu().numpy()
+        got = got.astype(np.float64)
+        assert np.all(np.isfinite(got)), path
+        assert np.abs(got[0]).max() <= 1e-30, (path, np.abs(got[0]).max())  # zero values everywhere
+        one = p.kv[(1, 0)][1][0].astype(np.float64)                           # [H][D]
+        want = np.repeat(one, w.n_q_heads // H, axis=0)
+        assert np.abs(got[1] - want).max() <= 1e-6 * np.abs(want).max(), path
+        for s, tol in ((2, ATTN_TOL), (3, 1e-2)):
+            # +-60,000 keys: the score's two terms S (q~ . code) and Z sigma
+            # reach ~1e5 in fp32 while their sum is ~1e3, so the score carries
+            # ~6e-8 x 1e5 = 6e-3 of error (log2 units), ~4e-3 relative on the
+            # weights of a softmax this peaked: 1e-2 bounds it
+            ref = p.ora.attention(0, s, q[s], 1.0)
+            err = float(np.max(np.abs(got[s] - ref)) / np.sqrt(np.mean(ref ** 2)))
+            _say(f"[degenerate] path={path} seq {s} err={err:.2e}")
+            assert err <= tol, (path, s, err)

@@ -126,6 +126,31 @@ def test_constant_row_scale_one():
     assert np.all(S == np.float16(1.0)) and np.all(Z == np.float16(3.0)) and np.all(codes == 0)
 
 
+def test_zero_tile_keeps_unit_scales():
+    """An all-zero tile (every token zero, e.g. padding) has zero spread in
+    every row and column: nothing is balanced, the log scales stay 0, C = 1,
+    and the rounding gives S = 1 (the zero-range rule), Z = 0 and code 0."""
+    for cols in (128, 256):
+        r = sinkhorn.balance(np.zeros((128, cols)), 16)
+        assert np.all(r["lr"] == 0.0) and np.all(r["lc_raw"] == 0.0)
+        assert np.all(r["C"] == np.float16(1.0))
+        codes, S, Z = rounding.round_rows(np.zeros((128, cols), np.float32), r["C"], 4)
+        assert np.all(S == np.float16(1.0)) and np.all(Z == np.float16(0.0)) and np.all(codes == 0)
+
+
+def test_zero_column_keeps_its_scale():
+    """A column that is zero in every row keeps lc = 0 through every pass; the
+    other columns are balanced as usual (finite, final column spreads 1)."""
+    x = inputs.normal_np(11, 3, 0, 128 * 256).reshape(128, 256)
+    x[:, 37] = 0.0
+    r = sinkhorn.balance(x, 16)
+    assert r["lc_raw"][37] == 0.0
+    assert np.all(np.isfinite(r["lc_raw"])) and np.all(np.isfinite(r["C"].astype(np.float64)))
+    y = x * np.exp(-r["lr"][:, None] - r["lc_raw"][None, :])
+    sd = y.std(axis=0)
+    assert abs(sd[37]) == 0.0 and np.allclose(np.delete(sd, 37), 1.0, atol=1e-12)
+
+
 def test_nibble_order_every_position_and_value():
     rng = np.random.default_rng(1)
     for bits, rows, cols in ((4, 128, 256), (4, 256, 128), (8, 128, 128)):

@@ -17,10 +17,14 @@ Readings:
 * log-domain state: lr (per row) and lc (per column), with
   y_ij = x_ij * exp(-lr_i - lc_j); a row pass sets lr_i += ln sigma_i where
   sigma_i is the spread of row i of y; a column pass does the same for lc;
-* a row or column whose spread is zero (at most 1e-30) cannot be balanced and
-  keeps its scale (its log scale is not updated): an all-zero tile keeps unit
-  scales.  Adding ln of a floor instead would grow the log scales of such a
-  row or column by ~69 per pass until exp overflows;
+* a row or column whose spread is zero cannot be balanced and keeps its scale
+  (its log scale is not updated): an all-zero tile keeps unit scales.  Adding
+  ln of a floor instead would grow the log scales of such a row or column by
+  ~69 per pass until exp overflows.  "Zero" is sigma <= 1e-30 or
+  sigma^2 <= 2^-16 mean(y^2) (a spread under 1/256 of the RMS): the fp32
+  one-pass form E[y^2] - mean^2 with 22-bit factors errs by up to ~2^-20
+  mean(y^2), so below that a spread cannot be told from zero and a row or
+  column of identical values (repeated tokens) must read as constant;
 * scale absorption: the row factors are not stored (each row gets its own
   rounding scale and zero point afterwards, which absorbs them); the column
   factors are kept as C_j = fp16(exp(lc_j)) after centring lc to mean zero
@@ -34,6 +38,7 @@ from __future__ import annotations
 import numpy as np
 
 LOG_FLOOR = 1e-30
+ZERO_SPREAD_REL = 2.0 ** -16  # sigma^2 / mean(y^2) at or below which a spread counts as zero
 LC_CLAMP = 9.0
 
 
@@ -46,12 +51,14 @@ def balance(x, passes: int):
     lc = np.zeros(cols)
     for p in range(passes):
         y = x * np.exp(-lr[:, None] - lc[None, :])
-        if p % 2 == 0:
-            sigma = y.std(axis=1)
-            lr = lr + np.where(sigma > LOG_FLOOR, np.log(np.maximum(sigma, LOG_FLOOR)), 0.0)
+        ax = 1 if p % 2 == 0 else 0
+        sigma = y.std(axis=ax)
+        upd = (sigma > LOG_FLOOR) & (sigma * sigma > ZERO_SPREAD_REL * (y * y).mean(axis=ax))
+        step = np.where(upd, np.log(np.maximum(sigma, LOG_FLOOR)), 0.0)
+        if ax == 1:
+            lr = lr + step
         else:
-            sigma = y.std(axis=0)
-            lc = lc + np.where(sigma > LOG_FLOOR, np.log(np.maximum(sigma, LOG_FLOOR)), 0.0)
+            lc = lc + step
     lc_c = np.clip(lc - lc.mean(), -LC_CLAMP, LC_CLAMP)
     C = np.exp(lc_c).astype(np.float16)
     return {"lr": lr, "lc_raw": lc, "lc": lc_c, "C": C}

@@ -23,9 +23,10 @@
 // both copies stay in registers (the second is built through a transposed tile
 // in LDS).  The updated side's factor is 1/spread (equal to exp(-l) of the
 // log-domain update l += ln spread, spread the population standard deviation);
-// a row or column whose spread is zero keeps its factor and log scale (it
-// cannot be balanced: an all-zero tile keeps unit scales); the factors pass
-// between waves through LDS, one barrier per pass.
+// a row or column whose spread is zero (kZeroSpread) keeps its factor and log
+// scale (it cannot be balanced: an all-zero tile keeps unit scales, constant
+// columns of repeated tokens keep theirs); the factors pass between waves
+// through LDS, one barrier per pass.
 //
 // The balancing factors (1/spread, ln spread) use the hardware square root,
 // reciprocal and log2 (about 1 ulp): only the column scales C leave the
@@ -45,6 +46,12 @@ namespace kvq {
 // reaches the cap, which then keeps its products finite; its log scale still
 // comes from its spread.
 constexpr float kFactorMax = 255.0f;
+// A spread counts as zero (the row or column keeps its scale) when it is at most
+// 1e-30 or its square at most 2^-16 of the mean square (under 1/256 of the
+// RMS): the one-pass variance E[y^2] - mean^2 from 22-bit factors errs by up to
+// ~2^-20 E[y^2], so below that it cannot tell a spread from zero, and a row or
+// column of identical values must read as constant.
+constexpr float kZeroSpread = 1.52587890625e-05f;  // 2^-16
 
 template <int SUBW>
 struct SealShape {
@@ -269,7 +276,8 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
       const float mean = s1 / (float)SUBW;
       const float var = fmaxf(s2 / (float)SUBW - mean * mean, 0.0f);
       const float sd = __builtin_amdgcn_sqrtf(var);
-      const float rf = sd > 1e-30f ? __builtin_amdgcn_rcpf(sd) : rf_keep;
+      const bool upd = sd > 1e-30f && var > kZeroSpread * (s2 / (float)SUBW);
+      const float rf = upd ? __builtin_amdgcn_rcpf(sd) : rf_keep;
       rf_keep = rf;
       if ((m & 1) == 0) {
 #pragma unroll
@@ -314,7 +322,7 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
         const float mean = x1 / (float)kGroup;
         const float var = fmaxf(x2 / (float)kGroup - mean * mean, 0.0f);
         const float sig = __builtin_amdgcn_sqrtf(var);
-        const bool upd = sig > 1e-30f;
+        const bool upd = sig > 1e-30f && var > kZeroSpread * (x2 / (float)kGroup);
         const float cf = upd ? fminf(__builtin_amdgcn_rcpf(sig), kFactorMax) : cf_keep[e];
         const float lc = upd ? __builtin_amdgcn_logf(sig) * 0.6931471805599453f : lc_keep[e];  // log2 -> ln
         cf_keep[e] = cf;

@@ -381,15 +381,18 @@ def test_degenerate_inputs():
     """The method's degenerate cases through append, seal and decode, against
     the oracle: all-zero tokens (tq6_0 scale 0, an all-zero tile through the
     balancing, row scale 0 read as 1), a one-token sequence (the output is its
-    value), and keys with channels far above the rest (+-2,000, and +-60,000
+    value), one token repeated 1,000 times (constant columns: they keep their
+    scales), and keys with channels far above the rest (+-2,000, and +-60,000
     near the fp16 maximum); sink and ring bytes exact, records by the
     conditional rule, attention within tolerance."""
     w = configs.QWEN27B.scaled(n_layers=1, n_kv_heads=2, n_q_heads=8, tail_min=256, tail_max=384, ctx=1000)
-    lens = [1000, 1, 1000, 1000]
+    lens = [1000, 1, 1000, 1000, 1000]
     p = Pair(w, lens, extra_ctx=4)
     H, D = w.n_kv_heads, w.head_dim
     zeros = np.zeros((lens[0], H, D), dtype=np.float16)
     p.kv[(0, 0)] = (zeros, zeros.copy())
+    k4, v4 = (np.repeat(a[:1], lens[4], axis=0) for a in p.kv[(4, 0)])  # one token repeated
+    p.kv[(4, 0)] = (k4, v4)
     for s, big in ((2, 2000.0), (3, 60000.0)):
         k, v = (a.copy() for a in p.kv[(s, 0)])
         k[:, :, 7] = np.where(np.arange(lens[s]) % 2 == 0, big, -big)[:, None].astype(np.float16)
@@ -413,6 +416,10 @@ def test_degenerate_inputs():
         one = p.kv[(1, 0)][1][0].astype(np.float64)                           # [H][D]
         want = np.repeat(one, w.n_q_heads // H, axis=0)
         assert np.abs(got[1] - want).max() <= 1e-6 * np.abs(want).max(), path
+        ref4 = p.ora.attention(0, 4, q[4], 1.0)
+        err4 = float(np.max(np.abs(got[4] - ref4)) / np.sqrt(np.mean(ref4 ** 2)))
+        _say(f"[degenerate] path={path} repeated token err={err4:.2e}")
+        assert err4 <= ATTN_TOL
         for s, tol in ((2, ATTN_TOL), (3, 1e-2)):
             # +-60,000 keys: the score's two terms S (q~ . code) and Z sigma
             # reach ~1e5 in fp32 while their sum is ~1e3, so the score carries

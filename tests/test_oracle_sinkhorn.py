@@ -151,6 +151,23 @@ def test_zero_column_keeps_its_scale():
     assert abs(sd[37]) == 0.0 and np.allclose(np.delete(sd, 37), 1.0, atol=1e-12)
 
 
+def test_identical_rows_keep_column_scales():
+    """A tile of identical rows (repeated tokens) has constant columns: they
+    keep lc = 0, so C = 1; the rows (all alike) are balanced."""
+    row = inputs.normal_np(12, 3, 0, 256)
+    r = sinkhorn.balance(np.tile(row, (128, 1)), 16)
+    assert np.all(r["lc_raw"] == 0.0) and np.all(r["C"] == np.float16(1.0))
+    assert np.allclose(r["lr"], np.log(row.std()), atol=1e-12)
+    # the same rows with one column perturbed by +-2^-10 of its value (a spread
+    # under 2^-8 of the RMS): it counts as constant too; by +-2^-4, it does not
+    alt = np.where(np.arange(128) % 2 == 0, 1.0, -1.0)
+    for rel, const in ((2.0 ** -10, True), (2.0 ** -4, False)):
+        x = np.tile(row, (128, 1))
+        x[:, 10] = row[10] * (1.0 + rel * alt)
+        lc = sinkhorn.balance(x, 16)["lc_raw"]
+        assert (lc[10] == 0.0) == const and (not const or np.all(lc == 0.0))
+
+
 def test_nibble_order_every_position_and_value():
     rng = np.random.default_rng(1)
     for bits, rows, cols in ((4, 128, 256), (4, 256, 128), (8, 128, 128)):

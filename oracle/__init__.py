@@ -27,7 +27,9 @@ section):
   Tail, section 2).
 * ``sizes``     -- the bytes-per-token and effective-bits arithmetic the pages
   print (SJ-KVaRN sections 1, 3, 7.2, 8.4; KV cache math; HAL #582 section 1).
-* ``tbq4``      -- the TBQ4 comparator block (KV cache math), oracle only.
+* ``tbq4``      -- the TBQ4 comparator codec: 128-point randomized
+  Walsh-Hadamard rotation, fp16 norm, 16 Lloyd-Max centroids of N(0, 1/128),
+  66-byte blocks (KV cache math, "rotate first" and the size table).
 
 Where the pages leave a step open, the plainest reading is taken and stated
 in the function that implements it.

@@ -232,6 +232,56 @@ def run_seal(args, w, torch, kvq, synthetic):
     return {"ms": ms, "tokens": tokens, "tokens_per_s": tokens / (ms * 1e-3), "tiles": tiles, "tflops": tflops}
 
 
+def run_tbq4(args, w, torch, kvq, inputs, sealed_us):
+    """The TBQ4 comparator at the same shape: one layer of every sequence held
+    whole as TBQ4 blocks (66 bytes per 128 values; no sink, ring or exact
+    tail), one fused rotated-domain decode per call, timed with HIP events on
+    the current stream over `steps` calls after `warmup`; the encoder is timed
+    the same way over the layer's keys.  Bytes per call = the K and V blocks
+    of every token (all decoded), partial rows excluded."""
+    n, h, hq, d, t = w.n_seqs, w.n_kv_heads, w.n_q_heads, w.head_dim, w.ctx
+    if d not in (128, 256):
+        log(f"[bench] TBQ4 comparator skipped: head_dim {d}")
+        return None
+    nb = d // 128
+    words = inputs.signs_to_words(inputs.rotation_signs(7))
+    dev = "cuda"
+    kv = [inputs.normal_t(70 + i, 140, 0, n * h * t * d, dev).to(torch.float16).view(-1, 128) for i in range(2)]
+    blocks = [torch.empty((n, h, t, nb, 66), dtype=torch.uint8, device=dev) for _ in range(2)]
+    q = inputs.normal_t(72, 141, 0, n * hq * d, dev).to(torch.float16).view(n, hq, d)
+    lens = [t] * n
+    ws = torch.empty(kvq.tbq4_workspace_bytes(n, hq, h, d, t), dtype=torch.uint8, device=dev)
+    out = torch.empty((n, hq, d), dtype=torch.float32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for i in range(2):
+        kvq.tbq4_encode(kv[i], words, out=blocks[i])
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(max(1, args.steps // 5)):
+        kvq.tbq4_encode(kv[0], words, out=blocks[0])
+    ev[1].record()
+    for _ in range(args.warmup):
+        kvq.tbq4_attn_decode(q, blocks[0], blocks[1], lens, words, 1.0 / d ** 0.5, out=out, workspace=ws)
+    ev[2].record()
+    for _ in range(args.steps):
+        kvq.tbq4_attn_decode(q, blocks[0], blocks[1], lens, words, 1.0 / d ** 0.5, out=out, workspace=ws)
+    ev[3].record()
+    torch.cuda.synchronize()
+    enc_us = ev[0].elapsed_time(ev[1]) * 1e3 / max(1, args.steps // 5)
+    dec_us = ev[2].elapsed_time(ev[3]) * 1e3 / args.steps
+    nbytes = 2 * n * h * t * nb * 66
+    gbs = nbytes / (dec_us * 1e-6) / 1e9
+    vals = n * h * t * d
+    log(f"[bench] TBQ4 comparator: {nbytes / 1e6:.1f} MB per layer, fused decode {dec_us:.1f} us "
+        f"({gbs:.1f} GB/s, {gbs / HBM_PEAK_GBS:.3f} of HBM peak) vs sealed-cache decode kernel {sealed_us:.1f} us; "
+        f"encode {vals / (enc_us * 1e-6) / 1e9:.2f} G values/s")
+    del kv, blocks
+    return {"bytes_per_call": nbytes, "decode_us": round(dec_us, 2), "gbs": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "sealed_decode_kernel_us": round(sealed_us, 2),
+            "encode_gvalues_per_s": round(vals / (enc_us * 1e-6) / 1e9, 2),
+            "note": "whole layer as TBQ4 blocks, fused rotated-domain decode incl. merge"}
+
+
 def run_cpu_baseline(w, budget_s):
     """The oracle as it stands, single thread, on a bounded sample: one layer and
     one KV head of the same shape at a shorter context (decode), and a few
@@ -297,6 +347,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle decode timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-seal", action="store_true")
+    ap.add_argument("--no-tbq4", action="store_true", help="skip the TBQ4 comparator leg")
     ap.add_argument("--save-restore", action="store_true",
                     help="also time saving and restoring sequence 0 to and from host memory (kvq_seq_save/_restore)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -326,6 +377,7 @@ def main():
          "batched": configs.BATCHED}[args.workload]
     dec = run_decode(args, w, torch, kvq, synthetic, inputs)
     seal = None if args.no_seal else run_seal(args, w, torch, kvq, synthetic)
+    tbq = None if args.no_tbq4 else run_tbq4(args, w, torch, kvq, inputs, dec["avg_kernel_us"])
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(w, args.cpu_budget)
     mfma_body = args.path != "valu"
     traffic = measured_traffic() if (args.workload == "qwen27b" and mfma_body) else None
@@ -373,6 +425,8 @@ def main():
             "roofline": {"bound": "alu", "achieved": round(seal["tflops"], 3), "peak": FP32_VALU_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(seal["tflops"] / FP32_VALU_PEAK_TFLOPS, 4)},
         }
+    if tbq:
+        res["tbq4_comparator"] = tbq
     print(json.dumps(res), flush=True)
 
 

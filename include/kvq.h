@@ -245,6 +245,45 @@ kvq_status kvq_unit_bytes(const kvq_cache* cache, int32_t region, size_t* bytes)
 kvq_status kvq_profile_start(kvq_cache* cache, int32_t max_calls);
 kvq_status kvq_profile_stop(kvq_cache* cache, float* us, int32_t* n_calls);
 
+/* TBQ4 comparator format (KV cache math: "rotate first", the fused
+ * rotated-domain decode, and the format table).  A block holds 128 values:
+ * y = R x with R the randomized Walsh-Hadamard transform (flip signs s1,
+ * Walsh-Hadamard transform in natural order, multiply by 1/sqrt(128), flip
+ * signs s2), norm = fp16(|y|), and per value the 4-bit index of the nearest
+ * of 16 centroids (the Lloyd-Max quantiser of N(0, 1/128); ties go to the
+ * lower index).  Bytes: [fp16 norm, little-endian][64 bytes of indices, value
+ * 2j in the low nibble of byte j, 2j+1 in the high], 66 bytes per block.
+ * signs: host, four words in the layout of kvq_config.rot_signs.
+ *
+ * kvq_tbq4_tables: host only, no device needed.  centroids (16 floats,
+ * ascending) and boundaries (15 floats, the midpoints) are host outputs;
+ * either may be NULL, not both.
+ * kvq_tbq4_encode: x device fp16 [n][128]; blocks device [n][66].
+ * kvq_tbq4_decode: blocks device [n][66]; out device fp32 [n][128], the
+ * original domain (R^T of centroid x norm).
+ * kvq_tbq4_attn_decode: one decode step over a TBQ4 cache, the query rotated
+ * once, keys and values read as centroid x norm, every split-K partial
+ * rotated back once, then merged under one softmax.  q device fp16
+ * [n_seqs][n_q_heads][head_dim] (query head i reads KV head i / g, g =
+ * n_q_heads / n_kv_heads <= 16); k_blocks, v_blocks device
+ * [n_seqs][n_kv_heads][cap][head_dim / 128][66] (head_dim 128 or 256; each
+ * 128-value block is its own TBQ4 block); seq_len host, n_seqs tokens counts
+ * in 1 .. cap; out device [n_seqs][n_q_heads][head_dim] fp32 or fp16
+ * (out_dtype); softmax(scale q.k).  workspace device, ws_bytes >=
+ * kvq_tbq4_workspace_bytes(n_seqs, ..., max_len) for any max_len >= the
+ * longest seq_len.  All work is queued on `stream`; nothing waits.
+ * Errors: KVQ_ERR_INVALID (range or NULL), KVQ_ERR_UNSUPPORTED (head_dim),
+ * KVQ_ERR_CAPACITY (workspace), KVQ_ERR_DEVICE. */
+kvq_status kvq_tbq4_tables(float* centroids, float* boundaries);
+kvq_status kvq_tbq4_encode(const void* x, int64_t n, const uint64_t* signs, void* blocks, void* stream);
+kvq_status kvq_tbq4_decode(const void* blocks, int64_t n, const uint64_t* signs, float* out, void* stream);
+kvq_status kvq_tbq4_workspace_bytes(int32_t n_seqs, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                    int64_t max_len, size_t* bytes);
+kvq_status kvq_tbq4_attn_decode(const void* q, const void* k_blocks, const void* v_blocks, int32_t n_seqs,
+                                int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int64_t cap,
+                                const int64_t* seq_len, const uint64_t* signs, float scale, void* out,
+                                int32_t out_dtype, void* workspace, size_t ws_bytes, void* stream);
+
 const char* kvq_status_string(kvq_status status);
 const char* kvq_last_error(void);
 

@@ -87,7 +87,8 @@ def tables():
 def encode(x16, signs):
     """x16: fp16 (n, 128) -> (norm fp16 (n,), idx uint8 (n, 128))."""
     y = rotation.rotate(np.asarray(x16, np.float16), DIM, signs).astype(np.float32)
-    norm = np.sqrt((y.astype(np.float64) ** 2).sum(axis=-1)).astype(np.float16)
+    with np.errstate(over="ignore"):  # a norm past the fp16 range is stored as infinity
+        norm = np.sqrt((y.astype(np.float64) ** 2).sum(axis=-1)).astype(np.float16)
     nf = norm.astype(np.float32)
     inv = np.where(nf > 0, np.float32(1.0) / np.where(nf > 0, nf, np.float32(1.0)), np.float32(0.0)).astype(np.float32)
     v = (y * inv[:, None]).astype(np.float32)

@@ -115,4 +115,33 @@ struct MergeArgs {
   int32_t n_chunks[kMaxLaunchSeqs];
 };
 
+// TBQ4 comparator block (KV cache math): [fp16 norm][64 bytes of 4-bit
+// indices, even value in the low nibble] per 128 rotated values.
+constexpr int kTbqBytes = 66;
+
+struct Tbq4CodecArgs {
+  const uint16_t* x;         // encode input: fp16 [n][128]
+  uint8_t* blocks_out;       // encode output: [n][66]
+  const uint8_t* blocks_in;  // decode input: [n][66]
+  float* y;                  // decode output: fp32 [n][128], original domain
+  int64_t n;
+  float cent[16];            // centroids, ascending
+  float bnd[16];             // cell boundaries (15 used)
+  uint32_t signs[8];         // bit i set: entry i of [s1 (128); s2 (128)] is -1
+};
+
+struct Tbq4AttnArgs {
+  const uint16_t* q;         // fp16 [n_seqs][Hq][D]
+  const uint8_t* kb;         // [n_seqs][H][cap][D / 128][66]
+  const uint8_t* vb;
+  float* qr;                 // workspace: rotated, scaled queries fp32 [n_seqs][Hq][D]
+  float* part;               // [n_seqs][Hq][max_chunks][part_stride(D)]
+  int64_t cap;
+  float scale_log2;          // softmax scale times log2(e)
+  int32_t D, H, Hq, g, n_seqs, max_chunks, chunk, pad;
+  float cent[16];
+  uint32_t signs[8];
+  int64_t len[kMaxLaunchSeqs];  // tokens per sequence (1 .. cap)
+};
+
 }  // namespace kvq

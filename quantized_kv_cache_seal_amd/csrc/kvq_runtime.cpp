@@ -23,6 +23,9 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int grid_x, hipStream_t strea
 hipError_t launch_decode_main(const DecodeArgs& a, int n_items, hipStream_t stream);
 hipError_t launch_decode_ring(const DecodeArgs& a, int n_items, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_tbq4_encode(const Tbq4CodecArgs& a, hipStream_t stream);
+hipError_t launch_tbq4_decode(const Tbq4CodecArgs& a, hipStream_t stream);
+hipError_t launch_tbq4_attn(const Tbq4AttnArgs& a, int grid_x, hipStream_t stream);
 }  // namespace kvq
 
 using namespace kvq;
@@ -856,6 +859,206 @@ kvq_status kvq_import(kvq_cache* c, int32_t seq, int32_t layer, int32_t h, int32
   kvq_status st = check_unit(c, seq, layer, h, region, index, host_src, bytes);
   if (st != KVQ_OK) return st;
   return copy_unit(c, seq, layer, h, region, index, (uint8_t*)host_src, false, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// TBQ4 comparator codec and its fused rotated-domain decode.
+
+namespace {
+
+struct Tbq4Tables {
+  float cent[16], bnd[15];
+};
+
+// Lloyd-Max quantiser of N(0, 1/128) with 16 levels: alternate "each cell
+// boundary is the midpoint of its two levels" and "each level is the mean of
+// its cell" until the levels stop moving.  The quantiser is symmetric, so the
+// iteration runs on the 8 positive levels of the unit Gaussian (the middle
+// boundary is 0) and scales by 1/sqrt(128) at the end, in binary64.
+const Tbq4Tables& tbq4_tables() {
+  static const Tbq4Tables t = [] {
+    const double inv_sqrt2pi = 0.39894228040143267794, inv_sqrt2 = 0.70710678118654752440;
+    auto pdf = [&](double z) { return std::isinf(z) ? 0.0 : inv_sqrt2pi * std::exp(-0.5 * z * z); };
+    double c[8];
+    for (int k = 0; k < 8; ++k) c[k] = 0.375 * (k + 0.5);
+    for (int it = 0; it < 200000; ++it) {
+      double bd[9];
+      bd[0] = 0.0;
+      for (int k = 1; k < 8; ++k) bd[k] = 0.5 * (c[k - 1] + c[k]);
+      bd[8] = INFINITY;
+      double moved = 0.0;
+      for (int k = 0; k < 8; ++k) {
+        const double mass = 0.5 * (std::erfc(bd[k] * inv_sqrt2) - std::erfc(bd[k + 1] * inv_sqrt2));
+        const double nc = (pdf(bd[k]) - pdf(bd[k + 1])) / mass;
+        moved = std::max(moved, std::fabs(nc - c[k]));
+        c[k] = nc;
+      }
+      if (moved <= 1e-15) break;
+    }
+    const double sigma = 1.0 / std::sqrt(128.0);
+    double lv[16];
+    for (int k = 0; k < 8; ++k) {
+      lv[8 + k] = c[k] * sigma;
+      lv[7 - k] = -c[k] * sigma;
+    }
+    Tbq4Tables r{};
+    for (int k = 0; k < 16; ++k) r.cent[k] = (float)lv[k];
+    for (int k = 0; k < 15; ++k) r.bnd[k] = (float)(0.5 * (lv[k] + lv[k + 1]));
+    return r;
+  }();
+  return t;
+}
+
+void tbq4_signs(const uint64_t* s, uint32_t* out) {
+  for (int w = 0; w < 4; ++w) {
+    out[2 * w] = (uint32_t)(s[w] & 0xFFFFFFFFu);
+    out[2 * w + 1] = (uint32_t)(s[w] >> 32);
+  }
+}
+
+// Split-K chunking of a TBQ4 decode: about 4096 workgroups per launch, whole
+// passes of 64 tokens.  The chunk count grows with max_len, so a workspace
+// sized for a bound on the length fits every shorter batch.
+int64_t tbq4_chunk_count(int32_t n_seqs, int32_t H, int64_t max_len) {
+  const int64_t per_launch = std::min<int32_t>(n_seqs, kMaxLaunchSeqs) * (int64_t)H;
+  const int64_t target = std::min<int64_t>(kMaxChunks, std::max<int64_t>(1, 4096 / std::max<int64_t>(1, per_launch)));
+  return std::min<int64_t>((max_len + 63) / 64, target);
+}
+
+// Workspace: the rotated queries (fp32, 256-byte aligned span), then the
+// split-K partial rows.
+size_t tbq4_qr_bytes(int32_t n_seqs, int32_t Hq, int32_t D) {
+  return (size_t)round_up((int64_t)n_seqs * Hq * D * (int64_t)sizeof(float), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_tbq4_tables(float* centroids, float* boundaries) {
+  if (!centroids && !boundaries) return fail(KVQ_ERR_INVALID, "no output");
+  const Tbq4Tables& t = tbq4_tables();
+  if (centroids) std::memcpy(centroids, t.cent, sizeof t.cent);
+  if (boundaries) std::memcpy(boundaries, t.bnd, sizeof t.bnd);
+  return KVQ_OK;
+}
+
+kvq_status kvq_tbq4_encode(const void* x, int64_t n, const uint64_t* signs, void* blocks, void* stream) {
+  if (n < 0 || !signs || (n > 0 && (!x || !blocks))) return fail(KVQ_ERR_INVALID, "bad TBQ4 encode arguments");
+  if (n == 0) return KVQ_OK;
+  Tbq4CodecArgs a{};
+  a.x = (const uint16_t*)x;
+  a.blocks_out = (uint8_t*)blocks;
+  a.n = n;
+  const Tbq4Tables& t = tbq4_tables();
+  std::memcpy(a.cent, t.cent, sizeof t.cent);
+  std::memcpy(a.bnd, t.bnd, sizeof t.bnd);
+  tbq4_signs(signs, a.signs);
+  hipError_t e = launch_tbq4_encode(a, (hipStream_t)stream);
+  return e == hipSuccess ? KVQ_OK : hip_fail(e, "TBQ4 encode launch");
+}
+
+kvq_status kvq_tbq4_decode(const void* blocks, int64_t n, const uint64_t* signs, float* out, void* stream) {
+  if (n < 0 || !signs || (n > 0 && (!blocks || !out))) return fail(KVQ_ERR_INVALID, "bad TBQ4 decode arguments");
+  if (n == 0) return KVQ_OK;
+  Tbq4CodecArgs a{};
+  a.blocks_in = (const uint8_t*)blocks;
+  a.y = out;
+  a.n = n;
+  const Tbq4Tables& t = tbq4_tables();
+  std::memcpy(a.cent, t.cent, sizeof t.cent);
+  tbq4_signs(signs, a.signs);
+  hipError_t e = launch_tbq4_decode(a, (hipStream_t)stream);
+  return e == hipSuccess ? KVQ_OK : hip_fail(e, "TBQ4 decode launch");
+}
+
+static kvq_status tbq4_check_shape(int32_t n_seqs, int32_t Hq, int32_t H, int32_t D) {
+  if (n_seqs < 0) return fail(KVQ_ERR_INVALID, "n_seqs < 0");
+  if (D != 128 && D != 256) return fail(KVQ_ERR_UNSUPPORTED, "TBQ4 decode takes head_dim 128 or 256, not %d", D);
+  if (H < 1 || Hq < H || Hq % H != 0 || Hq / H > kMaxGroup)
+    return fail(KVQ_ERR_INVALID, "n_q_heads must be 1 .. %d times n_kv_heads", kMaxGroup);
+  return KVQ_OK;
+}
+
+kvq_status kvq_tbq4_workspace_bytes(int32_t n_seqs, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                    int64_t max_len, size_t* bytes) {
+  kvq_status st = tbq4_check_shape(n_seqs, n_q_heads, n_kv_heads, head_dim);
+  if (st != KVQ_OK) return st;
+  if (!bytes || max_len < 1) return fail(KVQ_ERR_INVALID, "bad TBQ4 workspace arguments");
+  *bytes = tbq4_qr_bytes(n_seqs, n_q_heads, head_dim) +
+           (size_t)n_seqs * n_q_heads * tbq4_chunk_count(n_seqs, n_kv_heads, max_len) * part_stride(head_dim) *
+               sizeof(float);
+  return KVQ_OK;
+}
+
+kvq_status kvq_tbq4_attn_decode(const void* q, const void* k_blocks, const void* v_blocks, int32_t n_seqs,
+                                int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int64_t cap,
+                                const int64_t* seq_len, const uint64_t* signs, float scale, void* out,
+                                int32_t out_dtype, void* workspace, size_t ws_bytes, void* stream) {
+  kvq_status st = tbq4_check_shape(n_seqs, n_q_heads, n_kv_heads, head_dim);
+  if (st != KVQ_OK || n_seqs == 0) return st;
+  if (!q || !k_blocks || !v_blocks || !seq_len || !signs || !out || !workspace || cap < 1)
+    return fail(KVQ_ERR_INVALID, "bad TBQ4 decode arguments");
+  if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_F16) return fail(KVQ_ERR_INVALID, "bad out_dtype");
+  int64_t max_len = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    if (seq_len[i] < 1 || seq_len[i] > cap)
+      return fail(KVQ_ERR_INVALID, "seq_len[%d] = %lld is outside 1 .. cap", i, (long long)seq_len[i]);
+    max_len = std::max(max_len, seq_len[i]);
+  }
+  const int32_t H = n_kv_heads, Hq = n_q_heads, D = head_dim, NB = D / 128;
+  const int64_t nc = tbq4_chunk_count(n_seqs, H, max_len);
+  const int64_t chunk = round_up((max_len + nc - 1) / nc, 64);
+  const int64_t max_chunks = (max_len + chunk - 1) / chunk;
+  if (chunk > 0x7FFFFFFF) return fail(KVQ_ERR_CAPACITY, "sequence too long");
+  const size_t qr_bytes = tbq4_qr_bytes(n_seqs, Hq, D);
+  const size_t need = qr_bytes + (size_t)n_seqs * Hq * max_chunks * part_stride(D) * sizeof(float);
+  if (ws_bytes < need) return fail(KVQ_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  const Tbq4Tables& t = tbq4_tables();
+  float* qr_all = (float*)workspace;
+  float* part_all = (float*)((uint8_t*)workspace + qr_bytes);
+  const size_t out_elem = out_dtype == KVQ_OUT_F16 ? 2 : 4;
+  const int64_t head_bytes = cap * NB * kTbqBytes;
+  for (int b0 = 0; b0 < n_seqs; b0 += kMaxLaunchSeqs) {
+    Tbq4AttnArgs a{};
+    a.n_seqs = std::min(kMaxLaunchSeqs, n_seqs - b0);
+    a.q = (const uint16_t*)q + (int64_t)b0 * Hq * D;
+    a.kb = (const uint8_t*)k_blocks + (int64_t)b0 * H * head_bytes;
+    a.vb = (const uint8_t*)v_blocks + (int64_t)b0 * H * head_bytes;
+    a.qr = qr_all + (int64_t)b0 * Hq * D;
+    a.part = part_all + (int64_t)b0 * Hq * max_chunks * part_stride(D);
+    a.cap = cap;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.D = D;
+    a.H = H;
+    a.Hq = Hq;
+    a.g = Hq / H;
+    a.max_chunks = (int32_t)max_chunks;
+    a.chunk = (int32_t)chunk;
+    std::memcpy(a.cent, t.cent, sizeof t.cent);
+    tbq4_signs(signs, a.signs);
+    MergeArgs m{};
+    int grid_x = 1;
+    for (int b = 0; b < a.n_seqs; ++b) {
+      a.len[b] = seq_len[b0 + b];
+      m.n_chunks[b] = (int32_t)((a.len[b] + chunk - 1) / chunk);
+      grid_x = std::max(grid_x, m.n_chunks[b]);
+    }
+    hipError_t e = launch_tbq4_attn(a, grid_x, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "TBQ4 decode launch");
+    m.part = a.part;
+    m.out = (uint8_t*)out + (size_t)b0 * Hq * D * out_elem;
+    m.D = D;
+    m.Hq = Hq;
+    m.n_seqs = a.n_seqs;
+    m.max_chunks = a.max_chunks;
+    m.out_f16 = out_dtype == KVQ_OUT_F16;
+    e = launch_merge(m, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  return KVQ_OK;
 }
 
 }  // extern "C"

@@ -25,6 +25,7 @@ EXPORTS = [
     "kvq_workspace_bytes", "kvq_attn_decode", "kvq_decode_step", "kvq_set_decode_path", "kvq_seq_info", "kvq_seq_reset",
     "kvq_seq_truncate", "kvq_seq_save_bytes", "kvq_seq_save", "kvq_seq_restore", "kvq_export", "kvq_import",
     "kvq_unit_bytes", "kvq_profile_start", "kvq_profile_stop",
+    "kvq_tbq4_tables", "kvq_tbq4_encode", "kvq_tbq4_decode", "kvq_tbq4_workspace_bytes", "kvq_tbq4_attn_decode",
     "kvq_status_string", "kvq_last_error",
 ]
 
@@ -78,6 +79,12 @@ def lib():
             "kvq_unit_bytes": [vp, i32, P(sz)],
             "kvq_profile_start": [vp, i32],
             "kvq_profile_stop": [vp, P(ctypes.c_float), P(i32)],
+            "kvq_tbq4_tables": [P(ctypes.c_float), P(ctypes.c_float)],
+            "kvq_tbq4_encode": [vp, i64, P(ctypes.c_uint64), vp, vp],
+            "kvq_tbq4_decode": [vp, i64, P(ctypes.c_uint64), vp, vp],
+            "kvq_tbq4_workspace_bytes": [i32, i32, i32, i32, i64, P(sz)],
+            "kvq_tbq4_attn_decode": [vp, vp, vp, i32, i32, i32, i32, i64, P(i64), P(ctypes.c_uint64),
+                                     ctypes.c_float, vp, i32, vp, sz, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -288,3 +295,74 @@ def config_for(w, max_ctx=None, max_seqs=None, sign_words=(0, 0, 0, 0), flags=0)
                        max_seqs if max_seqs is not None else w.n_seqs,
                        max_ctx if max_ctx is not None else w.ctx, w.tail_min, w.tail_max, w.margin,
                        w.k_bits, w.v_bits, w.passes, sign_words, flags)
+
+
+# --- TBQ4 comparator codec ---------------------------------------------------
+
+TBQ4_BLOCK_BYTES = 66
+
+
+def _words(sign_words):
+    w = (ctypes.c_uint64 * 4)(*[int(x) for x in sign_words])
+    return w
+
+
+def tbq4_tables():
+    """(centroids[16], boundaries[15]) as float32 numpy arrays (host only)."""
+    import numpy as np
+    c = (ctypes.c_float * 16)()
+    b = (ctypes.c_float * 15)()
+    check(lib().kvq_tbq4_tables(c, b))
+    return np.array(c, np.float32), np.array(b, np.float32)
+
+
+def tbq4_encode(x, sign_words, out=None, stream=None):
+    """x: fp16 device tensor (..., 128) -> uint8 device tensor (n, 66)."""
+    import torch
+    assert x.dtype == torch.float16 and x.is_contiguous() and x.shape[-1] == 128
+    n = x.numel() // 128
+    if out is None:
+        out = torch.empty((n, TBQ4_BLOCK_BYTES), dtype=torch.uint8, device=x.device)
+    assert out.dtype == torch.uint8 and out.is_contiguous() and out.numel() >= n * TBQ4_BLOCK_BYTES
+    check(lib().kvq_tbq4_encode(_ptr(x), n, _words(sign_words), _ptr(out), _stream(stream)))
+    return out
+
+
+def tbq4_decode(blocks, sign_words, out=None, stream=None):
+    """blocks: uint8 device tensor (n, 66) -> fp32 device tensor (n, 128)."""
+    import torch
+    assert blocks.dtype == torch.uint8 and blocks.is_contiguous() and blocks.numel() % TBQ4_BLOCK_BYTES == 0
+    n = blocks.numel() // TBQ4_BLOCK_BYTES
+    if out is None:
+        out = torch.empty((n, 128), dtype=torch.float32, device=blocks.device)
+    assert out.dtype == torch.float32 and out.is_contiguous() and out.numel() >= n * 128
+    check(lib().kvq_tbq4_decode(_ptr(blocks), n, _words(sign_words), _ptr(out), _stream(stream)))
+    return out
+
+
+def tbq4_workspace_bytes(n_seqs, n_q_heads, n_kv_heads, head_dim, max_len) -> int:
+    b = ctypes.c_size_t()
+    check(lib().kvq_tbq4_workspace_bytes(n_seqs, n_q_heads, n_kv_heads, head_dim, max_len, ctypes.byref(b)))
+    return b.value
+
+
+def tbq4_attn_decode(q, k_blocks, v_blocks, seq_len, sign_words, scale=1.0, out=None, out_f16=False,
+                     workspace=None, stream=None):
+    """q fp16 (n_seqs, Hq, D); k_blocks/v_blocks uint8 (n_seqs, H, cap, D // 128, 66)."""
+    import torch
+    n_seqs, hq, d = q.shape
+    assert q.dtype == torch.float16 and q.is_contiguous()
+    assert k_blocks.shape == v_blocks.shape and k_blocks.dtype == v_blocks.dtype == torch.uint8
+    assert k_blocks.is_contiguous() and v_blocks.is_contiguous()
+    _, h, cap, nb, bb = k_blocks.shape
+    assert k_blocks.shape[0] == n_seqs and nb * 128 == d and bb == TBQ4_BLOCK_BYTES
+    lens = (ctypes.c_int64 * n_seqs)(*[int(x) for x in seq_len])
+    if workspace is None:
+        workspace = torch.empty(max(1, tbq4_workspace_bytes(n_seqs, hq, h, d, max(int(x) for x in seq_len))),
+                                dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((n_seqs, hq, d), dtype=torch.float16 if out_f16 else torch.float32, device=q.device)
+    check(lib().kvq_tbq4_attn_decode(_ptr(q), _ptr(k_blocks), _ptr(v_blocks), n_seqs, hq, h, d, cap, lens,
+                                     _words(sign_words), float(scale), _ptr(out), 1 if out_f16 else 0,
+                                     _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out

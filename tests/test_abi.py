@@ -153,3 +153,33 @@ def test_save_bytes_and_plan_only_save():
     assert kvq.lib().kvq_seq_restore(c.h, 1, buf, b0, None) == kvq.ERR_UNSUPPORTED
     n = ctypes.c_size_t()
     assert kvq.lib().kvq_seq_save_bytes(c.h, 2, ctypes.byref(n)) == kvq.ERR_INVALID
+
+
+def test_tbq4_tables_match_oracle():
+    """The library's own Lloyd-Max iteration lands on the oracle's fp32 tables."""
+    from oracle import tbq4
+    c, b = kvq.tbq4_tables()
+    oc, ob = tbq4.tables()
+    assert np.array_equal(c, oc) and np.array_equal(b, ob)
+
+
+def test_tbq4_argument_errors():
+    L = kvq.lib()
+    sz = ctypes.c_size_t()
+    assert L.kvq_tbq4_workspace_bytes(1, 24, 4, 192, 100, ctypes.byref(sz)) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_tbq4_workspace_bytes(1, 20, 3, 128, 100, ctypes.byref(sz)) == kvq.ERR_INVALID
+    assert L.kvq_tbq4_workspace_bytes(1, 68, 4, 128, 100, ctypes.byref(sz)) == kvq.ERR_INVALID
+    assert L.kvq_tbq4_workspace_bytes(1, 24, 4, 256, 0, ctypes.byref(sz)) == kvq.ERR_INVALID
+    w = (ctypes.c_uint64 * 4)()
+    assert L.kvq_tbq4_encode(None, -1, w, None, None) == kvq.ERR_INVALID
+    assert L.kvq_tbq4_encode(None, 0, w, None, None) == kvq.OK
+    assert L.kvq_tbq4_decode(None, 5, w, None, None) == kvq.ERR_INVALID
+    lens = (ctypes.c_int64 * 1)(0)
+    assert L.kvq_tbq4_attn_decode(1, 1, 1, 1, 4, 4, 128, 8, lens, w, 1.0, 1, 0, 1, 1 << 20, None) \
+        == kvq.ERR_INVALID  # a sequence of length 0
+    # the chunk count never shrinks as the bound on the length grows
+    prev = 0
+    for n in (1, 63, 64, 65, 1000, 4096, 110592, 1 << 20):
+        assert L.kvq_tbq4_workspace_bytes(1, 24, 4, 256, n, ctypes.byref(sz)) == kvq.OK
+        assert sz.value >= prev and (sz.value - 24 * 256 * 4) % (24 * (256 + 4) * 4) == 0
+        prev = sz.value

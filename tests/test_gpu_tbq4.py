@@ -1,0 +1,157 @@
+"""TBQ4 comparator on the GPU (KV cache math: rotate first; fused rotated-domain
+decode) against the oracle codec and float64 attention."""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import attention, tbq4
+from quantized_kv_cache_seal_amd import inputs, kvq
+
+pytestmark = pytest.mark.gpu
+
+# fp32 scores and sums against float64 (decoded values identical on both
+# sides): score error <= ~D * 2^-24 * |q| |k| * scale, a few 1e-5 for these
+# inputs; output error below that times max |v|.
+TBQ_ATTN_TOL = 5e-4
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _x16(seed, n):
+    """Generic fp16 blocks: N(0, 1) times a per-block scale 2^-12 .. 2^6, plus edge blocks."""
+    z = inputs.normal_np(seed, 101, 0, n * 128).reshape(n, 128)
+    sc = 2.0 ** (-12 + 18 * inputs.uniform_np(seed, 102, 0, n))
+    x = (z * sc[:, None]).astype(np.float16)
+    edges = [np.zeros(128), np.full(128, 60000.0), np.eye(128)[5] * 3.0,
+             np.full(128, 2.0 ** -24) * np.where(np.arange(128) % 3 == 0, -1, 1),
+             np.linspace(-7.0, 7.0, 128)]
+    for i, e in enumerate(edges[: n]):
+        x[i] = e.astype(np.float16)
+    return x
+
+
+@pytest.mark.parametrize("n,seed", [(1, 1), (3, 2), (4, 3), (5, 4), (1001, 5)])
+def test_encode_bit_exact(n, seed):
+    torch = _torch()
+    s = inputs.rotation_signs(10 + seed)
+    w = inputs.signs_to_words(s)
+    x = _x16(seed, n)
+    _say(f"tbq4 encode n={n} seed={seed}")
+    got = kvq.tbq4_encode(torch.from_numpy(x).cuda(), w).cpu().numpy()
+    want = tbq4.pack(*tbq4.encode(x, s))
+    assert got.shape == want.shape == (n, 66)
+    bad = np.nonzero((got != want).any(axis=1))[0]
+    assert bad.size == 0, f"blocks differ: {bad[:10]}"
+
+
+def test_decode_matches_oracle():
+    torch = _torch()
+    s = inputs.rotation_signs(21)
+    w = inputs.signs_to_words(s)
+    x = _x16(22, 777)
+    x[1] = 0  # keep every norm finite
+    blocks = tbq4.pack(*tbq4.encode(x, s))
+    _say("tbq4 decode n=777")
+    got = kvq.tbq4_decode(torch.from_numpy(blocks).cuda(), w).cpu().numpy().astype(np.float64)
+    want = tbq4.decode(blocks, s)
+    norm = tbq4.unpack(blocks)[0].astype(np.float64)
+    # one fp32 rounding of centroid x norm, seven fp32 butterfly stages
+    assert np.all(np.abs(got - want) <= 4e-6 * norm[:, None])
+    assert np.all(got[0] == 0)
+
+
+def _kv(seed, n, h, cap, d):
+    """Keys N(0, 1) with 2% outlier channels x15 per head; values N(0, 1)."""
+    k = inputs.normal_np(seed, 111, 0, n * h * cap * d).reshape(n, h, cap, d)
+    for hh in range(h):
+        ch = inputs.outlier_channels(seed, 0, hh, d, max(1, d // 50))
+        k[:, hh, :, ch] *= 15.0
+    v = inputs.normal_np(seed, 112, 0, n * h * cap * d).reshape(n, h, cap, d)
+    return k.astype(np.float16), v.astype(np.float16)
+
+
+CASES = {
+    "d128_g5_ragged": (128, 2, 10, [1, 200, 1000], 1024),
+    "d256_g6": (256, 4, 24, [777, 64, 130], 800),
+    "d256_g16": (256, 1, 16, [513], 520),
+    "d128_g1": (128, 8, 8, [2000], 2000),
+    "d256_g3_many": (256, 2, 6, [5 + 37 * i for i in range(35)], 1300),
+}
+
+
+def _oracle_attn(q, kd, vd, lens, scale, g):
+    n, hq, d = q.shape
+    out = np.zeros((n, hq, d))
+    for b in range(n):
+        out[b] = attention.attend_gqa(q[b].astype(np.float64), [kd[b, hh, :lens[b]] for hh in range(kd.shape[1])],
+                                      [vd[b, hh, :lens[b]] for hh in range(kd.shape[1])], scale)
+    return out
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_fused_decode_matches_oracle(name):
+    torch = _torch()
+    d, h, hq, lens, cap = CASES[name]
+    n, nb = len(lens), d // 128
+    s = inputs.rotation_signs(31)
+    w = inputs.signs_to_words(s)
+    k, v = _kv(32, n, h, cap, d)
+    q = inputs.normal_np(33, 113, 0, n * hq * d).reshape(n, hq, d).astype(np.float16)
+    kb = tbq4.pack(*tbq4.encode(k.reshape(-1, 128), s))
+    vb = tbq4.pack(*tbq4.encode(v.reshape(-1, 128), s))
+    scale = 1.0 / np.sqrt(d)
+    _say(f"tbq4 fused decode {name}")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    kbt, vbt = dev(kb.reshape(n, h, cap, nb, 66)), dev(vb.reshape(n, h, cap, nb, 66))
+    got = kvq.tbq4_attn_decode(dev(q), kbt, vbt, lens, w, scale).cpu().numpy()
+    got16 = kvq.tbq4_attn_decode(dev(q), kbt, vbt, lens, w, scale, out_f16=True).cpu().numpy()
+    kd = tbq4.decode(kb, s).reshape(n, h, cap, d)
+    vd = tbq4.decode(vb, s).reshape(n, h, cap, d)
+    want = _oracle_attn(q, kd, vd, lens, scale, hq // h)
+    err = np.abs(got - want).max()
+    _say(f"  max err {err:.3g}")
+    assert err <= TBQ_ATTN_TOL
+    assert np.all(np.abs(got16.astype(np.float64) - want) <= TBQ_ATTN_TOL + np.abs(want) * 2.0 ** -11)
+    one = [i for i, x in enumerate(lens) if x == 1]
+    for b in one:  # a single token: the output is that token's decoded value
+        assert np.abs(got[b] - np.repeat(vd[b, :, 0], hq // h, axis=0)).max() <= 1e-5
+
+
+def test_fused_decode_full_size_qwen27b_shape():
+    """One layer at 110,592 tokens, 4 KV heads x 256, 24 query heads, as timed; two KV heads checked."""
+    torch = _torch()
+    d, h, hq, t = 256, 4, 24, 110592
+    nb = d // 128
+    s = inputs.rotation_signs(41)
+    w = inputs.signs_to_words(s)
+    blocks = []
+    for side in range(2):  # seeded random blocks: fp16 norm 8 .. 16, uniform 4-bit indices
+        nblk = h * t * nb
+        bl = np.empty((nblk, 66), np.uint8)
+        bl[:, :2] = (8.0 + 8.0 * inputs.uniform_np(42, 120 + side, 0, nblk)).astype(np.float16).view(np.uint8).reshape(nblk, 2)
+        bl[:, 2:] = inputs.words_np(42, 130 + side, 0, nblk * 8).view(np.uint8).reshape(nblk, 64)
+        blocks.append(bl)
+    q = inputs.normal_np(43, 113, 0, hq * d).reshape(1, hq, d).astype(np.float16)
+    scale = 1.0 / 16.0
+    _say("tbq4 fused decode full size")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    got = kvq.tbq4_attn_decode(dev(q), dev(blocks[0].reshape(1, h, t, nb, 66)), dev(blocks[1].reshape(1, h, t, nb, 66)),
+                               [t], w, scale).cpu().numpy()
+    g = hq // h
+    err = 0.0
+    for hh in (0, h - 1):  # sampled KV heads: every output of their query heads
+        kd = tbq4.decode(blocks[0].reshape(h, t * nb, 66)[hh], s).reshape(t, d)
+        vd = tbq4.decode(blocks[1].reshape(h, t * nb, 66)[hh], s).reshape(t, d)
+        for i in range(g):
+            want = attention.attend(q[0, hh * g + i].astype(np.float64), kd, vd, scale)
+            err = max(err, np.abs(got[0, hh * g + i] - want).max())
+    _say(f"  max err {err:.3g}")
+    assert err <= TBQ_ATTN_TOL

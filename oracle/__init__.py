@@ -27,6 +27,8 @@ section):
   Tail, section 2).
 * ``sizes``     -- the bytes-per-token and effective-bits arithmetic the pages
   print (SJ-KVaRN sections 1, 3, 7.2, 8.4; KV cache math; HAL #582 section 1).
+* ``tq5``       -- the rotated 5-bit comparator block, 82 bytes per 128 values
+  (SJ-KVaRN section 6), quantised like the 6-bit staging format.
 * ``tbq4``      -- the TBQ4 comparator codec: 128-point randomized
   Walsh-Hadamard rotation, fp16 norm, 16 Lloyd-Max centroids of N(0, 1/128),
   66-byte blocks (KV cache math, "rotate first" and the size table).

@@ -247,6 +247,10 @@ def run_tbq4(args, w, torch, kvq, inputs, sealed_us):
     words = inputs.signs_to_words(inputs.rotation_signs(7))
     dev = "cuda"
     kv = [inputs.normal_t(70 + i, 140, 0, n * h * t * d, dev).to(torch.float16).view(-1, 128) for i in range(2)]
+    k4 = kv[0].view(n, h, t, d)
+    for hh in range(h):  # 2% outlier key channels x15, as in the workload recipe
+        ch = torch.from_numpy(inputs.outlier_channels(70, 0, hh, d, max(1, round(0.02 * d)))).to(dev)
+        k4[:, hh, :, ch] *= 15.0
     blocks = [torch.empty((n, h, t, nb, 66), dtype=torch.uint8, device=dev) for _ in range(2)]
     q = inputs.normal_t(72, 141, 0, n * hq * d, dev).to(torch.float16).view(n, hq, d)
     lens = [t] * n
@@ -275,8 +279,22 @@ def run_tbq4(args, w, torch, kvq, inputs, sealed_us):
     log(f"[bench] TBQ4 comparator: {nbytes / 1e6:.1f} MB per layer, fused decode {dec_us:.1f} us "
         f"({gbs:.1f} GB/s, {gbs / HBM_PEAK_GBS:.3f} of HBM peak) vs sealed-cache decode kernel {sealed_us:.1f} us; "
         f"encode {vals / (enc_us * 1e-6) / 1e9:.2f} G values/s")
+    quality = {}
+    for name, bits, fb in (("tbq4", None, 4.125), ("tq5_0", 5, 5.125), ("tq6_0", 6, 6.125)):
+        rel = []
+        for x in kv:
+            if bits is None:
+                xh = kvq.tbq4_decode(kvq.tbq4_encode(x, words), words)
+            else:
+                xh = kvq.tq_decode(kvq.tq_encode(x, bits, words), bits, words)
+            xf = x.float()
+            rel.append(float(((xh - xf) ** 2).sum() / (xf ** 2).sum()))
+            del xh, xf
+        quality[name] = {"bits": fb, "rel_sq_err_k": round(rel[0], 6), "rel_sq_err_v": round(rel[1], 6)}
+    log("[bench] quality per bit (relative squared error, K with outliers / V): " +
+        ", ".join(f"{k} {v['bits']} bits {v['rel_sq_err_k']:.2e} / {v['rel_sq_err_v']:.2e}" for k, v in quality.items()))
     del kv, blocks
-    return {"bytes_per_call": nbytes, "decode_us": round(dec_us, 2), "gbs": round(gbs, 1),
+    return {"quality_per_bit": quality, "bytes_per_call": nbytes, "decode_us": round(dec_us, 2), "gbs": round(gbs, 1),
             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "sealed_decode_kernel_us": round(sealed_us, 2),
             "encode_gvalues_per_s": round(vals / (enc_us * 1e-6) / 1e9, 2),
             "note": "whole layer as TBQ4 blocks, fused rotated-domain decode incl. merge"}

@@ -275,6 +275,22 @@ kvq_status kvq_profile_stop(kvq_cache* cache, float* us, int32_t* n_calls);
  * Errors: KVQ_ERR_INVALID (range or NULL), KVQ_ERR_UNSUPPORTED (head_dim),
  * KVQ_ERR_CAPACITY (workspace), KVQ_ERR_DEVICE. */
 kvq_status kvq_tbq4_tables(float* centroids, float* boundaries);
+
+/* tq5_0 and tq6_0 comparator blocks (SJ-KVaRN section 6: the rotated 5-bit
+ * format, 82 bytes per 128 values; the 6-bit one, 98 bytes, is the staging
+ * format's quantiser).  Per 128-value block: y = R x (the TBQ4 rotation
+ * above, exact and rounded once to fp32), d = fp16(max|y| / L) with
+ * L = 2^(bits-1) - 1, q = clamp(rne(y * fp32(1 / d)), -L, L), codes
+ * u = q + 2^(bits-1) (all 2^(bits-1) when d = 0).  Bytes: [fp16 d,
+ * little-endian][16 * bits bytes: LSB-first stream, value k in bits
+ * bits*k .. bits*k + bits - 1].  bits: 5 or 6 (else KVQ_ERR_UNSUPPORTED).
+ * kvq_tq_encode: x device fp16 [n][128]; blocks device [n][2 + 16 bits].
+ * kvq_tq_decode: out device fp32 [n][128], R^T (d (u - 2^(bits-1))).
+ * signs: host, as for TBQ4.  Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED,
+ * KVQ_ERR_DEVICE. */
+kvq_status kvq_tq_encode(const void* x, int64_t n, int32_t bits, const uint64_t* signs, void* blocks, void* stream);
+kvq_status kvq_tq_decode(const void* blocks, int64_t n, int32_t bits, const uint64_t* signs, float* out,
+                         void* stream);
 kvq_status kvq_tbq4_encode(const void* x, int64_t n, const uint64_t* signs, void* blocks, void* stream);
 kvq_status kvq_tbq4_decode(const void* blocks, int64_t n, const uint64_t* signs, float* out, void* stream);
 kvq_status kvq_tbq4_workspace_bytes(int32_t n_seqs, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,

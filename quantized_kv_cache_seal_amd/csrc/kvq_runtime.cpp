@@ -26,6 +26,7 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_tbq4_encode(const Tbq4CodecArgs& a, hipStream_t stream);
 hipError_t launch_tbq4_decode(const Tbq4CodecArgs& a, hipStream_t stream);
 hipError_t launch_tbq4_attn(const Tbq4AttnArgs& a, int grid_x, hipStream_t stream);
+hipError_t launch_tq_codec(const Tbq4CodecArgs& a, int bits, bool encode, hipStream_t stream);
 }  // namespace kvq
 
 using namespace kvq;
@@ -972,6 +973,34 @@ kvq_status kvq_tbq4_decode(const void* blocks, int64_t n, const uint64_t* signs,
   tbq4_signs(signs, a.signs);
   hipError_t e = launch_tbq4_decode(a, (hipStream_t)stream);
   return e == hipSuccess ? KVQ_OK : hip_fail(e, "TBQ4 decode launch");
+}
+
+kvq_status kvq_tq_encode(const void* x, int64_t n, int32_t bits, const uint64_t* signs, void* blocks,
+                          void* stream) {
+  if (n < 0 || !signs || (n > 0 && (!x || !blocks))) return fail(KVQ_ERR_INVALID, "bad tq encode arguments");
+  if (bits != 5 && bits != 6) return fail(KVQ_ERR_UNSUPPORTED, "tq blocks take 5 or 6 bits, not %d", bits);
+  if (n == 0) return KVQ_OK;
+  Tbq4CodecArgs a{};
+  a.x = (const uint16_t*)x;
+  a.blocks_out = (uint8_t*)blocks;
+  a.n = n;
+  tbq4_signs(signs, a.signs);
+  hipError_t e = launch_tq_codec(a, bits, true, (hipStream_t)stream);
+  return e == hipSuccess ? KVQ_OK : hip_fail(e, "tq encode launch");
+}
+
+kvq_status kvq_tq_decode(const void* blocks, int64_t n, int32_t bits, const uint64_t* signs, float* out,
+                          void* stream) {
+  if (n < 0 || !signs || (n > 0 && (!blocks || !out))) return fail(KVQ_ERR_INVALID, "bad tq decode arguments");
+  if (bits != 5 && bits != 6) return fail(KVQ_ERR_UNSUPPORTED, "tq blocks take 5 or 6 bits, not %d", bits);
+  if (n == 0) return KVQ_OK;
+  Tbq4CodecArgs a{};
+  a.blocks_in = (const uint8_t*)blocks;
+  a.y = out;
+  a.n = n;
+  tbq4_signs(signs, a.signs);
+  hipError_t e = launch_tq_codec(a, bits, false, (hipStream_t)stream);
+  return e == hipSuccess ? KVQ_OK : hip_fail(e, "tq decode launch");
 }
 
 static kvq_status tbq4_check_shape(int32_t n_seqs, int32_t Hq, int32_t H, int32_t D) {

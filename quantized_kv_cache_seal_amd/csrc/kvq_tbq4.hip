@@ -1,4 +1,4 @@
-// TBQ4 comparator format (KV cache math: "rotate first" and the format table):
+// Comparator formats.  TBQ4 (KV cache math: "rotate first" and the format table):
 // each 128-value block is rotated by the randomized Walsh-Hadamard transform
 // (sign flip, transform, sign flip), its norm is stored in fp16, and each
 // rotated value divided by the norm is replaced by the 4-bit index of the
@@ -122,6 +122,64 @@ __global__ __launch_bounds__(256) void tbq4_decode_kernel(Tbq4CodecArgs a) {
   const float nf = h2f(*(const uint16_t*)in);
   const uint32_t byte = in[2 + lane];
   float v[2] = {cent[byte & 15] * nf, cent[byte >> 4] * nf};
+  rwht128_f32<2, true>(v, lane, a.signs);
+  *(float2*)(a.y + blk * 128 + 2 * lane) = make_float2(v[0], v[1]);
+}
+
+// tqB_0 comparator blocks, B = 5 or 6 bits (SJ-KVaRN section 6 compares
+// against the rotated 5-bit format; the 6-bit one is the staging format): the
+// 128-point rotation as above, then the symmetric uniform quantiser of the
+// staging format with 2^(B-1) - 1 levels a side: d = fp16(amax / L) by IEEE
+// fp32 division, q = clamp(rne(y * fp32(1 / d)), -L, L), u = q + 2^(B-1);
+// block = [fp16 d][16 B bytes: LSB-first B-bit stream].  One wave per block:
+// lane l holds codes 2l and 2l + 1, so four lanes hold B whole bytes.
+template <int B>
+__global__ __launch_bounds__(256) void tq_encode_kernel(Tbq4CodecArgs a) {
+  constexpr int LEVEL = (1 << (B - 1)) - 1, OFF = 1 << (B - 1), BYTES = 2 + 16 * B;
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= a.n) return;
+  float y[2];
+  rwht128_exact(a.x + blk * 128, lane, a.signs, y);
+  float am = fmaxf(fabsf(y[0]), fabsf(y[1]));
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) am = fmaxf(am, shfl_xor_f(am, m));
+  const uint16_t dbits = f2h_bits(am / (float)LEVEL);
+  const float d = h2f(dbits);
+  const float inv = d > 0.0f ? 1.0f / d : 0.0f;
+  uint32_t pair = 0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float q = fminf(fmaxf(rintf(y[j] * inv), -(float)LEVEL), (float)LEVEL);
+    pair |= (uint32_t)((int)q + OFF) << (B * j);
+  }
+  const int g0 = lane & ~3;
+  const uint64_t w = (uint64_t)__shfl(pair, g0, 64) | ((uint64_t)__shfl(pair, g0 + 1, 64) << (2 * B)) |
+                     ((uint64_t)__shfl(pair, g0 + 2, 64) << (4 * B)) | ((uint64_t)__shfl(pair, g0 + 3, 64) << (6 * B));
+  uint8_t* out = a.blocks_out + blk * BYTES;
+  if ((lane & 3) == 0) {
+#pragma unroll
+    for (int k = 0; k < B; ++k) out[2 + B * (lane >> 2) + k] = (uint8_t)(w >> (8 * k));
+  }
+  if (lane == 0) *(uint16_t*)out = dbits;
+}
+
+// x^ = R^T (d (u - 2^(B-1))) in fp32, one wave per block.
+template <int B>
+__global__ __launch_bounds__(256) void tq_decode_kernel(Tbq4CodecArgs a) {
+  constexpr int OFF = 1 << (B - 1), BYTES = 2 + 16 * B;
+  constexpr uint32_t MASK = (1u << B) - 1u;
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= a.n) return;
+  const uint8_t* in = a.blocks_in + blk * BYTES;
+  const float d = h2f(*(const uint16_t*)in);
+  const int bit = 2 * B * lane, sh = bit & 7, nbytes = (sh + 2 * B + 7) >> 3;  // 2 or 3, inside the block
+  const uint8_t* p = in + 2 + (bit >> 3);
+  uint32_t w = p[0] | ((uint32_t)p[1] << 8);
+  if (nbytes > 2) w |= (uint32_t)p[2] << 16;
+  w >>= sh;
+  float v[2] = {d * (float)((int)(w & MASK) - OFF), d * (float)((int)((w >> B) & MASK) - OFF)};
   rwht128_f32<2, true>(v, lane, a.signs);
   *(float2*)(a.y + blk * 128 + 2 * lane) = make_float2(v[0], v[1]);
 }
@@ -303,6 +361,19 @@ hipError_t launch_tbq4_decode(const Tbq4CodecArgs& a, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(tbq4_decode_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tq_codec(const Tbq4CodecArgs& a, int bits, bool encode, hipStream_t stream) {
+  const int64_t grid = (a.n + 3) / 4;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 g((unsigned)grid), blk(256);
+  if (bits == 5 && encode) hipLaunchKernelGGL(tq_encode_kernel<5>, g, blk, 0, stream, a);
+  else if (bits == 5) hipLaunchKernelGGL(tq_decode_kernel<5>, g, blk, 0, stream, a);
+  else if (bits == 6 && encode) hipLaunchKernelGGL(tq_encode_kernel<6>, g, blk, 0, stream, a);
+  else if (bits == 6) hipLaunchKernelGGL(tq_decode_kernel<6>, g, blk, 0, stream, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

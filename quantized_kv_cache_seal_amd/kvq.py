@@ -26,6 +26,7 @@ EXPORTS = [
     "kvq_seq_truncate", "kvq_seq_save_bytes", "kvq_seq_save", "kvq_seq_restore", "kvq_export", "kvq_import",
     "kvq_unit_bytes", "kvq_profile_start", "kvq_profile_stop",
     "kvq_tbq4_tables", "kvq_tbq4_encode", "kvq_tbq4_decode", "kvq_tbq4_workspace_bytes", "kvq_tbq4_attn_decode",
+    "kvq_tq_encode", "kvq_tq_decode",
     "kvq_status_string", "kvq_last_error",
 ]
 
@@ -83,6 +84,8 @@ def lib():
             "kvq_tbq4_encode": [vp, i64, P(ctypes.c_uint64), vp, vp],
             "kvq_tbq4_decode": [vp, i64, P(ctypes.c_uint64), vp, vp],
             "kvq_tbq4_workspace_bytes": [i32, i32, i32, i32, i64, P(sz)],
+            "kvq_tq_encode": [vp, i64, i32, P(ctypes.c_uint64), vp, vp],
+            "kvq_tq_decode": [vp, i64, i32, P(ctypes.c_uint64), vp, vp],
             "kvq_tbq4_attn_decode": [vp, vp, vp, i32, i32, i32, i32, i64, P(i64), P(ctypes.c_uint64),
                                      ctypes.c_float, vp, i32, vp, sz, vp],
         }
@@ -365,4 +368,33 @@ def tbq4_attn_decode(q, k_blocks, v_blocks, seq_len, sign_words, scale=1.0, out=
     check(lib().kvq_tbq4_attn_decode(_ptr(q), _ptr(k_blocks), _ptr(v_blocks), n_seqs, hq, h, d, cap, lens,
                                      _words(sign_words), float(scale), _ptr(out), 1 if out_f16 else 0,
                                      _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def tq_block_bytes(bits: int) -> int:
+    return 2 + 16 * bits
+
+
+def tq_encode(x, bits, sign_words, out=None, stream=None):
+    """x: fp16 device tensor (..., 128) -> uint8 device tensor (n, 2 + 16 bits)."""
+    import torch
+    assert x.dtype == torch.float16 and x.is_contiguous() and x.shape[-1] == 128
+    n = x.numel() // 128
+    if out is None:
+        out = torch.empty((n, tq_block_bytes(bits)), dtype=torch.uint8, device=x.device)
+    assert out.dtype == torch.uint8 and out.is_contiguous() and out.numel() >= n * tq_block_bytes(bits)
+    check(lib().kvq_tq_encode(_ptr(x), n, bits, _words(sign_words), _ptr(out), _stream(stream)))
+    return out
+
+
+def tq_decode(blocks, bits, sign_words, out=None, stream=None):
+    """blocks: uint8 device tensor (n, 2 + 16 bits) -> fp32 device tensor (n, 128)."""
+    import torch
+    nb = tq_block_bytes(bits)
+    assert blocks.dtype == torch.uint8 and blocks.is_contiguous() and blocks.numel() % nb == 0
+    n = blocks.numel() // nb
+    if out is None:
+        out = torch.empty((n, 128), dtype=torch.float32, device=blocks.device)
+    assert out.dtype == torch.float32 and out.is_contiguous() and out.numel() >= n * 128
+    check(lib().kvq_tq_decode(_ptr(blocks), n, bits, _words(sign_words), _ptr(out), _stream(stream)))
     return out

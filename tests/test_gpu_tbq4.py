@@ -155,3 +155,49 @@ def test_fused_decode_full_size_qwen27b_shape():
             err = max(err, np.abs(got[0, hh * g + i] - want).max())
     _say(f"  max err {err:.3g}")
     assert err <= TBQ_ATTN_TOL
+
+
+def _tq_oracle_blocks(x, bits, s):
+    """Oracle blocks of the tq5_0 / tq6_0 comparator codec (128-point rotation)."""
+    from oracle import rotation, tq5, tq6
+    if bits == 5:
+        return tq5.encode(x, s)
+    d, u = tq6.encode_blocks(rotation.rotate(x, 128, s))
+    return np.stack([np.frombuffer(tq6.block_bytes(d[i], u[i]), np.uint8) for i in range(len(d))])
+
+
+def _tq_oracle_decode(blocks, bits, s):
+    from oracle import rotation, tq5, tq6
+    if bits == 5:
+        return tq5.decode(blocks, s), tq5.decode_rotated(blocks).astype(np.float64)
+    parsed = [tq6.parse_block(bytes(b)) for b in blocks]
+    yh = np.stack([tq6.decode_blocks(d, u) for d, u in parsed]).astype(np.float64)
+    return rotation.inverse_exact(yh, 128, s), yh
+
+
+@pytest.mark.parametrize("bits", [5, 6])
+@pytest.mark.parametrize("n,seed", [(1, 1), (5, 2), (1001, 3)])
+def test_tq_encode_bit_exact(bits, n, seed):
+    torch = _torch()
+    s = inputs.rotation_signs(50 + seed)
+    w = inputs.signs_to_words(s)
+    x = _x16(60 + seed, n)
+    _say(f"tq{bits} encode n={n} seed={seed}")
+    got = kvq.tq_encode(torch.from_numpy(x).cuda(), bits, w).cpu().numpy()
+    want = _tq_oracle_blocks(x, bits, s)
+    assert got.shape == want.shape == (n, 2 + 16 * bits)
+    bad = np.nonzero((got != want).any(axis=1))[0]
+    assert bad.size == 0, f"blocks differ: {bad[:10]}"
+
+
+@pytest.mark.parametrize("bits", [5, 6])
+def test_tq_decode_matches_oracle(bits):
+    torch = _torch()
+    s = inputs.rotation_signs(71)
+    w = inputs.signs_to_words(s)
+    blocks = _tq_oracle_blocks(_x16(72, 513), bits, s)
+    _say(f"tq{bits} decode n=513")
+    got = kvq.tq_decode(torch.from_numpy(blocks).cuda(), bits, w).cpu().numpy().astype(np.float64)
+    want, yh = _tq_oracle_decode(blocks, bits, s)
+    norm = np.sqrt((yh ** 2).sum(axis=1))
+    assert np.all(np.abs(got - want) <= 4e-6 * norm[:, None])

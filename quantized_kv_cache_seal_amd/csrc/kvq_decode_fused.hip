@@ -610,6 +610,12 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
     const float mrec = fmaxf(fmaxf(xm[0][q16], xm[1][q16]), fmaxf(xm[2][q16], xm[3][q16]));
     const float m_new = fmaxf(m_run, mrec);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first record
+    // the record's weights are taken relative to its own maximum, so that the
+    // fp16 hi/lo weight operands of its significant tokens stay normal (their
+    // absolute floor 2^-25 would otherwise grow relative to the weights as the
+    // chunk's running maximum climbs); its fp32 contribution and its share of
+    // l carry the factor 2^(mrec - m_new) <= 1
+    const float frec = __builtin_amdgcn_exp2f(mrec - m_new);
     m_run = m_new;
     if (alpha != 1.0f) {
 #pragma unroll
@@ -618,14 +624,15 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
         for (int i = 0; i < VT; ++i) acc[s][i] *= alpha;
     }
     l_part *= alpha;
-    float p[2][4];
+    float p[2][4], lrec = 0.0f;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        p[i][j] = __builtin_amdgcn_exp2f(sc[i][j] - m_new);  // argument <= 0
-        l_part += p[i][j];
+        p[i][j] = __builtin_amdgcn_exp2f(sc[i][j] - mrec);  // argument <= 0
+        lrec += p[i][j];
       }
+    l_part = fmaf(frec, lrec, l_part);
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       const uint8_t* vm = mr + s * MS;
@@ -702,10 +709,10 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
       for (int j = 0; j < VT; ++j) {
         const int cb = VT * wave + j;
         const float4 c = *(const float4*)(vm + Sh::L_VC + 4 * (16 * cb + 4 * g));
-        acc[s][j][0] = fmaf(c.x, o[j][0] + corr, acc[s][j][0]);
-        acc[s][j][1] = fmaf(c.y, o[j][1] + corr, acc[s][j][1]);
-        acc[s][j][2] = fmaf(c.z, o[j][2] + corr, acc[s][j][2]);
-        acc[s][j][3] = fmaf(c.w, o[j][3] + corr, acc[s][j][3]);
+        acc[s][j][0] = fmaf(c.x * frec, o[j][0] + corr, acc[s][j][0]);
+        acc[s][j][1] = fmaf(c.y * frec, o[j][1] + corr, acc[s][j][1]);
+        acc[s][j][2] = fmaf(c.z * frec, o[j][2] + corr, acc[s][j][2]);
+        acc[s][j][3] = fmaf(c.w * frec, o[j][3] + corr, acc[s][j][3]);
       }
     }
   }

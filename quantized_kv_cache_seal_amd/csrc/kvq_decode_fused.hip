@@ -890,7 +890,7 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
   const uint16_t* ksink = (const uint16_t*)(a.arena + y.off_sink) + sink_elem(y, sq.slot, a.layer, h, 0, 0);
   const uint16_t* vsink = (const uint16_t*)(a.arena + y.off_sink) + sink_elem(y, sq.slot, a.layer, h, 1, 0);
 
-  float m_run = -INFINITY, l_part = 0.0f;
+  float m_run = -INFINITY, m_ref = -INFINITY, l_part = 0.0f;
   float4v acc[CPW];
 #pragma unroll
   for (int i = 0; i < CPW; ++i) acc[i] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
@@ -993,9 +993,16 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
 
     // ---- (3) weights
     const float M = fmaxf(fmaxf(xm[0][q16], xm[1][q16]), fmaxf(xm[2][q16], xm[3][q16]));  // token t0 is valid
-    const float m_new = fmaxf(m_run, M);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first step
-    m_run = m_new;
+    // the step's weights are taken relative to m_ref = max(M, running maximum
+    // - 24), not to the running maximum itself: the fp16 hi/lo weight operands
+    // then stay in the normal range, where their relative precision holds
+    // (tokens more than 24 below the running maximum weigh under 2^-24 of it);
+    // the accumulators and l are rescaled from the previous reference, by a
+    // factor of at most 2^24
+    m_run = fmaxf(m_run, M);
+    const float m_new = fmaxf(M, m_run - 24.0f);
+    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 on the first step
+    m_ref = m_new;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) acc[i] *= alpha;
     l_part *= alpha;
@@ -1067,7 +1074,7 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
     for (int i = 0; i < CPW; ++i) *(float4v*)(rows + q16 * D + 16 * (CPW * wave + i) + 4 * g) = acc[i];
   }
   __syncthreads();
-  write_partial_rows<D>(a, b, h, c, rows, m_run, xl, !sink, wave, lane);
+  write_partial_rows<D>(a, b, h, c, rows, m_ref, xl, !sink, wave, lane);
 }
 
 // ---------------------------------------------------------------------------

@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn effective KV GB/s (% HBM peak) at 110,592 ctx; seal tokens/s"
 HBM_PEAK_GBS = 8000.0
+FP32_VALU_NONPACKED_TFLOPS = 78.6  # fp32 vector peak without packed instructions (disabled in this build)
 FP32_VALU_PEAK_TFLOPS = 157.3
 
 
@@ -294,7 +295,14 @@ def run_tbq4(args, w, torch, kvq, inputs, sealed_us):
     log("[bench] quality per bit (relative squared error, K with outliers / V): " +
         ", ".join(f"{k} {v['bits']} bits {v['rel_sq_err_k']:.2e} / {v['rel_sq_err_v']:.2e}" for k, v in quality.items()))
     del kv, blocks
-    return {"quality_per_bit": quality, "bytes_per_call": nbytes, "decode_us": round(dec_us, 2), "gbs": round(gbs, 1),
+    # fp32 FMAs per call: one per value and query head for the scores, one
+    # for the outputs (the scan is bound by this vector arithmetic, not HBM)
+    flops = 2 * 2 * n * h * t * d * (hq // h)
+    tflops = flops / (dec_us * 1e-6) / 1e12
+    return {"roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": FP32_VALU_NONPACKED_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / FP32_VALU_NONPACKED_TFLOPS, 4),
+                         "flops_per_call": flops, "time_basis": "whole call (query prologue, scan, merge)"},
+            "quality_per_bit": quality, "bytes_per_call": nbytes, "decode_us": round(dec_us, 2), "gbs": round(gbs, 1),
             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "sealed_decode_kernel_us": round(sealed_us, 2),
             "encode_gvalues_per_s": round(vals / (enc_us * 1e-6) / 1e9, 2),
             "note": "whole layer as TBQ4 blocks, fused rotated-domain decode incl. merge"}

@@ -187,6 +187,19 @@ class OracleCache:
             return s["records"][head][index]
         raise ValueError(region)
 
+    def import_ring(self, seq, layer, head, slot, buf):
+        """Canonical bytes of one ring slot (the export layout) into the ring: a
+        test hook that places chosen staged tiles."""
+        s = self._state(seq, layer)
+        buf = bytes(buf)
+        assert len(buf) == 2 * self.nb * tq6.BLOCK_BYTES
+        for side in (0, 1):
+            for b in range(self.nb):
+                o = (side * self.nb + b) * tq6.BLOCK_BYTES
+                d, u = tq6.parse_block(buf[o:o + tq6.BLOCK_BYTES])
+                s["ring_d"][side, slot, head, b] = d
+                s["ring_u"][side, slot, head, b] = u
+
     def import_record(self, seq, layer, head, index, buf):
         s = self._state(seq, layer)
         recs = s["records"][head]

@@ -11,20 +11,24 @@ normalization".
 
 Readings:
 * "spread" is the population standard deviation (mean subtracted), read from
-  "variance balancing";
+  "variance balancing".  It is computed about the first element of the row
+  or column (sigma of y equals sigma of y - y_first), so that a row or column
+  whose values are all equal has a spread of exactly zero;
 * a "pass" is one sweep over all rows or over all columns, rows first (the
   order of the words "row and column"), so 16 passes = 8 row + 8 column sweeps;
 * log-domain state: lr (per row) and lc (per column), with
   y_ij = x_ij * exp(-lr_i - lc_j); a row pass sets lr_i += ln sigma_i where
   sigma_i is the spread of row i of y; a column pass does the same for lc;
 * a row or column whose spread is zero cannot be balanced and keeps its scale
-  (its log scale is not updated): an all-zero tile keeps unit scales.  Adding
-  ln of a floor instead would grow the log scales of such a row or column by
-  ~69 per pass until exp overflows.  "Zero" is sigma <= 1e-30 or
-  sigma^2 <= 2^-16 mean(y^2) (a spread under 1/256 of the RMS): the fp32
-  one-pass form E[y^2] - mean^2 with 22-bit factors errs by up to ~2^-20
-  mean(y^2), so below that a spread cannot be told from zero and a row or
-  column of identical values (repeated tokens) must read as constant;
+  (its log scale is not updated): an all-zero tile keeps unit scales, and so
+  do the columns of a tile of repeated tokens.  "Zero" is decided by float64
+  arithmetic alone: sigma <= 2^-40 * rms(y).  Values that are equal in exact
+  arithmetic can differ after rounding in float64 -- y carries the rounding of
+  one exp and one product, ~2^-52 relative, e.g. rows that are power-of-two
+  multiples of one another leave columns equal up to an ulp or two after the
+  row pass -- so their computed spread is at most a few 2^-52 of their RMS;
+  2^-40 sits 2^10 above that, and every spread at or above it is balanced as
+  the unguarded passes would balance it;
 * scale absorption: the row factors are not stored (each row gets its own
   rounding scale and zero point afterwards, which absorbs them); the column
   factors are kept as C_j = fp16(exp(lc_j)) after centring lc to mean zero
@@ -37,9 +41,17 @@ from __future__ import annotations
 
 import numpy as np
 
-LOG_FLOOR = 1e-30
-ZERO_SPREAD_REL = 2.0 ** -16  # sigma^2 / mean(y^2) at or below which a spread counts as zero
+ZERO_SPREAD_REL = 2.0 ** -40  # sigma / rms(y) at or below which a spread counts as zero
 LC_CLAMP = 9.0
+
+
+def spread(y, axis: int):
+    """(sigma, rms) of y along `axis`: the population standard deviation,
+    taken about the first element, and the root mean square."""
+    first = np.take(y, [0], axis=axis)
+    sigma = np.std(y - first, axis=axis)
+    rms = np.sqrt(np.mean(y * y, axis=axis))
+    return sigma, rms
 
 
 def balance(x, passes: int):
@@ -52,9 +64,9 @@ def balance(x, passes: int):
     for p in range(passes):
         y = x * np.exp(-lr[:, None] - lc[None, :])
         ax = 1 if p % 2 == 0 else 0
-        sigma = y.std(axis=ax)
-        upd = (sigma > LOG_FLOOR) & (sigma * sigma > ZERO_SPREAD_REL * (y * y).mean(axis=ax))
-        step = np.where(upd, np.log(np.maximum(sigma, LOG_FLOOR)), 0.0)
+        sigma, rms = spread(y, ax)
+        upd = sigma > ZERO_SPREAD_REL * rms
+        step = np.where(upd, np.log(np.where(upd, sigma, 1.0)), 0.0)
         if ax == 1:
             lr = lr + step
         else:

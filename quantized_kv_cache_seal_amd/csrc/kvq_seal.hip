@@ -23,10 +23,25 @@
 // both copies stay in registers (the second is built through a transposed tile
 // in LDS).  The updated side's factor is 1/spread (equal to exp(-l) of the
 // log-domain update l += ln spread, spread the population standard deviation);
-// a row or column whose spread is zero (kZeroSpread) keeps its factor and log
-// scale (it cannot be balanced: an all-zero tile keeps unit scales, constant
-// columns of repeated tokens keep theirs); the factors pass between waves
-// through LDS, one barrier per pass.
+// a row or column of zeros (zero sum of squares: every product is exact, so
+// that sum is zero only then) keeps its factor and log scale; the factors pass
+// between waves through LDS, one barrier per pass.
+//
+// Tiles the fp32 passes cannot resolve go through binary64 instead.  The
+// one-pass variance E[y^2] - mean^2 loses bits in proportion to mean^2 /
+// variance, and the fp16 hi + lo operands hold a factor to 22 bits only within
+// a range of magnitudes.  So the tile is flagged, and balanced again from the
+// start in binary64 on the vector ALU (balance_f64: the passes exactly as
+// defined, the spread taken about the first element, so that equal values give
+// exactly zero, and a spread at or below 2^-40 of the RMS counting as zero),
+// when in any pass a nonzero row or column has a spread at or below 1/8 of its
+// RMS (kIllCond: the cancellation then costs at most 6 of fp32's 24 bits), or
+// a factor leaves the range in which its hi + lo operands and those of its
+// square keep ~2^-18 relative precision and stay finite.  Real caches are
+// rotated first, which spreads every channel's energy over the tile, so their
+// tiles stay on the fast path; repeated tokens, constant channels far above
+// their spread, and channels orders of magnitude below the rest take the
+// exact one.
 //
 // The balancing factors (1/spread, ln spread) use the hardware square root,
 // reciprocal and log2 (about 1 ulp): only the column scales C leave the
@@ -39,19 +54,18 @@
 
 namespace kvq {
 
-// Largest balancing factor passed to the matrix cores: the factors and their
-// squares go in as fp16 hi + lo, so f^2 must stay below 65504.  Balanced data
-// has factors near 1 (columns) or 1/|q| (rows); only a column whose spread is
-// nonzero but below 1/255 of the others' (nearly constant over the 128 tokens)
-// reaches the cap, which then keeps its products finite; its log scale still
-// comes from its spread.
-constexpr float kFactorMax = 255.0f;
-// A spread counts as zero (the row or column keeps its scale) when it is at most
-// 1e-30 or its square at most 2^-16 of the mean square (under 1/256 of the
-// RMS): the one-pass variance E[y^2] - mean^2 from 22-bit factors errs by up to
-// ~2^-20 E[y^2], so below that it cannot tell a spread from zero, and a row or
-// column of identical values must read as constant.
-constexpr float kZeroSpread = 1.52587890625e-05f;  // 2^-16
+// The fast passes flag a tile for the binary64 passes when a nonzero row or
+// column has variance <= kIllCond * mean square (spread <= RMS / 8).
+constexpr float kIllCond = 0.015625f;  // 2^-6
+// Factors enter the matrix cores pre-scaled by a power of two (column factors
+// c by kCScale, row factors d r by kRScale, so that typical balanced tiles sit
+// near 1 to 4) and must then lie in [kFMin, kFMax]: f^2 below 65504 in fp16,
+// and f, f^2 at or above 2^-3, 2^-6, where the fp16 hi + lo pair still
+// carries ~2^-18 of the value.  A factor outside flags the tile.
+constexpr float kCScale = 4.0f, kRScale = 16.0f;
+constexpr float kFMin = 0.125f, kFMax = 255.0f;
+// binary64 passes: a spread at or below 2^-40 of the RMS counts as zero
+constexpr double kZeroSpread64 = 9.094947017729282e-13;  // 2^-40
 
 template <int SUBW>
 struct SealShape {
@@ -141,7 +155,111 @@ struct SealLds {
   float rinv[kGroup];                       // fp32(1 / S_i)
   float zrow[kGroup];                       // Z_i
   float red[4];
+  double red64[4];
+  int bad[2];  // fast passes: tile flagged in a pass of this parity
 };
+
+// Binary64 balancing of a flagged tile, from the start: the passes as
+// defined (SJ-KVaRN 2.2: alternating row and column passes, rows first, log
+// domain, keep the final scales), y_ij = ((q_ij d_ib) exp(-lr_i)) exp(-lc_j),
+// the spread of a row or column the population standard deviation about its
+// first element (exactly zero when its values are equal) and zero at or below
+// 2^-40 of its RMS, in which case the log scale is kept.  The tile's codes are
+// copied from the row-layout registers into an int8 tile in LDS (the factor
+// exchange is no longer needed), followed by lr, lc and their exponentials.
+// Writes C (fp16) to meta and fp32(1 / C) to invc.
+template <int SUBW>
+__device__ __forceinline__ void balance_f64(SealLds<SUBW>& L, const half8 (&ar)[2][SUBW / 32], int passes,
+                                            uint8_t* meta) {
+  using Sh = SealShape<SUBW>;
+  constexpr int KR = Sh::KR;
+  static_assert(128 * SUBW + 8 * 2 * (128 + SUBW) <= Sh::BYTES, "binary64 state fits the tile's LDS");
+  int8_t* qs = (int8_t*)L.smem;                      // [128][SUBW]
+  double* lr = (double*)(L.smem + 128 * SUBW);       // [128]
+  double* lc = lr + 128;                             // [SUBW]
+  double* fr = lc + SUBW;                            // [128] exp(-lr)
+  double* fc = fr + 128;                             // [SUBW] exp(-lc)
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int kk = 0; kk < KR; ++kk) {
+      uint32_t wd[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wd[e >> 2] |= ((uint32_t)(int)(float)ar[t][kk][e] & 0xFFu) << (8 * (e & 3));
+      *(uint2*)(qs + (16 * (2 * w + t) + m) * SUBW + 32 * kk + 8 * g) = make_uint2(wd[0], wd[1]);
+    }
+  for (int i = tid; i < 128 + SUBW; i += 256) lr[i] = 0.0;  // lr and lc are contiguous
+  __syncthreads();
+  const int hf = tid & 1;
+  for (int p = 0; p < passes; ++p) {
+    for (int i = tid; i < 128 + SUBW; i += 256) fr[i] = exp(-lr[i]);  // fr, fc mirror lr, lc
+    __syncthreads();
+    if ((p & 1) == 0) {
+      // row tid / 2, columns hf SUBW / 2 .. + SUBW / 2 (one tq6_0 block at 256 wide)
+      const int row = tid >> 1, c0 = hf * (SUBW / 2);
+      const double frow = fr[row];
+      const double ref = ((double)qs[row * SUBW] * (double)L.ds[0][row]) * frow * fc[0];
+      double s1 = 0.0, s2 = 0.0, sq = 0.0;
+      for (int c = c0; c < c0 + SUBW / 2; c += 4) {
+        const double d = (double)L.ds[c / kQBlock][row];
+        const char4 q4 = *(const char4*)(qs + row * SUBW + c);
+        const int qv[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double yy = ((double)qv[e] * d) * frow * fc[c + e], dv = yy - ref;
+          s1 += dv;
+          s2 += dv * dv;
+          sq += yy * yy;
+        }
+      }
+      s1 += __shfl_xor(s1, 1, 64);
+      s2 += __shfl_xor(s2, 1, 64);
+      sq += __shfl_xor(sq, 1, 64);
+      const double mean = s1 / SUBW, var = fmax(s2 / SUBW - mean * mean, 0.0), sig = sqrt(var);
+      if (hf == 0 && sig > kZeroSpread64 * sqrt(sq / SUBW)) lr[row] += log(sig);
+    } else {
+      // column tid (256 wide), or tid / 2 with rows hf 64 .. + 64 (128 wide)
+      constexpr int TPC = 256 / SUBW, NR = 128 / TPC;
+      const int col = tid / TPC, r0 = TPC == 2 ? hf * NR : 0;
+      const double dcol0 = (double)L.ds[col / kQBlock][0];
+      const double fcol = fc[col];
+      const double ref = ((double)qs[col] * dcol0) * fr[0] * fcol;
+      double s1 = 0.0, s2 = 0.0, sq = 0.0;
+      for (int r = r0; r < r0 + NR; ++r) {
+        const double yy = ((double)qs[r * SUBW + col] * (double)L.ds[col / kQBlock][r]) * fr[r] * fcol,
+                     dv = yy - ref;
+        s1 += dv;
+        s2 += dv * dv;
+        sq += yy * yy;
+      }
+      if (TPC == 2) {
+        s1 += __shfl_xor(s1, 1, 64);
+        s2 += __shfl_xor(s2, 1, 64);
+        sq += __shfl_xor(sq, 1, 64);
+      }
+      const double mean = s1 / kGroup, var = fmax(s2 / kGroup - mean * mean, 0.0), sig = sqrt(var);
+      if ((TPC == 1 || hf == 0) && sig > kZeroSpread64 * sqrt(sq / kGroup)) lc[col] += log(sig);
+    }
+    __syncthreads();
+  }
+  // centre, clamp to [-9, 9], C = fp16(exp(lc))
+  double v = tid < SUBW ? lc[tid] : 0.0;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+  if (l == 0) L.red64[w] = v;
+  __syncthreads();
+  const double lmean = (L.red64[0] + L.red64[1] + L.red64[2] + L.red64[3]) / SUBW;
+  if (tid < SUBW) {
+    const double c = fmin(fmax(lc[tid] - lmean, -9.0), 9.0);
+    const half_t ch = (half_t)exp(c);
+    uint16_t cb;
+    __builtin_memcpy(&cb, &ch, 2);
+    ((uint16_t*)meta)[tid] = cb;
+    L.invc[tid] = 1.0f / h2f(cb);
+  }
+  __syncthreads();
+}
 
 // One tile; KV (0 keys, 1 values) is a compile-time choice so that the keys'
 // path holds one copy of the tile once the balancing is done.
@@ -216,13 +334,14 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
     for (int kr = 0; kr < 4; ++kr)
       ac[ct][kr] = mfma_a(*(const uint4*)(qt + (16 * (CT * w + ct) + m) * PITCH + 32 * kr + 8 * g));
   __syncthreads();  // the transposed tile is consumed: its area holds the factors from here on
-  for (int j = tid; j < SUBW; j += 256) {  // first row pass: c = 1 (exactly: hi 1, lo 0)
-    cfl[0 * SUBW + j] = 0x3C00;
+  for (int j = tid; j < SUBW; j += 256) {  // first row pass: c = 1, pre-scaled (hi kCScale, lo 0)
+    cfl[0 * SUBW + j] = f2h_bits(kCScale);
     cfl[1 * SUBW + j] = 0;
-    cfl[2 * SUBW + j] = 0x3C00;
+    cfl[2 * SUBW + j] = f2h_bits(kCScale * kCScale);
     cfl[3 * SUBW + j] = 0;
     lcs[j] = 0.0f;
   }
+  if (tid < 2) L.bad[tid] = 0;
   __syncthreads();
 
   // B carries the factor's fp16 hi in its even columns and lo in its odd ones
@@ -234,7 +353,7 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
   const int pr = m >> 1;                       // lane pair 0..7
   constexpr int NCL = CT / 2;                  // columns per lane pair in a column pass
   // the factors of this lane pair's row and columns from their last update:
-  // a row or column whose spread is zero keeps them (and its log scale)
+  // a row or column of zeros keeps them (and its log scale)
   float rf_keep = 1.0f, cf_keep[NCL], lc_keep[NCL];
 #pragma unroll
   for (int e = 0; e < NCL; ++e) {
@@ -242,7 +361,9 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
     lc_keep[e] = 0.0f;
   }
 
+  bool exact = false;  // flagged: the binary64 passes take the tile
   for (int p = 0; p < a.passes; ++p) {
+    bool flag = false;
     if ((p & 1) == 0) {
       // ---- row pass: pair pr takes row 16 (2w + t) + 4 g + i, t = pr / 4, i = pr % 4
       float4v a1[2][NB], a2[2][NB];
@@ -273,16 +394,19 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
         s1 = fmaf(d, x1, s1);
         s2 = fmaf(d * d, x2, s2);
       }
-      const float mean = s1 / (float)SUBW;
-      const float var = fmaxf(s2 / (float)SUBW - mean * mean, 0.0f);
-      const float sd = __builtin_amdgcn_sqrtf(var);
-      const bool upd = sd > 1e-30f && var > kZeroSpread * (s2 / (float)SUBW);
-      const float rf = upd ? __builtin_amdgcn_rcpf(sd) : rf_keep;
+      // the sums carry kCScale and its square (exact powers of two)
+      const float mean = s1 * (1.0f / (kCScale * SUBW));
+      const float ms = s2 * (1.0f / (kCScale * kCScale * SUBW));
+      const float var = ms - mean * mean;
+      const bool upd = s2 > 0.0f;
+      flag = upd && !(var > kIllCond * ms);
+      const float rf = upd ? __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(fmaxf(var, 0.0f))) : rf_keep;
       rf_keep = rf;
-      if ((m & 1) == 0) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const float f = fminf(ds[b][row] * rf, kFactorMax);
+      for (int b = 0; b < NB; ++b) {
+        const float f = ds[b][row] * rf * kRScale;
+        flag = flag || f > kFMax || (f != 0.0f && f < kFMin);
+        if ((m & 1) == 0) {
           uint16_t* base = rfl + b * 4 * kGroup;
           put_hilo(base + 0 * kGroup, base + 1 * kGroup, row, f);
           put_hilo(base + 2 * kGroup, base + 3 * kGroup, row, f * f);
@@ -319,24 +443,33 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
         float x1 = pick4(v1, i), x2 = pick4(v2, i);
         x1 += dpp<0xB1>(x1);
         x2 += dpp<0xB1>(x2);
-        const float mean = x1 / (float)kGroup;
-        const float var = fmaxf(x2 / (float)kGroup - mean * mean, 0.0f);
-        const float sig = __builtin_amdgcn_sqrtf(var);
-        const bool upd = sig > 1e-30f && var > kZeroSpread * (x2 / (float)kGroup);
-        const float cf = upd ? fminf(__builtin_amdgcn_rcpf(sig), kFactorMax) : cf_keep[e];
+        // the sums carry kRScale and its square
+        const float mean = x1 * (1.0f / (kRScale * kGroup));
+        const float ms = x2 * (1.0f / (kRScale * kRScale * kGroup));
+        const float var = ms - mean * mean;
+        const bool upd = x2 > 0.0f;
+        const float sig = __builtin_amdgcn_sqrtf(fmaxf(var, 0.0f));
+        const float cf = upd ? __builtin_amdgcn_rcpf(sig) : cf_keep[e];
         const float lc = upd ? __builtin_amdgcn_logf(sig) * 0.6931471805599453f : lc_keep[e];  // log2 -> ln
         cf_keep[e] = cf;
         lc_keep[e] = lc;
+        const float c = cf * kCScale;
+        flag = flag || (upd && !(var > kIllCond * ms)) || c > kFMax || c < kFMin;
         if ((m & 1) == 0) {
-          put_hilo(cfl + 0 * SUBW, cfl + 1 * SUBW, col, cf);
-          put_hilo(cfl + 2 * SUBW, cfl + 3 * SUBW, col, cf * cf);
+          put_hilo(cfl + 0 * SUBW, cfl + 1 * SUBW, col, c);
+          put_hilo(cfl + 2 * SUBW, cfl + 3 * SUBW, col, c * c);
           lcs[col] = lc;
         }
       }
     }
+    if (flag) L.bad[p & 1] = 1;  // read after this pass's barrier, written again two passes on
     // the other side's factors are written; every wave has read the ones the
     // pass used (CF in row passes, RF in column passes)
     __syncthreads();
+    if (L.bad[p & 1]) {
+      exact = true;
+      break;
+    }
   }
 
   // ---- column scales: centre the log scales, clamp, fp16 (thread j: column j)
@@ -344,7 +477,9 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
   const float levels = (float)((1 << bits) - 1);
   uint8_t* rec = a.arena + rec_off(y, s, layer, h, r) + (int64_t)sub * y.sub_bytes;
   uint8_t* meta = rec + y.kcode_bytes + y.vcode_bytes + kv * 2 * (SUBW + 2 * kGroup);
-  {
+  if (exact) {
+    balance_f64<SUBW>(L, ar, a.passes, meta);
+  } else {
     float v = tid < SUBW ? lcs[tid] : 0.0f;
     v += dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
     v += dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]

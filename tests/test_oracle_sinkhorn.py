@@ -152,20 +152,112 @@ def test_zero_column_keeps_its_scale():
 
 
 def test_identical_rows_keep_column_scales():
-    """A tile of identical rows (repeated tokens) has constant columns: they
-    keep lc = 0, so C = 1; the rows (all alike) are balanced."""
+    """A tile of identical rows (repeated tokens) has constant columns: their
+    spread about the first element is exactly zero, so they keep lc = 0 and
+    C = 1; the rows (all alike) are balanced."""
     row = inputs.normal_np(12, 3, 0, 256)
     r = sinkhorn.balance(np.tile(row, (128, 1)), 16)
     assert np.all(r["lc_raw"] == 0.0) and np.all(r["C"] == np.float16(1.0))
     assert np.allclose(r["lr"], np.log(row.std()), atol=1e-12)
-    # the same rows with one column perturbed by +-2^-10 of its value (a spread
-    # under 2^-8 of the RMS): it counts as constant too; by +-2^-4, it does not
+    # the same rows with one column perturbed by +-2^-10 of its value: a real
+    # spread in that column, and the even and odd rows now have slightly
+    # different spreads, so after the first row pass every column is a
+    # constant plus a small real spread: every column is balanced
     alt = np.where(np.arange(128) % 2 == 0, 1.0, -1.0)
-    for rel, const in ((2.0 ** -10, True), (2.0 ** -4, False)):
-        x = np.tile(row, (128, 1))
-        x[:, 10] = row[10] * (1.0 + rel * alt)
-        lc = sinkhorn.balance(x, 16)["lc_raw"]
-        assert (lc[10] == 0.0) == const and (not const or np.all(lc == 0.0))
+    x = np.tile(row, (128, 1))
+    x[:, 10] = row[10] * (1.0 + 2.0 ** -10 * alt)
+    lc = sinkhorn.balance(x, 16)["lc_raw"]
+    assert np.all(np.isfinite(lc)) and np.all(lc < -5.0)
+
+
+# ---------------------------------------------------------------------------
+# An independent high-precision reference: the same passes in 60-digit decimal
+# arithmetic (the spread taken about the mean, no shift), the inputs converted
+# exactly from binary64.  At 60 digits a row or column that is constant in
+# exact arithmetic comes out with a spread of ~1e-58 of its RMS; 1e-45 tells
+# it from zero with a wide margin on both sides.
+
+def _balance_decimal(x, passes):
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = 60
+        rows, cols = x.shape
+        X = [[Decimal(float(v)) for v in r] for r in x]
+        lr = [Decimal(0)] * rows
+        lc = [Decimal(0)] * cols
+        zero = Decimal("1e-45")
+        for p in range(passes):
+            if p % 2 == 0:
+                for i in range(rows):
+                    y = [X[i][j] * (-(lr[i] + lc[j])).exp() for j in range(cols)]
+                    mean = sum(y) / cols
+                    var = sum((v - mean) ** 2 for v in y) / cols
+                    ms = sum(v * v for v in y) / cols
+                    if var > zero * zero * ms:
+                        lr[i] += var.sqrt().ln()
+            else:
+                for j in range(cols):
+                    y = [X[i][j] * (-(lr[i] + lc[j])).exp() for i in range(rows)]
+                    mean = sum(y) / rows
+                    var = sum((v - mean) ** 2 for v in y) / rows
+                    ms = sum(v * v for v in y) / rows
+                    if var > zero * zero * ms:
+                        lc[j] += var.sqrt().ln()
+        m = sum(lc) / cols
+        return np.array([float(min(max(v - m, Decimal(-9)), Decimal(9))) for v in lc])
+
+
+def _small(seed, rows=16, cols=8):
+    x = inputs.normal_np(seed, 3, 0, rows * cols).reshape(rows, cols)
+    return x * np.exp(inputs.normal_np(seed, 4, 0, cols))[None, :]
+
+
+@pytest.mark.parametrize("passes", [2, 7, 16])
+def test_balance_matches_decimal_reference(passes):
+    x = _small(31)
+    assert np.max(np.abs(sinkhorn.balance(x, passes)["lc"] - _balance_decimal(x, passes))) < 1e-12
+
+
+@pytest.mark.parametrize("rel", [1e-3, 1e-5, 1e-8])
+def test_near_constant_columns_match_decimal_reference(rel):
+    """Every column a constant offset plus a spread of `rel` of it (rows =
+    one base row plus rel x noise): the spreads are real and are balanced
+    exactly as 60-digit arithmetic balances them."""
+    base = 1.0 + np.abs(inputs.normal_np(32, 1, 0, 8))
+    x = base[None, :] * (1.0 + rel * inputs.normal_np(32, 2, 0, 16 * 8).reshape(16, 8))
+    got = sinkhorn.balance(x, 16)
+    want = _balance_decimal(x, 16)
+    assert np.max(np.abs(got["lc"] - want)) < 1e-12 / rel
+    assert np.max(np.abs(got["lc"])) > 0.1          # the columns were balanced
+
+
+def test_exactly_constant_columns_keep_scales_like_the_decimal_reference():
+    """Rows that are power-of-two multiples of one row: after the first row
+    pass every column is constant in exact arithmetic, so its spread is zero
+    and its scale is kept (C = 1, as at 60 digits); float64 rounds exp(-lr_i)
+    differently per row, leaving a spread of ~1e-16 of the RMS that the
+    2^-40 floor reads as zero.  Without the floor the log scales would jump
+    by ~ln(1e-16) = -37."""
+    row = 1.0 + np.abs(inputs.normal_np(33, 1, 0, 8))
+    x = row[None, :] * np.exp2(np.arange(16) % 7 - 3.0)[:, None]
+    want = _balance_decimal(x, 16)
+    assert np.all(want == 0.0)
+    got = sinkhorn.balance(x, 16)
+    assert np.all(got["lc"] == 0.0) and np.all(got["C"] == np.float16(1.0))
+    old = sinkhorn.ZERO_SPREAD_REL
+    try:
+        sinkhorn.ZERO_SPREAD_REL = 0.0
+        wild = sinkhorn.balance(x, 16)["lc_raw"]
+    finally:
+        sinkhorn.ZERO_SPREAD_REL = old
+    assert np.max(np.abs(wild)) > 20.0
+
+
+def test_spread_is_taken_about_the_first_element():
+    y = 1e8 + np.array([[0.0, 1.0, 2.0, 3.0], [5.0, 5.0, 5.0, 5.0]])
+    sigma, rms = sinkhorn.spread(y, 1)
+    assert sigma[0] == np.std([0.0, 1.0, 2.0, 3.0]) and sigma[1] == 0.0
+    assert np.allclose(rms, 1e8 + np.array([1.5, 5.0]), rtol=1e-15)
 
 
 def test_nibble_order_every_position_and_value():

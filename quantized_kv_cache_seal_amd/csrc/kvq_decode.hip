@@ -16,16 +16,21 @@
 // workgroup (R^T is linear).  The merge kernel combines the partials of one
 // query head under one softmax and divides by the total weight.
 //
-// This path dequantises each tile into LDS as fp32 and uses plain fp32 dot
-// products: it is the reference the matrix-core body path is checked against.
+// This path is the reference the matrix-core path is checked against.  The
+// score side runs in binary64: the query is rotated exactly (a signed sum of
+// fp16 values), keys are dequantised exactly (fp16 products), the dot products
+// and the scores are binary64, so that scores in the thousands (keys near the
+// fp16 maximum) keep their fraction; each chunk's reference maximum is rounded
+// to fp32 before its weights are taken from it, so that the partial it writes
+// is exact relative to the m the merge reads.  Values and weights are fp32.
 #include "kvq_device.h"
 
 namespace kvq {
 
 // In-place rotation of one D-vector held in LDS by a 256-thread block.
 // forward: R x (signs s1 then transform then s2 for D = 128); inverse: R^T x.
-template <int D>
-__device__ void lds_rotate(float* v, const uint32_t* signs, bool inverse) {
+template <int D, typename T>
+__device__ void lds_rotate(T* v, const uint32_t* signs, bool inverse) {
   const int tid = threadIdx.x;
   if (D == 128) {
     for (int i = tid; i < D; i += 256)
@@ -36,19 +41,19 @@ __device__ void lds_rotate(float* v, const uint32_t* signs, bool inverse) {
   for (int st = 1; st < CH; st <<= 1) {
     for (int p = tid; p < D / 2; p += 256) {
       const int i = (p / st) * 2 * st + (p % st);
-      const float a = v[i], b = v[i + st];
+      const T a = v[i], b = v[i + st];
       v[i] = a + b;
       v[i + st] = a - b;
     }
     __syncthreads();
   }
   for (int i = tid; i < D; i += 256) {
-    float x = v[i];
+    T x = v[i];
     if (D == 128) {
-      x = x * (float)kInvSqrt128;
+      x = x * (T)kInvSqrt128;
       if (sign_neg(signs, (inverse ? 0 : 128) + i)) x = -x;
     } else {
-      x = x * 0.0625f;
+      x = x * (T)0.0625;
     }
     v[i] = x;
   }
@@ -57,13 +62,14 @@ __device__ void lds_rotate(float* v, const uint32_t* signs, bool inverse) {
 
 template <int D>
 __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
-  constexpr int TS = 8192 / D;  // tokens per LDS tile
+  constexpr int TS = 4096 / D;  // tokens per LDS tile
   constexpr int DP = D + 1;
   constexpr int CPT = (D + 255) / 256;
-  __shared__ float qs[kMaxGroup][D];
-  __shared__ float kt[TS][DP];
+  __shared__ double qs[kMaxGroup][D];  // query rows (binary64), later the partial rows
+  __shared__ double kt[TS][DP];
   __shared__ float vt[TS][DP];
-  __shared__ float sc[kMaxGroup][TS];
+  __shared__ double sd[kMaxGroup][TS];  // scores
+  __shared__ float sc[kMaxGroup][TS];   // weights
   __shared__ float ms[kMaxGroup], lsum[kMaxGroup], al[kMaxGroup];
 
   const Layout& y = a.y;
@@ -80,7 +86,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 
   for (int idx = tid; idx < g * D; idx += 256) {
     const int i = idx / D, j = idx % D;
-    qs[i][j] = h2f(a.q[((int64_t)b * a.Hq + h * g + i) * D + j]);
+    qs[i][j] = (double)h2f(a.q[((int64_t)b * a.Hq + h * g + i) * D + j]);
   }
   if (tid < kMaxGroup) {
     ms[tid] = -INFINITY;
@@ -88,7 +94,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   }
   __syncthreads();
   if (region != 0)
-    for (int i = 0; i < g; ++i) lds_rotate<D>(qs[i], a.signs, false);
+    for (int i = 0; i < g; ++i) lds_rotate<D, double>(qs[i], a.signs, false);
 
   int t_begin, t_end;
   if (region == 0) {
@@ -115,7 +121,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     for (int idx = tid; idx < nt * D; idx += 256) {
       const int t = idx / D, j = idx % D;
       const int tok = t0 + t;
-      float kx, vx;
+      double kx;
+      float vx;
       if (region == 0) {
         kx = h2f(sink[sink_elem(y, s, layer, h, 0, tok) + j]);
         vx = h2f(sink[sink_elem(y, s, layer, h, 1, tok) + j]);
@@ -151,8 +158,13 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
         const int vc = (ti & 1) ? (vbyte >> 4) : (vbyte & 15);
         const uint16_t* kmh = (const uint16_t*)km;
         const uint16_t* vmh = (const uint16_t*)vm;
-        kx = h2f(kmh[jj]) * (h2f(kmh[y.sub + ti]) * (float)kc + h2f(kmh[y.sub + kGroup + ti]));
-        vx = h2f(vmh[jj]) * (h2f(vmh[y.sub + ti]) * (float)vc + h2f(vmh[y.sub + kGroup + ti]));
+        // keys exact in binary64: C (S n + Z) of fp16 C, S, Z; values centred,
+        // C (S (n - 8) + (Z + 8 S)) in fp32 (Z + 8 S exact), so that rows whose
+        // range is far above their values do not cancel
+        kx = (double)h2f(kmh[jj]) *
+             ((double)h2f(kmh[y.sub + ti]) * (double)kc + (double)h2f(kmh[y.sub + kGroup + ti]));
+        const float vs = h2f(vmh[y.sub + ti]);
+        vx = h2f(vmh[jj]) * fmaf(vs, (float)vc - 8.0f, fmaf(8.0f, vs, h2f(vmh[y.sub + kGroup + ti])));
       }
       kt[t][j] = kx;
       vt[t][j] = vx;
@@ -160,19 +172,20 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     __syncthreads();
     for (int idx = tid; idx < g * nt; idx += 256) {
       const int i = idx / nt, t = idx % nt;
-      float dot = 0.0f;
-      for (int j = 0; j < D; ++j) dot = fmaf(qs[i][j], kt[t][j], dot);
-      sc[i][t] = dot * a.scale;
+      double dot = 0.0;
+      for (int j = 0; j < D; ++j) dot = fma(qs[i][j], kt[t][j], dot);
+      sd[i][t] = dot * (double)a.scale;
     }
     __syncthreads();
     if (tid < g) {
       const int i = tid;
-      float mx = ms[i];
-      for (int t = 0; t < nt; ++t) mx = fmaxf(mx, sc[i][t]);
+      double mxd = ms[i];
+      for (int t = 0; t < nt; ++t) mxd = fmax(mxd, sd[i][t]);
+      const float mx = (float)mxd;  // the chunk's reference, as the partial will hold it
       const float alpha = expf(ms[i] - mx);
       float sum = 0.0f;
       for (int t = 0; t < nt; ++t) {
-        const float p = expf(sc[i][t] - mx);
+        const float p = (float)exp(sd[i][t] - (double)mx);
         sc[i][t] = p;
         sum += p;
       }
@@ -210,10 +223,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   }
   __syncthreads();
   if (region != 0)
-    for (int i = 0; i < g; ++i) lds_rotate<D>(qs[i], a.signs, true);
+    for (int i = 0; i < g; ++i) lds_rotate<D, double>(qs[i], a.signs, true);
   for (int i = 0; i < g; ++i) {
     float* P = a.part + (((int64_t)b * a.Hq + h * g + i) * a.max_chunks + c) * part_stride(D);
-    for (int j = tid; j < D; j += 256) P[kPartHead + j] = qs[i][j];
+    for (int j = tid; j < D; j += 256) P[kPartHead + j] = (float)qs[i][j];
     if (tid == 0) {
       P[0] = ms[i];
       P[1] = lsum[i];

@@ -15,14 +15,13 @@
 // Body record math (SJ-KVaRN 2.2: column balance scales C absorbed, per-row
 // scale S and zero point Z): k_ij = C_j (S_i n_ij + Z_i), so for the rotated
 // query q' and q~_j = q'_j C_j, sigma = sum_j q~_j:
-//     q'.k_i = S_i (q~ . n_i) + Z_i sigma
+//     q'.k_i = S_i (q~ . (n_i - mid)) + (Z_i + mid S_i) sigma,   mid = 2^(b_K - 1)
 //     sum_i p_i v_ij = C_j ( sum_i (p_i S_i) (n_ij - 8) + sum_i p_i (Z_i + 8 S_i) ).
 // Ring math (tq6_0: one fp16 scale d per 128-value block, 6-bit codes u):
 //     score_t = sum_blocks d_t,b (q' . u_t,b),   out_j = sum_t (p_t d_t,b(j)) u_t,j.
 // Every inner product is dense (16 query columns, the group padded to 16) x
 // (32 codes) x (16 tokens or channels) on v_mfma_f32_16x16x32_f16, codes
-// entering exactly (key codes as fp16 subnormals n 2^-24, value and ring codes
-// as centred small integers); the non-code operand (q~, q', the weights)
+// entering exactly as centred small integers; the non-code operand (q~, q', the weights)
 // is split into hi + lo fp16 halves, two products each, which keeps fp32-level
 // precision.  The softmax scale and log2(e) are folded into the query, so
 // scores come out in log2 units.
@@ -76,39 +75,29 @@ __device__ __forceinline__ half8 nib8_centred(uint32_t w) {
   return mfma_a(u) - off;
 }
 
-// Eight 4-bit key codes of one dword as exact fp16 subnormals n 2^-24 (low
-// nibbles) or 16 n 2^-24 (high nibbles, whose 1/16 is folded into the other
-// operand): one AND per pair, slots as nib8_centred.  The matrix cores
-// multiply fp16 subnormals exactly (checked for subnormal x subnormal too);
-// the 2^24 is restored on the fp32 results.  The score needs no centre: its
-// zero-point term Z sigma is formed from the same rounded q~ operands as the
-// product, so their rounding enters both alike, and q~ takes both signs, so
-// the uncentred sums do not run away (~1e-6 relative).
-constexpr float kSub24 = 16777216.0f;  // 2^24
-__device__ __forceinline__ half8 nib8_sub(uint32_t w) {
-  const uint32_t w8 = w >> 8;
-  uint4 u;
-  u.x = w & 0x000F000Fu;
-  u.y = w & 0x00F000F0u;
-  u.z = w8 & 0x000F000Fu;
-  u.w = w8 & 0x00F000F0u;
-  return mfma_a(u);
-}
+// Key codes enter the score product centred too (nib8_centred, byte8_centred):
+// q'.k_i = S_i (q~ . (n_i - mid)) + (Z_i + mid S_i) sigma, mid = 2^(b-1).  The
+// zero point Z_i is the row minimum, so uncentred the two terms run to the size
+// of the row's range times |q~| and cancel to the score: with keys near the
+// fp16 maximum (channels at +-60,000) they reach ~1e5 in fp32 for a score of
+// ~1e3, and the matrix cores' fp32 partial sums of q~ . n lose the same bits.
+// Centred, both the products and Z + mid S stay at the size of the score.
 
 __device__ __forceinline__ uint32_t pick(const uint4& v, int e) {
   return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
 }
 
 // q~ = q' * C for one operand slot pair, split into hi + lo fp16 so that the
-// score keeps fp32-level precision: q' = qh + ql (both fp16), hi = fp16(qh C),
-// lo = fp16((qh C - hi) + ql C), with qh C - hi exact in fp32.
+// score keeps fp32-level precision: q' = qh + ql 2^-11 (both fp16, ql scaled
+// as split_h2s makes it), hi = fp16(qh C), lo = fp16((qh C - hi) 2^11 + ql C),
+// with qh C - hi exact in fp32; q~ = hi + lo 2^-11.
 __device__ __forceinline__ void qtilde_pair(uint32_t qh2, uint32_t ql2, uint32_t c2, uint32_t& hi2, uint32_t& lo2) {
   const half2v qh = as_h2(qh2), ql = as_h2(ql2), c = as_h2(c2);
   const half2v hi = qh * c;
   float r0 = fmaf((float)qh[0], (float)c[0], -(float)hi[0]);
   float r1 = fmaf((float)qh[1], (float)c[1], -(float)hi[1]);
-  r0 = fmaf((float)ql[0], (float)c[0], r0);
-  r1 = fmaf((float)ql[1], (float)c[1], r1);
+  r0 = fmaf((float)ql[0], (float)c[0], r0 * kLoScale);
+  r1 = fmaf((float)ql[1], (float)c[1], r1 * kLoScale);
   hi2 = as_u32(hi);
   lo2 = pack_h2(r0, r1);
 }
@@ -255,7 +244,7 @@ struct BodyShape {
   static constexpr int WG_PER_CU = NSUB == 2 ? 1 : 2;  // resident workgroups per compute unit
   // A sub-record's scales in LDS (stage_scales): the key C stays fp16 (the q~
   // products take it as is); the rest is widened to fp32 once, at staging:
-  // K S times 2^24 [128], K Z [128], V C [SUBW], V S [128], V Z [128].
+  // K S [128], K Z [128], V C [SUBW], V S [128], V Z [128].
   static constexpr int L_KS = 2 * SUBW, L_KZ = L_KS + 512, L_VC = L_KZ + 512, L_VS = L_VC + 4 * SUBW;
   static constexpr int L_VZ = L_VS + 512;
   static constexpr int MSTRIDE = 4096;  // LDS bytes per sub-record's scales
@@ -278,20 +267,24 @@ __device__ __forceinline__ int slot_token(int p) {  // token at position p (0..7
   return (p >> 1) + 4 * (p & 1);
 }
 
-// Eight 8-bit codes of two dwords as exact fp16 subnormals n 2^-24 in channel
-// order: one byte permute per pair (selector 12 gives a zero byte).
-__device__ __forceinline__ half8 byte8_sub(uint32_t w0, uint32_t w1) {
+// Eight 8-bit key codes of two dwords as exact centred fp16 values n - 128 in
+// channel order: one byte permute per pair puts n under the exponent byte of
+// 1024 (selector 4 takes a byte of the 0x64 pattern), one packed subtract per
+// pair removes 1024 + 128.
+__device__ __forceinline__ half8 byte8_centred(uint32_t w0, uint32_t w1) {
   uint4 u;
-  u.x = __builtin_amdgcn_perm(0u, w0, 0x0C010C00u);
-  u.y = __builtin_amdgcn_perm(0u, w0, 0x0C030C02u);
-  u.z = __builtin_amdgcn_perm(0u, w1, 0x0C010C00u);
-  u.w = __builtin_amdgcn_perm(0u, w1, 0x0C030C02u);
-  return mfma_a(u);
+  u.x = __builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u);
+  u.y = __builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u);
+  u.z = __builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u);
+  u.w = __builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u);
+  const half8 off = {(_Float16)1152.0f, (_Float16)1152.0f, (_Float16)1152.0f, (_Float16)1152.0f,
+                     (_Float16)1152.0f, (_Float16)1152.0f, (_Float16)1152.0f, (_Float16)1152.0f};
+  return mfma_a(u) - off;
 }
 
 // Thread tid's 8 bytes of a sub-record's scales (bytes 8 tid.. of the record's
 // scale block) into the LDS layout of BodyShape: key C copied, the rest as
-// fp32 at twice the offset past it (key S times 2^24).
+// fp32 at twice the offset past it.
 template <class Sh>
 __device__ __forceinline__ void stage_scales(uint8_t* dst, uint2 m, int tid) {
   const int o = 8 * tid;
@@ -300,9 +293,7 @@ __device__ __forceinline__ void stage_scales(uint8_t* dst, uint2 m, int tid) {
     return;
   }
   const half2v a = as_h2(m.x), b = as_h2(m.y);
-  const float f = o < 2 * Sh::SUBW + 256 ? kSub24 : 1.0f;
-  *(float4*)(dst + 2 * o - 2 * Sh::SUBW) =
-      make_float4(f * (float)a[0], f * (float)a[1], f * (float)b[0], f * (float)b[1]);
+  *(float4*)(dst + 2 * o - 2 * Sh::SUBW) = make_float4((float)a[0], (float)a[1], (float)b[0], (float)b[1]);
 }
 
 // q~ operands (hi, lo) of this wave's k-steps of one sub-record from its key
@@ -321,6 +312,7 @@ __device__ __forceinline__ void make_qtilde(const uint8_t* km, const uint4 (&qph
   const int i = lane & 7, g = (lane >> 3) & 3, h5 = lane >> 5;
   const int kk = Sh::KPW == 2 ? 2 * wave + h5 : wave;
   const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
+  const half2v lo_ones = {(_Float16)kLoUnscale, (_Float16)kLoUnscale};  // lo operands carry 2^11
   const uint4 c = *(const uint4*)(km + 2 * Sh::kbase(kk, g));
   uint32_t cp[4];
   if constexpr (Sh::KB == 4) {  // slot pairs (n0, n4), (n1, n5), (n2, n6), (n3, n7)
@@ -346,13 +338,13 @@ __device__ __forceinline__ void make_qtilde(const uint8_t* km, const uint4 (&qph
     qtilde_pair(qph[p].w, qpl[p].w, cp[3], hi.w, lo.w);
     float a1 = 0.0f, a16 = 0.0f;  // 4-bit keys: slots y and w carry 1/16
     a1 = __builtin_amdgcn_fdot2(as_h2(hi.x), ones, a1, false);
-    a1 = __builtin_amdgcn_fdot2(as_h2(lo.x), ones, a1, false);
+    a1 = __builtin_amdgcn_fdot2(as_h2(lo.x), lo_ones, a1, false);
     a16 = __builtin_amdgcn_fdot2(as_h2(hi.y), ones, a16, false);
-    a16 = __builtin_amdgcn_fdot2(as_h2(lo.y), ones, a16, false);
+    a16 = __builtin_amdgcn_fdot2(as_h2(lo.y), lo_ones, a16, false);
     a1 = __builtin_amdgcn_fdot2(as_h2(hi.z), ones, a1, false);
-    a1 = __builtin_amdgcn_fdot2(as_h2(lo.z), ones, a1, false);
+    a1 = __builtin_amdgcn_fdot2(as_h2(lo.z), lo_ones, a1, false);
     a16 = __builtin_amdgcn_fdot2(as_h2(hi.w), ones, a16, false);
-    a16 = __builtin_amdgcn_fdot2(as_h2(lo.w), ones, a16, false);
+    a16 = __builtin_amdgcn_fdot2(as_h2(lo.w), lo_ones, a16, false);
     if (!PK) {
       qt[kk][0][16 * g + row] = hi;
       qt[kk][1][16 * g + row] = lo;
@@ -478,9 +470,9 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
         for (int pr = 0; pr < 4; ++pr) {
           if (Sh::KB == 4) {
             const float f = (pr & 1) ? 0.0625f : 1.0f;  // pairs read from high nibbles carry 1/16
-            split_h2(row[pr] * f, row[pr + 4] * f, hb[pr], lb[pr]);
+            split_h2s(row[pr] * f, row[pr + 4] * f, hb[pr], lb[pr]);
           } else {
-            split_h2(row[2 * pr], row[2 * pr + 1], hb[pr], lb[pr]);
+            split_h2s(row[2 * pr], row[2 * pr + 1], hb[pr], lb[pr]);
           }
         }
         qph[s][p] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
@@ -548,9 +540,9 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         if (Sh::KB == 4)
-          av[i] = nib8_sub(pick(kd[s][i][kk >> 2], kk & 3));
+          av[i] = nib8_centred(pick(kd[s][i][kk >> 2], kk & 3));
         else
-          av[i] = byte8_sub(pick(kd[s][i][kk >> 1], 2 * (kk & 1)), pick(kd[s][i][kk >> 1], 2 * (kk & 1) + 1));
+          av[i] = byte8_centred(pick(kd[s][i][kk >> 1], 2 * (kk & 1)), pick(kd[s][i][kk >> 1], 2 * (kk & 1) + 1));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) sh[s][i] = mfma16(av[i], bh, sh[s][i]);
@@ -567,7 +559,7 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) sh[s][i][j] = add_x8(sh[s][i][j]);
+          for (int j = 0; j < 4; ++j) sh[s][i][j] = add_x8_lo(sh[s][i][j], lane);
     }
     // this lane's rows are positions 16 bb + 4 g + j: tokens base + {0,4,1,5}
     // (g even) or base + {2,6,3,7} (g odd), base = 16 bb + 8 (g / 2)
@@ -583,12 +575,13 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
         const int T = 16 * (2 * wave + i) + tb;
         const float2 s01 = *(const float2*)(km + Sh::L_KS + 4 * T), s45 = *(const float2*)(km + Sh::L_KS + 4 * T + 16);
         const float2 z01 = *(const float2*)(km + Sh::L_KZ + 4 * T), z45 = *(const float2*)(km + Sh::L_KZ + 4 * T + 16);
-        const float Sj[4] = {s01.x, s45.x, s01.y, s45.y};  // S 2^24
+        const float Sj[4] = {s01.x, s45.x, s01.y, s45.y};
         const float Zj[4] = {z01.x, z45.x, z01.y, z45.y};
-        const float4v dot = PK ? sh[s][i] : sh[s][i] + sl[s][i];
+        const float4v dot = PK ? sh[s][i] : sh[s][i] + sl[s][i] * kLoUnscale;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float v = fmaf(Sj[j], dot[j], Zj[j] * sig);
+          const float zc = fmaf((float)(1 << (Sh::KB - 1)), Sj[j], Zj[j]);  // Z + mid S: exact
+          const float v = fmaf(Sj[j], dot[j], zc * sig);
           sc[i][j] = s == 0 ? v : sc[i][j] + v;
         }
       }
@@ -876,7 +869,7 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
       const float* r = rows + (PK ? q16 & 7 : q16) * D + 32 * kk + 8 * g;
       uint32_t hh[4], ll[4];
 #pragma unroll
-      for (int pr = 0; pr < 4; ++pr) split_h2(r[2 * pr], r[2 * pr + 1], hh[pr], ll[pr]);
+      for (int pr = 0; pr < 4; ++pr) split_h2s(r[2 * pr], r[2 * pr + 1], hh[pr], ll[pr]);
       const uint4 hi = make_uint4(hh[0], hh[1], hh[2], hh[3]), lo = make_uint4(ll[0], ll[1], ll[2], ll[3]);
       if (PK) {
         qo[kk][0][lane] = q16 < 8 ? hi : lo;
@@ -952,9 +945,9 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
     }
 
     // ---- (2) scores of tile `wave`
-    float4v sacc[NB];
+    float4v sacc[NB], saccl[NB];  // hi and (unpacked) scaled-lo products
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) sacc[blk] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int blk = 0; blk < NB; ++blk) sacc[blk] = saccl[blk] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       half8 av;
@@ -966,13 +959,16 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
       }
       const int blk = kk / 4;
       sacc[blk] = mfma16(av, mfma_a(qo[kk][0][lane]), sacc[blk]);
-      if (!PK) sacc[blk] = mfma16(av, mfma_a(qo[kk][1][lane]), sacc[blk]);
+      if (!PK) saccl[blk] = mfma16(av, mfma_a(qo[kk][1][lane]), saccl[blk]);
     }
     if (PK) {  // lanes l and l ^ 8 both get the hi + lo sum of their column, bit for bit
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sacc[blk][r] = add_x8(sacc[blk][r]);
+        for (int r = 0; r < 4; ++r) sacc[blk][r] = add_x8_lo(sacc[blk][r], lane);
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) sacc[blk] += saccl[blk] * kLoUnscale;
     }
     float sc[4];
     float mx = -INFINITY;

@@ -37,6 +37,18 @@ __device__ __forceinline__ void split_h2(float x0, float x1, uint32_t& hi, uint3
   lo = pack_h2(x0 - h2f((uint16_t)hi), x1 - h2f((uint16_t)(hi >> 16)));
 }
 
+// The same split with the remainder stored times 2^11 (kLoScale): x = hi +
+// lo 2^-11.  The remainder is at most 2^-11 |hi|, so unscaled it falls into
+// the fp16 subnormals (absolute precision 2^-24) whenever |x| < 2^-3, and a
+// query operand near 0.1 keeps ~17 of its 22 bits; scaled, lo stays normal
+// down to |x| ~ 2^-14.  The products of lo operands take the 2^-11 back
+// (exact: a power of two).
+constexpr float kLoScale = 2048.0f, kLoUnscale = 1.0f / 2048.0f;
+__device__ __forceinline__ void split_h2s(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = pack_h2(x0, x1);
+  lo = pack_h2((x0 - h2f((uint16_t)hi)) * kLoScale, (x1 - h2f((uint16_t)(hi >> 16))) * kLoScale);
+}
+
 __device__ __forceinline__ half2v as_h2(uint32_t u) {
   half2v h;
   __builtin_memcpy(&h, &u, 4);
@@ -66,6 +78,12 @@ __device__ __forceinline__ float xmax4(float x) {
 // x + the value of lane l ^ 8 (within the 16-lane row: DPP row_ror:8)
 __device__ __forceinline__ float add_x8(float x) {
   return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+// The same for a packed hi/lo product whose columns 8..15 (lanes with bit 3
+// set) carry scaled lo operands: those lanes take the 2^-11 back first, so
+// lanes c and c + 8 add the same two values and get the same sum, bit for bit.
+__device__ __forceinline__ float add_x8_lo(float x, int lane) {
+  return add_x8((lane & 8) ? x * kLoUnscale : x);
 }
 
 // Eight 6-bit codes held as 48 bits (lo, low 16 bits of hi), as fp16 u - 32.

@@ -114,7 +114,7 @@ class Pair:
         return tq6.decode_blocks(d, u).reshape(128, self.w.head_dim)
 
     def check_records(self):
-        stats = {"codes": 0, "boundary": 0, "uncond_mismatch": 0, "scales": 0, "max_c_rel": 0.0}
+        stats = {"codes": 0, "boundary": 0, "uncond_mismatch": 0, "c_flips": 0, "scales": 0, "max_c_rel": 0.0}
         w = self.w
         sub = record.sub_width(w.head_dim)
         for s in range(self.n):
@@ -145,7 +145,18 @@ class Pair:
                                     stats["boundary"] += int(bad.sum())
                                 stats["codes"] += codes.size
                                 stats["scales"] += 1
-                                stats["uncond_mismatch"] += int((g["codes"] != o["codes"]).sum())
+                                # against the oracle's own codes: a code may differ only
+                                # where the inputs of its rounding differ (its column's
+                                # fp16 C, or its row's S or Z, which a flip of C moves)
+                                # or where it is a counted boundary code
+                                mism = g["codes"] != o["codes"]
+                                why = ((g["C"] != o["C"])[None, :] | (g["S"] != o["S"])[:, None]
+                                       | (g["Z"] != o["Z"])[:, None])
+                                if bad.any():
+                                    why = why | bad
+                                assert not (mism & ~why).any(), ("unexplained code", s, l, h, r, side, i)
+                                stats["uncond_mismatch"] += int(mism.sum())
+                                stats["c_flips"] += int((g["C"] != o["C"]).sum())
         return stats
 
     def import_oracle_records(self, first=0):

@@ -60,7 +60,9 @@ def test_records_conditional_parity(pair):
     if pair.name != "batched" or any(pair.ora.info(s, 0)[1] for s in range(pair.n)):
         assert st["scales"] > 0
     assert st["boundary"] <= max(1, st["codes"] // 10 ** 5)
-    assert st["uncond_mismatch"] <= 0.01 * max(1, st["codes"])
+    # every code that differs from the oracle's own is explained (check_records
+    # asserts it); the fp16 flips of C that explain them are rare
+    assert st["c_flips"] <= max(2, st["scales"])
 
 
 def test_decode_gpu_built_cache(pair):
@@ -420,12 +422,11 @@ def test_degenerate_inputs():
         err4 = float(np.max(np.abs(got[4] - ref4)) / np.sqrt(np.mean(ref4 ** 2)))
         _say(f"[degenerate] path={path} repeated token err={err4:.2e}")
         assert err4 <= ATTN_TOL
-        for s, tol in ((2, ATTN_TOL), (3, 1e-2)):
-            # +-60,000 keys: the score's two terms S (q~ . code) and Z sigma
-            # reach ~1e5 in fp32 while their sum is ~1e3, so the score carries
-            # ~6e-8 x 1e5 = 6e-3 of error (log2 units), ~4e-3 relative on the
-            # weights of a softmax this peaked: 1e-2 bounds it
+        for s in (2, 3):
+            # +-2,000 and +-60,000 keys (near the fp16 maximum): the key codes
+            # enter the score centred, with the zero point Z + mid S, so no two
+            # fp32 terms of the row's range cancel to the score
             ref = p.ora.attention(0, s, q[s], 1.0)
             err = float(np.max(np.abs(got[s] - ref)) / np.sqrt(np.mean(ref ** 2)))
             _say(f"[degenerate] path={path} seq {s} err={err:.2e}")
-            assert err <= tol, (path, s, err)
+            assert err <= ATTN_TOL, (path, s, err)

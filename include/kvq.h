@@ -146,6 +146,27 @@ kvq_status kvq_attn_decode(kvq_cache* cache, int32_t layer, const int32_t* seq_i
                            const void* q, void* out, int32_t out_dtype, float scale,
                            void* workspace, size_t ws_bytes, void* stream);
 
+/* kvq_attn_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same computation and kernels, with the split-K partials held in a
+ * device array the library owns instead of a caller workspace: 8 MiB
+ * (KVQ_NOALLOC_SCRATCH_BYTES) per GPU, allocated with the code object (no
+ * hipMalloc, hipFree or other allocating call) and held until the process
+ * ends.  Every call on a GPU shares that GPU's array and leaves its contents
+ * behind; calls that overlap on one GPU (several streams, or threads sharing
+ * a device) race on it and must be ordered by the caller.
+ * Arguments as kvq_attn_decode without workspace and ws_bytes.  Errors: those
+ * of kvq_attn_decode; KVQ_ERR_CAPACITY when the call's partials exceed the
+ * array, in which case nothing is enqueued.  The partials take n_seqs x
+ * n_q_heads x (chunks per sequence) x (head_dim + 4) x 4 bytes: ~3.2 MB for
+ * one 110,592-token sequence or 16 of 65,536 tokens (4 x 256 KV heads, 24
+ * query heads, matrix-core plan), ~4.2 MB at 512-wide heads; many sequences
+ * with short bodies, or the vector-ALU path (one partial per record), can
+ * need more. */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+kvq_status kvq_attn_decode_noalloc(kvq_cache* cache, int32_t layer, const int32_t* seq_ids, int32_t n_seqs,
+                                   const void* q, void* out, int32_t out_dtype, float scale, void* stream);
+
 /* One decode step of one layer: append one token per listed sequence, seal
  * what a KVQ_SEAL_IF_FULL seal of the layer would seal, then decode
  * attention of q over every cached token including the new one (SJ-KVaRN

@@ -23,6 +23,8 @@
 // fp16 maximum) keep their fraction; each chunk's reference maximum is rounded
 // to fp32 before its weights are taken from it, so that the partial it writes
 // is exact relative to the m the merge reads.  Values and weights are fp32.
+#include <mutex>
+
 #include "kvq_device.h"
 
 namespace kvq {
@@ -348,6 +350,37 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Device scratch of the allocation-free decode (kvq_attn_decode_noalloc): the
+// split-K partial rows of one call.  One array per GPU the library runs on,
+// held until the process ends; every call on a GPU shares it, so calls that
+// overlap on one GPU race.  Nothing in it needs clearing: every partial row a
+// merge reads is written by the same call first.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+// The array's device address on the current device.  In host code the name
+// `scratch` is a host-side stand-in, not a device address, so the address is
+// taken once per device with hipGetSymbolAddress (with that device current)
+// and kept; callers pass it to the kernels as they pass a workspace.
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace kvq

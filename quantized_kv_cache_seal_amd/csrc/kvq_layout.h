@@ -11,6 +11,7 @@
 // [K: C[SUB] S[128] Z[128] fp16][V: C S Z], codes packed two per byte (even
 // element in the low nibble) at 4 bits or one per byte at 8 bits.
 #pragma once
+#include <stddef.h>
 #include <stdint.h>
 
 namespace kvq {
@@ -23,6 +24,10 @@ constexpr int kMaxLaunchSeqs = 32;
 constexpr int kMaxSealTasks = 64;
 constexpr int kMaxGroup = 16;     // query heads per KV head
 constexpr int kMaxChunks = 4096;  // split-K partials per (sequence, query head)
+// Bytes of the per-GPU scratch array that holds the partials of the
+// allocation-free decode (8 MiB: the matrix-core plans of the benchmarked
+// workloads need at most ~4.2 MB).
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
 // A split-K partial row: [m, l, 0, 0, acc[D]] fp32, acc 16-byte aligned and in
 // the original domain (the producer rotates its rotated-domain sums back).
 constexpr int kPartHead = 4;

@@ -23,6 +23,7 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int grid_x, hipStream_t strea
 hipError_t launch_decode_main(const DecodeArgs& a, int n_items, hipStream_t stream);
 hipError_t launch_decode_ring(const DecodeArgs& a, int n_items, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_tbq4_encode(const Tbq4CodecArgs& a, hipStream_t stream);
 hipError_t launch_tbq4_decode(const Tbq4CodecArgs& a, hipStream_t stream);
 hipError_t launch_tbq4_attn(const Tbq4AttnArgs& a, int grid_x, hipStream_t stream);
@@ -30,6 +31,7 @@ hipError_t launch_tq_codec(const Tbq4CodecArgs& a, int bits, bool encode, hipStr
 }  // namespace kvq
 
 using namespace kvq;
+static_assert(kNoAllocScratchBytes == KVQ_NOALLOC_SCRATCH_BYTES, "scratch size as the header states it");
 
 struct kvq_cache {
   kvq_config cfg;
@@ -414,7 +416,7 @@ static kvq_status check_decode_args(const kvq_cache* c, int32_t layer, const int
 // ring and that no seal is due; the token is written and counted here.
 static kvq_status decode_impl(kvq_cache* c, int32_t layer, const int32_t* seq_ids, int32_t n_seqs, const void* q,
                               void* out, int32_t out_dtype, float scale, void* workspace, size_t ws_bytes,
-                              void* stream, const void* k_new, const void* v_new) {
+                              void* stream, const void* k_new, const void* v_new, bool noalloc = false) {
   const bool fused = k_new != nullptr;
   const bool use_mfma = c->path != KVQ_PATH_VALU && mfma_supported(c->y);
   const bool staged = c->path != KVQ_PATH_VALU && staged_supported(c->y);
@@ -455,7 +457,11 @@ static kvq_status decode_impl(kvq_cache* c, int32_t layer, const int32_t* seq_id
   if (max_chunks > kMaxChunks) return fail(KVQ_ERR_CAPACITY, "too many split-K chunks");
   const int Hq = c->cfg.n_q_heads, D = c->y.D;
   const size_t need = (size_t)n_seqs * Hq * max_chunks * part_stride(D) * sizeof(float);
-  if (ws_bytes < need) return fail(KVQ_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  if (ws_bytes < need)
+    return noalloc ? fail(KVQ_ERR_CAPACITY,
+                          "the allocation-free decode holds %zu bytes of split-K partials per GPU; this call needs "
+                          "%zu (fewer sequences per call, or kvq_attn_decode with a workspace)", ws_bytes, need)
+                   : fail(KVQ_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   const size_t out_elem = out_dtype == KVQ_OUT_F16 ? 2 : 4;
   for (int b0 = 0; b0 < n_seqs; b0 += kMaxLaunchSeqs) {
     DecodeArgs a{};
@@ -526,6 +532,17 @@ kvq_status kvq_attn_decode(kvq_cache* c, int32_t layer, const int32_t* seq_ids, 
   if (st != KVQ_OK || n_seqs == 0) return st;
   return decode_impl(c, layer, seq_ids, n_seqs, q, out, out_dtype, scale, workspace, ws_bytes, stream, nullptr,
                      nullptr);
+}
+
+kvq_status kvq_attn_decode_noalloc(kvq_cache* c, int32_t layer, const int32_t* seq_ids, int32_t n_seqs,
+                                   const void* q, void* out, int32_t out_dtype, float scale, void* stream) {
+  void* scratch = nullptr;
+  kvq_status st = check_decode_args(c, layer, seq_ids, n_seqs, q, out, out_dtype, (void*)&scratch);
+  if (st != KVQ_OK || n_seqs == 0) return st;
+  hipError_t e = noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "scratch address");
+  return decode_impl(c, layer, seq_ids, n_seqs, q, out, out_dtype, scale, scratch, kNoAllocScratchBytes, stream,
+                     nullptr, nullptr, true);
 }
 
 kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, const int32_t* seq_ids, int32_t n_seqs, const void* k,

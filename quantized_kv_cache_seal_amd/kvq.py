@@ -22,7 +22,7 @@ FLAG_PLAN_ONLY = 1
 
 EXPORTS = [
     "kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_append", "kvq_seal",
-    "kvq_workspace_bytes", "kvq_attn_decode", "kvq_decode_step", "kvq_set_decode_path", "kvq_seq_info", "kvq_seq_reset",
+    "kvq_workspace_bytes", "kvq_attn_decode", "kvq_attn_decode_noalloc", "kvq_decode_step", "kvq_set_decode_path", "kvq_seq_info", "kvq_seq_reset",
     "kvq_seq_truncate", "kvq_seq_save_bytes", "kvq_seq_save", "kvq_seq_restore", "kvq_export", "kvq_import",
     "kvq_unit_bytes", "kvq_profile_start", "kvq_profile_stop",
     "kvq_tbq4_tables", "kvq_tbq4_encode", "kvq_tbq4_decode", "kvq_tbq4_workspace_bytes", "kvq_tbq4_attn_decode",
@@ -67,6 +67,7 @@ def lib():
             "kvq_seal": [vp, i32, i32, vp, P(i32)],
             "kvq_workspace_bytes": [vp, i32, P(sz)],
             "kvq_attn_decode": [vp, i32, P(i32), i32, vp, vp, i32, ctypes.c_float, vp, sz, vp],
+            "kvq_attn_decode_noalloc": [vp, i32, P(i32), i32, vp, vp, i32, ctypes.c_float, vp],
             "kvq_decode_step": [vp, i32, P(i32), i32, vp, vp, vp, vp, i32, ctypes.c_float, vp, sz, vp, P(i32)],
             "kvq_set_decode_path": [vp, i32],
             "kvq_seq_info": [vp, i32, i32, P(i64), P(i64), P(i32)],
@@ -204,6 +205,20 @@ class Cache:
         check(lib().kvq_attn_decode(self.h, layer, ids, n, ctypes.c_void_p(q.data_ptr()),
                                     ctypes.c_void_p(out.data_ptr()), OUT_F16 if out_f16 else OUT_F32,
                                     float(scale), ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream)))
+        return out
+
+    def attn_decode_noalloc(self, layer, seq_ids, q, out=None, scale=1.0, out_f16=False, stream=None):
+        """attn_decode with the split-K partials in the library's per-GPU scratch
+        array (kvq_attn_decode_noalloc); out must be given by callers that
+        cannot allocate."""
+        import torch
+        ids, n = _ids(seq_ids)
+        assert q.is_contiguous() and q.dtype == torch.float16
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float16 if out_f16 else torch.float32, device=q.device)
+        check(lib().kvq_attn_decode_noalloc(self.h, layer, ids, n, ctypes.c_void_p(q.data_ptr()),
+                                            ctypes.c_void_p(out.data_ptr()), OUT_F16 if out_f16 else OUT_F32,
+                                            float(scale), _stream(stream)))
         return out
 
     def decode_step(self, layer, seq_ids, k, v, q, out=None, scale=1.0, out_f16=False, workspace=None,

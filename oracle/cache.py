@@ -25,6 +25,15 @@ Readings:
   first); appending beyond the per-sequence context capacity fails.
 The rotation, staging codec, balancing and rounding are the other oracle
 modules; this one only moves tokens between regions and builds records.
+
+Staging precision (SJ-KVaRN section 4.1: a 6-bit tail instead of 16-bit; KV
+Cache Precision Tail, section 2: KVarN's exact tail is F16, its staging and
+record path F16-based): with stage="f16" the ring holds each token's key and
+value exactly as given, in the original domain like the sink (an exact tail:
+unquantized floating point).  The seal then reads the group's fp16 rows and
+rotates them, R x computed exactly and rounded once to fp32 -- the values the
+6-bit staging would have quantised -- and balances and rounds them as usual.
+Decode reads f16 ring tokens as they are, like the sink.
 """
 from __future__ import annotations
 
@@ -65,8 +74,9 @@ class OracleCache:
     """Host model of one cache: every (sequence, layer) has its own regions."""
 
     def __init__(self, n_layers, n_kv_heads, head_dim, n_q_heads, max_seqs, max_ctx,
-                 tail_min, tail_max, margin=512, k_bits=4, v_bits=4, passes=16, signs=None):
-        assert head_dim in (128, 256, 512)
+                 tail_min, tail_max, margin=512, k_bits=4, v_bits=4, passes=16, signs=None, stage="tq6"):
+        assert head_dim in (128, 256, 512) and stage in ("tq6", "f16")
+        self.stage = stage
         assert tail_min % GROUP == 0 and tail_min <= tail_max
         self.L, self.H, self.D, self.Hq = n_layers, n_kv_heads, head_dim, n_q_heads
         self.max_seqs, self.max_ctx = max_seqs, max_ctx
@@ -89,6 +99,7 @@ class OracleCache:
                 "sink_k": np.zeros((SINK, H, D), np.float16), "sink_v": np.zeros((SINK, H, D), np.float16),
                 "ring_d": np.zeros((2, cap, H, nb), np.float16),
                 "ring_u": np.full((2, cap, H, nb, tq6.BLOCK), 32, np.uint8),
+                "ring_x": np.zeros((2, cap, H, D), np.float16),   # f16 staging: tokens as given
                 "records": [[] for _ in range(H)],
             }
         return self.st[key]
@@ -128,6 +139,9 @@ class OracleCache:
             if rest.any():
                 slots = (pos[rest] - SINK) % self.cap
                 for side, src in ((0, k16[b, rest]), (1, v16[b, rest])):
+                    if self.stage == "f16":
+                        s["ring_x"][side, slots] = src
+                        continue
                     x = rotation.rotate(src, self.D, self.signs).reshape(-1, self.H, self.nb, tq6.BLOCK)
                     d, u = tq6.encode_blocks(x)
                     s["ring_d"][side, slots] = d
@@ -140,6 +154,8 @@ class OracleCache:
         """Dequantised rotated fp32 values of 128 ring tokens: (128, D)."""
         s = self._state(seq, layer)
         slots = [(group_start_token + i - SINK) % self.cap for i in range(GROUP)]
+        if self.stage == "f16":
+            return rotation.rotate(s["ring_x"][side, slots, head], self.D, self.signs)
         d = s["ring_d"][side, slots, head]
         u = s["ring_u"][side, slots, head]
         return tq6.decode_blocks(d, u).reshape(GROUP, self.D)
@@ -177,6 +193,8 @@ class OracleCache:
         s = self._state(seq, layer)
         if region == REGION_SINK:
             return s["sink_k"][index, head].tobytes() + s["sink_v"][index, head].tobytes()
+        if region == REGION_RING and self.stage == "f16":
+            return s["ring_x"][0, index, head].tobytes() + s["ring_x"][1, index, head].tobytes()
         if region == REGION_RING:
             out = b""
             for side in (0, 1):
@@ -192,6 +210,11 @@ class OracleCache:
         test hook that places chosen staged tiles."""
         s = self._state(seq, layer)
         buf = bytes(buf)
+        if self.stage == "f16":
+            assert len(buf) == 4 * self.D
+            x = np.frombuffer(buf, np.float16).reshape(2, self.D)
+            s["ring_x"][:, slot, head] = x
+            return
         assert len(buf) == 2 * self.nb * tq6.BLOCK_BYTES
         for side in (0, 1):
             for b in range(self.nb):
@@ -228,6 +251,9 @@ class OracleCache:
         if n_tok > t0:
             slots = [(t - SINK) % self.cap for t in range(t0, n_tok)]
             for side, lst in ((0, ks), (1, vs)):
+                if self.stage == "f16":
+                    lst.append(s["ring_x"][side, slots, head].astype(np.float64))
+                    continue
                 x = tq6.decode_blocks(s["ring_d"][side, slots, head], s["ring_u"][side, slots, head])
                 lst.append(rotation.inverse_exact(x.reshape(len(slots), self.D), self.D, self.signs))
         return np.concatenate(ks), np.concatenate(vs)

@@ -128,3 +128,97 @@ def test_gqa_sink_only_cache():
         ref = attention.attend(q[h].astype(np.float64), k[:, h // 3].astype(np.float64),
                                v[:, h // 3].astype(np.float64), 1 / math.sqrt(128))
         assert np.array_equal(out[h], ref)
+
+
+# ---------------------------------------------------------------------------
+# Staging precision: the f16 ring (SJ-KVaRN section 4.1; KV Cache Precision
+# Tail, section 2: KVarN's exact F16 tail).
+
+def test_f16_staging_ring_size_printed():
+    """The f16 ring costs 65,536 - 25,088 = 40,448 more bytes per slot than
+    tq6_0 in the Qwen 27B-like shape; a ring of tail_max 8,192 + one 512-token
+    micro-batch holds 8,704 slots: 0.33 GB more, the low end of the printed
+    0.33 to 0.39 GB (the high end matches ~10,240 slots, 8,192 + 2,048)."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "printed_numbers.json")))
+    e = g["f16_staging_extra_gb_at_100k"]
+    per_slot = sizes.kv_bytes_per_token(16, 4, 256, 16) - sizes.kv_bytes_per_token(16, 4, 256, tq6.BITS_PER_VALUE)
+    assert per_slot == 40448
+    extra = cache.ring_capacity(8192, 512) * per_slot / sizes.GIB
+    assert round(extra, e["digits"]) == e["value"]
+    assert round(cache.ring_capacity(8192, 2048) * per_slot / sizes.GIB, 2) == e["upper"]
+
+
+def _f16_pair(D, signs):
+    w = configs.TINY.scaled(head_dim=D, n_q_heads=4, ctx=1200, tail_min=256, tail_max=384)
+    spec = inputs.KVSpec(1, 1, D, 5, outliers=3, outlier_scale=10.0)
+    k = spec.tokens(0, "k", 0, w.ctx)[None]
+    v = spec.tokens(0, "v", 0, w.ctx)[None]
+    caches = []
+    for stage in ("f16", "tq6"):
+        c = cache.OracleCache(1, 1, D, 4, 1, w.ctx, w.tail_min, w.tail_max, w.margin, 4, 4, 8, signs, stage=stage)
+        for t0 in range(0, w.ctx, 200):
+            assert c.append(0, [0], k[:, t0:t0 + 200], v[:, t0:t0 + 200]) == cache.OK
+            c.seal(0, cache.SEAL_IF_FULL)
+        caches.append(c)
+    return w, k[0], v[0], caches
+
+
+@pytest.mark.parametrize("D", [256, 128])
+def test_f16_staging_ring_holds_tokens_and_seals_their_rotation(D):
+    """Ring slots hold the tokens bit for bit; each sealed record is the
+    balancing and rounding of the group's tokens rotated exactly and rounded
+    once to fp32 (written out here from the rotation, balancing and rounding
+    functions); the seal schedule is the tq6 one."""
+    from oracle import record
+    signs = inputs.rotation_signs(3) if D == 128 else None
+    w, k, v, (c16, c6) = _f16_pair(D, signs)
+    assert c16.info(0, 0) == c6.info(0, 0)
+    n_tok, n_rec, ring = c16.info(0, 0)
+    assert n_rec > 0 and ring > 0
+    for t in range(128 + 128 * n_rec, n_tok):
+        slot = (t - 128) % c16.cap
+        assert c16.export(0, 0, 0, cache.REGION_RING, slot) == k[t, 0].tobytes() + v[t, 0].tobytes()
+    for r in range(n_rec):
+        toks = slice(128 + 128 * r, 256 + 128 * r)
+        want = []
+        for x16 in (k[toks, 0], v[toks, 0]):
+            xr = rotation.rotate(x16, D, signs)
+            want.append(cache.encode_tile(xr[:, :record.sub_width(D)], 8, 4))
+        got = record.parse_record(c16.export(0, 0, 0, cache.REGION_BODY, r), D, 4, 4)[0]
+        for g_, w_ in zip(got, want):
+            for n in ("codes", "C", "S", "Z"):
+                assert np.array_equal(g_[n], w_[n]), (r, n)
+
+
+def test_f16_staging_attention_is_exact_over_the_ring():
+    """Attention over an f16-staged cache equals float64 attention over the
+    sink and ring tokens as given plus the records dequantised and rotated
+    back (brute force, written out here); against the tq6-staged cache of
+    the same tokens it differs only by the staged ring's quantisation."""
+    from oracle import record, rounding
+    w, k, v, (c16, c6) = _f16_pair(256, None)
+    n_tok, n_rec, ring = c16.info(0, 0)
+    q = inputs.queries(5, 0, 0, 1, 4, 256)[0]
+    keys = [k[:128, 0].astype(np.float64)]
+    vals = [v[:128, 0].astype(np.float64)]
+    for r in range(n_rec):
+        kk, vv = record.parse_record(c16.export(0, 0, 0, cache.REGION_BODY, r), 256, 4, 4)[0]
+        keys.append(rotation.inverse_exact(rounding.dequant(kk["codes"], kk["C"], kk["S"], kk["Z"]), 256))
+        vals.append(rotation.inverse_exact(rounding.dequant(vv["codes"], vv["C"], vv["S"], vv["Z"]), 256))
+    keys.append(k[128 + 128 * n_rec:n_tok, 0].astype(np.float64))
+    vals.append(v[128 + 128 * n_rec:n_tok, 0].astype(np.float64))
+    K, V = np.concatenate(keys), np.concatenate(vals)
+    qf = q.astype(np.float64)
+    want = []
+    for h in range(4):
+        s = K @ qf[h]
+        p = np.exp(s - s.max())
+        want.append(p @ V / p.sum())
+    got = c16.attention(0, 0, q, 1.0)
+    assert np.max(np.abs(got - np.array(want))) < 1e-12
+    # the two stagings differ (the tq6 ring and the records sealed from it
+    # carry its 6-bit rounding), by a small fraction of the N(0, 1) values
+    other = c6.attention(0, 0, q, 1.0)
+    assert 0 < np.max(np.abs(got - other)) < 0.1

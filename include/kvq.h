@@ -53,6 +53,11 @@ enum { KVQ_REGION_SINK = 0, KVQ_REGION_RING = 1, KVQ_REGION_BODY = 2 };
 enum { KVQ_OUT_F32 = 0, KVQ_OUT_F16 = 1 };
 enum { KVQ_PATH_AUTO = 0, KVQ_PATH_VALU = 1, KVQ_PATH_MFMA = 2 };
 enum { KVQ_FLAG_PLAN_ONLY = 1 };   /* metadata only: no arena, no kernels */
+/* Staging precision of the ring (SJ-KVaRN section 4.1): tq6_0, the rotated
+ * 6-bit format (98 bytes per 128 values), or f16, the tokens kept exact in
+ * the original domain (the KVarN-style exact F16 tail: KV Cache Precision
+ * Tail, section 2), rotated when their group is sealed. */
+enum { KVQ_STAGE_TQ6 = 0, KVQ_STAGE_F16 = 1 };
 
 /* Sizes are in tokens unless noted.  Constraints checked by every call:
  *   head_dim in {128, 256, 512}; n_q_heads a multiple of n_kv_heads with
@@ -80,6 +85,8 @@ typedef struct {
    * 128-wide heads: entries 0..127 are applied before the transform, 128..255
    * after; bit b of word w set means entry 64*w+b is -1.  Ignored otherwise. */
   uint64_t rot_signs[4];
+  int32_t stage_fmt;        /* KVQ_STAGE_TQ6 (0, the default) or KVQ_STAGE_F16 */
+  int32_t reserved;         /* must be 0 */
 } kvq_config;
 
 typedef struct kvq_cache kvq_cache;
@@ -105,7 +112,8 @@ kvq_status kvq_cache_destroy(kvq_cache* cache);
  * later position is rotated (section 2.2; 128-wide heads: KV cache math) and
  * written to the ring slot (p - 128) mod capacity as tq6_0 blocks (98 bytes
  * per 128 values: an fp16 scale d = fp16(amax/31) and 128 six-bit codes
- * q + 32, q = clamp(rne(x / d), -31, 31)).
+ * q + 32, q = clamp(rne(x / d), -31, 31)), or, with f16 staging, copied to
+ * that slot unchanged (original domain, like the sink).
  * seq_ids: host [n_seqs], distinct, in [0, max_seqs).
  * k, v: device fp16 [n_seqs][n_tok][n_kv_heads][head_dim], contiguous.
  * Never seals: if the ring cannot take the tokens it returns
@@ -119,7 +127,8 @@ kvq_status kvq_append(kvq_cache* cache, int32_t layer, const int32_t* seq_ids, i
  * layer with ring length n: with KVQ_SEAL_IF_FULL nothing happens unless
  * n >= tail_max; then (both modes) the oldest floor((n - tail_min)/128)
  * groups are sealed: each 128-token x 256-channel tile (128-channel for
- * 128-wide heads) of K and of V is read back from the ring, balanced by
+ * 128-wide heads) of K and of V is read back from the ring (f16 staging: the
+ * fp16 rows rotated, exactly, rounded once to fp32), balanced by
  * sinkhorn_passes alternating row/column log-domain passes (section 2.2),
  * divided by its fp16 column scales C, and each row rounded to k_bits / v_bits
  * with its own fp16 scale S and zero point Z.
@@ -231,7 +240,8 @@ kvq_status kvq_seq_restore(kvq_cache* cache, int32_t seq, const void* host_src, 
 /* Copy canonical bytes of one cache unit to the host, synchronising `stream`:
  *   KVQ_REGION_SINK, index = token (< 128): [K fp16 x head_dim][V fp16 x head_dim];
  *   KVQ_REGION_RING, index = ring slot: for K then V, head_dim/128 tq6_0
- *     blocks of 98 bytes, each [fp16 d][96-byte LSB-first 6-bit stream];
+ *     blocks of 98 bytes, each [fp16 d][96-byte LSB-first 6-bit stream]
+ *     (f16 staging: [K fp16 x head_dim][V fp16 x head_dim], as the sink);
  *   KVQ_REGION_BODY, index = record: the record bytes, per 256-channel
  *     sub-tile (128 for 128-wide heads) [K codes 128 tokens x sub, row-major,
  *     two 4-bit codes per byte with the even channel low, or one 8-bit code]

@@ -28,6 +28,7 @@ class Workload:
     tail_max: int = 8192
     margin: int = 512        # ring slack beyond tail_max (one micro-batch)
     k_dist: str = "normal"
+    stage: str = "tq6"       # staging ring: "tq6" (rotated 6-bit) or "f16" (exact, original domain)
     outliers: int = 0
     outlier_scale: float = 1.0
     seed: int = 1
@@ -55,5 +56,8 @@ QWEN14B1M = Workload("qwen14b1m-like-48x8x128-ctx262144-k8v4", n_layers=48, n_kv
 BATCHED = Workload("batched-16seq-16x4x256-ctx65536", n_layers=16, n_kv_heads=4, head_dim=256,
                    n_q_heads=24, ctx=65_536, n_seqs=16, tail_min=4096, tail_max=4352,
                    outliers=5, outlier_scale=15.0, seed=5)
+
+# config 1 again with the KVarN-style f16 staging ring (SJ-KVaRN section 4.1)
+TINY_F16 = TINY.scaled(name="tiny-1x1x256-ctx2048-f16stage", stage="f16")
 
 ALL = [TINY, QWEN27B, GEMMA31B, QWEN14B1M, BATCHED]

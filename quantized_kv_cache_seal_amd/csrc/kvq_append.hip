@@ -3,7 +3,8 @@
 //
 // SJ-KVaRN 2.1 items 1-2: the first 128 tokens stay at 16 bits; every later
 // token's key and value are rotated (2.2) and written to the staging ring as
-// tq6_0 (98 bytes per 128 values).
+// tq6_0 (98 bytes per 128 values).  With f16 staging (section 4.1's 16-bit
+// alternative) a later token is copied to its ring slot as it is.
 #include "kvq_encode.h"
 
 namespace kvq {
@@ -23,6 +24,11 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
     return;
   }
   const int slot = (int)((pos - kSink) % y.cap);
+  if (y.f16ring) {
+    uint16_t* dst = (uint16_t*)(a.arena + rcode_off(y, s, a.layer, h, kv, slot));
+    for (int i = lane; i < y.D; i += 64) dst[i] = src[i];
+    return;
+  }
   uint8_t* codes = a.arena + rcode_off(y, s, a.layer, h, kv, slot);
   uint16_t* scales = (uint16_t*)(a.arena + rscale_off(y, s, a.layer, h, kv, slot));
   if (y.D == 128) {

@@ -85,6 +85,9 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   const int s = sq.slot, layer = a.layer;
   const int region = c == 0 ? 0 : (c < 1 + sq.n_ring_chunks ? 1 : 2);
   if (!((a.valu_regions >> region) & 1)) return;  // region handled by a matrix-core kernel
+  // ring (tq6_0 staging) and body are read in the rotated domain; the sink and
+  // an f16-staged ring in the original domain
+  const bool rotated = region == 2 || (region == 1 && !y.f16ring);
 
   for (int idx = tid; idx < g * D; idx += 256) {
     const int i = idx / D, j = idx % D;
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     lsum[tid] = 0.0f;
   }
   __syncthreads();
-  if (region != 0)
+  if (rotated)
     for (int i = 0; i < g; ++i) lds_rotate<D, double>(qs[i], a.signs, false);
 
   int t_begin, t_end;
@@ -128,6 +131,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
       if (region == 0) {
         kx = h2f(sink[sink_elem(y, s, layer, h, 0, tok) + j]);
         vx = h2f(sink[sink_elem(y, s, layer, h, 1, tok) + j]);
+      } else if (region == 1 && y.f16ring) {
+        const int slot = (sq.ring0 + tok) % y.cap;
+        kx = h2f(((const uint16_t*)(a.arena + rcode_off(y, s, layer, h, 0, slot)))[j]);
+        vx = h2f(((const uint16_t*)(a.arena + rcode_off(y, s, layer, h, 1, slot)))[j]);
       } else if (region == 1) {
         const int slot = (sq.ring0 + tok) % y.cap;
         const int blk = j / kQBlock, k = j % kQBlock;
@@ -224,7 +231,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  if (region != 0)
+  if (rotated)
     for (int i = 0; i < g; ++i) lds_rotate<D, double>(qs[i], a.signs, true);
   for (int i = 0; i < g; ++i) {
     float* P = a.part + (((int64_t)b * a.Hq + h * g + i) * a.max_chunks + c) * part_stride(D);

@@ -737,6 +737,9 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
 // ---------------------------------------------------------------------------
 // Sink / ring role: chunk c of one KV head, c = 0 the sink (n_sink fp16 tokens,
 // original domain), c >= 1 ring tokens [(c - 1) ring_chunk, c ring_chunk).
+// With f16 staging the ring chunks are read as the sink is: fp16 rows in the
+// original domain, scored with the unrotated query, their sums not rotated
+// back (the rows wrap around the ring's slots).
 // The chunk is scanned in steps of 64 tokens with an online softmax:
 //   (1) value codes (ring: 6-bit codes decoded; sink: fp16 rows) are written
 //       transposed into an fp16 tile V^T in LDS;
@@ -851,19 +854,20 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
   float(*xl)[16] = (float(*)[16])(smem + Ly::X + 256);
 
   const bool sink = c == 0;
+  const bool exact = sink || y.f16ring;  // fp16 rows in the original domain
   const int t_begin = sink ? 0 : (c - 1) * a.ring_chunk;
   const int t_end = sink ? sq.n_sink : min(sq.ring_len, c * a.ring_chunk);
 
   QueryRaw<D> qraw;
   query_load<D>(a, b, h, wave, lane, qraw);
   RingRegs<D> ra, rb;
-  if (!sink) ring_load<D>(a, sq, h, t_begin, t_end - t_begin, ra);
+  if (!exact) ring_load<D>(a, sq, h, t_begin, t_end - t_begin, ra);
 
   // ---- query operands in natural channel order, rotated (ring) or not (sink),
   // kept in LDS: wave w forms k-steps w, w + 4, ...
   {
     float* rows = (float*)vt;
-    query_rows<D>(a, qraw, !sink, rows, wave, lane);
+    query_rows<D>(a, qraw, !exact, rows, wave, lane);
     __syncthreads();
     for (int kk = wave; kk < KK; kk += 4) {
       const float* r = rows + (PK ? q16 & 7 : q16) * D + 32 * kk + 8 * g;
@@ -880,8 +884,18 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
     }
     __syncthreads();
   }
-  const uint16_t* ksink = (const uint16_t*)(a.arena + y.off_sink) + sink_elem(y, sq.slot, a.layer, h, 0, 0);
-  const uint16_t* vsink = (const uint16_t*)(a.arena + y.off_sink) + sink_elem(y, sq.slot, a.layer, h, 1, 0);
+  // fp16 rows: the sink's token t, or the f16 ring's token t at slot ring0 + t
+  const uint16_t* ksrc = sink ? (const uint16_t*)(a.arena + y.off_sink) + sink_elem(y, sq.slot, a.layer, h, 0, 0)
+                              : (const uint16_t*)(a.arena + rcode_off(y, sq.slot, a.layer, h, 0, 0));
+  const uint16_t* vsrc = sink ? (const uint16_t*)(a.arena + y.off_sink) + sink_elem(y, sq.slot, a.layer, h, 1, 0)
+                              : (const uint16_t*)(a.arena + rcode_off(y, sq.slot, a.layer, h, 1, 0));
+  auto row16 = [&](int t) -> int64_t {
+    if (sink) return (int64_t)t * D;
+    int sl = sq.ring0 + t;
+    sl = sl >= y.cap ? sl - y.cap : sl;
+    sl = sl >= y.cap ? sl - y.cap : sl;
+    return (int64_t)sl * D;
+  };
 
   float m_run = -INFINITY, m_ref = -INFINITY, l_part = 0.0f;
   float4v acc[CPW];
@@ -905,14 +919,14 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
       uint4 r[ITEMS][4];
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        ks_op[kk] = *(const uint4*)(ksink + (int64_t)(t0 + 16 * wave + q16) * D + 32 * kk + 8 * g);
+        ks_op[kk] = *(const uint4*)(ksrc + row16(t0 + 16 * wave + q16) + 32 * kk + 8 * g);
 #pragma unroll
       for (int j = 0; j < ITEMS; ++j) {
         const int it = tid + 256 * j, tq = it % (kStep / 4), c8 = it / (kStep / 4);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int tok = 4 * tq + k;
-          r[j][k] = *(const uint4*)(vsink + (int64_t)(t0 + (tok < n ? tok : 0)) * D + 8 * c8);
+          r[j][k] = *(const uint4*)(vsrc + row16(t0 + (tok < n ? tok : 0)) + 8 * c8);
         }
       }
 #pragma unroll
@@ -1043,7 +1057,7 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
     }
     __syncthreads();  // V^T and the weights are free
   };
-  if (sink) {
+  if (exact) {
     for (int t0 = t_begin; t0 < t_end; t0 += kStep) step(std::true_type{}, t0, ra, rb);
   } else {
     for (int t0 = t_begin;;) {
@@ -1070,7 +1084,7 @@ __device__ __forceinline__ void ring_role(const DecodeArgs& a, int b, int h, int
     for (int i = 0; i < CPW; ++i) *(float4v*)(rows + q16 * D + 16 * (CPW * wave + i) + 4 * g) = acc[i];
   }
   __syncthreads();
-  write_partial_rows<D>(a, b, h, c, rows, m_ref, xl, !sink, wave, lane);
+  write_partial_rows<D>(a, b, h, c, rows, m_ref, xl, !exact, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1091,7 +1105,16 @@ __device__ __forceinline__ void append_role(const DecodeArgs& a, int b, int h, u
   float* rows = (float*)smem;  // [16][D] query rows
   float* kv = rows + 16 * D;   // [2][D] decoded key and value
   uint8_t* arena = const_cast<uint8_t*>(a.arena);  // the one region this launch writes
-  if (wave < 2) {
+  if (wave < 2 && y.f16ring) {  // f16 staging: the token as it is, in the original domain
+    const uint16_t* src = (wave ? a.v_new : a.k_new) + ((int64_t)b * y.H + h) * D;
+    uint16_t* dst = (uint16_t*)(arena + rcode_off(y, sq.slot, a.layer, h, wave, sq.app_slot));
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const uint16_t e = src[VPL * lane + j];
+      dst[VPL * lane + j] = e;
+      kv[D * wave + VPL * lane + j] = h2f(e);
+    }
+  } else if (wave < 2) {
     const uint16_t* src = (wave ? a.v_new : a.k_new) + ((int64_t)b * y.H + h) * D;
     uint8_t* codes = arena + rcode_off(y, sq.slot, a.layer, h, wave, sq.app_slot);
     uint16_t* scales = (uint16_t*)(arena + rscale_off(y, sq.slot, a.layer, h, wave, sq.app_slot));
@@ -1112,12 +1135,12 @@ __device__ __forceinline__ void append_role(const DecodeArgs& a, int b, int h, u
   }
   QueryRaw<D> qraw;
   query_load<D>(a, b, h, wave, lane, qraw);
-  query_rows<D>(a, qraw, true, rows, wave, lane);
+  query_rows<D>(a, qraw, !y.f16ring, rows, wave, lane);
   __syncthreads();
-  float vo[VPL];  // the value, rotated back: the same accumulator for every query head
+  float vo[VPL];  // the value in the original domain: the same accumulator for every query head
 #pragma unroll
   for (int j = 0; j < VPL; ++j) vo[j] = kv[D + VPL * lane + j];
-  rotate_back<D>(vo, lane, a.signs);
+  if (!y.f16ring) rotate_back<D>(vo, lane, a.signs);
   for (int i = wave; i < G; i += 4) {
     float s = 0.0f;
 #pragma unroll

@@ -5,6 +5,8 @@
 //   sink        fp16  [S][L][H][2 (K,V)][128][D]            original domain
 //   ring codes  u8    [S][L][H][2][CAP][NB][96]             6-bit LSB-first codes
 //   ring scales fp16  [S][L][H][2][CAP][NB]                 d of each block
+// or, with f16 staging, the ring as fp16 [S][L][H][2][CAP][D] in the original
+// domain (the codes' place; no scales).
 //   body        u8    [S][L][H][MAX_REC][REC_BYTES]         sealed records
 // A record is NSUB sub-records of SUB channels (SUB = 256, or 128 for 128-wide
 // heads), each [K codes 128 x SUB row-major][V codes SUB x 128 channel-major]
@@ -34,7 +36,7 @@ constexpr int kPartHead = 4;
 __host__ __device__ inline int part_stride(int D) { return D + kPartHead; }
 
 struct Layout {
-  int32_t S, L, H, D, NB, cap, nsub, sub, kbits, vbits, max_rec, pad0;
+  int32_t S, L, H, D, NB, cap, nsub, sub, kbits, vbits, max_rec, f16ring;  // f16ring: f16 staging
   int64_t sub_bytes, rec_bytes, kcode_bytes, vcode_bytes;
   int64_t off_sink, off_rcode, off_rscale, off_body, total;
 };
@@ -47,9 +49,12 @@ __host__ __device__ inline int64_t slh(const Layout& y, int s, int l, int h) {
 __host__ __device__ inline int64_t sink_elem(const Layout& y, int s, int l, int h, int kv, int t) {
   return ((slh(y, s, l, h) * 2 + kv) * kSink + t) * (int64_t)y.D;
 }
-// byte offset (from arena) of ring codes[s][l][h][kv][slot][0]
+// bytes of one ring row (one token of one head, K or V): tq6_0 codes, or fp16
+__host__ __device__ inline int ring_row_bytes(const Layout& y) { return y.f16ring ? 2 * y.D : y.NB * kQBytes; }
+// byte offset (from arena) of ring codes[s][l][h][kv][slot][0] (with f16
+// staging: of the slot's fp16 row)
 __host__ __device__ inline int64_t rcode_off(const Layout& y, int s, int l, int h, int kv, int slot) {
-  return y.off_rcode + ((slh(y, s, l, h) * 2 + kv) * y.cap + slot) * (int64_t)(y.NB * kQBytes);
+  return y.off_rcode + ((slh(y, s, l, h) * 2 + kv) * y.cap + slot) * (int64_t)ring_row_bytes(y);
 }
 // byte offset of ring scales[s][l][h][kv][slot][0]
 __host__ __device__ inline int64_t rscale_off(const Layout& y, int s, int l, int h, int kv, int slot) {
@@ -79,6 +84,7 @@ struct SealArgs {
   uint8_t* arena;
   Layout y;
   int32_t passes, n_tasks, total_groups, pad;
+  uint32_t signs[8];  // f16 staging, 128-wide heads: the rotation's sign flips
   SealTask task[kMaxSealTasks];
 };
 

@@ -90,6 +90,8 @@ static kvq_status check_config(const kvq_config* c) {
     return fail(KVQ_ERR_INVALID, "sinkhorn_passes must be in [0, 64]");
   if ((int64_t)c->tail_max + c->margin > (1 << 28)) return fail(KVQ_ERR_INVALID, "ring too large");
   if (c->flags & ~KVQ_FLAG_PLAN_ONLY) return fail(KVQ_ERR_INVALID, "unknown flags");
+  if ((c->stage_fmt != KVQ_STAGE_TQ6 && c->stage_fmt != KVQ_STAGE_F16) || c->reserved != 0)
+    return fail(KVQ_ERR_INVALID, "stage_fmt must be KVQ_STAGE_TQ6 or KVQ_STAGE_F16 (reserved 0)");
   return KVQ_OK;
 }
 
@@ -106,6 +108,7 @@ static Layout make_layout(const kvq_config& c) {
   y.kbits = c.k_bits;
   y.vbits = c.v_bits;
   y.max_rec = (int32_t)std::max<int64_t>(0, (c.max_ctx - kSink) / kGroup);
+  y.f16ring = c.stage_fmt == KVQ_STAGE_F16;
   y.kcode_bytes = (int64_t)kGroup * y.sub * y.kbits / 8;
   y.vcode_bytes = (int64_t)y.sub * kGroup * y.vbits / 8;
   y.sub_bytes = y.kcode_bytes + y.vcode_bytes + 4 * (y.sub + 2 * kGroup);
@@ -115,9 +118,9 @@ static Layout make_layout(const kvq_config& c) {
   y.off_sink = off;
   off = round_up(off + slh * 2 * kSink * y.D * 2, 256);
   y.off_rcode = off;
-  off = round_up(off + slh * 2 * y.cap * (int64_t)y.NB * kQBytes, 256);
-  y.off_rscale = off;
-  off = round_up(off + slh * 2 * y.cap * (int64_t)y.NB * 2, 256);
+  off = round_up(off + slh * 2 * y.cap * (int64_t)ring_row_bytes(y), 256);
+  y.off_rscale = off;  // f16 staging has no block scales
+  off = round_up(off + (y.f16ring ? 0 : slh * 2 * y.cap * (int64_t)y.NB * 2), 256);
   y.off_body = off;
   off = round_up(off + slh * y.max_rec * y.rec_bytes, 256);
   y.total = off;
@@ -351,6 +354,7 @@ kvq_status kvq_seal(kvq_cache* c, int32_t layer, int32_t mode, void* stream, int
     a.arena = c->arena;
     a.y = c->y;
     a.passes = c->cfg.sinkhorn_passes;
+    std::memcpy(a.signs, c->signs, sizeof a.signs);
     a.n_tasks = (int32_t)std::min<size_t>(kMaxSealTasks, tasks.size() - t0);
     int32_t first = 0;
     for (int i = 0; i < a.n_tasks; ++i) {
@@ -664,12 +668,12 @@ kvq_status kvq_seq_truncate(kvq_cache* c, int32_t seq, int32_t layer, int64_t n_
 // records of each (layer, KV head), which are contiguous from record 0.
 namespace {
 constexpr uint32_t kSaveMagic = 0x5351564Bu;  // "KVQS"
-constexpr uint32_t kSaveVersion = 1;
+constexpr uint32_t kSaveVersion = 2;
 struct SaveHeader {
   uint32_t magic, version;
   // layout fingerprint: a blob restores only into a cache that lays the same
   // bytes out the same way and encodes further tokens the same way
-  int32_t L, H, D, NB, cap, kbits, vbits, sinkhorn_passes;
+  int32_t L, H, D, NB, cap, kbits, vbits, sinkhorn_passes, stage_fmt, pad;
   int64_t rec_bytes;
   uint64_t rot_signs[4];
 };
@@ -680,9 +684,9 @@ SeqSpans seq_spans(const Layout& y, int s) {
   SeqSpans p;
   p.sink_n = (int64_t)y.L * y.H * 2 * kSink * y.D * 2;
   p.sink_off = y.off_sink + (int64_t)s * p.sink_n;
-  p.rcode_n = (int64_t)y.L * y.H * 2 * y.cap * y.NB * kQBytes;
+  p.rcode_n = (int64_t)y.L * y.H * 2 * y.cap * ring_row_bytes(y);
   p.rcode_off = y.off_rcode + (int64_t)s * p.rcode_n;
-  p.rscale_n = (int64_t)y.L * y.H * 2 * y.cap * y.NB * 2;
+  p.rscale_n = y.f16ring ? 0 : (int64_t)y.L * y.H * 2 * y.cap * y.NB * 2;
   p.rscale_off = y.off_rscale + (int64_t)s * p.rscale_n;
   return p;
 }
@@ -698,6 +702,7 @@ SaveHeader save_header(const kvq_cache* c) {
   hd.kbits = c->y.kbits;
   hd.vbits = c->y.vbits;
   hd.sinkhorn_passes = c->cfg.sinkhorn_passes;
+  hd.stage_fmt = c->cfg.stage_fmt;
   hd.rec_bytes = c->y.rec_bytes;
   for (int i = 0; i < 4; ++i) hd.rot_signs[i] = c->cfg.rot_signs[i];
   return hd;
@@ -737,6 +742,7 @@ kvq_status kvq_seq_save(const kvq_cache* c, int32_t seq, void* host_dst, size_t 
   hipStream_t sm = (hipStream_t)stream;
   const int64_t spans[3][2] = {{p.sink_off, p.sink_n}, {p.rcode_off, p.rcode_n}, {p.rscale_off, p.rscale_n}};
   for (const auto& sp : spans) {
+    if (sp[1] == 0) continue;
     hipError_t e = hipMemcpyAsync(out + o, c->arena + sp[0], (size_t)sp[1], hipMemcpyDeviceToHost, sm);
     if (e != hipSuccess) return hip_fail(e, "save copy");
     o += (size_t)sp[1];
@@ -785,6 +791,7 @@ kvq_status kvq_seq_restore(kvq_cache* c, int32_t seq, const void* host_src, size
   hipStream_t sm = (hipStream_t)stream;
   const int64_t spans[3][2] = {{p.sink_off, p.sink_n}, {p.rcode_off, p.rcode_n}, {p.rscale_off, p.rscale_n}};
   for (const auto& sp : spans) {
+    if (sp[1] == 0) continue;
     hipError_t e = hipMemcpyAsync(c->arena + sp[0], in + o, (size_t)sp[1], hipMemcpyHostToDevice, sm);
     if (e != hipSuccess) return hip_fail(e, "restore copy");
     o += (size_t)sp[1];
@@ -810,7 +817,7 @@ kvq_status kvq_unit_bytes(const kvq_cache* c, int32_t region, size_t* bytes) {
   if (!c || !bytes) return fail(KVQ_ERR_INVALID, "bad arguments");
   switch (region) {
     case KVQ_REGION_SINK: *bytes = (size_t)2 * c->y.D * 2; return KVQ_OK;
-    case KVQ_REGION_RING: *bytes = (size_t)2 * c->y.NB * (2 + kQBytes); return KVQ_OK;
+    case KVQ_REGION_RING: *bytes = c->y.f16ring ? (size_t)2 * c->y.D * 2 : (size_t)2 * c->y.NB * (2 + kQBytes); return KVQ_OK;
     case KVQ_REGION_BODY: *bytes = (size_t)c->y.rec_bytes; return KVQ_OK;
   }
   return fail(KVQ_ERR_INVALID, "bad region %d", region);
@@ -844,6 +851,9 @@ static kvq_status copy_unit(const kvq_cache* c, int32_t seq, int32_t layer, int3
     for (int kv = 0; kv < 2; ++kv)
       pieces.push_back({y.off_sink + sink_elem(y, seq, layer, h, kv, (int)index) * 2, (size_t)kv * y.D * 2,
                         (size_t)y.D * 2});
+  } else if (region == KVQ_REGION_RING && y.f16ring) {
+    for (int kv = 0; kv < 2; ++kv)
+      pieces.push_back({rcode_off(y, seq, layer, h, kv, (int)index), (size_t)kv * y.D * 2, (size_t)y.D * 2});
   } else if (region == KVQ_REGION_RING) {
     size_t ho = 0;
     for (int kv = 0; kv < 2; ++kv)

@@ -598,8 +598,231 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     seal_tile<SUBW, 1>(a, L, r, sub, h, tk.slot, tk.layer);
 }
 
+// ---------------------------------------------------------------------------
+// Seal of f16-staged tiles (SJ-KVaRN 4.1: the 16-bit alternative to tq6_0
+// staging; KV Cache Precision Tail, section 2: KVarN's exact F16 tail).  The
+// ring holds the tokens in the original domain, so the seal first rotates the
+// group's rows (SJ-KVaRN 2.2; 128-wide heads: the randomized Walsh-Hadamard
+// transform of KV cache math): each row's signed sum of fp16 values is exact
+// in binary64 across the wave (the staging encoder's arithmetic) and is
+// rounded once to fp32, into an fp32 tile in LDS.  That tile has no integer
+// structure for the matrix cores, and this staging serves small caches, so it
+// is balanced by the binary64 passes (balance_f64's definition, read from the
+// fp32 tile) and rounded in IEEE fp32 exactly as the 6-bit path rounds.
+template <int SUBW>
+struct SealF16Lds {
+  float x[kGroup][SUBW];  // the rotated tile
+  double lr[kGroup], lc[SUBW], fr[kGroup], fc[SUBW];
+  double red64[4];
+  float invc[SUBW], rinv[kGroup], zrow[kGroup];
+};
+
+template <int SUBW>
+__global__ __launch_bounds__(256) void seal_f16_kernel(SealArgs a) {
+  __shared__ SealF16Lds<SUBW> L;
+  constexpr int VPL = SUBW / 64;
+  const Layout& y = a.y;
+  const int gx = blockIdx.x;
+  int ti = 0;
+  while (ti + 1 < a.n_tasks && gx >= a.task[ti + 1].first) ++ti;
+  const SealTask tk = a.task[ti];
+  const int r = tk.rec0 + (gx - tk.first);
+  int by = blockIdx.y;
+  const int sub = by % y.nsub;
+  by /= y.nsub;
+  const int kv = by & 1, h = by >> 1, s = tk.slot, layer = tk.layer;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int slot0 = (int)(((int64_t)r * kGroup) % y.cap);
+  const uint16_t* ring = (const uint16_t*)(a.arena + rcode_off(y, s, layer, h, kv, 0));
+
+  // ---- rotate: wave w takes rows w, w + 4, ...; lane l holds elements VPL l ..
+  for (int row = w; row < kGroup; row += 4) {
+    int slot = slot0 + row;
+    if (slot >= y.cap) slot -= y.cap;
+    const uint16_t* src = ring + (int64_t)slot * y.D + sub * SUBW;
+    double v[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int i = VPL * l + j;
+      const double e = (double)h2f(src[i]);
+      v[j] = SUBW == 128 && sign_neg(a.signs, i) ? -e : e;
+    }
+#pragma unroll
+    for (int st = 1; st < VPL; st <<= 1)
+#pragma unroll
+      for (int j = 0; j < VPL; ++j)
+        if (!(j & st)) {
+          const double p = v[j], q = v[j + st];
+          v[j] = p + q;
+          v[j + st] = p - q;
+        }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1)
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) {
+        const double o = shfl_xor_d(v[j], m);
+        v[j] = (l & m) ? (o - v[j]) : (v[j] + o);
+      }
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      double e;
+      if (SUBW == 128) {
+        e = v[j] * kInvSqrt128;
+        if (sign_neg(a.signs, 128 + VPL * l + j)) e = -e;
+      } else {
+        e = v[j] * 0.0625;
+      }
+      L.x[row][VPL * l + j] = (float)e;
+    }
+  }
+  for (int i = tid; i < kGroup; i += 256) L.lr[i] = 0.0;
+  for (int j = tid; j < SUBW; j += 256) L.lc[j] = 0.0;
+  __syncthreads();
+
+  // ---- binary64 balancing
+  const int hf = tid & 1;
+  for (int p = 0; p < a.passes; ++p) {
+    for (int i = tid; i < kGroup; i += 256) L.fr[i] = exp(-L.lr[i]);
+    for (int j = tid; j < SUBW; j += 256) L.fc[j] = exp(-L.lc[j]);
+    __syncthreads();
+    if ((p & 1) == 0) {  // row tid / 2, columns hf SUBW / 2 .. + SUBW / 2
+      const int row = tid >> 1, c0 = hf * (SUBW / 2);
+      const double frow = L.fr[row];
+      const double ref = (double)L.x[row][0] * frow * L.fc[0];
+      double s1 = 0.0, s2 = 0.0, sq = 0.0;
+      for (int c = c0; c < c0 + SUBW / 2; ++c) {
+        const double yy = (double)L.x[row][c] * frow * L.fc[c], dv = yy - ref;
+        s1 += dv;
+        s2 += dv * dv;
+        sq += yy * yy;
+      }
+      s1 += __shfl_xor(s1, 1, 64);
+      s2 += __shfl_xor(s2, 1, 64);
+      sq += __shfl_xor(sq, 1, 64);
+      const double mean = s1 / SUBW, sig = sqrt(fmax(s2 / SUBW - mean * mean, 0.0));
+      if (hf == 0 && sig > kZeroSpread64 * sqrt(sq / SUBW)) L.lr[row] += log(sig);
+    } else {  // column tid (256 wide), or tid / 2 with rows hf 64 .. + 64 (128 wide)
+      constexpr int TPC = 256 / SUBW, NR = kGroup / TPC;
+      const int col = tid / TPC, r0 = TPC == 2 ? hf * NR : 0;
+      const double fcol = L.fc[col];
+      const double ref = (double)L.x[0][col] * L.fr[0] * fcol;
+      double s1 = 0.0, s2 = 0.0, sq = 0.0;
+      for (int rr = r0; rr < r0 + NR; ++rr) {
+        const double yy = (double)L.x[rr][col] * L.fr[rr] * fcol, dv = yy - ref;
+        s1 += dv;
+        s2 += dv * dv;
+        sq += yy * yy;
+      }
+      if (TPC == 2) {
+        s1 += __shfl_xor(s1, 1, 64);
+        s2 += __shfl_xor(s2, 1, 64);
+        sq += __shfl_xor(sq, 1, 64);
+      }
+      const double mean = s1 / kGroup, sig = sqrt(fmax(s2 / kGroup - mean * mean, 0.0));
+      if ((TPC == 1 || hf == 0) && sig > kZeroSpread64 * sqrt(sq / kGroup)) L.lc[col] += log(sig);
+    }
+    __syncthreads();
+  }
+
+  // ---- column scales
+  const int bits = kv ? y.vbits : y.kbits;
+  const float levels = (float)((1 << bits) - 1);
+  uint8_t* rec = a.arena + rec_off(y, s, layer, h, r) + (int64_t)sub * y.sub_bytes;
+  uint8_t* meta = rec + y.kcode_bytes + y.vcode_bytes + kv * 2 * (SUBW + 2 * kGroup);
+  {
+    double v = tid < SUBW ? L.lc[tid] : 0.0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+    if (l == 0) L.red64[w] = v;
+    __syncthreads();
+    const double lmean = (L.red64[0] + L.red64[1] + L.red64[2] + L.red64[3]) / SUBW;
+    if (tid < SUBW) {
+      const double c = fmin(fmax(L.lc[tid] - lmean, -9.0), 9.0);
+      const half_t ch = (half_t)exp(c);
+      uint16_t cb;
+      __builtin_memcpy(&cb, &ch, 2);
+      ((uint16_t*)meta)[tid] = cb;
+      L.invc[tid] = 1.0f / h2f(cb);
+    }
+    __syncthreads();
+  }
+
+  // ---- per-row rounding: row tid / 2, columns hf SUBW / 2 .. + SUBW / 2
+  {
+    const int row = tid >> 1, c0 = hf * (SUBW / 2);
+    float mn = INFINITY, mx = -INFINITY;
+    for (int c = c0; c < c0 + SUBW / 2; ++c) {
+      const float yv = L.x[row][c] * L.invc[c];
+      mn = fminf(mn, yv);
+      mx = fmaxf(mx, yv);
+    }
+    mn = fminf(mn, __shfl_xor(mn, 1, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+    uint16_t Sb = f2h_sat_bits((mx - mn) / levels);
+    if (h2f(Sb) == 0.0f) Sb = 0x3C00;  // 1.0
+    const uint16_t Zb = f2h_sat_bits(mn);
+    const float Zf = h2f(Zb), inv = 1.0f / h2f(Sb);
+    if (hf == 0) {
+      ((uint16_t*)(meta + 2 * SUBW))[row] = Sb;
+      ((uint16_t*)(meta + 2 * SUBW + 2 * kGroup))[row] = Zb;
+      L.rinv[row] = inv;
+      L.zrow[row] = Zf;
+    }
+    if (kv == 0) {  // keys: row-major, two 4-bit codes per byte (even channel low) or one 8-bit code
+      for (int c = c0; c < c0 + SUBW / 2; c += 8) {
+        uint32_t cq[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float yv = L.x[row][c + e] * L.invc[c + e];
+          cq[e] = (uint32_t)__builtin_amdgcn_fmed3f(rintf((yv - Zf) * inv), 0.0f, levels);
+        }
+        if (bits == 4) {
+          uint32_t pk = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pk |= cq[e] << (4 * e);
+          *(uint32_t*)(rec + (int64_t)row * (SUBW / 2) + c / 2) = pk;
+        } else {
+          uint2 pk = make_uint2(0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pk.x |= cq[e] << (8 * e);
+            pk.y |= cq[e + 4] << (8 * e);
+          }
+          *(uint2*)(rec + (int64_t)row * SUBW + c) = pk;
+        }
+      }
+    }
+  }
+  if (kv == 1) {  // values: channel-major, two tokens per byte (even token low)
+    __syncthreads();
+    uint8_t* vbase = rec + y.kcode_bytes;
+    for (int col = tid; col < SUBW; col += 256) {
+      const float ic = L.invc[col];
+      for (int t0 = 0; t0 < kGroup; t0 += 8) {
+        uint32_t pk = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int row = t0 + e;
+          const float yv = L.x[row][col] * ic;
+          const uint32_t c = (uint32_t)__builtin_amdgcn_fmed3f(rintf((yv - L.zrow[row]) * L.rinv[row]), 0.0f, levels);
+          pk |= c << (4 * e);
+        }
+        *(uint32_t*)(vbase + (int64_t)col * (kGroup / 2) + t0 / 2) = pk;
+      }
+    }
+  }
+}
+
 hipError_t launch_seal(const SealArgs& a, hipStream_t stream) {
   dim3 grid(a.total_groups, 2 * a.y.H * a.y.nsub);
+  if (a.y.f16ring) {
+    if (a.y.vbits != 4) return hipErrorInvalidValue;
+    if (a.y.sub == 256)
+      hipLaunchKernelGGL(seal_f16_kernel<256>, grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(seal_f16_kernel<128>, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   if (a.y.sub == 256)
     hipLaunchKernelGGL(seal_kernel<256>, grid, dim3(256), 0, stream, a);
   else

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(HERE, "libkvq.so")
 
 OK, ERR_INVALID, ERR_CAPACITY, ERR_RING_FULL, ERR_SEALED, ERR_DEVICE, ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
 SEAL_IF_FULL, SEAL_TO_MIN = 0, 1
+STAGE_TQ6, STAGE_F16 = 0, 1
 REGION_SINK, REGION_RING, REGION_BODY = 0, 1, 2
 OUT_F32, OUT_F16 = 0, 1
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
@@ -44,6 +45,7 @@ class Config(ctypes.Structure):
         ("tail_max", ctypes.c_int32), ("margin", ctypes.c_int32), ("max_ctx", ctypes.c_int64),
         ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32), ("sinkhorn_passes", ctypes.c_int32),
         ("flags", ctypes.c_int32), ("rot_signs", ctypes.c_uint64 * 4),
+        ("stage_fmt", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -109,8 +111,10 @@ def check(status: int) -> int:
 
 
 def make_config(n_layers, n_kv_heads, head_dim, n_q_heads, max_seqs, max_ctx, tail_min, tail_max,
-                margin=512, k_bits=4, v_bits=4, passes=16, sign_words=(0, 0, 0, 0), flags=0) -> Config:
+                margin=512, k_bits=4, v_bits=4, passes=16, sign_words=(0, 0, 0, 0), flags=0,
+                stage=STAGE_TQ6) -> Config:
     c = Config()
+    c.stage_fmt = stage
     c.n_layers, c.n_kv_heads, c.head_dim, c.n_q_heads = n_layers, n_kv_heads, head_dim, n_q_heads
     c.max_seqs, c.max_ctx, c.tail_min, c.tail_max, c.margin = max_seqs, max_ctx, tail_min, tail_max, margin
     c.k_bits, c.v_bits, c.sinkhorn_passes, c.flags = k_bits, v_bits, passes, flags
@@ -312,7 +316,8 @@ def config_for(w, max_ctx=None, max_seqs=None, sign_words=(0, 0, 0, 0), flags=0)
     return make_config(w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads,
                        max_seqs if max_seqs is not None else w.n_seqs,
                        max_ctx if max_ctx is not None else w.ctx, w.tail_min, w.tail_max, w.margin,
-                       w.k_bits, w.v_bits, w.passes, sign_words, flags)
+                       w.k_bits, w.v_bits, w.passes, sign_words, flags,
+                       STAGE_F16 if getattr(w, "stage", "tq6") == "f16" else STAGE_TQ6)
 
 
 # --- TBQ4 comparator codec ---------------------------------------------------

@@ -40,7 +40,8 @@ class Pair:
         max_ctx = max(lens) + extra_ctx
         self.gpu = kvq.Cache(kvq.config_for(w, max_ctx=max_ctx, max_seqs=self.n, sign_words=words))
         self.ora = ocache.OracleCache(w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads, self.n, max_ctx,
-                                      w.tail_min, w.tail_max, w.margin, w.k_bits, w.v_bits, w.passes, signs)
+                                      w.tail_min, w.tail_max, w.margin, w.k_bits, w.v_bits, w.passes, signs,
+                                      stage=w.stage)
         self.specs = [seq_spec(w, s) for s in range(self.n)]
         self.kv = {}   # (s, layer) -> (k, v) fp16 numpy [len][H][D]
         for s in range(self.n):
@@ -107,8 +108,11 @@ class Pair:
         return n_units
 
     def tile_inputs(self, s, l, h, r, side):
-        """Rotated, tq6-staged fp32 tile of record r, recomputed from the inputs."""
+        """Rotated, tq6-staged fp32 tile of record r, recomputed from the inputs
+        (f16 staging: the rotation alone)."""
         x16 = self.kv[(s, l)][side][128 + 128 * r:256 + 128 * r, h]
+        if self.w.stage == "f16":
+            return rotation.rotate(x16, self.w.head_dim, self.signs)
         x = rotation.rotate(x16, self.w.head_dim, self.signs).reshape(128, -1, 128)
         d, u = tq6.encode_blocks(x)
         return tq6.decode_blocks(d, u).reshape(128, self.w.head_dim)

@@ -41,10 +41,14 @@ def test_config_validation():
         assert kvq.lib().kvq_cache_bytes(ctypes.byref(bad), ctypes.byref(n)) == kvq.ERR_INVALID, field
     g17 = kvq.make_config(1, 1, 256, 17, 1, 4096, 256, 512)
     assert kvq.lib().kvq_cache_bytes(ctypes.byref(g17), ctypes.byref(n)) == kvq.ERR_INVALID
+    for field, val in (("stage_fmt", 2), ("stage_fmt", -1), ("reserved", 1)):
+        bad = kvq.make_config(2, 4, 256, 24, 1, 4096, 256, 512)
+        setattr(bad, field, val)
+        assert kvq.lib().kvq_cache_bytes(ctypes.byref(bad), ctypes.byref(n)) == kvq.ERR_INVALID, field
 
 
 def test_arena_size_matches_layout():
-    for w in configs.ALL:
+    for w in configs.ALL + [configs.TINY_F16, configs.QWEN27B.scaled(stage="f16")]:
         cfg = kvq.config_for(w)
         n = ctypes.c_size_t()
         kvq.check(kvq.lib().kvq_cache_bytes(ctypes.byref(cfg), ctypes.byref(n)))
@@ -52,8 +56,11 @@ def test_arena_size_matches_layout():
         cap = ocache.ring_capacity(w.tail_max, w.margin)
         rup = lambda x: -(-x // 256) * 256
         expect = rup(S * L * H * 2 * 128 * D * 2)
-        expect += rup(S * L * H * 2 * cap * (D // 128) * 96)
-        expect += rup(S * L * H * 2 * cap * (D // 128) * 2)
+        if w.stage == "f16":  # the ring as fp16 rows, no block scales
+            expect += rup(S * L * H * 2 * cap * D * 2)
+        else:
+            expect += rup(S * L * H * 2 * cap * (D // 128) * 96)
+            expect += rup(S * L * H * 2 * cap * (D // 128) * 2)
         expect += rup(S * L * H * ocache.max_records(w.ctx) * record.record_bytes(D, w.k_bits, w.v_bits))
         assert n.value == expect, w.name
     # the 110,592-token shape: 831 records in use, 863 allocated, 34,816 B each
@@ -65,6 +72,8 @@ def test_unit_bytes():
     assert c.unit_bytes(kvq.REGION_SINK) == 2 * 512 * 2
     assert c.unit_bytes(kvq.REGION_RING) == 2 * 4 * 98
     assert c.unit_bytes(kvq.REGION_BODY) == record.record_bytes(512, 4, 4)
+    c16 = _plan(kvq.make_config(1, 2, 512, 4, 1, 4096, 256, 512, stage=kvq.STAGE_F16))
+    assert c16.unit_bytes(kvq.REGION_RING) == 2 * 512 * 2
 
 
 def test_plan_only_schedule_matches_oracle():

@@ -16,6 +16,13 @@ pytestmark = pytest.mark.gpu
 SMALL = {
     # config 1 as specified (1 layer, 1 KV head, 256, GQA 4, 2,048 tokens, 8 passes, tail 256/512)
     "tiny": (configs.TINY, [2048], 512, None),
+    # config 1 as specified with the f16 staging ring (KVarN-style exact tail)
+    "tiny_f16": (configs.TINY_F16, [2048], 512, None),
+    # f16 staging at 128-wide heads (randomized WHT at seal time) and at 512-wide heads, ragged
+    "qwen14b_f16": (configs.QWEN14B1M.scaled(n_layers=1, n_kv_heads=2, n_q_heads=10, tail_min=256, tail_max=512,
+                                             ctx=1500, stage="f16"), [1500, 700], 300, "signs"),
+    "gemma_f16": (configs.GEMMA31B.scaled(n_layers=1, tail_min=256, tail_max=512, ctx=1300, stage="f16"),
+                  [1300], 256, None),
     # config 2 shape, two layers, ragged chunking
     "qwen27b": (configs.QWEN27B.scaled(n_layers=2, tail_min=256, tail_max=512, ctx=2600), [2600], 300, None),
     # config 3 shape: 512-wide heads as two 256-point halves, Student-t keys
@@ -251,7 +258,7 @@ def test_groups_over_eight(shape, group):
     assert p.check_sink_ring() > 0
 
 
-@pytest.mark.parametrize("name", ["qwen27b", "batched", "gemma", "qwen14b"])
+@pytest.mark.parametrize("name", ["qwen27b", "batched", "gemma", "qwen14b", "tiny_f16", "qwen14b_f16"])
 def test_decode_step(name):
     """kvq_decode_step (append one token, seal if full, decode) step after step:
     one fused launch while every new token lands in the ring and no seal is due,
@@ -272,8 +279,12 @@ def test_decode_step(name):
     elif name == "gemma":  # 512-wide heads, two sequences
         w = configs.GEMMA31B.scaled(n_layers=1, tail_min=256, tail_max=384, ctx=1000)
         lens = [1000, 700]
-    else:                    # 128-wide heads, randomized WHT, 8-bit keys
-        w = configs.QWEN14B1M.scaled(n_layers=1, n_kv_heads=2, n_q_heads=10, tail_min=256, tail_max=384, ctx=1000)
+    elif name == "tiny_f16":  # config 1 with the f16 staging ring
+        w = configs.TINY_F16.scaled(tail_min=256, tail_max=384, ctx=1000)
+        lens = [1000]
+    else:                    # 128-wide heads, randomized WHT, 8-bit keys (f16 staging too)
+        w = configs.QWEN14B1M.scaled(n_layers=1, n_kv_heads=2, n_q_heads=10, tail_min=256, tail_max=384, ctx=1000,
+                                     stage="f16" if name.endswith("f16") else "tq6")
         lens = [1000]
         signs = inputs.rotation_signs(w.seed)
     _say(f"[step {name}] build lens={lens}")

@@ -41,6 +41,20 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_main_kernel_qwen27b_ctx
 KERNEL_SOURCE = os.path.join(ROOT, "quantized_kv_cache_seal_amd", "csrc", "kvq_decode_fused.hip")
 
 
+def profile_record(key):
+    """The `key:` record line of the decode profile summary as a dict, or None
+    when the summary is missing or the kernel source has changed since it was
+    taken."""
+    import hashlib
+    try:
+        line = next(l for l in open(TRAFFIC_PROFILE) if l.startswith(key + ":"))
+    except (OSError, StopIteration):
+        return None
+    rec = dict(kv.split("=", 1) for kv in line.split()[1:])
+    src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    return rec if rec.get("kernel_sha256") == src else None
+
+
 def measured_traffic():
     """HBM bytes per launch of the main decode kernel from the counter runs
     recorded in the profile summary (FETCH_SIZE and WRITE_SIZE in KiB per
@@ -194,6 +208,7 @@ def run_seal(args, w, torch, kvq, synthetic):
     cache = synthetic.build(w, ctx=ctx, max_ctx=ctx, seal_to_min=False, seal_if_full=False, chunk=512)
     ring = cache.info(0, 0)[2]
     assert ring == w.tail_max, ring
+    rec_bytes = cache.unit_bytes(kvq.REGION_BODY)
     specs = [synthetic.spec_for(w, s) for s in range(N)]
     seqs = list(range(N))
     dev = "cuda"
@@ -224,13 +239,17 @@ def run_seal(args, w, torch, kvq, synthetic):
     ms = sorted(times)[len(times) // 2]
     tokens = groups * 128 // L          # groups summed over layers; every layer seals the same tokens
     tiles = groups * w.n_kv_heads * 2 * max(1, w.head_dim // 256)
-    flops = tiles * seal_flops_per_tile(w.passes, 128, min(w.head_dim, 256))
+    sub = min(w.head_dim, 256)
+    flops = tiles * seal_flops_per_tile(w.passes, 128, sub)
     tflops = flops / (ms * 1e-3) / 1e12
+    # bytes: the tq6_0 tiles read, the records written
+    hbm = tiles * (128 * (sub // 128) * 98) + groups * w.n_kv_heads * rec_bytes
     log(f"[bench] seal: {groups} groups ({tokens} tokens x {L} layers), {ms * 1e3:.1f} us -> "
         f"{tokens / (ms * 1e-3) / 1e6:.2f} M tokens/s, {tflops:.2f} TFLOP/s (VALU)")
     del cache
     torch.cuda.empty_cache()
-    return {"ms": ms, "tokens": tokens, "tokens_per_s": tokens / (ms * 1e-3), "tiles": tiles, "tflops": tflops}
+    return {"ms": ms, "tokens": tokens, "tokens_per_s": tokens / (ms * 1e-3), "tiles": tiles, "tflops": tflops,
+            "hbm_bytes": hbm}
 
 
 def run_tbq4(args, w, torch, kvq, inputs, sealed_us):
@@ -308,21 +327,22 @@ def run_tbq4(args, w, torch, kvq, inputs, sealed_us):
             "note": "whole layer as TBQ4 blocks, fused rotated-domain decode incl. merge"}
 
 
-def run_cpu_baseline(w, budget_s):
-    """The oracle as it stands, single thread, on a bounded sample: one layer and
-    one KV head of the same shape at a shorter context (decode), and a few
-    sealed groups (seal)."""
-    import numpy as np
+def _oracle_unit(args):
+    """One oracle unit on one thread: a one-layer, one-KV-head cache of the
+    workload's shape built at `ctx` tokens (timed seal), then decode calls
+    for `budget_s` seconds.  Returns (decode bytes, decode seconds, calls,
+    sealed groups, seal seconds, info)."""
+    w, unit, ctx, budget_s = args
     from threadpoolctl import threadpool_limits
 
     from oracle import cache as ocache
+    from oracle import record as orecord
     from quantized_kv_cache_seal_amd import inputs, synthetic
 
-    ctx = 16_384
     with threadpool_limits(limits=1):
         oc = ocache.OracleCache(1, 1, w.head_dim, w.group, 1, ctx, w.tail_min, w.tail_max, w.margin,
                                 w.k_bits, w.v_bits, w.passes, synthetic.signs(w))
-        spec = inputs.KVSpec(1, 1, w.head_dim, w.seed, w.k_dist, w.outliers, w.outlier_scale)
+        spec = inputs.KVSpec(1, 1, w.head_dim, w.seed + 101 * unit, w.k_dist, w.outliers, w.outlier_scale)
         t_seal, groups = 0.0, 0
         for t0 in range(0, ctx, 512):
             k = spec.tokens(0, "k", t0, 512)[None]
@@ -335,28 +355,106 @@ def run_cpu_baseline(w, budget_s):
         groups += oc.seal(0, ocache.SEAL_TO_MIN)
         t_seal += time.perf_counter() - a
         n_tok, n_rec, ring = oc.info(0, 0)
-        q = inputs.queries(w.seed, 0, 0, 1, w.group, w.head_dim)[0]
+        q = inputs.queries(w.seed, unit, 0, 1, w.group, w.head_dim)[0]
         reps, t_dec = 0, 0.0
         while t_dec < budget_s or reps == 0:
             a = time.perf_counter()
             oc.attention(0, 0, q, 1.0)
             t_dec += time.perf_counter() - a
             reps += 1
-    from oracle import record as orecord
     nbytes = (128 * 2 * w.head_dim * 2 + ring * 2 * (w.head_dim // 128) * 98
               + n_rec * orecord.record_bytes(w.head_dim, w.k_bits, w.v_bits))
-    gbs = nbytes * reps / t_dec / 1e9
-    # a sealed token of the full shape is one group-row in every layer and KV head
-    seal_tok_s = groups * 128 / t_seal / (w.n_layers * w.n_kv_heads)
-    log(f"[bench] cpu oracle: decode {gbs:.4f} GB/s over {n_tok} tokens x 1 head ({reps} reps, {t_dec:.1f}s); "
-        f"seal {seal_tok_s:.1f} tokens/s ({groups} groups in {t_seal:.1f}s)")
+    return nbytes * reps, t_dec, reps, groups, t_seal, (n_tok, n_rec, ring)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def run_cpu_baseline(w, budget_s):
+    """The oracle as it stands (float64 numpy, never tuned for speed) on a
+    bounded sample of the same workload: one layer and one KV head of its
+    shape at 16,384 tokens (built through append and seal, the seal timed),
+    then decode calls for `budget_s` seconds; on one thread, and on every
+    available core at once (one process per core, each its own layer/head
+    unit: the work is independent per (layer, KV head)).  Rates are the
+    sample's compressed bytes per second and its sealed tokens per second
+    scaled to the full shape (a sealed token is one group row in every layer
+    and KV head)."""
+    import concurrent.futures
+    import multiprocessing as mp
+
+    ctx = 16_384
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16, int(os.environ.get("OMP_NUM_THREADS", "16") or 16)))
+    per_layer_head = w.n_layers * w.n_kv_heads
+    b, t, reps, groups, t_seal, (n_tok, n_rec, ring) = _oracle_unit((w, 0, ctx, budget_s))
+    one = {"gbs": b / t / 1e9, "seal_tok_s": groups * 128 / t_seal / per_layer_head}
+    log(f"[bench] cpu oracle, 1 thread: decode {one['gbs']:.4f} GB/s over {n_tok} tokens x 1 head "
+        f"({reps} calls, {t:.1f}s); seal {one['seal_tok_s']:.1f} tokens/s ({groups} groups in {t_seal:.1f}s)")
+    multi = None
+    if cores > 1:
+        wall0 = time.perf_counter()
+        with concurrent.futures.ProcessPoolExecutor(cores, mp_context=mp.get_context("spawn")) as ex:
+            outs = list(ex.map(_oracle_unit, [(w, u, ctx, budget_s) for u in range(cores)]))
+        wall = time.perf_counter() - wall0
+        gbs = sum(o[0] / o[1] for o in outs) / 1e9
+        seal = sum(o[3] * 128 / o[4] for o in outs) / per_layer_head
+        multi = {"gbs": gbs, "seal_tok_s": seal}
+        log(f"[bench] cpu oracle, {cores} processes: decode {gbs:.4f} GB/s, seal {seal:.1f} tokens/s "
+            f"(wall {wall:.1f}s)")
+    best = multi or one
     return {
-        "value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": f"float64 decode attention of one layer, one KV head ({w.group} query heads) at "
-                  f"{n_tok} tokens ({n_rec} records, ring {ring}), {reps} calls; seal: {groups} groups of one "
-                  f"head, scaled to {w.n_layers} layers x {w.n_kv_heads} heads",
-        "seal_tokens_per_s": seal_tok_s,
+        "value": best["gbs"], "unit": "GB/s", "cores": cores if multi else 1, "kind": "oracle",
+        "cpu_model": cpu_model(),
+        "sample": f"float64 decode attention of one layer and one KV head ({w.group} query heads) at "
+                  f"{n_tok} tokens ({n_rec} records, ring {ring}), repeated for {budget_s:.0f} s per thread, "
+                  f"on {cores} processes at once (independent layer/head units); seal of the same units' "
+                  f"groups, scaled to {w.n_layers} layers x {w.n_kv_heads} heads",
+        "seal_tokens_per_s": best["seal_tok_s"],
+        "one_core": {"value": one["gbs"], "seal_tokens_per_s": one["seal_tok_s"]},
+        "all_cores": None if multi is None else {"cores": cores, "value": multi["gbs"],
+                                                 "seal_tokens_per_s": multi["seal_tok_s"]},
     }
+
+
+def seal_entry(seal):
+    """Sealed tokens/s of one seal batch, against the non-packed fp32 vector
+    peak (packed fp32 instructions are disabled in this build) for the
+    balancing and rounding flops, and against HBM for its bytes."""
+    return {
+        "tokens_per_s": round(seal["tokens_per_s"], 1), "batch_tokens": seal["tokens"],
+        "us_per_batch": round(seal["ms"] * 1e3, 2), "tiles": seal["tiles"],
+        "roofline": {"bound": "alu", "achieved": round(seal["tflops"], 3), "peak": FP32_VALU_NONPACKED_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(seal["tflops"] / FP32_VALU_NONPACKED_TFLOPS, 4),
+                     "flops_basis": "per 128 x 256 tile: passes x 4 x 32,768 (two mat-vecs, y and y^2) "
+                                    "+ 6 x 32,768 (rounding)",
+                     "hbm_floor_us": round(seal["hbm_bytes"] / (HBM_PEAK_GBS * 1e9) * 1e6, 2)},
+    }
+
+
+def workload_entry(w, dec, seal, args):
+    """One extra workload's numbers, for the JSON line."""
+    e = {
+        "workload": w.name, "layers": w.n_layers, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+        "q_heads": w.n_q_heads, "ctx": w.ctx, "batch": w.n_seqs, "body_bits": f"{w.k_bits}/{w.v_bits}",
+        "steps": args.steps, "warmup": args.warmup,
+        "us_per_step": round(dec["ms_per_step"] * 1e3, 2), "gbs": round(dec["gbs"], 1),
+        "pct_hbm_peak": round(100 * dec["gbs"] / HBM_PEAK_GBS, 2), "bytes_per_step": int(dec["bytes_step"]),
+        "main_kernel_us": round(dec["avg_kernel_us"], 2),
+        "main_kernel_frac_hbm": round(dec["achieved"] / HBM_PEAK_GBS, 4),
+    }
+    if seal:
+        e["seal"] = seal_entry(seal)
+        if w.n_seqs > 1:  # one seal batch every 256 steps
+            e["amortized_us_per_step"] = round((dec["ms_per_step"] + seal["ms"] / 256) * 1e3, 2)
+    return e
 
 
 def main():
@@ -376,6 +474,9 @@ def main():
     ap.add_argument("--no-tbq4", action="store_true", help="skip the TBQ4 comparator leg")
     ap.add_argument("--save-restore", action="store_true",
                     help="also time saving and restoring sequence 0 to and from host memory (kvq_seq_save/_restore)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other measured workloads (512-wide heads, 128-wide K8/V4, the 16-sequence batch)")
+    ap.add_argument("--extra-steps", type=int, default=10, help="timed steps of each extra workload")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 20 times (calibrates HBM byte counters) and exit")
     args = ap.parse_args()
@@ -405,10 +506,20 @@ def main():
     seal = None if args.no_seal else run_seal(args, w, torch, kvq, synthetic)
     tbq = None if args.no_tbq4 else run_tbq4(args, w, torch, kvq, inputs, dec["avg_kernel_us"])
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(w, args.cpu_budget)
+    extra = {}
+    if args.workload == "qwen27b" and not args.no_extra:
+        sub = argparse.Namespace(**vars(args))
+        sub.steps, sub.warmup, sub.seal_reps, sub.save_restore = args.extra_steps, 2, 3, False
+        for key, wx in (("gemma31b", configs.GEMMA31B), ("qwen14b1m", configs.QWEN14B1M),
+                        ("batched", configs.BATCHED)):
+            dx = run_decode(sub, wx, torch, kvq, synthetic, inputs)
+            sx = None if args.no_seal else run_seal(sub, wx, torch, kvq, synthetic)
+            extra[key] = workload_entry(wx, dx, sx, sub)
     mfma_body = args.path != "valu"
     traffic = measured_traffic() if (args.workload == "qwen27b" and mfma_body) else None
     if traffic is not None:
         traffic = int(traffic)
+    durs = profile_record("duration-record") if (args.workload == "qwen27b" and mfma_body) else None
     res = {
         "metric": METRIC,
         "value": round(dec["gbs"], 2),
@@ -436,7 +547,14 @@ def main():
             "kernel": ("decode_main_kernel (fused sink, ring and body scan of one layer)" if mfma_body else
                        "decode_valu_kernel (body scan of one layer; sink and ring in decode_ring_kernel)"),
             "bytes_per_launch": int(dec["per_call_bytes"]), "avg_launch_us": round(dec["avg_kernel_us"], 2),
+            "time_basis": "device wall clock from the start of workgroup 0 to the end of the last workgroup "
+                          "(library stamps, every timed launch)",
             "traffic_over_algorithmic": None if traffic is None else round(traffic / dec["per_call_bytes"], 4),
+            # the same kernel's average duration under rocprofv3 --kernel-trace (committed profile of the
+            # current source): it also counts the dispatch ramp before workgroup 0 starts
+            "avg_launch_us_rocprof": None if durs is None else float(durs["avg_us"]),
+            "frac_rocprof": None if durs is None else
+            round(dec["per_call_bytes"] / (float(durs["avg_us"]) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         },
         "cpu_baseline": cpu,
     }
@@ -445,14 +563,11 @@ def main():
     if seal and w.n_seqs > 1:   # the batched workload meets one seal batch every 256 steps
         res["amortized_ms_per_step"] = round(dec["ms_per_step"] + seal["ms"] / 256, 4)
     if seal:
-        res["seal"] = {
-            "tokens_per_s": round(seal["tokens_per_s"], 1), "batch_tokens": seal["tokens"],
-            "us_per_batch": round(seal["ms"] * 1e3, 2),
-            "roofline": {"bound": "alu", "achieved": round(seal["tflops"], 3), "peak": FP32_VALU_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(seal["tflops"] / FP32_VALU_PEAK_TFLOPS, 4)},
-        }
+        res["seal"] = seal_entry(seal)
     if tbq:
         res["tbq4_comparator"] = tbq
+    if extra:
+        res["workloads"] = extra
     print(json.dumps(res), flush=True)
 
 

@@ -12,10 +12,15 @@ sub-tiles, one per rotation half, stored one after the other):
 
     [K codes][V codes][K C[sub] S[128] Z[128]][V C[sub] S[128] Z[128]]
 
-* K codes: 128 rows (tokens) x sub channels, row-major; 4-bit codes pack two
-  per byte, the even channel in the low nibble; 8-bit codes one per byte.
-* V codes: sub rows (channels) x 128 tokens, i.e. channel-major; 4-bit codes
-  pack two tokens per byte, the even token in the low nibble.
+* K codes: 128 rows (tokens) x sub channels, row-major; V codes: sub rows
+  (channels) x 128 tokens, i.e. channel-major.  Each row is an LSB-first
+  bitstream of b-bit codes: element k occupies stream bits b k .. b k + b - 1,
+  stream bit i is bit i % 8 of byte i // 8.  At 4 bits this is two codes per
+  byte with the even element in the low nibble, at 8 bits one per byte; at 3
+  bits eight codes fill three bytes, and codes 2 and 5 of every eight straddle
+  a byte boundary (SJ-KVaRN section 2.3: 4/4, 3/3 and 3/2 scalar bodies; KV
+  cache math, "a packing bug in the 3-bit codec": the elements that cross a
+  byte are where such a packer goes wrong).
 * C: per-channel balance scale; S, Z: per-token scale and zero point; all
   fp16, little-endian.
 This carries 2,048 bytes of scales per 256-channel record (the pages count
@@ -44,23 +49,32 @@ def record_bytes(head_dim: int, k_bits: int, v_bits: int) -> int:
     return n_sub(head_dim) * sub_bytes(sub_width(head_dim), k_bits, v_bits)
 
 
+BITS = (2, 3, 4, 8)
+
+
 def pack_rows(codes, bits: int) -> bytes:
-    """Row-major packing; 4-bit: element 2b in the low nibble of byte b."""
+    """Each row an LSB-first bitstream of `bits`-bit codes (a plain bit loop)."""
     c = np.asarray(codes, np.uint8)
-    if bits == 8:
-        return c.tobytes()
-    assert bits == 4 and c.shape[-1] % 2 == 0 and int(c.max(initial=0)) < 16
-    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8).tobytes()
+    assert bits in BITS and c.ndim == 2 and (c.shape[1] * bits) % 8 == 0
+    assert int(c.max(initial=0)) < (1 << bits)
+    rows, cols = c.shape
+    out = np.zeros((rows, cols * bits // 8), np.uint8)
+    for k in range(cols):
+        for i in range(bits):
+            bit = (c[:, k] >> i) & 1
+            pos = bits * k + i
+            out[:, pos // 8] |= (bit << (pos % 8)).astype(np.uint8)
+    return out.tobytes()
 
 
 def unpack_rows(buf, rows: int, cols: int, bits: int) -> np.ndarray:
-    b = np.frombuffer(bytes(buf), np.uint8)
-    if bits == 8:
-        return b.reshape(rows, cols).copy()
-    b = b.reshape(rows, cols // 2)
-    out = np.empty((rows, cols), np.uint8)
-    out[:, 0::2] = b & 0x0F
-    out[:, 1::2] = b >> 4
+    assert bits in BITS
+    b = np.frombuffer(bytes(buf), np.uint8).reshape(rows, cols * bits // 8)
+    out = np.zeros((rows, cols), np.uint8)
+    for k in range(cols):
+        for i in range(bits):
+            pos = bits * k + i
+            out[:, k] |= ((b[:, pos // 8] >> (pos % 8)) & 1) << i
     return out
 
 

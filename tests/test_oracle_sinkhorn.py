@@ -33,7 +33,7 @@ def test_checkerboard_closed_form(passes, cols):
     bal = sinkhorn.balance(x, passes)
     gm = np.exp(np.mean(np.log(b)))
     assert np.array_equal(bal["C"], (b / gm).astype(np.float16))
-    for bits in (4, 8):
+    for bits in (2, 3, 4, 8):
         codes, S, Z = rounding.round_rows(x.astype(np.float32), bal["C"], bits)
         assert np.array_equal(codes, np.where(x > 0, 2 ** bits - 1, 0).astype(np.uint8))
 
@@ -92,7 +92,7 @@ def test_column_scaling_equivariance():
 def test_round_rows_brute_force_nearest_level():
     x = _tile(12)
     C = sinkhorn.balance(x.astype(np.float64), 16)["C"]
-    for bits in (4, 8):
+    for bits in (2, 3, 4, 8):
         codes, S, Z = rounding.round_rows(x, C, bits)
         t = rounding.pre_round_values(x, C, S, Z).astype(np.float64)
         lv = np.arange(2 ** bits)
@@ -260,22 +260,50 @@ def test_spread_is_taken_about_the_first_element():
     assert np.allclose(rms, 1e8 + np.array([1.5, 5.0]), rtol=1e-15)
 
 
-def test_nibble_order_every_position_and_value():
-    rng = np.random.default_rng(1)
-    for bits, rows, cols in ((4, 128, 256), (4, 256, 128), (8, 128, 128)):
-        for pos in range(cols):
-            for val in range(0, 2 ** bits, 1 if bits == 4 else 17):
-                c = rng.integers(0, 2 ** bits, (rows, cols)).astype(np.uint8)
-                c[pos % rows, pos] = val
-                buf = record.pack_rows(c, bits)
-                assert len(buf) == rows * cols * bits // 8
-                raw = np.frombuffer(buf, np.uint8).reshape(rows, -1)
-                if bits == 4:
-                    byte = raw[pos % rows, pos // 2]
-                    assert ((byte >> (4 * (pos % 2))) & 15) == val
-                else:
-                    assert raw[pos % rows, pos] == val
-                assert np.array_equal(record.unpack_rows(buf, rows, cols, bits), c)
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("cols", [128, 256])
+def test_row_packing_every_position_and_value(bits, cols):
+    """Every element position of a row holds every code value in some row;
+    the packed bytes, read as numpy's little-endian bit order, give back
+    element k in stream bits bits k .. bits k + bits - 1."""
+    n = 1 << bits
+    c = ((np.arange(n)[:, None] + np.arange(cols)[None, :]) % n).astype(np.uint8)
+    buf = record.pack_rows(c, bits)
+    assert len(buf) == n * cols * bits // 8
+    stream = np.unpackbits(np.frombuffer(buf, np.uint8).reshape(n, -1), axis=1, bitorder="little")
+    ref = (stream.reshape(n, cols, bits) * (1 << np.arange(bits))).sum(axis=2)
+    assert np.array_equal(ref, c)
+    assert np.array_equal(record.unpack_rows(buf, n, cols, bits), c)
+
+
+def test_three_bit_group_bytes():
+    """Eight 3-bit codes in three bytes, written out: codes 2 and 5 straddle
+    a byte boundary (the codes a wrong shift corrupts)."""
+    for v in range(8 ** 2):
+        cc = [(v + 3 * k) % 8 for k in range(8)]
+        cc[2], cc[5] = v % 8, (v // 8) % 8
+        b = record.pack_rows(np.array([cc], np.uint8), 3)
+        want = bytes([cc[0] | cc[1] << 3 | (cc[2] & 3) << 6,
+                      cc[2] >> 2 | cc[3] << 1 | cc[4] << 4 | (cc[5] & 1) << 7,
+                      cc[5] >> 1 | cc[6] << 2 | cc[7] << 5])
+        assert b == want, (cc, b, want)
+
+
+@pytest.mark.parametrize("kb,vb", [(3, 3), (3, 2), (2, 2), (8, 3)])
+def test_low_bit_record_round_trip(kb, vb):
+    """A record at 3 and 2 bits: the sizes, and every field back unchanged."""
+    assert record.record_bytes(256, kb, vb) == 128 * 256 * (kb + vb) // 8 + 2048
+    x = _tile(15)
+    sides = []
+    for bits in (kb, vb):
+        C = sinkhorn.balance(x.astype(np.float64), 8)["C"]
+        codes, S, Z = rounding.round_rows(x, C, bits)
+        assert int(codes.max()) == 2 ** bits - 1
+        sides.append({"codes": codes, "C": C, "S": S, "Z": Z})
+    k, v = record.parse_sub(record.build_sub(sides[0], sides[1], kb, vb), 256, kb, vb)
+    for a, b in ((k, sides[0]), (v, sides[1])):
+        for n in ("codes", "C", "S", "Z"):
+            assert np.array_equal(a[n], b[n])
 
 
 def test_record_sizes_and_round_trip():

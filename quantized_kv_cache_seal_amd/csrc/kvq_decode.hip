@@ -156,24 +156,25 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
         const uint8_t* rec = a.arena + rec_off(y, s, layer, h, r) + (int64_t)sub * y.sub_bytes;
         const uint8_t* km = rec + y.kcode_bytes + y.vcode_bytes;
         const uint8_t* vm = km + 2 * (y.sub + 2 * kGroup);
-        int kc;
-        if (y.kbits == 4) {
-          const uint8_t byte = rec[(int64_t)ti * (y.sub / 2) + jj / 2];
-          kc = (jj & 1) ? (byte >> 4) : (byte & 15);
-        } else {
-          kc = rec[(int64_t)ti * y.sub + jj];
-        }
-        const uint8_t vbyte = rec[y.kcode_bytes + (int64_t)jj * (kGroup / 2) + ti / 2];
-        const int vc = (ti & 1) ? (vbyte >> 4) : (vbyte & 15);
+        // code k of a row: stream bits b k .. b k + b - 1, LSB first
+        auto code = [](const uint8_t* row, int k, int bits) {
+          const int bit = bits * k;
+          uint32_t w = row[bit >> 3];
+          if ((bit & 7) + bits > 8) w |= (uint32_t)row[(bit >> 3) + 1] << 8;
+          return (int)((w >> (bit & 7)) & ((1u << bits) - 1));
+        };
+        const int kc = code(rec + (int64_t)ti * (y.sub * y.kbits / 8), jj, y.kbits);
+        const int vc = code(rec + y.kcode_bytes + (int64_t)jj * (kGroup * y.vbits / 8), ti, y.vbits);
+        const float vmid = (float)(1 << (y.vbits - 1));
         const uint16_t* kmh = (const uint16_t*)km;
         const uint16_t* vmh = (const uint16_t*)vm;
         // keys exact in binary64: C (S n + Z) of fp16 C, S, Z; values centred,
-        // C (S (n - 8) + (Z + 8 S)) in fp32 (Z + 8 S exact), so that rows whose
-        // range is far above their values do not cancel
+        // C (S (n - mid) + (Z + mid S)) in fp32 (mid = 2^(b-1); Z + mid S exact),
+        // so that rows whose range is far above their values do not cancel
         kx = (double)h2f(kmh[jj]) *
              ((double)h2f(kmh[y.sub + ti]) * (double)kc + (double)h2f(kmh[y.sub + kGroup + ti]));
         const float vs = h2f(vmh[y.sub + ti]);
-        vx = h2f(vmh[jj]) * fmaf(vs, (float)vc - 8.0f, fmaf(8.0f, vs, h2f(vmh[y.sub + kGroup + ti])));
+        vx = h2f(vmh[jj]) * fmaf(vs, (float)vc - vmid, fmaf(vmid, vs, h2f(vmh[y.sub + kGroup + ti])));
       }
       kt[t][j] = kx;
       vt[t][j] = vx;

@@ -735,6 +735,316 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
 }
 
 // ---------------------------------------------------------------------------
+// Low-bit body role: 2- or 3-bit keys and values (SJ-KVaRN 2.3: the 3/3 and
+// 3/2 scalar bodies; 2/2), 256-wide heads, one chunk of records of one KV
+// head.  The same record math and work split as body_role, in natural slot
+// order: at k-step kk, lane group g of the score product feeds channels
+// 64 g + 8 kk .. + 7 (its 64 channels of a key row are 8 B bytes of the row),
+// and of the value product tokens 32 g + 8 t .. + 7 of a channel row (4 B
+// bytes); codes are unpacked into exact centred fp16 (c - 2^(B-1)).  The hi
+// and lo query and weight operands take separate products.
+template <int KB_, int VB_>
+struct LbShape {
+  static constexpr int KB = KB_, VB = VB_, SUBW = 256, KK = 8, VT = 4;
+  static constexpr int KROW = SUBW * KB / 8, VROW = 128 * VB / 8;  // bytes per key / value code row
+  static constexpr int KCODE = 128 * KROW, VCODE = SUBW * VROW;
+  static constexpr int META = 4 * (SUBW + 256);
+  static constexpr int SUB_BYTES = KCODE + VCODE + META;
+  static constexpr int KW = 2 * KB, VW = VB;  // dwords per lane of a key row / value row share
+  // scales in LDS as stage_scales lays them out
+  static constexpr int L_KS = 2 * SUBW, L_KZ = L_KS + 512, L_VC = L_KZ + 512, L_VS = L_VC + 4 * SUBW;
+  static constexpr int L_VZ = L_VS + 512, MSTRIDE = 4096;
+  // LDS: q~ operands [KK][hi, lo][64 lanes]; weights [hi, lo][16][kPPitch]; scales [3][MSTRIDE];
+  // exchange xm[4][16], xz[4][16], xs[4][16]
+  static constexpr int QT = 0, PW = QT + KK * 2 * 64 * 16, MB = PW + 2 * 16 * kPPitch * 2;
+  static constexpr int X = MB + 3 * MSTRIDE;
+  static constexpr int total = X + 3 * 256;
+  static_assert(16 * SUBW * 4 <= PW - QT, "query rows fit the q~ area");
+};
+
+// Eight consecutive B-bit codes (B = 2 or 3) at bits 0 .. 8 B - 1 of x as exact
+// centred fp16 values c - 2^(B-1), in order.  The low half of u keeps x, the
+// high half x >> B, so that one AND-OR per pair takes codes 2i and 2i + 1
+// (after a shift of u by 2 B i) into the mantissas of 1024 + c; at 3 bits the
+// last pair comes from x >> 18 the same way.
+template <int B>
+__device__ __forceinline__ half8 codes_lb(uint32_t x) {
+  const uint32_t mm = ((1u << B) - 1) * 0x10001u, e = 0x64006400u;
+  const uint32_t u0 = (x & 0xFFFFu) | ((x << (16 - B)) & 0xFFFF0000u);
+  uint4 u;
+  u.x = and_or(u0, mm, e);
+  u.y = and_or(u0 >> (2 * B), mm, e);
+  u.z = and_or(u0 >> (4 * B), mm, e);
+  if (B == 2) {
+    u.w = and_or(u0 >> (6 * B), mm, e);
+  } else {
+    const uint32_t x3 = x >> 18;
+    u.w = and_or((x3 & 0xFFFFu) | ((x3 << 13) & 0xFFFF0000u), mm, e);
+  }
+  const _Float16 c = (_Float16)(1024.0f + (float)(1 << (B - 1)));
+  const half8 off = {c, c, c, c, c, c, c, c};
+  return mfma_a(u) - off;
+}
+
+// Bits 8 B s .. 8 B s + 8 B - 1 of a lane's dwords d (the codes of its k-step s)
+// in the low bits of the result (higher bits are ignored by codes_lb).
+template <int B>
+__device__ __forceinline__ uint32_t step_bits(const uint32_t* d, int s) {
+  const int bit = 8 * B * s, w = bit >> 5, o = bit & 31;
+  return o == 0 ? d[w] : o + 8 * B <= 32 ? d[w] >> o : __builtin_amdgcn_alignbit(d[w + 1], d[w], o);
+}
+
+template <class Sh>
+__device__ __forceinline__ void load_keys_lb(const uint8_t* __restrict__ rec, uint32_t (&kd)[2][Sh::KW], int wave,
+                                             int lane, bool dummy) {
+  const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint8_t* p = rec + (dummy ? 0 : (16 * (2 * wave + i) + m) * Sh::KROW + 8 * Sh::KB * g);
+#pragma unroll
+    for (int j = 0; j < Sh::KW / 2; ++j) {
+      const uint2 v = *(const uint2*)(p + 8 * j);
+      kd[i][2 * j] = v.x;
+      kd[i][2 * j + 1] = v.y;
+    }
+  }
+}
+template <class Sh>
+__device__ __forceinline__ void load_values_lb(const uint8_t* __restrict__ rec, uint32_t (&vd)[Sh::VT][Sh::VW],
+                                               int wave, int lane, bool dummy) {
+  const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < Sh::VT; ++j) {
+    const uint32_t* p =
+        (const uint32_t*)(rec + (dummy ? 0 : Sh::KCODE + (16 * (Sh::VT * wave + j) + m) * Sh::VROW + 4 * Sh::VB * g));
+#pragma unroll
+    for (int k = 0; k < Sh::VW; ++k) vd[j][k] = p[k];
+  }
+}
+
+template <class Sh>
+__device__ __forceinline__ void body_role_lb(const DecodeArgs& a, int b, int h, int cbk, uint8_t* smem) {
+  constexpr int D = 256, SUBW = Sh::SUBW, KK = Sh::KK, VT = Sh::VT, MS = Sh::MSTRIDE;
+  constexpr float kMidK = (float)(1 << (Sh::KB - 1)), kMidV = (float)(1 << (Sh::VB - 1));
+  const Layout& y = a.y;
+  const DecodeSeq& sq = a.seq[b];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int q16 = lane & 15, g = lane >> 4;
+  uint4(*qt)[2][64] = (uint4(*)[2][64])(smem + Sh::QT);
+  uint16_t(*pw)[16][kPPitch] = (uint16_t(*)[16][kPPitch])(smem + Sh::PW);
+  uint8_t* mbuf = smem + Sh::MB;
+  float(*xm)[16] = (float(*)[16])(smem + Sh::X);
+  float(*xz)[16] = (float(*)[16])(smem + Sh::X + 256);
+  float(*xs)[16] = (float(*)[16])(smem + Sh::X + 512);
+
+  // records of this chunk: the weighted split of body_role (two workgroups per CU)
+  const int nb = sq.n_body_chunks;
+  int r0, r1;
+  if (sq.n_rec >= 4 * nb) {
+    const int g_base = (int)blockIdx.x - cbk * y.H - h;
+    const int n_first = max(0, (a.n_old - g_base - h + y.H - 1) / y.H);
+    auto wpref = [&](int c) -> int64_t {
+      return (int64_t)kWYoung * c + (int64_t)(kWOld - kWYoung) * min(n_first, c);
+    };
+    const int64_t W = wpref(nb);
+    r0 = (int)(wpref(cbk) * sq.n_rec / W);
+    r1 = (int)(wpref(cbk + 1) * sq.n_rec / W);
+  } else {
+    r0 = (int)((int64_t)cbk * sq.n_rec / nb);
+    r1 = (int)((int64_t)(cbk + 1) * sq.n_rec / nb);
+  }
+  const uint8_t* rec0 = a.arena + rec_off(y, sq.slot, a.layer, h, 0);
+  auto rec = [&](int r) { return rec0 + (int64_t)r * y.rec_bytes; };
+  auto mslot = [&](int r) { return mbuf + ((r - r0) % 3) * MS; };
+  const int mo = Sh::KCODE + Sh::VCODE + 8 * tid;  // META is 8 x 256 bytes
+
+  // ---- prologue: query, scales of r0 and r0 + 1, codes of r0
+  QueryRaw<D> qraw;
+  query_load<D>(a, b, h, wave, lane, qraw);
+  const uint2 m0 = *(const uint2*)(rec(r0) + mo);
+  const uint2 m1 = *(const uint2*)(r0 + 1 < r1 ? rec(r0 + 1) + mo : rec0);
+  uint32_t kd[2][Sh::KW], vd[VT][Sh::VW];
+  load_keys_lb<Sh>(rec(r0), kd, wave, lane, false);
+  float* rows = (float*)qt;
+  query_rows<D>(a, qraw, true, rows, wave, lane);
+  __syncthreads();
+  // q' of this lane's q~ slots: query row q16, channels 64 g + 8 kk .. + 7 for
+  // kk = 2 wave, 2 wave + 1, split hi + scaled lo
+  uint4 qph[2], qpl[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float* r = rows + q16 * D + 64 * g + 8 * (2 * wave + k);
+    uint32_t hh[4], ll[4];
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) split_h2s(r[2 * pr], r[2 * pr + 1], hh[pr], ll[pr]);
+    qph[k] = make_uint4(hh[0], hh[1], hh[2], hh[3]);
+    qpl[k] = make_uint4(ll[0], ll[1], ll[2], ll[3]);
+  }
+  __syncthreads();  // the query rows are read
+  stage_scales<Sh>(mslot(r0), m0, tid);
+  if (r0 + 1 < r1) stage_scales<Sh>(mslot(r0 + 1), m1, tid);
+  __syncthreads();
+  // q~ of the k-steps 2 wave, 2 wave + 1 for record r (key C fp16 at the start
+  // of its scale area) and this wave's part of sigma = sum q~ per query row
+  auto make_qt = [&](const uint8_t* km) {
+    const half2v lo_ones = {(_Float16)kLoUnscale, (_Float16)kLoUnscale};
+    const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
+    float part = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int kk = 2 * wave + k;
+      const uint4 c = *(const uint4*)(km + 2 * (64 * g + 8 * kk));
+      uint4 hi, lo;
+      qtilde_pair(qph[k].x, qpl[k].x, c.x, hi.x, lo.x);
+      qtilde_pair(qph[k].y, qpl[k].y, c.y, hi.y, lo.y);
+      qtilde_pair(qph[k].z, qpl[k].z, c.z, hi.z, lo.z);
+      qtilde_pair(qph[k].w, qpl[k].w, c.w, hi.w, lo.w);
+      qt[kk][0][lane] = hi;
+      qt[kk][1][lane] = lo;
+      part = __builtin_amdgcn_fdot2(as_h2(hi.x), ones, part, false);
+      part = __builtin_amdgcn_fdot2(as_h2(hi.y), ones, part, false);
+      part = __builtin_amdgcn_fdot2(as_h2(hi.z), ones, part, false);
+      part = __builtin_amdgcn_fdot2(as_h2(hi.w), ones, part, false);
+      part = __builtin_amdgcn_fdot2(as_h2(lo.x), lo_ones, part, false);
+      part = __builtin_amdgcn_fdot2(as_h2(lo.y), lo_ones, part, false);
+      part = __builtin_amdgcn_fdot2(as_h2(lo.z), lo_ones, part, false);
+      part = __builtin_amdgcn_fdot2(as_h2(lo.w), lo_ones, part, false);
+    }
+    part = xsum4(part);  // over the lane groups: the wave's 64 channels of row q16
+    if (g == 0) xs[wave][q16] = part;
+  };
+  make_qt(mslot(r0));
+  load_values_lb<Sh>(rec(r0), vd, wave, lane, false);
+  uint2 mnext = *(const uint2*)(r0 + 2 < r1 ? rec(r0 + 2) + mo : rec0);
+  __syncthreads();
+
+  float m_run = -INFINITY, l_part = 0.0f;
+  float4v acc[VT];
+#pragma unroll
+  for (int i = 0; i < VT; ++i) acc[i] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int r = r0; r < r1; ++r) {
+    const uint8_t* mr = mslot(r);
+    const bool more = r + 1 < r1;
+    // ---- scores of tiles 2 wave, 2 wave + 1: rows are tokens 16 (2 wave + i) + 4 g + j
+    float4v sh[2], sl[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) sh[i] = sl[i] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const half8 bh = mfma_a(qt[kk][0][lane]), bl = mfma_a(qt[kk][1][lane]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const half8 av = codes_lb<Sh::KB>(step_bits<Sh::KB>(kd[i], kk));
+        sh[i] = mfma16(av, bh, sh[i]);
+        sl[i] = mfma16(av, bl, sl[i]);
+      }
+    }
+    const float sig = xs[0][q16] + xs[1][q16] + xs[2][q16] + xs[3][q16];
+    float sc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int T = 16 * (2 * wave + i) + 4 * g;
+      const float4 S = *(const float4*)(mr + Sh::L_KS + 4 * T), Z = *(const float4*)(mr + Sh::L_KZ + 4 * T);
+      const float Sj[4] = {S.x, S.y, S.z, S.w}, Zj[4] = {Z.x, Z.y, Z.z, Z.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float dot = sh[i][j] + sl[i][j] * kLoUnscale;
+        sc[i][j] = fmaf(Sj[j], dot, fmaf(kMidK, Sj[j], Zj[j]) * sig);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sc[i][j]);
+    mx = xmax4(mx);
+    if (g == 0) xm[wave][q16] = mx;
+    __syncthreads();  // (B2) record maxima; q~ of r and the key codes are free
+    load_keys_lb<Sh>(more ? rec(r + 1) : rec0, kd, wave, lane, !more);
+
+    const float mrec = fmaxf(fmaxf(xm[0][q16], xm[1][q16]), fmaxf(xm[2][q16], xm[3][q16]));
+    const float m_new = fmaxf(m_run, mrec);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first record
+    const float frec = __builtin_amdgcn_exp2f(mrec - m_new);    // the record's weights are relative to mrec
+    m_run = m_new;
+    if (alpha != 1.0f) {
+#pragma unroll
+      for (int i = 0; i < VT; ++i) acc[i] *= alpha;
+    }
+    l_part *= alpha;
+    float lrec = 0.0f, zt = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int T = 16 * (2 * wave + i) + 4 * g;
+      const float4 S = *(const float4*)(mr + Sh::L_VS + 4 * T), Z = *(const float4*)(mr + Sh::L_VZ + 4 * T);
+      const float Sj[4] = {S.x, S.y, S.z, S.w}, Zj[4] = {Z.x, Z.y, Z.z, Z.w};
+      float x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p = __builtin_amdgcn_exp2f(sc[i][j] - mrec);
+        lrec += p;
+        zt = fmaf(p, fmaf(kMidV, Sj[j], Zj[j]), zt);
+        x[j] = p * Sj[j];
+      }
+      uint2 hi, lo;
+      split_h2s(x[0], x[1], hi.x, lo.x);
+      split_h2s(x[2], x[3], hi.y, lo.y);
+      *(uint2*)&pw[0][q16][T] = hi;
+      *(uint2*)&pw[1][q16][T] = lo;
+    }
+    l_part = fmaf(frec, lrec, l_part);
+    zt = xsum4(zt);
+    if (g == 0) xz[wave][q16] = zt;
+    if (more) make_qt(mslot(r + 1));
+    if (r + 2 < r1) stage_scales<Sh>(mslot(r + 2), mnext, tid);
+    mnext = *(const uint2*)(r + 3 < r1 ? rec(r + 3) + mo : rec0);
+    __syncthreads();  // (B3) weights, zero-point sums; q~ and scales of r + 1, r + 2
+
+    // ---- values: channel tiles VT wave + j over the record's 128 tokens
+    const float corr = xz[0][q16] + xz[1][q16] + xz[2][q16] + xz[3][q16];
+    half8 pbh[4], pbl[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      pbh[t] = mfma_a(*(const uint4*)&pw[0][q16][32 * g + 8 * t]);
+      pbl[t] = mfma_a(*(const uint4*)&pw[1][q16][32 * g + 8 * t]);
+    }
+    float4v oh[VT], ol[VT];
+#pragma unroll
+    for (int j = 0; j < VT; ++j) oh[j] = ol[j] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int j = 0; j < VT; ++j) {
+        const half8 av = codes_lb<Sh::VB>(step_bits<Sh::VB>(vd[j], t));
+        oh[j] = mfma16(av, pbh[t], oh[j]);
+        ol[j] = mfma16(av, pbl[t], ol[j]);
+      }
+    }
+    load_values_lb<Sh>(more ? rec(r + 1) : rec0, vd, wave, lane, !more);
+#pragma unroll
+    for (int j = 0; j < VT; ++j) {
+      const int cb = VT * wave + j;
+      const float4 c = *(const float4*)(mr + Sh::L_VC + 4 * (16 * cb + 4 * g));
+      const float cc[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc[j][e] = fmaf(cc[e] * frec, oh[j][e] + ol[j][e] * kLoUnscale + corr, acc[j][e]);
+    }
+  }
+
+  // ---- partial of this chunk, rotated back row by row through the q~ area
+  const float lsum = xsum4(l_part);
+  if (g == 0) xm[wave][q16] = lsum;
+  if (q16 < a.g) {
+#pragma unroll
+    for (int j = 0; j < VT; ++j) *(float4v*)(rows + q16 * D + 16 * (VT * wave + j) + 4 * g) = acc[j];
+  }
+  __syncthreads();
+  write_partial_rows<D>(a, b, h, 1 + sq.n_ring_chunks + cbk, rows, m_run, xm, true, wave, lane);
+}
+
+// ---------------------------------------------------------------------------
 // Sink / ring role: chunk c of one KV head, c = 0 the sink (n_sink fp16 tokens,
 // original domain), c >= 1 ring tokens [(c - 1) ring_chunk, c ring_chunk).
 // With f16 staging the ring chunks are read as the sink is: fp16 rows in the
@@ -1244,6 +1554,38 @@ __device__ __forceinline__ void decode_main(const DecodeArgs& a, uint8_t* smem) 
   prof_end(a.prof_ts);
 }
 
+// Low-bit bodies (2- or 3-bit keys and values), 256-wide heads: the same
+// items, the body scanned by body_role_lb.
+template <int KB, int VB>
+struct MainLdsLb {
+  static constexpr int body = LbShape<KB, VB>::total, ring = RingLds<256>::total, append = (16 + 2) * 256 * 4;
+  static constexpr int m0 = body > ring ? body : ring;
+  static constexpr int value = m0 > append ? m0 : append;
+};
+
+template <int KB, int VB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_main_kernel_lb(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[MainLdsLb<KB, VB>::value];
+  int b, h, c;
+  int item = blockIdx.x;
+  prof_start(a.prof_ts);
+  if (item < a.n_app_items) {
+    append_role<256>(a, item / a.y.H, item % a.y.H, smem);
+    prof_end(a.prof_ts);
+    return;
+  }
+  item -= a.n_app_items;
+  if (item < a.n_body_items) {
+    if (find_item(a, item, true, b, h, c)) body_role_lb<LbShape<KB, VB>>(a, b, h, c, smem);
+  } else if (find_item(a, item - a.n_body_items, false, b, h, c)) {
+    if (a.g <= 8)
+      ring_role<256, true>(a, b, h, c, smem);
+    else
+      ring_role<256, false>(a, b, h, c, smem);
+  }
+  prof_end(a.prof_ts);
+}
+
 // Two resident workgroups per compute unit (256 registers per lane each),
 // or one for 512-wide heads (whose sink/ring scan needs 125 KB of LDS).
 #define KVQ_MAIN_KERNEL(NAME, D, KB, W)                                                      \
@@ -1278,8 +1620,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // Append (optional), body and sink/ring items in one launch: head_dim 128,
 // 256 or 512 (two 256-channel sub-records), 4- or 8-bit keys, 4-bit values.
 hipError_t launch_decode_main(const DecodeArgs& a, int n_items, hipStream_t stream) {
-  if (a.y.vbits != 4 || a.ring_chunk % kStep != 0 || a.g > kMaxGroup) return hipErrorInvalidValue;
+  if (a.ring_chunk % kStep != 0 || a.g > kMaxGroup) return hipErrorInvalidValue;
   const dim3 grid(n_items), block(256);
+  if (a.y.vbits != 4) {  // low-bit bodies: 256-wide heads, 2- or 3-bit keys and values
+    if (a.y.D != 256) return hipErrorInvalidValue;
+    const int kb = a.y.kbits, vb = a.y.vbits;
+    if (kb == 3 && vb == 3)
+      hipLaunchKernelGGL((decode_main_kernel_lb<3, 3>), grid, block, 0, stream, a);
+    else if (kb == 3 && vb == 2)
+      hipLaunchKernelGGL((decode_main_kernel_lb<3, 2>), grid, block, 0, stream, a);
+    else if (kb == 2 && vb == 2)
+      hipLaunchKernelGGL((decode_main_kernel_lb<2, 2>), grid, block, 0, stream, a);
+    else if (kb == 2 && vb == 3)
+      hipLaunchKernelGGL((decode_main_kernel_lb<2, 3>), grid, block, 0, stream, a);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   if (a.y.D == 256 && a.y.kbits == 4)
     hipLaunchKernelGGL(decode_main_kernel, grid, block, 0, stream, a);
   else if (a.y.D == 512 && a.y.kbits == 4)

@@ -84,8 +84,9 @@ static kvq_status check_config(const kvq_config* c) {
   if (c->margin < 0) return fail(KVQ_ERR_INVALID, "margin must be >= 0");
   if (c->max_ctx < 1 || c->max_ctx > ((int64_t)1 << 31) - kGroup)
     return fail(KVQ_ERR_INVALID, "max_ctx out of range");
-  if ((c->k_bits != 4 && c->k_bits != 8) || c->v_bits != 4)
-    return fail(KVQ_ERR_INVALID, "supported bodies: k_bits 4 or 8, v_bits 4");
+  if ((c->k_bits != 2 && c->k_bits != 3 && c->k_bits != 4 && c->k_bits != 8) ||
+      (c->v_bits != 2 && c->v_bits != 3 && c->v_bits != 4) || (c->v_bits == 4) != (c->k_bits >= 4))
+    return fail(KVQ_ERR_INVALID, "supported bodies: k_bits 4 or 8 with v_bits 4; k_bits 2 or 3 with v_bits 2 or 3");
   if (c->sinkhorn_passes < 0 || c->sinkhorn_passes > 64)
     return fail(KVQ_ERR_INVALID, "sinkhorn_passes must be in [0, 64]");
   if ((int64_t)c->tail_max + c->margin > (1 << 28)) return fail(KVQ_ERR_INVALID, "ring too large");
@@ -143,7 +144,9 @@ static int device_cu_count() {
 // matrix-core body scan (fused with the sink and ring): every shape the cache
 // accepts (head_dim 128, 256 or 512; 4- or 8-bit K; 4-bit V)
 static bool mfma_supported(const Layout& y) {
-  return y.vbits == 4 && (y.kbits == 4 || y.kbits == 8) && (y.D == 128 || y.D == 256 || y.D == 512);
+  if (y.vbits != 4)  // low-bit bodies: 256-wide heads (other widths take the vector-ALU scan)
+    return y.D == 256 && (y.kbits == 2 || y.kbits == 3) && (y.vbits == 2 || y.vbits == 3);
+  return (y.kbits == 4 || y.kbits == 8) && (y.D == 128 || y.D == 256 || y.D == 512);
 }
 // matrix-core sink and ring scan on its own: head_dim 128 or 256
 static bool staged_supported(const Layout& y) { return y.D == 128 || y.D == 256; }
@@ -425,7 +428,8 @@ static kvq_status decode_impl(kvq_cache* c, int32_t layer, const int32_t* seq_id
   const bool use_mfma = c->path != KVQ_PATH_VALU && mfma_supported(c->y);
   const bool staged = c->path != KVQ_PATH_VALU && staged_supported(c->y);
   if (c->path == KVQ_PATH_MFMA && !use_mfma)
-    return fail(KVQ_ERR_UNSUPPORTED, "matrix-core body scan needs 4-bit V and 4- or 8-bit K");
+    return fail(KVQ_ERR_UNSUPPORTED, "matrix-core body scan: 4/4 or 8/4 at head_dim 128, 256, 512; 2- or 3-bit "
+                                     "bodies at head_dim 256");
   std::vector<int64_t> n_rec(n_seqs), ring(n_seqs);
   for (int i = 0; i < n_seqs; ++i) {
     if (c->tok(seq_ids[i], layer) < 1) return fail(KVQ_ERR_INVALID, "sequence %d holds no tokens", seq_ids[i]);

@@ -146,6 +146,26 @@ __device__ __forceinline__ float cvt_e(const half8& v, int e) {
   return d;
 }
 
+// Eight consecutive b-bit codes (code e at bits b e of an LSB-first stream)
+// as the b bytes at p: 8-, 4- and 2-bit groups are aligned words, a 3-bit
+// group three bytes (p is then only byte-aligned).
+__device__ __forceinline__ void put_codes8(uint8_t* p, const uint32_t (&cq)[8], int bits) {
+  uint64_t v = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v |= (uint64_t)cq[e] << (bits * e);
+  if (bits == 8) {
+    *(uint2*)p = make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+  } else if (bits == 4) {
+    *(uint32_t*)p = (uint32_t)v;
+  } else if (bits == 2) {
+    *(uint16_t*)p = (uint16_t)v;
+  } else {
+    p[0] = (uint8_t)v;
+    p[1] = (uint8_t)(v >> 8);
+    p[2] = (uint8_t)(v >> 16);
+  }
+}
+
 template <int SUBW>
 struct SealLds {
   uint8_t smem[SealShape<SUBW>::BYTES] __attribute__((aligned(16)));
@@ -540,20 +560,7 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
           const float yv = (d * cvt_e(ar[t][kk], e)) * ic[e];
           cq[e] = (uint32_t)__builtin_amdgcn_fmed3f(rintf((yv - Zf) * inv), 0.0f, levels);
         }
-        if (bits == 4) {
-          uint32_t pk = 0;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pk |= cq[e] << (4 * e);
-          *(uint32_t*)(rec + (int64_t)row * (SUBW / 2) + (32 * kk + 8 * g) / 2) = pk;
-        } else {
-          uint2 pk = make_uint2(0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pk.x |= cq[e] << (8 * e);
-            pk.y |= cq[e + 4] << (8 * e);
-          }
-          *(uint2*)(rec + (int64_t)row * SUBW + 32 * kk + 8 * g) = pk;
-        }
+        put_codes8(rec + (int64_t)row * (SUBW * bits / 8) + (32 * kk + 8 * g) * bits / 8, cq, bits);
       }
     }
   }
@@ -566,15 +573,14 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
       const float ic = invc[col];
 #pragma unroll
       for (int kr = 0; kr < 4; ++kr) {
-        uint32_t pk = 0;
+        uint32_t cq[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int row = 32 * kr + 8 * g + e;
           const float yv = (ds[wb][row] * (float)ac[ct][kr][e]) * ic;
-          const uint32_t c = (uint32_t)__builtin_amdgcn_fmed3f(rintf((yv - zrow[row]) * rinv[row]), 0.0f, levels);
-          pk |= c << (4 * e);
+          cq[e] = (uint32_t)__builtin_amdgcn_fmed3f(rintf((yv - zrow[row]) * rinv[row]), 0.0f, levels);
         }
-        *(uint32_t*)(vbase + (int64_t)col * (kGroup / 2) + (32 * kr + 8 * g) / 2) = pk;
+        put_codes8(vbase + (int64_t)col * (kGroup * bits / 8) + (32 * kr + 8 * g) * bits / 8, cq, bits);
       }
     }
   }
@@ -776,38 +782,24 @@ __global__ __launch_bounds__(256) void seal_f16_kernel(SealArgs a) {
           const float yv = L.x[row][c + e] * L.invc[c + e];
           cq[e] = (uint32_t)__builtin_amdgcn_fmed3f(rintf((yv - Zf) * inv), 0.0f, levels);
         }
-        if (bits == 4) {
-          uint32_t pk = 0;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pk |= cq[e] << (4 * e);
-          *(uint32_t*)(rec + (int64_t)row * (SUBW / 2) + c / 2) = pk;
-        } else {
-          uint2 pk = make_uint2(0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pk.x |= cq[e] << (8 * e);
-            pk.y |= cq[e + 4] << (8 * e);
-          }
-          *(uint2*)(rec + (int64_t)row * SUBW + c) = pk;
-        }
+        put_codes8(rec + (int64_t)row * (SUBW * bits / 8) + c * bits / 8, cq, bits);
       }
     }
   }
-  if (kv == 1) {  // values: channel-major, two tokens per byte (even token low)
+  if (kv == 1) {  // values: channel-major, an LSB-first stream of codes per channel
     __syncthreads();
     uint8_t* vbase = rec + y.kcode_bytes;
     for (int col = tid; col < SUBW; col += 256) {
       const float ic = L.invc[col];
       for (int t0 = 0; t0 < kGroup; t0 += 8) {
-        uint32_t pk = 0;
+        uint32_t cq[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int row = t0 + e;
           const float yv = L.x[row][col] * ic;
-          const uint32_t c = (uint32_t)__builtin_amdgcn_fmed3f(rintf((yv - L.zrow[row]) * L.rinv[row]), 0.0f, levels);
-          pk |= c << (4 * e);
+          cq[e] = (uint32_t)__builtin_amdgcn_fmed3f(rintf((yv - L.zrow[row]) * L.rinv[row]), 0.0f, levels);
         }
-        *(uint32_t*)(vbase + (int64_t)col * (kGroup / 2) + t0 / 2) = pk;
+        put_codes8(vbase + (int64_t)col * (kGroup * bits / 8) + t0 * bits / 8, cq, bits);
       }
     }
   }
@@ -816,7 +808,6 @@ __global__ __launch_bounds__(256) void seal_f16_kernel(SealArgs a) {
 hipError_t launch_seal(const SealArgs& a, hipStream_t stream) {
   dim3 grid(a.total_groups, 2 * a.y.H * a.y.nsub);
   if (a.y.f16ring) {
-    if (a.y.vbits != 4) return hipErrorInvalidValue;
     if (a.y.sub == 256)
       hipLaunchKernelGGL(seal_f16_kernel<256>, grid, dim3(256), 0, stream, a);
     else

@@ -35,10 +35,14 @@ def test_config_validation():
     n = ctypes.c_size_t()
     assert kvq.lib().kvq_cache_bytes(ctypes.byref(good), ctypes.byref(n)) == kvq.OK
     for field, val in (("head_dim", 192), ("n_q_heads", 25), ("tail_min", 100), ("tail_max", 128),
-                       ("k_bits", 3), ("v_bits", 8), ("sinkhorn_passes", 65), ("max_ctx", 0), ("n_layers", 0)):
+                       ("k_bits", 3), ("k_bits", 5), ("v_bits", 8), ("v_bits", 2), ("sinkhorn_passes", 65),
+                       ("max_ctx", 0), ("n_layers", 0)):
         bad = kvq.make_config(2, 4, 256, 24, 1, 4096, 256, 512)
         setattr(bad, field, val)
         assert kvq.lib().kvq_cache_bytes(ctypes.byref(bad), ctypes.byref(n)) == kvq.ERR_INVALID, field
+    for kb, vb in ((3, 3), (3, 2), (2, 2), (2, 3)):
+        ok = kvq.make_config(2, 4, 256, 24, 1, 4096, 256, 512, k_bits=kb, v_bits=vb)
+        assert kvq.lib().kvq_cache_bytes(ctypes.byref(ok), ctypes.byref(n)) == kvq.OK, (kb, vb)
     g17 = kvq.make_config(1, 1, 256, 17, 1, 4096, 256, 512)
     assert kvq.lib().kvq_cache_bytes(ctypes.byref(g17), ctypes.byref(n)) == kvq.ERR_INVALID
     for field, val in (("stage_fmt", 2), ("stage_fmt", -1), ("reserved", 1)):

@@ -23,6 +23,13 @@ SMALL = {
                                              ctx=1500, stage="f16"), [1500, 700], 300, "signs"),
     "gemma_f16": (configs.GEMMA31B.scaled(n_layers=1, tail_min=256, tail_max=512, ctx=1300, stage="f16"),
                   [1300], 256, None),
+    # lower scalar bodies at the config 2 shape (SJ-KVaRN 2.3: 3/3, 3/2; and 2/2), two layers, ragged
+    "qwen27b_33": (configs.QWEN27B.scaled(n_layers=2, tail_min=256, tail_max=512, ctx=2600, k_bits=3, v_bits=3),
+                   [2600, 1300], 300, None),
+    "qwen27b_32": (configs.QWEN27B.scaled(n_layers=2, tail_min=256, tail_max=512, ctx=2600, k_bits=3, v_bits=2),
+                   [2600], 300, None),
+    "qwen27b_22": (configs.QWEN27B.scaled(n_layers=1, tail_min=256, tail_max=512, ctx=2600, k_bits=2, v_bits=2,
+                                          stage="f16"), [2600], 300, None),
     # config 2 shape, two layers, ragged chunking
     "qwen27b": (configs.QWEN27B.scaled(n_layers=2, tail_min=256, tail_max=512, ctx=2600), [2600], 300, None),
     # config 3 shape: 512-wide heads as two 256-point halves, Student-t keys
@@ -258,7 +265,32 @@ def test_groups_over_eight(shape, group):
     assert p.check_sink_ring() > 0
 
 
-@pytest.mark.parametrize("name", ["qwen27b", "batched", "gemma", "qwen14b", "tiny_f16", "qwen14b_f16"])
+@pytest.mark.parametrize("shape", [(512, 3, 2), (128, 3, 3), (128, 2, 2)])
+def test_low_bit_bodies_other_widths(shape):
+    """Lower scalar bodies at 512- and 128-wide heads (the vector-ALU body scan
+    takes them; the matrix-core scan refuses them): records by the conditional
+    rule, decode against float64 attention."""
+    D, kb, vb = shape
+    base = configs.GEMMA31B if D == 512 else configs.QWEN14B1M
+    w = base.scaled(n_layers=1, n_kv_heads=2, n_q_heads=8 if D == 512 else 10, tail_min=256, tail_max=512,
+                    ctx=1400, k_bits=kb, v_bits=vb)
+    signs = inputs.rotation_signs(w.seed) if D == 128 else None
+    _say(f"[lowbit {shape}] build")
+    p = Pair(w, [1400], signs).build(200)
+    p.check_info()
+    assert p.check_sink_ring() > 0
+    st = p.check_records()
+    _say(f"[lowbit {shape}] records: {st}")
+    assert st["scales"] > 0 and st["boundary"] <= max(1, st["codes"] // 10 ** 5)
+    errs, _ = p.own_record_errors(0, p.queries(0, 0))
+    _say(f"[lowbit {shape}] decode (GPU-built cache) err={max(errs):.2e}")
+    assert max(errs) <= ATTN_TOL
+    p.gpu.set_decode_path(kvq.PATH_MFMA)
+    with pytest.raises(kvq.KVQError):
+        p.gpu.attn_decode(0, [0], p.torch.from_numpy(p.queries(0, 0)).cuda())
+
+
+@pytest.mark.parametrize("name", ["qwen27b", "batched", "gemma", "qwen14b", "tiny_f16", "qwen14b_f16", "qwen27b_32"])
 def test_decode_step(name):
     """kvq_decode_step (append one token, seal if full, decode) step after step:
     one fused launch while every new token lands in the ring and no seal is due,
@@ -273,6 +305,9 @@ def test_decode_step(name):
     if name == "qwen27b":  # ring 360 after the build: the seal fires at step 24
         w = configs.QWEN27B.scaled(n_layers=2, tail_min=256, tail_max=384, ctx=1000)
         lens = [1000]
+    elif name == "qwen27b_32":  # a 3/2 body
+        w = configs.QWEN27B.scaled(n_layers=1, tail_min=256, tail_max=384, ctx=1000, k_bits=3, v_bits=2)
+        lens = [1000, 600]
     elif name == "batched":  # one sequence starts in the sink: unfused until it leaves it
         w = configs.BATCHED.scaled(n_layers=1, n_kv_heads=2, n_q_heads=12, tail_min=256, tail_max=384, ctx=1000)
         lens = [1000, 897, 120]

@@ -477,6 +477,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other measured workloads (512-wide heads, 128-wide K8/V4, the 16-sequence batch)")
     ap.add_argument("--extra-steps", type=int, default=10, help="timed steps of each extra workload")
+    ap.add_argument("--no-widths", action="store_true",
+                    help="skip the lower body widths (3/3, 3/2, 2/2) at the headline shape")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 20 times (calibrates HBM byte counters) and exit")
     args = ap.parse_args()
@@ -515,6 +517,15 @@ def main():
             dx = run_decode(sub, wx, torch, kvq, synthetic, inputs)
             sx = None if args.no_seal else run_seal(sub, wx, torch, kvq, synthetic)
             extra[key] = workload_entry(wx, dx, sx, sub)
+    widths = {}
+    if args.workload == "qwen27b" and not args.no_widths:
+        sub = argparse.Namespace(**vars(args))
+        sub.steps, sub.warmup, sub.seal_reps, sub.save_restore = args.extra_steps, 2, 3, False
+        for kb, vb in ((3, 3), (3, 2), (2, 2)):
+            wx = w.scaled(name=f"{w.name}-{kb}{vb}", k_bits=kb, v_bits=vb)
+            dx = run_decode(sub, wx, torch, kvq, synthetic, inputs)
+            sx = None if args.no_seal else run_seal(sub, wx, torch, kvq, synthetic)
+            widths[f"{kb}/{vb}"] = workload_entry(wx, dx, sx, sub)
     mfma_body = args.path != "valu"
     traffic = measured_traffic() if (args.workload == "qwen27b" and mfma_body) else None
     if traffic is not None:
@@ -568,6 +579,8 @@ def main():
         res["tbq4_comparator"] = tbq
     if extra:
         res["workloads"] = extra
+    if widths:  # bytes vs time per body width at the headline shape (4/4 is the line itself)
+        res["body_widths"] = widths
     print(json.dumps(res), flush=True)
 
 

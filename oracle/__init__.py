@@ -24,7 +24,9 @@ section):
   body) and the journaled adaptive seal rule (SJ-KVaRN sections 2.1, 4.3).
 * ``attention`` -- float64 decode attention over every region under one
   softmax, in the original domain (SJ-KVaRN section 2.1; KV Cache Precision
-  Tail, section 2).
+  Tail, section 2), and block attention, where each of the newest n_q
+  tokens' queries sees the cached tokens up to its own position (prefill
+  chunks and verify blocks, HAL #582 section 3b).
 * ``sizes``     -- the bytes-per-token and effective-bits arithmetic the pages
   print (SJ-KVaRN sections 1, 3, 7.2, 8.4; KV cache math; HAL #582 section 1).
 * ``tq5``       -- the rotated 5-bit comparator block, 82 bytes per 128 values

@@ -59,3 +59,19 @@ def partial(q, keys, values, scale: float):
     m = s.max()
     p = np.exp(s - m)
     return m, p.sum(), p @ np.asarray(values, np.float64)
+
+
+def attend_causal_gqa(q, keys_by_head, values_by_head, p0: int, scale: float) -> np.ndarray:
+    """Block (prefill or verify) attention: q (n_q, H_q, D) holds the queries of
+    the tokens at positions p0 .. p0 + n_q - 1, each of which is already among
+    the cached tokens; query t sees tokens 0 .. p0 + t (the causal mask of a
+    prefill chunk, HAL #582 section 3b; a speculative verify block is the same
+    computation).  keys_by_head/values_by_head: (n, D) per KV head, n >= p0 + n_q.
+    Returns (n_q, H_q, D) float64."""
+    q = np.asarray(q, np.float64)
+    n_q = q.shape[0]
+    out = np.zeros_like(q)
+    for t in range(n_q):
+        n = p0 + t + 1
+        out[t] = attend_gqa(q[t], [k[:n] for k in keys_by_head], [v[:n] for v in values_by_head], scale)
+    return out

@@ -266,3 +266,20 @@ class OracleCache:
             keys.append(k)
             vals.append(v)
         return attention.attend_gqa(np.asarray(q16, np.float16).astype(np.float64), keys, vals, scale)
+
+    def attention_block(self, layer, seq, q16, scale: float) -> np.ndarray:
+        """Causal attention of the newest n_q cached tokens' queries.
+        q16 (n_q, H_q, D): query t belongs to the token at position
+        n_tok - n_q + t and sees every cached token up to that position,
+        whichever region holds it.  -> float64 (n_q, H_q, D)."""
+        q = np.asarray(q16, np.float16).astype(np.float64)
+        n_q = q.shape[0]
+        n_tok = self._state(seq, layer)["n_tok"]
+        if not 1 <= n_q <= n_tok:
+            raise ValueError("the query block must be among the cached tokens")
+        keys, vals = [], []
+        for h in range(self.H):
+            k, v = self.head_kv(seq, layer, h)
+            keys.append(k)
+            vals.append(v)
+        return attention.attend_causal_gqa(q, keys, vals, n_tok - n_q, scale)

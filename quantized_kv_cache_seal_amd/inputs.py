@@ -235,3 +235,11 @@ def queries(seed: int, step: int, layer: int, n_seqs: int, n_q_heads: int, head_
         return (normal_np(seed, st, 0, n) * s).astype(np.float16).reshape(n_seqs, n_q_heads, head_dim)
     import torch
     return (normal_t(seed, st, 0, n, device) * s).to(torch.float16).view(n_seqs, n_q_heads, head_dim)
+
+
+def block_queries(seed: int, step: int, layer: int, n_seqs: int, n_q: int, n_q_heads: int, head_dim: int,
+                  backend="numpy", device=None):
+    """Queries of a block of n_q tokens per sequence (a prefill chunk or a verify
+    block): the decode recipe over n_seqs * n_q rows, as fp16 [n_seqs][n_q][H_q][D]."""
+    q = queries(seed, step, layer, n_seqs * n_q, n_q_heads, head_dim, backend, device)
+    return q.reshape(n_seqs, n_q, n_q_heads, head_dim)

@@ -176,6 +176,26 @@ kvq_status kvq_attn_decode(kvq_cache* cache, int32_t layer, const int32_t* seq_i
 kvq_status kvq_attn_decode_noalloc(kvq_cache* cache, int32_t layer, const int32_t* seq_ids, int32_t n_seqs,
                                    const void* q, void* out, int32_t out_dtype, float scale, void* stream);
 
+/* Block attention of one layer, for prefill chunks and speculative verify
+ * blocks: the queries of the newest n_q cached tokens of each listed sequence
+ * (appended with kvq_append first), query t of the block belonging to the
+ * token at position n_tok - n_q + t and seeing every cached token at or before
+ * that position, whichever region holds it: sink, ring or sealed body (HAL
+ * #582 section 3b measures prefill over the same quantised caches; SJ-KVaRN
+ * 2.1 and KV Cache Precision Tail section 2: all regions under one softmax).
+ * The same rotated-domain arithmetic as kvq_attn_decode, on the matrix cores
+ * with up to 64 query rows (token, head) per product.
+ * q: device fp16 [n_seqs][n_q][n_q_heads][head_dim].  out: device
+ * [n_seqs][n_q][n_q_heads][head_dim], fp32 or fp16 per out_dtype.  scale
+ * multiplies q.k.  1 <= n_q <= 4096 and every listed sequence holds at least
+ * n_q tokens.  workspace: device, ws_bytes >= kvq_prefill_workspace_bytes(
+ * n_seqs, n_q).  Errors: KVQ_ERR_INVALID, KVQ_ERR_CAPACITY (workspace too
+ * small), KVQ_ERR_UNSUPPORTED (2- or 3-bit bodies), KVQ_ERR_DEVICE. */
+kvq_status kvq_prefill_workspace_bytes(const kvq_cache* cache, int32_t n_seqs, int32_t n_q, size_t* bytes);
+kvq_status kvq_attn_prefill(kvq_cache* cache, int32_t layer, const int32_t* seq_ids, int32_t n_seqs, int32_t n_q,
+                            const void* q, void* out, int32_t out_dtype, float scale, void* workspace,
+                            size_t ws_bytes, void* stream);
+
 /* One decode step of one layer: append one token per listed sequence, seal
  * what a KVQ_SEAL_IF_FULL seal of the layer would seal, then decode
  * attention of q over every cached token including the new one (SJ-KVaRN

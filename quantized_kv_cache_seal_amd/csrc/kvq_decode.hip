@@ -246,8 +246,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 }
 
 // Merge of the split-K partials (all in the original domain): one softmax
-// over the chunks of a query head, divided by the total weight.  One
-// workgroup per (sequence, query head, 64-channel slice): thread t takes
+// over the chunks of a query row, divided by the total weight.  One
+// workgroup per (sequence, query token, query head, 64-channel slice; one
+// query token per sequence for decode, the block's n_q for block attention,
+// whose partials with l = 0, fully masked, carry a finite m): thread t takes
 // channels 4 (t & 15) .. + 3 of the slice and chunks t >> 4, + 16, ...; every
 // load of a pass (the rows' float4 and their (m, l)) is issued before any is
 // used, so a pass costs one memory round trip, and each thread keeps a
@@ -263,11 +265,12 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int NSL = D / 64, U = kMergeUnroll;
   __shared__ float4 red[16][16];
   __shared__ float rm[2][16];
-  const int hq = blockIdx.x / NSL, sl = blockIdx.x % NSL, b = blockIdx.y;
+  const int hq = blockIdx.x / NSL, sl = blockIdx.x % NSL, b = blockIdx.z;
+  const int64_t row = ((int64_t)b * a.n_rows + blockIdx.y) * a.Hq + hq;  // (sequence, query token, head)
   const int tid = threadIdx.x, rg = tid >> 4, cq = tid & 15;
   const int n = a.n_chunks[b];
   const int ch = 64 * sl + 4 * cq;
-  const float* P = a.part + ((int64_t)b * a.Hq + hq) * a.max_chunks * part_stride(D);
+  const float* P = a.part + row * a.max_chunks * part_stride(D);
 
   float M = -INFINITY, L = 0.0f;
   float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -327,7 +330,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     o.w = fmaf(s, t.w, o.w);
   }
   const float inv_l = 1.0f / Lt;
-  const int64_t oi = ((int64_t)b * a.Hq + hq) * D + ch;
+  const int64_t oi = row * D + ch;
   if (a.out_f16) {
     uint2 h;
     h.x = (uint32_t)f2h_bits(o.x * inv_l) | ((uint32_t)f2h_bits(o.y * inv_l) << 16);
@@ -350,7 +353,8 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int grid_x, hipStream_t strea
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
-  dim3 grid(a.Hq * (a.D / 64), a.n_seqs);
+  if (a.n_rows < 1 || a.n_rows > 65535) return hipErrorInvalidValue;
+  dim3 grid(a.Hq * (a.D / 64), a.n_rows, a.n_seqs);
   switch (a.D) {
     case 128: hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(256), 0, stream, a); break;
     case 256: hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(256), 0, stream, a); break;

@@ -120,10 +120,37 @@ struct DecodeArgs {
 };
 
 struct MergeArgs {
-  const float* part;
-  void* out;          // [n_seqs][Hq][D] fp32 or fp16
-  int32_t D, Hq, n_seqs, max_chunks, out_f16, pad;
-  int32_t n_chunks[kMaxLaunchSeqs];
+  const float* part;  // [n_seqs][n_rows][Hq][max_chunks][part_stride(D)]
+  void* out;          // [n_seqs][n_rows][Hq][D] fp32 or fp16
+  int32_t D, Hq, n_seqs, max_chunks, out_f16;
+  int32_t n_rows;     // query tokens per sequence: 1 for decode, n_q for block attention
+  int32_t n_chunks[kMaxLaunchSeqs];  // partials per row of each sequence
+};
+
+// Block attention (prefill chunks, verify blocks): the queries of the newest
+// n_q cached tokens of each sequence, each seeing the tokens up to its own
+// position.  The rows of a (sequence, KV head) are r = t g + e (token t of
+// the block, query head e of the group), taken 16 NT at a time (a row block).
+constexpr int kMaxBlock = 4096;       // n_q limit
+constexpr int kMaxBlockChunks = 64;   // split-K chunks per row, sink included, at most 1 + this
+struct PrefillSeq {
+  int32_t slot, n_sink, ring_len, ring0, n_rec;
+  int32_t p0;          // position of the block's first token
+  int32_t ring_chunk;  // ring tokens per chunk (a multiple of 64)
+  int32_t n_ring_chunks, n_body_chunks, n_chunks;  // partial 0: sink; 1 ..: ring chunks; then body chunks
+  int32_t body_item0, ring_item0;  // this sequence's first item in the body / sink-and-ring launch
+};
+struct PrefillArgs {
+  const uint8_t* arena;
+  Layout y;
+  const uint16_t* q;  // fp16 [n_seqs][n_q][Hq][D]
+  float* part;        // [n_seqs][n_q][Hq][max_chunks][part_stride(D)]
+  float scale;
+  int32_t layer, Hq, g, n_seqs, n_q, max_chunks;
+  int32_t n_rb;       // row blocks per (sequence, KV head)
+  int32_t n_items;    // work items of the launch (the grid is rounded up to a multiple of 8)
+  uint32_t signs[8];
+  PrefillSeq seq[kMaxLaunchSeqs + 1];  // seq[n_seqs].*_item0: the launch's item counts
 };
 
 // TBQ4 comparator block (KV cache math): [fp16 norm][64 bytes of 4-bit

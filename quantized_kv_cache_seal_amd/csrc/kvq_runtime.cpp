@@ -23,6 +23,10 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int grid_x, hipStream_t strea
 hipError_t launch_decode_main(const DecodeArgs& a, int n_items, hipStream_t stream);
 hipError_t launch_decode_ring(const DecodeArgs& a, int n_items, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_prefill_body(const PrefillArgs& a, int nt, hipStream_t stream);
+hipError_t launch_prefill_ring(const PrefillArgs& a, int nt, hipStream_t stream);
+int prefill_row_tiles(int D, int rows, bool body);
+int prefill_lds_bytes(int D, int kb, int nt, bool body);
 hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_tbq4_encode(const Tbq4CodecArgs& a, hipStream_t stream);
 hipError_t launch_tbq4_decode(const Tbq4CodecArgs& a, hipStream_t stream);
@@ -151,6 +155,7 @@ static bool mfma_supported(const Layout& y) {
 // matrix-core sink and ring scan on its own: head_dim 128 or 256
 static bool staged_supported(const Layout& y) { return y.D == 128 || y.D == 256; }
 static constexpr int kRingStep = 64;         // tokens per step of the matrix-core sink/ring scan
+static constexpr int kBlockStepTokens = 64;  // tokens per step of the block-attention sink/ring scan
 static constexpr int kStagedRingChunk = 256; // ring tokens per chunk next to a vector-ALU body scan
 // resident workgroups per CU of the fused kernel (512-wide heads: one, for the LDS of their sink/ring scan)
 static int body_wg_per_cu(const Layout& y) { return y.D == 512 ? 1 : 2; }
@@ -524,6 +529,7 @@ static kvq_status decode_impl(kvq_cache* c, int32_t layer, const int32_t* seq_id
     m.n_seqs = a.n_seqs;
     m.max_chunks = max_chunks;
     m.out_f16 = out_dtype == KVQ_OUT_F16;
+    m.n_rows = 1;
     for (int b = 0; b < a.n_seqs; ++b) m.n_chunks[b] = a.seq[b].n_chunks;
     e = launch_merge(m, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
@@ -589,6 +595,136 @@ static void profile_clear(kvq_cache* c) {
   if (c->prof_ts) (void)hipFree(c->prof_ts);
   c->prof_ts = nullptr;
   c->prof_n = c->prof_used = 0;
+}
+
+// ---------------------------------------------------------------------------
+// Block attention (prefill chunks, verify blocks).  Plan: rows n_q g per
+// (sequence, KV head) in row blocks of 16 nt; every row gets the same chunks
+// as the others of its sequence: the sink, then ring chunks, then body chunks.
+// The chunk budget C per row is sized so that the launches hold about four
+// workgroups per resident slot (at least 2, at most kMaxBlockChunks chunks
+// besides the sink); a sequence's C chunks go to the ring and the body in
+// proportion to their tokens.
+static bool prefill_supported(const Layout& y) { return y.vbits == 4 && (y.kbits == 4 || y.kbits == 8); }
+
+static int prefill_chunk_budget(const kvq_cache* c, int n_seqs, int n_q) {
+  const int D = c->y.D, g = c->cfg.n_q_heads / c->y.H;
+  const int nt = prefill_row_tiles(D, n_q * g, true);
+  const int n_rb = (n_q * g + 16 * nt - 1) / (16 * nt);
+  const int lds = prefill_lds_bytes(D, c->y.kbits, nt, true);
+  const int per_cu = std::max(1, (160 << 10) / std::max(1, lds));
+  const int64_t slots = (int64_t)(c->n_cu ? c->n_cu : 256) * per_cu;
+  const int64_t pairs = std::max<int64_t>(1, (int64_t)n_seqs * c->y.H * n_rb);
+  return (int)std::min<int64_t>(kMaxBlockChunks, std::max<int64_t>(2, (4 * slots + pairs - 1) / pairs));
+}
+
+kvq_status kvq_prefill_workspace_bytes(const kvq_cache* c, int32_t n_seqs, int32_t n_q, size_t* bytes) {
+  if (!c || !bytes || n_seqs < 0 || n_q < 1 || n_q > kMaxBlock) return fail(KVQ_ERR_INVALID, "bad arguments");
+  const int C = prefill_chunk_budget(c, std::max(1, n_seqs), n_q);
+  *bytes = (size_t)n_seqs * n_q * c->cfg.n_q_heads * (1 + C) * part_stride(c->y.D) * sizeof(float);
+  return KVQ_OK;
+}
+
+kvq_status kvq_attn_prefill(kvq_cache* c, int32_t layer, const int32_t* seq_ids, int32_t n_seqs, int32_t n_q,
+                            const void* q, void* out, int32_t out_dtype, float scale, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  kvq_status st = check_decode_args(c, layer, seq_ids, n_seqs, q, out, out_dtype, workspace);
+  if (st != KVQ_OK) return st;
+  if (n_q < 1 || n_q > kMaxBlock) return fail(KVQ_ERR_INVALID, "n_q %d outside 1..%d", n_q, kMaxBlock);
+  if (n_seqs == 0) return KVQ_OK;
+  if (!prefill_supported(c->y))
+    return fail(KVQ_ERR_UNSUPPORTED, "block attention: 4- or 8-bit keys with 4-bit values");
+  for (int i = 0; i < n_seqs; ++i)
+    if (c->tok(seq_ids[i], layer) < n_q)
+      return fail(KVQ_ERR_INVALID, "sequence %d holds %lld tokens, fewer than the block's %d", seq_ids[i],
+                  (long long)c->tok(seq_ids[i], layer), n_q);
+  const int H = c->y.H, Hq = c->cfg.n_q_heads, D = c->y.D, g = Hq / H;
+  const int nt = prefill_row_tiles(D, n_q * g, true), nt_ring = prefill_row_tiles(D, n_q * g, false);
+  const int n_rb = (n_q * g + 16 * nt - 1) / (16 * nt), n_rb_ring = (n_q * g + 16 * nt_ring - 1) / (16 * nt_ring);
+  const int C = prefill_chunk_budget(c, n_seqs, n_q);
+  std::vector<PrefillSeq> plan(n_seqs);
+  int max_chunks = 1;
+  for (int i = 0; i < n_seqs; ++i) {
+    PrefillSeq& d = plan[i];
+    d = PrefillSeq{};
+    const int s = seq_ids[i];
+    const int64_t nt_tok = c->tok(s, layer);
+    d.slot = s;
+    d.n_sink = (int32_t)std::min<int64_t>(nt_tok, kSink);
+    d.n_rec = (int32_t)c->rec(s, layer);
+    d.ring_len = (int32_t)c->ring_len(s, layer);
+    d.ring0 = (int32_t)(((int64_t)kGroup * d.n_rec) % c->y.cap);
+    d.p0 = (int32_t)(nt_tok - n_q);
+    const double body_tok = (double)kGroup * d.n_rec, ring_tok = d.ring_len;
+    int nb = 0;
+    if (d.n_rec > 0) {
+      const int cap_b = std::min(d.n_rec, d.ring_len > 0 ? C - 1 : C);
+      nb = std::max(1, std::min(cap_b, (int)std::lround(C * body_tok / (body_tok + ring_tok))));
+    }
+    int nr = 0;
+    d.ring_chunk = kBlockStepTokens;
+    if (d.ring_len > 0) {
+      nr = std::max(1, C - nb);
+      d.ring_chunk = (int32_t)round_up((d.ring_len + nr - 1) / nr, kBlockStepTokens);
+      nr = (d.ring_len + d.ring_chunk - 1) / d.ring_chunk;
+    }
+    d.n_ring_chunks = nr;
+    d.n_body_chunks = nb;
+    d.n_chunks = 1 + nr + nb;
+    max_chunks = std::max(max_chunks, d.n_chunks);
+  }
+  const size_t need = (size_t)n_seqs * n_q * Hq * max_chunks * part_stride(D) * sizeof(float);
+  if (ws_bytes < need) return fail(KVQ_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  const size_t out_elem = out_dtype == KVQ_OUT_F16 ? 2 : 4;
+  for (int b0 = 0; b0 < n_seqs; b0 += kMaxLaunchSeqs) {
+    PrefillArgs a{};
+    a.arena = c->arena;
+    a.y = c->y;
+    a.n_seqs = std::min(kMaxLaunchSeqs, n_seqs - b0);
+    a.q = (const uint16_t*)q + (int64_t)b0 * n_q * Hq * D;
+    a.part = (float*)workspace + (int64_t)b0 * n_q * Hq * max_chunks * part_stride(D);
+    a.scale = scale;
+    a.layer = layer;
+    a.Hq = Hq;
+    a.g = g;
+    a.n_q = n_q;
+    a.max_chunks = max_chunks;
+    a.n_rb = n_rb;
+    std::memcpy(a.signs, c->signs, sizeof a.signs);
+    int body_items = 0, ring_items = 0;
+    for (int b = 0; b < a.n_seqs; ++b) {
+      a.seq[b] = plan[b0 + b];
+      a.seq[b].body_item0 = body_items;
+      a.seq[b].ring_item0 = ring_items;
+      body_items += H * n_rb * a.seq[b].n_body_chunks;
+      ring_items += H * n_rb_ring * (1 + a.seq[b].n_ring_chunks);
+    }
+    a.seq[a.n_seqs].body_item0 = body_items;
+    a.seq[a.n_seqs].ring_item0 = ring_items;
+    hipError_t e = hipSuccess;
+    if (body_items > 0) {
+      a.n_items = body_items;
+      e = launch_prefill_body(a, nt, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e, "block attention body launch");
+    }
+    a.n_items = ring_items;
+    a.n_rb = n_rb_ring;
+    e = launch_prefill_ring(a, nt_ring, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "block attention sink/ring launch");
+    MergeArgs m{};
+    m.part = a.part;
+    m.out = (uint8_t*)out + (size_t)b0 * n_q * Hq * D * out_elem;
+    m.D = D;
+    m.Hq = Hq;
+    m.n_seqs = a.n_seqs;
+    m.max_chunks = max_chunks;
+    m.out_f16 = out_dtype == KVQ_OUT_F16;
+    m.n_rows = n_q;
+    for (int b = 0; b < a.n_seqs; ++b) m.n_chunks[b] = a.seq[b].n_chunks;
+    e = launch_merge(m, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  return KVQ_OK;
 }
 
 kvq_status kvq_profile_start(kvq_cache* c, int32_t max_calls) {
@@ -1115,6 +1251,7 @@ kvq_status kvq_tbq4_attn_decode(const void* q, const void* k_blocks, const void*
     m.n_seqs = a.n_seqs;
     m.max_chunks = a.max_chunks;
     m.out_f16 = out_dtype == KVQ_OUT_F16;
+    m.n_rows = 1;
     e = launch_merge(m, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }

@@ -23,7 +23,8 @@ FLAG_PLAN_ONLY = 1
 
 EXPORTS = [
     "kvq_cache_bytes", "kvq_cache_create", "kvq_cache_destroy", "kvq_append", "kvq_seal",
-    "kvq_workspace_bytes", "kvq_attn_decode", "kvq_attn_decode_noalloc", "kvq_decode_step", "kvq_set_decode_path", "kvq_seq_info", "kvq_seq_reset",
+    "kvq_workspace_bytes", "kvq_attn_decode", "kvq_attn_decode_noalloc", "kvq_prefill_workspace_bytes",
+    "kvq_attn_prefill", "kvq_decode_step", "kvq_set_decode_path", "kvq_seq_info", "kvq_seq_reset",
     "kvq_seq_truncate", "kvq_seq_save_bytes", "kvq_seq_save", "kvq_seq_restore", "kvq_export", "kvq_import",
     "kvq_unit_bytes", "kvq_profile_start", "kvq_profile_stop",
     "kvq_tbq4_tables", "kvq_tbq4_encode", "kvq_tbq4_decode", "kvq_tbq4_workspace_bytes", "kvq_tbq4_attn_decode",
@@ -70,6 +71,8 @@ def lib():
             "kvq_workspace_bytes": [vp, i32, P(sz)],
             "kvq_attn_decode": [vp, i32, P(i32), i32, vp, vp, i32, ctypes.c_float, vp, sz, vp],
             "kvq_attn_decode_noalloc": [vp, i32, P(i32), i32, vp, vp, i32, ctypes.c_float, vp],
+            "kvq_prefill_workspace_bytes": [vp, i32, i32, P(sz)],
+            "kvq_attn_prefill": [vp, i32, P(i32), i32, i32, vp, vp, i32, ctypes.c_float, vp, sz, vp],
             "kvq_decode_step": [vp, i32, P(i32), i32, vp, vp, vp, vp, i32, ctypes.c_float, vp, sz, vp, P(i32)],
             "kvq_set_decode_path": [vp, i32],
             "kvq_seq_info": [vp, i32, i32, P(i64), P(i64), P(i32)],
@@ -223,6 +226,30 @@ class Cache:
         check(lib().kvq_attn_decode_noalloc(self.h, layer, ids, n, ctypes.c_void_p(q.data_ptr()),
                                             ctypes.c_void_p(out.data_ptr()), OUT_F16 if out_f16 else OUT_F32,
                                             float(scale), _stream(stream)))
+        return out
+
+    def prefill_workspace_bytes(self, n_seqs, n_q) -> int:
+        n = ctypes.c_size_t()
+        check(lib().kvq_prefill_workspace_bytes(self.h, n_seqs, n_q, ctypes.byref(n)))
+        return n.value
+
+    def attn_prefill(self, layer, seq_ids, q, out=None, scale=1.0, out_f16=False, workspace=None, stream=None):
+        """Block attention of the newest n_q tokens of each sequence:
+        q fp16 device [n_seqs][n_q][H_q][D] -> out fp32 (or fp16), same shape."""
+        import torch
+        ids, n = _ids(seq_ids)
+        assert q.is_contiguous() and q.dtype == torch.float16 and q.dim() == 4 and q.shape[0] == n
+        n_q = q.shape[1]
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float16 if out_f16 else torch.float32, device=q.device)
+        if workspace is None:
+            need = self.prefill_workspace_bytes(n, n_q)
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.arena.device)
+            workspace = self._ws
+        check(lib().kvq_attn_prefill(self.h, layer, ids, n, n_q, ctypes.c_void_p(q.data_ptr()),
+                                     ctypes.c_void_p(out.data_ptr()), OUT_F16 if out_f16 else OUT_F32, float(scale),
+                                     ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)))
         return out
 
     def decode_step(self, layer, seq_ids, k, v, q, out=None, scale=1.0, out_f16=False, workspace=None,

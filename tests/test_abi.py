@@ -145,6 +145,8 @@ def test_errors_and_truncate():
     assert kvq.lib().kvq_append(c.h, 1, *kvq._ids([1]), None, None, 200, None) == kvq.ERR_CAPACITY
     # decode and export need a device arena
     assert kvq.lib().kvq_attn_decode(c.h, 0, *kvq._ids([0]), None, None, 0, 1.0, None, 0, None) == kvq.ERR_UNSUPPORTED
+    assert kvq.lib().kvq_attn_prefill(c.h, 0, *kvq._ids([0]), 4, None, None, 0, 1.0, None, 0, None) == \
+        kvq.ERR_UNSUPPORTED
     buf = ctypes.create_string_buffer(1024)
     assert kvq.lib().kvq_export(c.h, 0, 0, 0, kvq.REGION_SINK, 0, buf, 1024, None) == kvq.ERR_UNSUPPORTED
     assert b"max_ctx" in kvq.lib().kvq_last_error() or kvq.lib().kvq_last_error()
@@ -196,3 +198,20 @@ def test_tbq4_argument_errors():
         assert L.kvq_tbq4_workspace_bytes(1, 24, 4, 256, n, ctypes.byref(sz)) == kvq.OK
         assert sz.value >= prev and (sz.value - 24 * 256 * 4) % (24 * (256 + 4) * 4) == 0
         prev = sz.value
+
+
+def test_prefill_workspace_bound():
+    """Host-only: the block-attention workspace holds n_seqs x n_q x H_q partial
+    rows for the sink plus at most 64 chunks each, and fewer chunks per row as
+    the block grows (more row blocks fill the device)."""
+    c = _plan(kvq.make_config(1, 4, 256, 24, 4, 200_000, 4096, 8192))
+    stride = (256 + 4) * 4
+    rows = lambda n_seqs, n_q: n_seqs * n_q * 24 * stride
+    verify = c.prefill_workspace_bytes(1, 8)
+    assert verify % rows(1, 8) == 0 and 3 <= verify // rows(1, 8) <= 65
+    chunk = c.prefill_workspace_bytes(1, 512)
+    assert chunk % rows(1, 512) == 0 and 3 <= chunk // rows(1, 512) < verify // rows(1, 8)
+    assert c.prefill_workspace_bytes(2, 512) <= 2 * chunk
+    n = ctypes.c_size_t()
+    for bad in ((1, 0), (1, 4097), (-1, 4)):
+        assert kvq.lib().kvq_prefill_workspace_bytes(c.h, bad[0], bad[1], ctypes.byref(n)) == kvq.ERR_INVALID

@@ -31,6 +31,7 @@ METRIC = "decode-attn effective KV GB/s (% HBM peak) at 110,592 ctx; seal tokens
 HBM_PEAK_GBS = 8000.0
 FP32_VALU_NONPACKED_TFLOPS = 78.6  # fp32 vector peak without packed instructions (disabled in this build)
 FP32_VALU_PEAK_TFLOPS = 157.3
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak
 
 
 def log(*a):
@@ -169,6 +170,78 @@ def run_decode(args, w, torch, kvq, synthetic, inputs):
         "ms_per_step": ms_step, "gbs": gbs, "bytes_step": bytes_step, "avg_kernel_us": avg_kernel_us,
         "achieved": achieved, "per_call_bytes": per_call_bytes, "info_after": info, "save_restore": sr,
     }
+
+
+def run_prefill(args, w, torch, kvq, synthetic, inputs, blocks):
+    """Block attention of the newest n_q tokens (a prefill chunk, a verify
+    block) of the built cache, every layer per step, for each n_q in blocks.
+    The record launch's matrix-core roofline: algorithmic flops per launch =
+    4 D x query rows x sealed tokens (q.k and p.v, two flops per product; the
+    block lies in the ring, so every sealed token is visible to every row)."""
+    L, H, D, Hq, N = w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads, w.n_seqs
+    t0 = time.time()
+    cache = synthetic.build(w, ctx=w.ctx, max_ctx=w.ctx)
+    n_tok, n_rec, ring = cache.info(0, 0)
+    log(f"[bench] prefill cache {w.name} built in {time.time() - t0:.1f}s: layer0 info {(n_tok, n_rec, ring)}")
+    stream = torch.cuda.current_stream()
+    out = {}
+    for n_q in blocks:
+        assert n_q <= ring, "the block lies in the ring"
+        qs = [inputs.block_queries(w.seed, 500 + l, l, N, n_q, Hq, D, backend="torch", device="cuda").contiguous()
+              for l in range(L)]
+        o = torch.empty((N, n_q, Hq, D), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(256, cache.prefill_workspace_bytes(N, n_q)), dtype=torch.uint8, device="cuda")
+        seqs = list(range(N))
+
+        def step():
+            for l in range(L):
+                cache.attn_prefill(l, seqs, qs[l], out=o, workspace=ws, stream=stream)
+
+        W, K = max(1, args.warmup // 5), args.prefill_steps
+        for _ in range(W):
+            step()
+        torch.cuda.synchronize()
+        cache.profile_start(K * L)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(K):
+            step()
+        end.record(stream)
+        torch.cuda.synchronize()
+        body_us = cache.profile_stop()
+        ms_step = start.elapsed_time(end) / K
+        rows = N * n_q * Hq
+        flops_body = 4.0 * D * rows * kvq_group_tokens(n_rec)
+        flops_all = sum(4.0 * D * N * Hq * (n_tok - n_q + t + 1) for t in range(n_q)) * L
+        avg_body = sum(body_us) / len(body_us)
+        tf_body = flops_body / (avg_body * 1e-6) / 1e12
+        cache_bytes = N * region_bytes(w, cache.unit_bytes(kvq.REGION_BODY), n_tok, n_rec, ring) * L
+        log(f"[bench] block attention n_q={n_q}: {ms_step * 1e3:.1f} us/step ({L} layers), "
+            f"{N * n_q / (ms_step * 1e-3):.0f} tokens/s; record launch avg {avg_body:.1f} us -> {tf_body:.1f} TFLOP/s")
+        out[str(n_q)] = {
+            "n_q": n_q, "us_per_step": round(ms_step * 1e3, 2),
+            "tokens_per_s": round(N * n_q / (ms_step * 1e-3), 1),
+            "attn_tflops": round(flops_all / (ms_step * 1e-3) / 1e12, 2),
+            "cache_gbs": round(cache_bytes / (ms_step * 1e-3) / 1e9, 1),
+            "record_launch_us": round(avg_body, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf_body, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf_body / MFMA_F16_PEAK_TFLOPS, 4),
+                         "kernel": "prefill_body_kernel (sealed records of one layer)",
+                         "flops_per_launch": flops_body,
+                         "flops_basis": "4 x head_dim x query rows (n_q x q_heads) x sealed tokens; the kernel "
+                                        "issues twice that on the matrix cores (hi + lo operands)",
+                         "time_basis": "library stamps: start of workgroup 0 to the end of the last workgroup",
+                         "hbm_floor_us": round(N * H * n_rec * cache.unit_bytes(kvq.REGION_BODY) /
+                                               (HBM_PEAK_GBS * 1e9) * 1e6, 2)},
+        }
+        del ws
+    del cache
+    torch.cuda.empty_cache()
+    return out
+
+
+def kvq_group_tokens(n_rec):
+    return 128 * n_rec
 
 
 def run_save_restore(cache, torch, kvq, q, ws, stream):
@@ -477,6 +550,10 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other measured workloads (512-wide heads, 128-wide K8/V4, the 16-sequence batch)")
     ap.add_argument("--extra-steps", type=int, default=10, help="timed steps of each extra workload")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the block-attention leg")
+    ap.add_argument("--prefill-steps", type=int, default=5, help="timed steps of each block-attention size")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run the block-attention leg alone (for profiling) and print its numbers")
     ap.add_argument("--no-widths", action="store_true",
                     help="skip the lower body widths (3/3, 3/2, 2/2) at the headline shape")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -504,6 +581,10 @@ def main():
     kvq.lib()
     w = {"qwen27b": configs.QWEN27B, "gemma31b": configs.GEMMA31B, "qwen14b1m": configs.QWEN14B1M,
          "batched": configs.BATCHED}[args.workload]
+    if args.prefill_only:
+        print(json.dumps({"workload": w.name, "block_attention":
+                          run_prefill(args, w, torch, kvq, synthetic, inputs, (512, 8))}), flush=True)
+        return
     dec = run_decode(args, w, torch, kvq, synthetic, inputs)
     seal = None if args.no_seal else run_seal(args, w, torch, kvq, synthetic)
     tbq = None if args.no_tbq4 else run_tbq4(args, w, torch, kvq, inputs, dec["avg_kernel_us"])
@@ -526,6 +607,9 @@ def main():
             dx = run_decode(sub, wx, torch, kvq, synthetic, inputs)
             sx = None if args.no_seal else run_seal(sub, wx, torch, kvq, synthetic)
             widths[f"{kb}/{vb}"] = workload_entry(wx, dx, sx, sub)
+    prefill = {}
+    if args.workload == "qwen27b" and not args.no_prefill:
+        prefill = run_prefill(args, w, torch, kvq, synthetic, inputs, (512, 8))
     mfma_body = args.path != "valu"
     traffic = measured_traffic() if (args.workload == "qwen27b" and mfma_body) else None
     if traffic is not None:
@@ -581,6 +665,8 @@ def main():
         res["workloads"] = extra
     if widths:  # bytes vs time per body width at the headline shape (4/4 is the line itself)
         res["body_widths"] = widths
+    if prefill:  # block attention at the headline shape: a 512-token prefill chunk and an 8-token verify block
+        res["block_attention"] = prefill
     print(json.dumps(res), flush=True)
 
 

@@ -282,11 +282,12 @@ kvq_status kvq_unit_bytes(const kvq_cache* cache, int32_t region, size_t* bytes)
 
 /* Profiling hook.  kvq_profile_start(cache, max_calls) allocates a small
  * device buffer (2 timestamps per call) on the current device; each of the
- * following kvq_attn_decode calls (up to max_calls of them) stamps, with the
- * device wall clock, the start of the first workgroup and the end of the last
- * workgroup of its main decode kernel: the fused sink/ring/body scan on the
- * matrix-core path, the vector-ALU scan otherwise (the merge is not
- * included).  The stamps cost two atomics per workgroup and add no launch or
+ * following kvq_attn_decode (and kvq_decode_step) calls, up to max_calls of
+ * them, stamps, with the device wall clock, the start of the first workgroup
+ * and the end of the last workgroup of its main decode kernel: the fused
+ * sink/ring/body scan on the matrix-core path, the vector-ALU scan otherwise
+ * (the merge is not included); a kvq_attn_prefill call whose sequences hold
+ * sealed records stamps its record launch the same way.  The stamps cost two atomics per workgroup and add no launch or
  * synchronisation to the stream.  kvq_profile_stop waits for the device,
  * writes the kernel durations in microseconds to us[0 .. *n_calls - 1] (us
  * may be NULL; otherwise it must hold max_calls floats), and frees the

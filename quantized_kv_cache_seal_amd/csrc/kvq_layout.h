@@ -132,7 +132,7 @@ struct MergeArgs {
 // position.  The rows of a (sequence, KV head) are r = t g + e (token t of
 // the block, query head e of the group), taken 16 NT at a time (a row block).
 constexpr int kMaxBlock = 4096;       // n_q limit
-constexpr int kMaxBlockChunks = 64;   // split-K chunks per row, sink included, at most 1 + this
+constexpr int kMaxBlockChunks = 64;   // ring chunks, and record chunks, per row (each at most this)
 struct PrefillSeq {
   int32_t slot, n_sink, ring_len, ring0, n_rec;
   int32_t p0;          // position of the block's first token
@@ -150,6 +150,7 @@ struct PrefillArgs {
   int32_t n_rb;       // row blocks per (sequence, KV head)
   int32_t n_items;    // work items of the launch (the grid is rounded up to a multiple of 8)
   uint32_t signs[8];
+  unsigned long long* prof_ts;  // profiling: {first start, last end} wall-clock stamps, or null
   PrefillSeq seq[kMaxLaunchSeqs + 1];  // seq[n_seqs].*_item0: the launch's item counts
 };
 

@@ -57,16 +57,16 @@ __device__ __forceinline__ int find_seq(const PrefillArgs& a, int item, bool bod
 
 // Query rows row0 .. row0 + nrows - 1 of the block (rows past its end zero)
 // into rows[nrows][D] fp32, times scale log2 e, rotated (R = H/16 per 256-point
-// half; s2 . H . s1 / sqrt(128) for 128-wide heads) or not.  Wave w takes rows
-// w, w + 4, ...; the caller synchronises before reading.
-template <int D>
+// half; s2 . H . s1 / sqrt(128) for 128-wide heads) or not.  Wave w of NW takes
+// rows w, w + NW, ...; the caller synchronises before reading.
+template <int D, int NW>
 __device__ __forceinline__ void block_query_rows(const PrefillArgs& a, int b, int h, int row0, int nrows, bool rotate,
                                                  float* rows) {
   constexpr int VPL = D / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const float sl = a.scale * kLog2e;
   const int n_rows = a.n_q * a.g;
-  for (int i = wave; i < nrows; i += 4) {
+  for (int i = wave; i < nrows; i += NW) {
     const int rr = row0 + i;
     float v[VPL];
     if (rr < n_rows) {
@@ -106,16 +106,16 @@ __device__ __forceinline__ void block_query_rows(const PrefillArgs& a, int b, in
 
 // Partial rows of a work item: rows[RB][D] fp32 in LDS (the accumulators,
 // rotated-domain when `rotate`), mrow[RB] the rows' maxima (log2 units),
-// lrow[4][RB] the waves' parts of l.  Wave w writes rows w, w + 4, ... that
+// lrow[NW][RB] the waves' parts of l.  Wave w writes rows w, w + NW, ... that
 // lie in the block.  The caller synchronises after filling the LDS arrays.
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void write_block_partials(const PrefillArgs& a, int b, int h, int rb, int RB, int chunk,
                                                      const float* rows, const float* mrow, const float* lrow,
                                                      bool rotate) {
   constexpr int VPL = D / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n_rows = a.n_q * a.g;
-  for (int i = wave; i < RB; i += 4) {
+  for (int i = wave; i < RB; i += NW) {
     const int rr = rb * RB + i;
     if (rr >= n_rows) break;
     const int t = rr / a.g, e = rr - t * a.g;
@@ -132,19 +132,21 @@ __device__ __forceinline__ void write_block_partials(const PrefillArgs& a, int b
       for (int j = 0; j < VPL; j += 4) *(float4*)(dst + j) = make_float4(v[j], v[j + 1], v[j + 2], v[j + 3]);
     }
     if (lane == 0) {
+      float l = 0.0f;
+      for (int w = 0; w < NW; ++w) l += lrow[w * RB + i];
       P[0] = fmaxf(mrow[i], kMaskedScore) * kLn2;
-      P[1] = lrow[i] + lrow[RB + i] + lrow[2 * RB + i] + lrow[3 * RB + i];
+      P[1] = l;
     }
   }
 }
 
 // A chunk none of whose keys any row of the block sees: (sentinel, 0, 0) rows.
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void write_empty_partials(const PrefillArgs& a, int b, int h, int rb, int RB, int chunk) {
   constexpr int VPL = D / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n_rows = a.n_q * a.g;
-  for (int i = wave; i < RB; i += 4) {
+  for (int i = wave; i < RB; i += NW) {
     const int rr = rb * RB + i;
     if (rr >= n_rows) break;
     const int t = rr / a.g, e = rr - t * a.g;
@@ -163,63 +165,69 @@ __device__ __forceinline__ void write_empty_partials(const PrefillArgs& a, int b
 //
 // Record shapes as in decode: NSUB sub-records of SUBW channels (256; 128 for
 // 128-wide heads; a 512-wide head is two 256-channel halves), 4- or 8-bit
-// keys, 4-bit values, each sub-record with its own C, S, Z.
+// keys, 4-bit values, each sub-record with its own C, S, Z.  NW waves (4, or 8
+// for 64-row blocks: two waves per SIMD, so that one wave's softmax overlaps
+// another's products):
 //   q~:     thread (wave w, lane (n, g)) owns the operand units
-//           (s, kk, t) = w + 4 u (t fastest, then kk): row 16 t + n, the 8
+//           (s, kk, t) = w + NW u (t fastest, then kk): row 16 t + n, the 8
 //           slots lane group g feeds at k-step kk of sub-record s.  Their q'
 //           (rotated query, hi + lo) stays in registers; per record the thread
 //           multiplies in the key C and stores q~ hi, lo to LDS;
-//   scores: wave w takes token tiles 2w, 2w + 1 (32 tokens) against every
-//           row tile; a lane's key share is CPL contiguous channels of a
-//           token row (k-step kk: channels CPL g + 8 kk ..);
-//   values: wave w takes SUBW / 64 channel tiles of each sub-record against
-//           every row tile, over the record's 128 tokens.
+//   scores: wave w takes the 16-token tiles TPW w .. (8 / NW of them) against
+//           every row tile; a lane's key share is CPL contiguous channels of a
+//           token row (k-step kk: channels CPL g + 8 kk ..).  The lo products
+//           take the key operand times 2^-11 (exact) and share the hi
+//           products' accumulator;
+//   values: wave w takes SUBW / (16 NW) channel tiles of each sub-record
+//           against every row tile, over the record's 128 tokens.
 // Token order inside a 16-token tile (position P holds token
 // (P & ~7) + [0, 4, 1, 5, 2, 6, 3, 7][P & 7]) and the 1/16 of high-nibble
 // slots are the decode kernel's: a lane's four score rows are four
 // consecutive slots of the value product's operand.  Two barriers per record.
-template <int D_, int KB_, int NT_>
+template <int D_, int KB_, int NT_, int NW_>
 struct PBody {
-  static constexpr int D = D_, KB = KB_, NT = NT_, RB = 16 * NT_;
+  static constexpr int D = D_, KB = KB_, NT = NT_, NW = NW_, RB = 16 * NT_, NTH = 64 * NW_;
   static constexpr int SUBW = D == 128 ? 128 : 256, NSUB = D / SUBW;
   static constexpr int KK = SUBW / 32;       // score k-steps per sub-record
   static constexpr int CPL = SUBW / 4;       // key channels per lane group
   static constexpr int KW = CPL * KB / 32;   // dwords of a lane's key-row share
-  static constexpr int VT = SUBW / 64;       // value channel tiles per wave and sub-record
+  static constexpr int TPW = 8 / NW;         // 16-token score tiles per wave
+  static constexpr int VT = SUBW / 16 / NW;  // value channel tiles per wave and sub-record
   static constexpr int ROWB = SUBW * KB / 8;
   static constexpr int KCODE = 128 * ROWB, VCODE = SUBW * 64;
   static constexpr int META = 4 * (SUBW + 256);
   static constexpr int SUB_BYTES = KCODE + VCODE + META;
   static constexpr int L_KS = 2 * SUBW, L_KZ = L_KS + 512, L_VC = L_KZ + 512, L_VS = L_VC + 4 * SUBW;
   static constexpr int L_VZ = L_VS + 512, MSTRIDE = 4096;
-  static constexpr int UNITS = NSUB * KK * NT * 64 / 256;  // q~ operand units per thread
+  static constexpr int UNITS = NSUB * KK * NT / NW;  // q~ operand units per thread
   // LDS: q~ [NSUB][KK][NT][hi, lo][64] uint4; weights [NSUB][hi, lo][RB][kPPitch]
-  // halves; scales [3][NSUB][MSTRIDE]; xm[4][RB], xz[NSUB][4][RB], xs[NSUB][4][RB] floats
+  // halves; scales [3][NSUB][MSTRIDE]; xm[NW][RB], xz[NSUB][NW][RB], xs[NSUB][NW][RB] floats
   static constexpr int kPPitch = 128 + 8;
   static constexpr int QT = 0, PW = QT + NSUB * KK * NT * 2 * 1024;
   static constexpr int MB = PW + NSUB * 2 * RB * kPPitch * 2;
   static constexpr int X = MB + 3 * NSUB * MSTRIDE;
-  static constexpr int total = X + (1 + 2 * NSUB) * 4 * RB * 4;
-  static_assert(NT == 1 || NT == 2 || NT == 4, "a thread's q~ units share one row tile");
-  static_assert(UNITS * 256 == NSUB * KK * NT * 64, "q~ units divide over the workgroup");
+  static constexpr int total = X + (1 + 2 * NSUB) * NW * RB * 4;
+  static_assert((NT == 1 || NT == 2 || NT == 4) && NW % NT == 0, "a thread's q~ units share one row tile");
+  static_assert(UNITS >= 1 && UNITS * NW == NSUB * KK * NT, "q~ units divide over the workgroup");
+  static_assert(TPW * NW == 8 && VT * NW * 16 == SUBW, "tiles divide over the waves");
   static_assert(RB * D * 4 <= PW - QT, "query rows (and the partial rows) fit the q~ area");
   static_assert(KW % 4 == 0, "key shares load as 16-byte pieces");
-  static_assert(L_VZ + 512 <= MSTRIDE, "scales of a sub-record fit one LDS area");
+  static_assert(L_VZ + 512 <= MSTRIDE && META <= 8 * 256, "scales of a sub-record fit one LDS area");
   static __device__ __forceinline__ int kslot(int j) { return KB == 4 ? (j >> 1) + 4 * (j & 1) : j; }
   static __device__ __forceinline__ float kfac(int j) { return KB == 4 && (j & 2) ? 0.0625f : 1.0f; }
 };
 
 template <class Sh>
-__device__ __forceinline__ void pb_load_keys(const uint8_t* __restrict__ sub, uint4 (&kd)[2][Sh::KW / 4], int wave,
-                                             int lane, bool dummy) {
+__device__ __forceinline__ void pb_load_keys(const uint8_t* __restrict__ sub, uint4 (&kd)[Sh::TPW][Sh::KW / 4],
+                                             int wave, int lane, bool dummy) {
   const int m = lane & 15, g = lane >> 4;
   const int row = (m & 8) + ((m & 7) >> 1) + 4 * (m & 1);  // position m of the tile holds this token
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < Sh::TPW; ++i)
 #pragma unroll
     for (int s = 0; s < Sh::KW / 4; ++s)
-      kd[i][s] = *(const uint4*)(sub + (dummy ? 0 : (16 * (2 * wave + i) + row) * Sh::ROWB + Sh::CPL * Sh::KB / 8 * g +
-                                                        16 * s));
+      kd[i][s] = *(const uint4*)(sub + (dummy ? 0 : (16 * (Sh::TPW * wave + i) + row) * Sh::ROWB +
+                                                        Sh::CPL * Sh::KB / 8 * g + 16 * s));
 }
 template <class Sh>
 __device__ __forceinline__ void pb_load_values(const uint8_t* __restrict__ sub, uint4 (&vd)[Sh::VT], int wave,
@@ -230,7 +238,7 @@ __device__ __forceinline__ void pb_load_values(const uint8_t* __restrict__ sub, 
     vd[j] = *(const uint4*)(sub + (dummy ? 0 : Sh::KCODE + (16 * (Sh::VT * wave + j) + m) * 64 + 16 * g));
 }
 
-// Key operand of token tile i at k-step kk (exact centred fp16).
+// Key operand of a token tile at k-step kk (exact centred fp16).
 template <class Sh>
 __device__ __forceinline__ half8 pb_key_op(const uint4 (&kd)[Sh::KW / 4], int kk) {
   if constexpr (Sh::KB == 4) {
@@ -246,7 +254,7 @@ __device__ __forceinline__ half8 pb_key_op(const uint4 (&kd)[Sh::KW / 4], int kk
 template <class Sh>
 __device__ __forceinline__ void pb_make_qtilde(const uint8_t* km, const uint4 (&qh)[Sh::UNITS],
                                                const uint4 (&ql)[Sh::UNITS], uint4* qt, float* xs, int wave, int lane) {
-  constexpr int NT = Sh::NT, KK = Sh::KK, NSUB = Sh::NSUB, RB = Sh::RB;
+  constexpr int NT = Sh::NT, KK = Sh::KK, NSUB = Sh::NSUB, RB = Sh::RB, NW = Sh::NW;
   const int n = lane & 15, g = lane >> 4;
   const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
   const half2v lo_ones = {(_Float16)kLoUnscale, (_Float16)kLoUnscale};
@@ -256,7 +264,7 @@ __device__ __forceinline__ void pb_make_qtilde(const uint8_t* km, const uint4 (&
   const int t = wave % NT;
 #pragma unroll
   for (int u = 0; u < Sh::UNITS; ++u) {
-    const int idx = wave + 4 * u, kk = (idx / NT) % KK, s = idx / (NT * KK);
+    const int idx = wave + NW * u, kk = (idx / NT) % KK, s = idx / (NT * KK);
     const uint4 c = *(const uint4*)(km + s * Sh::MSTRIDE + 2 * (Sh::CPL * g + 8 * kk));
     uint32_t cp[4];
     if constexpr (Sh::KB == 4) {  // slot pairs (c0, c4), (c1, c5), (c2, c6), (c3, c7)
@@ -292,14 +300,15 @@ __device__ __forceinline__ void pb_make_qtilde(const uint8_t* km, const uint4 (&
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
     const float v = xsum4(sig[s]);
-    if (g == 0) xs[(s * 4 + wave) * RB + 16 * t + n] = v;
+    if (g == 0) xs[(s * NW + wave) * RB + 16 * t + n] = v;
   }
 }
 
 template <class Sh>
 __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, int rb, int cbk, uint8_t* smem) {
   constexpr int D = Sh::D, SUBW = Sh::SUBW, NSUB = Sh::NSUB, KK = Sh::KK, VT = Sh::VT, NT = Sh::NT, RB = Sh::RB;
-  constexpr int SB = Sh::SUB_BYTES, MS = Sh::MSTRIDE, U = Sh::UNITS, NKS = Sh::KW / 4, PP = Sh::kPPitch;
+  constexpr int NW = Sh::NW, TPW = Sh::TPW, SB = Sh::SUB_BYTES, MS = Sh::MSTRIDE, U = Sh::UNITS, NKS = Sh::KW / 4;
+  constexpr int PP = Sh::kPPitch;
   constexpr float kMid = (float)(1 << (Sh::KB - 1));
   const Layout& y = a.y;
   const PrefillSeq& sq = a.seq[b];
@@ -307,9 +316,9 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
   uint4* qt = (uint4*)(smem + Sh::QT);
   uint16_t* pw = (uint16_t*)(smem + Sh::PW);  // [NSUB][hi, lo][RB][PP]
   uint8_t* mbuf = smem + Sh::MB;
-  float* xm = (float*)(smem + Sh::X);            // [4][RB]
-  float* xz = xm + 4 * RB;                       // [NSUB][4][RB]
-  float* xs = xz + NSUB * 4 * RB;                // [NSUB][4][RB]
+  float* xm = (float*)(smem + Sh::X);            // [NW][RB]
+  float* xz = xm + NW * RB;                      // [NSUB][NW][RB]
+  float* xs = xz + NSUB * NW * RB;               // [NSUB][NW][RB]
 
   const int chunk = 1 + sq.n_ring_chunks + cbk;
   const int r0 = (int)((int64_t)cbk * sq.n_rec / sq.n_body_chunks);
@@ -318,7 +327,7 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
   const int pmin = sq.p0 + row0 / a.g;
   const int pmax = sq.p0 + (min(n_rows, row0 + RB) - 1) / a.g;
   if (r1 <= r0 || kSink + kGroup * r0 > pmax) {
-    write_empty_partials<D>(a, b, h, rb, RB, chunk);
+    write_empty_partials<D, NW>(a, b, h, rb, RB, chunk);
     return;
   }
   int prow[NT];  // positions of this lane's rows (16 t + n); -1 past the block
@@ -331,7 +340,10 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
   const uint8_t* rec0 = a.arena + rec_off(y, sq.slot, a.layer, h, 0);
   auto rec = [&](int r) { return rec0 + (int64_t)r * y.rec_bytes; };
   auto mslot = [&](int r) { return mbuf + ((r - r0) % 3) * (NSUB * MS); };
-  const int mo = Sh::KCODE + Sh::VCODE + (Sh::META == 8 * 256 ? 8 * tid : min(8 * tid, Sh::META - 8));
+  // the first 256 threads stage the scales, 8 bytes each (clamped: threads
+  // past the end re-read the last 8 bytes and store them where nothing reads)
+  const bool stager = tid < 256;
+  const int mo = Sh::KCODE + Sh::VCODE + min(8 * (tid & 255), Sh::META - 8);
 
   // ---- prologue: scales of r0, r0 + 1 and the keys of r0 in flight while the
   // query rows are rotated into the q~ area and split into this thread's units
@@ -341,18 +353,18 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
     m0[s] = *(const uint2*)(rec(r0) + s * SB + mo);
     m1[s] = *(const uint2*)(r0 + 1 < r1 ? rec(r0 + 1) + s * SB + mo : rec0);
   }
-  uint4 kd[NSUB][2][NKS], vd[NSUB][VT];
+  uint4 kd[NSUB][TPW][NKS], vd[NSUB][VT];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) pb_load_keys<Sh>(rec(r0) + s * SB, kd[s], wave, lane, false);
   float* rows = (float*)qt;
-  block_query_rows<D>(a, b, h, row0, RB, true, rows);
+  block_query_rows<D, NW>(a, b, h, row0, RB, true, rows);
   __syncthreads();
   uint4 qh[U], ql[U];
   {
     const int t = wave % NT;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int idx = wave + 4 * u, kk = (idx / NT) % KK, s = idx / (NT * KK);
+      const int idx = wave + NW * u, kk = (idx / NT) % KK, s = idx / (NT * KK);
       const float* rp = rows + (16 * t + n) * D + SUBW * s + Sh::CPL * g + 8 * kk;
       uint32_t hb[4], lb[4];
 #pragma unroll
@@ -365,11 +377,13 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
     }
   }
   __syncthreads();  // the query rows are read: the q~ area is free
-  for (int i = tid; i < NSUB * 4 * RB; i += 256) xs[i] = 0.0f;  // rows a wave's units miss stay zero
+  for (int i = tid; i < NSUB * NW * RB; i += Sh::NTH) xs[i] = 0.0f;  // rows a wave's units miss stay zero
+  if (stager) {
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    stage_scales<Sh>(mslot(r0) + s * MS, m0[s], tid);
-    if (r0 + 1 < r1) stage_scales<Sh>(mslot(r0 + 1) + s * MS, m1[s], tid);
+    for (int s = 0; s < NSUB; ++s) {
+      stage_scales<Sh>(mslot(r0) + s * MS, m0[s], tid);
+      if (r0 + 1 < r1) stage_scales<Sh>(mslot(r0 + 1) + s * MS, m1[s], tid);
+    }
   }
   __syncthreads();
   pb_make_qtilde<Sh>(mslot(r0), qh, ql, qt, xs, wave, lane);
@@ -397,76 +411,91 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
   // this lane's score rows are tile positions 4 g + j: tokens tb + {0, 4, 1, 5}
   const int tb = 8 * (g >> 1) + 2 * (g & 1);
   constexpr int kTokOff[4] = {0, 4, 1, 5};
+  const half2v lo_a = {(_Float16)kLoUnscale, (_Float16)kLoUnscale};
 
   for (int r = r0; r < r1; ++r) {
     const uint8_t* mr = mslot(r);
     const bool more = r + 1 < r1;
     const bool masked = kSink + kGroup * r + kGroup - 1 > pmin;  // some key of the record is after some row
 
-    // ---- scores of tiles 2 wave, 2 wave + 1 against every row tile
-    float sc[2][NT][4];
+    // ---- scores of this wave's tiles against every row tile
+    float sc[TPW][NT][4];
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
-      float4v sh[2][NT], sl[2][NT];
+      float4v sh[TPW][NT];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TPW; ++i)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) sh[i][t] = sl[i][t] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+        for (int t = 0; t < NT; ++t) sh[i][t] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        half8 av[2];
+        half8 av[TPW], al[TPW];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) av[i] = pb_key_op<Sh>(kd[s][i], kk);
+        for (int i = 0; i < TPW; ++i) {
+          av[i] = pb_key_op<Sh>(kd[s][i], kk);
+          const half2v* p = (const half2v*)&av[i];
+          half2v q[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) q[e] = p[e] * lo_a;  // exact: small integers times 2^-11
+          __builtin_memcpy(&al[i], q, 16);
+        }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const uint4* op = qt + (((s * KK + kk) * NT + t) * 2) * 64 + lane;
           const half8 bh = mfma_a(op[0]), bl = mfma_a(op[64]);
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            sh[i][t] = mfma16(av[i], bh, sh[i][t]);
-            sl[i][t] = mfma16(av[i], bl, sl[i][t]);
-          }
+          for (int i = 0; i < TPW; ++i) sh[i][t] = mfma16(av[i], bh, sh[i][t]);
+#pragma unroll
+          for (int i = 0; i < TPW; ++i) sh[i][t] = mfma16(al[i], bl, sh[i][t]);
         }
       }
       const uint8_t* km = mr + s * MS;
+      float zc[TPW][4], Sk[TPW][4];
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int T = 16 * (TPW * wave + i) + tb;
+        const float2 s01 = *(const float2*)(km + Sh::L_KS + 4 * T), s45 = *(const float2*)(km + Sh::L_KS + 4 * T + 16);
+        const float2 z01 = *(const float2*)(km + Sh::L_KZ + 4 * T), z45 = *(const float2*)(km + Sh::L_KZ + 4 * T + 16);
+        Sk[i][0] = s01.x;
+        Sk[i][1] = s45.x;
+        Sk[i][2] = s01.y;
+        Sk[i][3] = s45.y;
+        zc[i][0] = fmaf(kMid, s01.x, z01.x);  // Z + mid S: exact
+        zc[i][1] = fmaf(kMid, s45.x, z45.x);
+        zc[i][2] = fmaf(kMid, s01.y, z01.y);
+        zc[i][3] = fmaf(kMid, s45.y, z45.y);
+      }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const int row = 16 * t + n;
-        const float* xr = xs + s * 4 * RB + row;
-        const float sig = xr[0] + xr[RB] + xr[2 * RB] + xr[3 * RB];
+        const float* xr = xs + s * NW * RB + 16 * t + n;
+        float sig = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int T = 16 * (2 * wave + i) + tb;
-          const float2 s01 = *(const float2*)(km + Sh::L_KS + 4 * T), s45 = *(const float2*)(km + Sh::L_KS + 4 * T + 16);
-          const float2 z01 = *(const float2*)(km + Sh::L_KZ + 4 * T), z45 = *(const float2*)(km + Sh::L_KZ + 4 * T + 16);
-          const float Sj[4] = {s01.x, s45.x, s01.y, s45.y};
-          const float Zj[4] = {z01.x, z45.x, z01.y, z45.y};
-          const float4v dot = sh[i][t] + sl[i][t] * kLoUnscale;
+        for (int w = 0; w < NW; ++w) sig += xr[w * RB];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float zc = fmaf(kMid, Sj[j], Zj[j]);  // Z + mid S: exact
-            const float v = fmaf(Sj[j], dot[j], zc * sig);
+            const float v = fmaf(Sk[i][j], sh[i][t][j], zc[i][j] * sig);
             sc[i][t][j] = s == 0 ? v : sc[i][t][j] + v;
           }
-        }
       }
     }
     if (masked) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TPW; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int pos = kSink + kGroup * r + 16 * (2 * wave + i) + tb + kTokOff[j];
+          const int pos = kSink + kGroup * r + 16 * (TPW * wave + i) + tb + kTokOff[j];
 #pragma unroll
           for (int t = 0; t < NT; ++t)
-            if (pos > prow[t]) sc[i][t][j] = kMaskedScore;
+            if (pos > prow[t]) sc[i][t][j] = -INFINITY;
         }
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       float mx = sc[0][t][0];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TPW; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sc[i][t][j]);
       mx = xmax4(mx);
@@ -480,21 +509,26 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int row = 16 * t + n;
-      const float mrec = fmaxf(fmaxf(xm[row], xm[RB + row]), fmaxf(xm[2 * RB + row], xm[3 * RB + row]));
+      float mrec = xm[row];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) mrec = fmaxf(mrec, xm[w * RB + row]);
+      mrec = fmaxf(mrec, kMaskedScore);  // a row that sees no key of the record: weights exp2(-inf) = 0
       const float m_new = fmaxf(m_run[t], mrec);
       const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_new);  // 0 on the first record
       frec[t] = __builtin_amdgcn_exp2f(mrec - m_new);
       m_run[t] = m_new;
+      if (alpha != 1.0f) {  // skipped by every lane whose maximum held
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s)
+        for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-        for (int j = 0; j < VT; ++j) acc[s][j][t] *= alpha;
+          for (int j = 0; j < VT; ++j) acc[s][j][t] *= alpha;
+      }
       float lrec = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TPW; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p = sc[i][t][j] == kMaskedScore ? 0.0f : __builtin_amdgcn_exp2f(sc[i][t][j] - mrec);
+          const float p = __builtin_amdgcn_exp2f(sc[i][t][j] - mrec);
           sc[i][t][j] = p;  // the weight from here on
           lrec += p;
         }
@@ -507,15 +541,14 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
 #pragma unroll
       for (int t = 0; t < NT; ++t) zt[t] = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int T = 16 * (2 * wave + i) + tb;
+      for (int i = 0; i < TPW; ++i) {
+        const int T = 16 * (TPW * wave + i) + tb;
         const float2 s01 = *(const float2*)(vm + Sh::L_VS + 4 * T), s45 = *(const float2*)(vm + Sh::L_VS + 4 * T + 16);
         const float2 z01 = *(const float2*)(vm + Sh::L_VZ + 4 * T), z45 = *(const float2*)(vm + Sh::L_VZ + 4 * T + 16);
-        const float Sj[4] = {s01.x, s45.x, s01.y, s45.y};
-        const float Zj[4] = {z01.x, z45.x, z01.y, z45.y};
-        float zc[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) zc[j] = fmaf(8.0f, Sj[j], Zj[j]);
+        // odd tokens sit in the high nibbles: their slots (2 and 3 here) carry 1/16
+        const float Sj[4] = {s01.x, s45.x, s01.y * 0.0625f, s45.y * 0.0625f};
+        const float zc[4] = {fmaf(8.0f, s01.x, z01.x), fmaf(8.0f, s45.x, z45.x), fmaf(8.0f, s01.y, z01.y),
+                             fmaf(8.0f, s45.y, z45.y)};
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           float x[4];
@@ -524,12 +557,10 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
             zt[t] = fmaf(sc[i][t][j], zc[j], zt[t]);
             x[j] = sc[i][t][j] * Sj[j];
           }
-          x[2] *= 0.0625f;  // odd tokens sit in the high nibbles: their slots carry 1/16
-          x[3] *= 0.0625f;
           uint2 hi, lo;
           split_h2(x[0], x[1], hi.x, lo.x);
           split_h2(x[2], x[3], hi.y, lo.y);
-          uint16_t* dst = pw + ((2 * s) * RB + 16 * t + n) * PP + 16 * (2 * wave + i) + 4 * g;
+          uint16_t* dst = pw + ((2 * s) * RB + 16 * t + n) * PP + 16 * (TPW * wave + i) + 4 * g;
           *(uint2*)dst = hi;
           *(uint2*)(dst + RB * PP) = lo;
         }
@@ -537,14 +568,16 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const float v = xsum4(zt[t]);
-        if (g == 0) xz[(s * 4 + wave) * RB + 16 * t + n] = v;
+        if (g == 0) xz[(s * NW + wave) * RB + 16 * t + n] = v;
       }
     }
     if (more) pb_make_qtilde<Sh>(mslot(r + 1), qh, ql, qt, xs, wave, lane);
+    if (stager) {
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      if (r + 2 < r1) stage_scales<Sh>(mslot(r + 2) + s * MS, mnext[s], tid);
-      mnext[s] = *(const uint2*)(r + 3 < r1 ? rec(r + 3) + s * SB + mo : rec0);
+      for (int s = 0; s < NSUB; ++s) {
+        if (r + 2 < r1) stage_scales<Sh>(mslot(r + 2) + s * MS, mnext[s], tid);
+        mnext[s] = *(const uint2*)(r + 3 < r1 ? rec(r + 3) + s * SB + mo : rec0);
+      }
     }
     __syncthreads();  // (B3) weights, zero-point sums; q~ and scales of r + 1, r + 2
 
@@ -557,11 +590,16 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
         for (int tt = 0; tt < 4; ++tt) av[j][tt] = nib8_centred(pick(vd[s][j], tt));
       pb_load_values<Sh>(more ? rec(r + 1) + s * SB : rec0, vd[s], wave, lane, !more);
       const uint8_t* vm = mr + s * MS;
+      float4 cv[VT];
+#pragma unroll
+      for (int j = 0; j < VT; ++j) cv[j] = *(const float4*)(vm + Sh::L_VC + 4 * (16 * (VT * wave + j) + 4 * g));
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int row = 16 * t + n;
-        const float* zr = xz + s * 4 * RB + row;
-        const float corr = zr[0] + zr[RB] + zr[2 * RB] + zr[3 * RB];
+        const float* zr = xz + s * NW * RB + row;
+        float corr = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) corr += zr[w * RB];
         const uint16_t* src = pw + ((2 * s) * RB + row) * PP + 32 * g;
         float4v o[VT];
 #pragma unroll
@@ -577,11 +615,10 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
         }
 #pragma unroll
         for (int j = 0; j < VT; ++j) {
-          const float4 c = *(const float4*)(vm + Sh::L_VC + 4 * (16 * (VT * wave + j) + 4 * g));
-          acc[s][j][t][0] = fmaf(c.x * frec[t], o[j][0] + corr, acc[s][j][t][0]);
-          acc[s][j][t][1] = fmaf(c.y * frec[t], o[j][1] + corr, acc[s][j][t][1]);
-          acc[s][j][t][2] = fmaf(c.z * frec[t], o[j][2] + corr, acc[s][j][t][2]);
-          acc[s][j][t][3] = fmaf(c.w * frec[t], o[j][3] + corr, acc[s][j][t][3]);
+          acc[s][j][t][0] = fmaf(cv[j].x * frec[t], o[j][0] + corr, acc[s][j][t][0]);
+          acc[s][j][t][1] = fmaf(cv[j].y * frec[t], o[j][1] + corr, acc[s][j][t][1]);
+          acc[s][j][t][2] = fmaf(cv[j].z * frec[t], o[j][2] + corr, acc[s][j][t][2]);
+          acc[s][j][t][3] = fmaf(cv[j].w * frec[t], o[j][3] + corr, acc[s][j][t][3]);
         }
       }
     }
@@ -604,13 +641,20 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
         *(float4v*)(rows + (16 * t + n) * D + SUBW * s + 16 * (VT * wave + j) + 4 * g) = acc[s][j][t];
   }
   __syncthreads();
-  write_block_partials<D>(a, b, h, rb, RB, chunk, rows, xm, xs, true);
+  write_block_partials<D, NW>(a, b, h, rb, RB, chunk, rows, xm, xs, true);
+}
+
+// 64-row blocks take 8 waves (two per SIMD), smaller blocks 4
+template <int NT>
+constexpr int body_waves() {
+  return NT == 4 ? 8 : 4;
 }
 
 template <int D, int KB, int NT>
-__global__ __launch_bounds__(256) void prefill_body_kernel(PrefillArgs a) {
-  using Sh = PBody<D, KB, NT>;
+__global__ __launch_bounds__(64 * body_waves<NT>()) void prefill_body_kernel(PrefillArgs a) {
+  using Sh = PBody<D, KB, NT, body_waves<NT>()>;
   extern __shared__ __align__(16) uint8_t smem[];
+  prof_start(a.prof_ts);
   const int item = block_item();
   if (item >= a.n_items) return;
   const int b = find_seq(a, item, true);
@@ -620,6 +664,7 @@ __global__ __launch_bounds__(256) void prefill_body_kernel(PrefillArgs a) {
   j /= a.n_rb;
   const int c = j % sq.n_body_chunks, h = j / sq.n_body_chunks;
   body_block<Sh>(a, b, h, rb, c, smem);
+  prof_end(a.prof_ts);
 }
 
 // ---------------------------------------------------------------------------
@@ -671,7 +716,7 @@ __device__ __forceinline__ void ring_block(const PrefillArgs& a, int b, int h, i
   const int pmin = sq.p0 + row0 / a.g;
   const int pmax = sq.p0 + (min(n_rows, row0 + RB) - 1) / a.g;
   if (t_begin >= t_end || pos0 + t_begin > pmax) {
-    write_empty_partials<D>(a, b, h, rb, RB, c);
+    write_empty_partials<D, 4>(a, b, h, rb, RB, c);
     return;
   }
   const int t_stop = min(t_end, pmax - pos0 + 1);  // later tokens are after every row
@@ -686,7 +731,7 @@ __device__ __forceinline__ void ring_block(const PrefillArgs& a, int b, int h, i
   // through the V^T area: k-step kk, lane (n, g): channels 32 kk + 8 g ..
   for (int t = 0; t < NT; ++t) {
     float* rows = (float*)vt;
-    block_query_rows<D>(a, b, h, row0 + 16 * t, 16, !exact, rows);
+    block_query_rows<D, 4>(a, b, h, row0 + 16 * t, 16, !exact, rows);
     __syncthreads();
     for (int kk = wave; kk < KK; kk += 4) {
       const float* r = rows + n * D + 32 * kk + 8 * g;
@@ -889,7 +934,7 @@ __device__ __forceinline__ void ring_block(const PrefillArgs& a, int b, int h, i
     for (int i = 0; i < CPW; ++i) *(float4v*)(rows + (16 * t + n) * D + 16 * (CPW * wave + i) + 4 * g) = acc[i][t];
   }
   __syncthreads();
-  write_block_partials<D>(a, b, h, rb, RB, c, rows, xm, xl, !exact);
+  write_block_partials<D, 4>(a, b, h, rb, RB, c, rows, xm, xl, !exact);
 }
 
 template <int D, int NT>
@@ -908,22 +953,23 @@ __global__ __launch_bounds__(256) void prefill_ring_kernel(PrefillArgs a) {
 }
 
 template <class K>
-hipError_t launch_lds(K kernel, int n_items, int lds, const PrefillArgs& a, hipStream_t stream) {
+hipError_t launch_lds(K kernel, int n_items, int lds, int threads, const PrefillArgs& a, hipStream_t stream) {
   if (n_items <= 0) return hipSuccess;
   hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   const int grid = (n_items + 7) / 8 * 8;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), lds, stream, a);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), lds, stream, a);
   return hipGetLastError();
 }
 
 template <int D, int KB, int NT>
 hipError_t launch_body_t(const PrefillArgs& a, hipStream_t stream) {
-  return launch_lds(prefill_body_kernel<D, KB, NT>, a.n_items, PBody<D, KB, NT>::total, a, stream);
+  using Sh = PBody<D, KB, NT, body_waves<NT>()>;
+  return launch_lds(prefill_body_kernel<D, KB, NT>, a.n_items, Sh::total, Sh::NTH, a, stream);
 }
 template <int D, int NT>
 hipError_t launch_ring_t(const PrefillArgs& a, hipStream_t stream) {
-  return launch_lds(prefill_ring_kernel<D, NT>, a.n_items, PRing<D, NT>::total, a, stream);
+  return launch_lds(prefill_ring_kernel<D, NT>, a.n_items, PRing<D, NT>::total, 256, a, stream);
 }
 
 }  // namespace
@@ -932,11 +978,12 @@ hipError_t launch_ring_t(const PrefillArgs& a, hipStream_t stream) {
 int prefill_lds_bytes(int D, int kb, int nt, bool body) {
 #define KVQ_LDS(DD, NTT)                                                                            \
   if (D == DD && nt == NTT)                                                                         \
-    return body ? (kb == 8 ? PBody<DD, 8, NTT>::total : PBody<DD, 4, NTT>::total) : PRing<DD, NTT>::total;
+    return body ? (kb == 8 ? PBody<DD, 8, NTT, body_waves<NTT>()>::total : PBody<DD, 4, NTT, body_waves<NTT>()>::total) \
+                : PRing<DD, NTT>::total;
   KVQ_LDS(128, 1) KVQ_LDS(128, 2) KVQ_LDS(128, 4)
   KVQ_LDS(256, 1) KVQ_LDS(256, 2) KVQ_LDS(256, 4)
   KVQ_LDS(512, 1)
-  if (D == 512 && nt == 2 && body) return kb == 8 ? PBody<512, 8, 2>::total : PBody<512, 4, 2>::total;
+  if (D == 512 && nt == 2 && body) return kb == 8 ? PBody<512, 8, 2, 4>::total : PBody<512, 4, 2, 4>::total;
 #undef KVQ_LDS
   return 0;
 }

@@ -599,29 +599,41 @@ static void profile_clear(kvq_cache* c) {
 
 // ---------------------------------------------------------------------------
 // Block attention (prefill chunks, verify blocks).  Plan: rows n_q g per
-// (sequence, KV head) in row blocks of 16 nt; every row gets the same chunks
-// as the others of its sequence: the sink, then ring chunks, then body chunks.
-// The chunk budget C per row is sized so that the launches hold about four
-// workgroups per resident slot (at least 2, at most kMaxBlockChunks chunks
-// besides the sink); a sequence's C chunks go to the ring and the body in
-// proportion to their tokens.
+// (sequence, KV head) in row blocks of 16 nt (the record and the sink/ring
+// launches each have their own nt); every row gets the same chunks as the
+// others of its sequence: the sink, then ring chunks, then record chunks.
+// The two launches run one after the other, so each is sized to fill the
+// device on its own: record chunks to about four workgroups per resident slot,
+// ring chunks (multiples of one 64-token step) to about two, each at most
+// kMaxBlockChunks per sequence.
 static bool prefill_supported(const Layout& y) { return y.vbits == 4 && (y.kbits == 4 || y.kbits == 8); }
 
-static int prefill_chunk_budget(const kvq_cache* c, int n_seqs, int n_q) {
-  const int D = c->y.D, g = c->cfg.n_q_heads / c->y.H;
-  const int nt = prefill_row_tiles(D, n_q * g, true);
-  const int n_rb = (n_q * g + 16 * nt - 1) / (16 * nt);
-  const int lds = prefill_lds_bytes(D, c->y.kbits, nt, true);
-  const int per_cu = std::max(1, (160 << 10) / std::max(1, lds));
-  const int64_t slots = (int64_t)(c->n_cu ? c->n_cu : 256) * per_cu;
-  const int64_t pairs = std::max<int64_t>(1, (int64_t)n_seqs * c->y.H * n_rb);
-  return (int)std::min<int64_t>(kMaxBlockChunks, std::max<int64_t>(2, (4 * slots + pairs - 1) / pairs));
+struct BlockBudget {
+  int nt, n_rb, nt_ring, n_rb_ring, body_chunks, ring_chunks;
+};
+static BlockBudget prefill_budget(const kvq_cache* c, int n_seqs, int n_q) {
+  const int D = c->y.D, g = c->cfg.n_q_heads / c->y.H, rows = n_q * g;
+  BlockBudget b;
+  b.nt = prefill_row_tiles(D, rows, true);
+  b.nt_ring = prefill_row_tiles(D, rows, false);
+  b.n_rb = (rows + 16 * b.nt - 1) / (16 * b.nt);
+  b.n_rb_ring = (rows + 16 * b.nt_ring - 1) / (16 * b.nt_ring);
+  const int64_t n_cu = c->n_cu ? c->n_cu : 256;
+  auto chunks = [&](int lds, int n_rb, int per_slot) {
+    const int64_t slots = n_cu * std::max(1, (160 << 10) / std::max(1, lds));
+    const int64_t pairs = std::max<int64_t>(1, (int64_t)std::max(1, n_seqs) * c->y.H * n_rb);
+    return (int)std::min<int64_t>(kMaxBlockChunks, std::max<int64_t>(1, (per_slot * slots + pairs - 1) / pairs));
+  };
+  b.body_chunks = chunks(prefill_lds_bytes(D, c->y.kbits, b.nt, true), b.n_rb, 4);
+  b.ring_chunks = chunks(prefill_lds_bytes(D, c->y.kbits, b.nt_ring, false), b.n_rb_ring, 2);
+  return b;
 }
 
 kvq_status kvq_prefill_workspace_bytes(const kvq_cache* c, int32_t n_seqs, int32_t n_q, size_t* bytes) {
   if (!c || !bytes || n_seqs < 0 || n_q < 1 || n_q > kMaxBlock) return fail(KVQ_ERR_INVALID, "bad arguments");
-  const int C = prefill_chunk_budget(c, std::max(1, n_seqs), n_q);
-  *bytes = (size_t)n_seqs * n_q * c->cfg.n_q_heads * (1 + C) * part_stride(c->y.D) * sizeof(float);
+  const BlockBudget bb = prefill_budget(c, n_seqs, n_q);
+  *bytes = (size_t)n_seqs * n_q * c->cfg.n_q_heads * (1 + bb.ring_chunks + bb.body_chunks) * part_stride(c->y.D) *
+           sizeof(float);
   return KVQ_OK;
 }
 
@@ -639,9 +651,8 @@ kvq_status kvq_attn_prefill(kvq_cache* c, int32_t layer, const int32_t* seq_ids,
       return fail(KVQ_ERR_INVALID, "sequence %d holds %lld tokens, fewer than the block's %d", seq_ids[i],
                   (long long)c->tok(seq_ids[i], layer), n_q);
   const int H = c->y.H, Hq = c->cfg.n_q_heads, D = c->y.D, g = Hq / H;
-  const int nt = prefill_row_tiles(D, n_q * g, true), nt_ring = prefill_row_tiles(D, n_q * g, false);
-  const int n_rb = (n_q * g + 16 * nt - 1) / (16 * nt), n_rb_ring = (n_q * g + 16 * nt_ring - 1) / (16 * nt_ring);
-  const int C = prefill_chunk_budget(c, n_seqs, n_q);
+  const BlockBudget bb = prefill_budget(c, n_seqs, n_q);
+  const int nt = bb.nt, nt_ring = bb.nt_ring, n_rb = bb.n_rb, n_rb_ring = bb.n_rb_ring;
   std::vector<PrefillSeq> plan(n_seqs);
   int max_chunks = 1;
   for (int i = 0; i < n_seqs; ++i) {
@@ -655,22 +666,15 @@ kvq_status kvq_attn_prefill(kvq_cache* c, int32_t layer, const int32_t* seq_ids,
     d.ring_len = (int32_t)c->ring_len(s, layer);
     d.ring0 = (int32_t)(((int64_t)kGroup * d.n_rec) % c->y.cap);
     d.p0 = (int32_t)(nt_tok - n_q);
-    const double body_tok = (double)kGroup * d.n_rec, ring_tok = d.ring_len;
-    int nb = 0;
-    if (d.n_rec > 0) {
-      const int cap_b = std::min(d.n_rec, d.ring_len > 0 ? C - 1 : C);
-      nb = std::max(1, std::min(cap_b, (int)std::lround(C * body_tok / (body_tok + ring_tok))));
-    }
-    int nr = 0;
+    d.n_body_chunks = std::min(d.n_rec, bb.body_chunks);
     d.ring_chunk = kBlockStepTokens;
+    d.n_ring_chunks = 0;
     if (d.ring_len > 0) {
-      nr = std::max(1, C - nb);
+      const int nr = std::min((d.ring_len + kBlockStepTokens - 1) / kBlockStepTokens, bb.ring_chunks);
       d.ring_chunk = (int32_t)round_up((d.ring_len + nr - 1) / nr, kBlockStepTokens);
-      nr = (d.ring_len + d.ring_chunk - 1) / d.ring_chunk;
+      d.n_ring_chunks = (d.ring_len + d.ring_chunk - 1) / d.ring_chunk;
     }
-    d.n_ring_chunks = nr;
-    d.n_body_chunks = nb;
-    d.n_chunks = 1 + nr + nb;
+    d.n_chunks = 1 + d.n_ring_chunks + d.n_body_chunks;
     max_chunks = std::max(max_chunks, d.n_chunks);
   }
   const size_t need = (size_t)n_seqs * n_q * Hq * max_chunks * part_stride(D) * sizeof(float);
@@ -704,8 +708,10 @@ kvq_status kvq_attn_prefill(kvq_cache* c, int32_t layer, const int32_t* seq_ids,
     hipError_t e = hipSuccess;
     if (body_items > 0) {
       a.n_items = body_items;
+      if (b0 == 0 && c->prof_used < c->prof_n) a.prof_ts = c->prof_ts + 2 * c->prof_used++;
       e = launch_prefill_body(a, nt, (hipStream_t)stream);
       if (e != hipSuccess) return hip_fail(e, "block attention body launch");
+      a.prof_ts = nullptr;
     }
     a.n_items = ring_items;
     a.n_rb = n_rb_ring;

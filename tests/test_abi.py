@@ -202,13 +202,13 @@ def test_tbq4_argument_errors():
 
 def test_prefill_workspace_bound():
     """Host-only: the block-attention workspace holds n_seqs x n_q x H_q partial
-    rows for the sink plus at most 64 chunks each, and fewer chunks per row as
-    the block grows (more row blocks fill the device)."""
+    rows for the sink plus at most 64 ring and 64 record chunks each, and fewer
+    chunks per row as the block grows (more row blocks fill the device)."""
     c = _plan(kvq.make_config(1, 4, 256, 24, 4, 200_000, 4096, 8192))
     stride = (256 + 4) * 4
     rows = lambda n_seqs, n_q: n_seqs * n_q * 24 * stride
     verify = c.prefill_workspace_bytes(1, 8)
-    assert verify % rows(1, 8) == 0 and 3 <= verify // rows(1, 8) <= 65
+    assert verify % rows(1, 8) == 0 and 3 <= verify // rows(1, 8) <= 129
     chunk = c.prefill_workspace_bytes(1, 512)
     assert chunk % rows(1, 512) == 0 and 3 <= chunk // rows(1, 512) < verify // rows(1, 8)
     assert c.prefill_workspace_bytes(2, 512) <= 2 * chunk

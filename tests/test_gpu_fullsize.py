@@ -179,3 +179,52 @@ def test_fullsize_sampled_records(full):
     _say(f"[fullsize] {W.name}: sampled records {len(sample)} x {W.n_kv_heads} heads x K,V: scales within "
          f"{SCALE_TOL}, codes exact ({ties} midpoint ties)")
     assert math.isfinite(ties)
+
+
+def _float_kv(cache, W, specs, layer, s, n_tok, n_rec):
+    """Keys and values of every cached token of (s, layer) as float64 per KV
+    head, in the original domain: the sink's and ring's inputs as the oracle
+    stages them, the GPU's own records dequantised by the oracle."""
+    D, H = W.head_dim, W.n_kv_heads
+    sg = synthetic.signs(W)
+    t_ring = 128 + 128 * n_rec
+    k_sink, v_sink = _ring_tokens(specs[s], layer, 0, 128)
+    k_ring, v_ring = _ring_tokens(specs[s], layer, t_ring, n_tok)
+    keys, vals = [], []
+    for h in range(H):
+        rr = []
+        for x16 in (k_ring[:, h], v_ring[:, h]):
+            d, u = tq6.encode_blocks(rotation.rotate(x16, D, sg).reshape(-1, D // 128, 128))
+            rr.append(rotation.inverse_exact(tq6.decode_blocks(d, u).reshape(-1, D), D, sg))
+        bufs = [cache.export(s, layer, h, kvq.REGION_BODY, r) for r in range(n_rec)]
+        kb = rotation.inverse_exact(np.concatenate([_dequant_record(b, W, 0) for b in bufs]), D, sg)
+        vb = rotation.inverse_exact(np.concatenate([_dequant_record(b, W, 1) for b in bufs]), D, sg)
+        keys.append(np.concatenate([k_sink[:, h].astype(np.float64), kb, rr[0]]))
+        vals.append(np.concatenate([v_sink[:, h].astype(np.float64), vb, rr[1]]))
+    return keys, vals
+
+
+def test_fullsize_block_attention(full):
+    """kvq_attn_prefill as bench.py times it at the headline shape: a 512-token
+    prefill chunk and an 8-token verify block (the newest tokens) of the
+    110,592-token cache, every query head of sampled rows (and every row of the
+    verify block) against float64 causal attention over the same cache."""
+    cache, torch, W, layers = full
+    if W.name != configs.QWEN27B.name:
+        pytest.skip("the block-attention leg is timed at the headline shape")
+    D, Hq, N = W.head_dim, W.n_q_heads, W.n_seqs
+    specs = [synthetic.spec_for(W, s) for s in range(N)]
+    layer = layers[-1]
+    n_tok, n_rec, ring = cache.info(0, layer)
+    keys, vals = _float_kv(cache, W, specs, layer, 0, n_tok, n_rec)
+    for n_q, rows in ((512, (0, 1, 127, 255, 256, 510, 511)), (8, tuple(range(8)))):
+        q = inputs.block_queries(W.seed, 500 + layer, layer, N, n_q, Hq, D)
+        _say(f"[fullsize] {W.name} layer {layer}: block attention n_q={n_q} at {n_tok} tokens")
+        got = cache.attn_prefill(layer, list(range(N)), torch.from_numpy(q).cuda()).cpu().numpy().astype(np.float64)
+        worst = 0.0
+        for t in rows:
+            n = n_tok - n_q + t + 1
+            ref = attention.attend_gqa(q[0, t].astype(np.float64), [k[:n] for k in keys], [v[:n] for v in vals], 1.0)
+            worst = max(worst, float(np.max(np.abs(got[0, t] - ref)) / math.sqrt(np.mean(ref ** 2))))
+        _say(f"[fullsize] block attention n_q={n_q}: err max {worst:.2e} over rows {rows} x {Hq} heads")
+        assert worst <= ATTN_TOL

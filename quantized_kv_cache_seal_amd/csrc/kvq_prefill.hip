@@ -201,7 +201,9 @@ struct PBody {
   static constexpr int L_VZ = L_VS + 512, MSTRIDE = 4096;
   static constexpr int UNITS = NSUB * KK * NT / NW;  // q~ operand units per thread
   // LDS: q~ [NSUB][KK][NT][hi, lo][64] uint4; weights [NSUB][hi, lo][RB][kPPitch]
-  // halves; scales [3][NSUB][MSTRIDE]; xm[NW][RB], xz[NSUB][NW][RB], xs[NSUB][NW][RB] floats
+  // halves; scales [3][NSUB][MSTRIDE]; per-row exchange of the waves' parts
+  // (a row's NW parts contiguous, read as 16-byte vectors): xm[RB][NW],
+  // xz[NSUB][RB][NW], xs[NSUB][RB][NW] floats
   static constexpr int kPPitch = 128 + 8;
   static constexpr int QT = 0, PW = QT + NSUB * KK * NT * 2 * 1024;
   static constexpr int MB = PW + NSUB * 2 * RB * kPPitch * 2;
@@ -250,7 +252,7 @@ __device__ __forceinline__ half8 pb_key_op(const uint4 (&kd)[Sh::KW / 4], int kk
 
 // q~ = q' C of this thread's units for the record whose scales sit at km
 // (NSUB areas of MSTRIDE), into the q~ area; sigma = sum_j q~_j of each
-// sub-record's rows: this wave's part, in xs[s][wave][row].
+// sub-record's rows: this wave's part, in xs[s][row][wave].
 template <class Sh>
 __device__ __forceinline__ void pb_make_qtilde(const uint8_t* km, const uint4 (&qh)[Sh::UNITS],
                                                const uint4 (&ql)[Sh::UNITS], uint4* qt, float* xs, int wave, int lane) {
@@ -300,7 +302,7 @@ __device__ __forceinline__ void pb_make_qtilde(const uint8_t* km, const uint4 (&
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
     const float v = xsum4(sig[s]);
-    if (g == 0) xs[(s * NW + wave) * RB + 16 * t + n] = v;
+    if (g == 0) xs[(s * RB + 16 * t + n) * NW + wave] = v;
   }
 }
 
@@ -316,9 +318,28 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
   uint4* qt = (uint4*)(smem + Sh::QT);
   uint16_t* pw = (uint16_t*)(smem + Sh::PW);  // [NSUB][hi, lo][RB][PP]
   uint8_t* mbuf = smem + Sh::MB;
-  float* xm = (float*)(smem + Sh::X);            // [NW][RB]
-  float* xz = xm + NW * RB;                      // [NSUB][NW][RB]
-  float* xs = xz + NSUB * NW * RB;               // [NSUB][NW][RB]
+  float* xm = (float*)(smem + Sh::X);            // [RB][NW]
+  float* xz = xm + NW * RB;                      // [NSUB][RB][NW]
+  float* xs = xz + NSUB * NW * RB;               // [NSUB][RB][NW]
+  // sum / maximum of a row's NW parts (16-byte reads)
+  auto sum_nw = [&](const float* p) {
+    float v = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NW; k += 4) {
+      const float4 q = *(const float4*)(p + k);
+      v += (q.x + q.y) + (q.z + q.w);
+    }
+    return v;
+  };
+  auto max_nw = [&](const float* p) {
+    float v = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NW; k += 4) {
+      const float4 q = *(const float4*)(p + k);
+      v = fmaxf(v, fmaxf(fmaxf(q.x, q.y), fmaxf(q.z, q.w)));
+    }
+    return v;
+  };
 
   const int chunk = 1 + sq.n_ring_chunks + cbk;
   const int r0 = (int)((int64_t)cbk * sq.n_rec / sq.n_body_chunks);
@@ -377,7 +398,6 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
     }
   }
   __syncthreads();  // the query rows are read: the q~ area is free
-  for (int i = tid; i < NSUB * NW * RB; i += Sh::NTH) xs[i] = 0.0f;  // rows a wave's units miss stay zero
   if (stager) {
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
@@ -467,10 +487,11 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const float* xr = xs + s * NW * RB + 16 * t + n;
+        // sigma of row tile t: the parts of the waves w = t mod NT, which own its units
+        const float* xr = xs + (s * RB + 16 * t + n) * NW;
         float sig = 0.0f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) sig += xr[w * RB];
+        for (int w = t; w < NW; w += NT) sig += xr[w];
 #pragma unroll
         for (int i = 0; i < TPW; ++i)
 #pragma unroll
@@ -499,7 +520,7 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
 #pragma unroll
         for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sc[i][t][j]);
       mx = xmax4(mx);
-      if (g == 0) xm[wave * RB + 16 * t + n] = mx;
+      if (g == 0) xm[(16 * t + n) * NW + wave] = mx;
     }
     __syncthreads();  // (B2) record maxima; q~ of r and the key codes are free
 #pragma unroll
@@ -509,10 +530,8 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int row = 16 * t + n;
-      float mrec = xm[row];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) mrec = fmaxf(mrec, xm[w * RB + row]);
-      mrec = fmaxf(mrec, kMaskedScore);  // a row that sees no key of the record: weights exp2(-inf) = 0
+      // a row that sees no key of the record: weights exp2(-inf) = 0
+      const float mrec = fmaxf(max_nw(xm + row * NW), kMaskedScore);
       const float m_new = fmaxf(m_run[t], mrec);
       const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_new);  // 0 on the first record
       frec[t] = __builtin_amdgcn_exp2f(mrec - m_new);
@@ -523,6 +542,9 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
 #pragma unroll
           for (int j = 0; j < VT; ++j) acc[s][j][t] *= alpha;
       }
+      // the record's weights are taken relative to its own maximum, so that the
+      // fp16 hi/lo weight operands of its significant tokens stay normal; its
+      // value sums enter the running ones times 2^(mrec - m_new) <= 1
       float lrec = 0.0f;
 #pragma unroll
       for (int i = 0; i < TPW; ++i)
@@ -568,7 +590,7 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const float v = xsum4(zt[t]);
-        if (g == 0) xz[(s * NW + wave) * RB + 16 * t + n] = v;
+        if (g == 0) xz[(s * RB + 16 * t + n) * NW + wave] = v;
       }
     }
     if (more) pb_make_qtilde<Sh>(mslot(r + 1), qh, ql, qt, xs, wave, lane);
@@ -596,10 +618,7 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int row = 16 * t + n;
-        const float* zr = xz + s * NW * RB + row;
-        float corr = 0.0f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) corr += zr[w * RB];
+        const float corr = sum_nw(xz + (s * RB + row) * NW);
         const uint16_t* src = pw + ((2 * s) * RB + row) * PP + 32 * g;
         float4v o[VT];
 #pragma unroll
@@ -644,15 +663,16 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
   write_block_partials<D, NW>(a, b, h, rb, RB, chunk, rows, xm, xs, true);
 }
 
-// 64-row blocks take 8 waves (two per SIMD), smaller blocks 4
-template <int NT>
+// 8 waves (two per SIMD) wherever the q~ units go round them (at least one
+// per thread): all but 16-row blocks of 128-wide heads, which take 4
+template <int D, int NT>
 constexpr int body_waves() {
-  return NT == 4 ? 8 : 4;
+  return (D == 128 ? 4 : 8 * (D / 256)) * NT >= 8 ? 8 : 4;
 }
 
 template <int D, int KB, int NT>
-__global__ __launch_bounds__(64 * body_waves<NT>()) void prefill_body_kernel(PrefillArgs a) {
-  using Sh = PBody<D, KB, NT, body_waves<NT>()>;
+__global__ __launch_bounds__((64 * body_waves<D, NT>())) void prefill_body_kernel(PrefillArgs a) {
+  using Sh = PBody<D, KB, NT, body_waves<D, NT>()>;
   extern __shared__ __align__(16) uint8_t smem[];
   prof_start(a.prof_ts);
   const int item = block_item();
@@ -713,7 +733,6 @@ __device__ __forceinline__ void ring_block(const PrefillArgs& a, int b, int h, i
   const int t_end = sink ? sq.n_sink : min(sq.ring_len, c * sq.ring_chunk);
   const int pos0 = sink ? 0 : kSink + kGroup * sq.n_rec;  // position of token 0 of the region
   const int n_rows = a.n_q * a.g, row0 = rb * RB;
-  const int pmin = sq.p0 + row0 / a.g;
   const int pmax = sq.p0 + (min(n_rows, row0 + RB) - 1) / a.g;
   if (t_begin >= t_end || pos0 + t_begin > pmax) {
     write_empty_partials<D, 4>(a, b, h, rb, RB, c);
@@ -964,7 +983,7 @@ hipError_t launch_lds(K kernel, int n_items, int lds, int threads, const Prefill
 
 template <int D, int KB, int NT>
 hipError_t launch_body_t(const PrefillArgs& a, hipStream_t stream) {
-  using Sh = PBody<D, KB, NT, body_waves<NT>()>;
+  using Sh = PBody<D, KB, NT, body_waves<D, NT>()>;
   return launch_lds(prefill_body_kernel<D, KB, NT>, a.n_items, Sh::total, Sh::NTH, a, stream);
 }
 template <int D, int NT>
@@ -978,12 +997,14 @@ hipError_t launch_ring_t(const PrefillArgs& a, hipStream_t stream) {
 int prefill_lds_bytes(int D, int kb, int nt, bool body) {
 #define KVQ_LDS(DD, NTT)                                                                            \
   if (D == DD && nt == NTT)                                                                         \
-    return body ? (kb == 8 ? PBody<DD, 8, NTT, body_waves<NTT>()>::total : PBody<DD, 4, NTT, body_waves<NTT>()>::total) \
+    return body ? (kb == 8 ? PBody<DD, 8, NTT, body_waves<DD, NTT>()>::total                                     \
+                           : PBody<DD, 4, NTT, body_waves<DD, NTT>()>::total)                                    \
                 : PRing<DD, NTT>::total;
   KVQ_LDS(128, 1) KVQ_LDS(128, 2) KVQ_LDS(128, 4)
   KVQ_LDS(256, 1) KVQ_LDS(256, 2) KVQ_LDS(256, 4)
   KVQ_LDS(512, 1)
-  if (D == 512 && nt == 2 && body) return kb == 8 ? PBody<512, 8, 2, 4>::total : PBody<512, 4, 2, 4>::total;
+  if (D == 512 && nt == 2 && body)
+    return kb == 8 ? PBody<512, 8, 2, body_waves<512, 2>()>::total : PBody<512, 4, 2, body_waves<512, 2>()>::total;
 #undef KVQ_LDS
   return 0;
 }

@@ -39,21 +39,31 @@ def log(*a):
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_main_kernel_qwen27b_ctx110592.md")
-KERNEL_SOURCE = os.path.join(ROOT, "quantized_kv_cache_seal_amd", "csrc", "kvq_decode_fused.hip")
+# the decode kernel's source and the headers it includes
+KERNEL_SOURCES = [os.path.join(ROOT, "quantized_kv_cache_seal_amd", "csrc", f) for f in
+                  ("kvq_decode_fused.hip", "kvq_codes.h", "kvq_mfma.h", "kvq_encode.h", "kvq_device.h",
+                   "kvq_layout.h")]
+
+
+def kernel_sha():
+    """First 16 hex digits of the SHA-256 of the decode kernel's sources, concatenated."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def profile_record(key):
     """The `key:` record line of the decode profile summary as a dict, or None
-    when the summary is missing or the kernel source has changed since it was
+    when the summary is missing or the kernel sources have changed since it was
     taken."""
-    import hashlib
     try:
         line = next(l for l in open(TRAFFIC_PROFILE) if l.startswith(key + ":"))
     except (OSError, StopIteration):
         return None
     rec = dict(kv.split("=", 1) for kv in line.split()[1:])
-    src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
-    return rec if rec.get("kernel_sha256") == src else None
+    return rec if rec.get("kernel_sha256") == kernel_sha() else None
 
 
 def measured_traffic():
@@ -61,14 +71,8 @@ def measured_traffic():
     recorded in the profile summary (FETCH_SIZE and WRITE_SIZE in KiB per
     dispatch, each times its copy-calibrated scale), or None when the kernel
     source has changed since the counters were taken."""
-    import hashlib
-    try:
-        line = next(l for l in open(TRAFFIC_PROFILE) if l.startswith("traffic-record:"))
-    except (OSError, StopIteration):
-        return None
-    rec = dict(kv.split("=", 1) for kv in line.split()[1:])
-    src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
-    if rec.get("kernel_sha256") != src:
+    rec = profile_record("traffic-record")
+    if rec is None:
         return None
     return (float(rec["fetch_kib"]) * float(rec["fetch_scale"]) + float(rec["write_kib"]) * float(rec["write_scale"])) * 1024
 

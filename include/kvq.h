@@ -1,7 +1,9 @@
 /*
  * kvq.h -- C ABI of an MI355X (gfx950) quantized KV cache: a 128-token fp16
- * sink, a rotated 6-bit staging ring holding the exact tail, and sealed 4-bit
- * (or 8-bit key) body records, read by one split-K decode-attention pass.
+ * sink, a staging ring holding the exact tail (rotated 6-bit, or fp16), and
+ * sealed body records (4/4, 8/4, 3/3, 3/2, 2/2 or 2/3 bits per key/value
+ * code), read by one split-K decode-attention pass, or by block attention
+ * for prefill chunks and verify blocks.
  *
  * The method is SJ-KVaRN (page "SJ-KVaRN", sections 2-4) built on KVarN:
  *   - section 2.1 "The life of a token": sink, staging, exact tail, seal;
@@ -61,7 +63,8 @@ enum { KVQ_STAGE_TQ6 = 0, KVQ_STAGE_F16 = 1 };
 
 /* Sizes are in tokens unless noted.  Constraints checked by every call:
  *   head_dim in {128, 256, 512}; n_q_heads a multiple of n_kv_heads with
- *   n_q_heads / n_kv_heads <= 16; k_bits in {4, 8}, v_bits == 4;
+ *   n_q_heads / n_kv_heads <= 16; (k_bits, v_bits) in {(4, 4), (8, 4)}, or
+ *   k_bits and v_bits both in {2, 3} (SJ-KVaRN 2.3: 3/3, 3/2; and 2/2, 2/3);
  *   tail_min a multiple of 128, 128 <= tail_min <= tail_max;
  *   margin >= 0; max_ctx >= 1; 0 <= sinkhorn_passes <= 64.
  * Ring capacity = round_up(tail_max + margin, 128) token slots, allocated up
@@ -216,9 +219,11 @@ kvq_status kvq_decode_step(kvq_cache* cache, int32_t layer, const int32_t* seq_i
                            int32_t* groups_sealed);
 
 /* Select the kernel that scans sealed records: KVQ_PATH_AUTO (the default)
- * and KVQ_PATH_MFMA take the matrix cores (every shape the cache accepts:
- * head_dim 128, 256 or 512, 4- or 8-bit K, 4-bit V), KVQ_PATH_VALU the
- * vector-ALU reference scan (kept for A/B checks).  Errors: KVQ_ERR_INVALID. */
+ * and KVQ_PATH_MFMA take the matrix cores (head_dim 128, 256 or 512 with
+ * 4- or 8-bit K and 4-bit V; the 2- and 3-bit bodies at head_dim 256; AUTO
+ * takes the vector-ALU scan for the 2- and 3-bit bodies of other widths,
+ * MFMA refuses them with KVQ_ERR_UNSUPPORTED), KVQ_PATH_VALU the vector-ALU
+ * reference scan (kept for A/B checks).  Errors: KVQ_ERR_INVALID. */
 kvq_status kvq_set_decode_path(kvq_cache* cache, int32_t path);
 
 /* Host-side counts of one (sequence, layer): tokens cached, sealed records,
@@ -263,10 +268,11 @@ kvq_status kvq_seq_restore(kvq_cache* cache, int32_t seq, const void* host_src, 
  *     blocks of 98 bytes, each [fp16 d][96-byte LSB-first 6-bit stream]
  *     (f16 staging: [K fp16 x head_dim][V fp16 x head_dim], as the sink);
  *   KVQ_REGION_BODY, index = record: the record bytes, per 256-channel
- *     sub-tile (128 for 128-wide heads) [K codes 128 tokens x sub, row-major,
- *     two 4-bit codes per byte with the even channel low, or one 8-bit code]
- *     [V codes sub channels x 128 tokens, channel-major, even token low]
- *     [K: C[sub] S[128] Z[128] fp16][V: the same].
+ *     sub-tile (128 for 128-wide heads) [K codes 128 tokens x sub, row-major]
+ *     [V codes sub channels x 128 tokens, channel-major] [K: C[sub] S[128]
+ *     Z[128] fp16][V: the same]; each row of codes an LSB-first stream of
+ *     k_bits (v_bits) values, value i in bits b i .. b i + b - 1 (4 bits: the
+ *     even element in the low nibble; 8 bits: one byte each).
  * bytes must equal the unit's size (kvq_unit_bytes).  Errors:
  * KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED (plan-only cache), KVQ_ERR_DEVICE. */
 kvq_status kvq_export(const kvq_cache* cache, int32_t seq, int32_t layer, int32_t kv_head, int32_t region,

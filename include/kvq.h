@@ -192,8 +192,10 @@ kvq_status kvq_attn_decode_noalloc(kvq_cache* cache, int32_t layer, const int32_
  * [n_seqs][n_q][n_q_heads][head_dim], fp32 or fp16 per out_dtype.  scale
  * multiplies q.k.  1 <= n_q <= 4096 and every listed sequence holds at least
  * n_q tokens.  workspace: device, ws_bytes >= kvq_prefill_workspace_bytes(
- * n_seqs, n_q).  Errors: KVQ_ERR_INVALID, KVQ_ERR_CAPACITY (workspace too
- * small), KVQ_ERR_UNSUPPORTED (2- or 3-bit bodies), KVQ_ERR_DEVICE. */
+ * n_seqs, n_q).  Every body width is supported at head_dim 256; at 128 and
+ * 512 the 4/4 and 8/4 bodies.  Errors: KVQ_ERR_INVALID, KVQ_ERR_CAPACITY
+ * (workspace too small), KVQ_ERR_UNSUPPORTED (2- or 3-bit bodies at head_dim
+ * 128 or 512), KVQ_ERR_DEVICE. */
 kvq_status kvq_prefill_workspace_bytes(const kvq_cache* cache, int32_t n_seqs, int32_t n_q, size_t* bytes);
 kvq_status kvq_attn_prefill(kvq_cache* cache, int32_t layer, const int32_t* seq_ids, int32_t n_seqs, int32_t n_q,
                             const void* q, void* out, int32_t out_dtype, float scale, void* workspace,

@@ -180,21 +180,28 @@ __device__ __forceinline__ void write_empty_partials(const PrefillArgs& a, int b
 //           products' accumulator;
 //   values: wave w takes SUBW / (16 NW) channel tiles of each sub-record
 //           against every row tile, over the record's 128 tokens.
-// Token order inside a 16-token tile (position P holds token
-// (P & ~7) + [0, 4, 1, 5, 2, 6, 3, 7][P & 7]) and the 1/16 of high-nibble
-// slots are the decode kernel's: a lane's four score rows are four
-// consecutive slots of the value product's operand.  Two barriers per record.
-template <int D_, int KB_, int NT_, int NW_>
+// With 4-bit values the token order inside a 16-token tile (position P holds
+// token (P & ~7) + [0, 4, 1, 5, 2, 6, 3, 7][P & 7]) and the 1/16 of
+// high-nibble slots are the decode kernel's: a lane's four score rows are four
+// consecutive slots of the value product's operand.  The 2- and 3-bit bodies
+// (SJ-KVaRN 2.3: 3/3, 3/2; and 2/2, 2/3) take natural order instead (NAT):
+// position P holds token P, k-step kk of a key row feeds channels
+// CPL g + 8 kk .. in order, and the codes are unpacked from the b-bit row
+// streams (codes_lb), as the decode's low-bit scan does.  Two barriers per
+// record.
+template <int D_, int KB_, int VB_, int NT_, int NW_>
 struct PBody {
-  static constexpr int D = D_, KB = KB_, NT = NT_, NW = NW_, RB = 16 * NT_, NTH = 64 * NW_;
+  static constexpr int D = D_, KB = KB_, VB = VB_, NT = NT_, NW = NW_, RB = 16 * NT_, NTH = 64 * NW_;
+  static constexpr bool NAT = VB != 4;
   static constexpr int SUBW = D == 128 ? 128 : 256, NSUB = D / SUBW;
   static constexpr int KK = SUBW / 32;       // score k-steps per sub-record
   static constexpr int CPL = SUBW / 4;       // key channels per lane group
   static constexpr int KW = CPL * KB / 32;   // dwords of a lane's key-row share
   static constexpr int TPW = 8 / NW;         // 16-token score tiles per wave
   static constexpr int VT = SUBW / 16 / NW;  // value channel tiles per wave and sub-record
-  static constexpr int ROWB = SUBW * KB / 8;
-  static constexpr int KCODE = 128 * ROWB, VCODE = SUBW * 64;
+  static constexpr int ROWB = SUBW * KB / 8, VROW = 128 * VB / 8;  // bytes per key / value code row
+  static constexpr int VW = VB;                                       // dwords of a lane's value-row share
+  static constexpr int KCODE = 128 * ROWB, VCODE = SUBW * VROW;
   static constexpr int META = 4 * (SUBW + 256);
   static constexpr int SUB_BYTES = KCODE + VCODE + META;
   static constexpr int L_KS = 2 * SUBW, L_KZ = L_KS + 512, L_VC = L_KZ + 512, L_VS = L_VC + 4 * SUBW;
@@ -213,40 +220,81 @@ struct PBody {
   static_assert(UNITS >= 1 && UNITS * NW == NSUB * KK * NT, "q~ units divide over the workgroup");
   static_assert(TPW * NW == 8 && VT * NW * 16 == SUBW, "tiles divide over the waves");
   static_assert(RB * D * 4 <= PW - QT, "query rows (and the partial rows) fit the q~ area");
-  static_assert(KW % 4 == 0, "key shares load as 16-byte pieces");
+  static_assert(KW % 2 == 0 && (!NAT || (SUBW == 256 && KB <= 3)), "key shares load as 8-byte pieces");
   static_assert(L_VZ + 512 <= MSTRIDE && META <= 8 * 256, "scales of a sub-record fit one LDS area");
   static __device__ __forceinline__ int kslot(int j) { return KB == 4 ? (j >> 1) + 4 * (j & 1) : j; }
   static __device__ __forceinline__ float kfac(int j) { return KB == 4 && (j & 2) ? 0.0625f : 1.0f; }
+  // tile position of a lane's score row jj (lane group g): token tok_base(g) + tok_off(jj)
+  static __device__ __forceinline__ int tok_base(int g) { return NAT ? 4 * g : 8 * (g >> 1) + 2 * (g & 1); }
+  static __device__ __forceinline__ int tok_off(int jj) { return NAT ? jj : (jj >> 1) + 4 * (jj & 1); }
 };
 
 template <class Sh>
-__device__ __forceinline__ void pb_load_keys(const uint8_t* __restrict__ sub, uint4 (&kd)[Sh::TPW][Sh::KW / 4],
+__device__ __forceinline__ void pb_load_keys(const uint8_t* __restrict__ sub, uint32_t (&kd)[Sh::TPW][Sh::KW],
                                              int wave, int lane, bool dummy) {
   const int m = lane & 15, g = lane >> 4;
-  const int row = (m & 8) + ((m & 7) >> 1) + 4 * (m & 1);  // position m of the tile holds this token
+  // position m of the tile holds this token
+  const int row = Sh::NAT ? m : (m & 8) + ((m & 7) >> 1) + 4 * (m & 1);
 #pragma unroll
-  for (int i = 0; i < Sh::TPW; ++i)
+  for (int i = 0; i < Sh::TPW; ++i) {
+    const uint8_t* p = sub + (dummy ? 0 : (16 * (Sh::TPW * wave + i) + row) * Sh::ROWB + Sh::CPL * Sh::KB / 8 * g);
+    if constexpr (Sh::KW % 4 == 0) {
 #pragma unroll
-    for (int s = 0; s < Sh::KW / 4; ++s)
-      kd[i][s] = *(const uint4*)(sub + (dummy ? 0 : (16 * (Sh::TPW * wave + i) + row) * Sh::ROWB +
-                                                        Sh::CPL * Sh::KB / 8 * g + 16 * s));
+      for (int s = 0; s < Sh::KW / 4; ++s) {
+        const uint4 v = *(const uint4*)(p + 16 * s);
+        kd[i][4 * s] = v.x;
+        kd[i][4 * s + 1] = v.y;
+        kd[i][4 * s + 2] = v.z;
+        kd[i][4 * s + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < Sh::KW / 2; ++s) {
+        const uint2 v = *(const uint2*)(p + 8 * s);
+        kd[i][2 * s] = v.x;
+        kd[i][2 * s + 1] = v.y;
+      }
+    }
+  }
 }
 template <class Sh>
-__device__ __forceinline__ void pb_load_values(const uint8_t* __restrict__ sub, uint4 (&vd)[Sh::VT], int wave,
-                                               int lane, bool dummy) {
+__device__ __forceinline__ void pb_load_values(const uint8_t* __restrict__ sub, uint32_t (&vd)[Sh::VT][Sh::VW],
+                                               int wave, int lane, bool dummy) {
   const int m = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int j = 0; j < Sh::VT; ++j)
-    vd[j] = *(const uint4*)(sub + (dummy ? 0 : Sh::KCODE + (16 * (Sh::VT * wave + j) + m) * 64 + 16 * g));
+  for (int j = 0; j < Sh::VT; ++j) {
+    const uint8_t* p = sub + (dummy ? 0 : Sh::KCODE + (16 * (Sh::VT * wave + j) + m) * Sh::VROW + 4 * Sh::VB * g);
+    if constexpr (Sh::VW == 4) {
+      const uint4 v = *(const uint4*)p;
+      vd[j][0] = v.x;
+      vd[j][1] = v.y;
+      vd[j][2] = v.z;
+      vd[j][3] = v.w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < Sh::VW; ++k) vd[j][k] = ((const uint32_t*)p)[k];
+    }
+  }
 }
 
-// Key operand of a token tile at k-step kk (exact centred fp16).
+// Key operand of a token tile at k-step kk, value operand of a channel tile
+// at k-step tt (exact centred fp16).
 template <class Sh>
-__device__ __forceinline__ half8 pb_key_op(const uint4 (&kd)[Sh::KW / 4], int kk) {
+__device__ __forceinline__ half8 pb_key_op(const uint32_t (&kd)[Sh::KW], int kk) {
   if constexpr (Sh::KB == 4) {
-    return nib8_centred(pick(kd[kk >> 2], kk & 3));
+    return nib8_centred(kd[kk]);
+  } else if constexpr (Sh::KB == 8) {
+    return byte8_centred(kd[2 * kk], kd[2 * kk + 1]);
   } else {
-    return byte8_centred(pick(kd[kk >> 1], 2 * (kk & 1)), pick(kd[kk >> 1], 2 * (kk & 1) + 1));
+    return codes_lb<Sh::KB>(step_bits<Sh::KB>(kd, kk));
+  }
+}
+template <class Sh>
+__device__ __forceinline__ half8 pb_value_op(const uint32_t (&vd)[Sh::VW], int tt) {
+  if constexpr (Sh::VB == 4) {
+    return nib8_centred(vd[tt]);
+  } else {
+    return codes_lb<Sh::VB>(step_bits<Sh::VB>(vd, tt));
   }
 }
 
@@ -309,7 +357,7 @@ __device__ __forceinline__ void pb_make_qtilde(const uint8_t* km, const uint4 (&
 template <class Sh>
 __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, int rb, int cbk, uint8_t* smem) {
   constexpr int D = Sh::D, SUBW = Sh::SUBW, NSUB = Sh::NSUB, KK = Sh::KK, VT = Sh::VT, NT = Sh::NT, RB = Sh::RB;
-  constexpr int NW = Sh::NW, TPW = Sh::TPW, SB = Sh::SUB_BYTES, MS = Sh::MSTRIDE, U = Sh::UNITS, NKS = Sh::KW / 4;
+  constexpr int NW = Sh::NW, TPW = Sh::TPW, SB = Sh::SUB_BYTES, MS = Sh::MSTRIDE, U = Sh::UNITS, KW = Sh::KW;
   constexpr int PP = Sh::kPPitch;
   constexpr float kMid = (float)(1 << (Sh::KB - 1));
   const Layout& y = a.y;
@@ -374,7 +422,7 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
     m0[s] = *(const uint2*)(rec(r0) + s * SB + mo);
     m1[s] = *(const uint2*)(r0 + 1 < r1 ? rec(r0 + 1) + s * SB + mo : rec0);
   }
-  uint4 kd[NSUB][TPW][NKS], vd[NSUB][VT];
+  uint32_t kd[NSUB][TPW][KW], vd[NSUB][VT][Sh::VW];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) pb_load_keys<Sh>(rec(r0) + s * SB, kd[s], wave, lane, false);
   float* rows = (float*)qt;
@@ -429,8 +477,7 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
       for (int t = 0; t < NT; ++t) acc[s][j][t] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 
   // this lane's score rows are tile positions 4 g + j: tokens tb + {0, 4, 1, 5}
-  const int tb = 8 * (g >> 1) + 2 * (g & 1);
-  constexpr int kTokOff[4] = {0, 4, 1, 5};
+  const int tb = Sh::tok_base(g);
   const half2v lo_a = {(_Float16)kLoUnscale, (_Float16)kLoUnscale};
 
   for (int r = r0; r < r1; ++r) {
@@ -474,16 +521,31 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
         const int T = 16 * (TPW * wave + i) + tb;
-        const float2 s01 = *(const float2*)(km + Sh::L_KS + 4 * T), s45 = *(const float2*)(km + Sh::L_KS + 4 * T + 16);
-        const float2 z01 = *(const float2*)(km + Sh::L_KZ + 4 * T), z45 = *(const float2*)(km + Sh::L_KZ + 4 * T + 16);
-        Sk[i][0] = s01.x;
-        Sk[i][1] = s45.x;
-        Sk[i][2] = s01.y;
-        Sk[i][3] = s45.y;
-        zc[i][0] = fmaf(kMid, s01.x, z01.x);  // Z + mid S: exact
-        zc[i][1] = fmaf(kMid, s45.x, z45.x);
-        zc[i][2] = fmaf(kMid, s01.y, z01.y);
-        zc[i][3] = fmaf(kMid, s45.y, z45.y);
+        float Zk[4];
+        if constexpr (Sh::NAT) {  // tokens T .. T + 3
+          const float4 s4 = *(const float4*)(km + Sh::L_KS + 4 * T), z4 = *(const float4*)(km + Sh::L_KZ + 4 * T);
+          Sk[i][0] = s4.x;
+          Sk[i][1] = s4.y;
+          Sk[i][2] = s4.z;
+          Sk[i][3] = s4.w;
+          Zk[0] = z4.x;
+          Zk[1] = z4.y;
+          Zk[2] = z4.z;
+          Zk[3] = z4.w;
+        } else {  // tokens T + {0, 4, 1, 5}
+          const float2 s01 = *(const float2*)(km + Sh::L_KS + 4 * T), s45 = *(const float2*)(km + Sh::L_KS + 4 * T + 16);
+          const float2 z01 = *(const float2*)(km + Sh::L_KZ + 4 * T), z45 = *(const float2*)(km + Sh::L_KZ + 4 * T + 16);
+          Sk[i][0] = s01.x;
+          Sk[i][1] = s45.x;
+          Sk[i][2] = s01.y;
+          Sk[i][3] = s45.y;
+          Zk[0] = z01.x;
+          Zk[1] = z45.x;
+          Zk[2] = z01.y;
+          Zk[3] = z45.y;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) zc[i][j] = fmaf(kMid, Sk[i][j], Zk[j]);  // Z + mid S: exact
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -506,7 +568,7 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
       for (int i = 0; i < TPW; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int pos = kSink + kGroup * r + 16 * (TPW * wave + i) + tb + kTokOff[j];
+          const int pos = kSink + kGroup * r + 16 * (TPW * wave + i) + tb + Sh::tok_off(j);
 #pragma unroll
           for (int t = 0; t < NT; ++t)
             if (pos > prow[t]) sc[i][t][j] = -INFINITY;
@@ -565,12 +627,31 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
         const int T = 16 * (TPW * wave + i) + tb;
-        const float2 s01 = *(const float2*)(vm + Sh::L_VS + 4 * T), s45 = *(const float2*)(vm + Sh::L_VS + 4 * T + 16);
-        const float2 z01 = *(const float2*)(vm + Sh::L_VZ + 4 * T), z45 = *(const float2*)(vm + Sh::L_VZ + 4 * T + 16);
-        // odd tokens sit in the high nibbles: their slots (2 and 3 here) carry 1/16
-        const float Sj[4] = {s01.x, s45.x, s01.y * 0.0625f, s45.y * 0.0625f};
-        const float zc[4] = {fmaf(8.0f, s01.x, z01.x), fmaf(8.0f, s45.x, z45.x), fmaf(8.0f, s01.y, z01.y),
-                             fmaf(8.0f, s45.y, z45.y)};
+        constexpr float kMidV = (float)(1 << (Sh::VB - 1));
+        float Sj[4], zc[4];
+        if constexpr (Sh::NAT) {  // tokens T .. T + 3
+          const float4 s4 = *(const float4*)(vm + Sh::L_VS + 4 * T), z4 = *(const float4*)(vm + Sh::L_VZ + 4 * T);
+          Sj[0] = s4.x;
+          Sj[1] = s4.y;
+          Sj[2] = s4.z;
+          Sj[3] = s4.w;
+          zc[0] = fmaf(kMidV, s4.x, z4.x);
+          zc[1] = fmaf(kMidV, s4.y, z4.y);
+          zc[2] = fmaf(kMidV, s4.z, z4.z);
+          zc[3] = fmaf(kMidV, s4.w, z4.w);
+        } else {  // tokens T + {0, 4, 1, 5}
+          const float2 s01 = *(const float2*)(vm + Sh::L_VS + 4 * T), s45 = *(const float2*)(vm + Sh::L_VS + 4 * T + 16);
+          const float2 z01 = *(const float2*)(vm + Sh::L_VZ + 4 * T), z45 = *(const float2*)(vm + Sh::L_VZ + 4 * T + 16);
+          // odd tokens sit in the high nibbles: their slots (2 and 3 here) carry 1/16
+          Sj[0] = s01.x;
+          Sj[1] = s45.x;
+          Sj[2] = s01.y * 0.0625f;
+          Sj[3] = s45.y * 0.0625f;
+          zc[0] = fmaf(kMidV, s01.x, z01.x);
+          zc[1] = fmaf(kMidV, s45.x, z45.x);
+          zc[2] = fmaf(kMidV, s01.y, z01.y);
+          zc[3] = fmaf(kMidV, s45.y, z45.y);
+        }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           float x[4];
@@ -609,7 +690,7 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
 #pragma unroll
       for (int j = 0; j < VT; ++j)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) av[j][tt] = nib8_centred(pick(vd[s][j], tt));
+        for (int tt = 0; tt < 4; ++tt) av[j][tt] = pb_value_op<Sh>(vd[s][j], tt);
       pb_load_values<Sh>(more ? rec(r + 1) + s * SB : rec0, vd[s], wave, lane, !more);
       const uint8_t* vm = mr + s * MS;
       float4 cv[VT];
@@ -670,9 +751,9 @@ constexpr int body_waves() {
   return (D == 128 ? 4 : 8 * (D / 256)) * NT >= 8 ? 8 : 4;
 }
 
-template <int D, int KB, int NT>
+template <int D, int KB, int VB, int NT>
 __global__ __launch_bounds__((64 * body_waves<D, NT>())) void prefill_body_kernel(PrefillArgs a) {
-  using Sh = PBody<D, KB, NT, body_waves<D, NT>()>;
+  using Sh = PBody<D, KB, VB, NT, body_waves<D, NT>()>;
   extern __shared__ __align__(16) uint8_t smem[];
   prof_start(a.prof_ts);
   const int item = block_item();
@@ -981,10 +1062,10 @@ hipError_t launch_lds(K kernel, int n_items, int lds, int threads, const Prefill
   return hipGetLastError();
 }
 
-template <int D, int KB, int NT>
+template <int D, int KB, int VB, int NT>
 hipError_t launch_body_t(const PrefillArgs& a, hipStream_t stream) {
-  using Sh = PBody<D, KB, NT, body_waves<D, NT>()>;
-  return launch_lds(prefill_body_kernel<D, KB, NT>, a.n_items, Sh::total, Sh::NTH, a, stream);
+  using Sh = PBody<D, KB, VB, NT, body_waves<D, NT>()>;
+  return launch_lds(prefill_body_kernel<D, KB, VB, NT>, a.n_items, Sh::total, Sh::NTH, a, stream);
 }
 template <int D, int NT>
 hipError_t launch_ring_t(const PrefillArgs& a, hipStream_t stream) {
@@ -997,14 +1078,15 @@ hipError_t launch_ring_t(const PrefillArgs& a, hipStream_t stream) {
 int prefill_lds_bytes(int D, int kb, int nt, bool body) {
 #define KVQ_LDS(DD, NTT)                                                                            \
   if (D == DD && nt == NTT)                                                                         \
-    return body ? (kb == 8 ? PBody<DD, 8, NTT, body_waves<DD, NTT>()>::total                                     \
-                           : PBody<DD, 4, NTT, body_waves<DD, NTT>()>::total)                                    \
+    return body ? (kb == 8 ? PBody<DD, 8, 4, NTT, body_waves<DD, NTT>()>::total                                  \
+                           : PBody<DD, 4, 4, NTT, body_waves<DD, NTT>()>::total)                                 \
                 : PRing<DD, NTT>::total;
   KVQ_LDS(128, 1) KVQ_LDS(128, 2) KVQ_LDS(128, 4)
   KVQ_LDS(256, 1) KVQ_LDS(256, 2) KVQ_LDS(256, 4)
   KVQ_LDS(512, 1)
   if (D == 512 && nt == 2 && body)
-    return kb == 8 ? PBody<512, 8, 2, body_waves<512, 2>()>::total : PBody<512, 4, 2, body_waves<512, 2>()>::total;
+    return kb == 8 ? PBody<512, 8, 4, 2, body_waves<512, 2>()>::total
+                   : PBody<512, 4, 4, 2, body_waves<512, 2>()>::total;
 #undef KVQ_LDS
   return 0;
 }
@@ -1019,20 +1101,23 @@ int prefill_row_tiles(int D, int rows, bool body) {
 // The body launch: PrefillArgs.n_items body items, each (sequence, KV head,
 // body chunk, row block); nt = prefill_row_tiles(D, n_q g, true).
 hipError_t launch_prefill_body(const PrefillArgs& a, int nt, hipStream_t stream) {
-  const int D = a.y.D, kb = a.y.kbits;
-  if (a.y.vbits != 4) return hipErrorInvalidValue;
-#define KVQ_BODY(DD, KBB)                                              \
-  if (D == DD && kb == KBB) {                                          \
-    if (nt == 1) return launch_body_t<DD, KBB, 1>(a, stream);          \
-    if (nt == 2) return launch_body_t<DD, KBB, 2>(a, stream);          \
-    if (nt == 4 && DD != 512) return launch_body_t<DD, KBB, (DD == 512 ? 2 : 4)>(a, stream); \
+  const int D = a.y.D, kb = a.y.kbits, vb = a.y.vbits;
+#define KVQ_BODY(DD, KBB, VBB)                                                         \
+  if (D == DD && kb == KBB && vb == VBB) {                                             \
+    if (nt == 1) return launch_body_t<DD, KBB, VBB, 1>(a, stream);                     \
+    if (nt == 2) return launch_body_t<DD, KBB, VBB, 2>(a, stream);                     \
+    if (nt == 4 && DD != 512) return launch_body_t<DD, KBB, VBB, (DD == 512 ? 2 : 4)>(a, stream); \
   }
-  KVQ_BODY(128, 4)
-  KVQ_BODY(128, 8)
-  KVQ_BODY(256, 4)
-  KVQ_BODY(256, 8)
-  KVQ_BODY(512, 4)
-  KVQ_BODY(512, 8)
+  KVQ_BODY(128, 4, 4)
+  KVQ_BODY(128, 8, 4)
+  KVQ_BODY(256, 4, 4)
+  KVQ_BODY(256, 8, 4)
+  KVQ_BODY(512, 4, 4)
+  KVQ_BODY(512, 8, 4)
+  KVQ_BODY(256, 3, 3)
+  KVQ_BODY(256, 3, 2)
+  KVQ_BODY(256, 2, 2)
+  KVQ_BODY(256, 2, 3)
 #undef KVQ_BODY
   return hipErrorInvalidValue;
 }

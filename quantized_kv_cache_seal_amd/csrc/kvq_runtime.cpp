@@ -606,7 +606,10 @@ static void profile_clear(kvq_cache* c) {
 // device on its own: record chunks to about four workgroups per resident slot,
 // ring chunks (multiples of one 64-token step) to about two, each at most
 // kMaxBlockChunks per sequence.
-static bool prefill_supported(const Layout& y) { return y.vbits == 4 && (y.kbits == 4 || y.kbits == 8); }
+static bool prefill_supported(const Layout& y) {
+  if (y.vbits == 4) return y.kbits == 4 || y.kbits == 8;
+  return y.D == 256;  // the 2- and 3-bit bodies: 256-wide heads (as their matrix-core decode)
+}
 
 struct BlockBudget {
   int nt, n_rb, nt_ring, n_rb_ring, body_chunks, ring_chunks;
@@ -645,7 +648,7 @@ kvq_status kvq_attn_prefill(kvq_cache* c, int32_t layer, const int32_t* seq_ids,
   if (n_q < 1 || n_q > kMaxBlock) return fail(KVQ_ERR_INVALID, "n_q %d outside 1..%d", n_q, kMaxBlock);
   if (n_seqs == 0) return KVQ_OK;
   if (!prefill_supported(c->y))
-    return fail(KVQ_ERR_UNSUPPORTED, "block attention: 4- or 8-bit keys with 4-bit values");
+    return fail(KVQ_ERR_UNSUPPORTED, "block attention over 2- and 3-bit bodies: head_dim 256 only");
   for (int i = 0; i < n_seqs; ++i)
     if (c->tok(seq_ids[i], layer) < n_q)
       return fail(KVQ_ERR_INVALID, "sequence %d holds %lld tokens, fewer than the block's %d", seq_ids[i],

@@ -7,7 +7,8 @@ bytes; each case builds the cache with the seal rule as the workloads do, then
 attends the newest n_q tokens.  Block sizes cover one row, single and several
 16-row tiles with ragged ends, blocks longer than the unsealed tail (rows whose
 own tokens are sealed: the body's causal mask), and blocks that start inside
-the sink.  Criterion per (sequence, query token): max |o_gpu - o_ref| over the
+the sink; every body width (4/4, 8/4, 3/3, 3/2, 2/2, 2/3) and both staging
+formats.  Criterion per (sequence, query token): max |o_gpu - o_ref| over the
 token's heads and channels / rms of the token's reference outputs <= 2e-3."""
 import math
 import sys
@@ -37,6 +38,15 @@ CASES = {
                                          ctx=1900), [1900, 700], 500, "signs", [1, 9, 100]),
     "qwen14b_f16": (configs.QWEN14B1M.scaled(n_layers=1, n_kv_heads=2, n_q_heads=10, tail_min=256, tail_max=512,
                                              ctx=1500, stage="f16"), [1500], 300, "signs", [33]),
+    # lower scalar bodies at the config 2 shape (SJ-KVaRN 2.3: 3/3, 3/2; and 2/2 with f16 staging, 2/3)
+    "qwen27b_33": (configs.QWEN27B.scaled(n_layers=1, tail_min=256, tail_max=512, ctx=2600, k_bits=3, v_bits=3),
+                   [2600, 1300], 300, None, [5, 100, 300]),
+    "qwen27b_32": (configs.QWEN27B.scaled(n_layers=1, tail_min=256, tail_max=512, ctx=2600, k_bits=3, v_bits=2),
+                   [2600], 300, None, [16, 64]),
+    "qwen27b_22": (configs.QWEN27B.scaled(n_layers=1, tail_min=256, tail_max=512, ctx=2600, k_bits=2, v_bits=2,
+                                          stage="f16"), [2600], 300, None, [8, 200]),
+    "qwen27b_23": (configs.QWEN27B.scaled(n_layers=1, tail_min=256, tail_max=512, ctx=1800, k_bits=2, v_bits=3),
+                   [1800], 300, None, [40]),
     # config 5 shape: a ragged batch, one block starting inside the sink
     "batched": (configs.BATCHED.scaled(n_layers=1, tail_min=256, tail_max=512, ctx=3000), [130, 700, 3000], 128,
                 None, [1, 100, 130]),
@@ -131,7 +141,11 @@ def test_block_attention_errors():
     with pytest.raises(kvq.KVQError) as e:
         p.gpu.attn_prefill(0, [0], q[:, :10].contiguous(), workspace=small)
     assert e.value.status == kvq.ERR_CAPACITY
-    lb = Pair(w.scaled(k_bits=3, v_bits=3), [300]).build(300)
+    # the 2- and 3-bit bodies of 128-wide heads (their decode is the vector-ALU scan)
+    w128 = configs.QWEN14B1M.scaled(n_layers=1, n_kv_heads=1, n_q_heads=5, tail_min=256, tail_max=512, k_bits=3,
+                                    v_bits=3)
+    lb = Pair(w128, [300], inputs.rotation_signs(w128.seed)).build(300)
+    q128 = t.from_numpy(inputs.block_queries(w128.seed, 0, 0, 1, 10, 5, 128)).cuda()
     with pytest.raises(kvq.KVQError) as e:
-        lb.gpu.attn_prefill(0, [0], q[:, :10].contiguous())
+        lb.gpu.attn_prefill(0, [0], q128)
     assert e.value.status == kvq.ERR_UNSUPPORTED

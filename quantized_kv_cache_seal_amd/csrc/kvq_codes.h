@@ -44,13 +44,42 @@ __device__ __forceinline__ half8 nib8_centred(uint32_t w) {
   return mfma_a(u) - off;
 }
 
-// Key codes enter the score product centred too (nib8_centred, byte8_centred):
-// q'.k_i = S_i (q~ . (n_i - mid)) + (Z_i + mid S_i) sigma, mid = 2^(b-1).  The
-// zero point Z_i is the row minimum, so uncentred the two terms run to the size
-// of the row's range times |q~| and cancel to the score: with keys near the
-// fp16 maximum (channels at +-60,000) they reach ~1e5 in fp32 for a score of
-// ~1e3, and the matrix cores' fp32 partial sums of q~ . n lose the same bits.
-// Centred, both the products and Z + mid S stay at the size of the score.
+// Key codes enter the score product as exact fp16 subnormals n 2^-24 (one AND
+// per pair, no subtract: nib8_sub, byte8_sub), and the centre leaves the fp32
+// product instead: q'.k_i = S_i 2^24 (q~ . n_i 2^-24 - mid sigma 2^-24) +
+// (Z_i + mid S_i) sigma, mid = 2^(b-1).  The zero point Z_i is the row
+// minimum, so the plain form S_i (q~ . n_i) + Z_i sigma runs both terms to the
+// size of the row's range times |q~|, which then cancel to the score: with keys
+// near the fp16 maximum (channels at +-60,000) they reach ~1e5 in fp32 for a
+// score of ~1e3.  With the centre taken off the dot product before the scale
+// multiplies, both terms stay at the size of the score; the dot product itself
+// runs to at most twice its centred size (codes 0..2^b - 1 against -mid..mid).
+// (Value codes stay centred in the operand: nib8_centred.)
+
+// Eight 4-bit key codes of one dword as fp16 subnormals, in the slot order of
+// nib8_centred: [n0, n4, 16 n1, 16 n5, n2, n6, 16 n3, 16 n7] 2^-24.
+__device__ __forceinline__ half8 nib8_sub(uint32_t w) {
+  const uint32_t w8 = w >> 8;
+  uint4 u;
+  u.x = w & 0x000F000Fu;
+  u.y = w & 0x00F000F0u;
+  u.z = w8 & 0x000F000Fu;
+  u.w = w8 & 0x00F000F0u;
+  return mfma_a(u);
+}
+
+// Eight 8-bit key codes of two dwords as fp16 subnormals n 2^-24 in channel
+// order: one byte permute per pair (selector 4 takes a zero byte).
+__device__ __forceinline__ half8 byte8_sub(uint32_t w0, uint32_t w1) {
+  uint4 u;
+  u.x = __builtin_amdgcn_perm(0u, w0, 0x04010400u);
+  u.y = __builtin_amdgcn_perm(0u, w0, 0x04030402u);
+  u.z = __builtin_amdgcn_perm(0u, w1, 0x04010400u);
+  u.w = __builtin_amdgcn_perm(0u, w1, 0x04030402u);
+  return mfma_a(u);
+}
+constexpr float kSub = 5.9604644775390625e-08f;  // 2^-24: the fp16 subnormal unit
+constexpr float kUnSub = 16777216.0f;            // 2^24
 
 __device__ __forceinline__ uint32_t pick(const uint4& v, int e) {
   return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;

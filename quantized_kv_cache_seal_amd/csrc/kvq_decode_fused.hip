@@ -443,9 +443,9 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         if (Sh::KB == 4)
-          av[i] = nib8_centred(pick(kd[s][i][kk >> 2], kk & 3));
+          av[i] = nib8_sub(pick(kd[s][i][kk >> 2], kk & 3));
         else
-          av[i] = byte8_centred(pick(kd[s][i][kk >> 1], 2 * (kk & 1)), pick(kd[s][i][kk >> 1], 2 * (kk & 1) + 1));
+          av[i] = byte8_sub(pick(kd[s][i][kk >> 1], 2 * (kk & 1)), pick(kd[s][i][kk >> 1], 2 * (kk & 1) + 1));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) sh[s][i] = mfma16(av[i], bh, sh[s][i]);
@@ -465,14 +465,18 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
           for (int j = 0; j < 4; ++j) sh[s][i][j] = add_x8_lo(sh[s][i][j], lane);
     }
     // this lane's rows are positions 16 bb + 4 g + j: tokens base + {0,4,1,5}
-    // (g even) or base + {2,6,3,7} (g odd), base = 16 bb + 8 (g / 2)
+    // (g even) or base + {2,6,3,7} (g odd), base = 16 bb + 8 (g / 2).  The
+    // products hold q~ . n 2^-24 (subnormal key codes); the scores are kept
+    // times 2^-24 up to the exponent's argument: S (dot - mid sigma 2^-24) +
+    // (Z + mid S) sigma 2^-24, the centre taken off before the scale.
     const int tb = 8 * (g >> 1) + 2 * (g & 1);
     float sc[2][4];
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       const uint8_t* km = mr + s * MS;
       const int qr = PK ? q16 & 7 : q16;  // packed: columns c and c + 8 score query row c
-      const float sig = xs[s][0][qr] + xs[s][1][qr] + xs[s][2][qr] + xs[s][3][qr];
+      const float sig = (xs[s][0][qr] + xs[s][1][qr] + xs[s][2][qr] + xs[s][3][qr]) * kSub;
+      const float cm = (float)(1 << (Sh::KB - 1)) * sig;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int T = 16 * (2 * wave + i) + tb;
@@ -483,8 +487,8 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
         const float4v dot = PK ? sh[s][i] : sh[s][i] + sl[s][i] * kLoUnscale;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float zc = fmaf((float)(1 << (Sh::KB - 1)), Sj[j], Zj[j]);  // Z + mid S: exact
-          const float v = fmaf(Sj[j], dot[j], zc * sig);
+          const float zc = fmaf((float)(1 << (Sh::KB - 1)), Sj[j], Zj[j]);  // Z + mid S
+          const float v = fmaf(Sj[j], dot[j] - cm, zc * sig);
           sc[i][j] = s == 0 ? v : sc[i][j] + v;
         }
       }
@@ -503,7 +507,7 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) load_keys<Sh>(more ? rec(r + 1) + s * SB : rec0, kd[s], wave, lane, !more);
 
-    const float mrec = fmaxf(fmaxf(xm[0][q16], xm[1][q16]), fmaxf(xm[2][q16], xm[3][q16]));
+    const float mrec = fmaxf(fmaxf(xm[0][q16], xm[1][q16]), fmaxf(xm[2][q16], xm[3][q16])) * kUnSub;
     const float m_new = fmaxf(m_run, mrec);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first record
     // the record's weights are taken relative to its own maximum, so that the
@@ -525,7 +529,7 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        p[i][j] = __builtin_amdgcn_exp2f(sc[i][j] - mrec);  // argument <= 0
+        p[i][j] = __builtin_amdgcn_exp2f(fmaf(sc[i][j], kUnSub, -mrec));  // argument <= 0 (exact scaling)
         lrec += p[i][j];
       }
     l_part = fmaf(frec, lrec, l_part);

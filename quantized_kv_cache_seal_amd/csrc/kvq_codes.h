@@ -157,6 +157,25 @@ __device__ __forceinline__ half8 codes_lb(uint32_t x) {
   return mfma_a(u) - off;
 }
 
+// The same eight codes as fp16 subnormals c 2^-24, uncentred (keys: the
+// centre leaves the fp32 product, as for nib8_sub).
+template <int B>
+__device__ __forceinline__ half8 codes_lb_sub(uint32_t x) {
+  const uint32_t mm = ((1u << B) - 1) * 0x10001u;
+  const uint32_t u0 = (x & 0xFFFFu) | ((x << (16 - B)) & 0xFFFF0000u);
+  uint4 u;
+  u.x = u0 & mm;
+  u.y = (u0 >> (2 * B)) & mm;
+  u.z = (u0 >> (4 * B)) & mm;
+  if (B == 2) {
+    u.w = (u0 >> (6 * B)) & mm;
+  } else {
+    const uint32_t x3 = x >> 18;
+    u.w = ((x3 & 0xFFFFu) | ((x3 << 13) & 0xFFFF0000u)) & mm;
+  }
+  return mfma_a(u);
+}
+
 // Bits 8 B s .. 8 B s + 8 B - 1 of a lane's dwords d (the codes of its k-step s)
 // in the low bits of the result (higher bits are ignored by codes_lb).
 template <int B>

@@ -810,12 +810,15 @@ __device__ __forceinline__ void body_role_lb(const DecodeArgs& a, int b, int h, 
       const half8 bh = mfma_a(qt[kk][0][lane]), bl = mfma_a(qt[kk][1][lane]);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const half8 av = codes_lb<Sh::KB>(step_bits<Sh::KB>(kd[i], kk));
+        const half8 av = codes_lb_sub<Sh::KB>(step_bits<Sh::KB>(kd[i], kk));
         sh[i] = mfma16(av, bh, sh[i]);
         sl[i] = mfma16(av, bl, sl[i]);
       }
     }
-    const float sig = xs[0][q16] + xs[1][q16] + xs[2][q16] + xs[3][q16];
+    // subnormal key codes: scores times 2^-24 up to the exponent's argument,
+    // S (dot - mid sigma 2^-24) + (Z + mid S) sigma 2^-24 (as in body_role)
+    const float sig = (xs[0][q16] + xs[1][q16] + xs[2][q16] + xs[3][q16]) * kSub;
+    const float cm = kMidK * sig;
     float sc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -825,7 +828,7 @@ __device__ __forceinline__ void body_role_lb(const DecodeArgs& a, int b, int h, 
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float dot = sh[i][j] + sl[i][j] * kLoUnscale;
-        sc[i][j] = fmaf(Sj[j], dot, fmaf(kMidK, Sj[j], Zj[j]) * sig);
+        sc[i][j] = fmaf(Sj[j], dot - cm, fmaf(kMidK, Sj[j], Zj[j]) * sig);
       }
     }
     float mx = -INFINITY;
@@ -838,7 +841,7 @@ __device__ __forceinline__ void body_role_lb(const DecodeArgs& a, int b, int h, 
     __syncthreads();  // (B2) record maxima; q~ of r and the key codes are free
     load_keys_lb<Sh>(more ? rec(r + 1) : rec0, kd, wave, lane, !more);
 
-    const float mrec = fmaxf(fmaxf(xm[0][q16], xm[1][q16]), fmaxf(xm[2][q16], xm[3][q16]));
+    const float mrec = fmaxf(fmaxf(xm[0][q16], xm[1][q16]), fmaxf(xm[2][q16], xm[3][q16])) * kUnSub;
     const float m_new = fmaxf(m_run, mrec);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first record
     const float frec = __builtin_amdgcn_exp2f(mrec - m_new);    // the record's weights are relative to mrec
@@ -857,7 +860,7 @@ __device__ __forceinline__ void body_role_lb(const DecodeArgs& a, int b, int h, 
       float x[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float p = __builtin_amdgcn_exp2f(sc[i][j] - mrec);
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[i][j], kUnSub, -mrec));
         lrec += p;
         zt = fmaf(p, fmaf(kMidV, Sj[j], Zj[j]), zt);
         x[j] = p * Sj[j];

@@ -18,6 +18,7 @@ cpu_baseline entry.  Progress goes to stderr; stdout carries one JSON line.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -92,11 +93,14 @@ def seal_flops_per_tile(passes, rows=128, cols=256):
     return passes * 4 * rows * cols + 6 * rows * cols
 
 
-def run_decode(args, w, torch, kvq, synthetic, inputs):
+kPreWarmMaxSteps = 1000
+
+
+def run_decode(args, w, torch, kvq, synthetic, inputs, read_first=False):
     L, H, D, Hq, N = w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads, w.n_seqs
     W, K = args.warmup, args.steps
     t0 = time.time()
-    cache = synthetic.build(w, ctx=w.ctx, max_ctx=w.ctx + W + K + 1)
+    cache = synthetic.build(w, ctx=w.ctx, max_ctx=w.ctx + W + 3 * K + kPreWarmMaxSteps + 1)
     log(f"[bench] built {w.name} in {time.time() - t0:.1f}s: layer0 info {cache.info(0, 0)}")
     path = {"auto": kvq.PATH_AUTO, "valu": kvq.PATH_VALU, "mfma": kvq.PATH_MFMA}[args.path]
     cache.set_decode_path(path)
@@ -107,10 +111,11 @@ def run_decode(args, w, torch, kvq, synthetic, inputs):
     nk, nv = [], []
     for l in range(L):
         for kind, dst in (("k", nk), ("v", nv)):
-            t = torch.stack([sp.tokens(l, kind, w.ctx, W + K, backend="torch", device=dev) for sp in specs], dim=1)
+            t = torch.stack([sp.tokens(l, kind, w.ctx, W + 3 * K, backend="torch", device=dev) for sp in specs],
+                            dim=1)
             dst.append(t.contiguous())
     qs = [[inputs.queries(w.seed, s, l, N, Hq, D, backend="torch", device=dev).contiguous() for l in range(L)]
-          for s in range(W + K)]
+          for s in range(W + 3 * K)]
     out = torch.empty((L, N, Hq, D), dtype=torch.float32, device=dev)
     ws = cache.workspace(N)
     stream = torch.cuda.current_stream()
@@ -120,6 +125,7 @@ def run_decode(args, w, torch, kvq, synthetic, inputs):
     # that the timed loop makes no extra calls
     state = [[list(cache.info(s, l)) for s in seqs] for l in range(L)]   # [n_tok, n_rec, ring]
     rec_bytes = cache.unit_bytes(kvq.REGION_BODY)
+    read_ceiling = run_read_ceiling(torch, kvq) if read_first else None
 
     def one_step(s):
         nbytes = 0
@@ -140,12 +146,32 @@ def run_decode(args, w, torch, kvq, synthetic, inputs):
             nbytes += sum(region_bytes(w, rec_bytes, *st) for st in state[l])
         return nbytes
 
+    # Pre-warm: the device's power management settles only after some tens of
+    # milliseconds of this load (measured step by step after an idle second:
+    # ~565 us for the first 10 steps, 600-666 us for the next 10, then
+    # 545 -> 537 us), so the same steps run untimed for prewarm_ms first; their
+    # inputs cycle over the generated ones, and the host counts follow them.
+    # Python's cyclic garbage collector stays off while steps run: a full
+    # collection inside the timed loop (tens of ms, triggered by the objects the
+    # calls allocate) would leave the device waiting for work
+    gc.collect()
+    gc.disable()
+    n_pre = 0
+    if args.prewarm_ms > 0:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < args.prewarm_ms and n_pre < kPreWarmMaxSteps:
+            one_step(n_pre % (W + 3 * K))
+            n_pre += 1
+            if n_pre % 8 == 0:  # keep the device fed, the queue short
+                torch.cuda.synchronize()
+    torch.cuda.synchronize()
     for s in range(W):
         one_step(s)
     torch.cuda.synchronize()
+    # the timed steps: nothing but the steps between the two events
     tot_bytes = 0
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    cache.profile_start(K * L)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
@@ -154,24 +180,44 @@ def run_decode(args, w, torch, kvq, synthetic, inputs):
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    kernel_us = cache.profile_stop()
     ms_step = start.elapsed_time(end) / K
     bytes_step = tot_bytes / K
     gbs = bytes_step / (ms_step * 1e-3) / 1e9
-    per_call_bytes = bytes_step / L
+    # the main kernel's own duration: a second pass of K steps with the
+    # library's wall-clock stamps on (two atomics per workgroup, so kept out of
+    # the timed steps)
+    cache.profile_start(K * L)
+    stamp_bytes = 0
+    for s in range(K):
+        stamp_bytes += one_step(W + K + s)
+    kernel_us = cache.profile_stop()
+    per_call_bytes = stamp_bytes / (K * L)
     avg_kernel_us = sum(kernel_us) / len(kernel_us)
     achieved = per_call_bytes / (avg_kernel_us * 1e-6) / 1e9
+    # the spread of single steps: a third pass of K steps, one event recorded
+    # on the stream between consecutive steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for s in range(K):
+        one_step(W + 2 * K + s)
+        evs[s + 1].record(stream)
+    torch.cuda.synchronize()
+    gc.enable()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(K))
+    step_us = {f"p{q}": round(per[min(K - 1, int(round(q / 100 * (K - 1))))], 1) for q in (10, 50, 90)}
     for l in (0, L - 1):
         assert [list(cache.info(q, l)) for q in seqs] == state[l]
     log(f"[bench] decode: {ms_step * 1e3:.1f} us/step (wall {wall / K * 1e3:.1f} ms), {bytes_step / 1e9:.4f} GB/step, "
         f"{gbs:.1f} GB/s; main decode kernel avg {avg_kernel_us:.1f} us over {len(kernel_us)} calls -> "
-        f"{achieved:.1f} GB/s")
+        f"{achieved:.1f} GB/s; single steps p10/p50/p90 {step_us['p10']}/{step_us['p50']}/{step_us['p90']} us")
     info = cache.info(0, 0)
     sr = run_save_restore(cache, torch, kvq, qs[0][0], ws, stream) if args.save_restore else None
     del cache
     torch.cuda.empty_cache()
     return {
-        "ms_per_step": ms_step, "gbs": gbs, "bytes_step": bytes_step, "avg_kernel_us": avg_kernel_us,
+        "ms_per_step": ms_step, "gbs": gbs, "bytes_step": bytes_step, "avg_kernel_us": avg_kernel_us, "step_us": step_us,
+        "read_ceiling": read_ceiling, "prewarm_steps": n_pre,
         "achieved": achieved, "per_call_bytes": per_call_bytes, "info_after": info, "save_restore": sr,
     }
 
@@ -202,18 +248,23 @@ def run_prefill(args, w, torch, kvq, synthetic, inputs, blocks):
                 cache.attn_prefill(l, seqs, qs[l], out=o, workspace=ws, stream=stream)
 
         W, K = max(1, args.warmup // 5), args.prefill_steps
+        gc.collect()
+        gc.disable()  # as in the decode timing
         for _ in range(W):
             step()
         torch.cuda.synchronize()
-        cache.profile_start(K * L)
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record(stream)
         for _ in range(K):
             step()
         end.record(stream)
         torch.cuda.synchronize()
-        body_us = cache.profile_stop()
         ms_step = start.elapsed_time(end) / K
+        cache.profile_start(K * L)  # the record launch's own duration, in a pass of its own
+        for _ in range(K):
+            step()
+        body_us = cache.profile_stop()
+        gc.enable()
         rows = N * n_q * Hq
         flops_body = 4.0 * D * rows * kvq_group_tokens(n_rec)
         flops_all = sum(4.0 * D * N * Hq * (n_tok - n_q + t + 1) for t in range(n_q)) * L
@@ -246,6 +297,36 @@ def run_prefill(args, w, torch, kvq, synthetic, inputs, blocks):
 
 def kvq_group_tokens(n_rec):
     return 128 * n_rec
+
+
+def run_read_ceiling(torch, kvq, gib=4, reps=10, warm_ms=100.0):
+    """The device's achievable HBM read rate: kvq_read_probe over a buffer of
+    `gib` GiB (16 times the 256 MB Infinity Cache), timed with one event pair
+    around `reps` reads after untimed ones that keep the device reading for
+    `warm_ms` (its clocks reach their sustained level only after some tens of
+    milliseconds of load)."""
+    n = gib << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    out = torch.empty(kvq.READ_PROBE_OUT_BYTES, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < warm_ms:
+        kvq.read_probe(src, out, stream)
+        torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        kvq.read_probe(src, out, stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    gbs = n * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    log(f"[bench] read ceiling: {gbs:.1f} GB/s ({reps} reads of {gib} GiB)")
+    del src, out
+    torch.cuda.empty_cache()
+    return gbs
 
 
 def run_save_restore(cache, torch, kvq, q, ws, stream):
@@ -560,6 +641,11 @@ def main():
                     help="run the block-attention leg alone (for profiling) and print its numbers")
     ap.add_argument("--no-widths", action="store_true",
                     help="skip the lower body widths (3/3, 3/2, 2/2) at the headline shape")
+    ap.add_argument("--prewarm-ms", type=float, default=150.0,
+                    help="untimed decode steps for this long before the warm-up steps (the device's power "
+                         "management settles after some tens of milliseconds of load); 0 turns it off")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the achievable-HBM-read measurement (kvq_read_probe over 4 GiB)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer 20 times (calibrates HBM byte counters) and exit")
     args = ap.parse_args()
@@ -589,7 +675,8 @@ def main():
         print(json.dumps({"workload": w.name, "block_attention":
                           run_prefill(args, w, torch, kvq, synthetic, inputs, (512, 8))}), flush=True)
         return
-    dec = run_decode(args, w, torch, kvq, synthetic, inputs)
+    dec = run_decode(args, w, torch, kvq, synthetic, inputs, read_first=not args.no_read_ceiling)
+    read_ceiling = dec["read_ceiling"]
     seal = None if args.no_seal else run_seal(args, w, torch, kvq, synthetic)
     tbq = None if args.no_tbq4 else run_tbq4(args, w, torch, kvq, inputs, dec["avg_kernel_us"])
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(w, args.cpu_budget)
@@ -627,6 +714,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(dec["ms_per_step"], 4),
+        "step_us": dec["step_us"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -647,15 +735,22 @@ def main():
                        "decode_valu_kernel (body scan of one layer; sink and ring in decode_ring_kernel)"),
             "bytes_per_launch": int(dec["per_call_bytes"]), "avg_launch_us": round(dec["avg_kernel_us"], 2),
             "time_basis": "device wall clock from the start of workgroup 0 to the end of the last workgroup "
-                          "(library stamps, every timed launch)",
+                          "(library stamps, every launch of a second pass of the same number of steps)",
             "traffic_over_algorithmic": None if traffic is None else round(traffic / dec["per_call_bytes"], 4),
             # the same kernel's average duration under rocprofv3 --kernel-trace (committed profile of the
             # current source): it also counts the dispatch ramp before workgroup 0 starts
             "avg_launch_us_rocprof": None if durs is None else float(durs["avg_us"]),
             "frac_rocprof": None if durs is None else
             round(dec["per_call_bytes"] / (float(durs["avg_us"]) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            # context, not the peak: what a plain streaming read achieves on this device (kvq_read_probe)
+            "read_ceiling_gbs": None if read_ceiling is None else round(read_ceiling, 1),
+            "frac_of_read_ceiling": None if read_ceiling is None else round(dec["achieved"] / read_ceiling, 4),
         },
         "cpu_baseline": cpu,
+        "prewarm": {"ms": args.prewarm_ms, "steps": dec["prewarm_steps"],
+                    "why": "untimed decode steps before the warm-up steps: the device's power management settles "
+                           "only after some tens of milliseconds of this load (steps 11-20 after an idle second "
+                           "run ~15 % slower than the steady state)"},
     }
     if dec["save_restore"]:
         res["save_restore"] = dec["save_restore"]

@@ -305,6 +305,19 @@ kvq_status kvq_unit_bytes(const kvq_cache* cache, int32_t region, size_t* bytes)
 kvq_status kvq_profile_start(kvq_cache* cache, int32_t max_calls);
 kvq_status kvq_profile_stop(kvq_cache* cache, float* us, int32_t* n_calls);
 
+/* Measurement utility, not part of the method: one streaming read of `bytes`
+ * bytes of the device buffer src (16-byte aligned, bytes a positive multiple
+ * of 16) by coalesced 16-byte loads from every compute unit, enqueued on
+ * stream (non-temporal loads, eight in flight per thread, 16,384 workgroups).
+ * Timed over a buffer much larger than the 256 MB Infinity Cache it
+ * gives the device's achievable HBM read rate, the ceiling next to which the
+ * decode's bytes per second can be read.  out: device, at least
+ * KVQ_READ_PROBE_OUT_BYTES bytes; receives one XOR checksum word per wave (it
+ * keeps the loads live; the XOR of all its words is the XOR of the buffer's
+ * 32-bit words).  Errors: KVQ_ERR_INVALID, KVQ_ERR_DEVICE. */
+#define KVQ_READ_PROBE_OUT_BYTES ((size_t)262144)
+kvq_status kvq_read_probe(const void* src, size_t bytes, void* out, void* stream);
+
 /* TBQ4 comparator format (KV cache math: "rotate first", the fused
  * rotated-domain decode, and the format table).  A block holds 128 values:
  * y = R x with R the randomized Walsh-Hadamard transform (flip signs s1,

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libkvq.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["kvq_runtime.cpp", "kvq_append.hip", "kvq_seal.hip", "kvq_decode.hip", "kvq_decode_fused.hip", "kvq_prefill.hip", "kvq_tbq4.hip"]
+SOURCES = ["kvq_runtime.cpp", "kvq_append.hip", "kvq_seal.hip", "kvq_decode.hip", "kvq_decode_fused.hip", "kvq_prefill.hip", "kvq_tbq4.hip", "kvq_probe.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -284,7 +284,7 @@ __device__ __forceinline__ void load_keys(const uint8_t* __restrict__ sub, uint4
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int s = 0; s < Sh::NKS; ++s)
-      kd[i][s] = *(const uint4*)(sub + (dummy ? 0 : (16 * (2 * wave + i) + row) * Sh::ROWB + 64 * s + 16 * g));
+      kd[i][s] = ld_stream16(sub + (dummy ? 0 : (16 * (2 * wave + i) + row) * Sh::ROWB + 64 * s + 16 * g));
 }
 template <class Sh>
 __device__ __forceinline__ void load_values(const uint8_t* __restrict__ sub, uint4 (&vd)[Sh::VT], int wave, int lane,
@@ -292,7 +292,7 @@ __device__ __forceinline__ void load_values(const uint8_t* __restrict__ sub, uin
   const int m = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int j = 0; j < Sh::VT; ++j)
-    vd[j] = *(const uint4*)(sub + (dummy ? 0 : Sh::KCODE + (16 * (Sh::VT * wave + j) + m) * 64 + 16 * g));
+    vd[j] = ld_stream16(sub + (dummy ? 0 : Sh::KCODE + (16 * (Sh::VT * wave + j) + m) * 64 + 16 * g));
 }
 
 template <class Sh, bool PK>
@@ -349,8 +349,8 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
   uint2 m0[NSUB], m1[NSUB];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
-    m0[s] = *(const uint2*)(rec(r0) + s * SB + mo);
-    m1[s] = *(const uint2*)(r0 + 1 < r1 ? rec(r0 + 1) + s * SB + mo : rec0);
+    m0[s] = ld_stream8(rec(r0) + s * SB + mo);
+    m1[s] = ld_stream8(r0 + 1 < r1 ? rec(r0 + 1) + s * SB + mo : rec0);
   }
   uint4 kd[NSUB][2][Sh::NKS], vd[NSUB][VT];
 #pragma unroll
@@ -401,7 +401,7 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
   for (int s = 0; s < NSUB; ++s) load_values<Sh>(rec(r0) + s * SB, vd[s], wave, lane);
   uint2 mnext[NSUB];
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) mnext[s] = *(const uint2*)(r0 + 2 < r1 ? rec(r0 + 2) + s * SB + mo : rec0);
+  for (int s = 0; s < NSUB; ++s) mnext[s] = ld_stream8(r0 + 2 < r1 ? rec(r0 + 2) + s * SB + mo : rec0);
   __syncthreads();
 
   float m_run = -INFINITY, l_part = 0.0f;
@@ -573,7 +573,7 @@ __device__ __forceinline__ void body_role(const DecodeArgs& a, int b, int h, int
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       if (r + 2 < r1) stage_scales<Sh>(mslot(r + 2) + s * MS, mnext[s], tid);
-      mnext[s] = *(const uint2*)(r + 3 < r1 ? rec(r + 3) + s * SB + mo : rec0);
+      mnext[s] = ld_stream8(r + 3 < r1 ? rec(r + 3) + s * SB + mo : rec0);
     }
     __syncthreads();  // (B3) weights, zero-point sums; q~ and scales of r + 1, r + 2
 
@@ -678,7 +678,7 @@ __device__ __forceinline__ void load_keys_lb(const uint8_t* __restrict__ rec, ui
     const uint8_t* p = rec + (dummy ? 0 : (16 * (2 * wave + i) + m) * Sh::KROW + 8 * Sh::KB * g);
 #pragma unroll
     for (int j = 0; j < Sh::KW / 2; ++j) {
-      const uint2 v = *(const uint2*)(p + 8 * j);
+      const uint2 v = ld_stream8(p + 8 * j);
       kd[i][2 * j] = v.x;
       kd[i][2 * j + 1] = v.y;
     }
@@ -736,8 +736,8 @@ __device__ __forceinline__ void body_role_lb(const DecodeArgs& a, int b, int h, 
   // ---- prologue: query, scales of r0 and r0 + 1, codes of r0
   QueryRaw<D> qraw;
   query_load<D>(a, b, h, wave, lane, qraw);
-  const uint2 m0 = *(const uint2*)(rec(r0) + mo);
-  const uint2 m1 = *(const uint2*)(r0 + 1 < r1 ? rec(r0 + 1) + mo : rec0);
+  const uint2 m0 = ld_stream8(rec(r0) + mo);
+  const uint2 m1 = ld_stream8(r0 + 1 < r1 ? rec(r0 + 1) + mo : rec0);
   uint32_t kd[2][Sh::KW], vd[VT][Sh::VW];
   load_keys_lb<Sh>(rec(r0), kd, wave, lane, false);
   float* rows = (float*)qt;
@@ -790,7 +790,7 @@ __device__ __forceinline__ void body_role_lb(const DecodeArgs& a, int b, int h, 
   };
   make_qt(mslot(r0));
   load_values_lb<Sh>(rec(r0), vd, wave, lane, false);
-  uint2 mnext = *(const uint2*)(r0 + 2 < r1 ? rec(r0 + 2) + mo : rec0);
+  uint2 mnext = ld_stream8(r0 + 2 < r1 ? rec(r0 + 2) + mo : rec0);
   __syncthreads();
 
   float m_run = -INFINITY, l_part = 0.0f;
@@ -876,7 +876,7 @@ __device__ __forceinline__ void body_role_lb(const DecodeArgs& a, int b, int h, 
     if (g == 0) xz[wave][q16] = zt;
     if (more) make_qt(mslot(r + 1));
     if (r + 2 < r1) stage_scales<Sh>(mslot(r + 2), mnext, tid);
-    mnext = *(const uint2*)(r + 3 < r1 ? rec(r + 3) + mo : rec0);
+    mnext = ld_stream8(r + 3 < r1 ? rec(r + 3) + mo : rec0);
     __syncthreads();  // (B3) weights, zero-point sums; q~ and scales of r + 1, r + 2
 
     // ---- values: channel tiles VT wave + j over the record's 128 tokens

@@ -30,6 +30,7 @@ constexpr int kMaxChunks = 4096;  // split-K partials per (sequence, query head)
 // allocation-free decode (8 MiB: the matrix-core plans of the benchmarked
 // workloads need at most ~4.2 MB).
 constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+constexpr int kReadProbeBlocks = 16384;  // workgroups of the read probe (4 waves, one output word each)
 // A split-K partial row: [m, l, 0, 0, acc[D]] fp32, acc 16-byte aligned and in
 // the original domain (the producer rotates its rotated-domain sums back).
 constexpr int kPartHead = 4;

@@ -18,6 +18,7 @@
 
 namespace kvq {
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_read_probe(const void* src, int64_t bytes, void* out, hipStream_t stream);
 hipError_t launch_seal(const SealArgs& a, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs& a, int grid_x, hipStream_t stream);
 hipError_t launch_decode_main(const DecodeArgs& a, int n_items, hipStream_t stream);
@@ -36,6 +37,7 @@ hipError_t launch_tq_codec(const Tbq4CodecArgs& a, int bits, bool encode, hipStr
 
 using namespace kvq;
 static_assert(kNoAllocScratchBytes == KVQ_NOALLOC_SCRATCH_BYTES, "scratch size as the header states it");
+static_assert((size_t)kReadProbeBlocks * 4 * 4 == KVQ_READ_PROBE_OUT_BYTES, "read probe output as the header states it");
 
 struct kvq_cache {
   kvq_config cfg;
@@ -218,6 +220,13 @@ static void fill_signs(const kvq_config& c, uint32_t* out) {
 }
 
 extern "C" {
+
+kvq_status kvq_read_probe(const void* src, size_t bytes, void* out, void* stream) {
+  if (!src || !out || bytes == 0 || bytes % 16 != 0 || (uintptr_t)src % 16 != 0)
+    return fail(KVQ_ERR_INVALID, "read probe: src and out non-NULL, src 16-byte aligned, bytes a positive multiple of 16");
+  const hipError_t e = launch_read_probe(src, (int64_t)bytes, out, (hipStream_t)stream);
+  return e == hipSuccess ? KVQ_OK : hip_fail(e, "read probe launch");
+}
 
 const char* kvq_status_string(kvq_status st) {
   switch (st) {

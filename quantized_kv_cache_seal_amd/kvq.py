@@ -28,7 +28,7 @@ EXPORTS = [
     "kvq_seq_truncate", "kvq_seq_save_bytes", "kvq_seq_save", "kvq_seq_restore", "kvq_export", "kvq_import",
     "kvq_unit_bytes", "kvq_profile_start", "kvq_profile_stop",
     "kvq_tbq4_tables", "kvq_tbq4_encode", "kvq_tbq4_decode", "kvq_tbq4_workspace_bytes", "kvq_tbq4_attn_decode",
-    "kvq_tq_encode", "kvq_tq_decode",
+    "kvq_tq_encode", "kvq_tq_decode", "kvq_read_probe",
     "kvq_status_string", "kvq_last_error",
 ]
 
@@ -92,6 +92,7 @@ def lib():
             "kvq_tbq4_workspace_bytes": [i32, i32, i32, i32, i64, P(sz)],
             "kvq_tq_encode": [vp, i64, i32, P(ctypes.c_uint64), vp, vp],
             "kvq_tq_decode": [vp, i64, i32, P(ctypes.c_uint64), vp, vp],
+            "kvq_read_probe": [vp, sz, vp, vp],
             "kvq_tbq4_attn_decode": [vp, vp, vp, i32, i32, i32, i32, i64, P(i64), P(ctypes.c_uint64),
                                      ctypes.c_float, vp, i32, vp, sz, vp],
         }
@@ -444,4 +445,20 @@ def tq_decode(blocks, bits, sign_words, out=None, stream=None):
         out = torch.empty((n, 128), dtype=torch.float32, device=blocks.device)
     assert out.dtype == torch.float32 and out.is_contiguous() and out.numel() >= n * 128
     check(lib().kvq_tq_decode(_ptr(blocks), n, bits, _words(sign_words), _ptr(out), _stream(stream)))
+    return out
+
+
+READ_PROBE_OUT_BYTES = 262144
+
+
+def read_probe(src, out=None, stream=None):
+    """One streaming read of the device tensor src (contiguous, 16-byte
+    aligned, a multiple of 16 bytes) by kvq_read_probe; out: uint8 device
+    tensor of READ_PROBE_OUT_BYTES receiving the per-wave XOR words."""
+    import torch
+    assert src.is_cuda and src.is_contiguous()
+    if out is None:
+        out = torch.empty(READ_PROBE_OUT_BYTES, dtype=torch.uint8, device=src.device)
+    assert out.dtype == torch.uint8 and out.numel() >= READ_PROBE_OUT_BYTES
+    check(lib().kvq_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(out), _stream(stream)))
     return out

@@ -200,6 +200,18 @@ def test_tbq4_argument_errors():
         prev = sz.value
 
 
+def test_read_probe_argument_errors():
+    """The read probe rejects what it cannot read before launching anything."""
+    L = kvq.lib()
+    p = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails its checks
+    assert L.kvq_read_probe(None, 1024, p, None) == kvq.ERR_INVALID
+    assert L.kvq_read_probe(p, 1024, None, None) == kvq.ERR_INVALID
+    assert L.kvq_read_probe(p, 0, p, None) == kvq.ERR_INVALID
+    assert L.kvq_read_probe(p, 1000, p, None) == kvq.ERR_INVALID
+    assert L.kvq_read_probe(ctypes.c_void_p((1 << 20) + 8), 1024, p, None) == kvq.ERR_INVALID
+    assert kvq.READ_PROBE_OUT_BYTES == 262144
+
+
 def test_prefill_workspace_bound():
     """Host-only: the block-attention workspace holds n_seqs x n_q x H_q partial
     rows for the sink plus at most 64 ring and 64 record chunks each, and fewer

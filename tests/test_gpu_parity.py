@@ -476,3 +476,16 @@ def test_degenerate_inputs():
             err = float(np.max(np.abs(got[s] - ref)) / np.sqrt(np.mean(ref ** 2)))
             _say(f"[degenerate] path={path} seq {s} err={err:.2e}")
             assert err <= ATTN_TOL, (path, s, err)
+
+def test_read_probe_checksum():
+    """The read probe (the bench's HBM read ceiling) reads every 16 bytes of
+    its buffer once: the XOR of its output words equals the XOR of the
+    buffer's 32-bit words.  Nine and a half grid strides of 64 MiB (past the
+    eight loads a thread has in flight) and a ragged tail."""
+    import torch
+    n = 9 * (64 << 20) + (32 << 20) + 4096 + 16
+    host = np.random.default_rng(5).integers(0, 2 ** 32, size=n // 4, dtype=np.uint32)
+    src = torch.from_numpy(host.view(np.uint8)).cuda()
+    out = kvq.read_probe(src)
+    torch.cuda.synchronize()
+    assert np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32)) == np.bitwise_xor.reduce(host)

@@ -207,6 +207,11 @@ struct PBody {
   static constexpr int L_KS = 2 * SUBW, L_KZ = L_KS + 512, L_VC = L_KZ + 512, L_VS = L_VC + 4 * SUBW;
   static constexpr int L_VZ = L_VS + 512, MSTRIDE = 4096;
   static constexpr int UNITS = NSUB * KK * NT / NW;  // q~ operand units per thread
+  // OWN: every unit of a thread is in row tile wave mod NT (NT divides NW), so
+  // a row tile's sigma parts come from its NW / NT owning waves; otherwise
+  // (three row tiles over eight waves) unit idx is in row tile idx mod NT and
+  // every wave writes a part (zero where it has no unit) for every row tile
+  static constexpr bool OWN = NW % NT == 0;
   // LDS: q~ [NSUB][KK][NT][hi, lo][64] uint4; weights [NSUB][hi, lo][RB][kPPitch]
   // halves; scales [3][NSUB][MSTRIDE]; per-row exchange of the waves' parts
   // (a row's NW parts contiguous, read as 16-byte vectors): xm[RB][NW],
@@ -216,7 +221,7 @@ struct PBody {
   static constexpr int MB = PW + NSUB * 2 * RB * kPPitch * 2;
   static constexpr int X = MB + 3 * NSUB * MSTRIDE;
   static constexpr int total = X + (1 + 2 * NSUB) * NW * RB * 4;
-  static_assert((NT == 1 || NT == 2 || NT == 4) && NW % NT == 0, "a thread's q~ units share one row tile");
+  static_assert(NT >= 1 && NT <= 4 && (OWN || NW == 8), "row tiles per block");
   static_assert(UNITS >= 1 && UNITS * NW == NSUB * KK * NT, "q~ units divide over the workgroup");
   static_assert(TPW * NW == 8 && VT * NW * 16 == SUBW, "tiles divide over the waves");
   static_assert(RB * D * 4 <= PW - QT, "query rows (and the partial rows) fit the q~ area");
@@ -308,13 +313,16 @@ __device__ __forceinline__ void pb_make_qtilde(const uint8_t* km, const uint4 (&
   const int n = lane & 15, g = lane >> 4;
   const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
   const half2v lo_ones = {(_Float16)kLoUnscale, (_Float16)kLoUnscale};
-  float sig[NSUB];
+  constexpr int NTS = Sh::OWN ? 1 : NT;  // sigma parts per sub-record this thread keeps
+  float sig[NSUB][NTS];
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) sig[s] = 0.0f;
-  const int t = wave % NT;
+  for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+    for (int t = 0; t < NTS; ++t) sig[s][t] = 0.0f;
 #pragma unroll
   for (int u = 0; u < Sh::UNITS; ++u) {
     const int idx = wave + NW * u, kk = (idx / NT) % KK, s = idx / (NT * KK);
+    const int t = Sh::OWN ? wave % NT : idx % NT;
     const uint4 c = *(const uint4*)(km + s * Sh::MSTRIDE + 2 * (Sh::CPL * g + 8 * kk));
     uint32_t cp[4];
     if constexpr (Sh::KB == 4) {  // slot pairs (c0, c4), (c1, c5), (c2, c6), (c3, c7)
@@ -342,16 +350,19 @@ __device__ __forceinline__ void pb_make_qtilde(const uint8_t* km, const uint4 (&
     a1 = __builtin_amdgcn_fdot2(as_h2(lo.z), lo_ones, a1, false);
     a16 = __builtin_amdgcn_fdot2(as_h2(hi.w), ones, a16, false);
     a16 = __builtin_amdgcn_fdot2(as_h2(lo.w), lo_ones, a16, false);
-    sig[s] += Sh::KB == 4 ? fmaf(16.0f, a16, a1) : a1 + a16;
+    sig[s][Sh::OWN ? 0 : t] += Sh::KB == 4 ? fmaf(16.0f, a16, a1) : a1 + a16;
     uint4* dst = qt + (((s * KK + kk) * NT + t) * 2) * 64 + lane;
     dst[0] = hi;
     dst[64] = lo;
   }
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    const float v = xsum4(sig[s]);
-    if (g == 0) xs[(s * RB + 16 * t + n) * NW + wave] = v;
-  }
+  for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+    for (int tt = 0; tt < NTS; ++tt) {
+      const int t = Sh::OWN ? wave % NT : tt;
+      const float v = xsum4(sig[s][tt]);
+      if (g == 0) xs[(s * RB + 16 * t + n) * NW + wave] = v;
+    }
 }
 
 template <class Sh>
@@ -430,10 +441,10 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
   __syncthreads();
   uint4 qh[U], ql[U];
   {
-    const int t = wave % NT;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int idx = wave + NW * u, kk = (idx / NT) % KK, s = idx / (NT * KK);
+      const int t = Sh::OWN ? wave % NT : idx % NT;
       const float* rp = rows + (16 * t + n) * D + SUBW * s + Sh::CPL * g + 8 * kk;
       uint32_t hb[4], lb[4];
 #pragma unroll
@@ -549,11 +560,16 @@ __device__ __forceinline__ void body_block(const PrefillArgs& a, int b, int h, i
       }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        // sigma of row tile t: the parts of the waves w = t mod NT, which own its units
+        // sigma of row tile t: the parts of the waves w = t mod NT, which own its
+        // units (OWN), or of every wave
         const float* xr = xs + (s * RB + 16 * t + n) * NW;
         float sig = 0.0f;
+        if constexpr (Sh::OWN) {
 #pragma unroll
-        for (int w = t; w < NW; w += NT) sig += xr[w];
+          for (int w = t; w < NW; w += NT) sig += xr[w];
+        } else {
+          sig = sum_nw(xr);
+        }
 #pragma unroll
         for (int i = 0; i < TPW; ++i)
 #pragma unroll
@@ -1083,6 +1099,8 @@ int prefill_lds_bytes(int D, int kb, int nt, bool body) {
                 : PRing<DD, NTT>::total;
   KVQ_LDS(128, 1) KVQ_LDS(128, 2) KVQ_LDS(128, 4)
   KVQ_LDS(256, 1) KVQ_LDS(256, 2) KVQ_LDS(256, 4)
+  if (D == 256 && nt == 3 && body)
+    return kb == 8 ? PBody<256, 8, 4, 3, body_waves<256, 3>()>::total : PBody<256, 4, 4, 3, body_waves<256, 3>()>::total;
   KVQ_LDS(512, 1)
   if (D == 512 && nt == 2 && body)
     return kb == 8 ? PBody<512, 8, 4, 2, body_waves<512, 2>()>::total
@@ -1091,11 +1109,17 @@ int prefill_lds_bytes(int D, int kb, int nt, bool body) {
   return 0;
 }
 
-// Row tiles of 16 query rows per work item for n_q g rows: body (records)
-// and sink/ring work items (512-wide heads: at most 2 and 1, for LDS).
+// Row tiles of 16 query rows per work item for n_q g rows.  Record items:
+// 1, 2, 3 (256-wide heads: the three tiles of a 48-row verify block, where
+// four would leave a quarter of the block empty) or 4 (512-wide heads: at
+// most 2, for LDS).  Sink/ring items: one tile for blocks of up to 64 rows
+// (their 16-row items fit two workgroups per compute unit and the launch has
+// more of them: an 8-token block at g = 6 took 11 % less time per step than
+// with 64-row items), else as the records (512-wide heads: 1).
 int prefill_row_tiles(int D, int rows, bool body) {
-  const int nt = rows <= 16 ? 1 : rows <= 32 ? 2 : 4;
-  return D == 512 ? (body ? (nt > 2 ? 2 : nt) : 1) : nt;
+  if (!body) return D == 512 || rows <= 64 ? 1 : 4;
+  const int nt = rows <= 16 ? 1 : rows <= 32 ? 2 : rows <= 48 && D == 256 ? 3 : 4;
+  return D == 512 ? (nt > 2 ? 2 : nt) : nt;
 }
 
 // The body launch: PrefillArgs.n_items body items, each (sequence, KV head,
@@ -1119,6 +1143,15 @@ hipError_t launch_prefill_body(const PrefillArgs& a, int nt, hipStream_t stream)
   KVQ_BODY(256, 2, 2)
   KVQ_BODY(256, 2, 3)
 #undef KVQ_BODY
+  // three row tiles: 256-wide heads only (eight waves, three q~ units each)
+  if (nt == 3 && D == 256) {
+    if (kb == 4 && vb == 4) return launch_body_t<256, 4, 4, 3>(a, stream);
+    if (kb == 8 && vb == 4) return launch_body_t<256, 8, 4, 3>(a, stream);
+    if (kb == 3 && vb == 3) return launch_body_t<256, 3, 3, 3>(a, stream);
+    if (kb == 3 && vb == 2) return launch_body_t<256, 3, 2, 3>(a, stream);
+    if (kb == 2 && vb == 2) return launch_body_t<256, 2, 2, 3>(a, stream);
+    if (kb == 2 && vb == 3) return launch_body_t<256, 2, 3, 3>(a, stream);
+  }
   return hipErrorInvalidValue;
 }
 

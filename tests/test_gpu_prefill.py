@@ -7,7 +7,7 @@ bytes; each case builds the cache with the seal rule as the workloads do, then
 attends the newest n_q tokens.  Block sizes cover one row, single and several
 16-row tiles with ragged ends, blocks longer than the unsealed tail (rows whose
 own tokens are sealed: the body's causal mask), and blocks that start inside
-the sink; every body width (4/4, 8/4, 3/3, 3/2, 2/2, 2/3) and both staging
+the sink; 48-row blocks (three row tiles per record item); every body width (4/4, 8/4, 3/3, 3/2, 2/2, 2/3) and both staging
 formats.  Criterion per (sequence, query token): max |o_gpu - o_ref| over the
 token's heads and channels / rms of the token's reference outputs <= 2e-3."""
 import math
@@ -24,12 +24,15 @@ pytestmark = pytest.mark.gpu
 
 CASES = {
     # config 1 (256-wide, GQA 4, 4/4): verify-sized blocks, a long chunk, one reaching 44 tokens into the body
-    "tiny": (configs.TINY, [2048], 512, None, [1, 7, 64, 300]),
+    "tiny": (configs.TINY, [2048], 512, None, [1, 7, 12, 64, 300]),
     # f16 staging ring (exact tail in the original domain)
     "tiny_f16": (configs.TINY_F16, [2048], 512, None, [5, 130, 400]),
     # config 2 shape (4 KV heads x 256, GQA 6), two sequences of different lengths
     "qwen27b": (configs.QWEN27B.scaled(n_layers=1, tail_min=256, tail_max=512, ctx=2600), [2600, 1300], 300,
-                None, [3, 16, 100]),
+                None, [3, 8, 16, 100]),
+    # 8-bit keys at 256-wide heads: a 48-row verify block (three row tiles) and a longer one
+    "qwen27b_k8": (configs.QWEN27B.scaled(n_layers=1, tail_min=256, tail_max=512, ctx=1800, k_bits=8), [1800], 300,
+                   None, [8, 40]),
     # config 3 shape: 512-wide heads as two 256-point halves, GQA 8
     "gemma": (configs.GEMMA31B.scaled(n_layers=1, tail_min=256, tail_max=512, ctx=1500), [1500], 256, None,
               [2, 40, 300]),

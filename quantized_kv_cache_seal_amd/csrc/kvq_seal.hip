@@ -131,19 +131,42 @@ __device__ __forceinline__ half8 sq8(half8 v) {
   return mfma_a(o);
 }
 
-// fp32 of element e of a packed operand, written out so that the second
-// rounding sweep over the tile recomputes y instead of keeping the first
-// sweep's 64 values per row alive
-__device__ __forceinline__ float cvt_e(const half8& v, int e) {
+// fp32(d * x) for element e of a packed fp16 operand in one instruction:
+// v_fma_mix_f32 reads x as fp16 and adds nz = -0, the identity of every
+// product (signed zeros included), so the result is the product rounded once
+// to fp32, as a v_mul_f32 after the conversion would give.  Written out (the
+// compiler folds a -0 addend into a plain multiply) and volatile, so that the
+// second rounding sweep over the tile recomputes y instead of keeping the
+// first sweep's 64 values per row alive.
+__device__ __forceinline__ float mul_e(float d, const half8& v, int e, float nz) {
   uint4 u;
   __builtin_memcpy(&u, &v, 16);
   const uint32_t wd = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
-  float d;
+  float r;
   if (e & 1)
-    asm volatile("v_cvt_f32_f16_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1" : "=v"(d) : "v"(wd));
+    asm volatile("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(d), "v"(wd), "v"(nz));
   else
-    asm volatile("v_cvt_f32_f16 %0, %1" : "=v"(d) : "v"(wd));
-  return d;
+    asm volatile("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(d), "v"(wd), "v"(nz));
+  return r;
+}
+// the same product, not volatile: the compiler may share it and move loads
+// across it (the value codes' sweep, whose per-row operands come from LDS)
+__device__ __forceinline__ float mul_e_pure(float d, const half8& v, int e, float nz) {
+  uint4 u;
+  __builtin_memcpy(&u, &v, 16);
+  const uint32_t wd = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
+  float r;
+  if (e & 1)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(d), "v"(wd), "v"(nz));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(d), "v"(wd), "v"(nz));
+  return r;
+}
+// -0.0f, opaque to the compiler
+__device__ __forceinline__ float neg_zero() {
+  float z = -0.0f;
+  asm volatile("" : "+v"(z));
+  return z;
 }
 
 // Eight consecutive b-bit codes (code e at bits b e of an LSB-first stream)
@@ -163,6 +186,34 @@ __device__ __forceinline__ void put_codes8(uint8_t* p, const uint32_t (&cq)[8], 
     p[0] = (uint8_t)v;
     p[1] = (uint8_t)(v >> 8);
     p[2] = (uint8_t)(v >> 16);
+  }
+}
+
+// Eight codes held as fp32 integers in [0, 2^b - 1] (rounded and clamped),
+// stored as put_codes8 does.  4 and 8 bits: bytes formed as exact fp32 sums
+// (c0 + 16 c1 for two 4-bit codes) and inserted by v_cvt_pk_u8_f32, whose
+// conversion of an integer in [0, 255] is that integer; other widths go
+// through 32-bit integers.
+template <int BITS>
+__device__ __forceinline__ void store_codes8(uint8_t* p, const float (&cf)[8], int bits) {
+  if constexpr (BITS == 4) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(16.0f, cf[2 * k + 1], cf[2 * k]), k, w);
+    *(uint32_t*)p = w;
+  } else if constexpr (BITS == 8) {
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      w0 = __builtin_amdgcn_cvt_pk_u8_f32(cf[k], k, w0);
+      w1 = __builtin_amdgcn_cvt_pk_u8_f32(cf[k + 4], k, w1);
+    }
+    *(uint2*)p = make_uint2(w0, w1);
+  } else {
+    uint32_t cq[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cq[e] = (uint32_t)cf[e];
+    put_codes8(p, cq, bits);
   }
 }
 
@@ -282,8 +333,10 @@ __device__ __forceinline__ void balance_f64(SealLds<SUBW>& L, const half8 (&ar)[
 }
 
 // One tile; KV (0 keys, 1 values) is a compile-time choice so that the keys'
-// path holds one copy of the tile once the balancing is done.
-template <int SUBW, int KV>
+// path holds one copy of the tile once the balancing is done.  BITS is the
+// code width when known at compile time (the 4- and 8-bit bodies: constant
+// shifts in the packing), 0 to read it from the layout.
+template <int SUBW, int KV, int BITS>
 __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, int r, int sub, int h, int s,
                                           int layer) {
   using Sh = SealShape<SUBW>;
@@ -493,7 +546,7 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
   }
 
   // ---- column scales: centre the log scales, clamp, fp16 (thread j: column j)
-  const int bits = kv ? y.vbits : y.kbits;
+  const int bits = BITS ? BITS : kv ? y.vbits : y.kbits;
   const float levels = (float)((1 << bits) - 1);
   uint8_t* rec = a.arena + rec_off(y, s, layer, h, r) + (int64_t)sub * y.sub_bytes;
   uint8_t* meta = rec + y.kcode_bytes + y.vcode_bytes + kv * 2 * (SUBW + 2 * kGroup);
@@ -519,6 +572,7 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
   }
 
   // ---- per-row rounding (row layout): y = x * fp32(1 / C), min and max per row
+  const float nz = neg_zero();
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int row = 16 * (2 * w + t) + m;
@@ -530,7 +584,7 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
       const float ic[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float yv = (d * (float)ar[t][kk][e]) * ic[e];
+        const float yv = mul_e(d, ar[t][kk], e, nz) * ic[e];
         mn = fminf(mn, yv);
         mx = fmaxf(mx, yv);
       }
@@ -554,13 +608,13 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
         const float d = ds[kk / 4][row];
         const float4 i0 = *(const float4*)(invc + 32 * kk + 8 * g), i1 = *(const float4*)(invc + 32 * kk + 8 * g + 4);
         const float ic[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-        uint32_t cq[8];
+        float cf[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float yv = (d * cvt_e(ar[t][kk], e)) * ic[e];
-          cq[e] = (uint32_t)__builtin_amdgcn_fmed3f(rintf((yv - Zf) * inv), 0.0f, levels);
+          const float yv = mul_e(d, ar[t][kk], e, nz) * ic[e];
+          cf[e] = __builtin_amdgcn_fmed3f(rintf((yv - Zf) * inv), 0.0f, levels);
         }
-        put_codes8(rec + (int64_t)row * (SUBW * bits / 8) + (32 * kk + 8 * g) * bits / 8, cq, bits);
+        store_codes8<BITS>(rec + (int64_t)row * (SUBW * bits / 8) + (32 * kk + 8 * g) * bits / 8, cf, bits);
       }
     }
   }
@@ -573,20 +627,20 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
       const float ic = invc[col];
 #pragma unroll
       for (int kr = 0; kr < 4; ++kr) {
-        uint32_t cq[8];
+        float cf[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int row = 32 * kr + 8 * g + e;
-          const float yv = (ds[wb][row] * (float)ac[ct][kr][e]) * ic;
-          cq[e] = (uint32_t)__builtin_amdgcn_fmed3f(rintf((yv - zrow[row]) * rinv[row]), 0.0f, levels);
+          const float yv = mul_e_pure(ds[wb][row], ac[ct][kr], e, nz) * ic;
+          cf[e] = __builtin_amdgcn_fmed3f(rintf((yv - zrow[row]) * rinv[row]), 0.0f, levels);
         }
-        put_codes8(vbase + (int64_t)col * (kGroup * bits / 8) + (32 * kr + 8 * g) * bits / 8, cq, bits);
+        store_codes8<BITS>(vbase + (int64_t)col * (kGroup * bits / 8) + (32 * kr + 8 * g) * bits / 8, cf, bits);
       }
     }
   }
 }
 
-template <int SUBW>
+template <int SUBW, int KB, int VB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void seal_kernel(SealArgs a) {
   __shared__ SealLds<SUBW> L;
   const int gx = blockIdx.x;
@@ -599,9 +653,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   by /= a.y.nsub;
   const int kv = by & 1, h = by >> 1;
   if (kv == 0)
-    seal_tile<SUBW, 0>(a, L, r, sub, h, tk.slot, tk.layer);
+    seal_tile<SUBW, 0, KB>(a, L, r, sub, h, tk.slot, tk.layer);
   else
-    seal_tile<SUBW, 1>(a, L, r, sub, h, tk.slot, tk.layer);
+    seal_tile<SUBW, 1, VB>(a, L, r, sub, h, tk.slot, tk.layer);
 }
 
 // ---------------------------------------------------------------------------
@@ -814,10 +868,11 @@ hipError_t launch_seal(const SealArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL(seal_f16_kernel<128>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
-  if (a.y.sub == 256)
-    hipLaunchKernelGGL(seal_kernel<256>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(seal_kernel<128>, grid, dim3(256), 0, stream, a);
+  // the 4/4 and 8/4 bodies with constant widths, the lower ones read them
+  const bool k4 = a.y.kbits == 4 && a.y.vbits == 4, k8 = a.y.kbits == 8 && a.y.vbits == 4;
+  auto kern = a.y.sub == 256 ? (k4 ? seal_kernel<256, 4, 4> : k8 ? seal_kernel<256, 8, 4> : seal_kernel<256, 0, 0>)
+                             : (k4 ? seal_kernel<128, 4, 4> : k8 ? seal_kernel<128, 8, 4> : seal_kernel<128, 0, 0>);
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -72,14 +72,42 @@ struct SealShape {
   static constexpr int NB = SUBW / kQBlock;  // tq6_0 blocks per row
   static constexpr int KR = SUBW / 32;       // row-pass k-steps (32 columns each)
   static constexpr int CT = SUBW / 64;       // column tiles (16 columns) per wave
-  static constexpr int PITCH = 128 + 8;      // halves per row of the transposed tile (one column)
-  // LDS: the transposed tile, reused once consumed for the factor exchange
-  //   CF  [q, q^2][hi, lo][SUBW] fp16: B operands of the row pass (c, c^2)
-  //   RF  [NB][q, q^2][hi, lo][128] fp16: B operands of the column pass (d r, (d r)^2)
-  static constexpr int QT_BYTES = SUBW * PITCH * 2;
-  static constexpr int CF = 0, RF = CF + 2 * 2 * SUBW * 2, X_BYTES = RF + NB * 2 * 2 * 128 * 2;
-  static constexpr int BYTES = QT_BYTES > X_BYTES ? QT_BYTES : X_BYTES;
+  // LDS: the tile q, row-major fp16 (tile_half), from the load to the last
+  // rounding; the binary64 passes of a flagged tile take the area for their
+  // own state
+  static constexpr int BYTES = 128 * SUBW * 2;
 };
+
+// Half index of tile element (r, c) in LDS: rows of SUBW halves, the row's
+// 16-byte chunks permuted by an XOR with 2 ((r & 3) | ((r >> 3) & 1) << 2), so
+// that a transpose load (load_col8) of 4 + 4 rows x 2 chunks per half-wave
+// meets 16 distinct chunk positions modulo 16: no bank conflicts.
+template <int SUBW>
+__device__ __forceinline__ int tile_half(int r, int c) {
+  return r * SUBW + 8 * ((c >> 3) ^ (2 * ((r & 3) | (((r >> 3) & 1) << 2)))) + (c & 7);
+}
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+
+// The column layout of the tile (the A operand of a column pass, 8 rows of one
+// column per lane) by two LDS transpose loads (ds_read_b64_tr_b16).  Within
+// each group of 16 lanes, element k of lane j's result is element j & 3 of the
+// four halves that lane 4 k + (j >> 2) of the group addresses.  So lane L of
+// group g addresses row r0 + 8 g + (L >> 2) (4 more for the second load) at
+// columns c0 + 4 (L & 3) .. + 3, and lane (j, g) receives column c0 + j, rows
+// r0 + 8 g .. + 7.  c0 a multiple of 16, r0 of 8.
+template <int SUBW>
+__device__ __forceinline__ half8 load_col8(const uint16_t* tile, int r0, int c0, int l) {
+  const int L = l & 15, r = r0 + 8 * (l >> 4) + (L >> 2), c = c0 + 4 * (L & 3);
+  const __attribute__((address_space(3))) uint16_t* t = (const __attribute__((address_space(3))) uint16_t*)tile;
+  const short4v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(t + tile_half<SUBW>(r, c)));
+  const short4v b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(t + tile_half<SUBW>(r + 4, c)));
+  half8 h;
+  __builtin_memcpy(&h, &a, 8);
+  __builtin_memcpy((char*)&h + 8, &b, 8);
+  return h;
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -118,9 +146,9 @@ __device__ __forceinline__ void put_hilo(uint16_t* hi, uint16_t* lo, int i, floa
   lo[i] = f2h_bits(x - h2f(hb));
 }
 
-// q^2 of a packed operand (exact: |q| <= 31), formed in every pass: kept
-// opaque so that the compiler does not hoist the squares of the loop-invariant
-// tile out of the pass loop, which would double the tile's registers.
+// q^2 of a packed operand (exact: |q| <= 31), for the column passes' operands
+// as they come from LDS: kept opaque so that the compiler forms each square
+// next to its product.
 __device__ __forceinline__ half8 sq8(half8 v) {
   uint4 u, o;
   __builtin_memcpy(&u, &v, 16);
@@ -220,6 +248,10 @@ __device__ __forceinline__ void store_codes8(uint8_t* p, const float (&cf)[8], i
 template <int SUBW>
 struct SealLds {
   uint8_t smem[SealShape<SUBW>::BYTES] __attribute__((aligned(16)));
+  // B operands: [q, q^2][hi, lo][SUBW] fp16 of the row pass (c, c^2);
+  // [NB][q, q^2][hi, lo][128] of the column pass (d r, (d r)^2)
+  uint16_t cfl[2 * 2 * SUBW] __attribute__((aligned(16)));
+  uint16_t rfl[SealShape<SUBW>::NB * 2 * 2 * 128] __attribute__((aligned(16)));
   float ds[SealShape<SUBW>::NB][kGroup];     // d_ib
   float lcs[SUBW] __attribute__((aligned(16)));   // ln spread of each column (last column pass)
   float invc[SUBW] __attribute__((aligned(16)));  // fp32(1 / C_j)
@@ -340,7 +372,7 @@ template <int SUBW, int KV, int BITS>
 __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, int r, int sub, int h, int s,
                                           int layer) {
   using Sh = SealShape<SUBW>;
-  constexpr int NB = Sh::NB, KR = Sh::KR, CT = Sh::CT, PITCH = Sh::PITCH;
+  constexpr int NB = Sh::NB, KR = Sh::KR, CT = Sh::CT;
   constexpr int kv = KV;
   const Layout& y = a.y;
   uint8_t* smem = L.smem;
@@ -350,9 +382,9 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
   float* rinv = L.rinv;
   float* zrow = L.zrow;
   float* red = L.red;
-  uint16_t* qt = (uint16_t*)smem;
-  uint16_t* cfl = (uint16_t*)(smem + Sh::CF);  // [2][2][SUBW]
-  uint16_t* rfl = (uint16_t*)(smem + Sh::RF);  // [NB][2][2][128]
+  uint16_t* tile = (uint16_t*)smem;  // q, row-major (tile_half)
+  uint16_t* cfl = L.cfl;
+  uint16_t* rfl = L.rfl;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, m = l & 15, g = l >> 4;
   const int slot0 = (int)(((int64_t)r * kGroup) % y.cap);
@@ -376,37 +408,23 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
       ar[t][kk] = codes6_reg(__builtin_amdgcn_alignbit(hi, lo, sh), hi >> sh);
     }
   }
+  // the same tile in LDS for the column layout (load_col8)
+  auto put_tile = [&]() {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int kk = 0; kk < KR; ++kk) {
+        uint4 u;
+        __builtin_memcpy(&u, &ar[t][kk], 16);
+        *(uint4*)(tile + tile_half<SUBW>(16 * (2 * w + t) + m, 32 * kk + 8 * g)) = u;
+      }
+  };
+  put_tile();
   // block scales d of every row
   for (int i = tid; i < NB * kGroup; i += 256) {
     const int row = i % kGroup, b = i / kGroup;
     ds[b][row] = h2f(*(const uint16_t*)(scales + (int64_t)slot_of(row) * (y.NB * 2) + 2 * b));
   }
-  // transposed tile in LDS: item (tq, c16) = rows 4 tq .. + 3, columns 16 c16 .. + 15
-  for (int it = tid; it < 32 * (SUBW / 16); it += 256) {
-    const int tq = it & 31, c16 = it >> 5;
-    uint4 lo8[4], hi8[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t* p = (const uint32_t*)(codes + (int64_t)slot_of(4 * tq + k) * row_bytes + (c16 / 8) * kQBytes +
-                                            12 * (c16 % 8));
-      const uint32_t v0 = p[0], v1 = p[1], v2 = p[2];
-      const half8 x0 = codes6_reg(v0, v1);
-      const half8 x1 = codes6_reg(__builtin_amdgcn_alignbit(v2, v1, 16), v2 >> 16);
-      __builtin_memcpy(&lo8[k], &x0, 16);
-      __builtin_memcpy(&hi8[k], &x1, 16);
-    }
-    store_t4x8(qt, PITCH, 16 * c16, 4 * tq, lo8);
-    store_t4x8(qt, PITCH, 16 * c16 + 8, 4 * tq, hi8);
-  }
-  __syncthreads();
-  // column layout: ac[ct][kr] = q of column 16 (CT w + ct) + m, rows 32 kr + 8 g .. + 7
-  half8 ac[CT][4];
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-    for (int kr = 0; kr < 4; ++kr)
-      ac[ct][kr] = mfma_a(*(const uint4*)(qt + (16 * (CT * w + ct) + m) * PITCH + 32 * kr + 8 * g));
-  __syncthreads();  // the transposed tile is consumed: its area holds the factors from here on
   for (int j = tid; j < SUBW; j += 256) {  // first row pass: c = 1, pre-scaled (hi kCScale, lo 0)
     cfl[0 * SUBW + j] = f2h_bits(kCScale);
     cfl[1 * SUBW + j] = 0;
@@ -415,6 +433,13 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
     lcs[j] = 0.0f;
   }
   if (tid < 2) L.bad[tid] = 0;
+  // q^2 of the row layout (exact: |q| <= 31), the A operand of the row passes'
+  // second moments; the column passes square their operands as they load them
+  half8 ar2[2][KR];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int kk = 0; kk < KR; ++kk) ar2[t][kk] = ar[t][kk] * ar[t][kk];
   __syncthreads();
 
   // B carries the factor's fp16 hi in its even columns and lo in its odd ones
@@ -434,6 +459,10 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
     lc_keep[e] = 0.0f;
   }
 
+  // d of this lane pair's row in a row pass (row 16 (2w + t) + 4 g + i, t = pr / 4, i = pr % 4)
+  float drow[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) drow[b] = ds[b][16 * (2 * w + (pr >> 2)) + 4 * g + (pr & 3)];
   bool exact = false;  // flagged: the binary64 passes take the tile
   for (int p = 0; p < a.passes; ++p) {
     bool flag = false;
@@ -452,7 +481,7 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           a1[t][b] = mfma16(ar[t][kk], b1, a1[t][b]);
-          a2[t][b] = mfma16(sq8(ar[t][kk]), b2, a2[t][b]);
+          a2[t][b] = mfma16(ar2[t][kk], b2, a2[t][b]);
         }
       }
       const int t = pr >> 2, i = pr & 3;
@@ -463,7 +492,7 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
         float x1 = pick4(t ? a1[1][b] : a1[0][b], i), x2 = pick4(t ? a2[1][b] : a2[0][b], i);
         x1 += dpp<0xB1>(x1);  // hi + lo (quad_perm [1, 0, 3, 2])
         x2 += dpp<0xB1>(x2);
-        const float d = ds[b][row];
+        const float d = drow[b];
         s1 = fmaf(d, x1, s1);
         s2 = fmaf(d * d, x2, s2);
       }
@@ -477,7 +506,7 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
       rf_keep = rf;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const float f = ds[b][row] * rf * kRScale;
+        const float f = drow[b] * rf * kRScale;
         flag = flag || f > kFMax || (f != 0.0f && f < kFMin);
         if ((m & 1) == 0) {
           uint16_t* base = rfl + b * 4 * kGroup;
@@ -492,15 +521,32 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) c1[ct] = c2[ct] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
       const uint16_t* base = rfl + wb * 4 * kGroup;
+      // software-pipelined over the 4 CT steps (kr, ct): the column operand of
+      // step j + 2 (and the factors of its kr) is loaded before the products of
+      // step j (the scheduling barriers keep that order), so each product
+      // waits for loads issued two steps earlier
+      constexpr int NS = 4 * CT, LA = 2;
+      half8 op[LA + 1], bf1[2], bf2[2];
+      auto load_b = [&](int kr) {
+        bf1[kr & 1] = mfma_a(*(const uint4*)(base + (0 + (m & 1)) * kGroup + 32 * kr + 8 * g));
+        bf2[kr & 1] = mfma_a(*(const uint4*)(base + (2 + (m & 1)) * kGroup + 32 * kr + 8 * g));
+      };
+      auto load_op = [&](int j) { op[j % (LA + 1)] = load_col8<SUBW>(tile, 32 * (j / CT), 16 * (CT * w + j % CT), l); };
+      load_b(0);
 #pragma unroll
-      for (int kr = 0; kr < 4; ++kr) {
-        const half8 b1 = mfma_a(*(const uint4*)(base + (0 + (m & 1)) * kGroup + 32 * kr + 8 * g));
-        const half8 b2 = mfma_a(*(const uint4*)(base + (2 + (m & 1)) * kGroup + 32 * kr + 8 * g));
+      for (int j = 0; j < LA; ++j) load_op(j);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          c1[ct] = mfma16(ac[ct][kr], b1, c1[ct]);
-          c2[ct] = mfma16(sq8(ac[ct][kr]), b2, c2[ct]);
+      for (int j = 0; j < NS; ++j) {
+        const int kr = j / CT, ct = j % CT;
+        if (j + LA < NS) {
+          if ((j + LA) % CT == 0) load_b((j + LA) / CT);
+          load_op(j + LA);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        const half8 a = op[j % (LA + 1)];
+        c1[ct] = mfma16(a, bf1[kr & 1], c1[ct]);
+        c2[ct] = mfma16(sq8(a), bf2[kr & 1], c2[ct]);
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int e = 0; e < NCL; ++e) {
@@ -552,6 +598,7 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
   uint8_t* meta = rec + y.kcode_bytes + y.vcode_bytes + kv * 2 * (SUBW + 2 * kGroup);
   if (exact) {
     balance_f64<SUBW>(L, ar, a.passes, meta);
+    if constexpr (kv == 1) put_tile();  // its state took the tile's area; the value codes read the tile
   } else {
     float v = tid < SUBW ? lcs[tid] : 0.0f;
     v += dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
@@ -627,11 +674,12 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
       const float ic = invc[col];
 #pragma unroll
       for (int kr = 0; kr < 4; ++kr) {
+        const half8 ac = load_col8<SUBW>(tile, 32 * kr, 16 * (CT * w + ct), l);
         float cf[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int row = 32 * kr + 8 * g + e;
-          const float yv = mul_e_pure(ds[wb][row], ac[ct][kr], e, nz) * ic;
+          const float yv = mul_e_pure(ds[wb][row], ac, e, nz) * ic;
           cf[e] = __builtin_amdgcn_fmed3f(rintf((yv - zrow[row]) * rinv[row]), 0.0f, levels);
         }
         store_codes8<BITS>(vbase + (int64_t)col * (kGroup * bits / 8) + (32 * kr + 8 * g) * bits / 8, cf, bits);

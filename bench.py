@@ -593,7 +593,10 @@ def seal_entry(seal):
                      "unit": "TFLOP/s", "frac": round(seal["tflops"] / FP32_VALU_NONPACKED_TFLOPS, 4),
                      "flops_basis": "per 128 x 256 tile: passes x 4 x 32,768 (two mat-vecs, y and y^2) "
                                     "+ 6 x 32,768 (rounding)",
-                     "hbm_floor_us": round(seal["hbm_bytes"] / (HBM_PEAK_GBS * 1e9) * 1e6, 2)},
+                     "hbm_floor_us": round(seal["hbm_bytes"] / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+                     "limited_by": "LDS bandwidth of the matrix-core factor operands and each pass's dependent "
+                                   "statistics chain (counters: matrix cores 23 % busy, vector issue 32 % of "
+                                   "wave life)"},
     }
 
 

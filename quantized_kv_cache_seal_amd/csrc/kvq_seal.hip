@@ -18,10 +18,11 @@
 // (or its square, exact up to 961) as the A operand and the factor vector in B
 // (fp16 hi in the even columns, fp16 lo, the remainder, in the odd ones), so
 // each factor keeps 22 significant bits and every product is exact; a column
-// pair of the result is added.  Row passes read the tile with 8 consecutive columns of one
-// row per lane, column passes with 8 consecutive rows of one column per lane;
-// both copies stay in registers (the second is built through a transposed tile
-// in LDS).  The updated side's factor is 1/spread (equal to exp(-l) of the
+// pair of the result is added.  Row passes take the tile from registers (8
+// consecutive columns of one row per lane, their squares kept beside them);
+// column passes read 8 consecutive rows of one column per lane from a
+// row-major copy in LDS by transpose loads, two k-steps ahead of the products.
+// The updated side's factor is 1/spread (equal to exp(-l) of the
 // log-domain update l += ln spread, spread the population standard deviation);
 // a row or column of zeros (zero sum of squares: every product is exact, so
 // that sum is zero only then) keeps its factor and log scale; the factors pass
@@ -49,7 +50,8 @@
 // fused multiply-add (built with -ffp-contract=off): y = x * fp32(1/C),
 // S = fp16((max - min) / (2^b - 1)) (1.0 if zero), Z = fp16(min),
 // code = clamp(rne((y - Z) * fp32(1/S)), 0, 2^b - 1) (the clamp as one median
-// of three, the same value for every finite input).
+// of three, the same value for every finite input); x = d q as one mixed
+// fp16 x fp32 multiply (mul_e), the codes packed as bytes (store_codes8).
 #include "kvq_mfma.h"
 
 namespace kvq {

@@ -148,18 +148,14 @@ __device__ __forceinline__ void put_hilo(uint16_t* hi, uint16_t* lo, int i, floa
   lo[i] = f2h_bits(x - h2f(hb));
 }
 
-// q^2 of a packed operand (exact: |q| <= 31), for the column passes' operands
-// as they come from LDS: kept opaque so that the compiler forms each square
-// next to its product.
-__device__ __forceinline__ half8 sq8(half8 v) {
-  uint4 u, o;
-  __builtin_memcpy(&u, &v, 16);
-  asm volatile("v_pk_mul_f16 %0, %1, %1" : "=v"(o.x) : "v"(u.x));
-  asm volatile("v_pk_mul_f16 %0, %1, %1" : "=v"(o.y) : "v"(u.y));
-  asm volatile("v_pk_mul_f16 %0, %1, %1" : "=v"(o.z) : "v"(u.z));
-  asm volatile("v_pk_mul_f16 %0, %1, %1" : "=v"(o.w) : "v"(u.w));
-  return mfma_a(o);
-}
+// q^2 of a packed operand (exact: |q| <= 31) as fma(q, q, z) with z a zero
+// that every pass reads from LDS, so that the compiler forms each square in
+// the pass that uses it; the packed FMAs are ordinary instructions, whose
+// hazards with the matrix cores the compiler tracks (it inserts the wait
+// states a product reading a just-written VGPR needs, and never hands a
+// register that an in-flight product will still write to them -- neither
+// holds for VGPRs written inside inline asm).
+__device__ __forceinline__ half8 sq8(half8 v, half8 z) { return __builtin_elementwise_fma(v, v, z); }
 
 // fp32(d * x) for element e of a packed fp16 operand in one instruction:
 // v_fma_mix_f32 reads x as fp16 and adds nz = -0, the identity of every
@@ -262,6 +258,7 @@ struct SealLds {
   float red[4];
   double red64[4];
   int bad[2];  // fast passes: tile flagged in a pass of this parity
+  uint4 zero16;  // fp16 zeros, read every pass (sq8)
 };
 
 // Binary64 balancing of a flagged tile, from the start: the passes as
@@ -435,6 +432,7 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
     lcs[j] = 0.0f;
   }
   if (tid < 2) L.bad[tid] = 0;
+  if (tid == 0) L.zero16 = make_uint4(0u, 0u, 0u, 0u);
   // q^2 of the row layout (exact: |q| <= 31), the A operand of the row passes'
   // second moments; the column passes square their operands as they load them
   half8 ar2[2][KR];
@@ -468,6 +466,7 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
   bool exact = false;  // flagged: the binary64 passes take the tile
   for (int p = 0; p < a.passes; ++p) {
     bool flag = false;
+    const half8 zq = mfma_a(L.zero16);
     if ((p & 1) == 0) {
       // ---- row pass: pair pr takes row 16 (2w + t) + 4 g + i, t = pr / 4, i = pr % 4
       float4v a1[2][NB], a2[2][NB];
@@ -547,7 +546,7 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
         __builtin_amdgcn_sched_barrier(0);
         const half8 a = op[j % (LA + 1)];
         c1[ct] = mfma16(a, bf1[kr & 1], c1[ct]);
-        c2[ct] = mfma16(sq8(a), bf2[kr & 1], c2[ct]);
+        c2[ct] = mfma16(sq8(a, zq), bf2[kr & 1], c2[ct]);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll

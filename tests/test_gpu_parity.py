@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 from oracle import cache as ocache
+from oracle import record
 from quantized_kv_cache_seal_amd import configs, inputs, kvq
 
 from harness import ATTN_TOL, Pair
@@ -263,6 +264,29 @@ def test_groups_over_eight(shape, group):
             err = float(np.max(np.abs(got[s] - ref)) / np.sqrt(np.mean(ref ** 2)))
             assert err <= ATTN_TOL, (shape, group, step, s, err)
     assert p.check_sink_ring() > 0
+
+
+@pytest.mark.parametrize("passes", [0, 1, 3, 5])
+def test_records_other_pass_counts(passes):
+    """Balancing pass counts other than the configurations' 8 and 16 (SJ-KVaRN
+    2.2: alternating passes, rows first): none and a single row pass (every
+    column scale stays 1), and odd counts, whose last pass is a row pass (the
+    column scales come from the column pass before it).  Records by the
+    conditional rule at the config 2 shape and at 128-wide heads."""
+    for base, signs in ((configs.QWEN27B, False), (configs.QWEN14B1M, True)):
+        w = base.scaled(n_layers=1, n_kv_heads=2, n_q_heads=2 * (base.n_q_heads // base.n_kv_heads), tail_min=256,
+                        tail_max=512, ctx=1200, passes=passes)
+        sg = inputs.rotation_signs(w.seed) if signs else None
+        _say(f"[passes {passes}] {w.name} build")
+        p = Pair(w, [1200], sg).build(300)
+        st = p.check_records()
+        _say(f"[passes {passes}] {w.name} records: {st}")
+        assert st["scales"] > 0 and st["boundary"] <= max(1, st["codes"] // 10 ** 5)
+        if passes < 2:
+            for r in range(p.ora.info(0, 0)[1]):
+                for sub in record.parse_record(p.gpu.export(0, 0, 0, kvq.REGION_BODY, r), w.head_dim, w.k_bits,
+                                               w.v_bits):
+                    assert np.all(sub[0]["C"] == np.float16(1.0)) and np.all(sub[1]["C"] == np.float16(1.0))
 
 
 @pytest.mark.parametrize("shape", [(512, 3, 2), (128, 3, 3), (128, 2, 2)])

@@ -44,8 +44,8 @@
 // their spread, and channels orders of magnitude below the rest take the
 // exact one.
 //
-// The balancing factors (1/spread, ln spread) use the hardware square root,
-// reciprocal and log2 (about 1 ulp): only the column scales C leave the
+// The balancing factors (1/spread, ln spread) use the hardware reciprocal
+// square root and log2 of the variance (about 1 ulp): only the column scales C leave the
 // balancing, and they are rounded to fp16.  Rounding is IEEE fp32 with no
 // fused multiply-add (built with -ffp-contract=off): y = x * fp32(1/C),
 // S = fp16((max - min) / (2^b - 1)) (1.0 if zero), Z = fp16(min),
@@ -503,17 +503,17 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
       const float var = ms - mean * mean;
       const bool upd = s2 > 0.0f;
       flag = upd && !(var > kIllCond * ms);
-      const float rf = upd ? __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(fmaxf(var, 0.0f))) : rf_keep;
+      const float rf = upd ? __builtin_amdgcn_rsqf(fmaxf(var, 0.0f)) : rf_keep;
       rf_keep = rf;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const float f = drow[b] * rf * kRScale;
         flag = flag || f > kFMax || (f != 0.0f && f < kFMin);
-        if ((m & 1) == 0) {
-          uint16_t* base = rfl + b * 4 * kGroup;
-          put_hilo(base + 0 * kGroup, base + 1 * kGroup, row, f);
-          put_hilo(base + 2 * kGroup, base + 3 * kGroup, row, f * f);
-        }
+        // both lanes of the pair hold the row's sums: both store (the same
+        // halves to the same place), with no branch around the stores
+        uint16_t* base = rfl + b * 4 * kGroup;
+        put_hilo(base + 0 * kGroup, base + 1 * kGroup, row, f);
+        put_hilo(base + 2 * kGroup, base + 3 * kGroup, row, f * f);
       }
     } else {
       // ---- column pass: pair pr takes columns 16 (CT w + ct) + 4 g + i of its
@@ -568,18 +568,16 @@ __device__ __forceinline__ void seal_tile(const SealArgs& a, SealLds<SUBW>& L, i
         const float ms = x2 * (1.0f / (kRScale * kRScale * kGroup));
         const float var = ms - mean * mean;
         const bool upd = x2 > 0.0f;
-        const float sig = __builtin_amdgcn_sqrtf(fmaxf(var, 0.0f));
-        const float cf = upd ? __builtin_amdgcn_rcpf(sig) : cf_keep[e];
-        const float lc = upd ? __builtin_amdgcn_logf(sig) * 0.6931471805599453f : lc_keep[e];  // log2 -> ln
+        const float v0 = fmaxf(var, 0.0f);
+        const float cf = upd ? __builtin_amdgcn_rsqf(v0) : cf_keep[e];
+        const float lc = upd ? __builtin_amdgcn_logf(v0) * 0.34657359027997264f : lc_keep[e];  // ln sqrt: log2 / 2 ln 2
         cf_keep[e] = cf;
         lc_keep[e] = lc;
         const float c = cf * kCScale;
         flag = flag || (upd && !(var > kIllCond * ms)) || c > kFMax || c < kFMin;
-        if ((m & 1) == 0) {
-          put_hilo(cfl + 0 * SUBW, cfl + 1 * SUBW, col, c);
-          put_hilo(cfl + 2 * SUBW, cfl + 3 * SUBW, col, c * c);
-          lcs[col] = lc;
-        }
+        put_hilo(cfl + 0 * SUBW, cfl + 1 * SUBW, col, c);  // both lanes of the pair, as above
+        put_hilo(cfl + 2 * SUBW, cfl + 3 * SUBW, col, c * c);
+        lcs[col] = lc;
       }
     }
     if (flag) L.bad[p & 1] = 1;  // read after this pass's barrier, written again two passes on
